@@ -1,0 +1,128 @@
+/*
+ * kvq_oracle.h -- plain, slow CPU oracle for rotated INT2 KV-cache quantization
+ * and decode attention over the packed cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may build, load or call this code.  The
+ * product path (the HIP library and its Python binding) never does, and this
+ * code includes, links and calls nothing from the product path.
+ *
+ * Sources (all citations are to the pages the method is described on):
+ *   [OptR]  "Output-Aware Rotation for INT2 KV-Cache Quantization" (paper deep
+ *           dive page: full text of arXiv 2608.02691v2).
+ *   [Eval]  "Output-aware INT2 KV-cache rotation evaluation" (project page
+ *           with the observed 4,096-token envelope).
+ *
+ * Precision: every floating-point step is fp64, except the INT2 quantizer,
+ * whose scale/zero are fp16 [Eval, observed envelope: fp16 scale/zero is part
+ * of the recipe] and whose fp32 step sequence is this implementation's stated
+ * reading of "group-wise affine INT2 with clipping ratio c" [OptR, §3.1 and
+ * Appendix Table A].  The file is compiled with -O2 -ffp-contract=off and no
+ * fast-math, so every fp32 operation rounds once, to nearest even.
+ */
+#ifndef KVQ_ORACLE_H
+#define KVQ_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQO_D 128 /* head dimension == quantization group size */
+
+enum {
+  KVQO_OK = 0,
+  KVQO_ERR_ARG = 1,       /* bad shape, null pointer, out-of-range index   */
+  KVQO_ERR_NONFINITE = 2, /* NaN/Inf input to the quantizer                */
+  KVQO_ERR_RANGE = 3      /* scale or zero does not fit in fp16            */
+};
+
+enum { KVQO_ROT_IDENTITY = 0, KVQO_ROT_SIGNED_HADAMARD = 1, KVQO_ROT_DENSE = 2 };
+enum { KVQO_SELECT_JOINT = 0, KVQO_SELECT_PER_HEAD = 1 };
+
+/* fp32 -> fp16 bits, round to nearest even.  Returns KVQO_ERR_RANGE when the
+ * rounded magnitude exceeds 65504, KVQO_ERR_NONFINITE for NaN/Inf. */
+int kvqo_f32_to_f16(float x, uint16_t *bits);
+float kvqo_f16_to_f32(uint16_t bits);
+
+/* Sylvester Hadamard matrix of order n (power of two), entries +1/-1, built
+ * by the doubling rule H(2m) = [[H(m), H(m)], [H(m), -H(m)]]. */
+int kvqo_sylvester(int n, double *h);
+
+/* Dense fp64 rotation R (row-vector convention z' = z R) for one head.
+ * kind IDENTITY: R = I.  SIGNED_HADAMARD: R = diag(signs) H / sqrt(128).
+ * DENSE: R = the given fp32 matrix (row-major [128][128]). */
+int kvqo_rotation_matrix(int kind, const int8_t *signs, const float *matrix, double *r);
+
+/* One INT2 group (n values, n >= 1): scale/zero and codes 0..3. */
+int kvqo_quantize_group(const float *x, int n, float clip, uint8_t *codes, uint16_t *scale_bits,
+                        uint16_t *zero_bits);
+
+/* Paged packed cache, byte layout fixed by the C-ABI header of the library
+ * (see the per-field comments in kvq_oracle.c, which restate it). */
+typedef struct {
+  uint8_t *pages;      /* [num_pages][num_kv_heads][72 * page_size] */
+  int64_t num_pages;
+  int32_t page_size;   /* tokens per page, multiple of 4 */
+  int32_t num_kv_heads;
+} kvqo_cache;
+
+/* Rotations for all heads of one side (K or V). */
+typedef struct {
+  int32_t kind;
+  const int8_t *signs;  /* [H][128] when kind == SIGNED_HADAMARD */
+  const float *matrix;  /* [H][128][128] when kind == DENSE      */
+} kvqo_rotation;
+
+/* Cache write: rotate (and center keys), quantize every (token, head, K|V)
+ * group, pack into slot slot_mapping[t] (identity when NULL).
+ * k, v: [num_tokens][H][128] (bf16 inputs are passed widened to fp32). */
+int kvqo_quantize(const float *k, const float *v, int64_t num_tokens, const int64_t *slot_mapping,
+                  const kvqo_rotation *rot_k, const kvqo_rotation *rot_v, const float *key_mean,
+                  float clip_k, float clip_v, kvqo_cache *cache);
+
+/* Rotated values as fp32 (what the quantizer sees): out[t][h][:] */
+int kvqo_rotate(const float *x, int64_t num_tokens, int32_t num_heads, const kvqo_rotation *rot,
+                const float *mean, float *out);
+
+/* Read back one group: codes[128], scale and zero bits. kv = 0 for K, 1 for V. */
+int kvqo_read_group(const kvqo_cache *cache, int64_t slot, int32_t head, int kv, uint8_t *codes,
+                    uint16_t *scale_bits, uint16_t *zero_bits);
+
+/* Decode attention over the packed cache.
+ * q: [num_seqs * queries_per_seq][Hq][128]; query row r belongs to sequence
+ * r / queries_per_seq; page_table [num_seqs][max_pages] (NULL: page of token t
+ * of sequence b is b * max_pages + t / page_size); seq_lens [num_seqs].
+ * w_o: [Hq * 128][d_model] or NULL.  out_o: [rows][Hq][128]; out_y: [rows][d_model]. */
+int kvqo_decode(const float *q, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                const kvqo_cache *cache, const int32_t *page_table, int32_t max_pages,
+                const int32_t *seq_lens, const kvqo_rotation *rot_k, const kvqo_rotation *rot_v,
+                const float *w_o, int32_t d_model, float *out_o, float *out_y);
+
+/* Same decode but returning fp64 results (used by the candidate search). */
+int kvqo_decode_f64(const float *q, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                    const kvqo_cache *cache, const int32_t *page_table, int32_t max_pages,
+                    const int32_t *seq_lens, const kvqo_rotation *rot_k, const kvqo_rotation *rot_v,
+                    double *out_o);
+
+/* Full-precision reference attention over raw K, V ([T][H][128]); every query
+ * row attends all num_tokens tokens.  out_o: [rows][Hq][128] fp64. */
+int kvqo_attention_ref(const float *q, int32_t rows, int32_t num_q_heads, const float *k,
+                       const float *v, int64_t num_tokens, int32_t num_kv_heads, double *out_o);
+
+/* Candidate search by post-W_O NMSE.  candidates: [C]; clips: [n_clip].
+ * mode JOINT: one unit (the whole layer output); PER_HEAD: one unit per KV head.
+ * out_nmse [U][C][n_clip] (mean over queries), out_nmse_q [U][C][n_clip][Nq]
+ * (may be NULL), out_best [U] = r * n_clip + i of the first minimum. */
+int kvqo_candidate_nmse(const float *k, const float *v, const float *q, int64_t num_tokens,
+                        int32_t num_kv_heads, int32_t num_q_heads, int32_t num_queries,
+                        const kvqo_rotation *candidates, int32_t num_candidates, const float *clips,
+                        int32_t num_clips, const float *key_mean, const float *w_o, int32_t d_model,
+                        int32_t mode, double *out_nmse, double *out_nmse_q, int32_t *out_best);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
