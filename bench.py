@@ -1,0 +1,182 @@
+"""Benchmark of the rotated-INT2 KV-cache hot path on one MI355X.
+
+One step = cache write of the whole batch (kvq_quantize: rotation, clip,
+INT2 quantize, pack, paged write) + one decode step over it (kvq_decode_attn:
+query rotation, split-K attention straight from the packed cache, merge,
+inverse value rotation, W_O), on the paged batched-decode workload:
+16 sequences x 32,768 tokens, 16-token pages with a permuted page table,
+32 query / 8 KV heads, head_dim 128, bf16 K/V/q/W_O, signed-Hadamard rotation
+per head, W_O [4096, 4096].  Inputs are seeded synthetic data resident in HBM
+before the timed region.
+
+Two cache buffers alternate: step i writes cache i%2 and decodes cache
+(i+1)%2 (written one step earlier and followed by >2 GB of other traffic), so
+the decode reads its 302 MB from HBM, not from the 256 MB Infinity Cache.
+
+Prints one JSON line.  value = effective KV GB/s of the split-K attention
+kernel (72 bytes per cached token per KV head / its average duration,
+measured with HIP events recorded on the launch stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
+BYTES_PER_TOKEN_HEAD = 72      # 2 x 32 B codes + 2 x 4 B fp16 scale/zero
+WORKLOAD = "paged16x32k"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_split_paged16x32k_traffic.json"))
+    return ap.parse_args()
+
+
+def cpu_baseline(w_cpu) -> dict:
+    """The oracle as it stands, timed on this host on a bounded sample of the
+    same workload: one sequence, 2 of its 8 KV heads (8 query heads), all
+    32,768 tokens: cache write then decode."""
+    import numpy as np
+    import oracle
+
+    H_s = 2
+    T = w_cpu["tokens"]
+    k = w_cpu["k"][:T, :H_s].astype(np.float32)
+    v = w_cpu["v"][:T, :H_s].astype(np.float32)
+    q = w_cpu["q"][:1, :H_s * 4].astype(np.float32)
+    signs = w_cpu["signs"][:H_s]
+    P = 16
+    pages = (T + P - 1) // P
+    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=signs)
+    cache = oracle.Cache(pages, P, H_s)
+    t0 = time.perf_counter()
+    oracle.quantize(k, v, cache, rot, rot, clip_k=0.96, clip_v=0.92)
+    t1 = time.perf_counter()
+    oracle.decode(q, cache, [T], rot, rot, num_seqs=1, max_pages=pages)
+    t2 = time.perf_counter()
+    dec_gbs = T * H_s * BYTES_PER_TOKEN_HEAD / (t2 - t1) / 1e9
+    tok_equiv = T * H_s / 8.0  # tokens of the 8-KV-head layer
+    return {"value": dec_gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 sequence x 2 of 8 KV heads x {T} tokens: oracle cache write "
+                      f"{t1 - t0:.2f} s, oracle decode (8 query heads) {t2 - t1:.2f} s",
+            "quantize_mtok_s": tok_equiv / (t1 - t0) / 1e6}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (every box here has one GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synthetic
+    from decode_attention_int2_amd import kvq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvq.load_library()
+    w = synthetic.make(WORKLOAD, dev)
+    B, T, H, Hq, dm, P = w.num_seqs, w.tokens, w.H, w.Hq, w.d_model, w.page_size
+    rot = kvq.Rotation(w.rot_k.kind, signs=w.rot_k.signs)
+    caches = [kvq.Cache(w.num_pages, P, H, device=dev) for _ in range(2)]
+    max_pages = w.page_table.shape[1]
+    rows = B * w.queries_per_seq
+    out_o = torch.empty((rows, Hq, 128), dtype=torch.float32, device=dev)
+    out_y = torch.empty((rows, dm), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, 1, Hq, H, T, dm), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kvq.kvq_quantize(w.k, w.v, caches[i % 2], rot, rot, clip_k=w.clip_k, clip_v=w.clip_v,
+                         slot_mapping=w.slot_mapping)
+        if ev is not None:
+            ev[1].record(stream)
+        kvq.kvq_decode_attn(w.q, B, 1, caches[(i + 1) % 2], w.page_table, max_pages, w.seq_lens, T, rot, rot, out_o,
+                            w_o=w.w_o, out_y=out_y, workspace=ws, split_events=None if ev is None else (ev[2], ev[3]))
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(2):                      # both cache buffers hold a valid cache before warmup
+        kvq.kvq_quantize(w.k, w.v, caches[i], rot, rot, clip_k=w.clip_k, clip_v=w.clip_v,
+                         slot_mapping=w.slot_mapping)
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / a.steps
+    split_ms = sum(e[2].elapsed_time(e[3]) for e in events) / a.steps
+    decode_ms = sum(e[1].elapsed_time(e[4]) for e in events) / a.steps
+    kv_bytes = B * T * H * BYTES_PER_TOKEN_HEAD
+    split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
+    tokens = B * T
+    quant_bytes = tokens * H * (2 * 128 * 2 + BYTES_PER_TOKEN_HEAD)
+    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(a.traffic_json):
+        try:
+            with open(a.traffic_json) as f:
+                traffic = json.load(f).get("hbm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    base = None
+    if not a.no_cpu_baseline:
+        w_cpu = {"tokens": T, "k": w.k[:T].float().cpu().numpy(), "v": w.v[:T].float().cpu().numpy(),
+                 "q": w.q[:1].float().cpu().numpy(), "signs": w.rot_k.signs.cpu().numpy()}
+        base = cpu_baseline(w_cpu)
+
+    out = {
+        "metric": "INT2 decode-attn effective KV GB/s (% HBM peak) + quantize Mtok/s, 32K ctx",
+        "value": round(split_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall * 1e3 / a.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "description": synthetic.DESCRIPTIONS[WORKLOAD], "batch": B,
+                   "context": T, "kv_heads": H, "q_heads": Hq, "head_dim": 128, "page_size": P, "d_model": dm,
+                   "kv_input_dtype": "bf16", "cache": "int2 group-128 + fp16 scale/zero",
+                   "rotation": "signed_hadamard", "clip_k": w.clip_k, "clip_v": w.clip_v},
+        "pct_hbm_peak": round(100.0 * split_gbs / HBM_PEAK_GBS, 2),
+        "quantize_mtok_s": round(tokens / (quant_ms * 1e-3) / 1e6, 2),
+        "quantize_gbs": round(quant_gbs, 1),
+        "quantize_us": round(quant_ms * 1e3, 2),
+        "decode_split_us": round(split_ms * 1e3, 2),
+        "decode_call_us": round(decode_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_split_kernel", "algorithmic_bytes_per_launch": kv_bytes},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

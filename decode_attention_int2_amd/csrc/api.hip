@@ -1,0 +1,244 @@
+// api.hip -- the C ABI of libkvq: argument validation and launch order.
+// Every check that can run on the host runs before the first launch.
+#include <cmath>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool valid_dtype(int32_t dt) { return dt == KVQ_F32 || dt == KVQ_BF16; }
+
+// 0 = ok, else a kvq_status.
+int check_rotation(const kvq_rotation *r) {
+  if (!r) return KVQ_ERR_INVALID_ARGUMENT;
+  switch (r->kind) {
+    case KVQ_ROT_IDENTITY:
+      return KVQ_OK;
+    case KVQ_ROT_SIGNED_HADAMARD:
+      return r->signs ? KVQ_OK : KVQ_ERR_INVALID_ARGUMENT;
+    case KVQ_ROT_DENSE:
+      return r->matrix ? KVQ_OK : KVQ_ERR_INVALID_ARGUMENT;
+    default:
+      return KVQ_ERR_UNSUPPORTED;
+  }
+}
+
+bool valid_clip(float c) { return std::isfinite(c) && c > 0.0f && c <= 1.0f; }
+
+int check_cache(const kvq_cache *c) {
+  if (!c || !c->pages) return KVQ_ERR_INVALID_ARGUMENT;
+  if (c->num_pages < 1 || c->num_kv_heads < 1 || c->page_size < 16 || c->page_size % 16) return KVQ_ERR_INVALID_ARGUMENT;
+  return KVQ_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct CandidateLayout {
+  int64_t num_pages;
+  DecodePlan plan;
+  size_t off_cache, off_dec, off_seqlen, off_ohat, off_oref, off_nmse, total;
+};
+
+CandidateLayout candidate_layout(int64_t T, int H, int Hq, int Nq, int C, int n_clip) {
+  CandidateLayout L{};
+  L.num_pages = (T + 15) / 16;
+  L.plan = make_decode_plan(1, Nq, Hq, H, static_cast<int>(T), 0, 0);
+  const int U = H;  // upper bound over both modes
+  size_t off = 0;
+  L.off_cache = off;
+  off = align256(off + kvq_cache_bytes(L.num_pages, 16, H));
+  L.off_dec = off;
+  off = align256(off + L.plan.total);
+  L.off_seqlen = off;
+  off = align256(off + sizeof(int32_t));
+  L.off_ohat = off;
+  off = align256(off + static_cast<size_t>(Nq) * Hq * D * sizeof(float));
+  L.off_oref = off;
+  off = align256(off + static_cast<size_t>(Nq) * Hq * D * sizeof(float));
+  L.off_nmse = off;
+  off = align256(off + static_cast<size_t>(U) * C * n_clip * Nq * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+#define KVQ_TRY(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return KVQ_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_cache_bytes(int64_t num_pages, int32_t page_size, int32_t num_kv_heads) {
+  if (num_pages < 0 || page_size < 0 || num_kv_heads < 0) return 0;
+  return static_cast<size_t>(num_pages) * static_cast<size_t>(num_kv_heads) * 72u * static_cast<size_t>(page_size);
+}
+
+int kvq_quantize(const void *k, const void *v, int32_t dtype, int64_t num_tokens, const int64_t *slot_mapping,
+                 const kvq_rotation *rot_k, const kvq_rotation *rot_v, const float *key_mean, float clip_k,
+                 float clip_v, const kvq_cache *cache, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  int rc = check_rotation(rot_k);
+  if (rc) return rc;
+  rc = check_rotation(rot_v);
+  if (rc) return rc;
+  rc = check_cache(cache);
+  if (rc) return rc;
+  if (!valid_clip(clip_k) || !valid_clip(clip_v)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && (!k || !v)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return KVQ_OK;
+  KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, cache->num_kv_heads, slot_mapping, to_dev(*rot_k),
+                          to_dev(*rot_v), key_mean, clip_k, clip_v, cache->pages, cache->num_pages, cache->page_size,
+                          stream));
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t max_seq_len, int32_t d_model, int32_t num_splits) {
+  if (num_seqs < 0 || queries_per_seq < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 0 ||
+      num_q_heads % num_kv_heads)
+    return 0;
+  return make_decode_plan(num_seqs, queries_per_seq, num_q_heads, num_kv_heads, max_seq_len, d_model > 0 ? d_model : 0,
+                          num_splits)
+      .total;
+}
+
+int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                    const kvq_cache *cache, const int32_t *page_table, int32_t max_pages_per_seq,
+                    const int32_t *seq_lens, int32_t max_seq_len, const kvq_rotation *rot_k,
+                    const kvq_rotation *rot_v, const void *w_o, int32_t d_model, float *out_o, float *out_y,
+                    void *workspace, size_t workspace_bytes, int32_t num_splits, const kvq_decode_events *events,
+                    hipStream_t stream) {
+  if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  rc = check_rotation(rot_k);
+  if (rc) return rc;
+  rc = check_rotation(rot_v);
+  if (rc) return rc;
+  if (num_seqs < 0 || queries_per_seq < 1 || num_q_heads < 1 || max_pages_per_seq < 1 || max_seq_len < 0 ||
+      num_splits < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const int H = cache->num_kv_heads;
+  if (num_q_heads % H) return KVQ_ERR_INVALID_ARGUMENT;
+  if (static_cast<int64_t>(queries_per_seq) * (num_q_heads / H) > kMaxRows) return KVQ_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_pages_per_seq) * cache->page_size)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (!page_table && static_cast<int64_t>(num_seqs) * max_pages_per_seq > cache->num_pages)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (w_o && (d_model < 1 || !out_y)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_seqs > 0 && (!q || !seq_lens || !out_o)) return KVQ_ERR_INVALID_ARGUMENT;
+  const DecodePlan pl = make_decode_plan(num_seqs, queries_per_seq, num_q_heads, H, max_seq_len,
+                                         w_o ? d_model : 0, num_splits);
+  if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return KVQ_ERR_WORKSPACE;
+  if (num_seqs == 0) return KVQ_OK;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  float *qrot = reinterpret_cast<float *>(ws + pl.off_qrot);
+  float *qsum = reinterpret_cast<float *>(ws + pl.off_qsum);
+  float *part = reinterpret_cast<float *>(ws + pl.off_part);
+  float *ypart = reinterpret_cast<float *>(ws + pl.off_ypart);
+  KVQ_TRY(launch_query_rotation(q, dtype, pl, to_dev(*rot_k), qrot, qsum, stream));
+  if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
+  KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
+                              seq_lens, qrot, qsum, part, stream));
+  if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
+  KVQ_TRY(launch_combine(pl, part, to_dev(*rot_v), out_o, stream));
+  if (w_o) KVQ_TRY(launch_wo_projection(pl, out_o, w_o, dtype, ypart, out_y, stream));
+  return KVQ_OK;
+}
+
+size_t kvq_candidate_workspace_bytes(int64_t num_tokens, int32_t num_kv_heads, int32_t num_q_heads,
+                                     int32_t num_queries, int32_t num_candidates, int32_t num_clips,
+                                     int32_t d_model) {
+  (void)d_model;
+  if (num_tokens < 1 || num_tokens > INT32_MAX || num_kv_heads < 1 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads || num_queries < 1 || num_candidates < 1 || num_clips < 1)
+    return 0;
+  return candidate_layout(num_tokens, num_kv_heads, num_q_heads, num_queries, num_candidates, num_clips).total;
+}
+
+int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtype, int64_t num_tokens,
+                       int32_t num_kv_heads, int32_t num_q_heads, int32_t num_queries,
+                       const kvq_rotation *candidates, int32_t num_candidates, const float *clips,
+                       int32_t num_clips, const float *key_mean, const void *w_o, int32_t d_model, int32_t mode,
+                       float *out_nmse, float *out_nmse_per_query, int32_t *out_best, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
+  if (mode != KVQ_SELECT_JOINT && mode != KVQ_SELECT_PER_HEAD) return KVQ_ERR_UNSUPPORTED;
+  if (!k || !v || !q || !candidates || !clips || !w_o || !out_nmse || !out_best) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 1 || num_tokens > INT32_MAX || num_kv_heads < 1 || num_q_heads < 1 || num_queries < 1 ||
+      num_candidates < 1 || num_clips < 1 || d_model < 1)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads) return KVQ_ERR_INVALID_ARGUMENT;
+  const int H = num_kv_heads, Hq = num_q_heads, G = Hq / H, Nq = num_queries;
+  if (static_cast<int64_t>(Nq) * G > kMaxRows) return KVQ_ERR_UNSUPPORTED;
+  for (int r = 0; r < num_candidates; ++r) {
+    const int rc = check_rotation(&candidates[r]);
+    if (rc) return rc;
+  }
+  for (int i = 0; i < num_clips; ++i)
+    if (!valid_clip(clips[i])) return KVQ_ERR_INVALID_ARGUMENT;
+  const CandidateLayout L = candidate_layout(num_tokens, H, Hq, Nq, num_candidates, num_clips);
+  if (!workspace || workspace_bytes < L.total) return KVQ_ERR_WORKSPACE;
+
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  uint8_t *pages = ws + L.off_cache;
+  uint8_t *dec = ws + L.off_dec;
+  int32_t *seq_len = reinterpret_cast<int32_t *>(ws + L.off_seqlen);
+  float *o_hat = reinterpret_cast<float *>(ws + L.off_ohat);
+  float *o_ref = reinterpret_cast<float *>(ws + L.off_oref);
+  float *nmse_q = out_nmse_per_query ? out_nmse_per_query : reinterpret_cast<float *>(ws + L.off_nmse);
+  const DecodePlan &pl = L.plan;
+  float *qrot = reinterpret_cast<float *>(dec + pl.off_qrot);
+  float *qsum = reinterpret_cast<float *>(dec + pl.off_qsum);
+  float *part = reinterpret_cast<float *>(dec + pl.off_part);
+  const RotDev ident{KVQ_ROT_IDENTITY, nullptr, nullptr};
+  const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
+  const size_t stride_u = static_cast<size_t>(num_candidates) * num_clips * Nq;
+
+  // Full-precision reference readout of the raw K, V.
+  KVQ_TRY(launch_query_rotation(q, dtype, pl, ident, qrot, qsum, stream));
+  KVQ_TRY(launch_reference_split(pl, k, v, dtype, num_tokens, qrot, part, stream));
+  KVQ_TRY(launch_combine(pl, part, ident, o_ref, stream));
+  KVQ_TRY(launch_fill_i32(seq_len, static_cast<int32_t>(num_tokens), 1, stream));
+  for (int r = 0; r < num_candidates; ++r) {
+    const RotDev rot = to_dev(candidates[r]);
+    KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
+    for (int i = 0; i < num_clips; ++i) {
+      KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips[i], clips[i], pages,
+                              L.num_pages, 16, stream));
+      KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len, qrot,
+                                  qsum, part, stream));
+      KVQ_TRY(launch_combine(pl, part, rot, o_hat, stream));
+      KVQ_TRY(launch_nmse_terms(o_hat, o_ref, w_o, dtype, Nq, Hq, H, d_model, mode,
+                                nmse_q + (static_cast<size_t>(r) * num_clips + i) * Nq, stride_u, stream));
+    }
+  }
+  KVQ_TRY(launch_select(nmse_q, U, num_candidates, num_clips, Nq, out_nmse, out_best, stream));
+  return KVQ_OK;
+}
+
+const char *kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK:
+      return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARGUMENT:
+      return "KVQ_ERR_INVALID_ARGUMENT";
+    case KVQ_ERR_UNSUPPORTED:
+      return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_WORKSPACE:
+      return "KVQ_ERR_WORKSPACE";
+    case KVQ_ERR_HIP:
+      return "KVQ_ERR_HIP";
+    default:
+      return "KVQ_UNKNOWN_STATUS";
+  }
+}
+
+int kvq_version(void) { return KVQ_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// kvq_internal.h -- device helpers and launcher declarations shared by the
+// kernel translation units of libkvq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;         // head dimension == quantization group size
+constexpr int kMaxRows = 64;   // query rows sharing one (sequence, KV head)
+constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
+
+// Rotation descriptor passed by value to kernels.
+struct RotDev {
+  int32_t kind;
+  const int8_t *signs;   // [H][128]
+  const float *matrix;   // [H][128][128]
+};
+
+inline RotDev to_dev(const kvq_rotation &r) { return RotDev{r.kind, r.signs, r.matrix}; }
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void *p, size_t idx) {
+  if constexpr (DT == KVQ_F32) {
+    return static_cast<const float *>(p)[idx];
+  } else {
+    uint32_t b = static_cast<const uint16_t *>(p)[idx];
+    return __uint_as_float(b << 16);
+  }
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  _Float16 h;
+  uint16_t b = static_cast<uint16_t>(bits16);
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+
+// Entry of the Sylvester Hadamard matrix H[i][j] = (-1)^popcount(i & j).
+__device__ __forceinline__ float hadamard_sign(int i, int j) {
+  return (__popc(static_cast<unsigned>(i & j)) & 1) ? -1.0f : 1.0f;
+}
+
+// R[i][j] of one head as fp32 (used off the hot path: query rotation, inverse
+// value rotation).  inv_sqrt_d = 1/sqrt(128).
+__device__ __forceinline__ float rot_entry(const RotDev &r, int h, int i, int j, float inv_sqrt_d) {
+  if (r.kind == KVQ_ROT_IDENTITY) return i == j ? 1.0f : 0.0f;
+  if (r.kind == KVQ_ROT_SIGNED_HADAMARD)
+    return static_cast<float>(r.signs[h * D + i]) * hadamard_sign(i, j) * inv_sqrt_d;
+  return r.matrix[(static_cast<size_t>(h) * D + i) * D + j];
+}
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
+                           const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean, float clip_k,
+                           float clip_v, uint8_t *pages, int64_t num_pages, int page_size, hipStream_t stream);
+
+struct DecodePlan {
+  int num_seqs, queries_per_seq, Hq, H, G, rows_per_head;  // rows_per_head = queries_per_seq * G
+  int max_seq_len, splits, split_tokens;                   // split_tokens % kChunk == 0
+  int d_model, wo_ksplit;
+  size_t off_qrot, off_qsum, off_part, off_ypart, total;   // workspace layout (bytes)
+};
+DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, int max_seq_len, int d_model,
+                            int num_splits);
+
+// Rotated, pre-scaled queries and their sums (prologue of the decode step).
+hipError_t launch_query_rotation(const void *q, int dtype, const DecodePlan &pl, RotDev rk, float *qrot,
+                                 float *qsum, hipStream_t stream);
+// Split-K partial attention over the packed cache.
+hipError_t launch_decode_split(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
+                               const int32_t *page_table, int max_pages, const int32_t *seq_lens,
+                               const float *qrot, const float *qsum, float *part, hipStream_t stream);
+// Split-K partial attention over raw (unquantized, unrotated) K and V that
+// every query row attends in full (reference readout of the candidate search).
+hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
+                                  int64_t num_tokens, const float *qrot, float *part, hipStream_t stream);
+// Merge splits, inverse value rotation, write out_o.
+hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, hipStream_t stream);
+// out_y = concat(out_o) W_O.
+hipError_t launch_wo_projection(const DecodePlan &pl, const float *o, const void *w_o, int dtype, float *ypart,
+                                float *out_y, hipStream_t stream);
+
+// Candidate search helpers.
+hipError_t launch_fill_i32(int32_t *p, int32_t value, int n, hipStream_t stream);
+hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const void *w_o, int dtype, int Nq, int Hq,
+                             int H, int d_model, int mode, float *nmse_q_out, size_t stride_u, hipStream_t stream);
+hipError_t launch_select(const float *nmse_q, int U, int C, int n_clip, int Nq, float *out_nmse, int32_t *out_best,
+                         hipStream_t stream);
+
+}  // namespace kvq

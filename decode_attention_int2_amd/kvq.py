@@ -1,0 +1,211 @@
+"""Thin ctypes binding of libkvq (the C ABI declared in include/kvq.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of libkvq.so.  Tensors must be torch tensors on the GPU; there is no
+CPU path, and a missing library raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_INVALID_ARGUMENT, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = 0, 1, 2, 3, 4
+KVQ_F32, KVQ_BF16 = 0, 1
+KVQ_ROT_IDENTITY, KVQ_ROT_SIGNED_HADAMARD, KVQ_ROT_DENSE = 0, 1, 2
+KVQ_SELECT_JOINT, KVQ_SELECT_PER_HEAD = 0, 1
+HEAD_DIM = 128
+
+EXPORTED = ("kvq_cache_bytes", "kvq_quantize", "kvq_decode_workspace_bytes", "kvq_decode_attn",
+            "kvq_candidate_workspace_bytes", "kvq_candidate_nmse", "kvq_status_string", "kvq_version")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class _Rot(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("signs", ctypes.c_void_p), ("matrix", ctypes.c_void_p)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("num_pages", ctypes.c_int64), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32)]
+
+
+class _Events(ctypes.Structure):
+    _fields_ = [("split_start", ctypes.c_void_p), ("split_stop", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkvq.so; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkvq.so not found at {path}; build it with `python -m decode_attention_int2_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.kvq_cache_bytes.argtypes = [i64, i32, i32]
+    lib.kvq_cache_bytes.restype = sz
+    lib.kvq_quantize.argtypes = [P, P, i32, i64, P, P, P, P, f32, f32, P, P]
+    lib.kvq_quantize.restype = ctypes.c_int
+    lib.kvq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.kvq_decode_workspace_bytes.restype = sz
+    lib.kvq_decode_attn.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, i32, P, P, P, i32, P, P, P, sz, i32, P, P]
+    lib.kvq_decode_attn.restype = ctypes.c_int
+    lib.kvq_candidate_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.kvq_candidate_workspace_bytes.restype = sz
+    lib.kvq_candidate_nmse.argtypes = [P, P, P, i32, i64, i32, i32, i32, P, i32, P, i32, P, P, i32, i32, P, P, P, P,
+                                       sz, P]
+    lib.kvq_candidate_nmse.restype = ctypes.c_int
+    lib.kvq_status_string.argtypes = [ctypes.c_int]
+    lib.kvq_status_string.restype = ctypes.c_char_p
+    lib.kvq_version.argtypes = []
+    lib.kvq_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kvq_status_string(status).decode()
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU (libkvq has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    if t.dtype == torch.bfloat16:
+        return KVQ_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Rotation:
+    """kvq_rotation: kind + signs (int8 [H][128]) or matrix (fp32 [H][128][128]) on the GPU."""
+
+    def __init__(self, kind: int, signs: Optional[torch.Tensor] = None, matrix: Optional[torch.Tensor] = None):
+        self.kind = int(kind)
+        self.signs = signs
+        self.matrix = matrix
+
+    def _c(self) -> _Rot:
+        return _Rot(self.kind, _dev_ptr(self.signs, "signs"), _dev_ptr(self.matrix, "matrix"))
+
+
+class Cache:
+    """kvq_cache: packed pages uint8 [num_pages][H][72 * page_size] on the GPU."""
+
+    def __init__(self, num_pages: int, page_size: int, num_kv_heads: int, device="cuda",
+                 pages: Optional[torch.Tensor] = None):
+        self.num_pages, self.page_size, self.num_kv_heads = int(num_pages), int(page_size), int(num_kv_heads)
+        if pages is None:
+            pages = torch.zeros((self.num_pages, self.num_kv_heads, 72 * self.page_size), dtype=torch.uint8,
+                                device=device)
+        self.pages = pages
+
+    def _c(self) -> _Cache:
+        return _Cache(_dev_ptr(self.pages, "pages"), self.num_pages, self.page_size, self.num_kv_heads)
+
+    @property
+    def nbytes(self) -> int:
+        return int(load_library().kvq_cache_bytes(self.num_pages, self.page_size, self.num_kv_heads))
+
+
+def _check(rc: int, what: str):
+    if rc != KVQ_OK:
+        raise KvqError(rc, what)
+
+
+def kvq_quantize(k: torch.Tensor, v: torch.Tensor, cache: Cache, rot_k: Rotation, rot_v: Rotation,
+                 key_mean: Optional[torch.Tensor] = None, clip_k: float = 1.0, clip_v: float = 1.0,
+                 slot_mapping: Optional[torch.Tensor] = None, stream=None) -> None:
+    lib = load_library()
+    c, rk, rv = cache._c(), rot_k._c(), rot_v._c()
+    _check(lib.kvq_quantize(_dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k), k.shape[0],
+                            _dev_ptr(slot_mapping, "slot_mapping"), ctypes.byref(rk), ctypes.byref(rv),
+                            _dev_ptr(key_mean, "key_mean"), clip_k, clip_v, ctypes.byref(c), _stream(stream)),
+           "kvq_quantize")
+
+
+def kvq_decode_workspace_bytes(num_seqs: int, queries_per_seq: int, num_q_heads: int, num_kv_heads: int,
+                               max_seq_len: int, d_model: int = 0, num_splits: int = 0) -> int:
+    return int(load_library().kvq_decode_workspace_bytes(num_seqs, queries_per_seq, num_q_heads, num_kv_heads,
+                                                         max_seq_len, d_model, num_splits))
+
+
+def kvq_decode_attn(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache: Cache,
+                    page_table: Optional[torch.Tensor], max_pages_per_seq: int, seq_lens: torch.Tensor,
+                    max_seq_len: int, rot_k: Rotation, rot_v: Rotation, out_o: torch.Tensor,
+                    w_o: Optional[torch.Tensor] = None, out_y: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None,
+                    split_events: Optional[tuple] = None) -> None:
+    """split_events: optional (start, stop) torch.cuda.Event pair recorded around the split-K kernel."""
+    lib = load_library()
+    Hq = q.shape[1]
+    d_model = int(w_o.shape[1]) if w_o is not None else 0
+    c, rk, rv = cache._c(), rot_k._c(), rot_v._c()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ev = None
+    if split_events is not None:
+        ev = ctypes.byref(_Events(ctypes.c_void_p(split_events[0].cuda_event),
+                                  ctypes.c_void_p(split_events[1].cuda_event)))
+    _check(lib.kvq_decode_attn(_dev_ptr(q, "q"), _dtype_code(q), num_seqs, queries_per_seq, Hq, ctypes.byref(c),
+                               _dev_ptr(page_table, "page_table"), max_pages_per_seq, _dev_ptr(seq_lens, "seq_lens"),
+                               max_seq_len, ctypes.byref(rk), ctypes.byref(rv), _dev_ptr(w_o, "w_o"), d_model,
+                               _dev_ptr(out_o, "out_o"), _dev_ptr(out_y, "out_y"), _dev_ptr(workspace, "workspace"),
+                               ws_bytes, num_splits, ev, _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_candidate_workspace_bytes(num_tokens: int, num_kv_heads: int, num_q_heads: int, num_queries: int,
+                                  num_candidates: int, num_clips: int, d_model: int) -> int:
+    return int(load_library().kvq_candidate_workspace_bytes(num_tokens, num_kv_heads, num_q_heads, num_queries,
+                                                            num_candidates, num_clips, d_model))
+
+
+def kvq_candidate_nmse(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, candidates: Sequence[Rotation],
+                       clips: Sequence[float], w_o: torch.Tensor, mode: int, out_nmse: torch.Tensor,
+                       out_best: torch.Tensor, out_nmse_per_query: Optional[torch.Tensor] = None,
+                       key_mean: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    lib = load_library()
+    T, H = k.shape[0], k.shape[1]
+    Nq, Hq = q.shape[0], q.shape[1]
+    rots = (_Rot * len(candidates))(*[c._c() for c in candidates])
+    cl = (ctypes.c_float * len(clips))(*[float(x) for x in clips])
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.kvq_candidate_nmse(_dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(q, "q"), _dtype_code(k), T, H, Hq, Nq,
+                                  rots, len(candidates), cl, len(clips), _dev_ptr(key_mean, "key_mean"),
+                                  _dev_ptr(w_o, "w_o"), int(w_o.shape[1]), mode, _dev_ptr(out_nmse, "out_nmse"),
+                                  _dev_ptr(out_nmse_per_query, "out_nmse_per_query"), _dev_ptr(out_best, "out_best"),
+                                  _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
+           "kvq_candidate_nmse")
+
+
+def kvq_version() -> int:
+    return int(load_library().kvq_version())

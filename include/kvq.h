@@ -1,0 +1,227 @@
+/*
+ * kvq.h -- C ABI of libkvq: rotated INT2 KV-cache quantization and decode
+ * attention over the packed cache, for AMD MI355X (gfx950).
+ *
+ * Method sources (cited by title and section):
+ *   [OptR]  "Output-Aware Rotation for INT2 KV-Cache Quantization"
+ *   [Eval]  "Output-aware INT2 KV-cache rotation evaluation"
+ *
+ * General rules for every entry point
+ *   - Pointers are device pointers unless an argument says "host".  All
+ *     arrays are dense, row-major, with the shapes given below.
+ *   - The caller owns every buffer.  The library allocates and frees no
+ *     memory and keeps no mutable global state between calls.
+ *   - Work is enqueued on `stream` and is asynchronous; results are ready
+ *     after the caller synchronizes that stream.
+ *   - All arguments that can be checked on the host are checked before the
+ *     first launch; on any error nothing is launched and nothing is written.
+ *   - There is no implicit fallback: a request outside what is implemented
+ *     returns KVQ_ERR_UNSUPPORTED, never a slower path ([Eval], contract).
+ *   - Device-resident indices (slot_mapping, page_table, seq_lens) cannot be
+ *     checked on the host.  Kernels never access memory out of bounds: a
+ *     slot outside the cache is skipped by kvq_quantize; a page index outside
+ *     the cache, or seq_len < 0 or > max_seq_len, makes kvq_decode_attn write
+ *     NaN to every output of the affected sequence.
+ *   - Head dimension and quantization group size are both 128 ([OptR],
+ *     Appendix Table A; [Eval]: group size 128, per-token-group K/V).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_HEAD_DIM 128
+#define KVQ_GROUP_SIZE 128
+#define KVQ_VERSION 1
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad shape, bad value          */
+  KVQ_ERR_UNSUPPORTED = 2,      /* well-formed but not implemented             */
+  KVQ_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required  */
+  KVQ_ERR_HIP = 4               /* a HIP launch reported an error              */
+} kvq_status;
+
+/* Element type of K, V, q and W_O (all four share it in one call). */
+enum { KVQ_F32 = 0, KVQ_BF16 = 1 };
+
+/* Rotation kinds ([OptR] §3.1 Eq. (4): z' = z R, row-vector convention).
+ *   IDENTITY         R = I (no rotation; also the "pre-rotated input" mode).
+ *   SIGNED_HADAMARD  R = diag(s) H / sqrt(128), H the Sylvester Hadamard
+ *                    matrix, s in {-1,+1}^128 ([Eval]: signed-Hadamard
+ *                    candidates).
+ *   DENSE            any orthogonal R given as fp32 ([OptR] §4.2 Eq. (11):
+ *                    learned rotations R0 exp(A - A^T)). */
+enum { KVQ_ROT_IDENTITY = 0, KVQ_ROT_SIGNED_HADAMARD = 1, KVQ_ROT_DENSE = 2 };
+
+/* Candidate-search objective units. */
+enum { KVQ_SELECT_JOINT = 0, KVQ_SELECT_PER_HEAD = 1 };
+
+/* Per-KV-head rotations of one side (K or V).
+ *   signs:  int8 [H][128], each +1 or -1 (kind SIGNED_HADAMARD), else unused.
+ *   matrix: fp32 [H][128][128], row-major, z'_j = sum_i z_i R[i][j]
+ *           (kind DENSE), else unused. */
+typedef struct {
+  int32_t kind;
+  const int8_t *signs;
+  const float *matrix;
+} kvq_rotation;
+
+/* Packed paged INT2 cache ([OptR] §1 and §6: rotation keeps the cache shape
+ * and the paged layout; [Eval]: 2-bit codes, group 128).
+ *
+ *   pages: uint8 [num_pages][num_kv_heads][72 * page_size]
+ *
+ * One block per (page, KV head) holds page_size = P tokens (P % 16 == 0):
+ *   bytes [0, 32P)     K codes, token-major: token p at 32p; byte m holds
+ *                      dims 4m..4m+3, dim 4m+e in bits 2e..2e+1.
+ *   bytes [32P, 64P)   V codes, four tokens interleaved: byte m of token p
+ *                      at 32P + 128*(p/4) + 4m + (p%4), same bit order.
+ *   bytes [64P, 68P)   K metadata: token p at 64P + 4p: fp16 scale (bytes
+ *                      0-1) then fp16 zero (bytes 2-3), little-endian.
+ *   bytes [68P, 72P)   V metadata, same format.
+ * A code q of a group with scale s and zero z dequantizes to q*s + z.
+ * Slot index = page * P + position in page.  Codes of one (token, head) pair
+ * take 64 bytes (K + V) and metadata 8 bytes: 72 bytes in all. */
+typedef struct {
+  uint8_t *pages;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+} kvq_cache;
+
+/* Bytes of a cache buffer (num_pages * num_kv_heads * 72 * page_size). */
+size_t kvq_cache_bytes(int64_t num_pages, int32_t page_size, int32_t num_kv_heads);
+
+/* ---------------------------------------------------------------------------
+ * kvq_quantize -- cache write ([OptR] §6 Efficiency Analysis; Appendix
+ * Eq. (20)-(21); §4.1 key reparameterization; §3.1 Q2).
+ *
+ * For every token t < num_tokens and KV head h:
+ *   k' = (k[t][h] - key_mean[h]) R_K[h]      (key_mean NULL: no centering)
+ *   v' = v[t][h] R_V[h]
+ * each 128-group is quantized with clip ratio clip_k (keys) or clip_v
+ * (values): lo = c*min, hi = c*max, s = fp16((hi - lo)/3), z = fp16(lo),
+ * code = clamp(round_half_even((x - z) * (1/s)), 0, 3), all codes 0 when
+ * s == 0; codes and metadata are written to slot slot_mapping[t].
+ *
+ *   k, v          [num_tokens][H][128], dtype KVQ_F32 or KVQ_BF16, H =
+ *                 cache->num_kv_heads.
+ *   slot_mapping  int64 [num_tokens], or NULL for slot = t.  Negative slots
+ *                 are skipped (token not written).
+ *   rot_k, rot_v  host pointers to rotation descriptors (device arrays).
+ *   key_mean      fp32 [H][128] or NULL.
+ *   clip_k/clip_v in (0, 1].
+ *   cache         host pointer to the descriptor; cache->pages is written.
+ * Inputs must be finite and give |lo| and (hi-lo)/3 within fp16 range;
+ * otherwise the metadata holds fp16 infinities (defined as unsupported
+ * input).  With IDENTITY rotations, no key_mean and KVQ_F32 inputs, codes and
+ * metadata equal the fp32 definition above bit for bit.
+ * Errors: INVALID_ARGUMENT (nulls, num_tokens < 0, clip outside (0,1],
+ * page_size % 16 != 0, H < 1), UNSUPPORTED (unknown dtype or rotation kind),
+ * HIP.
+ * ------------------------------------------------------------------------- */
+int kvq_quantize(const void *k, const void *v, int32_t dtype, int64_t num_tokens, const int64_t *slot_mapping,
+                 const kvq_rotation *rot_k, const kvq_rotation *rot_v, const float *key_mean, float clip_k,
+                 float clip_v, const kvq_cache *cache, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * kvq_decode_attn -- decode attention straight from the packed cache
+ * ([OptR] Appendix Eq. (21)-(22), (26): rotated query against stored rotated
+ * keys; §3 Eq. (1)-(3): softmax over the cached tokens with scale
+ * 1/sqrt(128), probability-weighted values, per-head W_O blocks; Appendix
+ * Eq. (27)-(28): explicit inverse value rotation).
+ *
+ * Query row r (r < num_seqs * queries_per_seq) belongs to sequence
+ * b = r / queries_per_seq.  For query head j (KV head h = j / (Hq / H)):
+ *   q'     = q[r][j] R_K[h]
+ *   p_t    = softmax_t(q' . k_hat_t / sqrt(128)),  t < seq_lens[b]
+ *   o'     = sum_t p_t v_hat_t;   out_o[r][j] = o' R_V[h]^T
+ *   out_y[r] = sum_j out_o[r][j] W_O[j*128 : j*128+128, :]
+ * Token t of sequence b sits in page page_table[b][t / P] at position t % P.
+ *
+ *   q            [num_seqs * queries_per_seq][Hq][128], dtype.
+ *   page_table   int32 [num_seqs][max_pages_per_seq], or NULL for page
+ *                b * max_pages_per_seq + t / P (contiguous caches).
+ *   seq_lens     int32 [num_seqs], each in [0, max_seq_len]; an empty
+ *                sequence gives out_o = 0.
+ *   max_seq_len  host bound on seq_lens, <= max_pages_per_seq * P.
+ *   w_o          [Hq*128][d_model], dtype, or NULL (then out_y is not
+ *                written and d_model is ignored).
+ *   out_o        fp32 [rows][Hq][128];  out_y fp32 [rows][d_model] or NULL.
+ *   workspace    device scratch of at least kvq_decode_workspace_bytes(...)
+ *                bytes with the same shape arguments.
+ *   num_splits   split-K parts per sequence (0 = automatic).
+ *   events       host pointer to a kvq_decode_events, or NULL.
+ * Limits: Hq % H == 0 and queries_per_seq * Hq / H <= 64, else UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+/* Optional timing hook of kvq_decode_attn: when non-NULL, split_start and
+ * split_stop are recorded on `stream` immediately before and after the
+ * split-K attention kernel (the step that reads the packed cache), so a caller
+ * can time that kernel alone with hipEventElapsedTime.  Work is unchanged. */
+typedef struct {
+  hipEvent_t split_start;
+  hipEvent_t split_stop;
+} kvq_decode_events;
+
+size_t kvq_decode_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t max_seq_len, int32_t d_model, int32_t num_splits);
+
+int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                    const kvq_cache *cache, const int32_t *page_table, int32_t max_pages_per_seq,
+                    const int32_t *seq_lens, int32_t max_seq_len, const kvq_rotation *rot_k,
+                    const kvq_rotation *rot_v, const void *w_o, int32_t d_model, float *out_o, float *out_y,
+                    void *workspace, size_t workspace_bytes, int32_t num_splits, const kvq_decode_events *events,
+                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * kvq_candidate_nmse -- batched post-W_O NMSE over a grid of candidate
+ * rotations and clip ratios, and selection of the best one ([Eval], observed
+ * envelope: identity + signed-Hadamard candidates x clip grid, chosen by
+ * post-W_O output NMSE; [OptR] §3.2 Eq. (7), (10): the post-W_O error).
+ *
+ * For candidate r (used for both K and V) and clip clips[i] (used for both):
+ * quantize K (centered by key_mean when given) and V as kvq_quantize does,
+ * decode every query over all num_tokens tokens, and compare with the
+ * full-precision output of the raw, unrotated K and V:
+ *   JOINT     (U = 1):  NMSE_q = ||y_hat_q - y_q||^2 / ||y_q||^2 over the
+ *                       whole layer output y_q = sum_j o_qj W_O[j-block].
+ *   PER_HEAD  (U = H):  NMSE_q,h = sum_{j in G_h} ||y_hat_qj - y_qj||^2 /
+ *                       sum_{j in G_h} ||y_qj||^2, y_qj = o_qj W_O[j-block].
+ *   out_nmse[u][r][i]  = mean over queries of NMSE (fp32, device)
+ *   out_nmse_per_query[u][r][i][q] (device, may be NULL)
+ *   out_best[u] = r * num_clips + i of the first minimum in (r, i) order.
+ *
+ *   k, v          [num_tokens][H][128], dtype;  q [num_queries][Hq][128].
+ *   candidates    host array [num_candidates] of rotation descriptors.
+ *   clips         host array [num_clips], each in (0, 1].
+ *   w_o           [Hq*128][d_model], dtype.
+ *   workspace     at least kvq_candidate_workspace_bytes(...) bytes.
+ * Limits: num_queries * Hq / H <= 64, else UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+size_t kvq_candidate_workspace_bytes(int64_t num_tokens, int32_t num_kv_heads, int32_t num_q_heads,
+                                     int32_t num_queries, int32_t num_candidates, int32_t num_clips,
+                                     int32_t d_model);
+
+int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtype, int64_t num_tokens,
+                       int32_t num_kv_heads, int32_t num_q_heads, int32_t num_queries,
+                       const kvq_rotation *candidates, int32_t num_candidates, const float *clips,
+                       int32_t num_clips, const float *key_mean, const void *w_o, int32_t d_model, int32_t mode,
+                       float *out_nmse, float *out_nmse_per_query, int32_t *out_best, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a kvq_status value (static string). */
+const char *kvq_status_string(int status);
+/* KVQ_VERSION of the built library. */
+int kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

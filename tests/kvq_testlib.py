@@ -1,0 +1,80 @@
+"""Helpers shared by the GPU tests: run the HIP path through the C ABI and the
+oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from decode_attention_int2_amd import kvq
+
+
+def f32np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def gpu_rot(spec) -> kvq.Rotation:
+    return kvq.Rotation(spec.kind, signs=spec.signs, matrix=spec.matrix)
+
+
+def oracle_rot(spec, heads=None) -> oracle.Rotation:
+    s = None if spec.signs is None else spec.signs.cpu().numpy()
+    m = None if spec.matrix is None else spec.matrix.cpu().numpy()
+    if heads is not None:
+        s = None if s is None else s[heads]
+        m = None if m is None else m[heads]
+    return oracle.Rotation(spec.kind, signs=s, matrix=m)
+
+
+def gpu_quantize(w, dev, rot_k=None, rot_v=None, key_mean="default", clip_k=None, clip_v=None, slot_mapping="default"):
+    cache = kvq.Cache(w.num_pages, w.page_size, w.H, device=dev)
+    kvq.kvq_quantize(w.k, w.v, cache, gpu_rot(rot_k or w.rot_k), gpu_rot(rot_v or w.rot_v),
+                     key_mean=w.key_mean if isinstance(key_mean, str) else key_mean,
+                     clip_k=w.clip_k if clip_k is None else clip_k, clip_v=w.clip_v if clip_v is None else clip_v,
+                     slot_mapping=w.slot_mapping if isinstance(slot_mapping, str) else slot_mapping)
+    return cache
+
+
+def gpu_decode(w, cache, dev, seq_lens=None, page_table="default", with_wo=True, num_splits=0, max_seq_len=None):
+    seq_lens = w.seq_lens if seq_lens is None else seq_lens
+    pt = w.page_table if isinstance(page_table, str) else page_table
+    max_pages = w.page_table.shape[1]
+    msl = w.tokens if max_seq_len is None else max_seq_len
+    rows = w.num_seqs * w.queries_per_seq
+    out_o = torch.full((rows, w.Hq, 128), 12345.0, dtype=torch.float32, device=dev)
+    out_y = torch.full((rows, w.d_model), 12345.0, dtype=torch.float32, device=dev) if with_wo else None
+    ws = torch.empty(max(1, kvq.kvq_decode_workspace_bytes(w.num_seqs, w.queries_per_seq, w.Hq, w.H, msl,
+                                                           w.d_model if with_wo else 0, num_splits)),
+                     dtype=torch.uint8, device=dev)
+    kvq.kvq_decode_attn(w.q, w.num_seqs, w.queries_per_seq, cache, pt, max_pages, seq_lens, msl, gpu_rot(w.rot_k),
+                        gpu_rot(w.rot_v), out_o, w_o=w.w_o if with_wo else None, out_y=out_y, workspace=ws,
+                        num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out_o, out_y
+
+
+def oracle_cache_and_decode(w, seq_lens=None, with_wo=True):
+    """Oracle path on the same inputs: its own cache write, then decode."""
+    seq_lens = w.seq_lens if seq_lens is None else seq_lens
+    ocache = oracle.Cache(w.num_pages, w.page_size, w.H)
+    ork, orv = oracle_rot(w.rot_k), oracle_rot(w.rot_v)
+    km = None if w.key_mean is None else f32np(w.key_mean)
+    oracle.quantize(f32np(w.k), f32np(w.v), ocache, ork, orv, key_mean=km, clip_k=w.clip_k, clip_v=w.clip_v,
+                    slot_mapping=w.slot_mapping.cpu().numpy())
+    res = oracle.decode(f32np(w.q), ocache, seq_lens.cpu().numpy(), ork, orv, num_seqs=w.num_seqs,
+                        queries_per_seq=w.queries_per_seq, page_table=w.page_table.cpu().numpy(),
+                        max_pages=w.page_table.shape[1], w_o=f32np(w.w_o) if with_wo else None,
+                        d_model=w.d_model if with_wo else 0)
+    return ocache, res
+
+
+def tolerance(w) -> float:
+    """Float tolerance on rel-L2: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs."""
+    return 1e-4 if w.dtype == "f32" else 2e-2

@@ -1,0 +1,117 @@
+"""The C-ABI library loads on a CPU-only host, exports every symbol that
+include/kvq.h declares, and rejects bad arguments on the host before any
+launch (no GPU needed: validation never touches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char \*)\s*(kvq_\w+)\s*\(", hdr, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from decode_attention_int2_amd import kvq
+    if not os.path.exists(kvq.LIB_PATH):
+        from decode_attention_int2_amd import build
+        build.build()
+    return kvq.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    from decode_attention_int2_amd import kvq
+    assert set(kvq.EXPORTED) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvq_version() == 1
+    assert lib.kvq_status_string(0) == b"KVQ_OK"
+    assert lib.kvq_status_string(3) == b"KVQ_ERR_WORKSPACE"
+    assert lib.kvq_status_string(99) == b"KVQ_UNKNOWN_STATUS"
+
+
+def test_cache_bytes(lib):
+    # 72 bytes per (token, head): 1,152-byte blocks for 16-token pages
+    assert lib.kvq_cache_bytes(32768, 16, 8) == 32768 * 8 * 1152
+    assert lib.kvq_cache_bytes(-1, 16, 8) == 0
+
+
+def _rot(kind=0):
+    from decode_attention_int2_amd.kvq import _Rot
+    return _Rot(kind, None, None)
+
+
+def _cache(pages=1, P=16, H=2):
+    from decode_attention_int2_amd.kvq import _Cache
+    return _Cache(ctypes.c_void_p(0x1000), pages, P, H)
+
+
+def test_quantize_validation(lib):
+    f = ctypes.c_float
+    ok_rot, c = _rot(), _cache()
+    fake = ctypes.c_void_p(0x2000)
+    # unknown dtype / rotation kind -> UNSUPPORTED
+    assert lib.kvq_quantize(fake, fake, 7, 4, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c), None) == 2
+    bad_kind = _rot(5)
+    assert lib.kvq_quantize(fake, fake, 0, 4, None, ctypes.byref(bad_kind), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c), None) == 2
+    # signed Hadamard without signs, clip out of range, page size not a multiple of 16 -> INVALID
+    sh = _rot(1)
+    assert lib.kvq_quantize(fake, fake, 0, 4, None, ctypes.byref(sh), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c), None) == 1
+    for clip in (0.0, 1.01, float("nan")):
+        assert lib.kvq_quantize(fake, fake, 0, 4, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None,
+                                f(clip), f(1), ctypes.byref(c), None) == 1
+    c8 = _cache(P=8)
+    assert lib.kvq_quantize(fake, fake, 0, 4, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c8), None) == 1
+    # nothing to do: zero tokens succeeds without touching the device
+    assert lib.kvq_quantize(None, None, 0, 0, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c), None) == 0
+
+
+def test_decode_validation(lib):
+    fake = ctypes.c_void_p(0x2000)
+    r, c = _rot(), _cache(pages=4, H=2)
+    call = lambda **kw: lib.kvq_decode_attn(
+        kw.get("q", fake), kw.get("dtype", 1), kw.get("num_seqs", 1), kw.get("qps", 1), kw.get("hq", 4),
+        ctypes.byref(kw.get("cache", c)), kw.get("pt", fake), kw.get("max_pages", 4), fake, kw.get("msl", 64),
+        ctypes.byref(r), ctypes.byref(r), kw.get("wo", None), kw.get("dm", 0), fake, kw.get("y", None),
+        kw.get("ws", fake), kw.get("wsb", 1 << 30), 0, None, None)
+    assert call(dtype=3) == 2
+    assert call(hq=3) == 1                      # Hq not a multiple of H
+    assert call(qps=40, hq=4) == 2              # 80 rows per KV head > 64
+    assert call(msl=65) == 1                    # max_seq_len > max_pages * P
+    assert call(pt=None, num_seqs=2) == 1       # contiguous table needs num_seqs * max_pages <= num_pages
+    assert call(wo=fake, dm=16, y=None) == 1    # W_O without out_y
+    assert call(ws=None) == 3 and call(wsb=8) == 3
+    assert call(num_seqs=0) == 0
+
+
+def test_candidate_validation(lib):
+    fake = ctypes.c_void_p(0x2000)
+    from decode_attention_int2_amd.kvq import _Rot
+    cands = (_Rot * 2)(_Rot(0, None, None), _Rot(1, None, None))
+    clips = (ctypes.c_float * 2)(1.0, 0.9)
+    call = lambda **kw: lib.kvq_candidate_nmse(
+        fake, fake, fake, kw.get("dtype", 1), kw.get("T", 100), 2, 2, kw.get("nq", 4), kw.get("cands", cands),
+        kw.get("nc", 2), kw.get("clips", clips), 2, None, fake, 16, kw.get("mode", 0), fake, None, fake,
+        fake, 1 << 30, None)
+    assert call(mode=5) == 2
+    assert call(nq=65) == 2
+    assert call() == 1                           # candidate 1 is signed Hadamard without signs
+    one = (_Rot * 1)(_Rot(0, None, None))
+    bad_clips = (ctypes.c_float * 2)(1.0, 0.0)
+    assert call(cands=one, nc=1, clips=bad_clips) == 1
+    assert lib.kvq_candidate_workspace_bytes(100, 2, 2, 4, 1, 2, 16) > 0

@@ -1,0 +1,227 @@
+"""HIP path vs CPU oracle, element by element, on seeded inputs through the C ABI.
+
+Bars: codes and metadata bit-exact (byte work); floats within rel-L2 1e-4 for
+fp32 inputs and 2e-2 for bf16 inputs; candidate NMSE within 1e-3 relative and
+the selected candidate identical unless the oracle's best two are a near-tie.
+Sizes span several 256-token chunks, several splits and ragged tails.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from kvq_testlib import (f32np, gpu_decode, gpu_quantize, gpu_rot, oracle_cache_and_decode, oracle_rot, rel_l2,
+                         tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_attention_int2_amd import kvq
+    kvq.load_library()
+    return torch.device("cuda:0")
+
+
+def _special_groups(n_tok, H, rng):
+    """Edge groups: constant (s == 0), exact rounding ties, one huge outlier, tiny range."""
+    x = rng.standard_normal((n_tok, H, 128)).astype(np.float32)
+    x[0, 0, :] = 1.25                                  # degenerate: all codes 0, z = 1.25
+    tie = np.zeros(128, np.float32)
+    tie[:4] = [0.0, 3.0, 0.5, 2.5]                     # c = 1: s = 1, z = 0; ties 0.5 -> 0, 2.5 -> 2
+    tie[4:] = 1.5                                      # tie 1.5 -> 2
+    x[1, 0, :] = tie
+    x[2, 0, 7] = 4000.0                                # outlier dominates the range
+    x[3, 0, :] *= 1e-4                                 # tiny range, fp16 subnormal scale
+    return x
+
+
+@pytest.mark.parametrize("clip_k,clip_v", [(1.0, 1.0), (0.96, 0.92), (0.8, 0.85)])
+def test_quantize_prerotated_bitexact(dev, clip_k, clip_v):
+    """Identity rotation on fp32 inputs: codes and metadata equal the oracle bit for bit."""
+    rng = np.random.default_rng(100)
+    T, H, P = 777, 4, 16
+    k = _special_groups(T, H, rng)
+    v = _special_groups(T, H, rng) * 3
+    num_pages = (T + P - 1) // P + 5
+    slots = rng.permutation(num_pages * P)[:T].astype(np.int64)
+    slots[5] = -1                                     # negative slot: token skipped
+    ident = oracle.Rotation(oracle.ROT_IDENTITY)
+    ocache = oracle.Cache(num_pages, P, H)
+    oracle.quantize(k, v, ocache, ident, ident, clip_k=clip_k, clip_v=clip_v, slot_mapping=slots)
+    from decode_attention_int2_amd import kvq
+    cache = kvq.Cache(num_pages, P, H, device=dev)
+    gid = kvq.Rotation(kvq.KVQ_ROT_IDENTITY)
+    kvq.kvq_quantize(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), cache, gid, gid, clip_k=clip_k,
+                     clip_v=clip_v, slot_mapping=torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    got = cache.pages.cpu().numpy()
+    assert np.array_equal(got, ocache.pages), f"{int((got != ocache.pages).sum())} bytes differ"
+
+
+@pytest.mark.parametrize("preset,rot", [("envelope", "sh"), ("gqa32k", "dense"), ("paged16x32k", "sh"),
+                                        ("long131k", "dense")])
+def test_quantize_end_to_end(dev, preset, rot):
+    """Rotation (+ key centering where the preset has it) then quantization:
+    cache bytes vs the oracle's own cache write of the same inputs."""
+    w = synthetic.make(preset, dev, tokens=600, num_seqs=2, H=3, Hq=6, d_model=64)
+    if preset == "envelope":
+        w.rot_k = w.rot_v = w.candidates[3]
+    cache = gpu_quantize(w, dev)
+    torch.cuda.synchronize()
+    ocache = oracle.Cache(w.num_pages, w.page_size, w.H)
+    km = None if w.key_mean is None else f32np(w.key_mean)
+    oracle.quantize(f32np(w.k), f32np(w.v), ocache, oracle_rot(w.rot_k), oracle_rot(w.rot_v), key_mean=km,
+                    clip_k=w.clip_k, clip_v=w.clip_v, slot_mapping=w.slot_mapping.cpu().numpy())
+    got = cache.pages.cpu().numpy()
+    frac = float(np.mean(got != ocache.pages))
+    print(f"{preset}: byte mismatch fraction {frac:.3e}")
+    assert frac <= 1e-4
+
+
+@pytest.mark.parametrize("case", ["envelope_f32_sh", "gqa_bf16_dense_centered", "paged_bf16_sh_ragged",
+                                  "t3_bf16_dense_multiquery"])
+def test_decode_parity(dev, case):
+    if case == "envelope_f32_sh":
+        w = synthetic.make("envelope", dev, tokens=1000, queries=3)
+        w.rot_k = w.rot_v = w.candidates[5]
+        seq_lens = None
+    elif case == "gqa_bf16_dense_centered":
+        w = synthetic.make("gqa32k", dev, tokens=1500, H=2, Hq=8, d_model=256)
+        seq_lens = None
+    elif case == "paged_bf16_sh_ragged":
+        w = synthetic.make("paged16x32k", dev, tokens=900, num_seqs=5, H=2, Hq=8, d_model=128)
+        seq_lens = synthetic.ragged_seq_lens(5, 900, seed=3).to(dev)
+    else:
+        w = synthetic.make("long131k", dev, tokens=1100, num_seqs=2, H=2, Hq=4, d_model=192, queries=3)
+        seq_lens = synthetic.ragged_seq_lens(2, 1100, seed=4).to(dev)
+    cache = gpu_quantize(w, dev)
+    out_o, out_y = gpu_decode(w, cache, dev, seq_lens=seq_lens)
+    _, (ref_o, ref_y) = oracle_cache_and_decode(w, seq_lens=seq_lens)
+    tol = tolerance(w)
+    eo, ey = rel_l2(f32np(out_o), ref_o), rel_l2(f32np(out_y), ref_y)
+    print(f"{case}: rel-L2 out_o {eo:.2e} out_y {ey:.2e} (tol {tol})")
+    assert eo <= tol and ey <= tol
+    # per (row, head) too, so no small output hides behind a large one
+    per = [rel_l2(f32np(out_o)[r, j], ref_o[r, j]) for r in range(ref_o.shape[0]) for j in range(ref_o.shape[1])]
+    assert max(per) <= tol
+
+
+def test_decode_split_count_invariance(dev):
+    """The split-K log-sum-exp merge equals a single pass (one split)."""
+    w = synthetic.make("paged16x32k", dev, tokens=3000, num_seqs=2, H=2, Hq=8, d_model=64)
+    cache = gpu_quantize(w, dev)
+    base, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=1)
+    for ns in (0, 3, 12):
+        o, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=ns)
+        assert rel_l2(f32np(o), f32np(base)) < 2e-6
+
+
+def test_decode_edge_cases(dev):
+    """Empty and one-token sequences; an out-of-range page index or seq_len
+    gives NaN for that sequence only (host-forced condition)."""
+    w = synthetic.make("paged16x32k", dev, tokens=200, num_seqs=4, H=2, Hq=4, d_model=32)
+    cache = gpu_quantize(w, dev)
+    lens = torch.tensor([0, 1, 200, 57], dtype=torch.int32, device=dev)
+    out_o, out_y = gpu_decode(w, cache, dev, seq_lens=lens)
+    _, (ref_o, ref_y) = oracle_cache_and_decode(w, seq_lens=lens)
+    o = f32np(out_o)
+    assert np.all(o[0] == 0.0)
+    assert rel_l2(o[1:], ref_o[1:]) <= 2e-2
+    pt = w.page_table.clone()
+    pt[2, 3] = w.num_pages + 7                         # invalid page inside sequence 2
+    bad_lens = lens.clone()
+    bad_lens[3] = 10_000                               # beyond max_seq_len
+    out_o, out_y = gpu_decode(w, cache, dev, seq_lens=bad_lens, page_table=pt)
+    o, y = f32np(out_o), f32np(out_y)
+    assert np.all(np.isnan(o[2])) and np.all(np.isnan(o[3])) and np.all(np.isnan(y[2]))
+    assert np.all(o[0] == 0.0) and rel_l2(o[1], ref_o[1]) <= 2e-2
+
+
+def test_api_rejects_bad_arguments(dev):
+    from decode_attention_int2_amd import kvq
+    w = synthetic.make("paged16x32k", dev, tokens=64, num_seqs=1, H=2, Hq=4, d_model=32)
+    cache = kvq.Cache(w.num_pages, w.page_size, w.H, device=dev)
+    rot = gpu_rot(w.rot_k)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_quantize(w.k, w.v, cache, rot, rot, clip_k=1.5)
+    assert e.value.status == kvq.KVQ_ERR_INVALID_ARGUMENT
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_quantize(w.k, w.v, cache, kvq.Rotation(9), rot)
+    assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
+    out = torch.empty((1, 4, 128), device=dev)
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attn(w.q, 1, 1, cache, w.page_table, w.page_table.shape[1], w.seq_lens, 64, rot, rot, out,
+                            workspace=small)
+    assert e.value.status == kvq.KVQ_ERR_WORKSPACE
+    assert torch.all(out == out)  # untouched memory is still readable
+
+
+def _candidate_case(dev, preset, mode, T, H, Hq, Nq, n_cand, clips, dm, center=False):
+    from decode_attention_int2_amd import kvq
+    w = synthetic.make(preset, dev, tokens=T, H=H, Hq=Hq, queries=Nq, d_model=dm, num_candidates=n_cand)
+    if center:  # calibration mean of the cached keys (input preparation, as the generator does)
+        w.key_mean = w.k.to(torch.float64).mean(dim=0).to(torch.float32).contiguous()
+    U = 1 if mode == kvq.KVQ_SELECT_JOINT else H
+    C, n = len(w.candidates), len(clips)
+    out = torch.empty((U, C, n), dtype=torch.float32, device=dev)
+    outq = torch.empty((U, C, n, Nq), dtype=torch.float32, device=dev)
+    best = torch.empty((U,), dtype=torch.int32, device=dev)
+    ws = torch.empty(kvq.kvq_candidate_workspace_bytes(T, H, Hq, Nq, C, n, dm), dtype=torch.uint8, device=dev)
+    kvq.kvq_candidate_nmse(w.k, w.v, w.q, [gpu_rot(c) for c in w.candidates], clips, w.w_o, mode, out, best,
+                           out_nmse_per_query=outq, key_mean=w.key_mean, workspace=ws)
+    torch.cuda.synchronize()
+    km = None if w.key_mean is None else f32np(w.key_mean)
+    ref, refq, rbest = oracle.candidate_nmse(f32np(w.k), f32np(w.v), f32np(w.q), [oracle_rot(c) for c in w.candidates],
+                                             clips, f32np(w.w_o), mode, key_mean=km)
+    return f32np(out), f32np(outq), best.cpu().numpy(), ref, refq, rbest
+
+
+def _check_selection(best, rbest, ref):
+    for u in range(len(rbest)):
+        flat = np.sort(ref[u].ravel())
+        near_tie = (flat[1] - flat[0]) <= 2e-3 * flat[0]
+        if not near_tie:
+            assert best[u] == rbest[u], (u, best[u], rbest[u])
+        else:
+            print(f"unit {u}: near-tie between the oracle's best two ({flat[0]:.6g}, {flat[1]:.6g})")
+
+
+def test_candidate_nmse_joint_envelope(dev):
+    from decode_attention_int2_amd import kvq
+    clips = list(synthetic.CLIP_GRID)
+    got, gotq, best, ref, refq, rbest = _candidate_case(dev, "envelope", kvq.KVQ_SELECT_JOINT, 1024, 4, 4, 1, 9,
+                                                        clips, 128)
+    rel = np.abs(got - ref) / np.abs(ref)
+    print("joint envelope: max NMSE rel diff", rel.max(), "best", best, rbest)
+    assert rel.max() <= 1e-3
+    assert np.abs(gotq - refq).max() / np.abs(refq).max() <= 1e-3
+    _check_selection(best, rbest, ref)
+
+
+def test_candidate_nmse_per_head_dense(dev):
+    from decode_attention_int2_amd import kvq
+    clips = [1.0, 0.9, 0.8]
+    got, gotq, best, ref, refq, rbest = _candidate_case(dev, "calib64k", kvq.KVQ_SELECT_PER_HEAD, 800, 2, 2, 5, 3,
+                                                        clips, 96)
+    rel = np.abs(got - ref) / np.abs(ref)
+    print("per-head dense: max NMSE rel diff", rel.max(), "best", best, rbest)
+    assert rel.max() <= 1e-3
+    _check_selection(best, rbest, ref)
+
+
+def test_candidate_nmse_per_head_gqa(dev):
+    """Per-head units with G = 2 query heads per KV head and centered keys."""
+    from decode_attention_int2_amd import kvq
+    clips = [1.0, 0.85]
+    got, gotq, best, ref, refq, rbest = _candidate_case(dev, "envelope", kvq.KVQ_SELECT_PER_HEAD, 700, 2, 4, 3, 4,
+                                                        clips, 64, center=True)
+    rel = np.abs(got - ref) / np.abs(ref)
+    assert rel.max() <= 1e-3
+    _check_selection(best, rbest, ref)
