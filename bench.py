@@ -40,6 +40,9 @@ def _args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--num-splits", type=int, default=0, help="split-K parts per sequence (0 = library default)")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_split_paged16x32k_traffic.json"))
     return ap.parse_args()
 
@@ -86,6 +89,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.profile_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": 1 << 30, "copy_bytes_written_per_launch": 1 << 30}))
+        return
     kvq.load_library()
     w = synthetic.make(WORKLOAD, dev)
     B, T, H, Hq, dm, P = w.num_seqs, w.tokens, w.H, w.Hq, w.d_model, w.page_size
@@ -95,7 +106,8 @@ def main():
     rows = B * w.queries_per_seq
     out_o = torch.empty((rows, Hq, 128), dtype=torch.float32, device=dev)
     out_y = torch.empty((rows, dm), dtype=torch.float32, device=dev)
-    ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, 1, Hq, H, T, dm), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, 1, Hq, H, T, dm, a.num_splits), dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -106,7 +118,8 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         kvq.kvq_decode_attn(w.q, B, 1, caches[(i + 1) % 2], w.page_table, max_pages, w.seq_lens, T, rot, rot, out_o,
-                            w_o=w.w_o, out_y=out_y, workspace=ws, split_events=None if ev is None else (ev[2], ev[3]))
+                            w_o=w.w_o, out_y=out_y, workspace=ws, num_splits=a.num_splits,
+                            split_events=None if ev is None else (ev[2], ev[3]))
         if ev is not None:
             ev[4].record(stream)
 
@@ -117,7 +130,11 @@ def main():
         step(i)
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    for ev in events:          # torch creates the HIP event on first record; the library records 2 of them
+        for e in ev:
+            e.record(stream)
     torch.cuda.synchronize()
+    assert all(e.cuda_event != 0 for ev in events for e in ev)
     t0 = time.perf_counter()
     for i in range(a.steps):
         step(a.warmup + i, events[i])

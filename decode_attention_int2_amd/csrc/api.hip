@@ -128,6 +128,7 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   if (static_cast<int64_t>(queries_per_seq) * (num_q_heads / H) > kMaxRows) return KVQ_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_pages_per_seq) * cache->page_size)
     return KVQ_ERR_INVALID_ARGUMENT;
+  if (static_cast<int64_t>(max_seq_len) > kMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
   if (!page_table && static_cast<int64_t>(num_seqs) * max_pages_per_seq > cache->num_pages)
     return KVQ_ERR_INVALID_ARGUMENT;
   if (w_o && (d_model < 1 || !out_y)) return KVQ_ERR_INVALID_ARGUMENT;
@@ -141,10 +142,18 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   float *qsum = reinterpret_cast<float *>(ws + pl.off_qsum);
   float *part = reinterpret_cast<float *>(ws + pl.off_part);
   float *ypart = reinterpret_cast<float *>(ws + pl.off_ypart);
+  int32_t *qdig = reinterpret_cast<int32_t *>(ws + pl.off_qdig);
+  int32_t *qexp = reinterpret_cast<int32_t *>(ws + pl.off_qexp);
+  const bool mfma = decode_mfma_supported(pl, cache->page_size);
   KVQ_TRY(launch_query_rotation(q, dtype, pl, to_dev(*rot_k), qrot, qsum, stream));
+  if (mfma) KVQ_TRY(launch_query_digits(pl, qrot, qdig, qexp, stream));
   if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
-  KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
-                              seq_lens, qrot, qsum, part, stream));
+  if (mfma)
+    KVQ_TRY(launch_decode_split_mfma(pl, cache->pages, cache->num_pages, cache->page_size, page_table,
+                                     max_pages_per_seq, seq_lens, qdig, qexp, qsum, part, stream));
+  else
+    KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
+                                seq_lens, qrot, qsum, part, stream));
   if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
   KVQ_TRY(launch_combine(pl, part, to_dev(*rot_v), out_o, stream));
   if (w_o) KVQ_TRY(launch_wo_projection(pl, out_o, w_o, dtype, ypart, out_y, stream));
@@ -196,6 +205,9 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   float *qrot = reinterpret_cast<float *>(dec + pl.off_qrot);
   float *qsum = reinterpret_cast<float *>(dec + pl.off_qsum);
   float *part = reinterpret_cast<float *>(dec + pl.off_part);
+  int32_t *qdig = reinterpret_cast<int32_t *>(dec + pl.off_qdig);
+  int32_t *qexp = reinterpret_cast<int32_t *>(dec + pl.off_qexp);
+  const bool mfma = decode_mfma_supported(pl, 16);
   const RotDev ident{KVQ_ROT_IDENTITY, nullptr, nullptr};
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
   const size_t stride_u = static_cast<size_t>(num_candidates) * num_clips * Nq;
@@ -208,11 +220,16 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   for (int r = 0; r < num_candidates; ++r) {
     const RotDev rot = to_dev(candidates[r]);
     KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
+    if (mfma) KVQ_TRY(launch_query_digits(pl, qrot, qdig, qexp, stream));
     for (int i = 0; i < num_clips; ++i) {
       KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips[i], clips[i], pages,
                               L.num_pages, 16, stream));
-      KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len, qrot,
-                                  qsum, part, stream));
+      if (mfma)
+        KVQ_TRY(launch_decode_split_mfma(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
+                                         qdig, qexp, qsum, part, stream));
+      else
+        KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
+                                    qrot, qsum, part, stream));
       KVQ_TRY(launch_combine(pl, part, rot, o_hat, stream));
       KVQ_TRY(launch_nmse_terms(o_hat, o_ref, w_o, dtype, Nq, Hq, H, d_model, mode,
                                 nmse_q + (static_cast<size_t>(r) * num_clips + i) * Nq, stride_u, stream));

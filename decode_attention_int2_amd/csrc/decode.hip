@@ -383,28 +383,56 @@ __global__ __launch_bounds__(256) void reference_split_kernel(SplitArgs a) {
 
 // ------------------------------------------------------------ combine
 // Merge split partials (base-2 log-sum-exp), apply R_V^T, write out_o.
+constexpr int kMaxCombineSplits = kMaxSplits;
 __global__ __launch_bounds__(128) void combine_kernel(const float *part, int splits, int Hq, int G, RotDev rv,
                                                       float *out_o) {
   __shared__ float os[D];
+  __shared__ float wsh[kMaxCombineSplits];
+  __shared__ float stat[4];  // l, z, nan flag
   const int rj = blockIdx.x;
   const int j = rj % Hq, h = j / G;
   const int i = threadIdx.x;
   const float *p = part + static_cast<size_t>(rj) * splits * (D + 4);
-  float mstar = -INFINITY;
-  for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, p[s * (D + 4)]);
-  float l = 0.0f, z = 0.0f, acc = 0.0f;
-  bool nan = false;
-  for (int s = 0; s < splits; ++s) {
-    const float *q = p + s * (D + 4);
-    if (q[1] != q[1]) nan = true;
-    if (q[0] == -INFINITY) continue;
-    const float w = exp2f(q[0] - mstar);
-    l += w * q[1];
-    z += w * q[2];
-    acc += w * q[4 + i];
+  // split statistics in parallel: max of m, then weights 2^(m_s - m*)
+  float mloc = -INFINITY;
+  for (int s = i; s < splits; s += D) mloc = fmaxf(mloc, p[static_cast<size_t>(s) * (D + 4)]);
+  mloc = wave_maxf(mloc);
+  if ((i & 63) == 0) os[i >> 6] = mloc;
+  __syncthreads();
+  const float mstar = fmaxf(os[0], os[1]);
+  float lloc = 0.0f, zloc = 0.0f, nanloc = 0.0f;
+  for (int s = i; s < splits; s += D) {
+    const float *q = p + static_cast<size_t>(s) * (D + 4);
+    const float w = (q[0] == -INFINITY) ? 0.0f : exp2f(q[0] - mstar);
+    wsh[s] = w;
+    if (q[1] != q[1]) nanloc = 1.0f;
+    if (w != 0.0f) {
+      lloc += w * q[1];
+      zloc += w * q[2];
+    }
   }
+  lloc = wave_sum(lloc);
+  zloc = wave_sum(zloc);
+  nanloc = wave_maxf(nanloc);
+  __syncthreads();
+  if (i == 0) stat[0] = stat[1] = stat[2] = 0.0f;
+  __syncthreads();
+  if ((i & 63) == 0) {
+    atomicAdd(&stat[0], lloc);
+    atomicAdd(&stat[1], zloc);
+    atomicMax(reinterpret_cast<int *>(&stat[2]), __float_as_int(nanloc));
+  }
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) {
+    const float w = wsh[s];
+    if (w != 0.0f) acc += w * p[static_cast<size_t>(s) * (D + 4) + 4 + i];
+  }
+  const float l = stat[0], z = stat[1];
   float o = (l > 0.0f) ? (acc + z) / l : 0.0f;
-  if (nan) o = __builtin_nanf("");
+  if (stat[2] != 0.0f) o = __builtin_nanf("");
+  __syncthreads();
   os[i] = o;
   __syncthreads();
   float r = 0.0f;
@@ -420,26 +448,63 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *part, int spl
 // ------------------------------------------------------------ W_O projection
 constexpr int kRowGroup = 16;
 
+// y partial for 128 columns (2 per lane) x one K slice; the 4 waves of the
+// block split the slice and are summed in shared memory.  Rows of o for the
+// slice are staged in shared memory; the K loop keeps 8 loads in flight.
+constexpr int kWoCols = 128;
+constexpr int kWoSplit = 8;
+
 template <int DT>
 __global__ __launch_bounds__(256) void wo_partial_kernel(const float *o, const void *w_o, int rows, int K,
                                                          int d_model, int kchunk, float *ypart) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  __shared__ float osh[kRowGroup][512];          // kchunk <= 512
+  __shared__ float red[kRowGroup][kWoCols];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = blockIdx.x * kWoCols + 2 * lane;
   const int ks = blockIdx.y;
   const int k0 = ks * kchunk, k1 = min(K, k0 + kchunk);
+  const int span = k1 - k0;
+  const int wq = (span + 3) / 4;
+  const int wk0 = min(span, wave * wq), wk1 = min(span, wk0 + wq);
   for (int r0 = 0; r0 < rows; r0 += kRowGroup) {
-    float acc[kRowGroup];
+    const int rg = min(kRowGroup, rows - r0);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rg * span; idx += 256) {
+      const int r = idx / span, kk = idx % span;
+      osh[r][kk] = o[static_cast<size_t>(r0 + r) * K + k0 + kk];
+    }
+    for (int idx = threadIdx.x; idx < kRowGroup * kWoCols; idx += 256) (&red[0][0])[idx] = 0.0f;
+    __syncthreads();
+    float acc[kRowGroup][2];
 #pragma unroll
-    for (int r = 0; r < kRowGroup; ++r) acc[r] = 0.0f;
-    if (n < d_model) {
-      for (int kk = k0; kk < k1; ++kk) {
-        const float w = load_elem<DT>(w_o, static_cast<size_t>(kk) * d_model + n);
+    for (int r = 0; r < kRowGroup; ++r) acc[r][0] = acc[r][1] = 0.0f;
+    const bool c0 = n < d_model, c1 = n + 1 < d_model;
+#pragma unroll 8
+    for (int kk = wk0; kk < wk1; ++kk) {
+      const size_t base = static_cast<size_t>(k0 + kk) * d_model + n;
+      const float w0 = c0 ? load_elem<DT>(w_o, base) : 0.0f;
+      const float w1 = c1 ? load_elem<DT>(w_o, base + 1) : 0.0f;
 #pragma unroll
-        for (int r = 0; r < kRowGroup; ++r)
-          if (r0 + r < rows) acc[r] += o[static_cast<size_t>(r0 + r) * K + kk] * w;
+      for (int r = 0; r < kRowGroup; ++r) {
+        const float ov = osh[r][kk];
+        acc[r][0] += ov * w0;
+        acc[r][1] += ov * w1;
       }
+    }
+    for (int w = 0; w < 4; ++w) {  // sum the 4 K quarters in a fixed order
+      if (wave == w) {
 #pragma unroll
-      for (int r = 0; r < kRowGroup; ++r)
-        if (r0 + r < rows) ypart[(static_cast<size_t>(ks) * rows + r0 + r) * d_model + n] = acc[r];
+        for (int r = 0; r < kRowGroup; ++r) {
+          red[r][2 * lane] += acc[r][0];
+          red[r][2 * lane + 1] += acc[r][1];
+        }
+      }
+      __syncthreads();
+    }
+    for (int idx = threadIdx.x; idx < rg * kWoCols; idx += 256) {
+      const int r = idx / kWoCols, c = idx % kWoCols;
+      const int nn = blockIdx.x * kWoCols + c;
+      if (nn < d_model) ypart[(static_cast<size_t>(ks) * rows + r0 + r) * d_model + nn] = red[r][c];
     }
   }
 }
@@ -502,20 +567,24 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   const int max_chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   int splits = num_splits;
   if (splits <= 0) {
+    // enough workgroups to fill 256 CUs several times; the matrix-core kernel
+    // (<= 4 rows per KV head) runs 4 waves per workgroup on longer splits
     const int units = num_seqs * H > 0 ? num_seqs * H : 1;
-    splits = (4096 + units - 1) / units;
+    const int target = (queries_per_seq * (Hq / H) <= 4) ? 1024 : 4096;
+    splits = (target + units - 1) / units;
   }
   if (splits > max_chunks) splits = max_chunks;
+  if (splits > kMaxCombineSplits) splits = kMaxCombineSplits;
   if (splits < 1) splits = 1;
   int chunks_per_split = (max_chunks + splits - 1) / splits;
+  if (chunks_per_split * kChunk > kMaxMfmaSplitTokens) chunks_per_split = kMaxMfmaSplitTokens / kChunk;
   pl.split_tokens = chunks_per_split * kChunk;
   pl.splits = (max_chunks + chunks_per_split - 1) / chunks_per_split;
   pl.d_model = d_model;
   const int K = Hq * D;
-  const int ncb = d_model > 0 ? (d_model + 255) / 256 : 1;
-  int ks = (512 + ncb - 1) / ncb;
-  if (ks > K / 64) ks = K / 64;
-  if (ks < 1) ks = 1;
+  int ks = kWoSplit;
+  while (ks > 1 && (K + ks - 1) / ks < 64) ks /= 2;
+  while ((K + ks - 1) / ks > 512) ks *= 2;  // K slice must fit the staging buffer
   pl.wo_ksplit = ks;
   const size_t rows = static_cast<size_t>(num_seqs) * queries_per_seq;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -528,6 +597,10 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   off = align(off + rows * Hq * static_cast<size_t>(pl.splits) * (D + 4) * sizeof(float));
   pl.off_ypart = off;
   off = align(off + (d_model > 0 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
+  pl.off_qdig = off;  // [num_seqs][H][64 lanes][8] int32
+  off = align(off + static_cast<size_t>(num_seqs) * H * 64 * 8 * sizeof(int32_t));
+  pl.off_qexp = off;  // [num_seqs][H][4 rows] int32
+  off = align(off + static_cast<size_t>(num_seqs) * H * 4 * sizeof(int32_t));
   pl.total = off;
   return pl;
 }
@@ -603,7 +676,7 @@ hipError_t launch_wo_projection(const DecodePlan &pl, const float *o, const void
   if (rows == 0 || pl.d_model <= 0) return hipSuccess;
   const int K = pl.Hq * D;
   const int kchunk = (K + pl.wo_ksplit - 1) / pl.wo_ksplit;
-  dim3 grid((pl.d_model + 255) / 256, pl.wo_ksplit);
+  dim3 grid((pl.d_model + kWoCols - 1) / kWoCols, pl.wo_ksplit);
   if (dtype == KVQ_F32)
     hipLaunchKernelGGL(wo_partial_kernel<KVQ_F32>, grid, dim3(256), 0, stream, o, w_o, rows, K, pl.d_model, kchunk,
                        ypart);

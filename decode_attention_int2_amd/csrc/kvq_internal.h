@@ -12,6 +12,9 @@ namespace kvq {
 constexpr int D = 128;         // head dimension == quantization group size
 constexpr int kMaxRows = 64;   // query rows sharing one (sequence, KV head)
 constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
+constexpr int kMaxMfmaSplitTokens = 16384;  // tokens per split (page ids of a split fit in LDS)
+constexpr int kMaxSplits = 4096;            // split partials merged per (row, head)
+constexpr int64_t kMaxSeqLen = static_cast<int64_t>(kMaxSplits) * kMaxMfmaSplitTokens;
 
 // Rotation descriptor passed by value to kernels.
 struct RotDev {
@@ -62,7 +65,8 @@ struct DecodePlan {
   int num_seqs, queries_per_seq, Hq, H, G, rows_per_head;  // rows_per_head = queries_per_seq * G
   int max_seq_len, splits, split_tokens;                   // split_tokens % kChunk == 0
   int d_model, wo_ksplit;
-  size_t off_qrot, off_qsum, off_part, off_ypart, total;   // workspace layout (bytes)
+  size_t off_qrot, off_qsum, off_part, off_ypart;          // workspace layout (bytes)
+  size_t off_qdig, off_qexp, total;                        // key-side query digits (matrix-core kernel)
 };
 DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, int max_seq_len, int d_model,
                             int num_splits);
@@ -74,6 +78,16 @@ hipError_t launch_query_rotation(const void *q, int dtype, const DecodePlan &pl,
 hipError_t launch_decode_split(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
                                const int32_t *page_table, int max_pages, const int32_t *seq_lens,
                                const float *qrot, const float *qsum, float *part, hipStream_t stream);
+// Same partials from the matrix-core kernel (rows_per_head <= 4).
+bool decode_mfma_supported(const DecodePlan &pl, int page_size);
+// Fixed-point int8 digits of the rotated queries, one 64-lane operand set per
+// (sequence, KV head) (prologue of the matrix-core kernel).
+hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t *qdig, int32_t *qexp,
+                               hipStream_t stream);
+hipError_t launch_decode_split_mfma(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
+                                    const int32_t *page_table, int max_pages, const int32_t *seq_lens,
+                                    const int32_t *qdig, const int32_t *qexp, const float *qsum, float *part,
+                                    hipStream_t stream);
 // Split-K partial attention over raw (unquantized, unrotated) K and V that
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,

@@ -119,10 +119,15 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(QuantArgs a) {
       // INT2 group quantizer, fixed fp32 step order.
       const float mn = wave_min(fminf(r0, r1));
       const float mx = wave_max(fmaxf(r0, r1));
-      const float lo = clip * mn;
+      float lo = clip * mn;
       const float hi = clip * mx;
       const float span = hi - lo;
-      const float s32 = span / 3.0f;
+      float s32 = span / 3.0f;
+      // Round lo and s32 to fp32 before the fp16 conversion: without the
+      // register barrier the backend fuses clip*mn and the conversion into one
+      // mixed-precision FMA that rounds once, which is not the defined order.
+      asm volatile("" : "+v"(lo));
+      asm volatile("" : "+v"(s32));
       const _Float16 sh = static_cast<_Float16>(s32);
       const _Float16 zh = static_cast<_Float16>(lo);
       const float s = static_cast<float>(sh);

@@ -159,7 +159,8 @@ int kvq_quantize(const void *k, const void *v, int32_t dtype, int64_t num_tokens
  *                bytes with the same shape arguments.
  *   num_splits   split-K parts per sequence (0 = automatic).
  *   events       host pointer to a kvq_decode_events, or NULL.
- * Limits: Hq % H == 0 and queries_per_seq * Hq / H <= 64, else UNSUPPORTED.
+ * Limits: Hq % H == 0 (else INVALID_ARGUMENT); queries_per_seq * Hq / H <= 64
+ * and max_seq_len <= 2^26, else UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 /* Optional timing hook of kvq_decode_attn: when non-NULL, split_start and
  * split_stop are recorded on `stream` immediately before and after the

@@ -61,7 +61,9 @@ def test_quantize_prerotated_bitexact(dev, clip_k, clip_v):
                      clip_v=clip_v, slot_mapping=torch.from_numpy(slots).to(dev))
     torch.cuda.synchronize()
     got = cache.pages.cpu().numpy()
-    assert np.array_equal(got, ocache.pages), f"{int((got != ocache.pages).sum())} bytes differ"
+    diff = np.argwhere(got != ocache.pages)
+    where = [(int(p), int(h), int(o), "code" if o < 64 * P else "meta") for p, h, o in diff[:8]]
+    assert diff.shape[0] == 0, f"{diff.shape[0]} bytes differ (page, head, offset, kind): {where}"
 
 
 @pytest.mark.parametrize("preset,rot", [("envelope", "sh"), ("gqa32k", "dense"), ("paged16x32k", "sh"),
@@ -119,7 +121,7 @@ def test_decode_split_count_invariance(dev):
     base, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=1)
     for ns in (0, 3, 12):
         o, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=ns)
-        assert rel_l2(f32np(o), f32np(base)) < 2e-6
+        assert rel_l2(f32np(o), f32np(base)) < 1e-5   # fp32 summation order only
 
 
 def test_decode_edge_cases(dev):
