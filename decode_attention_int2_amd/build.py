@@ -19,6 +19,8 @@ SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "candidat
 # -packed-fp32-ops: no v_pk_*_f32 instructions; denormals kept; IEEE fp32 division.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
+         # matrix-core results and accumulators in ordinary VGPRs (no AGPR copies)
+         "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
          "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -162,6 +162,342 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(QuantArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------------
+// bf16 inputs: rotation on the matrix cores (v_mfma_f32_16x16x32_bf16).
+//
+// One workgroup takes one KV head of one side (keys or values) over a run
+// of 16-token tiles; the head's rotation is staged once in LDS as the A
+// operand.  For a tile, D = R'^T X^T: A rows are output dims, B columns are
+// the 16 tokens (the bf16 input rows, exact), k runs over input dims.  The A
+// rows are permuted so that lane (token tk = l%16, g = l/16) ends up with the
+// 32 consecutive output dims 32g..32g+31 of token tk: dim 32g + 4nt + i sits
+// in accumulator nt, element i, i.e. the codes of byte 8g + nt.
+//   signed Hadamard: R' = diag(s) H (entries +-1, exact in bf16) and the
+//                    1/sqrt(128) is applied to the fp32 result;
+//   dense:           R = R_hi + R_mid + R_lo, three bf16 parts (24 bits);
+//   identity:        no product, the lane loads its 32 dims directly.
+// Key centering subtracts mu R (fp64 dot products, one per dim) after the
+// product: (k - mu) R = k R - mu R.
+// The quantizer is the same fp32 sequence as the exact kernel; with the
+// identity rotation the codes are therefore identical to it.  With a
+// rotation the rotated values differ from an fp64 product by fp32 rounding.
+// ------------------------------------------------------------------------
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kQTiles = 32;       // 16-token tiles per workgroup
+constexpr int kQWaves = 4;
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic rounds x to an integer (ties to even)
+constexpr uint32_t kMagicBits = 0x4B400000u;
+
+// sum_{j<16} kMagicBits * 4^j (mod 2^32): the offset left by packing 16
+// magic-biased codes with shift-add.
+__host__ __device__ constexpr uint32_t magic_pack_offset() {
+  uint32_t acc = 0;
+  for (int j = 15; j >= 0; --j) acc = (acc << 2) + kMagicBits;
+  return acc;
+}
+
+struct FastArgs {
+  const uint16_t *x;  // [T][H][128] bf16 bits
+  int64_t T;
+  int H;
+  const int64_t *slot_mapping;
+  const int8_t *signs;  // [H][128]
+  const float *matrix;  // [H][128][128]
+  const float *mean;    // [H][128] or null (keys only)
+  float clip;
+  uint8_t *pages;
+  int64_t num_pages;
+  int P;
+  int side;  // 0 keys, 1 values
+};
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ int qdpp_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int qdpp_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
+
+// Output dim of A row r of accumulator tile nt.
+__device__ __forceinline__ int a_row_dim(int nt, int r) { return 32 * (r >> 2) + 4 * nt + (r & 3); }
+
+template <int KIND, bool kCenter, bool kWide>
+__global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
+  constexpr int kParts = KIND == KVQ_ROT_DENSE ? 3 : (KIND == KVQ_ROT_SIGNED_HADAMARD ? 1 : 0);
+  extern __shared__ __attribute__((aligned(16))) uint4 ash[];  // [kParts][4 ks][8 nt][64 lanes]
+  __shared__ float mrot[D];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tk = lane & 15, g = lane >> 4;
+
+  // ---- stage the rotation (A operand) and mu R
+  if constexpr (kParts > 0) {
+    for (int e = threadIdx.x; e < 4 * 8 * 64; e += blockDim.x) {
+      const int ks = e >> 9, nt = (e >> 6) & 7, ln = e & 63;
+      const int d = a_row_dim(nt, ln & 15);
+      const int k0 = 32 * ks + 8 * (ln >> 4);
+      uint32_t w[kParts > 0 ? kParts : 1][4];
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        uint32_t lo[kParts > 0 ? kParts : 1], hi[kParts > 0 ? kParts : 1];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int k = k0 + 2 * j2 + jj;
+          if constexpr (KIND == KVQ_ROT_SIGNED_HADAMARD) {
+            const bool neg = (a.signs[h * D + k] < 0) != ((__popc(static_cast<unsigned>(k & d)) & 1) != 0);
+            (jj ? hi : lo)[0] = neg ? 0xBF80u : 0x3F80u;
+          } else {
+            const float r = a.matrix[(static_cast<size_t>(h) * D + k) * D + d];
+            const uint32_t b0 = bf16_rne_bits(r);
+            const float r1 = r - bf16_to_float(b0);
+            const uint32_t b1 = bf16_rne_bits(r1);
+            const float r2 = r1 - bf16_to_float(b1);
+            const uint32_t b2 = bf16_rne_bits(r2);
+            (jj ? hi : lo)[0] = b0;
+            (jj ? hi : lo)[kParts > 1 ? 1 : 0] = b1;
+            (jj ? hi : lo)[kParts > 2 ? 2 : 0] = b2;
+          }
+        }
+#pragma unroll
+        for (int pp = 0; pp < kParts; ++pp) w[pp][j2] = lo[pp] | (hi[pp] << 16);
+      }
+#pragma unroll
+      for (int pp = 0; pp < kParts; ++pp) ash[pp * 2048 + e] = uint4{w[pp][0], w[pp][1], w[pp][2], w[pp][3]};
+    }
+  }
+  if constexpr (kCenter) {
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      const float *mu = a.mean + h * D;
+      if constexpr (KIND == KVQ_ROT_IDENTITY) {
+        mrot[d] = mu[d];
+      } else {
+        double acc = 0.0;
+        for (int k = 0; k < D; ++k) {
+          double r;
+          if constexpr (KIND == KVQ_ROT_SIGNED_HADAMARD)
+            r = static_cast<double>(a.signs[h * D + k]) * ((__popc(static_cast<unsigned>(k & d)) & 1) ? -1.0 : 1.0) *
+                (1.0 / __builtin_sqrt(128.0));
+          else
+            r = static_cast<double>(a.matrix[(static_cast<size_t>(h) * D + k) * D + d]);
+          acc += static_cast<double>(mu[k]) * r;
+        }
+        mrot[d] = static_cast<float>(acc);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t n_tiles = (a.T + 15) / 16;
+  const int64_t tile_begin = static_cast<int64_t>(blockIdx.x) * kQTiles;
+  const int64_t tile_end = min(tile_begin + kQTiles, n_tiles);
+  const int64_t slots = a.num_pages * a.P;
+  const size_t row_stride = static_cast<size_t>(a.H) * D;  // elements between tokens
+  const float scale = KIND == KVQ_ROT_SIGNED_HADAMARD ? 0.08838834764831845f : 1.0f;  // 1/sqrt(128)
+  const int qi = tk & 3;
+
+  // this lane's loads: 4 x 16 bytes of token tk (B operand k-slices, or 32 dims for identity)
+  auto load_tile = [&](int64_t tile, uint4 (&xb)[4]) {
+    const int64_t t = min(tile * 16 + tk, a.T - 1);
+    const uint16_t *row = a.x + static_cast<size_t>(t) * row_stride + static_cast<size_t>(h) * D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int off = KIND == KVQ_ROT_IDENTITY ? 32 * g + 8 * ks : 32 * ks + 8 * g;
+      xb[ks] = *reinterpret_cast<const uint4 *>(row + off);
+    }
+  };
+
+  int64_t tile = tile_begin + wave;
+  if (tile >= tile_end) return;
+  uint4 xcur[4], xnext[4];
+  load_tile(tile, xcur);
+  for (; tile < tile_end; tile += kQWaves) {
+    load_tile(min(tile + kQWaves, tile_end - 1), xnext);  // prefetch (the last tile re-reads itself)
+
+    // ---- rotated values y[nt][i] = dim 32g + 4nt + i of token tk
+    float y[8][4];
+    if constexpr (KIND == KVQ_ROT_IDENTITY) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t w[4] = {xcur[ks].x, xcur[ks].y, xcur[ks].z, xcur[ks].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = bf16_to_float((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+          y[2 * ks + (j >> 2)][j & 3] = v;
+        }
+      }
+    } else {
+      v4f acc[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int pp = 0; pp < kParts; ++pp)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const v8bf bop = __builtin_bit_cast(v8bf, xcur[ks]);
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const v8bf aop = __builtin_bit_cast(v8bf, ash[((pp * 4 + ks) * 8 + nt) * 64 + lane]);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc[nt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[nt][i] = acc[nt][i] * scale;
+    }
+    if constexpr (kCenter) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const float4 m = *reinterpret_cast<const float4 *>(&mrot[32 * g + 4 * nt]);
+        y[nt][0] = y[nt][0] - m.x;
+        y[nt][1] = y[nt][1] - m.y;
+        y[nt][2] = y[nt][2] - m.z;
+        y[nt][3] = y[nt][3] - m.w;
+      }
+    }
+
+    // ---- group statistics of token tk (its 4 lanes g hold 32 dims each)
+    float mn = y[0][0], mx = y[0][0];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mn = fminf(mn, y[nt][i]);
+        mx = fmaxf(mx, y[nt][i]);
+      }
+    mn = fminf(mn, __shfl_xor(mn, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float lo = a.clip * mn;
+    const float hi = a.clip * mx;
+    const float span = hi - lo;
+    float s32 = span / 3.0f;
+    asm volatile("" : "+v"(lo));
+    asm volatile("" : "+v"(s32));
+    const _Float16 sh = static_cast<_Float16>(s32);
+    const _Float16 zh = static_cast<_Float16>(lo);
+    const float s = static_cast<float>(sh);
+    const float z = static_cast<float>(zh);
+    const float inv = s != 0.0f ? 1.0f / s : 0.0f;  // s == 0: every code is 0
+
+    // ---- codes, packed 16 per dword by shift-add of magic-biased values
+    uint32_t cw[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int nt = 3; nt >= 0; --nt)
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          const float d = y[4 * half + nt][i] - z;
+          float tq;
+          if constexpr (KIND == KVQ_ROT_IDENTITY) {
+            const float t = d * inv;
+            tq = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f) + kMagic;
+          } else {
+            tq = __builtin_amdgcn_fmed3f(__builtin_fmaf(d, inv, kMagic), kMagic, kMagic + 3.0f);
+          }
+          acc = (acc << 2) + __float_as_uint(tq);
+        }
+      cw[half] = acc - magic_pack_offset();
+    }
+
+    // ---- destination slot of token tk
+    const int64_t t = tile * 16 + tk;
+    int64_t slot = -1;
+    if (t < a.T) slot = a.slot_mapping ? a.slot_mapping[t] : t;
+    const bool valid = slot >= 0 && slot < slots;
+    int64_t page = 0;
+    int p = 0;
+    if (valid) {
+      if constexpr (kWide) {
+        page = slot / a.P;
+        p = static_cast<int>(slot - page * a.P);
+      } else {
+        const uint32_t us = static_cast<uint32_t>(slot), up = static_cast<uint32_t>(a.P);
+        const uint32_t pg = us / up;
+        page = pg;
+        p = static_cast<int>(us - pg * up);
+      }
+    }
+    uint8_t *base = a.pages + (static_cast<size_t>(page) * a.H + h) * static_cast<size_t>(72 * a.P);
+
+    if (a.side == 0) {
+      if (valid) *reinterpret_cast<uint2 *>(base + 32 * p + 8 * g) = uint2{cw[0], cw[1]};
+    } else {
+      // 4 consecutive tokens of a tile form one interleaved 128-byte V group
+      // when their slots are 4 consecutive, 4-aligned positions: transpose
+      // the quad's code bytes (lane qi takes bytes 8g+2qi, 8g+2qi+1 of all
+      // 4 tokens) and write 8 bytes per lane; otherwise write bytes singly.
+      const int slot_lo = static_cast<int>(slot);
+      const int s0 = __builtin_amdgcn_mov_dpp(slot_lo, 0x00, 0xF, 0xF, false);  // quad lane 0
+      int ok = (valid && slot_lo == s0 + qi && (s0 & 3) == 0) ? 1 : 0;
+      ok &= qdpp_xor1(ok);
+      ok &= qdpp_xor2(ok);
+      const bool odd = (qi & 1) != 0, up2 = (qi & 2) != 0;
+      const uint32_t L = cw[0], Hh = cw[1];
+      const uint32_t r1 = static_cast<uint32_t>(qdpp_xor2(static_cast<int>(up2 ? L : Hh)));
+      const uint32_t X0 = up2 ? r1 : L, X1 = up2 ? Hh : r1;
+      const uint32_t sel_send = odd ? 0x05040100u : 0x07060302u;
+      const uint32_t sel_keep = odd ? 0x07060302u : 0x05040100u;
+      const uint32_t send = __builtin_amdgcn_perm(X1, X0, sel_send);
+      const uint32_t keep = __builtin_amdgcn_perm(X1, X0, sel_keep);
+      const uint32_t r2 = static_cast<uint32_t>(qdpp_xor1(static_cast<int>(send)));
+      const uint32_t E = odd ? r2 : keep, O = odd ? keep : r2;
+      const uint32_t W0 = __builtin_amdgcn_perm(O, E, 0x06020400u);
+      const uint32_t W1 = __builtin_amdgcn_perm(O, E, 0x07030501u);
+      uint8_t *vg = base + 32 * a.P + 128 * (p >> 2);
+      if (ok) {
+        *reinterpret_cast<uint2 *>(vg + 32 * g + 8 * qi) = uint2{W0, W1};
+      } else if (valid) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          vg[4 * (8 * g + m) + (p & 3)] = static_cast<uint8_t>(cw[m >> 2] >> (8 * (m & 3)));
+      }
+    }
+    if (valid && g == 0) {
+      const uint32_t meta = f16_bits(sh) | (f16_bits(zh) << 16);
+      *reinterpret_cast<uint32_t *>(base + (a.side ? 68 : 64) * a.P + 4 * p) = meta;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) xcur[ks] = xnext[ks];
+  }
+}
+
+template <int KIND, bool kCenter>
+hipError_t launch_fast_kind(const FastArgs &a, bool wide, hipStream_t stream) {
+  constexpr int kParts = KIND == KVQ_ROT_DENSE ? 3 : (KIND == KVQ_ROT_SIGNED_HADAMARD ? 1 : 0);
+  const size_t lds = static_cast<size_t>(kParts) * 2048 * sizeof(uint4);
+  const int64_t n_tiles = (a.T + 15) / 16;
+  const dim3 grid(static_cast<unsigned>((n_tiles + kQTiles - 1) / kQTiles), static_cast<unsigned>(a.H));
+  auto kern = wide ? quantize_fast_kernel<KIND, kCenter, true> : quantize_fast_kernel<KIND, kCenter, false>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_side(const FastArgs &a, int kind, bool wide, hipStream_t stream) {
+  const bool center = a.mean != nullptr;
+  if (kind == KVQ_ROT_IDENTITY)
+    return center ? launch_fast_kind<KVQ_ROT_IDENTITY, true>(a, wide, stream)
+                  : launch_fast_kind<KVQ_ROT_IDENTITY, false>(a, wide, stream);
+  if (kind == KVQ_ROT_SIGNED_HADAMARD)
+    return center ? launch_fast_kind<KVQ_ROT_SIGNED_HADAMARD, true>(a, wide, stream)
+                  : launch_fast_kind<KVQ_ROT_SIGNED_HADAMARD, false>(a, wide, stream);
+  return center ? launch_fast_kind<KVQ_ROT_DENSE, true>(a, wide, stream)
+                : launch_fast_kind<KVQ_ROT_DENSE, false>(a, wide, stream);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
@@ -170,14 +506,20 @@ hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_
   if (num_tokens == 0) return hipSuccess;
   QuantArgs a{k, v, num_tokens, H, slot_mapping, rk, rv, key_mean, clip_k, clip_v, pages, num_pages, page_size,
               1.0 / __builtin_sqrt(128.0)};
+  if (dtype == KVQ_BF16) {
+    const bool wide = num_pages * static_cast<int64_t>(page_size) > (static_cast<int64_t>(1) << 31);
+    FastArgs fk{static_cast<const uint16_t *>(k), num_tokens, H, slot_mapping, rk.signs, rk.matrix, key_mean,
+                clip_k, pages, num_pages, page_size, 0};
+    FastArgs fv{static_cast<const uint16_t *>(v), num_tokens, H, slot_mapping, rv.signs, rv.matrix, nullptr,
+                clip_v, pages, num_pages, page_size, 1};
+    hipError_t e = launch_fast_side(fk, rk.kind, wide, stream);
+    if (e != hipSuccess) return e;
+    return launch_fast_side(fv, rv.kind, wide, stream);
+  }
   const int64_t items = num_tokens * H;
   int64_t blocks = (items + 3) / 4;
   if (blocks > 16384) blocks = 16384;
-  if (dtype == KVQ_F32)
-    hipLaunchKernelGGL(quantize_exact_kernel<KVQ_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(quantize_exact_kernel<KVQ_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       a);
+  hipLaunchKernelGGL(quantize_exact_kernel<KVQ_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -78,3 +78,63 @@ def oracle_cache_and_decode(w, seq_lens=None, with_wo=True):
 def tolerance(w) -> float:
     """Float tolerance on rel-L2: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs."""
     return 1e-4 if w.dtype == "f32" else 2e-2
+
+
+def parse_cache(pages: np.ndarray, slots: np.ndarray, P: int):
+    """Codes [T][H][128] and fp16 scale/zero [T][H] of both sides, read from a
+    packed cache (uint8 [num_pages][H][72 P]) at the given slots, following
+    the layout documented in include/kvq.h."""
+    pages = np.asarray(pages)
+    page, p = slots // P, slots % P
+    blk = pages[page]                                     # [T][H][72 P]
+    T, H = blk.shape[0], blk.shape[1]
+    shifts = np.array([0, 2, 4, 6], np.uint8)
+    kb = np.stack([blk[i, :, 32 * p[i]:32 * p[i] + 32] for i in range(T)])           # [T][H][32]
+    vidx = 32 * P + 128 * (p[:, None] // 4) + 4 * np.arange(32)[None, :] + (p[:, None] % 4)
+    vb = np.stack([blk[i][:, vidx[i]] for i in range(T)])                              # [T][H][32]
+    out = {}
+    for name, by, moff in (("k", kb, 64 * P), ("v", vb, 68 * P)):
+        codes = ((by[..., None] >> shifts) & 3).reshape(T, H, 128)
+        meta = np.stack([blk[i, :, moff + 4 * p[i]:moff + 4 * p[i] + 4] for i in range(T)])
+        sb = meta[..., 0].astype(np.uint16) | (meta[..., 1].astype(np.uint16) << 8)
+        zb = meta[..., 2].astype(np.uint16) | (meta[..., 3].astype(np.uint16) << 8)
+        out[name] = (codes, sb.view(np.float16).astype(np.float64), zb.view(np.float16).astype(np.float64))
+    return out
+
+
+def fp16_spacing(x: np.ndarray) -> np.ndarray:
+    """Distance from |x| to the next fp16 value (subnormal spacing at the bottom)."""
+    a = np.abs(np.asarray(x, np.float64)).astype(np.float16)
+    return np.abs(np.nextafter(a, np.float16(np.inf)).astype(np.float64) - a.astype(np.float64))
+
+
+def check_rotated_quantization(got_pages, ref_pages, y_ref: dict, slots: np.ndarray, P: int,
+                               max_code_mismatch=2e-3, max_meta_mismatch=1e-2):
+    """Cache write with a rotation computed in a different rounding order than
+    the oracle's fp64 product: fp16 scale and zero may move by one fp16 step
+    and codes may differ at rounding boundaries, nothing more.
+
+    y_ref[side]: the oracle's rotated (centered) fp32 values [T][H][128].
+    Checks, per group: scale and zero within one fp16 spacing of the oracle's;
+    every code is a nearest (or boundary-adjacent) rounding of the oracle's
+    value under the cache's own scale and zero; mismatch fractions bounded."""
+    keep = slots >= 0
+    g = parse_cache(got_pages, slots[keep], P)
+    r = parse_cache(ref_pages, slots[keep], P)
+    stats = {}
+    for side in ("k", "v"):
+        cg, sg, zg = g[side]
+        cr, sr, zr = r[side]
+        y = np.asarray(y_ref[side], np.float64)[keep]
+        assert np.all(np.abs(sg - sr) <= fp16_spacing(sr)), f"{side}: scale moved by more than one fp16 step"
+        assert np.all(np.abs(zg - zr) <= fp16_spacing(zr)), f"{side}: zero moved by more than one fp16 step"
+        pos = sg > 0
+        t = np.where(pos[..., None], (y - zg[..., None]) / np.where(pos, sg, 1.0)[..., None], 0.0)
+        t = np.clip(t, 0.0, 3.0)
+        err = np.abs(t - cg)
+        assert np.all(err <= 0.5 + 1e-2), f"{side}: code off its rounding interval by {err.max() - 0.5:.3e}"
+        assert np.all(cg[~pos] == 0)
+        stats[side] = (float(np.mean(cg != cr)), float(np.mean((sg != sr) | (zg != zr))))
+        assert stats[side][0] <= max_code_mismatch, (side, stats[side])
+        assert stats[side][1] <= max_meta_mismatch, (side, stats[side])
+    return stats

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 import synthetic
-from kvq_testlib import (f32np, gpu_decode, gpu_quantize, gpu_rot, oracle_cache_and_decode, oracle_rot, rel_l2,
-                         tolerance)
+from kvq_testlib import (check_rotated_quantization, f32np, gpu_decode, gpu_quantize, gpu_rot,
+                         oracle_cache_and_decode, oracle_rot, rel_l2, tolerance)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,23 +41,38 @@ def _special_groups(n_tok, H, rng):
     return x
 
 
-@pytest.mark.parametrize("clip_k,clip_v", [(1.0, 1.0), (0.96, 0.92), (0.8, 0.85)])
-def test_quantize_prerotated_bitexact(dev, clip_k, clip_v):
-    """Identity rotation on fp32 inputs: codes and metadata equal the oracle bit for bit."""
+@pytest.mark.parametrize("dtype,clip_k,clip_v,center", [("f32", 1.0, 1.0, False), ("f32", 0.96, 0.92, False),
+                                                         ("f32", 0.8, 0.85, True), ("bf16", 1.0, 1.0, False),
+                                                         ("bf16", 0.96, 0.92, False), ("bf16", 0.8, 0.85, True)])
+def test_quantize_prerotated_bitexact(dev, dtype, clip_k, clip_v, center):
+    """Identity rotation (pre-rotated inputs), fp32 inputs (exact kernel) and
+    bf16 inputs (matrix-core kernel's identity path), with and without key
+    centering: codes and metadata equal the oracle bit for bit."""
     rng = np.random.default_rng(100)
     T, H, P = 777, 4, 16
     k = _special_groups(T, H, rng)
     v = _special_groups(T, H, rng) * 3
+    if dtype == "bf16":                               # both sides see the same bf16 values
+        k = torch.from_numpy(k).to(torch.bfloat16).float().numpy()
+        v = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+    mean = (rng.standard_normal((H, 128)) * 0.3).astype(np.float32) if center else None
     num_pages = (T + P - 1) // P + 5
-    slots = rng.permutation(num_pages * P)[:T].astype(np.int64)
+    run_a = np.arange(64) + P * (num_pages - 5)       # 4-aligned consecutive slots (grouped V writes)
+    run_b = np.arange(10) + P * (num_pages - 1) + 3   # consecutive but not 4-aligned
+    others = np.setdiff1d(np.arange(num_pages * P), np.concatenate([run_a, run_b]))
+    slots = rng.permutation(others)[:T].astype(np.int64)
+    slots[100:164] = run_a
+    slots[300:310] = run_b
     slots[5] = -1                                     # negative slot: token skipped
     ident = oracle.Rotation(oracle.ROT_IDENTITY)
     ocache = oracle.Cache(num_pages, P, H)
-    oracle.quantize(k, v, ocache, ident, ident, clip_k=clip_k, clip_v=clip_v, slot_mapping=slots)
+    oracle.quantize(k, v, ocache, ident, ident, key_mean=mean, clip_k=clip_k, clip_v=clip_v, slot_mapping=slots)
     from decode_attention_int2_amd import kvq
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     cache = kvq.Cache(num_pages, P, H, device=dev)
     gid = kvq.Rotation(kvq.KVQ_ROT_IDENTITY)
-    kvq.kvq_quantize(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), cache, gid, gid, clip_k=clip_k,
+    kvq.kvq_quantize(torch.from_numpy(k).to(dev).to(tdt), torch.from_numpy(v).to(dev).to(tdt), cache, gid, gid,
+                     key_mean=None if mean is None else torch.from_numpy(mean).to(dev), clip_k=clip_k,
                      clip_v=clip_v, slot_mapping=torch.from_numpy(slots).to(dev))
     torch.cuda.synchronize()
     got = cache.pages.cpu().numpy()
@@ -70,7 +85,11 @@ def test_quantize_prerotated_bitexact(dev, clip_k, clip_v):
                                         ("long131k", "dense")])
 def test_quantize_end_to_end(dev, preset, rot):
     """Rotation (+ key centering where the preset has it) then quantization:
-    cache bytes vs the oracle's own cache write of the same inputs."""
+    cache bytes vs the oracle's own cache write of the same inputs.  fp32
+    inputs (exact kernel): bytes equal up to 1e-4.  bf16 inputs (matrix-core
+    rotation, fp32 accumulation): every group checked against the oracle's
+    rotated values (scale/zero within one fp16 step, codes on their rounding
+    interval, rare boundary flips)."""
     w = synthetic.make(preset, dev, tokens=600, num_seqs=2, H=3, Hq=6, d_model=64)
     if preset == "envelope":
         w.rot_k = w.rot_v = w.candidates[3]
@@ -78,12 +97,18 @@ def test_quantize_end_to_end(dev, preset, rot):
     torch.cuda.synchronize()
     ocache = oracle.Cache(w.num_pages, w.page_size, w.H)
     km = None if w.key_mean is None else f32np(w.key_mean)
+    slots = w.slot_mapping.cpu().numpy()
     oracle.quantize(f32np(w.k), f32np(w.v), ocache, oracle_rot(w.rot_k), oracle_rot(w.rot_v), key_mean=km,
-                    clip_k=w.clip_k, clip_v=w.clip_v, slot_mapping=w.slot_mapping.cpu().numpy())
+                    clip_k=w.clip_k, clip_v=w.clip_v, slot_mapping=slots)
     got = cache.pages.cpu().numpy()
-    frac = float(np.mean(got != ocache.pages))
-    print(f"{preset}: byte mismatch fraction {frac:.3e}")
-    assert frac <= 1e-4
+    if w.dtype == "f32":
+        frac = float(np.mean(got != ocache.pages))
+        print(f"{preset}: byte mismatch fraction {frac:.3e}")
+        assert frac <= 1e-4
+        return
+    y = {"k": oracle.rotate(f32np(w.k), oracle_rot(w.rot_k), km), "v": oracle.rotate(f32np(w.v), oracle_rot(w.rot_v))}
+    stats = check_rotated_quantization(got, ocache.pages, y, slots, w.page_size)
+    print(f"{preset}: (code, meta) mismatch fractions {stats}")
 
 
 @pytest.mark.parametrize("case", ["envelope_f32_sh", "gqa_bf16_dense_centered", "paged_bf16_sh_ragged",
