@@ -155,8 +155,9 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
     KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
                                 seq_lens, qrot, qsum, part, stream));
   if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
-  KVQ_TRY(launch_combine(pl, part, to_dev(*rot_v), out_o, stream));
-  if (w_o) KVQ_TRY(launch_wo_projection(pl, out_o, w_o, dtype, ypart, out_y, stream));
+  float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
+  KVQ_TRY(launch_combine(pl, part, to_dev(*rot_v), out_o, ot, stream));
+  if (w_o) KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, ypart, out_y, stream));
   return KVQ_OK;
 }
 
@@ -215,7 +216,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   // Full-precision reference readout of the raw K, V.
   KVQ_TRY(launch_query_rotation(q, dtype, pl, ident, qrot, qsum, stream));
   KVQ_TRY(launch_reference_split(pl, k, v, dtype, num_tokens, qrot, part, stream));
-  KVQ_TRY(launch_combine(pl, part, ident, o_ref, stream));
+  KVQ_TRY(launch_combine(pl, part, ident, o_ref, nullptr, stream));
   KVQ_TRY(launch_fill_i32(seq_len, static_cast<int32_t>(num_tokens), 1, stream));
   for (int r = 0; r < num_candidates; ++r) {
     const RotDev rot = to_dev(candidates[r]);
@@ -230,7 +231,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
       else
         KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
                                     qrot, qsum, part, stream));
-      KVQ_TRY(launch_combine(pl, part, rot, o_hat, stream));
+      KVQ_TRY(launch_combine(pl, part, rot, o_hat, nullptr, stream));
       KVQ_TRY(launch_nmse_terms(o_hat, o_ref, w_o, dtype, Nq, Hq, H, d_model, mode,
                                 nmse_q + (static_cast<size_t>(r) * num_clips + i) * Nq, stride_u, stream));
     }

@@ -11,6 +11,8 @@
 // s and zero z, q . (c s + z) = s (q . c) + z sum(q), and
 // sum_t w_t (c_t s_t + z_t) = sum_t (w_t s_t) c_t + sum_t w_t z_t.
 // Softmax runs in base 2: queries are pre-scaled by log2(e) / sqrt(128).
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -27,31 +29,64 @@ __device__ __forceinline__ float wave_maxf(float x) {
   return x;
 }
 
+// ------------------------------------------------------------ rotations of one head vector
+// One wave holds a 128-vector as two registers per lane: x0 = x[lane],
+// x1 = x[lane + 64].
+
+// In-place fast Walsh-Hadamard transform: x <- x H, H[i][j] = (-1)^popcount(i & j)
+// (Sylvester order, unnormalized): one butterfly stage per index bit.
+__device__ __forceinline__ void fwht128(float &x0, float &x1, int lane) {
+  const float a = x0 + x1, b = x0 - x1;  // bit 6: pairs (lane, lane + 64)
+  x0 = a;
+  x1 = b;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float p0 = __shfl_xor(x0, d), p1 = __shfl_xor(x1, d);
+    const bool upper = (lane & d) != 0;
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+  }
+}
+
 // ------------------------------------------------------------ query rotation
 // q'[row][j] = q[row][j] R_K[h(j)] * log2(e)/sqrt(128); qsum = sum_c q'_c.
+// One wave per (query row, query head).
 template <int DT>
-__global__ __launch_bounds__(128) void query_rotation_kernel(const void *q, int Hq, int G, RotDev rk, float *qrot,
-                                                             float *qsum) {
-  __shared__ float qs[D];
-  __shared__ float red[2];
-  const int rj = blockIdx.x;  // row * Hq + j
-  const int j = rj % Hq, h = j / G;
-  const int c = threadIdx.x;
-  qs[c] = load_elem<DT>(q, static_cast<size_t>(rj) * D + c);
-  __syncthreads();
+__global__ __launch_bounds__(256) void query_rotation_kernel(const void *q, int n_items, int Hq, int G, RotDev rk,
+                                                             float *qrot, float *qsum) {
+  const int lane = threadIdx.x & 63;
+  const int rj = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rj >= n_items) return;
+  const int h = (rj % Hq) / G;
   const float inv_sqrt_d = 0.08838834764831845f;
-  float acc = 0.0f;
-  if (rk.kind == KVQ_ROT_IDENTITY) {
-    acc = qs[c];
-  } else {
-    for (int i = 0; i < D; ++i) acc += qs[i] * rot_entry(rk, h, i, c, inv_sqrt_d);
+  float x0 = load_elem<DT>(q, static_cast<size_t>(rj) * D + lane);
+  float x1 = load_elem<DT>(q, static_cast<size_t>(rj) * D + lane + 64);
+  float y0 = x0, y1 = x1;
+  if (rk.kind == KVQ_ROT_SIGNED_HADAMARD) {
+    // z R = ((z * s) H) / sqrt(128)
+    x0 *= static_cast<float>(rk.signs[h * D + lane]);
+    x1 *= static_cast<float>(rk.signs[h * D + lane + 64]);
+    fwht128(x0, x1, lane);
+    y0 = x0 * inv_sqrt_d;
+    y1 = x1 * inv_sqrt_d;
+  } else if (rk.kind == KVQ_ROT_DENSE) {
+    const float *m = rk.matrix + static_cast<size_t>(h) * D * D;
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < D; ++i) {
+      const float zi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(i < 64 ? x0 : x1), i & 63));
+      a0 += zi * m[i * D + lane];
+      a1 += zi * m[i * D + lane + 64];
+    }
+    y0 = a0;
+    y1 = a1;
   }
-  acc *= kLog2e * inv_sqrt_d;
-  qrot[static_cast<size_t>(rj) * D + c] = acc;
-  float s = wave_sum(acc);
-  if ((c & 63) == 0) red[c >> 6] = s;
-  __syncthreads();
-  if (c == 0) qsum[rj] = red[0] + red[1];
+  y0 *= kLog2e * inv_sqrt_d;
+  y1 *= kLog2e * inv_sqrt_d;
+  qrot[static_cast<size_t>(rj) * D + lane] = y0;
+  qrot[static_cast<size_t>(rj) * D + lane + 64] = y1;
+  const float sum = wave_sum(y0 + y1);
+  if (lane == 0) qsum[rj] = sum;
 }
 
 // ------------------------------------------------------------ split kernels
@@ -382,130 +417,195 @@ __global__ __launch_bounds__(256) void reference_split_kernel(SplitArgs a) {
 }
 
 // ------------------------------------------------------------ combine
-// Merge split partials (base-2 log-sum-exp), apply R_V^T, write out_o.
+// Merge split partials (base-2 log-sum-exp), apply R_V^T, write out_o (and,
+// for the W_O projection, a copy of o laid out [row group][K][16 rows]).
+// One wave per (query row, query head).
 constexpr int kMaxCombineSplits = kMaxSplits;
-__global__ __launch_bounds__(128) void combine_kernel(const float *part, int splits, int Hq, int G, RotDev rv,
-                                                      float *out_o) {
-  __shared__ float os[D];
-  __shared__ float wsh[kMaxCombineSplits];
-  __shared__ float stat[4];  // l, z, nan flag
-  const int rj = blockIdx.x;
-  const int j = rj % Hq, h = j / G;
-  const int i = threadIdx.x;
+constexpr int kWoRows = 16;  // rows of o per W_O pass
+
+__global__ __launch_bounds__(256) void combine_kernel(const float *part, int n_items, int splits, int Hq, int G,
+                                                      RotDev rv, float *out_o, float *ot) {
+  const int lane = threadIdx.x & 63;
+  const int rj = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rj >= n_items) return;
+  const int row = rj / Hq, j = rj % Hq, h = j / G;
+  const float inv_sqrt_d = 0.08838834764831845f;
   const float *p = part + static_cast<size_t>(rj) * splits * (D + 4);
-  // split statistics in parallel: max of m, then weights 2^(m_s - m*)
   float mloc = -INFINITY;
-  for (int s = i; s < splits; s += D) mloc = fmaxf(mloc, p[static_cast<size_t>(s) * (D + 4)]);
-  mloc = wave_maxf(mloc);
-  if ((i & 63) == 0) os[i >> 6] = mloc;
-  __syncthreads();
-  const float mstar = fmaxf(os[0], os[1]);
+  for (int s2 = lane; s2 < splits; s2 += 64) mloc = fmaxf(mloc, p[static_cast<size_t>(s2) * (D + 4)]);
+  const float mstar = wave_maxf(mloc);
   float lloc = 0.0f, zloc = 0.0f, nanloc = 0.0f;
-  for (int s = i; s < splits; s += D) {
-    const float *q = p + static_cast<size_t>(s) * (D + 4);
+  for (int s2 = lane; s2 < splits; s2 += 64) {
+    const float *q = p + static_cast<size_t>(s2) * (D + 4);
     const float w = (q[0] == -INFINITY) ? 0.0f : exp2f(q[0] - mstar);
-    wsh[s] = w;
     if (q[1] != q[1]) nanloc = 1.0f;
     if (w != 0.0f) {
       lloc += w * q[1];
       zloc += w * q[2];
     }
   }
-  lloc = wave_sum(lloc);
-  zloc = wave_sum(zloc);
-  nanloc = wave_maxf(nanloc);
-  __syncthreads();
-  if (i == 0) stat[0] = stat[1] = stat[2] = 0.0f;
-  __syncthreads();
-  if ((i & 63) == 0) {
-    atomicAdd(&stat[0], lloc);
-    atomicAdd(&stat[1], zloc);
-    atomicMax(reinterpret_cast<int *>(&stat[2]), __float_as_int(nanloc));
+  const float l = wave_sum(lloc), z = wave_sum(zloc);
+  const bool any_nan = wave_maxf(nanloc) != 0.0f;
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 4
+  for (int s2 = 0; s2 < splits; ++s2) {
+    const float *q = p + static_cast<size_t>(s2) * (D + 4);
+    const float m = q[0];  // uniform
+    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
+    if (w != 0.0f) {
+      a0 += w * q[4 + lane];
+      a1 += w * q[4 + 64 + lane];
+    }
   }
-  __syncthreads();
-  float acc = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < splits; ++s) {
-    const float w = wsh[s];
-    if (w != 0.0f) acc += w * p[static_cast<size_t>(s) * (D + 4) + 4 + i];
+  float o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
+  float o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
+  if (any_nan) o0 = o1 = __builtin_nanf("");
+  // out[i] = sum_c o'[c] R_V[i][c]
+  float r0 = o0, r1 = o1;
+  if (rv.kind == KVQ_ROT_SIGNED_HADAMARD) {
+    // R[i][c] = s_i H[i][c] / sqrt(128), H symmetric: out = s * (o' H) / sqrt(128)
+    fwht128(o0, o1, lane);
+    r0 = o0 * (static_cast<float>(rv.signs[h * D + lane]) * inv_sqrt_d);
+    r1 = o1 * (static_cast<float>(rv.signs[h * D + lane + 64]) * inv_sqrt_d);
+  } else if (rv.kind == KVQ_ROT_DENSE) {
+    const float *m0 = rv.matrix + (static_cast<size_t>(h) * D + lane) * D;
+    const float *m1 = m0 + 64 * D;
+    r0 = r1 = 0.0f;
+    for (int c = 0; c < D; c += 4) {
+      const float4 e0 = *reinterpret_cast<const float4 *>(m0 + c);
+      const float4 e1 = *reinterpret_cast<const float4 *>(m1 + c);
+      const float src = c < 64 ? o0 : o1;
+      const int cl = c & 63;
+      const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl));
+      const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 1));
+      const float v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 2));
+      const float v3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 3));
+      r0 += v0 * e0.x + v1 * e0.y + v2 * e0.z + v3 * e0.w;
+      r1 += v0 * e1.x + v1 * e1.y + v2 * e1.z + v3 * e1.w;
+    }
   }
-  const float l = stat[0], z = stat[1];
-  float o = (l > 0.0f) ? (acc + z) / l : 0.0f;
-  if (stat[2] != 0.0f) o = __builtin_nanf("");
-  __syncthreads();
-  os[i] = o;
-  __syncthreads();
-  float r = 0.0f;
-  if (rv.kind == KVQ_ROT_IDENTITY) {
-    r = os[i];
-  } else {
-    const float inv_sqrt_d = 0.08838834764831845f;
-    for (int c = 0; c < D; ++c) r += os[c] * rot_entry(rv, h, i, c, inv_sqrt_d);
+  const int K = Hq * D;
+  const size_t base = static_cast<size_t>(row) * K + j * D;
+  out_o[base + lane] = r0;
+  out_o[base + lane + 64] = r1;
+  if (ot) {
+    float *dst = ot + (static_cast<size_t>(row / kWoRows) * K + j * D) * kWoRows + row % kWoRows;
+    dst[static_cast<size_t>(lane) * kWoRows] = r0;
+    dst[static_cast<size_t>(lane + 64) * kWoRows] = r1;
   }
-  out_o[static_cast<size_t>(rj) * D + i] = r;
 }
 
 // ------------------------------------------------------------ W_O projection
-constexpr int kRowGroup = 16;
-
-// y partial for 128 columns (2 per lane) x one K slice; the 4 waves of the
-// block split the slice and are summed in shared memory.  Rows of o for the
-// slice are staged in shared memory; the K loop keeps 8 loads in flight.
-constexpr int kWoCols = 128;
-constexpr int kWoSplit = 8;
+// y[row][n] = sum_k o[row][k] W_O[k][n].  A block takes 256 columns (4 per
+// lane) of one K slice for 16 rows; the 16 values o[.][k] of a k are one
+// scalar load (o laid out [K][16]) broadcast to every lane, so each W_O
+// element is loaded once per 16 rows and feeds 16 FMAs.  The block's 4 waves
+// split the slice and are summed in shared memory in a fixed order; slices
+// are summed by a second kernel in a fixed order.
+constexpr int kWoCols = 256;
 
 template <int DT>
-__global__ __launch_bounds__(256) void wo_partial_kernel(const float *o, const void *w_o, int rows, int K,
-                                                         int d_model, int kchunk, float *ypart) {
-  __shared__ float osh[kRowGroup][512];          // kchunk <= 512
-  __shared__ float red[kRowGroup][kWoCols];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = blockIdx.x * kWoCols + 2 * lane;
-  const int ks = blockIdx.y;
-  const int k0 = ks * kchunk, k1 = min(K, k0 + kchunk);
-  const int span = k1 - k0;
-  const int wq = (span + 3) / 4;
-  const int wk0 = min(span, wave * wq), wk1 = min(span, wk0 + wq);
-  for (int r0 = 0; r0 < rows; r0 += kRowGroup) {
-    const int rg = min(kRowGroup, rows - r0);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < rg * span; idx += 256) {
-      const int r = idx / span, kk = idx % span;
-      osh[r][kk] = o[static_cast<size_t>(r0 + r) * K + k0 + kk];
-    }
-    for (int idx = threadIdx.x; idx < kRowGroup * kWoCols; idx += 256) (&red[0][0])[idx] = 0.0f;
-    __syncthreads();
-    float acc[kRowGroup][2];
+__device__ __forceinline__ float4 load_w4(const void *__restrict__ w, size_t idx, int n, int d_model) {
+  float e[4];
 #pragma unroll
-    for (int r = 0; r < kRowGroup; ++r) acc[r][0] = acc[r][1] = 0.0f;
-    const bool c0 = n < d_model, c1 = n + 1 < d_model;
-#pragma unroll 8
-    for (int kk = wk0; kk < wk1; ++kk) {
-      const size_t base = static_cast<size_t>(k0 + kk) * d_model + n;
-      const float w0 = c0 ? load_elem<DT>(w_o, base) : 0.0f;
-      const float w1 = c1 ? load_elem<DT>(w_o, base + 1) : 0.0f;
+  for (int c = 0; c < 4; ++c) e[c] = (n + c < d_model) ? load_elem<DT>(w, idx + c) : 0.0f;
+  return float4{e[0], e[1], e[2], e[3]};
+}
+
+constexpr int kWoWaves = 8;
+constexpr int kWoMaxSlice = 256;  // k per block (o slice staged in shared memory)
+
+template <int DT>
+__global__ __launch_bounds__(512) void wo_kernel(const float *__restrict__ ot, const void *__restrict__ w_o, int rows,
+                                                 int K, int d_model, int kslice, float *__restrict__ ypart) {
+  __shared__ float4 osh[kWoMaxSlice][kWoRows / 4];
+  __shared__ float4 red[4][kWoRows][64];  // [wave % 4][row][lane] column quads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = blockIdx.x * kWoCols + 4 * lane;
+  const int ks = blockIdx.y, rg = blockIdx.z;
+  const int k0 = ks * kslice, k1 = min(K, k0 + kslice);
+  // stage o[.][k0:k1] (16 rows per k, contiguous)
+  const float4 *src = reinterpret_cast<const float4 *>(ot + (static_cast<size_t>(rg) * K + k0) * kWoRows);
+  for (int idx = threadIdx.x; idx < (k1 - k0) * (kWoRows / 4); idx += blockDim.x)
+    osh[idx / (kWoRows / 4)][idx % (kWoRows / 4)] = src[idx];
+  __syncthreads();
+  const int kq = (kslice + kWoWaves - 1) / kWoWaves;
+  const int wk0 = min(k1, k0 + wave * kq), wk1 = min(k1, wk0 + kq);
+  float acc[kWoRows][4];
 #pragma unroll
-      for (int r = 0; r < kRowGroup; ++r) {
-        const float ov = osh[r][kk];
-        acc[r][0] += ov * w0;
-        acc[r][1] += ov * w1;
+  for (int r = 0; r < kWoRows; ++r) acc[r][0] = acc[r][1] = acc[r][2] = acc[r][3] = 0.0f;
+  auto body = [&](int k, float4 w) {
+#pragma unroll
+    for (int r4 = 0; r4 < kWoRows / 4; ++r4) {
+      const float4 ov = osh[k - k0][r4];  // same address in every lane: broadcast
+      const float o4[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        acc[4 * r4 + rr][0] += o4[rr] * w.x;
+        acc[4 * r4 + rr][1] += o4[rr] * w.y;
+        acc[4 * r4 + rr][2] += o4[rr] * w.z;
+        acc[4 * r4 + rr][3] += o4[rr] * w.w;
       }
     }
-    for (int w = 0; w < 4; ++w) {  // sum the 4 K quarters in a fixed order
-      if (wave == w) {
-#pragma unroll
-        for (int r = 0; r < kRowGroup; ++r) {
-          red[r][2 * lane] += acc[r][0];
-          red[r][2 * lane + 1] += acc[r][1];
-        }
+  };
+  // block-uniform choice: whole 256-column block in range with 4-aligned rows -> vector loads only
+  if ((d_model & 3) == 0 && static_cast<int>(blockIdx.x + 1) * kWoCols <= d_model) {
+    // batches of 8 rows of W_O, the next batch in flight while one is used
+    using Raw = typename std::conditional<DT == KVQ_F32, float4, uint2>::type;
+    const Raw *wp = reinterpret_cast<const Raw *>(static_cast<const char *>(w_o) +
+                                                  (static_cast<size_t>(n) * (DT == KVQ_F32 ? 4 : 2)));
+    const size_t row_raw = static_cast<size_t>(d_model) / 4;  // Raw elements per W_O row
+    auto unpack = [](Raw r) -> float4 {
+      if constexpr (DT == KVQ_F32) {
+        return r;
+      } else {
+        return float4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+                      __uint_as_float(r.y & 0xFFFF0000u)};
       }
-      __syncthreads();
+    };
+    constexpr int kB = 8;
+    Raw cur[kB], nxt[kB];
+    if (wk0 < wk1) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) cur[u] = wp[static_cast<size_t>(min(wk0 + u, wk1 - 1)) * row_raw];
+      for (int k = wk0; k < wk1; k += kB) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) nxt[u] = wp[static_cast<size_t>(min(k + kB + u, wk1 - 1)) * row_raw];
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+          if (k + u < wk1) body(k + u, unpack(cur[u]));
+#pragma unroll
+        for (int u = 0; u < kB; ++u) cur[u] = nxt[u];
+      }
     }
-    for (int idx = threadIdx.x; idx < rg * kWoCols; idx += 256) {
-      const int r = idx / kWoCols, c = idx % kWoCols;
-      const int nn = blockIdx.x * kWoCols + c;
-      if (nn < d_model) ypart[(static_cast<size_t>(ks) * rows + r0 + r) * d_model + nn] = red[r][c];
+  } else {
+    for (int k = wk0; k < wk1; ++k) body(k, load_w4<DT>(w_o, static_cast<size_t>(k) * d_model + n, n, d_model));
+  }
+  // fixed-order sum over the 8 waves: (w + (w+4)) for w < 4, then the four
+  if (wave >= 4) {
+#pragma unroll
+    for (int r = 0; r < kWoRows; ++r) red[wave - 4][r][lane] = float4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int r = 0; r < kWoRows; ++r) {
+      const float4 o = red[wave][r][lane];
+      red[wave][r][lane] = float4{acc[r][0] + o.x, acc[r][1] + o.y, acc[r][2] + o.z, acc[r][3] + o.w};
     }
+  }
+  __syncthreads();
+  const int nrows = min(kWoRows, rows - rg * kWoRows);
+  for (int idx = threadIdx.x; idx < nrows * 64; idx += blockDim.x) {
+    const int r = idx >> 6, l = idx & 63;
+    const float4 a0 = red[0][r][l], a1 = red[1][r][l], a2 = red[2][r][l], a3 = red[3][r][l];
+    const float e[4] = {((a0.x + a1.x) + a2.x) + a3.x, ((a0.y + a1.y) + a2.y) + a3.y, ((a0.z + a1.z) + a2.z) + a3.z,
+                        ((a0.w + a1.w) + a2.w) + a3.w};
+    const int nn = blockIdx.x * kWoCols + 4 * l;
+    float *dst = ypart + (static_cast<size_t>(ks) * rows + rg * kWoRows + r) * d_model;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (nn + c < d_model) dst[nn + c] = e[c];
   }
 }
 
@@ -581,11 +681,15 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   pl.split_tokens = chunks_per_split * kChunk;
   pl.splits = (max_chunks + chunks_per_split - 1) / chunks_per_split;
   pl.d_model = d_model;
+  // W_O: K slices so that column blocks x slices x row groups fill the chip
   const int K = Hq * D;
-  int ks = kWoSplit;
-  while (ks > 1 && (K + ks - 1) / ks < 64) ks /= 2;
-  while ((K + ks - 1) / ks > 512) ks *= 2;  // K slice must fit the staging buffer
-  pl.wo_ksplit = ks;
+  const size_t rows_w = static_cast<size_t>(num_seqs) * queries_per_seq;
+  const int col_blocks = d_model > 0 ? (d_model + kWoCols - 1) / kWoCols : 1;
+  const int row_groups = static_cast<int>((rows_w + kWoRows - 1) / kWoRows);
+  const int kslice = K < kWoMaxSlice ? K : kWoMaxSlice;
+  pl.wo_kslice = kslice;
+  pl.wo_ksplit = (K + kslice - 1) / kslice;
+  const int ks = pl.wo_ksplit;
   const size_t rows = static_cast<size_t>(num_seqs) * queries_per_seq;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t off = 0;
@@ -596,7 +700,9 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   pl.off_part = off;
   off = align(off + rows * Hq * static_cast<size_t>(pl.splits) * (D + 4) * sizeof(float));
   pl.off_ypart = off;
-  off = align(off + (d_model > 0 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
+  off = align(off + (d_model > 0 && ks > 1 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
+  pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection
+  off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * K * kWoRows * sizeof(float) : 0));
   pl.off_qdig = off;  // [num_seqs][H][64 lanes][8] int32
   off = align(off + static_cast<size_t>(num_seqs) * H * 64 * 8 * sizeof(int32_t));
   pl.off_qexp = off;  // [num_seqs][H][4 rows] int32
@@ -609,11 +715,12 @@ hipError_t launch_query_rotation(const void *q, int dtype, const DecodePlan &pl,
                                  float *qsum, hipStream_t stream) {
   const int n = pl.num_seqs * pl.queries_per_seq * pl.Hq;
   if (n == 0) return hipSuccess;
+  const dim3 grid((n + 3) / 4);
   if (dtype == KVQ_F32)
-    hipLaunchKernelGGL(query_rotation_kernel<KVQ_F32>, dim3(n), dim3(128), 0, stream, q, pl.Hq, pl.G, rk, qrot,
+    hipLaunchKernelGGL(query_rotation_kernel<KVQ_F32>, grid, dim3(256), 0, stream, q, n, pl.Hq, pl.G, rk, qrot,
                        qsum);
   else
-    hipLaunchKernelGGL(query_rotation_kernel<KVQ_BF16>, dim3(n), dim3(128), 0, stream, q, pl.Hq, pl.G, rk, qrot,
+    hipLaunchKernelGGL(query_rotation_kernel<KVQ_BF16>, grid, dim3(256), 0, stream, q, n, pl.Hq, pl.G, rk, qrot,
                        qsum);
   return hipGetLastError();
 }
@@ -663,31 +770,33 @@ hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const voi
   return launch_split(pl, a, true, dtype, stream);
 }
 
-hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, hipStream_t stream) {
+hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, float *ot,
+                          hipStream_t stream) {
   const int n = pl.num_seqs * pl.queries_per_seq * pl.Hq;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(n), dim3(128), 0, stream, part, pl.splits, pl.Hq, pl.G, rv, out_o);
+  hipLaunchKernelGGL(combine_kernel, dim3((n + 3) / 4), dim3(256), 0, stream, part, n, pl.splits, pl.Hq, pl.G, rv,
+                     out_o, ot);
   return hipGetLastError();
 }
 
-hipError_t launch_wo_projection(const DecodePlan &pl, const float *o, const void *w_o, int dtype, float *ypart,
+hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *ypart,
                                 float *out_y, hipStream_t stream) {
   const int rows = pl.num_seqs * pl.queries_per_seq;
   if (rows == 0 || pl.d_model <= 0) return hipSuccess;
   const int K = pl.Hq * D;
-  const int kchunk = (K + pl.wo_ksplit - 1) / pl.wo_ksplit;
-  dim3 grid((pl.d_model + kWoCols - 1) / kWoCols, pl.wo_ksplit);
+  const int ks = pl.wo_ksplit;
+  float *dst = ks > 1 ? ypart : out_y;
+  dim3 grid((pl.d_model + kWoCols - 1) / kWoCols, ks, (rows + kWoRows - 1) / kWoRows);
   if (dtype == KVQ_F32)
-    hipLaunchKernelGGL(wo_partial_kernel<KVQ_F32>, grid, dim3(256), 0, stream, o, w_o, rows, K, pl.d_model, kchunk,
-                       ypart);
+    hipLaunchKernelGGL(wo_kernel<KVQ_F32>, grid, dim3(64 * kWoWaves), 0, stream, ot, w_o, rows, K, pl.d_model, pl.wo_kslice,
+                       dst);
   else
-    hipLaunchKernelGGL(wo_partial_kernel<KVQ_BF16>, grid, dim3(256), 0, stream, o, w_o, rows, K, pl.d_model,
-                       kchunk, ypart);
+    hipLaunchKernelGGL(wo_kernel<KVQ_BF16>, grid, dim3(64 * kWoWaves), 0, stream, ot, w_o, rows, K, pl.d_model, pl.wo_kslice,
+                       dst);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || ks == 1) return e;
   const int total = rows * pl.d_model;
-  hipLaunchKernelGGL(wo_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, ypart, pl.wo_ksplit, total,
-                     out_y);
+  hipLaunchKernelGGL(wo_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, ypart, ks, total, out_y);
   return hipGetLastError();
 }
 

@@ -64,9 +64,10 @@ hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_
 struct DecodePlan {
   int num_seqs, queries_per_seq, Hq, H, G, rows_per_head;  // rows_per_head = queries_per_seq * G
   int max_seq_len, splits, split_tokens;                   // split_tokens % kChunk == 0
-  int d_model, wo_ksplit;
+  int d_model, wo_ksplit, wo_kslice;
   size_t off_qrot, off_qsum, off_part, off_ypart;          // workspace layout (bytes)
-  size_t off_qdig, off_qexp, total;                        // key-side query digits (matrix-core kernel)
+  size_t off_qdig, off_qexp;                               // key-side query digits (matrix-core kernel)
+  size_t off_ot, total;                                    // o laid out for the W_O projection
 };
 DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, int max_seq_len, int d_model,
                             int num_splits);
@@ -92,10 +93,12 @@ hipError_t launch_decode_split_mfma(const DecodePlan &pl, const uint8_t *pages, 
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
                                   int64_t num_tokens, const float *qrot, float *part, hipStream_t stream);
-// Merge splits, inverse value rotation, write out_o.
-hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, hipStream_t stream);
-// out_y = concat(out_o) W_O.
-hipError_t launch_wo_projection(const DecodePlan &pl, const float *o, const void *w_o, int dtype, float *ypart,
+// Merge splits, inverse value rotation, write out_o (and the W_O operand
+// copy `ot` when not null).
+hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, float *ot,
+                          hipStream_t stream);
+// out_y = concat(out_o) W_O, from the copy written by launch_combine.
+hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *ypart,
                                 float *out_y, hipStream_t stream);
 
 // Candidate search helpers.
