@@ -150,7 +150,8 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
   if (mfma)
     KVQ_TRY(launch_decode_split_mfma(pl, cache->pages, cache->num_pages, cache->page_size, page_table,
-                                     max_pages_per_seq, seq_lens, qdig, qexp, qsum, part, stream));
+                                     max_pages_per_seq, seq_lens, qdig, qexp, qsum,
+                                     reinterpret_cast<uint64_t *>(ws + pl.off_tiles), part, stream));
   else
     KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
                                 seq_lens, qrot, qsum, part, stream));
@@ -227,7 +228,8 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
                               L.num_pages, 16, stream));
       if (mfma)
         KVQ_TRY(launch_decode_split_mfma(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
-                                         qdig, qexp, qsum, part, stream));
+                                         qdig, qexp, qsum, reinterpret_cast<uint64_t *>(dec + pl.off_tiles), part,
+                                         stream));
       else
         KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
                                     qrot, qsum, part, stream));

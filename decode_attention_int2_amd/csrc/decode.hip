@@ -707,6 +707,9 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   off = align(off + static_cast<size_t>(num_seqs) * H * 64 * 8 * sizeof(int32_t));
   pl.off_qexp = off;  // [num_seqs][H][4 rows] int32
   off = align(off + static_cast<size_t>(num_seqs) * H * 4 * sizeof(int32_t));
+  pl.tiles_per_seq = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
+  pl.off_tiles = off;  // [num_seqs][tiles_per_seq][2] uint64
+  off = align(off + static_cast<size_t>(num_seqs) * pl.tiles_per_seq * 2 * sizeof(uint64_t));
   pl.total = off;
   return pl;
 }

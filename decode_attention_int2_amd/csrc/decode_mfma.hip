@@ -7,29 +7,34 @@
 //   stored rotated keys; §3 Eq. (1)-(2): softmax over the cached tokens and the
 //   probability-weighted sum of the (rotated) values.
 //
-// Arithmetic (exact integer contractions on the matrix cores):
-//   keys:   dot(q', c_t) with q' in fixed point, Q = round(q' 2^S), |Q| <= 2^26,
-//           written as 4 int8 digits (7 bits each, top digit signed); each
-//           digit is one MFMA column, so one 16x16x64 MFMA contracts 64 key
-//           dims of 16 tokens for 4 query rows x 4 digits.  Codes 0..3 are the
-//           int8 A operand, extracted from the packed bytes with one mask per
-//           2-bit slot; slots 1 and 2 come out multiplied by 4 and 16, which is
-//           divided out of the query digits of those dims.  Digits are
-//           recombined in fp32 by a reduce-scatter inside each 4-lane quad,
-//           after which every lane owns 4 distinct tokens.
-//   values: sum_t w_t c_t with w_t = 2^(logit_t + kappa) s_t rounded to an
-//           integer < 2^28 and split into 4 unsigned 7-bit digits (MFMA
-//           columns); kappa is a per-row power-of-two scale chosen from a
-//           running bound of logit + log2(s) with 2^6 of headroom, so the sums
-//           stay exact int32 in the MFMA accumulators; if the bound outgrows the
-//           headroom the accumulators are flushed to fp32 in LDS (rare) and the
-//           scale moves.  l = sum 2^(logit+kappa) and z = sum 2^(logit+kappa) z_t
-//           stay in fp32 per lane.
-// Loads are branch-free (tiles past the end are clamped into the last valid
-// tile and masked) and the next 64-token block is fetched while the current
-// one is computed.  The per-split result is written in the same
-// (m, l, z, acc[128]) form as the VALU kernel, with m = -kappa, and merged by
-// the same combine kernel.
+// Lane l = 16 g + c of a wave.  A wave takes 64-token blocks (4 tiles of 16).
+// Keys (exact integer products):
+//   q' is held in fixed point, Q = round(q' 2^S), |Q| <= 2^26, as 4 int8
+//   digits (7 bits, top digit signed).  The MFMA's A operand is the digits
+//   (row 4 r + d = digit d of query row r), its B operand the codes of 16
+//   tokens (column = token), k = 64 key dims; codes 0..3 are extracted from
+//   the packed bytes with one mask per 2-bit slot (slots 1 and 2 come out
+//   multiplied by 4 and 16, which the digits divide out).  Lane (c, g) thus
+//   receives the 4 digit sums of query row g against token c of the tile and
+//   forms the logit alone: no cross-lane reduction.
+// Values:
+//   w_t = 2^(logit_t + kappa) s_t rounded to an integer < 2^24 is split into
+//   its 3 bytes; each byte b is fed as the int8 b - 128, and a fourth column
+//   of ones accumulates sum_t c_t to undo the offset.  kappa is a per-row
+//   power-of-two scale chosen from a running bound of logit + log2(s) with
+//   2^2 of headroom; if the bound outgrows it the int32 accumulators are
+//   flushed to fp32 in LDS (rare) and the scale moves.  l = sum 2^(logit +
+//   kappa) and z = sum 2^(logit + kappa) z_t stay in fp32 per lane.  The bytes
+//   reach the MFMA's B layout (column 4 r + byte, k = 16 tokens per lane
+//   group) by a byte transpose inside each lane quad and one lane permutation.
+// Addresses: a small kernel resolves the page of every 16-token tile once per
+// decode step into absolute code / metadata base addresses; the split kernel
+// reads them with scalar loads and issues every vector load as scalar base +
+// per-lane constant offset.  The next 64-token block is fetched while the
+// current one is computed; tiles past the split end are clamped into its last
+// tile and masked.  The per-split result is written in the same (m, l, z,
+// acc[128]) form as the VALU kernel, with m = -kappa, and merged by the same
+// combine kernel.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -38,7 +43,9 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kM0 = 0x03030303u, kM1 = 0x0C0C0C0Cu, kM2 = 0x30303030u;
-constexpr int kHeadroom = 6;  // log2 headroom of the value scale
+constexpr int kHeadroom = 2;       // log2 headroom of the value scale
+constexpr int kWeightBits = 24;    // value weights are integers < 2^24 (3 bytes)
+constexpr uint32_t kByteOffset = 0x01808080u;  // bytes 0-2: b -> b - 128 as int8; byte 3: the ones column
 
 // The 4 code slots of every byte of x as int8 lanes; slot 1 and 2 are scaled by 4 and 16.
 __device__ __forceinline__ v4i slots(uint32_t x) {
@@ -52,43 +59,62 @@ __device__ __forceinline__ float slot_inv(int e) { return e == 1 ? 0.25f : e == 
 
 __device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ float dpp_xor1f(float v) { return __int_as_float(dpp_xor1(__float_as_int(v))); }
-__device__ __forceinline__ float dpp_xor2f(float v) { return __int_as_float(dpp_xor2(__float_as_int(v))); }
+__device__ __forceinline__ int dpp_ror4(int v) { return __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
+__device__ __forceinline__ float fdpp_xor1(float v) { return __int_as_float(dpp_xor1(__float_as_int(v))); }
+__device__ __forceinline__ float fdpp_xor2(float v) { return __int_as_float(dpp_xor2(__float_as_int(v))); }
+__device__ __forceinline__ float fdpp_ror4(float v) { return __int_as_float(dpp_ror4(__float_as_int(v))); }
+__device__ __forceinline__ float fdpp_ror8(float v) { return __int_as_float(dpp_ror8(__float_as_int(v))); }
 
-// max / sum over the 16 lanes of one query row (4 quad lanes x 4 lane groups)
+// max / sum over the 16 lanes of a DPP row (rotations reach every lane of the row)
 __device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_xor1f(x));
-  x = fmaxf(x, dpp_xor2f(x));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+  x = fmaxf(x, fdpp_xor1(x));
+  x = fmaxf(x, fdpp_xor2(x));
+  x = fmaxf(x, fdpp_ror4(x));
+  x = fmaxf(x, fdpp_ror8(x));
   return x;
 }
 __device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_xor1f(x);
-  x += dpp_xor2f(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+  x += fdpp_xor1(x);
+  x += fdpp_xor2(x);
+  x += fdpp_ror4(x);
+  x += fdpp_ror8(x);
   return x;
+}
+
+// 4x4 byte transpose inside each lane quad: afterwards byte j of quad lane x
+// is byte x of quad lane j before.  sel1/sel2 are the lane's v_perm selectors.
+__device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t a, uint32_t sel1, uint32_t sel2) {
+  a = __builtin_amdgcn_perm(static_cast<uint32_t>(dpp_xor1(static_cast<int>(a))), a, sel1);
+  a = __builtin_amdgcn_perm(static_cast<uint32_t>(dpp_xor2(static_cast<int>(a))), a, sel2);
+  return a;
+}
+
+// Sum over tokens of (byte x of W) * code for value-accumulator lane x of a
+// quad (x < 3): the MFMA summed (byte - 128) * code, the quad's lane 3 holds
+// sum code; the correction is applied in int32 (|.| < 2^31 over a split) so
+// that no large offset is cancelled in fp32.  Lane x = 3 yields 0.
+__device__ __forceinline__ int byte_sum(int d, int x) {
+  const int ones = __builtin_amdgcn_mov_dpp(d, 0xFF, 0xF, 0xF, false);  // quad lane 3
+  return x < 3 ? d + 128 * ones : 0;
 }
 
 struct MfmaArgs {
   int R, G, Hq, H, Nq;
   int split_tokens, splits, max_seq_len;
-  const uint8_t *pages;
-  int64_t num_pages;
   int P;
-  const int32_t *page_table;
-  int max_pages;
+  int tiles_per_seq;
   const int32_t *seq_lens;
-  const int32_t *qdig;  // [num_seqs][H][64 lanes][8] key-side B operand
-  const int32_t *qexp;  // [num_seqs][H][4 rows] fixed-point shift S of each query row
+  const int32_t *qdig;     // [num_seqs][H][64 lanes][8] key-side A operand
+  const int32_t *qexp;     // [num_seqs][H][4 rows] fixed-point shift S of each query row
   const float *qsum;
+  const uint64_t *tiles;   // [num_seqs][tiles_per_seq][2] code base, metadata base (bit 0: bad page)
   float *part;
 };
 
 // Fixed-point digits of the rotated queries of one (sequence, KV head): lane
-// (col, grp) gets the 8 dwords of its B-operand column (row col/4, digit col%4)
-// for the two 64-dim MFMAs.  Dim 16*(2*grp + m) + 4*bb + e goes to dword
+// (col, grp) gets the 8 dwords of its A-operand row (query row col/4, digit
+// col%4) for the two 64-dim MFMAs.  Dim 16*(2*grp + m) + 4*bb + e goes to dword
 // [m][e], byte bb; slot e of the unpacked codes carries a factor 1/slot_inv(e),
 // which is divided out here.  Q = round(q' 2^S) with |Q| <= 2^26.
 __global__ __launch_bounds__(64) void query_digits_kernel(const float *qrot, int R, int G, int Hq, int H, int Nq,
@@ -132,56 +158,104 @@ __global__ __launch_bounds__(64) void query_digits_kernel(const float *qrot, int
   if (grp == 0 && dg == 0) qexp[static_cast<size_t>(bh) * 4 + hr] = qshift;
 }
 
+// Absolute addresses of every 16-token tile of every sequence (head 0 of its
+// page; the head's offset is part of the lanes' constant offsets):
+//   [0] page block + 32 * (position of the tile in its page)   K/V codes
+//   [1] page block + 64 P + 4 * (position)                     K/V metadata
+// A page index outside the cache is replaced by page 0 and flagged in bit 0
+// of the metadata address.
+__global__ __launch_bounds__(256) void tile_table_kernel(const uint8_t *pages, int64_t num_pages, int P, int H,
+                                                         const int32_t *page_table, int max_pages,
+                                                         int tiles_per_seq, uint64_t *tiles) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= tiles_per_seq) return;
+  const int pi = (16 * i) / P, off = (16 * i) % P;
+  int64_t p = (page_table && pi < max_pages) ? static_cast<int64_t>(page_table[static_cast<size_t>(b) * max_pages + pi])
+                                             : static_cast<int64_t>(b) * max_pages + pi;
+  uint64_t flag = 0;
+  if (pi >= max_pages || p < 0 || p >= num_pages) {
+    p = 0;
+    flag = 1;
+  }
+  const uint64_t blk = reinterpret_cast<uint64_t>(pages) + static_cast<uint64_t>(p) * H * 72 * P;
+  uint64_t *e = tiles + (static_cast<size_t>(b) * tiles_per_seq + i) * 2;
+  e[0] = blk + 32 * off;
+  e[1] = (blk + 64 * static_cast<uint64_t>(P) + 4 * off) | flag;
+}
+
 constexpr int kWaves = 4;
 constexpr int kBlk = 64;  // tokens per wave iteration (4 tiles of 16)
-constexpr int kMaxSplitTiles = kMaxMfmaSplitTokens / 16;
-constexpr int kSlackTiles = (kWaves * kBlk) / 16 + 4;  // page ids read past the split end by the prefetch
 
 // Per-lane data of one 64-token block.
 struct Blk {
-  uint2 kc[4];        // K codes: token `col` of tile q, bytes 8*grp .. 8*grp+7
-  uint32_t vx[4][2];  // V codes: 4-group `grp` of tile q, dwords 2*col and 2*col+1 (dims 8*col..8*col+7)
-  uint4 km, vm;       // K / V metadata of tokens 4*grp..4*grp+3 of tile dg
+  uint2 kc[4];      // K codes of token c of tile q, bytes 8g .. 8g+7
+  uint2 vx[4];      // V codes of 4-token group g of tile q, dims 8c .. 8c+7
+  uint32_t km[4];   // K metadata of token c of tile q
+  uint32_t vm[4];   // V metadata of token c of tile q
+};
+
+struct Addr {
+  uint64_t code[4], meta[4];
 };
 
 struct Ctx {
   const MfmaArgs *a;
-  int b, h, col, grp, dg;
-  int t_end, t_last;  // t_last: first token of the last tile that holds a valid token
-  size_t block_bytes;
+  const uint64_t *tab;  // this sequence's tile table
+  int last_tile;        // last tile index of the split (loads clamp into it)
+  int t_end;
+  int c, g;
+  uint32_t vo_k, vo_v, vo_km, vo_vm;  // per-lane constant byte offsets
 };
 
-// Page ids of the split's 16-token tiles, validated and clamped into the last
-// valid tile, are staged in shared memory by the workgroup prologue.
-__device__ __forceinline__ void load_block(const Ctx &c, int t0, const int *tile_page, int t_begin, Blk &o) {
-  const MfmaArgs &a = *c.a;
-  const uint8_t *bp[4];
-  int off[4];
-  const int4 pid = *reinterpret_cast<const int4 *>(tile_page + (t0 - t_begin) / 16);
-  const int pids[4] = {pid.x, pid.y, pid.z, pid.w};
+__device__ __forceinline__ void load_addr(const Ctx &c, int t0, Addr &ad) {
+  // the table is read-only for the kernel's lifetime: constant address space, scalar loads
+  const __attribute__((address_space(4))) uint64_t *tab =
+      (const __attribute__((address_space(4))) uint64_t *)(reinterpret_cast<uintptr_t>(c.tab));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int tt = min(t0 + 16 * q, c.t_last);  // clamped into a valid tile (masked later)
-    off[q] = static_cast<int>(static_cast<unsigned>(tt) % static_cast<unsigned>(a.P));
-    bp[q] = a.pages + (static_cast<size_t>(pids[q]) * a.H + c.h) * c.block_bytes;
+    const int idx = min(t0 / 16 + q, c.last_tile);
+    ad.code[q] = tab[2 * idx];
+    ad.meta[q] = tab[2 * idx + 1];
   }
+}
+
+// global-memory pointers (address space 1): scalar base + 32-bit lane offset
+typedef const __attribute__((address_space(1))) uint8_t *gbyte_ptr;
+__device__ __forceinline__ uint2 gload_u64(gbyte_ptr base, uint32_t off) {
+  const uint64_t v = *reinterpret_cast<const __attribute__((address_space(1))) uint64_t *>(base + off);
+  return uint2{static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32)};
+}
+__device__ __forceinline__ uint32_t gload_u32(gbyte_ptr base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t *>(base + off);
+}
+
+__device__ __forceinline__ void load_block(const Ctx &c, const Addr &ad, Blk &o, bool &bad) {
+  // (the empty asm keeps the 32-bit offsets in this block, so that the
+  // loads are selected as scalar base + 32-bit VGPR offset)
+  uint32_t vo_k = c.vo_k, vo_v = c.vo_v, vo_km = c.vo_km, vo_vm = c.vo_vm;
+  asm volatile("" : "+v"(vo_k), "+v"(vo_v), "+v"(vo_km), "+v"(vo_vm));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    o.kc[q] = *reinterpret_cast<const uint2 *>(bp[q] + 32 * (off[q] + c.col) + 8 * c.grp);
-    const uint2 v = *reinterpret_cast<const uint2 *>(bp[q] + 32 * a.P + 128 * ((off[q] >> 2) + c.grp) + 8 * c.col);
-    o.vx[q][0] = v.x;
-    o.vx[q][1] = v.y;
+    const gbyte_ptr cb = reinterpret_cast<gbyte_ptr>(ad.code[q]);
+    const gbyte_ptr mb = reinterpret_cast<gbyte_ptr>(ad.meta[q] & ~static_cast<uint64_t>(1));
+    bad = bad || (ad.meta[q] & 1) != 0;
+    o.kc[q] = gload_u64(cb, vo_k);
+    o.vx[q] = gload_u64(cb, vo_v);
+    o.km[q] = gload_u32(mb, vo_km);
+    o.vm[q] = gload_u32(mb, vo_vm);
   }
-  const uint8_t *ob = c.dg == 0 ? bp[0] : c.dg == 1 ? bp[1] : c.dg == 2 ? bp[2] : bp[3];
-  const int oo = c.dg == 0 ? off[0] : c.dg == 1 ? off[1] : c.dg == 2 ? off[2] : off[3];
-  o.km = *reinterpret_cast<const uint4 *>(ob + 64 * a.P + 4 * (oo + 4 * c.grp));
-  o.vm = *reinterpret_cast<const uint4 *>(ob + 68 * a.P + 4 * (oo + 4 * c.grp));
 }
 
 struct State {
-  v4i bk[2];        // key-side B operand (query digits), dims half m
-  float qsum;       // sum of q' (for the zero-point term)
-  float unscale;    // weight of this lane's key digit / 2^S
+  v4i bk[2];        // key-side A operand (query digits), dims half m
+  float qsum;       // sum of q' of this lane's query row (zero-point term)
+  float unscale;    // 2^-S of this lane's query row
+  bool row_ok;
+  uint32_t sel1, sel2;  // byte-transpose selectors
+  int src_lane4;        // 4 * lane whose bytes this lane takes for the value operand
+  int krow_lane4;       // 4 * a lane of the query row of this lane's value accumulators
+  int vx_lane;          // this lane's column within its quad (byte index, 3 = ones)
   v4i accv[8];      // value accumulators (int32, MFMA), 16 dims each
   float lsum, zsum;
   int kappa;
@@ -189,53 +263,29 @@ struct State {
 };
 
 __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &blk, State &st, float *facc) {
-  // ---- key side: 2 MFMAs per tile (64 dims each)
-  v4i dk[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    dk[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(slots(blk.kc[q].x), st.bk[0], v4i{0, 0, 0, 0}, 0, 0, 0);
-    dk[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(slots(blk.kc[q].y), st.bk[1], dk[q], 0, 0, 0);
-  }
-  // ---- digits -> fp32, reduce-scatter inside the quad: lane keeps tile dg
-  const bool hiA = (c.dg & 2) != 0, hiB = (c.dg & 1) != 0;
-  float k2[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float lo = static_cast<float>(dk[j][r]) * st.unscale;
-      const float hi = static_cast<float>(dk[j + 2][r]) * st.unscale;
-      const float send = hiA ? lo : hi;
-      const float keep = hiA ? hi : lo;
-      k2[j][r] = keep + dpp_xor2f(send);
-    }
-  float dot[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float send = hiB ? k2[0][r] : k2[1][r];
-    const float keep = hiB ? k2[1][r] : k2[0][r];
-    dot[r] = keep + dpp_xor1f(send);
-  }
-
-  // ---- logits of the 4 owned tokens (base-2 units); bound u = logit + log2 bound of s_v
+  // ---- keys: lane (c, g) gets the 4 digit sums of query row g and token (q, c)
   float logit[4], sv[4], zv[4];
   float umax = -INFINITY;
-  const uint32_t kmw[4] = {blk.km.x, blk.km.y, blk.km.z, blk.km.w};
-  const uint32_t vmw[4] = {blk.vm.x, blk.vm.y, blk.vm.z, blk.vm.w};
-  const int tok0 = t0 + 16 * c.dg + 4 * c.grp;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float ks = half_bits_to_float(kmw[r] & 0xffffu), kz = half_bits_to_float(kmw[r] >> 16);
-    sv[r] = half_bits_to_float(vmw[r] & 0xffffu);
-    zv[r] = half_bits_to_float(vmw[r] >> 16);
-    logit[r] = (tok0 + r < c.t_end) ? dot[r] * ks + kz * st.qsum : -INFINITY;
-    const int es = static_cast<int>((vmw[r] >> 10) & 31u) - 14;  // s_v < 2^es
-    umax = fmaxf(umax, logit[r] + static_cast<float>(es));
+  for (int q = 0; q < 4; ++q) {
+    v4i dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.bk[0], slots(blk.kc[q].x), v4i{0, 0, 0, 0}, 0, 0, 0);
+    dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.bk[1], slots(blk.kc[q].y), dk, 0, 0, 0);
+    const int low = (dk[2] << 7) + dk[3];  // |.| < 2^26: no int32 overflow
+    const float dot = fmaf(static_cast<float>(dk[0]), 2097152.0f,
+                           fmaf(static_cast<float>(dk[1]), 16384.0f, static_cast<float>(low)));
+    const float ks = half_bits_to_float(blk.km[q] & 0xffffu), kz = half_bits_to_float(blk.km[q] >> 16);
+    sv[q] = half_bits_to_float(blk.vm[q] & 0xffffu);
+    zv[q] = half_bits_to_float(blk.vm[q] >> 16);
+    const bool valid = st.row_ok && (t0 + 16 * q + c.c < c.t_end);
+    logit[q] = valid ? dot * (ks * st.unscale) + kz * st.qsum : -INFINITY;
+    int es;
+    (void)frexpf(sv[q], &es);  // s_v < 2^es
+    umax = fmaxf(umax, logit[q] + static_cast<float>(es));
   }
   umax = row16_max(umax);
   int need = st.kappa;
   if (umax != -INFINITY) {
-    need = 27 - static_cast<int>(ceilf(umax));
+    need = (kWeightBits - 1) - static_cast<int>(ceilf(umax));
     if (!st.have_ref) {
       st.kappa = need - kHeadroom;
       st.have_ref = true;
@@ -244,13 +294,15 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
   // wave-uniform decision: flush when any row outgrew its headroom
   if (__any(st.have_ref && need < st.kappa)) {
     const int newk = (st.have_ref && need < st.kappa) ? need - kHeadroom : st.kappa;
-    const float f2 = ldexpf(1.0f, newk - st.kappa);
+    const float f2 = ldexpf(1.0f, newk - st.kappa);  // factor of query row g
+    // the value accumulators of this lane belong to query row (c >> 2)
+    const float f2v = __int_as_float(__builtin_amdgcn_ds_bpermute(st.krow_lane4, __float_as_int(f2)));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float *p = facc + (4 * i + r) * 64;
-        *p = (*p + static_cast<float>(st.accv[i][r])) * f2;
+        *p = (*p + static_cast<float>(byte_sum(st.accv[i][r], st.vx_lane))) * f2v;
       }
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.accv[i] = v4i{0, 0, 0, 0};
@@ -258,44 +310,38 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     st.zsum *= f2;
     st.kappa = newk;
   }
-  // ---- weights: p = 2^(logit + kappa), W = round(p s_v) < 2^28, 4 digits packed per tile
-  uint32_t dw[4] = {0, 0, 0, 0};
+  // ---- weights W = round(2^(logit + kappa) s_v) < 2^24, bytes offset to int8
   const float kf = static_cast<float>(st.kappa);
+  uint32_t w[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float p = exp2f(logit[r] + kf);
+  for (int q = 0; q < 4; ++q) {
+    const float p = exp2f(logit[q] + kf);
     st.lsum += p;
-    st.zsum += p * zv[r];
-    const uint32_t W = static_cast<uint32_t>(p * sv[r] + 0.5f);
-    dw[0] |= __builtin_amdgcn_ubfe(W, 21, 7) << (8 * r);
-    dw[1] |= __builtin_amdgcn_ubfe(W, 14, 7) << (8 * r);
-    dw[2] |= __builtin_amdgcn_ubfe(W, 7, 7) << (8 * r);
-    dw[3] |= (W & 127u) << (8 * r);
+    st.zsum += p * zv[q];
+    const uint32_t W = static_cast<uint32_t>(fmaf(p, sv[q], 0.5f));
+    w[q] = W ^ kByteOffset;
   }
-  // quad transpose: lane dg gets digit dg of every tile (dword q from quad lane q)
-  {
-    const bool odd = (c.dg & 1) != 0, hi2 = (c.dg & 2) != 0;
-    const uint32_t x0 = dpp_xor1(dw[0]), x1 = dpp_xor1(dw[1]), x2 = dpp_xor1(dw[2]), x3 = dpp_xor1(dw[3]);
-    const uint32_t t0v = odd ? x1 : dw[0], t1v = odd ? dw[1] : x0, t2v = odd ? x3 : dw[2], t3v = odd ? dw[3] : x2;
-    const uint32_t y0 = dpp_xor2(t0v), y1 = dpp_xor2(t1v), y2 = dpp_xor2(t2v), y3 = dpp_xor2(t3v);
-    dw[0] = hi2 ? y2 : t0v;
-    dw[1] = hi2 ? y3 : t1v;
-    dw[2] = hi2 ? t2v : y0;
-    dw[3] = hi2 ? t3v : y1;
+  // quad lane x takes byte x (digit x, or the ones for x = 3) of its quad's 4 tokens;
+  // then the lanes move to the B layout: column 4 r + x, k-slice = token group
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    w[q] = quad_byte_transpose(w[q], st.sel1, st.sel2);
+    w[q] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(st.src_lane4, static_cast<int>(w[q])));
   }
-  const v4i bv{static_cast<int>(dw[0]), static_cast<int>(dw[1]), static_cast<int>(dw[2]), static_cast<int>(dw[3])};
+  const v4i bv{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
 
-  // ---- value side: 8 MFMAs (16 dims each), k = the 64 tokens of the block
+  // ---- values: 8 MFMAs (16 dims each), k = the 64 tokens of the block
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const v4i av{slot(blk.vx[0][hf], e), slot(blk.vx[1][hf], e), slot(blk.vx[2][hf], e), slot(blk.vx[3][hf], e)};
+      const uint32_t x0 = hf ? blk.vx[0].y : blk.vx[0].x, x1 = hf ? blk.vx[1].y : blk.vx[1].x;
+      const uint32_t x2 = hf ? blk.vx[2].y : blk.vx[2].x, x3 = hf ? blk.vx[3].y : blk.vx[3].x;
+      const v4i av{slot(x0, e), slot(x1, e), slot(x2, e), slot(x3, e)};
       st.accv[4 * hf + e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, st.accv[4 * hf + e], 0, 0, 0);
     }
 }
 
-template <bool kPaged>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float red[kWaves][4][4 + D];  // per wave, per row: m, l, z, flag, acc[128]
   __shared__ float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
@@ -304,12 +350,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   const int lane = threadIdx.x & 63;
   Ctx c;
   c.a = &a;
-  c.b = b;
-  c.h = h;
-  c.col = lane & 15;
-  c.grp = lane >> 4;
-  c.dg = c.col & 3;
-  const int hr = c.col >> 2;  // query row of this lane's column
+  c.c = lane & 15;
+  c.g = lane >> 4;
   float *facc = &facc_all[wave][lane];
 
   int L = a.seq_lens[b];
@@ -317,23 +359,37 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   if (bad) L = 0;
   const int t_begin = s * a.split_tokens;
   c.t_end = min(t_begin + a.split_tokens, L);
-  c.t_last = c.t_end > 0 ? ((c.t_end - 1) / 16) * 16 : 0;
-  c.block_bytes = static_cast<size_t>(72) * a.P;
+  c.last_tile = c.t_end > t_begin ? (c.t_end - 1) / 16 : t_begin / 16;
+  c.tab = a.tiles + static_cast<size_t>(b) * a.tiles_per_seq * 2;
+  const uint32_t hoff = static_cast<uint32_t>(h) * 72u * static_cast<uint32_t>(a.P);
+  c.vo_k = hoff + 32u * c.c + 8u * c.g;
+  c.vo_v = hoff + 32u * a.P + 128u * c.g + 8u * c.c;
+  c.vo_km = hoff + 4u * c.c;
+  c.vo_vm = hoff + 4u * a.P + 4u * c.c;
 
-  // ---- precomputed query digits of this lane's column (key-side B operand)
+  // ---- query digits (key-side A operand: row c = 4 r + d, k-slice g) and this lane's query row g
   State st;
-  const bool row_ok = hr < a.R;
-  const int qi = hr / a.G, gh = hr % a.G;
-  const size_t rj = (static_cast<size_t>(b) * a.Nq + qi) * a.Hq + h * a.G + gh;
   {
     const int4 *dsrc = reinterpret_cast<const int4 *>(a.qdig + ((static_cast<size_t>(b) * a.H + h) * 64 + lane) * 8);
     const int4 d0 = dsrc[0], d1 = dsrc[1];
     st.bk[0] = v4i{d0.x, d0.y, d0.z, d0.w};
     st.bk[1] = v4i{d1.x, d1.y, d1.z, d1.w};
   }
-  const int qshift = a.qexp[(static_cast<size_t>(b) * a.H + h) * 4 + hr];
-  st.qsum = row_ok ? a.qsum[rj] : 0.0f;
-  st.unscale = ldexpf(1.0f, 21 - 7 * c.dg - qshift);
+  const int hr = c.g;  // query row of the key-side lanes
+  st.row_ok = hr < a.R;
+  {
+    const int qi = hr / a.G, gh = hr % a.G;
+    const size_t rj = (static_cast<size_t>(b) * a.Nq + qi) * a.Hq + h * a.G + gh;
+    st.qsum = st.row_ok ? a.qsum[rj] : 0.0f;
+    st.unscale = ldexpf(1.0f, -a.qexp[(static_cast<size_t>(b) * a.H + h) * 4 + hr]);
+  }
+  const int x = lane & 3;
+  st.sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
+  st.sel2 = (x & 2) ? 0x03020706u : 0x05040100u;
+  // value operand lane 16 g' + 4 r + x takes from lane 16 r + 4 g' + x
+  st.src_lane4 = 4 * (16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + x);
+  st.krow_lane4 = 4 * (16 * ((lane >> 2) & 3));
+  st.vx_lane = x;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.accv[i] = v4i{0, 0, 0, 0};
   st.lsum = st.zsum = 0.0f;
@@ -342,68 +398,50 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) facc[i * 64] = 0.0f;
 
-  // ---- page id of every 16-token tile of the split, validated; entries past
-  // the end (read by the over-fetch of the last block) clamp to the last tile
-  __shared__ __attribute__((aligned(16))) int tile_page[kMaxSplitTiles + kSlackTiles];
-  __shared__ int page_fault;
-  if (threadIdx.x == 0) page_fault = 0;
-  __syncthreads();
-  if (c.t_end > t_begin) {
-    const int n_fill = (c.t_end - t_begin + 15) / 16 + kSlackTiles;
-    for (int i = threadIdx.x; i < n_fill; i += 256) {
-      const int tt = min(t_begin + 16 * i, c.t_last);
-      const int pi = tt / a.P;
-      int64_t p = kPaged ? static_cast<int64_t>(a.page_table[static_cast<size_t>(b) * a.max_pages + pi])
-                         : static_cast<int64_t>(b) * a.max_pages + pi;
-      if (p < 0 || p >= a.num_pages) {
-        page_fault = 1;
-        p = 0;
-      }
-      tile_page[i] = static_cast<int>(p);
-    }
-  }
-  __syncthreads();
-  if (page_fault) bad = true;
-
-  // ---- main loop: wave w takes blocks w, w+4, ...; the next block is always
-  // fetched while the current one is computed (past the end it re-reads the
-  // clamped last tile, which is masked)
-  // (the trip count is fixed up front so the loop has a single exit and the
-  // prefetched block is the only load in flight across the back edge)
+  // ---- main loop: wave w takes blocks w, w+4, ...; block i+1 is in flight
+  // while block i is computed and the addresses of block i+2 are fetched
   constexpr int kStride = kWaves * kBlk;
   int t0 = t_begin + wave * kBlk;
   const int n_blk = t0 < c.t_end ? (c.t_end - t0 + kStride - 1) / kStride : 0;
   if (n_blk > 0) {
     Blk b0, b1;
-    load_block(c, t0, tile_page, t_begin, b0);
+    Addr a0, a1;
+    load_addr(c, t0, a0);
+    load_block(c, a0, b0, bad);
+    load_addr(c, t0 + kStride, a1);
     for (int i = 0; i < n_blk / 2; ++i) {
-      load_block(c, t0 + kStride, tile_page, t_begin, b1);
+      load_block(c, a1, b1, bad);
+      load_addr(c, t0 + 2 * kStride, a0);
       compute_block(c, t0, b0, st, facc);
-      load_block(c, t0 + 2 * kStride, tile_page, t_begin, b0);
+      load_block(c, a0, b0, bad);
+      load_addr(c, t0 + 3 * kStride, a1);
       compute_block(c, t0 + kStride, b1, st, facc);
       t0 += 2 * kStride;
     }
     if (n_blk & 1) compute_block(c, t0, b0, st, facc);
   }
 
-  // ---- per-wave result for each row: totals over the row's 16 lanes, digits recombined
+  // ---- per-wave result for each row
   const float lrow = row16_sum(st.lsum);
   const float zrow = row16_sum(st.zsum);
-  const float wdig = ldexpf(1.0f, 21 - 7 * c.dg);
   const bool any_bad = __any(bad);
+  // value accumulators: lane (4 r + x, g') holds column x (byte x, or the
+  // ones for x = 3) of query row r for dims 8 (4 g' + i) + 4 hf + e
+  const int vr = (lane >> 2) & 3;
+  const float wbyte = x == 0 ? 1.0f : x == 1 ? 256.0f : x == 2 ? 65536.0f : 0.0f;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * hf + e;
-        float x = (facc[(4 * i + r) * 64] + static_cast<float>(st.accv[i][r])) * (wdig * slot_inv(e));
-        x += dpp_xor1f(x);
-        x += dpp_xor2f(x);
-        if (c.dg == 0 && row_ok) red[wave][hr][4 + 8 * (4 * c.grp + r) + 4 * hf + e] = x;
+      for (int i = 0; i < 4; ++i) {
+        const int k = 4 * hf + e;
+        float v = (facc[(4 * k + i) * 64] + static_cast<float>(byte_sum(st.accv[k][i], x))) * (wbyte * slot_inv(e));
+        v += fdpp_xor1(v);
+        v += fdpp_xor2(v);
+        if (x == 0 && vr < a.R) red[wave][vr][4 + 8 * (4 * c.g + i) + 4 * hf + e] = v;
       }
-  if (c.dg == 0 && c.grp == 0 && row_ok) {
+  if (c.c == 0 && st.row_ok) {
     red[wave][hr][0] = st.have_ref ? -static_cast<float>(st.kappa) : -INFINITY;
     red[wave][hr][1] = lrow;
     red[wave][hr][2] = zrow;
@@ -417,18 +455,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
     float mstar = -INFINITY;
     bool nan = false;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      mstar = fmaxf(mstar, red[w][r][0]);
-      nan = nan || red[w][r][3] != 0.0f;
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      mstar = fmaxf(mstar, red[w2][r][0]);
+      nan = nan || red[w2][r][3] != 0.0f;
     }
     float l = 0.0f, z = 0.0f, acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (red[w][r][0] == -INFINITY) continue;
-      const float sc = exp2f(red[w][r][0] - mstar);
-      l += sc * red[w][r][1];
-      z += sc * red[w][r][2];
-      acc += sc * red[w][r][4 + i];
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      if (red[w2][r][0] == -INFINITY) continue;
+      const float sc = exp2f(red[w2][r][0] - mstar);
+      l += sc * red[w2][r][1];
+      z += sc * red[w2][r][2];
+      acc += sc * red[w2][r][4 + i];
     }
     const int qq = r / a.G, g2 = r % a.G;
     const size_t row = static_cast<size_t>(b) * a.Nq + qq;
@@ -446,7 +484,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
 }  // namespace
 
 bool decode_mfma_supported(const DecodePlan &pl, int page_size) {
-  return pl.rows_per_head <= 4 && page_size % 16 == 0;
+  return pl.rows_per_head <= 4 && page_size % 16 == 0 &&
+         static_cast<int64_t>(pl.H) * 72 * page_size < (static_cast<int64_t>(1) << 31);
 }
 
 hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t *qdig, int32_t *qexp,
@@ -460,9 +499,14 @@ hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t 
 
 hipError_t launch_decode_split_mfma(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
                                     const int32_t *page_table, int max_pages, const int32_t *seq_lens,
-                                    const int32_t *qdig, const int32_t *qexp, const float *qsum, float *part,
-                                    hipStream_t stream) {
+                                    const int32_t *qdig, const int32_t *qexp, const float *qsum, uint64_t *tiles,
+                                    float *part, hipStream_t stream) {
   if (pl.num_seqs == 0) return hipSuccess;
+  const int tps = pl.tiles_per_seq;
+  hipLaunchKernelGGL(tile_table_kernel, dim3((tps + 255) / 256, pl.num_seqs), dim3(256), 0, stream, pages, num_pages,
+                     page_size, pl.H, page_table, max_pages, tps, tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   MfmaArgs a{};
   a.R = pl.rows_per_head;
   a.G = pl.G;
@@ -472,20 +516,15 @@ hipError_t launch_decode_split_mfma(const DecodePlan &pl, const uint8_t *pages, 
   a.split_tokens = pl.split_tokens;
   a.splits = pl.splits;
   a.max_seq_len = pl.max_seq_len;
-  a.pages = pages;
-  a.num_pages = num_pages;
   a.P = page_size;
-  a.page_table = page_table;
-  a.max_pages = max_pages;
+  a.tiles_per_seq = tps;
   a.seq_lens = seq_lens;
   a.qdig = qdig;
   a.qexp = qexp;
   a.qsum = qsum;
+  a.tiles = tiles;
   a.part = part;
-  if (page_table)
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(pl.splits, pl.H, pl.num_seqs), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(pl.splits, pl.H, pl.num_seqs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_mfma_kernel, dim3(pl.splits, pl.H, pl.num_seqs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -67,7 +67,9 @@ struct DecodePlan {
   int d_model, wo_ksplit, wo_kslice;
   size_t off_qrot, off_qsum, off_part, off_ypart;          // workspace layout (bytes)
   size_t off_qdig, off_qexp;                               // key-side query digits (matrix-core kernel)
-  size_t off_ot, total;                                    // o laid out for the W_O projection
+  size_t off_ot;                                           // o laid out for the W_O projection
+  int tiles_per_seq;                                       // 16-token tiles per sequence
+  size_t off_tiles, total;                                 // tile address table (matrix-core kernel)
 };
 DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, int max_seq_len, int d_model,
                             int num_splits);
@@ -85,10 +87,11 @@ bool decode_mfma_supported(const DecodePlan &pl, int page_size);
 // (sequence, KV head) (prologue of the matrix-core kernel).
 hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t *qdig, int32_t *qexp,
                                hipStream_t stream);
+// (resolves the page of every tile into `tiles`, then runs the split kernel)
 hipError_t launch_decode_split_mfma(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
                                     const int32_t *page_table, int max_pages, const int32_t *seq_lens,
-                                    const int32_t *qdig, const int32_t *qexp, const float *qsum, float *part,
-                                    hipStream_t stream);
+                                    const int32_t *qdig, const int32_t *qexp, const float *qsum, uint64_t *tiles,
+                                    float *part, hipStream_t stream);
 // Split-K partial attention over raw (unquantized, unrotated) K and V that
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
