@@ -189,7 +189,7 @@ def main():
         "decode_call_us": round(decode_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel", "algorithmic_bytes_per_launch": kv_bytes},
+                     "kernel": "decode_mfma_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": base,
     }
     print(json.dumps(out))

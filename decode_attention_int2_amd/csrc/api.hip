@@ -145,13 +145,16 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   int32_t *qdig = reinterpret_cast<int32_t *>(ws + pl.off_qdig);
   int32_t *qexp = reinterpret_cast<int32_t *>(ws + pl.off_qexp);
   const bool mfma = decode_mfma_supported(pl, cache->page_size);
+  uint64_t *tiles = reinterpret_cast<uint64_t *>(ws + pl.off_tiles);
   KVQ_TRY(launch_query_rotation(q, dtype, pl, to_dev(*rot_k), qrot, qsum, stream));
-  if (mfma) KVQ_TRY(launch_query_digits(pl, qrot, qdig, qexp, stream));
+  if (mfma) {
+    KVQ_TRY(launch_query_digits(pl, qrot, qdig, qexp, stream));
+    KVQ_TRY(launch_tile_table(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
+                              tiles, stream));
+  }
   if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
   if (mfma)
-    KVQ_TRY(launch_decode_split_mfma(pl, cache->pages, cache->num_pages, cache->page_size, page_table,
-                                     max_pages_per_seq, seq_lens, qdig, qexp, qsum,
-                                     reinterpret_cast<uint64_t *>(ws + pl.off_tiles), part, stream));
+    KVQ_TRY(launch_decode_split_mfma(pl, cache->page_size, seq_lens, qdig, qexp, qsum, tiles, part, stream));
   else
     KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
                                 seq_lens, qrot, qsum, part, stream));
@@ -209,6 +212,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   float *part = reinterpret_cast<float *>(dec + pl.off_part);
   int32_t *qdig = reinterpret_cast<int32_t *>(dec + pl.off_qdig);
   int32_t *qexp = reinterpret_cast<int32_t *>(dec + pl.off_qexp);
+  uint64_t *tiles = reinterpret_cast<uint64_t *>(dec + pl.off_tiles);
   const bool mfma = decode_mfma_supported(pl, 16);
   const RotDev ident{KVQ_ROT_IDENTITY, nullptr, nullptr};
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
@@ -223,13 +227,13 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
     const RotDev rot = to_dev(candidates[r]);
     KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
     if (mfma) KVQ_TRY(launch_query_digits(pl, qrot, qdig, qexp, stream));
+    if (mfma && r == 0)
+      KVQ_TRY(launch_tile_table(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), tiles, stream));
     for (int i = 0; i < num_clips; ++i) {
       KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips[i], clips[i], pages,
                               L.num_pages, 16, stream));
       if (mfma)
-        KVQ_TRY(launch_decode_split_mfma(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
-                                         qdig, qexp, qsum, reinterpret_cast<uint64_t *>(dec + pl.off_tiles), part,
-                                         stream));
+        KVQ_TRY(launch_decode_split_mfma(pl, 16, seq_len, qdig, qexp, qsum, tiles, part, stream));
       else
         KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
                                     qrot, qsum, part, stream));

@@ -667,11 +667,19 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   const int max_chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   int splits = num_splits;
   if (splits <= 0) {
-    // enough workgroups to fill 256 CUs several times; the matrix-core kernel
-    // (<= 4 rows per KV head) runs 4 waves per workgroup on longer splits
+    // The matrix-core kernel (<= 4 rows per KV head): ~2 workgroups of 4
+    // waves per CU, all resident at once (a partial second round of
+    // workgroups would run the tail at low occupancy), and splits of at least
+    // 1024 tokens so the per-split prologue and merge stay small.  The VALU
+    // kernel: enough workgroups to fill 256 CUs several times.
     const int units = num_seqs * H > 0 ? num_seqs * H : 1;
-    const int target = (queries_per_seq * (Hq / H) <= 4) ? 1024 : 4096;
+    const bool mfma_path = queries_per_seq * (Hq / H) <= 4;
+    const int target = mfma_path ? 512 : 4096;
     splits = (target + units - 1) / units;
+    if (mfma_path) {
+      const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens
+      if (splits > max_by_len) splits = max_by_len;
+    }
   }
   if (splits > max_chunks) splits = max_chunks;
   if (splits > kMaxCombineSplits) splits = kMaxCombineSplits;

@@ -497,16 +497,20 @@ hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_split_mfma(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
-                                    const int32_t *page_table, int max_pages, const int32_t *seq_lens,
-                                    const int32_t *qdig, const int32_t *qexp, const float *qsum, uint64_t *tiles,
-                                    float *part, hipStream_t stream) {
+hipError_t launch_tile_table(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
+                             const int32_t *page_table, int max_pages, uint64_t *tiles, hipStream_t stream) {
   if (pl.num_seqs == 0) return hipSuccess;
   const int tps = pl.tiles_per_seq;
   hipLaunchKernelGGL(tile_table_kernel, dim3((tps + 255) / 256, pl.num_seqs), dim3(256), 0, stream, pages, num_pages,
                      page_size, pl.H, page_table, max_pages, tps, tiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const int32_t *seq_lens,
+                                    const int32_t *qdig, const int32_t *qexp, const float *qsum,
+                                    const uint64_t *tiles, float *part, hipStream_t stream) {
+  if (pl.num_seqs == 0) return hipSuccess;
+  const int tps = pl.tiles_per_seq;
   MfmaArgs a{};
   a.R = pl.rows_per_head;
   a.G = pl.G;

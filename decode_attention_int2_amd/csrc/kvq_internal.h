@@ -87,11 +87,13 @@ bool decode_mfma_supported(const DecodePlan &pl, int page_size);
 // (sequence, KV head) (prologue of the matrix-core kernel).
 hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t *qdig, int32_t *qexp,
                                hipStream_t stream);
-// (resolves the page of every tile into `tiles`, then runs the split kernel)
-hipError_t launch_decode_split_mfma(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
-                                    const int32_t *page_table, int max_pages, const int32_t *seq_lens,
-                                    const int32_t *qdig, const int32_t *qexp, const float *qsum, uint64_t *tiles,
-                                    float *part, hipStream_t stream);
+// Absolute code / metadata addresses of every 16-token tile (prologue of the
+// matrix-core kernel; page indices are validated here).
+hipError_t launch_tile_table(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
+                             const int32_t *page_table, int max_pages, uint64_t *tiles, hipStream_t stream);
+hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const int32_t *seq_lens,
+                                    const int32_t *qdig, const int32_t *qexp, const float *qsum,
+                                    const uint64_t *tiles, float *part, hipStream_t stream);
 // Split-K partial attention over raw (unquantized, unrotated) K and V that
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
