@@ -47,34 +47,60 @@ def _args():
     return ap.parse_args()
 
 
+SPLIT_KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_int2_amd", "csrc", "decode_mfma.hip")
+
+
+def kernel_source_digest() -> str:
+    """sha256 of the split kernel's source: counter figures taken from another
+    version of the kernel are not reported."""
+    import hashlib
+    with open(SPLIT_KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(path: str):
+    """HBM bytes per split-kernel launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None if there is
+    none for the current kernel source."""
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(w_cpu) -> dict:
     """The oracle as it stands, timed on this host on a bounded sample of the
-    same workload: one sequence, 2 of its 8 KV heads (8 query heads), all
-    32,768 tokens: cache write then decode."""
+    same workload (about 10-20 s single-threaded): two of the 16 sequences,
+    all 8 KV heads (32 query heads), 32,768 tokens each: cache write of the
+    sample, then one decode step over it."""
     import numpy as np
     import oracle
 
-    H_s = 2
+    S = 2
     T = w_cpu["tokens"]
-    k = w_cpu["k"][:T, :H_s].astype(np.float32)
-    v = w_cpu["v"][:T, :H_s].astype(np.float32)
-    q = w_cpu["q"][:1, :H_s * 4].astype(np.float32)
-    signs = w_cpu["signs"][:H_s]
+    H = w_cpu["k"].shape[1]
+    k = w_cpu["k"][:S * T].astype(np.float32)
+    v = w_cpu["v"][:S * T].astype(np.float32)
+    q = w_cpu["q"][:S].astype(np.float32)
     P = 16
-    pages = (T + P - 1) // P
-    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=signs)
-    cache = oracle.Cache(pages, P, H_s)
+    pages_per_seq = (T + P - 1) // P
+    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=w_cpu["signs"])
+    cache = oracle.Cache(S * pages_per_seq, P, H)
+    slots = np.concatenate([s * pages_per_seq * P + np.arange(T) for s in range(S)]).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.quantize(k, v, cache, rot, rot, clip_k=0.96, clip_v=0.92)
+    oracle.quantize(k, v, cache, rot, rot, clip_k=0.96, clip_v=0.92, slot_mapping=slots)
     t1 = time.perf_counter()
-    oracle.decode(q, cache, [T], rot, rot, num_seqs=1, max_pages=pages)
+    oracle.decode(q, cache, [T] * S, rot, rot, num_seqs=S, max_pages=pages_per_seq)
     t2 = time.perf_counter()
-    dec_gbs = T * H_s * BYTES_PER_TOKEN_HEAD / (t2 - t1) / 1e9
-    tok_equiv = T * H_s / 8.0  # tokens of the 8-KV-head layer
+    dec_gbs = S * T * H * BYTES_PER_TOKEN_HEAD / (t2 - t1) / 1e9
     return {"value": dec_gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"1 sequence x 2 of 8 KV heads x {T} tokens: oracle cache write "
-                      f"{t1 - t0:.2f} s, oracle decode (8 query heads) {t2 - t1:.2f} s",
-            "quantize_mtok_s": tok_equiv / (t1 - t0) / 1e6}
+            "sample": f"{S} of 16 sequences x {H} KV heads x {T} tokens: oracle cache write {t1 - t0:.2f} s, "
+                      f"oracle decode ({q.shape[1]} query heads) {t2 - t1:.2f} s",
+            "quantize_mtok_s": S * T / (t1 - t0) / 1e6}
 
 
 def main():
@@ -150,18 +176,12 @@ def main():
     quant_bytes = tokens * H * (2 * 128 * 2 + BYTES_PER_TOKEN_HEAD)
     quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
 
-    traffic = None
-    if os.path.exists(a.traffic_json):
-        try:
-            with open(a.traffic_json) as f:
-                traffic = json.load(f).get("hbm_bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = measured_traffic(a.traffic_json)
 
     base = None
     if not a.no_cpu_baseline:
-        w_cpu = {"tokens": T, "k": w.k[:T].float().cpu().numpy(), "v": w.v[:T].float().cpu().numpy(),
-                 "q": w.q[:1].float().cpu().numpy(), "signs": w.rot_k.signs.cpu().numpy()}
+        w_cpu = {"tokens": T, "k": w.k[:2 * T].float().cpu().numpy(), "v": w.v[:2 * T].float().cpu().numpy(),
+                 "q": w.q[:2].float().cpu().numpy(), "signs": w.rot_k.signs.cpu().numpy()}
         base = cpu_baseline(w_cpu)
 
     out = {
