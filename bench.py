@@ -13,9 +13,12 @@ Two cache buffers alternate: step i writes cache i%2 and decodes cache
 (i+1)%2 (written one step earlier and followed by >2 GB of other traffic), so
 the decode reads its 302 MB from HBM, not from the 256 MB Infinity Cache.
 
-Prints one JSON line.  value = effective KV GB/s of the split-K attention
-kernel (72 bytes per cached token per KV head / its average duration,
-measured with HIP events recorded on the launch stream).
+Prints one JSON line.  value = effective KV GB/s of decode attention: 72
+bytes per cached token per KV head / the average time of the attention part
+of the decode call (query rotation, split-K attention, split merge and inverse
+value rotation; the W_O projection is timed separately), from HIP events
+recorded on the launch stream.  roofline = the split-K kernel alone (its own
+events), the dominant kernel.
 """
 from __future__ import annotations
 
@@ -145,7 +148,7 @@ def main():
             ev[1].record(stream)
         kvq.kvq_decode_attn(w.q, B, 1, caches[(i + 1) % 2], w.page_table, max_pages, w.seq_lens, T, rot, rot, out_o,
                             w_o=w.w_o, out_y=out_y, workspace=ws, num_splits=a.num_splits,
-                            split_events=None if ev is None else (ev[2], ev[3]))
+                            split_events=None if ev is None else (ev[2], ev[3], ev[5]))
         if ev is not None:
             ev[4].record(stream)
 
@@ -155,7 +158,7 @@ def main():
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
     for ev in events:          # torch creates the HIP event on first record; the library records 2 of them
         for e in ev:
             e.record(stream)
@@ -170,8 +173,10 @@ def main():
     quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / a.steps
     split_ms = sum(e[2].elapsed_time(e[3]) for e in events) / a.steps
     decode_ms = sum(e[1].elapsed_time(e[4]) for e in events) / a.steps
+    attn_ms = sum(e[1].elapsed_time(e[5]) for e in events) / a.steps
     kv_bytes = B * T * H * BYTES_PER_TOKEN_HEAD
     split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
+    attn_gbs = kv_bytes / (attn_ms * 1e-3) / 1e9
     tokens = B * T
     quant_bytes = tokens * H * (2 * 128 * 2 + BYTES_PER_TOKEN_HEAD)
     quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
@@ -186,7 +191,7 @@ def main():
 
     out = {
         "metric": "INT2 decode-attn effective KV GB/s (% HBM peak) + quantize Mtok/s, 32K ctx",
-        "value": round(split_gbs, 1),
+        "value": round(attn_gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -201,7 +206,10 @@ def main():
                    "context": T, "kv_heads": H, "q_heads": Hq, "head_dim": 128, "page_size": P, "d_model": dm,
                    "kv_input_dtype": "bf16", "cache": "int2 group-128 + fp16 scale/zero",
                    "rotation": "signed_hadamard", "clip_k": w.clip_k, "clip_v": w.clip_v},
-        "pct_hbm_peak": round(100.0 * split_gbs / HBM_PEAK_GBS, 2),
+        "pct_hbm_peak": round(100.0 * attn_gbs / HBM_PEAK_GBS, 2),
+        "decode_attn_us": round(attn_ms * 1e3, 2),
+        "split_kernel_gbs": round(split_gbs, 1),
+        "split_kernel_pct_hbm_peak": round(100.0 * split_gbs / HBM_PEAK_GBS, 2),
         "quantize_mtok_s": round(tokens / (quant_ms * 1e-3) / 1e6, 2),
         "quantize_gbs": round(quant_gbs, 1),
         "quantize_us": round(quant_ms * 1e3, 2),

@@ -146,12 +146,11 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   int32_t *qexp = reinterpret_cast<int32_t *>(ws + pl.off_qexp);
   const bool mfma = decode_mfma_supported(pl, cache->page_size);
   uint64_t *tiles = reinterpret_cast<uint64_t *>(ws + pl.off_tiles);
-  KVQ_TRY(launch_query_rotation(q, dtype, pl, to_dev(*rot_k), qrot, qsum, stream));
-  if (mfma) {
-    KVQ_TRY(launch_query_digits(pl, qrot, qdig, qexp, stream));
-    KVQ_TRY(launch_tile_table(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
-                              tiles, stream));
-  }
+  if (mfma)
+    KVQ_TRY(launch_decode_prologue(pl, q, dtype, to_dev(*rot_k), cache->pages, cache->num_pages, cache->page_size,
+                                   page_table, max_pages_per_seq, qrot, qsum, qdig, qexp, tiles, stream));
+  else
+    KVQ_TRY(launch_query_rotation(q, dtype, pl, to_dev(*rot_k), qrot, qsum, stream));
   if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
   if (mfma)
     KVQ_TRY(launch_decode_split_mfma(pl, cache->page_size, seq_lens, qdig, qexp, qsum, tiles, part, stream));
@@ -161,6 +160,7 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
   float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
   KVQ_TRY(launch_combine(pl, part, to_dev(*rot_v), out_o, ot, stream));
+  if (events && events->attn_stop) KVQ_TRY(hipEventRecord(events->attn_stop, stream));
   if (w_o) KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, ypart, out_y, stream));
   return KVQ_OK;
 }
@@ -225,10 +225,11 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   KVQ_TRY(launch_fill_i32(seq_len, static_cast<int32_t>(num_tokens), 1, stream));
   for (int r = 0; r < num_candidates; ++r) {
     const RotDev rot = to_dev(candidates[r]);
-    KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
-    if (mfma) KVQ_TRY(launch_query_digits(pl, qrot, qdig, qexp, stream));
-    if (mfma && r == 0)
-      KVQ_TRY(launch_tile_table(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), tiles, stream));
+    if (mfma)
+      KVQ_TRY(launch_decode_prologue(pl, q, dtype, rot, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages),
+                                     qrot, qsum, qdig, qexp, tiles, stream));
+    else
+      KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
     for (int i = 0; i < num_clips; ++i) {
       KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips[i], clips[i], pages,
                               L.num_pages, 16, stream));

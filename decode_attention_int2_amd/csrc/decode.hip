@@ -33,21 +33,6 @@ __device__ __forceinline__ float wave_maxf(float x) {
 // One wave holds a 128-vector as two registers per lane: x0 = x[lane],
 // x1 = x[lane + 64].
 
-// In-place fast Walsh-Hadamard transform: x <- x H, H[i][j] = (-1)^popcount(i & j)
-// (Sylvester order, unnormalized): one butterfly stage per index bit.
-__device__ __forceinline__ void fwht128(float &x0, float &x1, int lane) {
-  const float a = x0 + x1, b = x0 - x1;  // bit 6: pairs (lane, lane + 64)
-  x0 = a;
-  x1 = b;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const float p0 = __shfl_xor(x0, d), p1 = __shfl_xor(x1, d);
-    const bool upper = (lane & d) != 0;
-    x0 = upper ? p0 - x0 : x0 + p0;
-    x1 = upper ? p1 - x1 : x1 + p1;
-  }
-}
-
 // ------------------------------------------------------------ query rotation
 // q'[row][j] = q[row][j] R_K[h(j)] * log2(e)/sqrt(128); qsum = sum_c q'_c.
 // One wave per (query row, query head).
@@ -58,31 +43,9 @@ __global__ __launch_bounds__(256) void query_rotation_kernel(const void *q, int 
   const int rj = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rj >= n_items) return;
   const int h = (rj % Hq) / G;
-  const float inv_sqrt_d = 0.08838834764831845f;
-  float x0 = load_elem<DT>(q, static_cast<size_t>(rj) * D + lane);
-  float x1 = load_elem<DT>(q, static_cast<size_t>(rj) * D + lane + 64);
-  float y0 = x0, y1 = x1;
-  if (rk.kind == KVQ_ROT_SIGNED_HADAMARD) {
-    // z R = ((z * s) H) / sqrt(128)
-    x0 *= static_cast<float>(rk.signs[h * D + lane]);
-    x1 *= static_cast<float>(rk.signs[h * D + lane + 64]);
-    fwht128(x0, x1, lane);
-    y0 = x0 * inv_sqrt_d;
-    y1 = x1 * inv_sqrt_d;
-  } else if (rk.kind == KVQ_ROT_DENSE) {
-    const float *m = rk.matrix + static_cast<size_t>(h) * D * D;
-    float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < D; ++i) {
-      const float zi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(i < 64 ? x0 : x1), i & 63));
-      a0 += zi * m[i * D + lane];
-      a1 += zi * m[i * D + lane + 64];
-    }
-    y0 = a0;
-    y1 = a1;
-  }
-  y0 *= kLog2e * inv_sqrt_d;
-  y1 *= kLog2e * inv_sqrt_d;
+  float y0 = load_elem<DT>(q, static_cast<size_t>(rj) * D + lane);
+  float y1 = load_elem<DT>(q, static_cast<size_t>(rj) * D + lane + 64);
+  rotate_query_wave(y0, y1, rk, h, lane);
   qrot[static_cast<size_t>(rj) * D + lane] = y0;
   qrot[static_cast<size_t>(rj) * D + lane + 64] = y1;
   const float sum = wave_sum(y0 + y1);

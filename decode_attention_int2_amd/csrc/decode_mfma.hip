@@ -112,18 +112,81 @@ struct MfmaArgs {
   float *part;
 };
 
-// Fixed-point digits of the rotated queries of one (sequence, KV head): lane
-// (col, grp) gets the 8 dwords of its A-operand row (query row col/4, digit
-// col%4) for the two 64-dim MFMAs.  Dim 16*(2*grp + m) + 4*bb + e goes to dword
-// [m][e], byte bb; slot e of the unpacked codes carries a factor 1/slot_inv(e),
-// which is divided out here.  Q = round(q' 2^S) with |Q| <= 2^26.
-__global__ __launch_bounds__(64) void query_digits_kernel(const float *qrot, int R, int G, int Hq, int H, int Nq,
-                                                          int32_t *qdig, int32_t *qexp) {
-  const int bh = blockIdx.x;  // b * H + h
-  const int b = bh / H, h = bh % H;
-  const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4, hr = col >> 2, dg = col & 3;
-  const bool row_ok = hr < R;
-  const size_t rj = (static_cast<size_t>(b) * Nq + hr / G) * Hq + h * G + hr % G;
+// Prologue of the split kernel, one launch:
+//  * blocks [0, num_seqs*H): one per (sequence, KV head).  Wave r < R
+//    rotates query row r (q' = q R_K log2(e)/sqrt(128)), writes q' and
+//    sum(q'); then wave 0 writes the fixed-point int8 digits of the R rows in
+//    the key-side A-operand layout: lane (col, grp) gets the 8 dwords of query
+//    row col/4, digit col%4, for the two 64-dim MFMAs; dim 16*(2*grp + m) +
+//    4*bb + e goes to dword [m][e], byte bb.  Slot e of the unpacked codes
+//    carries a factor 1/slot_inv(e), divided out here.  Q = round(q' 2^S)
+//    with |Q| < 2^26 (S from the row group's largest |q'|).
+//  * the remaining blocks: absolute addresses of every 16-token tile of every
+//    sequence (head 0 of its page; the head's offset is part of the lanes'
+//    constant offsets):
+//      [0] page block + 32 * (position of the tile in its page)   K/V codes
+//      [1] page block + 64 P + 4 * (position)                     K/V metadata
+//    A page index outside the cache is replaced by page 0 and flagged in
+//    bit 0 of the metadata address.
+struct PrologueArgs {
+  const void *q;
+  RotDev rk;
+  int R, G, Hq, H, Nq, num_seqs;
+  float *qrot, *qsum;
+  int32_t *qdig, *qexp;
+  const uint8_t *pages;
+  int64_t num_pages;
+  int P;
+  const int32_t *page_table;
+  int max_pages, tiles_per_seq, table_chunks;
+  uint64_t *tiles;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void decode_prologue_kernel(PrologueArgs p) {
+  const int n_bh = p.num_seqs * p.H;
+  if (static_cast<int>(blockIdx.x) >= n_bh) {
+    const int idx = blockIdx.x - n_bh;
+    const int b = idx / p.table_chunks;
+    const int i = (idx % p.table_chunks) * 256 + threadIdx.x;
+    if (i >= p.tiles_per_seq) return;
+    const int pi = (16 * i) / p.P, off = (16 * i) % p.P;
+    int64_t pg = (p.page_table && pi < p.max_pages)
+                     ? static_cast<int64_t>(p.page_table[static_cast<size_t>(b) * p.max_pages + pi])
+                     : static_cast<int64_t>(b) * p.max_pages + pi;
+    uint64_t flag = 0;
+    if (pi >= p.max_pages || pg < 0 || pg >= p.num_pages) {
+      pg = 0;
+      flag = 1;
+    }
+    const uint64_t blk = reinterpret_cast<uint64_t>(p.pages) + static_cast<uint64_t>(pg) * p.H * 72 * p.P;
+    uint64_t *e = p.tiles + (static_cast<size_t>(b) * p.tiles_per_seq + i) * 2;
+    e[0] = blk + 32 * off;
+    e[1] = (blk + 64 * static_cast<uint64_t>(p.P) + 4 * off) | flag;
+    return;
+  }
+  __shared__ float qs[4][D];
+  const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  {
+    float y0 = 0.0f, y1 = 0.0f;
+    if (wave < p.R) {
+      const size_t rj = (static_cast<size_t>(b) * p.Nq + wave / p.G) * p.Hq + h * p.G + wave % p.G;
+      y0 = load_elem<DT>(p.q, rj * D + lane);
+      y1 = load_elem<DT>(p.q, rj * D + lane + 64);
+      rotate_query_wave(y0, y1, p.rk, h, lane);
+      p.qrot[rj * D + lane] = y0;
+      p.qrot[rj * D + lane + 64] = y1;
+      float sum = y0 + y1;
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      if (lane == 0) p.qsum[rj] = sum;
+    }
+    qs[wave][lane] = y0;
+    qs[wave][lane + 64] = y1;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int col = lane & 15, grp = lane >> 4, hr = col >> 2, dg = col & 3;
   float qv[2][16];
   float qabs = 0.0f;
 #pragma unroll
@@ -132,16 +195,17 @@ __global__ __launch_bounds__(64) void query_digits_kernel(const float *qrot, int
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const float x = row_ok ? qrot[rj * D + 16 * (2 * grp + m) + 4 * bb + e] : 0.0f;
+        const float x = qs[hr][16 * (2 * grp + m) + 4 * bb + e];
         qv[m][4 * e + bb] = x * slot_inv(e);
         qabs = fmaxf(qabs, fabsf(x));
       }
+  // one shift S per query row: the row's 16 lanes x 4 lane groups hold all its dims
   qabs = fmaxf(qabs, __shfl_xor(qabs, 16));
   qabs = fmaxf(qabs, __shfl_xor(qabs, 32));
   int e2 = 0;
   (void)frexpf(qabs, &e2);  // qabs < 2^e2
   const int qshift = 26 - e2;
-  int32_t *dst = qdig + (static_cast<size_t>(bh) * 64 + lane) * 8;
+  int32_t *dst = p.qdig + (static_cast<size_t>(blockIdx.x) * 64 + lane) * 8;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -155,33 +219,7 @@ __global__ __launch_bounds__(64) void query_digits_kernel(const float *qrot, int
       }
       dst[4 * m + e] = static_cast<int32_t>(word);
     }
-  if (grp == 0 && dg == 0) qexp[static_cast<size_t>(bh) * 4 + hr] = qshift;
-}
-
-// Absolute addresses of every 16-token tile of every sequence (head 0 of its
-// page; the head's offset is part of the lanes' constant offsets):
-//   [0] page block + 32 * (position of the tile in its page)   K/V codes
-//   [1] page block + 64 P + 4 * (position)                     K/V metadata
-// A page index outside the cache is replaced by page 0 and flagged in bit 0
-// of the metadata address.
-__global__ __launch_bounds__(256) void tile_table_kernel(const uint8_t *pages, int64_t num_pages, int P, int H,
-                                                         const int32_t *page_table, int max_pages,
-                                                         int tiles_per_seq, uint64_t *tiles) {
-  const int b = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= tiles_per_seq) return;
-  const int pi = (16 * i) / P, off = (16 * i) % P;
-  int64_t p = (page_table && pi < max_pages) ? static_cast<int64_t>(page_table[static_cast<size_t>(b) * max_pages + pi])
-                                             : static_cast<int64_t>(b) * max_pages + pi;
-  uint64_t flag = 0;
-  if (pi >= max_pages || p < 0 || p >= num_pages) {
-    p = 0;
-    flag = 1;
-  }
-  const uint64_t blk = reinterpret_cast<uint64_t>(pages) + static_cast<uint64_t>(p) * H * 72 * P;
-  uint64_t *e = tiles + (static_cast<size_t>(b) * tiles_per_seq + i) * 2;
-  e[0] = blk + 32 * off;
-  e[1] = (blk + 64 * static_cast<uint64_t>(P) + 4 * off) | flag;
+  if (grp == 0 && dg == 0) p.qexp[static_cast<size_t>(blockIdx.x) * 4 + hr] = qshift;
 }
 
 constexpr int kWaves = 4;
@@ -488,21 +526,37 @@ bool decode_mfma_supported(const DecodePlan &pl, int page_size) {
          static_cast<int64_t>(pl.H) * 72 * page_size < (static_cast<int64_t>(1) << 31);
 }
 
-hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t *qdig, int32_t *qexp,
-                               hipStream_t stream) {
-  const int n = pl.num_seqs * pl.H;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(query_digits_kernel, dim3(n), dim3(64), 0, stream, qrot, pl.rows_per_head, pl.G, pl.Hq, pl.H,
-                     pl.queries_per_seq, qdig, qexp);
-  return hipGetLastError();
-}
-
-hipError_t launch_tile_table(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
-                             const int32_t *page_table, int max_pages, uint64_t *tiles, hipStream_t stream) {
+hipError_t launch_decode_prologue(const DecodePlan &pl, const void *q, int dtype, RotDev rk, const uint8_t *pages,
+                                  int64_t num_pages, int page_size, const int32_t *page_table, int max_pages,
+                                  float *qrot, float *qsum, int32_t *qdig, int32_t *qexp, uint64_t *tiles,
+                                  hipStream_t stream) {
   if (pl.num_seqs == 0) return hipSuccess;
-  const int tps = pl.tiles_per_seq;
-  hipLaunchKernelGGL(tile_table_kernel, dim3((tps + 255) / 256, pl.num_seqs), dim3(256), 0, stream, pages, num_pages,
-                     page_size, pl.H, page_table, max_pages, tps, tiles);
+  PrologueArgs p{};
+  p.q = q;
+  p.rk = rk;
+  p.R = pl.rows_per_head;
+  p.G = pl.G;
+  p.Hq = pl.Hq;
+  p.H = pl.H;
+  p.Nq = pl.queries_per_seq;
+  p.num_seqs = pl.num_seqs;
+  p.qrot = qrot;
+  p.qsum = qsum;
+  p.qdig = qdig;
+  p.qexp = qexp;
+  p.pages = pages;
+  p.num_pages = num_pages;
+  p.P = page_size;
+  p.page_table = page_table;
+  p.max_pages = max_pages;
+  p.tiles_per_seq = pl.tiles_per_seq;
+  p.table_chunks = (pl.tiles_per_seq + 255) / 256;
+  p.tiles = tiles;
+  const dim3 grid(pl.num_seqs * pl.H + pl.num_seqs * p.table_chunks);
+  if (dtype == KVQ_F32)
+    hipLaunchKernelGGL(decode_prologue_kernel<KVQ_F32>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_prologue_kernel<KVQ_BF16>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

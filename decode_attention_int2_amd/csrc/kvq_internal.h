@@ -56,6 +56,51 @@ __device__ __forceinline__ float rot_entry(const RotDev &r, int h, int i, int j,
   return r.matrix[(static_cast<size_t>(h) * D + i) * D + j];
 }
 
+// One wave holds a 128-vector as x0 = x[lane], x1 = x[lane + 64].
+// In-place fast Walsh-Hadamard transform: x <- x H, H[i][j] = (-1)^popcount(i & j)
+// (Sylvester order, unnormalized): one butterfly stage per index bit.
+__device__ __forceinline__ void fwht128(float &x0, float &x1, int lane) {
+  const float a = x0 + x1, b = x0 - x1;  // bit 6: pairs (lane, lane + 64)
+  x0 = a;
+  x1 = b;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float p0 = __shfl_xor(x0, d), p1 = __shfl_xor(x1, d);
+    const bool upper = (lane & d) != 0;
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+  }
+}
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
+
+// q' = q R_K * log2(e)/sqrt(128) of one 128-vector held by a wave (row-vector
+// convention z' = z R; signed Hadamard by the transform above).
+__device__ __forceinline__ void rotate_query_wave(float &x0, float &x1, const RotDev &rk, int h, int lane) {
+  float y0 = x0, y1 = x1;
+  if (rk.kind == KVQ_ROT_SIGNED_HADAMARD) {
+    x0 *= static_cast<float>(rk.signs[h * D + lane]);
+    x1 *= static_cast<float>(rk.signs[h * D + lane + 64]);
+    fwht128(x0, x1, lane);
+    y0 = x0 * kInvSqrtD;
+    y1 = x1 * kInvSqrtD;
+  } else if (rk.kind == KVQ_ROT_DENSE) {
+    const float *m = rk.matrix + static_cast<size_t>(h) * D * D;
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < D; ++i) {
+      const float zi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(i < 64 ? x0 : x1), i & 63));
+      a0 += zi * m[i * D + lane];
+      a1 += zi * m[i * D + lane + 64];
+    }
+    y0 = a0;
+    y1 = a1;
+  }
+  x0 = y0 * (kLog2eF * kInvSqrtD);
+  x1 = y1 * (kLog2eF * kInvSqrtD);
+}
+
 // ----------------------------------------------------------------- launchers
 hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
                            const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean, float clip_k,
@@ -83,14 +128,14 @@ hipError_t launch_decode_split(const DecodePlan &pl, const uint8_t *pages, int64
                                const float *qrot, const float *qsum, float *part, hipStream_t stream);
 // Same partials from the matrix-core kernel (rows_per_head <= 4).
 bool decode_mfma_supported(const DecodePlan &pl, int page_size);
-// Fixed-point int8 digits of the rotated queries, one 64-lane operand set per
-// (sequence, KV head) (prologue of the matrix-core kernel).
-hipError_t launch_query_digits(const DecodePlan &pl, const float *qrot, int32_t *qdig, int32_t *qexp,
-                               hipStream_t stream);
-// Absolute code / metadata addresses of every 16-token tile (prologue of the
-// matrix-core kernel; page indices are validated here).
-hipError_t launch_tile_table(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
-                             const int32_t *page_table, int max_pages, uint64_t *tiles, hipStream_t stream);
+// Prologue of the matrix-core kernel (one launch): rotated queries and their
+// sums, their fixed-point int8 digits (one 64-lane operand set per (sequence,
+// KV head)) and the absolute code / metadata addresses of every 16-token tile
+// (page indices validated here).
+hipError_t launch_decode_prologue(const DecodePlan &pl, const void *q, int dtype, RotDev rk, const uint8_t *pages,
+                                  int64_t num_pages, int page_size, const int32_t *page_table, int max_pages,
+                                  float *qrot, float *qsum, int32_t *qdig, int32_t *qexp, uint64_t *tiles,
+                                  hipStream_t stream);
 hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const int32_t *seq_lens,
                                     const int32_t *qdig, const int32_t *qexp, const float *qsum,
                                     const uint64_t *tiles, float *part, hipStream_t stream);

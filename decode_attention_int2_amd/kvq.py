@@ -41,7 +41,7 @@ class _Cache(ctypes.Structure):
 
 
 class _Events(ctypes.Structure):
-    _fields_ = [("split_start", ctypes.c_void_p), ("split_stop", ctypes.c_void_p)]
+    _fields_ = [("split_start", ctypes.c_void_p), ("split_stop", ctypes.c_void_p), ("attn_stop", ctypes.c_void_p)]
 
 
 _lib = None
@@ -165,7 +165,8 @@ def kvq_decode_attn(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache:
                     w_o: Optional[torch.Tensor] = None, out_y: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None,
                     split_events: Optional[tuple] = None) -> None:
-    """split_events: optional (start, stop) torch.cuda.Event pair recorded around the split-K kernel."""
+    """split_events: optional (start, stop) or (start, stop, attn_stop) torch.cuda.Event tuple: start/stop
+    are recorded around the split-K kernel, attn_stop after the merge (before W_O)."""
     lib = load_library()
     Hq = q.shape[1]
     d_model = int(w_o.shape[1]) if w_o is not None else 0
@@ -173,8 +174,8 @@ def kvq_decode_attn(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ev = None
     if split_events is not None:
-        ev = ctypes.byref(_Events(ctypes.c_void_p(split_events[0].cuda_event),
-                                  ctypes.c_void_p(split_events[1].cuda_event)))
+        handles = [ctypes.c_void_p(e.cuda_event) for e in split_events] + [ctypes.c_void_p(0)] * 3
+        ev = ctypes.byref(_Events(*handles[:3]))
     _check(lib.kvq_decode_attn(_dev_ptr(q, "q"), _dtype_code(q), num_seqs, queries_per_seq, Hq, ctypes.byref(c),
                                _dev_ptr(page_table, "page_table"), max_pages_per_seq, _dev_ptr(seq_lens, "seq_lens"),
                                max_seq_len, ctypes.byref(rk), ctypes.byref(rv), _dev_ptr(w_o, "w_o"), d_model,

@@ -165,10 +165,13 @@ int kvq_quantize(const void *k, const void *v, int32_t dtype, int64_t num_tokens
 /* Optional timing hook of kvq_decode_attn: when non-NULL, split_start and
  * split_stop are recorded on `stream` immediately before and after the
  * split-K attention kernel (the step that reads the packed cache), so a caller
- * can time that kernel alone with hipEventElapsedTime.  Work is unchanged. */
+ * can time that kernel alone with hipEventElapsedTime; attn_stop is recorded
+ * after the split merge and inverse value rotation (out_o complete), before
+ * the W_O projection.  Any of the three may be NULL.  Work is unchanged. */
 typedef struct {
   hipEvent_t split_start;
   hipEvent_t split_stop;
+  hipEvent_t attn_stop;
 } kvq_decode_events;
 
 size_t kvq_decode_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
