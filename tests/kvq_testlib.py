@@ -138,3 +138,45 @@ def check_rotated_quantization(got_pages, ref_pages, y_ref: dict, slots: np.ndar
         assert stats[side][0] <= max_code_mismatch, (side, stats[side])
         assert stats[side][1] <= max_meta_mismatch, (side, stats[side])
     return stats
+
+
+def oracle_decode_on_cache(w, cache_pages: np.ndarray, seqs, with_wo=True):
+    """The oracle's decode of the sequences `seqs` of workload w, reading the
+    given cache bytes (the GPU's), with the workload's page table: returns
+    (out_o [rows][Hq][128], out_y [rows][d_model] or None) for those
+    sequences' query rows."""
+    seqs = list(seqs)
+    oc = oracle.Cache(w.num_pages, w.page_size, w.H)
+    oc.pages[...] = cache_pages
+    nq = w.queries_per_seq
+    rows = np.concatenate([np.arange(s * nq, (s + 1) * nq) for s in seqs])
+    q = f32np(w.q)[rows]
+    pt = w.page_table.cpu().numpy()[seqs]
+    sl = w.seq_lens.cpu().numpy()[seqs]
+    res = oracle.decode(q, oc, sl, oracle_rot(w.rot_k), oracle_rot(w.rot_v), num_seqs=len(seqs),
+                        queries_per_seq=nq, page_table=pt, max_pages=pt.shape[1],
+                        w_o=f32np(w.w_o) if with_wo else None, d_model=w.d_model if with_wo else 0)
+    return (res if with_wo else (res, None)), rows
+
+
+def sampled_quantize_check(w, cache_pages: np.ndarray, n_sample: int, seed: int):
+    """Cache write of n_sample seeded tokens, group by group, against the
+    oracle's rotation and quantizer of the same tokens (rotated path:
+    check_rotated_quantization; fp32 inputs: bytes equal)."""
+    rng = np.random.default_rng(seed)
+    T = w.k.shape[0]
+    idx = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
+    slots = w.slot_mapping.cpu().numpy()[idx]
+    k = f32np(w.k[torch.from_numpy(idx).to(w.k.device)])
+    v = f32np(w.v[torch.from_numpy(idx).to(w.v.device)])
+    km = None if w.key_mean is None else f32np(w.key_mean)
+    oc = oracle.Cache(w.num_pages, w.page_size, w.H)
+    oracle.quantize(k, v, oc, oracle_rot(w.rot_k), oracle_rot(w.rot_v), key_mean=km, clip_k=w.clip_k,
+                    clip_v=w.clip_v, slot_mapping=slots)
+    if w.dtype == "f32":
+        got = parse_cache(cache_pages, slots, w.page_size)
+        ref = parse_cache(oc.pages, slots, w.page_size)
+        mism = sum(float(np.mean(got[s][0] != ref[s][0])) for s in ("k", "v")) / 2
+        return {"code_mismatch": mism}
+    y = {"k": oracle.rotate(k, oracle_rot(w.rot_k), km), "v": oracle.rotate(v, oracle_rot(w.rot_v))}
+    return check_rotated_quantization(cache_pages, oc.pages, y, slots, w.page_size)
