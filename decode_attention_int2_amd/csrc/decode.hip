@@ -630,19 +630,15 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   const int max_chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   int splits = num_splits;
   if (splits <= 0) {
-    // The matrix-core kernel (<= 4 rows per KV head): ~2 workgroups of 4
-    // waves per CU, all resident at once (a partial second round of
-    // workgroups would run the tail at low occupancy), and splits of at least
-    // 1024 tokens so the per-split prologue and merge stay small.  The VALU
-    // kernel: enough workgroups to fill 256 CUs several times.
-    const int units = num_seqs * H > 0 ? num_seqs * H : 1;
-    const bool mfma_path = queries_per_seq * (Hq / H) <= 4;
-    const int target = mfma_path ? 512 : 4096;
-    splits = (target + units - 1) / units;
-    if (mfma_path) {
-      const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens
-      if (splits > max_by_len) splits = max_by_len;
-    }
+    // ~2 workgroups of 4 waves per CU, all resident at once (a partial second
+    // round of workgroups would run the tail at low occupancy), and splits of
+    // at least 1024 tokens so the per-split prologue and merge stay small.
+    // A workgroup of the matrix-core kernel takes one group of 4 query rows.
+    const int n_rg = (queries_per_seq * (Hq / H) + 3) / 4;
+    const int units = num_seqs * H * n_rg > 0 ? num_seqs * H * n_rg : 1;
+    splits = (512 + units - 1) / units;
+    const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens
+    if (splits > max_by_len) splits = max_by_len;
   }
   if (splits > max_chunks) splits = max_chunks;
   if (splits > kMaxCombineSplits) splits = kMaxCombineSplits;
@@ -674,10 +670,11 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   off = align(off + (d_model > 0 && ks > 1 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
   pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection
   off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * K * kWoRows * sizeof(float) : 0));
-  pl.off_qdig = off;  // [num_seqs][H][64 lanes][8] int32
-  off = align(off + static_cast<size_t>(num_seqs) * H * 64 * 8 * sizeof(int32_t));
-  pl.off_qexp = off;  // [num_seqs][H][4 rows] int32
-  off = align(off + static_cast<size_t>(num_seqs) * H * 4 * sizeof(int32_t));
+  const size_t n_rg_all = static_cast<size_t>(num_seqs) * H * ((queries_per_seq * (Hq / H) + 3) / 4);
+  pl.off_qdig = off;  // [num_seqs][H][row groups][64 lanes][8] int32
+  off = align(off + n_rg_all * 64 * 8 * sizeof(int32_t));
+  pl.off_qexp = off;  // [num_seqs][H][row groups][4 rows] int32
+  off = align(off + n_rg_all * 4 * sizeof(int32_t));
   pl.tiles_per_seq = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
   pl.off_tiles = off;  // [num_seqs][tiles_per_seq][2] uint64
   off = align(off + static_cast<size_t>(num_seqs) * pl.tiles_per_seq * 2 * sizeof(uint64_t));

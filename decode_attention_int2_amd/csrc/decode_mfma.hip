@@ -100,27 +100,28 @@ __device__ __forceinline__ int byte_sum(int d, int x) {
 }
 
 struct MfmaArgs {
-  int R, G, Hq, H, Nq;
+  int R, G, Hq, H, Nq, n_rg;  // n_rg: groups of 4 query rows per KV head
   int split_tokens, splits, max_seq_len;
   int P;
   int tiles_per_seq;
   const int32_t *seq_lens;
-  const int32_t *qdig;     // [num_seqs][H][64 lanes][8] key-side A operand
-  const int32_t *qexp;     // [num_seqs][H][4 rows] fixed-point shift S of each query row
+  const int32_t *qdig;     // [num_seqs][H][n_rg][64 lanes][8] key-side A operand
+  const int32_t *qexp;     // [num_seqs][H][n_rg][4 rows] fixed-point shift S of each query row
   const float *qsum;
   const uint64_t *tiles;   // [num_seqs][tiles_per_seq][2] code base, metadata base (bit 0: bad page)
   float *part;
 };
 
 // Prologue of the split kernel, one launch:
-//  * blocks [0, num_seqs*H): one per (sequence, KV head).  Wave r < R
-//    rotates query row r (q' = q R_K log2(e)/sqrt(128)), writes q' and
-//    sum(q'); then wave 0 writes the fixed-point int8 digits of the R rows in
-//    the key-side A-operand layout: lane (col, grp) gets the 8 dwords of query
-//    row col/4, digit col%4, for the two 64-dim MFMAs; dim 16*(2*grp + m) +
-//    4*bb + e goes to dword [m][e], byte bb.  Slot e of the unpacked codes
-//    carries a factor 1/slot_inv(e), divided out here.  Q = round(q' 2^S)
-//    with |Q| < 2^26 (S from the row group's largest |q'|).
+//  * blocks [0, num_seqs*H*n_rg): one per (sequence, KV head, group of 4
+//    query rows).  Wave r rotates row 4 rg + r of the head's R rows (q' = q R_K
+//    log2(e)/sqrt(128)), writes q' and sum(q'); then wave 0 writes the
+//    fixed-point int8 digits of the group's rows in the key-side A-operand
+//    layout: lane (col, grp) gets the 8 dwords of query row col/4, digit
+//    col%4, for the two 64-dim MFMAs; dim 16*(2*grp + m) + 4*bb + e goes to
+//    dword [m][e], byte bb.  Slot e of the unpacked codes carries a factor
+//    1/slot_inv(e), divided out here.  Q = round(q' 2^S) with |Q| < 2^26 (S
+//    per query row from its largest |q'|).
 //  * the remaining blocks: absolute addresses of every 16-token tile of every
 //    sequence (head 0 of its page; the head's offset is part of the lanes'
 //    constant offsets):
@@ -131,7 +132,7 @@ struct MfmaArgs {
 struct PrologueArgs {
   const void *q;
   RotDev rk;
-  int R, G, Hq, H, Nq, num_seqs;
+  int R, G, Hq, H, Nq, num_seqs, n_rg;
   float *qrot, *qsum;
   int32_t *qdig, *qexp;
   const uint8_t *pages;
@@ -144,7 +145,7 @@ struct PrologueArgs {
 
 template <int DT>
 __global__ __launch_bounds__(256) void decode_prologue_kernel(PrologueArgs p) {
-  const int n_bh = p.num_seqs * p.H;
+  const int n_bh = p.num_seqs * p.H * p.n_rg;
   if (static_cast<int>(blockIdx.x) >= n_bh) {
     const int idx = blockIdx.x - n_bh;
     const int b = idx / p.table_chunks;
@@ -166,12 +167,13 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(PrologueArgs p) {
     return;
   }
   __shared__ float qs[4][D];
-  const int b = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int b = blockIdx.x / (p.H * p.n_rg), h = (blockIdx.x / p.n_rg) % p.H, rg = blockIdx.x % p.n_rg;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   {
     float y0 = 0.0f, y1 = 0.0f;
-    if (wave < p.R) {
-      const size_t rj = (static_cast<size_t>(b) * p.Nq + wave / p.G) * p.Hq + h * p.G + wave % p.G;
+    const int r = 4 * rg + wave;  // query row of this wave within the head's R rows
+    if (r < p.R) {
+      const size_t rj = (static_cast<size_t>(b) * p.Nq + r / p.G) * p.Hq + h * p.G + r % p.G;
       y0 = load_elem<DT>(p.q, rj * D + lane);
       y1 = load_elem<DT>(p.q, rj * D + lane + 64);
       rotate_query_wave(y0, y1, p.rk, h, lane);
@@ -383,7 +385,10 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
 __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float red[kWaves][4][4 + D];  // per wave, per row: m, l, z, flag, acc[128]
   __shared__ float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s = blockIdx.x, b = blockIdx.z;
+  const int h = blockIdx.y / a.n_rg, rg = blockIdx.y % a.n_rg;  // KV head, group of 4 query rows
+  const int row0 = 4 * rg, nrows = min(4, a.R - row0);
+  const size_t unit = (static_cast<size_t>(b) * a.H + h) * a.n_rg + rg;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   Ctx c;
@@ -408,18 +413,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   // ---- query digits (key-side A operand: row c = 4 r + d, k-slice g) and this lane's query row g
   State st;
   {
-    const int4 *dsrc = reinterpret_cast<const int4 *>(a.qdig + ((static_cast<size_t>(b) * a.H + h) * 64 + lane) * 8);
+    const int4 *dsrc = reinterpret_cast<const int4 *>(a.qdig + (unit * 64 + lane) * 8);
     const int4 d0 = dsrc[0], d1 = dsrc[1];
     st.bk[0] = v4i{d0.x, d0.y, d0.z, d0.w};
     st.bk[1] = v4i{d1.x, d1.y, d1.z, d1.w};
   }
-  const int hr = c.g;  // query row of the key-side lanes
-  st.row_ok = hr < a.R;
+  const int hr = c.g;  // query row (within the group) of the key-side lanes
+  st.row_ok = hr < nrows;
   {
-    const int qi = hr / a.G, gh = hr % a.G;
+    const int r = row0 + hr, qi = r / a.G, gh = r % a.G;
     const size_t rj = (static_cast<size_t>(b) * a.Nq + qi) * a.Hq + h * a.G + gh;
     st.qsum = st.row_ok ? a.qsum[rj] : 0.0f;
-    st.unscale = ldexpf(1.0f, -a.qexp[(static_cast<size_t>(b) * a.H + h) * 4 + hr]);
+    st.unscale = ldexpf(1.0f, -a.qexp[unit * 4 + hr]);
   }
   const int x = lane & 3;
   st.sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
         float v = (facc[(4 * k + i) * 64] + static_cast<float>(byte_sum(st.accv[k][i], x))) * (wbyte * slot_inv(e));
         v += fdpp_xor1(v);
         v += fdpp_xor2(v);
-        if (x == 0 && vr < a.R) red[wave][vr][4 + 8 * (4 * c.g + i) + 4 * hf + e] = v;
+        if (x == 0 && vr < nrows) red[wave][vr][4 + 8 * (4 * c.g + i) + 4 * hf + e] = v;
       }
   if (c.c == 0 && st.row_ok) {
     red[wave][hr][0] = st.have_ref ? -static_cast<float>(st.kappa) : -INFINITY;
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   __syncthreads();
 
   // ---- merge the 4 waves (base-2 log-sum-exp) and write this split's partial
-  for (int idx = threadIdx.x; idx < a.R * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
     const int r = idx / D, i = idx % D;
     float mstar = -INFINITY;
     bool nan = false;
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
       z += sc * red[w2][r][2];
       acc += sc * red[w2][r][4 + i];
     }
-    const int qq = r / a.G, g2 = r % a.G;
+    const int qq = (row0 + r) / a.G, g2 = (row0 + r) % a.G;
     const size_t row = static_cast<size_t>(b) * a.Nq + qq;
     float *dst = a.part + ((row * a.Hq + h * a.G + g2) * a.splits + s) * (D + 4);
     dst[4 + i] = mstar == -INFINITY ? 0.0f : acc;
@@ -522,7 +527,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
 }  // namespace
 
 bool decode_mfma_supported(const DecodePlan &pl, int page_size) {
-  return pl.rows_per_head <= 4 && page_size % 16 == 0 &&
+  return pl.rows_per_head <= kMaxRows && page_size % 16 == 0 &&
          static_cast<int64_t>(pl.H) * 72 * page_size < (static_cast<int64_t>(1) << 31);
 }
 
@@ -540,6 +545,7 @@ hipError_t launch_decode_prologue(const DecodePlan &pl, const void *q, int dtype
   p.H = pl.H;
   p.Nq = pl.queries_per_seq;
   p.num_seqs = pl.num_seqs;
+  p.n_rg = (pl.rows_per_head + 3) / 4;
   p.qrot = qrot;
   p.qsum = qsum;
   p.qdig = qdig;
@@ -552,7 +558,7 @@ hipError_t launch_decode_prologue(const DecodePlan &pl, const void *q, int dtype
   p.tiles_per_seq = pl.tiles_per_seq;
   p.table_chunks = (pl.tiles_per_seq + 255) / 256;
   p.tiles = tiles;
-  const dim3 grid(pl.num_seqs * pl.H + pl.num_seqs * p.table_chunks);
+  const dim3 grid(pl.num_seqs * pl.H * p.n_rg + pl.num_seqs * p.table_chunks);
   if (dtype == KVQ_F32)
     hipLaunchKernelGGL(decode_prologue_kernel<KVQ_F32>, grid, dim3(256), 0, stream, p);
   else
@@ -571,6 +577,7 @@ hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const i
   a.Hq = pl.Hq;
   a.H = pl.H;
   a.Nq = pl.queries_per_seq;
+  a.n_rg = (pl.rows_per_head + 3) / 4;
   a.split_tokens = pl.split_tokens;
   a.splits = pl.splits;
   a.max_seq_len = pl.max_seq_len;
@@ -582,7 +589,7 @@ hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const i
   a.qsum = qsum;
   a.tiles = tiles;
   a.part = part;
-  hipLaunchKernelGGL(decode_mfma_kernel, dim3(pl.splits, pl.H, pl.num_seqs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_mfma_kernel, dim3(pl.splits, pl.H * a.n_rg, pl.num_seqs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
