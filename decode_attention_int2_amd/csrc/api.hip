@@ -37,20 +37,26 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct CandidateLayout {
   int64_t num_pages;
-  DecodePlan plan;
-  size_t off_cache, off_dec, off_seqlen, off_ohat, off_oref, off_nmse, total;
+  DecodePlan plan;      // matrix-core decode of the quantized variants
+  DecodePlan ref_plan;  // full-precision reference readout (VALU kernel): more splits
+  size_t off_cache, off_dec, off_refdec, off_seqlen, off_ohat, off_oref, off_nmse, total;
 };
 
 CandidateLayout candidate_layout(int64_t T, int H, int Hq, int Nq, int C, int n_clip) {
   CandidateLayout L{};
   L.num_pages = (T + 15) / 16;
   L.plan = make_decode_plan(1, Nq, Hq, H, static_cast<int>(T), 0, 0);
+  // the reference kernel runs one workgroup per (split, KV head) for all rows: ~4096 workgroups
+  const int ref_splits = (4096 + H - 1) / H;
+  L.ref_plan = make_decode_plan(1, Nq, Hq, H, static_cast<int>(T), 0, ref_splits);
   const int U = H;  // upper bound over both modes
   size_t off = 0;
   L.off_cache = off;
   off = align256(off + kvq_cache_bytes(L.num_pages, 16, H));
   L.off_dec = off;
   off = align256(off + L.plan.total);
+  L.off_refdec = off;
+  off = align256(off + L.ref_plan.total);
   L.off_seqlen = off;
   off = align256(off + sizeof(int32_t));
   L.off_ohat = off;
@@ -218,10 +224,17 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
   const size_t stride_u = static_cast<size_t>(num_candidates) * num_clips * Nq;
 
-  // Full-precision reference readout of the raw K, V.
-  KVQ_TRY(launch_query_rotation(q, dtype, pl, ident, qrot, qsum, stream));
-  KVQ_TRY(launch_reference_split(pl, k, v, dtype, num_tokens, qrot, part, stream));
-  KVQ_TRY(launch_combine(pl, part, ident, o_ref, nullptr, stream));
+  // Full-precision reference readout of the raw K, V (own plan and workspace region).
+  {
+    const DecodePlan &rp = L.ref_plan;
+    uint8_t *rdec = ws + L.off_refdec;
+    float *rq = reinterpret_cast<float *>(rdec + rp.off_qrot);
+    float *rs = reinterpret_cast<float *>(rdec + rp.off_qsum);
+    float *rpart = reinterpret_cast<float *>(rdec + rp.off_part);
+    KVQ_TRY(launch_query_rotation(q, dtype, rp, ident, rq, rs, stream));
+    KVQ_TRY(launch_reference_split(rp, k, v, dtype, num_tokens, rq, rpart, stream));
+    KVQ_TRY(launch_combine(rp, rpart, ident, o_ref, nullptr, stream));
+  }
   KVQ_TRY(launch_fill_i32(seq_len, static_cast<int32_t>(num_tokens), 1, stream));
   for (int r = 0; r < num_candidates; ++r) {
     const RotDev rot = to_dev(candidates[r]);

@@ -311,56 +311,62 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
     }
   };
 
-  int64_t tile = tile_begin + wave;
-  if (tile >= tile_end) return;
-  uint4 xcur[4], xnext[4];
-  load_tile(tile, xcur);
-  for (; tile < tile_end; tile += kQWaves) {
-    load_tile(min(tile + kQWaves, tile_end - 1), xnext);  // prefetch (the last tile re-reads itself)
-
-    // ---- rotated values y[nt][i] = dim 32g + 4nt + i of token tk
-    float y[8][4];
+  // rotated values y[nt][i] = dim 32g + 4nt + i of token tk of the tile whose
+  // 16 B slices this lane holds (for the identity: its 32 dims directly)
+  auto rotate_pair = [&](const uint4 (&x0)[4], const uint4 (&x1)[4], float (&y0)[8][4], float (&y1)[8][4]) {
     if constexpr (KIND == KVQ_ROT_IDENTITY) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t w[4] = {xcur[ks].x, xcur[ks].y, xcur[ks].z, xcur[ks].w};
+        const uint32_t w0[4] = {x0[ks].x, x0[ks].y, x0[ks].z, x0[ks].w};
+        const uint32_t w1[4] = {x1[ks].x, x1[ks].y, x1[ks].z, x1[ks].w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float v = bf16_to_float((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-          y[2 * ks + (j >> 2)][j & 3] = v;
+          y0[2 * ks + (j >> 2)][j & 3] = bf16_to_float((w0[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+          y1[2 * ks + (j >> 2)][j & 3] = bf16_to_float((w1[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
         }
       }
     } else {
-      v4f acc[8];
+      // each A operand (rotation slice) read from LDS once feeds both tiles
+      v4f acc0[8], acc1[8];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int nt = 0; nt < 8; ++nt) acc0[nt] = acc1[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int pp = 0; pp < kParts; ++pp)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const v8bf bop = __builtin_bit_cast(v8bf, xcur[ks]);
+          const v8bf b0 = __builtin_bit_cast(v8bf, x0[ks]);
+          const v8bf b1 = __builtin_bit_cast(v8bf, x1[ks]);
 #pragma unroll
           for (int nt = 0; nt < 8; ++nt) {
             const v8bf aop = __builtin_bit_cast(v8bf, ash[((pp * 4 + ks) * 8 + nt) * 64 + lane]);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc[nt], 0, 0, 0);
+            acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b0, acc0[nt], 0, 0, 0);
+            acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b1, acc1[nt], 0, 0, 0);
           }
         }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[nt][i] = acc[nt][i] * scale;
+        for (int i = 0; i < 4; ++i) {
+          y0[nt][i] = acc0[nt][i] * scale;
+          y1[nt][i] = acc1[nt][i] * scale;
+        }
     }
     if constexpr (kCenter) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const float4 m = *reinterpret_cast<const float4 *>(&mrot[32 * g + 4 * nt]);
-        y[nt][0] = y[nt][0] - m.x;
-        y[nt][1] = y[nt][1] - m.y;
-        y[nt][2] = y[nt][2] - m.z;
-        y[nt][3] = y[nt][3] - m.w;
+        const float mm[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y0[nt][i] = y0[nt][i] - mm[i];
+          y1[nt][i] = y1[nt][i] - mm[i];
+        }
       }
     }
+  };
 
+  // quantize, pack and write token tk of `tile` from its rotated values
+  auto finish_tile = [&](float (&y)[8][4], int64_t tile) {
     // ---- group statistics of token tk (its 4 lanes g hold 32 dims each)
     float mn = y[0][0], mx = y[0][0];
 #pragma unroll
@@ -465,8 +471,29 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
       const uint32_t meta = f16_bits(sh) | (f16_bits(zh) << 16);
       *reinterpret_cast<uint32_t *>(base + (a.side ? 68 : 64) * a.P + 4 * p) = meta;
     }
+  };
+
+  // waves take tile pairs (2w, 2w+1), (2w+8, 2w+9), ...; the next pair is
+  // fetched while one is rotated and written (past the end loads re-read the
+  // last tile)
+  int64_t tile = tile_begin + 2 * wave;
+  if (tile >= tile_end) return;
+  uint4 xa[4], xb[4], na[4], nb[4];
+  load_tile(tile, xa);
+  load_tile(min(tile + 1, tile_end - 1), xb);
+  for (; tile < tile_end; tile += 2 * kQWaves) {
+    const int64_t nxt = tile + 2 * kQWaves;
+    load_tile(min(nxt, tile_end - 1), na);
+    load_tile(min(nxt + 1, tile_end - 1), nb);
+    float ya[8][4], yb[8][4];
+    rotate_pair(xa, xb, ya, yb);
+    finish_tile(ya, tile);
+    if (tile + 1 < tile_end) finish_tile(yb, tile + 1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) xcur[ks] = xnext[ks];
+    for (int ks = 0; ks < 4; ++ks) {
+      xa[ks] = na[ks];
+      xb[ks] = nb[ks];
+    }
   }
 }
 
