@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(QuantArgs a) {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kQTiles = 32;       // 16-token tiles per workgroup
+constexpr int kQTiles = 64;       // 16-token tiles per workgroup
 constexpr int kQWaves = 4;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic rounds x to an integer (ties to even)
 constexpr uint32_t kMagicBits = 0x4B400000u;
@@ -211,7 +211,8 @@ struct FastArgs {
   uint8_t *pages;
   int64_t num_pages;
   int P;
-  int side;  // 0 keys, 1 values
+  int side;     // 0 keys, 1 values
+  int p_shift;  // log2(P) if P is a power of two, else -1
 };
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -286,7 +287,8 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
             r = static_cast<double>(a.matrix[(static_cast<size_t>(h) * D + k) * D + d]);
           acc += static_cast<double>(mu[k]) * r;
         }
-        mrot[d] = static_cast<float>(acc);
+        // stored divided by the scale applied after the product (1/sqrt(128) for signed Hadamard)
+        mrot[d] = static_cast<float>(KIND == KVQ_ROT_SIGNED_HADAMARD ? acc * __builtin_sqrt(128.0) : acc);
       }
     }
   }
@@ -301,14 +303,18 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
   const int qi = tk & 3;
 
   // this lane's loads: 4 x 16 bytes of token tk (B operand k-slices, or 32 dims for identity)
-  auto load_tile = [&](int64_t tile, uint4 (&xb)[4]) {
-    const int64_t t = min(tile * 16 + tk, a.T - 1);
+  // this lane's 4 x 16 B of token tk of `tile` and the token's destination
+  // slot (-1: not written), fetched together so the slot's latency is hidden
+  auto load_tile = [&](int64_t tile, uint4 (&xb)[4], int64_t &slot) {
+    const int64_t tt = tile * 16 + tk;
+    const int64_t t = min(tt, a.T - 1);
     const uint16_t *row = a.x + static_cast<size_t>(t) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int off = KIND == KVQ_ROT_IDENTITY ? 32 * g + 8 * ks : 32 * ks + 8 * g;
       xb[ks] = *reinterpret_cast<const uint4 *>(row + off);
     }
+    slot = tt < a.T ? (a.slot_mapping ? a.slot_mapping[t] : t) : -1;
   };
 
   // rotated values y[nt][i] = dim 32g + 4nt + i of token tk of the tile whose
@@ -330,28 +336,42 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
       v4f acc0[8], acc1[8];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc0[nt] = acc1[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      // the 8 A slices of a k-step are read from LDS together, one step ahead
+      // of their MFMAs (the scheduler barriers keep the reads from being
+      // sunk next to their uses, which would expose the LDS latency per MFMA)
+      uint4 acur[8], anext[8];
 #pragma unroll
-      for (int pp = 0; pp < kParts; ++pp)
+      for (int nt = 0; nt < 8; ++nt) acur[nt] = ash[nt * 64 + lane];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const v8bf b0 = __builtin_bit_cast(v8bf, x0[ks]);
-          const v8bf b1 = __builtin_bit_cast(v8bf, x1[ks]);
+      for (int step = 0; step < kParts * 4; ++step) {
+        const int ks = step & 3;
+        if (step + 1 < kParts * 4) {
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
-            const v8bf aop = __builtin_bit_cast(v8bf, ash[((pp * 4 + ks) * 8 + nt) * 64 + lane]);
-            acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b0, acc0[nt], 0, 0, 0);
-            acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b1, acc1[nt], 0, 0, 0);
-          }
+          for (int nt = 0; nt < 8; ++nt) anext[nt] = ash[((step + 1) * 8 + nt) * 64 + lane];
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const v8bf b0 = __builtin_bit_cast(v8bf, x0[ks]);
+        const v8bf b1 = __builtin_bit_cast(v8bf, x1[ks]);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const v8bf aop = __builtin_bit_cast(v8bf, acur[nt]);
+          acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b0, acc0[nt], 0, 0, 0);
+          acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b1, acc1[nt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acur[nt] = anext[nt];
+      }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          y0[nt][i] = acc0[nt][i] * scale;
-          y1[nt][i] = acc1[nt][i] * scale;
+          y0[nt][i] = acc0[nt][i];  // rotated value / scale (the scale is applied in finish_tile)
+          y1[nt][i] = acc1[nt][i];
         }
     }
     if constexpr (kCenter) {
+      // mrot holds mu R / scale for rotated kinds (mu for the identity)
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const float4 m = *reinterpret_cast<const float4 *>(&mrot[32 * g + 4 * nt]);
@@ -366,7 +386,7 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
   };
 
   // quantize, pack and write token tk of `tile` from its rotated values
-  auto finish_tile = [&](float (&y)[8][4], int64_t tile) {
+  auto finish_tile = [&](float (&y)[8][4], int64_t slot) {
     // ---- group statistics of token tk (its 4 lanes g hold 32 dims each)
     float mn = y[0][0], mx = y[0][0];
 #pragma unroll
@@ -380,6 +400,10 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mn = fminf(mn, __shfl_xor(mn, 32));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if constexpr (KIND != KVQ_ROT_IDENTITY) {  // min / max of y = u * scale (scale > 0: monotone)
+      mn = mn * scale;
+      mx = mx * scale;
+    }
     float lo = a.clip * mn;
     const float hi = a.clip * mx;
     const float span = hi - lo;
@@ -391,6 +415,8 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
     const float s = static_cast<float>(sh);
     const float z = static_cast<float>(zh);
     const float inv = s != 0.0f ? 1.0f / s : 0.0f;  // s == 0: every code is 0
+    // rotated kinds: t = (u scale - z) inv computed as u (scale inv) - z inv
+    const float si = scale * inv, zi = z * inv;
 
     // ---- codes, packed 16 per dword by shift-add of magic-biased values
     uint32_t cw[2];
@@ -401,23 +427,20 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
       for (int nt = 3; nt >= 0; --nt)
 #pragma unroll
         for (int i = 3; i >= 0; --i) {
-          const float d = y[4 * half + nt][i] - z;
           float tq;
           if constexpr (KIND == KVQ_ROT_IDENTITY) {
-            const float t = d * inv;
+            const float t = (y[4 * half + nt][i] - z) * inv;
             tq = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f) + kMagic;
           } else {
-            tq = __builtin_amdgcn_fmed3f(__builtin_fmaf(d, inv, kMagic), kMagic, kMagic + 3.0f);
+            const float t = __builtin_fmaf(y[4 * half + nt][i], si, -zi);
+            tq = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f) + kMagic;
           }
           acc = (acc << 2) + __float_as_uint(tq);
         }
       cw[half] = acc - magic_pack_offset();
     }
 
-    // ---- destination slot of token tk
-    const int64_t t = tile * 16 + tk;
-    int64_t slot = -1;
-    if (t < a.T) slot = a.slot_mapping ? a.slot_mapping[t] : t;
+    // ---- destination of token tk
     const bool valid = slot >= 0 && slot < slots;
     int64_t page = 0;
     int p = 0;
@@ -425,6 +448,10 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
       if constexpr (kWide) {
         page = slot / a.P;
         p = static_cast<int>(slot - page * a.P);
+      } else if (a.p_shift >= 0) {  // power-of-two page size
+        const uint32_t us = static_cast<uint32_t>(slot);
+        page = us >> a.p_shift;
+        p = static_cast<int>(us & static_cast<uint32_t>(a.P - 1));
       } else {
         const uint32_t us = static_cast<uint32_t>(slot), up = static_cast<uint32_t>(a.P);
         const uint32_t pg = us / up;
@@ -479,21 +506,24 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
   int64_t tile = tile_begin + 2 * wave;
   if (tile >= tile_end) return;
   uint4 xa[4], xb[4], na[4], nb[4];
-  load_tile(tile, xa);
-  load_tile(min(tile + 1, tile_end - 1), xb);
+  int64_t sa, sb, sna, snb;
+  load_tile(tile, xa, sa);
+  load_tile(min(tile + 1, tile_end - 1), xb, sb);
   for (; tile < tile_end; tile += 2 * kQWaves) {
     const int64_t nxt = tile + 2 * kQWaves;
-    load_tile(min(nxt, tile_end - 1), na);
-    load_tile(min(nxt + 1, tile_end - 1), nb);
+    load_tile(min(nxt, tile_end - 1), na, sna);
+    load_tile(min(nxt + 1, tile_end - 1), nb, snb);
     float ya[8][4], yb[8][4];
     rotate_pair(xa, xb, ya, yb);
-    finish_tile(ya, tile);
-    if (tile + 1 < tile_end) finish_tile(yb, tile + 1);
+    finish_tile(ya, sa);
+    if (tile + 1 < tile_end) finish_tile(yb, sb);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       xa[ks] = na[ks];
       xb[ks] = nb[ks];
     }
+    sa = sna;
+    sb = snb;
   }
 }
 
@@ -535,10 +565,13 @@ hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_
               1.0 / __builtin_sqrt(128.0)};
   if (dtype == KVQ_BF16) {
     const bool wide = num_pages * static_cast<int64_t>(page_size) > (static_cast<int64_t>(1) << 31);
+    int p_shift = -1;
+    for (int sh = 4; sh < 31; ++sh)
+      if (page_size == (1 << sh)) p_shift = sh;
     FastArgs fk{static_cast<const uint16_t *>(k), num_tokens, H, slot_mapping, rk.signs, rk.matrix, key_mean,
-                clip_k, pages, num_pages, page_size, 0};
+                clip_k, pages, num_pages, page_size, 0, p_shift};
     FastArgs fv{static_cast<const uint16_t *>(v), num_tokens, H, slot_mapping, rv.signs, rv.matrix, nullptr,
-                clip_v, pages, num_pages, page_size, 1};
+                clip_v, pages, num_pages, page_size, 1, p_shift};
     hipError_t e = launch_fast_side(fk, rk.kind, wide, stream);
     if (e != hipSuccess) return e;
     return launch_fast_side(fv, rv.kind, wide, stream);
