@@ -396,10 +396,17 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
         mn = fminf(mn, y[nt][i]);
         mx = fmaxf(mx, y[nt][i]);
       }
-    mn = fminf(mn, __shfl_xor(mn, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mn = fminf(mn, __shfl_xor(mn, 32));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // across the token's 4 lanes (l, l^16, l^32, l^48) with VALU lane permutes
+    {
+      const auto n16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mn = fminf(__uint_as_float(n16[0]), __uint_as_float(n16[1]));
+      mx = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+      const auto n32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mn = fminf(__uint_as_float(n32[0]), __uint_as_float(n32[1]));
+      mx = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    }
     if constexpr (KIND != KVQ_ROT_IDENTITY) {  // min / max of y = u * scale (scale > 0: monotone)
       mn = mn * scale;
       mx = mx * scale;
