@@ -9,16 +9,23 @@ inverse value rotation, W_O), on the paged batched-decode workload:
 per head, W_O [4096, 4096].  Inputs are seeded synthetic data resident in HBM
 before the timed region.
 
-Two cache buffers alternate: step i writes cache i%2 and decodes cache
-(i+1)%2 (written one step earlier and followed by >2 GB of other traffic), so
-the decode reads its 302 MB from HBM, not from the 256 MB Infinity Cache.
+Three cache buffers rotate: step i writes cache i%3 and decodes cache
+(i+1)%3, written earlier and followed by >2 GB of other traffic, so the
+decode reads its 302 MB from HBM, not from the 256 MB Infinity Cache.
+
+Timed regions, each a run of back-to-back calls on one stream between two
+HIP events (an event recorded between two kernels leaves the GPU idle for
+several microseconds, so none is recorded inside a region):
+  * steps: K full steps (cache write + decode with W_O) -> ms_per_step;
+  * attention: K decode calls without W_O (query rotation, split-K attention,
+    split merge and inverse value rotation: one kernel launch with a signed
+    Hadamard R_K) over the rotating caches -> decode_attn_us;
+  * cache write: K kvq_quantize calls -> quantize_us;
+  * decode call: K decode calls with W_O -> decode_call_us.
 
 Prints one JSON line.  value = effective KV GB/s of decode attention: 72
-bytes per cached token per KV head / the average time of the attention part
-of the decode call (query rotation, split-K attention, split merge and inverse
-value rotation; the W_O projection is timed separately), from HIP events
-recorded on the launch stream.  roofline = the split-K kernel alone (its own
-events), the dominant kernel.
+bytes per cached token per KV head / decode_attn_us.  roofline = the decode
+kernel (decode_mfma_kernel, the only launch of the attention region).
 """
 from __future__ import annotations
 
@@ -130,7 +137,8 @@ def main():
     w = synthetic.make(WORKLOAD, dev)
     B, T, H, Hq, dm, P = w.num_seqs, w.tokens, w.H, w.Hq, w.d_model, w.page_size
     rot = kvq.Rotation(w.rot_k.kind, signs=w.rot_k.signs)
-    caches = [kvq.Cache(w.num_pages, P, H, device=dev) for _ in range(2)]
+    NC = 3
+    caches = [kvq.Cache(w.num_pages, P, H, device=dev) for _ in range(NC)]
     max_pages = w.page_table.shape[1]
     rows = B * w.queries_per_seq
     out_o = torch.empty((rows, Hq, 128), dtype=torch.float32, device=dev)
@@ -139,43 +147,44 @@ def main():
                      device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        kvq.kvq_quantize(w.k, w.v, caches[i % 2], rot, rot, clip_k=w.clip_k, clip_v=w.clip_v,
+    def quantize(i):
+        kvq.kvq_quantize(w.k, w.v, caches[i % NC], rot, rot, clip_k=w.clip_k, clip_v=w.clip_v,
                          slot_mapping=w.slot_mapping)
-        if ev is not None:
-            ev[1].record(stream)
-        kvq.kvq_decode_attn(w.q, B, 1, caches[(i + 1) % 2], w.page_table, max_pages, w.seq_lens, T, rot, rot, out_o,
-                            w_o=w.w_o, out_y=out_y, workspace=ws, num_splits=a.num_splits,
-                            split_events=None if ev is None else (ev[2], ev[3], ev[5]))
-        if ev is not None:
-            ev[4].record(stream)
 
-    for i in range(2):                      # both cache buffers hold a valid cache before warmup
-        kvq.kvq_quantize(w.k, w.v, caches[i], rot, rot, clip_k=w.clip_k, clip_v=w.clip_v,
-                         slot_mapping=w.slot_mapping)
+    def decode(i, with_wo=True):
+        kvq.kvq_decode_attn(w.q, B, 1, caches[i % NC], w.page_table, max_pages, w.seq_lens, T, rot, rot, out_o,
+                            w_o=w.w_o if with_wo else None, out_y=out_y if with_wo else None, workspace=ws,
+                            num_splits=a.num_splits)
+
+    def step(i):
+        quantize(i)
+        decode(i + 1)
+
+    def timed(fn, n):
+        """Average GPU time (ms) of n back-to-back calls fn(i), one event pair around them."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for i in range(NC):                     # every cache buffer holds a valid cache before warmup
+        quantize(i)
     for i in range(a.warmup):
         step(i)
+        decode(i, with_wo=False)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
-    for ev in events:          # torch creates the HIP event on first record; the library records 2 of them
-        for e in ev:
-            e.record(stream)
-    torch.cuda.synchronize()
-    assert all(e.cuda_event != 0 for ev in events for e in ev)
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(a.warmup + i, events[i])
-    torch.cuda.synchronize()
+    step_ms = timed(lambda i: step(a.warmup + i), a.steps)
     wall = time.perf_counter() - t0
+    attn_ms = timed(lambda i: decode(i, with_wo=False), a.steps)
+    quant_ms = timed(quantize, a.steps)
+    decode_ms = timed(decode, a.steps)
 
-    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / a.steps
-    split_ms = sum(e[2].elapsed_time(e[3]) for e in events) / a.steps
-    decode_ms = sum(e[1].elapsed_time(e[4]) for e in events) / a.steps
-    attn_ms = sum(e[1].elapsed_time(e[5]) for e in events) / a.steps
     kv_bytes = B * T * H * BYTES_PER_TOKEN_HEAD
-    split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
     attn_gbs = kv_bytes / (attn_ms * 1e-3) / 1e9
     tokens = B * T
     quant_bytes = tokens * H * (2 * 128 * 2 + BYTES_PER_TOKEN_HEAD)
@@ -196,7 +205,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(wall * 1e3 / a.steps, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -208,15 +217,13 @@ def main():
                    "rotation": "signed_hadamard", "clip_k": w.clip_k, "clip_v": w.clip_v},
         "pct_hbm_peak": round(100.0 * attn_gbs / HBM_PEAK_GBS, 2),
         "decode_attn_us": round(attn_ms * 1e3, 2),
-        "split_kernel_gbs": round(split_gbs, 1),
-        "split_kernel_pct_hbm_peak": round(100.0 * split_gbs / HBM_PEAK_GBS, 2),
+        "decode_call_us": round(decode_ms * 1e3, 2),
         "quantize_mtok_s": round(tokens / (quant_ms * 1e-3) / 1e6, 2),
         "quantize_gbs": round(quant_gbs, 1),
         "quantize_us": round(quant_ms * 1e3, 2),
-        "decode_split_us": round(split_ms * 1e3, 2),
-        "decode_call_us": round(decode_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "wall_ms_per_step": round(wall * 1e3 / a.steps, 4),
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_mfma_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": base,
     }

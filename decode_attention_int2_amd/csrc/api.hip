@@ -148,24 +148,31 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   float *qsum = reinterpret_cast<float *>(ws + pl.off_qsum);
   float *part = reinterpret_cast<float *>(ws + pl.off_part);
   float *ypart = reinterpret_cast<float *>(ws + pl.off_ypart);
-  int32_t *qdig = reinterpret_cast<int32_t *>(ws + pl.off_qdig);
-  int32_t *qexp = reinterpret_cast<int32_t *>(ws + pl.off_qexp);
-  const bool mfma = decode_mfma_supported(pl, cache->page_size);
-  uint64_t *tiles = reinterpret_cast<uint64_t *>(ws + pl.off_tiles);
-  if (mfma)
-    KVQ_TRY(launch_decode_prologue(pl, q, dtype, to_dev(*rot_k), cache->pages, cache->num_pages, cache->page_size,
-                                   page_table, max_pages_per_seq, qrot, qsum, qdig, qexp, tiles, stream));
-  else
-    KVQ_TRY(launch_query_rotation(q, dtype, pl, to_dev(*rot_k), qrot, qsum, stream));
-  if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
-  if (mfma)
-    KVQ_TRY(launch_decode_split_mfma(pl, cache->page_size, seq_lens, qdig, qexp, qsum, tiles, part, stream));
-  else
+  float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
+  const RotDev rk = to_dev(*rot_k), rv = to_dev(*rot_v);
+  if (decode_mfma_supported(pl, cache->page_size)) {
+    // one launch: query rotation, split attention, merge, R_V^T (a dense R_K
+    // is applied by its own launch first)
+    const void *qk = q;
+    RotDev rq = rk;
+    if (rk.kind == KVQ_ROT_DENSE) {
+      KVQ_TRY(launch_query_rotation(q, dtype, pl, rk, qrot, qsum, stream));
+      qk = qrot;
+      rq = RotDev{kRotPrescaled, nullptr, nullptr};
+    }
+    if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
+    KVQ_TRY(launch_decode_mfma(pl, qk, dtype, rq, rv, cache->pages, cache->num_pages, cache->page_size, page_table,
+                               max_pages_per_seq, seq_lens, part, reinterpret_cast<uint64_t *>(ws + pl.off_cnt),
+                               out_o, ot, stream));
+    if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
+  } else {
+    KVQ_TRY(launch_query_rotation(q, dtype, pl, rk, qrot, qsum, stream));
+    if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
     KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
                                 seq_lens, qrot, qsum, part, stream));
-  if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
-  float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
-  KVQ_TRY(launch_combine(pl, part, to_dev(*rot_v), out_o, ot, stream));
+    if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
+    KVQ_TRY(launch_combine(pl, part, rv, out_o, ot, stream));
+  }
   if (events && events->attn_stop) KVQ_TRY(hipEventRecord(events->attn_stop, stream));
   if (w_o) KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, ypart, out_y, stream));
   return KVQ_OK;
@@ -216,9 +223,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   float *qrot = reinterpret_cast<float *>(dec + pl.off_qrot);
   float *qsum = reinterpret_cast<float *>(dec + pl.off_qsum);
   float *part = reinterpret_cast<float *>(dec + pl.off_part);
-  int32_t *qdig = reinterpret_cast<int32_t *>(dec + pl.off_qdig);
-  int32_t *qexp = reinterpret_cast<int32_t *>(dec + pl.off_qexp);
-  uint64_t *tiles = reinterpret_cast<uint64_t *>(dec + pl.off_tiles);
+  uint64_t *counters = reinterpret_cast<uint64_t *>(dec + pl.off_cnt);
   const bool mfma = decode_mfma_supported(pl, 16);
   const RotDev ident{KVQ_ROT_IDENTITY, nullptr, nullptr};
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
@@ -238,20 +243,25 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   KVQ_TRY(launch_fill_i32(seq_len, static_cast<int32_t>(num_tokens), 1, stream));
   for (int r = 0; r < num_candidates; ++r) {
     const RotDev rot = to_dev(candidates[r]);
-    if (mfma)
-      KVQ_TRY(launch_decode_prologue(pl, q, dtype, rot, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages),
-                                     qrot, qsum, qdig, qexp, tiles, stream));
-    else
+    // matrix-core path: queries rotated inside the decode launch, except a dense R_K (once per candidate)
+    const void *qk = q;
+    RotDev rq = rot;
+    if (!mfma || rot.kind == KVQ_ROT_DENSE) {
       KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
+      qk = qrot;
+      rq = RotDev{kRotPrescaled, nullptr, nullptr};
+    }
     for (int i = 0; i < num_clips; ++i) {
       KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips[i], clips[i], pages,
                               L.num_pages, 16, stream));
-      if (mfma)
-        KVQ_TRY(launch_decode_split_mfma(pl, 16, seq_len, qdig, qexp, qsum, tiles, part, stream));
-      else
+      if (mfma) {
+        KVQ_TRY(launch_decode_mfma(pl, qk, dtype, rq, rot, pages, L.num_pages, 16, nullptr,
+                                   static_cast<int>(L.num_pages), seq_len, part, counters, o_hat, nullptr, stream));
+      } else {
         KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
                                     qrot, qsum, part, stream));
-      KVQ_TRY(launch_combine(pl, part, rot, o_hat, nullptr, stream));
+        KVQ_TRY(launch_combine(pl, part, rot, o_hat, nullptr, stream));
+      }
       KVQ_TRY(launch_nmse_terms(o_hat, o_ref, w_o, dtype, Nq, Hq, H, d_model, mode,
                                 nmse_q + (static_cast<size_t>(r) * num_clips + i) * Nq, stride_u, stream));
     }

@@ -20,14 +20,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ float wave_maxf(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
 
 // ------------------------------------------------------------ rotations of one head vector
 // One wave holds a 128-vector as two registers per lane: x0 = x[lane],
@@ -384,78 +376,17 @@ __global__ __launch_bounds__(256) void reference_split_kernel(SplitArgs a) {
 // for the W_O projection, a copy of o laid out [row group][K][16 rows]).
 // One wave per (query row, query head).
 constexpr int kMaxCombineSplits = kMaxSplits;
-constexpr int kWoRows = 16;  // rows of o per W_O pass
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *part, int n_items, int splits, int Hq, int G,
                                                       RotDev rv, float *out_o, float *ot) {
   const int lane = threadIdx.x & 63;
   const int rj = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rj >= n_items) return;
-  const int row = rj / Hq, j = rj % Hq, h = j / G;
-  const float inv_sqrt_d = 0.08838834764831845f;
-  const float *p = part + static_cast<size_t>(rj) * splits * (D + 4);
-  float mloc = -INFINITY;
-  for (int s2 = lane; s2 < splits; s2 += 64) mloc = fmaxf(mloc, p[static_cast<size_t>(s2) * (D + 4)]);
-  const float mstar = wave_maxf(mloc);
-  float lloc = 0.0f, zloc = 0.0f, nanloc = 0.0f;
-  for (int s2 = lane; s2 < splits; s2 += 64) {
-    const float *q = p + static_cast<size_t>(s2) * (D + 4);
-    const float w = (q[0] == -INFINITY) ? 0.0f : exp2f(q[0] - mstar);
-    if (q[1] != q[1]) nanloc = 1.0f;
-    if (w != 0.0f) {
-      lloc += w * q[1];
-      zloc += w * q[2];
-    }
-  }
-  const float l = wave_sum(lloc), z = wave_sum(zloc);
-  const bool any_nan = wave_maxf(nanloc) != 0.0f;
-  float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll 4
-  for (int s2 = 0; s2 < splits; ++s2) {
-    const float *q = p + static_cast<size_t>(s2) * (D + 4);
-    const float m = q[0];  // uniform
-    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
-    if (w != 0.0f) {
-      a0 += w * q[4 + lane];
-      a1 += w * q[4 + 64 + lane];
-    }
-  }
-  float o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
-  float o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
-  if (any_nan) o0 = o1 = __builtin_nanf("");
-  // out[i] = sum_c o'[c] R_V[i][c]
-  float r0 = o0, r1 = o1;
-  if (rv.kind == KVQ_ROT_SIGNED_HADAMARD) {
-    // R[i][c] = s_i H[i][c] / sqrt(128), H symmetric: out = s * (o' H) / sqrt(128)
-    fwht128(o0, o1, lane);
-    r0 = o0 * (static_cast<float>(rv.signs[h * D + lane]) * inv_sqrt_d);
-    r1 = o1 * (static_cast<float>(rv.signs[h * D + lane + 64]) * inv_sqrt_d);
-  } else if (rv.kind == KVQ_ROT_DENSE) {
-    const float *m0 = rv.matrix + (static_cast<size_t>(h) * D + lane) * D;
-    const float *m1 = m0 + 64 * D;
-    r0 = r1 = 0.0f;
-    for (int c = 0; c < D; c += 4) {
-      const float4 e0 = *reinterpret_cast<const float4 *>(m0 + c);
-      const float4 e1 = *reinterpret_cast<const float4 *>(m1 + c);
-      const float src = c < 64 ? o0 : o1;
-      const int cl = c & 63;
-      const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl));
-      const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 1));
-      const float v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 2));
-      const float v3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 3));
-      r0 += v0 * e0.x + v1 * e0.y + v2 * e0.z + v3 * e0.w;
-      r1 += v0 * e1.x + v1 * e1.y + v2 * e1.z + v3 * e1.w;
-    }
-  }
-  const int K = Hq * D;
-  const size_t base = static_cast<size_t>(row) * K + j * D;
-  out_o[base + lane] = r0;
-  out_o[base + lane + 64] = r1;
-  if (ot) {
-    float *dst = ot + (static_cast<size_t>(row / kWoRows) * K + j * D) * kWoRows + row % kWoRows;
-    dst[static_cast<size_t>(lane) * kWoRows] = r0;
-    dst[static_cast<size_t>(lane + 64) * kWoRows] = r1;
-  }
+  const int row = rj / Hq, j = rj % Hq;
+  float o0, o1;
+  merge_splits_wave(part + static_cast<size_t>(rj) * splits * (D + 4), splits, lane, o0, o1);
+  unrotate_value_wave(o0, o1, rv, j / G, lane);
+  store_output_wave(out_o, ot, row, j, Hq, lane, o0, o1);
 }
 
 // ------------------------------------------------------------ W_O projection
@@ -671,13 +602,8 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection
   off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * K * kWoRows * sizeof(float) : 0));
   const size_t n_rg_all = static_cast<size_t>(num_seqs) * H * ((queries_per_seq * (Hq / H) + 3) / 4);
-  pl.off_qdig = off;  // [num_seqs][H][row groups][64 lanes][8] int32
-  off = align(off + n_rg_all * 64 * 8 * sizeof(int32_t));
-  pl.off_qexp = off;  // [num_seqs][H][row groups][4 rows] int32
-  off = align(off + n_rg_all * 4 * sizeof(int32_t));
-  pl.tiles_per_seq = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
-  pl.off_tiles = off;  // [num_seqs][tiles_per_seq][2] uint64
-  off = align(off + static_cast<size_t>(num_seqs) * pl.tiles_per_seq * 2 * sizeof(uint64_t));
+  pl.off_cnt = off;  // [num_seqs][H][row groups] uint64
+  off = align(off + n_rg_all * sizeof(uint64_t));
   pl.total = off;
   return pl;
 }

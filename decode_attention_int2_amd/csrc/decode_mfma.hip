@@ -1,6 +1,9 @@
-// decode_mfma.hip -- split-K decode attention over the packed INT2 cache on
-// the gfx950 matrix cores (v_mfma_i32_16x16x64_i8), for up to 4 query rows
-// per KV head (GQA groups of <= 4 heads, one query per sequence).
+// decode_mfma.hip -- decode attention over the packed INT2 cache on the
+// gfx950 matrix cores (v_mfma_i32_16x16x64_i8) in one launch: query
+// rotation, split-K attention, split merge and inverse value rotation.  A
+// workgroup takes one group of 4 query rows of one (sequence, KV head) --
+// up to 64 rows per KV head: GQA group x queries per sequence -- and one
+// split of the sequence's tokens.
 //
 // [OptR] = "Output-Aware Rotation for INT2 KV-Cache Quantization":
 //   Appendix Eq. (21)-(22), (26): logit = (q R_K) . k_R / sqrt(128) against the
@@ -27,14 +30,21 @@
 //   kappa) and z = sum 2^(logit + kappa) z_t stay in fp32 per lane.  The bytes
 //   reach the MFMA's B layout (column 4 r + byte, k = 16 tokens per lane
 //   group) by a byte transpose inside each lane quad and one lane permutation.
-// Addresses: a small kernel resolves the page of every 16-token tile once per
-// decode step into absolute code / metadata base addresses; the split kernel
-// reads them with scalar loads and issues every vector load as scalar base +
-// per-lane constant offset.  The next 64-token block is fetched while the
-// current one is computed; tiles past the split end are clamped into its last
-// tile and masked.  The per-split result is written in the same (m, l, z,
-// acc[128]) form as the VALU kernel, with m = -kappa, and merged by the same
-// combine kernel.
+// Query: each workgroup rotates its own query rows (signed Hadamard by the
+//   fast transform; a dense R_K is applied by an earlier launch) and forms
+//   their digits while its first key / value loads are in flight.
+// Addresses: the page of every 16-token tile is read from the page table with
+//   scalar loads one block ahead and turned into code / metadata base
+//   addresses on the scalar unit; every vector load is scalar base + per-lane
+//   constant offset.  The next 64-token block is fetched while the current
+//   one is computed; tiles past the split end are clamped into its last tile
+//   and masked.
+// Merge: each split writes an (m, l, z, acc[128]) partial with m = -kappa;
+//   the last split of a (sequence, KV head, row group) to arrive (a tagged
+//   arrival counter) merges the partials, applies R_V^T and writes the output.
+#include <atomic>
+#include <chrono>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -102,92 +112,33 @@ __device__ __forceinline__ int byte_sum(int d, int x) {
 struct MfmaArgs {
   int R, G, Hq, H, Nq, n_rg;  // n_rg: groups of 4 query rows per KV head
   int split_tokens, splits, max_seq_len;
-  int P;
-  int tiles_per_seq;
-  const int32_t *seq_lens;
-  const int32_t *qdig;     // [num_seqs][H][n_rg][64 lanes][8] key-side A operand
-  const int32_t *qexp;     // [num_seqs][H][n_rg][4 rows] fixed-point shift S of each query row
-  const float *qsum;
-  const uint64_t *tiles;   // [num_seqs][tiles_per_seq][2] code base, metadata base (bit 0: bad page)
-  float *part;
-};
-
-// Prologue of the split kernel, one launch:
-//  * blocks [0, num_seqs*H*n_rg): one per (sequence, KV head, group of 4
-//    query rows).  Wave r rotates row 4 rg + r of the head's R rows (q' = q R_K
-//    log2(e)/sqrt(128)), writes q' and sum(q'); then wave 0 writes the
-//    fixed-point int8 digits of the group's rows in the key-side A-operand
-//    layout: lane (col, grp) gets the 8 dwords of query row col/4, digit
-//    col%4, for the two 64-dim MFMAs; dim 16*(2*grp + m) + 4*bb + e goes to
-//    dword [m][e], byte bb.  Slot e of the unpacked codes carries a factor
-//    1/slot_inv(e), divided out here.  Q = round(q' 2^S) with |Q| < 2^26 (S
-//    per query row from its largest |q'|).
-//  * the remaining blocks: absolute addresses of every 16-token tile of every
-//    sequence (head 0 of its page; the head's offset is part of the lanes'
-//    constant offsets):
-//      [0] page block + 32 * (position of the tile in its page)   K/V codes
-//      [1] page block + 64 P + 4 * (position)                     K/V metadata
-//    A page index outside the cache is replaced by page 0 and flagged in
-//    bit 0 of the metadata address.
-struct PrologueArgs {
-  const void *q;
-  RotDev rk;
-  int R, G, Hq, H, Nq, num_seqs, n_rg;
-  float *qrot, *qsum;
-  int32_t *qdig, *qexp;
-  const uint8_t *pages;
+  int P, p_shift;             // page size in tokens (a power of two) and its log2
+  int max_pages;
   int64_t num_pages;
-  int P;
-  const int32_t *page_table;
-  int max_pages, tiles_per_seq, table_chunks;
-  uint64_t *tiles;
+  uint64_t page_bytes;        // H * 72 * P
+  const uint8_t *pages;
+  // page of entry i of sequence b: (ptab[b * tab_stride + (i & tab_mask)] & val_mask) + (i & id_mask) + b * base_mul;
+  // with a page table: stride max_pages, masks ~0, ~0, 0, base_mul 0;
+  // without (pages b * max_pages + i): ptab = any readable int32, stride 0, masks 0, 0, ~0, base_mul max_pages
+  const int32_t *ptab;
+  int tab_stride, tab_mask, val_mask, id_mask, base_mul;
+  const int32_t *seq_lens;
+  const void *q;              // query rows (dtype of the launch), or rotated fp32 rows
+  RotDev rk, rv;
+  float *part;                // [rows][Hq][splits][132] split partials
+  unsigned long long *counters;  // [num_seqs][H][n_rg] arrival counters
+  uint32_t epoch;
+  float *out_o, *ot;
 };
 
-template <int DT>
-__global__ __launch_bounds__(256) void decode_prologue_kernel(PrologueArgs p) {
-  const int n_bh = p.num_seqs * p.H * p.n_rg;
-  if (static_cast<int>(blockIdx.x) >= n_bh) {
-    const int idx = blockIdx.x - n_bh;
-    const int b = idx / p.table_chunks;
-    const int i = (idx % p.table_chunks) * 256 + threadIdx.x;
-    if (i >= p.tiles_per_seq) return;
-    const int pi = (16 * i) / p.P, off = (16 * i) % p.P;
-    int64_t pg = (p.page_table && pi < p.max_pages)
-                     ? static_cast<int64_t>(p.page_table[static_cast<size_t>(b) * p.max_pages + pi])
-                     : static_cast<int64_t>(b) * p.max_pages + pi;
-    uint64_t flag = 0;
-    if (pi >= p.max_pages || pg < 0 || pg >= p.num_pages) {
-      pg = 0;
-      flag = 1;
-    }
-    const uint64_t blk = reinterpret_cast<uint64_t>(p.pages) + static_cast<uint64_t>(pg) * p.H * 72 * p.P;
-    uint64_t *e = p.tiles + (static_cast<size_t>(b) * p.tiles_per_seq + i) * 2;
-    e[0] = blk + 32 * off;
-    e[1] = (blk + 64 * static_cast<uint64_t>(p.P) + 4 * off) | flag;
-    return;
-  }
-  __shared__ float qs[4][D];
-  const int b = blockIdx.x / (p.H * p.n_rg), h = (blockIdx.x / p.n_rg) % p.H, rg = blockIdx.x % p.n_rg;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  {
-    float y0 = 0.0f, y1 = 0.0f;
-    const int r = 4 * rg + wave;  // query row of this wave within the head's R rows
-    if (r < p.R) {
-      const size_t rj = (static_cast<size_t>(b) * p.Nq + r / p.G) * p.Hq + h * p.G + r % p.G;
-      y0 = load_elem<DT>(p.q, rj * D + lane);
-      y1 = load_elem<DT>(p.q, rj * D + lane + 64);
-      rotate_query_wave(y0, y1, p.rk, h, lane);
-      p.qrot[rj * D + lane] = y0;
-      p.qrot[rj * D + lane + 64] = y1;
-      float sum = y0 + y1;
-      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-      if (lane == 0) p.qsum[rj] = sum;
-    }
-    qs[wave][lane] = y0;
-    qs[wave][lane + 64] = y1;
-  }
-  __syncthreads();
-  if (wave != 0) return;
+// Fixed-point int8 digits of the 4 query rows of a row group (qs: their q',
+// zero rows past the head's last row) in the key-side A-operand layout of
+// lane (col, grp): query row col/4, digit col%4; dim 16 (2 grp + m) + 4 bb + e
+// goes to dword [m][e], byte bb.  Slot e of the unpacked codes carries a
+// factor 1/slot_inv(e), divided out here.  Q = round(q' 2^S) with
+// |Q| < 2^26; S per query row from its largest |q'|.  Returns S of the
+// lane's digit row.
+__device__ __forceinline__ int query_digits(const float (*qs)[D], int lane, v4i bk[2]) {
   const int col = lane & 15, grp = lane >> 4, hr = col >> 2, dg = col & 3;
   float qv[2][16];
   float qabs = 0.0f;
@@ -207,7 +158,6 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(PrologueArgs p) {
   int e2 = 0;
   (void)frexpf(qabs, &e2);  // qabs < 2^e2
   const int qshift = 26 - e2;
-  int32_t *dst = p.qdig + (static_cast<size_t>(blockIdx.x) * 64 + lane) * 8;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -219,9 +169,92 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(PrologueArgs p) {
         const int dig = (dg == 0) ? (Q >> 21) : ((Q >> (21 - 7 * dg)) & 127);
         word |= (static_cast<uint32_t>(dig) & 0xffu) << (8 * bb);
       }
-      dst[4 * m + e] = static_cast<int32_t>(word);
+      bk[m][e] = static_cast<int>(word);
     }
-  if (grp == 0 && dg == 0) p.qexp[static_cast<size_t>(blockIdx.x) * 4 + hr] = qshift;
+  return qshift;
+}
+
+// Device-scope load of a split partial written by another workgroup.
+__device__ __forceinline__ float load_partial(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The merge of merge_splits_wave (same result, same order of operations)
+// with few memory round trips: the value sums of up to 8 splits are loaded
+// together with their scales.
+__device__ __forceinline__ void merge_partials(const float *p, int splits, int lane, float &o0, float &o1) {
+  constexpr int kU = 8;
+  float mv[kU], av0[kU], av1[kU];
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float *q = p + static_cast<size_t>(min(s0 + u, splits - 1)) * (D + 4);
+      mv[u] = load_partial(q);
+      av0[u] = load_partial(q + 4 + lane);
+      av1[u] = load_partial(q + 4 + 64 + lane);
+    }
+  };
+  fetch(0);
+  float mloc = -INFINITY;
+  bool nanloc = false;
+  // split statistics: lane s2 holds split s2 (and s2 + 64, ...)
+  for (int s2 = lane; s2 < splits; s2 += 64) mloc = fmaxf(mloc, load_partial(p + static_cast<size_t>(s2) * (D + 4)));
+  const float mstar = wave_maxf(mloc);
+  float lloc = 0.0f, zloc = 0.0f;
+  for (int s2 = lane; s2 < splits; s2 += 64) {
+    const float *q = p + static_cast<size_t>(s2) * (D + 4);
+    const float m = load_partial(q), l = load_partial(q + 1), z = load_partial(q + 2);
+    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
+    if (l != l) nanloc = true;
+    if (w != 0.0f) {
+      lloc += w * l;
+      zloc += w * z;
+    }
+  }
+  const float l = wave_sum(lloc), z = wave_sum(zloc);
+  const bool any_nan = __any(nanloc);
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int s0 = 0; s0 < splits; s0 += kU) {
+    if (s0 > 0) fetch(s0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s0 + u >= splits) break;
+      const float w = (mv[u] == -INFINITY) ? 0.0f : exp2f(mv[u] - mstar);
+      if (w != 0.0f) {
+        a0 += w * av0[u];
+        a1 += w * av1[u];
+      }
+    }
+  }
+  o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
+  o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
+  if (any_nan) o0 = o1 = __builtin_nanf("");
+}
+
+// Device-scope store of a split partial (read by the merging workgroup).
+__device__ __forceinline__ void store_partial(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival of one split at the counter of its (sequence, KV head, row group):
+// the high 32 bits hold the epoch of the launch, the low 32 bits the
+// arrivals; a word of another epoch (an earlier launch, or memory never
+// written by this kernel) or an impossible count reads as zero arrivals.
+// The last arrival writes zero arrivals back, so a replay with the same
+// epoch starts from zero as well.  Each failed exchange means another split
+// arrived in between, so the loop runs at most `splits` times.
+__device__ __forceinline__ bool arrive_last(unsigned long long *cnt, uint32_t epoch, int splits) {
+  const unsigned long long tag = static_cast<unsigned long long>(epoch) << 32;
+  unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    uint32_t n = (old >> 32) == epoch ? static_cast<uint32_t>(old) : 0u;
+    if (n >= static_cast<uint32_t>(splits)) n = 0;
+    ++n;
+    const unsigned long long want = n == static_cast<uint32_t>(splits) ? tag : (tag | n);
+    const unsigned long long seen = atomicCAS(cnt, old, want);
+    if (seen == old) return n == static_cast<uint32_t>(splits);
+    old = seen;
+  }
 }
 
 constexpr int kWaves = 4;
@@ -235,28 +268,35 @@ struct Blk {
   uint32_t vm[4];   // V metadata of token c of tile q
 };
 
+// Page of each tile of a block (wave-uniform) and the tile's first token in it.
 struct Addr {
-  uint64_t code[4], meta[4];
+  int32_t pg[4], off[4];
 };
 
 struct Ctx {
   const MfmaArgs *a;
-  const uint64_t *tab;  // this sequence's tile table
+  const int32_t *ptab;  // this sequence's page-table row
+  int32_t pg_base;
   int last_tile;        // last tile index of the split (loads clamp into it)
   int t_end;
   int c, g;
   uint32_t vo_k, vo_v, vo_km, vo_vm;  // per-lane constant byte offsets
 };
 
+// Pages of the 4 tiles of the block at t0.  Every token read lies below the
+// sequence length, which is at most max_pages * P, so the page-table index
+// stays inside the row.
 __device__ __forceinline__ void load_addr(const Ctx &c, int t0, Addr &ad) {
-  // the table is read-only for the kernel's lifetime: constant address space, scalar loads
-  const __attribute__((address_space(4))) uint64_t *tab =
-      (const __attribute__((address_space(4))) uint64_t *)(reinterpret_cast<uintptr_t>(c.tab));
+  // the page table is read-only for the kernel's lifetime: constant address space, scalar loads
+  const __attribute__((address_space(4))) int32_t *pt =
+      (const __attribute__((address_space(4))) int32_t *)(reinterpret_cast<uintptr_t>(c.ptab));
+  const MfmaArgs &a = *c.a;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int idx = min(t0 / 16 + q, c.last_tile);
-    ad.code[q] = tab[2 * idx];
-    ad.meta[q] = tab[2 * idx + 1];
+    const int tok = 16 * min(t0 / 16 + q, c.last_tile);
+    const int pi = tok >> a.p_shift;
+    ad.off[q] = tok & (a.P - 1);
+    ad.pg[q] = (pt[pi & a.tab_mask] & a.val_mask) + (pi & a.id_mask) + c.pg_base;
   }
 }
 
@@ -270,16 +310,23 @@ __device__ __forceinline__ uint32_t gload_u32(gbyte_ptr base, uint32_t off) {
   return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t *>(base + off);
 }
 
+// Issues the block's loads.  A page index outside the cache reads page 0
+// instead and sets `bad` (the rows' outputs become NaN).
 __device__ __forceinline__ void load_block(const Ctx &c, const Addr &ad, Blk &o, bool &bad) {
   // (the empty asm keeps the 32-bit offsets in this block, so that the
   // loads are selected as scalar base + 32-bit VGPR offset)
   uint32_t vo_k = c.vo_k, vo_v = c.vo_v, vo_km = c.vo_km, vo_vm = c.vo_vm;
   asm volatile("" : "+v"(vo_k), "+v"(vo_v), "+v"(vo_km), "+v"(vo_vm));
+  const MfmaArgs &a = *c.a;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const gbyte_ptr cb = reinterpret_cast<gbyte_ptr>(ad.code[q]);
-    const gbyte_ptr mb = reinterpret_cast<gbyte_ptr>(ad.meta[q] & ~static_cast<uint64_t>(1));
-    bad = bad || (ad.meta[q] & 1) != 0;
+    const bool ok = ad.pg[q] >= 0 && ad.pg[q] < a.num_pages;
+    bad = bad || !ok;
+    const uint64_t blk = reinterpret_cast<uint64_t>(a.pages) +
+                         static_cast<uint64_t>(ok ? ad.pg[q] : 0) * a.page_bytes;
+    const gbyte_ptr cb = reinterpret_cast<gbyte_ptr>(blk + 32u * static_cast<uint32_t>(ad.off[q]));
+    const gbyte_ptr mb = reinterpret_cast<gbyte_ptr>(blk + 64u * static_cast<uint32_t>(a.P) +
+                                                     4u * static_cast<uint32_t>(ad.off[q]));
     o.kc[q] = gload_u64(cb, vo_k);
     o.vx[q] = gload_u64(cb, vo_v);
     o.km[q] = gload_u32(mb, vo_km);
@@ -382,9 +429,13 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     }
 }
 
+template <int DT>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float red[kWaves][4][4 + D];  // per wave, per row: m, l, z, flag, acc[128]
   __shared__ float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
+  __shared__ float qs[4][D];               // q' of the group's rows
+  __shared__ float qsum_s[4];
+  __shared__ uint32_t s_last;
   const int s = blockIdx.x, b = blockIdx.z;
   const int h = blockIdx.y / a.n_rg, rg = blockIdx.y % a.n_rg;  // KV head, group of 4 query rows
   const int row0 = 4 * rg, nrows = min(4, a.R - row0);
@@ -402,30 +453,70 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   if (bad) L = 0;
   const int t_begin = s * a.split_tokens;
   c.t_end = min(t_begin + a.split_tokens, L);
-  c.last_tile = c.t_end > t_begin ? (c.t_end - 1) / 16 : t_begin / 16;
-  c.tab = a.tiles + static_cast<size_t>(b) * a.tiles_per_seq * 2;
+  c.last_tile = c.t_end > t_begin ? (c.t_end - 1) / 16 : 0;  // (empty split: loads read tile 0, unused)
+  c.ptab = a.ptab + static_cast<size_t>(b) * a.tab_stride;
+  c.pg_base = b * a.base_mul;
   const uint32_t hoff = static_cast<uint32_t>(h) * 72u * static_cast<uint32_t>(a.P);
   c.vo_k = hoff + 32u * c.c + 8u * c.g;
   c.vo_v = hoff + 32u * a.P + 128u * c.g + 8u * c.c;
   c.vo_km = hoff + 4u * c.c;
   c.vo_vm = hoff + 4u * a.P + 4u * c.c;
 
-  // ---- query digits (key-side A operand: row c = 4 r + d, k-slice g) and this lane's query row g
+  // ---- loads of the query row of this wave (row0 + wave), then of the
+  // first block, so that the query is prepared while the block is in flight
+  // (loads complete in issue order)
+  // (raw bits, unconditionally from valid addresses: a use right after a
+  // load would wait for it before the block's loads are issued)
+  uint32_t qb0, qb1;
+  int32_t sb0, sb1;
+  {
+    const int r = row0 + min(wave, nrows - 1);
+    const size_t rj = (static_cast<size_t>(b) * a.Nq + r / a.G) * a.Hq + h * a.G + r % a.G;
+    if constexpr (DT == KVQ_F32) {
+      qb0 = static_cast<const uint32_t *>(a.q)[rj * D + lane];
+      qb1 = static_cast<const uint32_t *>(a.q)[rj * D + lane + 64];
+    } else {
+      qb0 = static_cast<const uint16_t *>(a.q)[rj * D + lane];
+      qb1 = static_cast<const uint16_t *>(a.q)[rj * D + lane + 64];
+    }
+    // signs of the head (signed Hadamard); any readable bytes otherwise
+    const int8_t *sp = a.rk.kind == KVQ_ROT_SIGNED_HADAMARD ? a.rk.signs + h * D : static_cast<const int8_t *>(a.q);
+    sb0 = sp[lane];
+    sb1 = sp[lane + 64];
+  }
+  constexpr int kStride = kWaves * kBlk;
+  int t0 = t_begin + wave * kBlk;
+  const int n_blk = t0 < c.t_end ? (c.t_end - t0 + kStride - 1) / kStride : 0;
+  Blk b0, b1;
+  Addr a0, a1;
+  // (unconditional: every address is clamped into the split, or tile 0)
+  load_addr(c, t0, a0);
+  load_block(c, a0, b0, bad);
+  load_addr(c, t0 + kStride, a1);
+
+  // ---- query rows: q' = q R_K log2(e)/sqrt(128)
+  {
+    float y0 = 0.0f, y1 = 0.0f;
+    if (wave < nrows) {
+      y0 = DT == KVQ_F32 ? __uint_as_float(qb0) : __uint_as_float(qb0 << 16);
+      y1 = DT == KVQ_F32 ? __uint_as_float(qb1) : __uint_as_float(qb1 << 16);
+      rotate_query_signed(y0, y1, a.rk.kind, static_cast<float>(sb0), static_cast<float>(sb1), lane);
+    }
+    const float sum = wave_sum(y0 + y1);
+    qs[wave][lane] = y0;
+    qs[wave][lane + 64] = y1;
+    if (lane == 0) qsum_s[wave] = sum;
+  }
+  __syncthreads();
+  // key-side A operand (row c = 4 r + d, k-slice g) and this lane's query row g
   State st;
-  {
-    const int4 *dsrc = reinterpret_cast<const int4 *>(a.qdig + (unit * 64 + lane) * 8);
-    const int4 d0 = dsrc[0], d1 = dsrc[1];
-    st.bk[0] = v4i{d0.x, d0.y, d0.z, d0.w};
-    st.bk[1] = v4i{d1.x, d1.y, d1.z, d1.w};
-  }
   const int hr = c.g;  // query row (within the group) of the key-side lanes
-  st.row_ok = hr < nrows;
   {
-    const int r = row0 + hr, qi = r / a.G, gh = r % a.G;
-    const size_t rj = (static_cast<size_t>(b) * a.Nq + qi) * a.Hq + h * a.G + gh;
-    st.qsum = st.row_ok ? a.qsum[rj] : 0.0f;
-    st.unscale = ldexpf(1.0f, -a.qexp[unit * 4 + hr]);
+    const int qshift = query_digits(qs, lane, st.bk);
+    st.unscale = ldexpf(1.0f, -__shfl(qshift, 4 * hr));  // lane 4 hr forms the digits of row hr
+    st.qsum = qsum_s[hr];
   }
+  st.row_ok = hr < nrows;
   const int x = lane & 3;
   st.sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
   st.sel2 = (x & 2) ? 0x03020706u : 0x05040100u;
@@ -443,15 +534,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
 
   // ---- main loop: wave w takes blocks w, w+4, ...; block i+1 is in flight
   // while block i is computed and the addresses of block i+2 are fetched
-  constexpr int kStride = kWaves * kBlk;
-  int t0 = t_begin + wave * kBlk;
-  const int n_blk = t0 < c.t_end ? (c.t_end - t0 + kStride - 1) / kStride : 0;
   if (n_blk > 0) {
-    Blk b0, b1;
-    Addr a0, a1;
-    load_addr(c, t0, a0);
-    load_block(c, a0, b0, bad);
-    load_addr(c, t0 + kStride, a1);
     for (int i = 0; i < n_blk / 2; ++i) {
       load_block(c, a1, b1, bad);
       load_addr(c, t0 + 2 * kStride, a0);
@@ -514,63 +597,54 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
     const int qq = (row0 + r) / a.G, g2 = (row0 + r) % a.G;
     const size_t row = static_cast<size_t>(b) * a.Nq + qq;
     float *dst = a.part + ((row * a.Hq + h * a.G + g2) * a.splits + s) * (D + 4);
-    dst[4 + i] = mstar == -INFINITY ? 0.0f : acc;
+    store_partial(dst + 4 + i, mstar == -INFINITY ? 0.0f : acc);
     if (i == 0) {
-      dst[0] = mstar;
-      dst[1] = nan ? __builtin_nanf("") : (mstar == -INFINITY ? 0.0f : l);
-      dst[2] = mstar == -INFINITY ? 0.0f : z;
-      dst[3] = 0.0f;
+      store_partial(dst, mstar);
+      store_partial(dst + 1, nan ? __builtin_nanf("") : (mstar == -INFINITY ? 0.0f : l));
+      store_partial(dst + 2, mstar == -INFINITY ? 0.0f : z);
+      store_partial(dst + 3, 0.0f);
     }
+  }
+
+  // ---- the last split of this row group to arrive merges all splits.
+  // The partials travel between workgroups (and XCDs) through device-scope
+  // stores and loads only; every store of this workgroup is acknowledged
+  // (all counters drained) before its arrival is counted, and the merging
+  // workgroup issues its loads after it has seen the final count.  No cache
+  // write-back or invalidation is needed for that.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = arrive_last(a.counters + unit, a.epoch, a.splits) ? 1u : 0u;
+  __syncthreads();
+  if (s_last == 0) return;
+  if (wave < nrows) {
+    const int qq = (row0 + wave) / a.G, j = h * a.G + (row0 + wave) % a.G;
+    const size_t row = static_cast<size_t>(b) * a.Nq + qq;
+    float o0, o1;
+    merge_partials(a.part + (row * a.Hq + j) * a.splits * (D + 4), a.splits, lane, o0, o1);
+    unrotate_value_wave(o0, o1, a.rv, h, lane);
+    store_output_wave(a.out_o, a.ot, row, j, a.Hq, lane, o0, o1);
   }
 }
 
 }  // namespace
 
 bool decode_mfma_supported(const DecodePlan &pl, int page_size) {
-  return pl.rows_per_head <= kMaxRows && page_size % 16 == 0 &&
+  return pl.rows_per_head <= kMaxRows && page_size >= 16 && (page_size & (page_size - 1)) == 0 &&
          static_cast<int64_t>(pl.H) * 72 * page_size < (static_cast<int64_t>(1) << 31);
 }
 
-hipError_t launch_decode_prologue(const DecodePlan &pl, const void *q, int dtype, RotDev rk, const uint8_t *pages,
-                                  int64_t num_pages, int page_size, const int32_t *page_table, int max_pages,
-                                  float *qrot, float *qsum, int32_t *qdig, int32_t *qexp, uint64_t *tiles,
-                                  hipStream_t stream) {
+hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, RotDev rk, RotDev rv,
+                              const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
+                              int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
+                              float *out_o, float *ot, hipStream_t stream) {
   if (pl.num_seqs == 0) return hipSuccess;
-  PrologueArgs p{};
-  p.q = q;
-  p.rk = rk;
-  p.R = pl.rows_per_head;
-  p.G = pl.G;
-  p.Hq = pl.Hq;
-  p.H = pl.H;
-  p.Nq = pl.queries_per_seq;
-  p.num_seqs = pl.num_seqs;
-  p.n_rg = (pl.rows_per_head + 3) / 4;
-  p.qrot = qrot;
-  p.qsum = qsum;
-  p.qdig = qdig;
-  p.qexp = qexp;
-  p.pages = pages;
-  p.num_pages = num_pages;
-  p.P = page_size;
-  p.page_table = page_table;
-  p.max_pages = max_pages;
-  p.tiles_per_seq = pl.tiles_per_seq;
-  p.table_chunks = (pl.tiles_per_seq + 255) / 256;
-  p.tiles = tiles;
-  const dim3 grid(pl.num_seqs * pl.H * p.n_rg + pl.num_seqs * p.table_chunks);
-  if (dtype == KVQ_F32)
-    hipLaunchKernelGGL(decode_prologue_kernel<KVQ_F32>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(decode_prologue_kernel<KVQ_BF16>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const int32_t *seq_lens,
-                                    const int32_t *qdig, const int32_t *qexp, const float *qsum,
-                                    const uint64_t *tiles, float *part, hipStream_t stream) {
-  if (pl.num_seqs == 0) return hipSuccess;
-  const int tps = pl.tiles_per_seq;
+  if (rk.kind == KVQ_ROT_DENSE) return hipErrorInvalidValue;  // rotated by launch_query_rotation first
+  // arrival tags: a new value per launch, starting from a per-process value
+  // so that counters left in memory by other processes rarely carry it
+  static std::atomic<uint32_t> next_epoch{static_cast<uint32_t>(
+      std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
+  uint32_t epoch = next_epoch.fetch_add(1);
   MfmaArgs a{};
   a.R = pl.rows_per_head;
   a.G = pl.G;
@@ -582,14 +656,36 @@ hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const i
   a.splits = pl.splits;
   a.max_seq_len = pl.max_seq_len;
   a.P = page_size;
-  a.tiles_per_seq = tps;
+  a.p_shift = __builtin_ctz(static_cast<unsigned>(page_size));
+  a.max_pages = max_pages;
+  if (page_table) {
+    a.ptab = page_table;
+    a.tab_stride = max_pages;
+    a.tab_mask = a.val_mask = -1;
+    a.id_mask = a.base_mul = 0;
+  } else {
+    a.ptab = seq_lens;  // read, then masked to zero
+    a.tab_stride = a.tab_mask = a.val_mask = 0;
+    a.id_mask = -1;
+    a.base_mul = max_pages;
+  }
+  a.num_pages = num_pages;
+  a.page_bytes = static_cast<uint64_t>(pl.H) * 72u * static_cast<uint64_t>(page_size);
+  a.pages = pages;
   a.seq_lens = seq_lens;
-  a.qdig = qdig;
-  a.qexp = qexp;
-  a.qsum = qsum;
-  a.tiles = tiles;
+  a.q = q;
+  a.rk = rk;
+  a.rv = rv;
   a.part = part;
-  hipLaunchKernelGGL(decode_mfma_kernel, dim3(pl.splits, pl.H * a.n_rg, pl.num_seqs), dim3(256), 0, stream, a);
+  a.counters = reinterpret_cast<unsigned long long *>(counters);
+  a.epoch = epoch;
+  a.out_o = out_o;
+  a.ot = ot;
+  const dim3 grid(pl.splits, pl.H * a.n_rg, pl.num_seqs);
+  if (dtype == KVQ_F32 || rk.kind == kRotPrescaled)
+    hipLaunchKernelGGL(decode_mfma_kernel<KVQ_F32>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_mfma_kernel<KVQ_BF16>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -72,20 +72,44 @@ __device__ __forceinline__ void fwht128(float &x0, float &x1, int lane) {
   }
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_maxf(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 
-// q' = q R_K * log2(e)/sqrt(128) of one 128-vector held by a wave (row-vector
-// convention z' = z R; signed Hadamard by the transform above).
-__device__ __forceinline__ void rotate_query_wave(float &x0, float &x1, const RotDev &rk, int h, int lane) {
-  float y0 = x0, y1 = x1;
-  if (rk.kind == KVQ_ROT_SIGNED_HADAMARD) {
-    x0 *= static_cast<float>(rk.signs[h * D + lane]);
-    x1 *= static_cast<float>(rk.signs[h * D + lane + 64]);
+// Rotation kind used inside the library only: the query rows were already
+// rotated and scaled by an earlier launch (rotate_query_wave leaves them alone).
+constexpr int32_t kRotPrescaled = -1;
+
+// q' = q R_K * log2(e)/sqrt(128) of one 128-vector held by a wave for the
+// kinds without a matrix (identity, signed Hadamard, already rotated), with
+// the head's signs s0 = s[lane], s1 = s[lane + 64] already loaded (signed
+// Hadamard only): x <- (x * s) H / sqrt(128) by the transform above.
+__device__ __forceinline__ void rotate_query_signed(float &x0, float &x1, int32_t kind, float s0, float s1,
+                                                    int lane) {
+  if (kind == kRotPrescaled) return;
+  if (kind == KVQ_ROT_SIGNED_HADAMARD) {
+    x0 *= s0;
+    x1 *= s1;
     fwht128(x0, x1, lane);
-    y0 = x0 * kInvSqrtD;
-    y1 = x1 * kInvSqrtD;
-  } else if (rk.kind == KVQ_ROT_DENSE) {
+    x0 *= kInvSqrtD;
+    x1 *= kInvSqrtD;
+  }
+  x0 *= kLog2eF * kInvSqrtD;
+  x1 *= kLog2eF * kInvSqrtD;
+}
+
+// q' = q R_K * log2(e)/sqrt(128) of one 128-vector held by a wave (row-vector
+// convention z' = z R), every rotation kind.
+__device__ __forceinline__ void rotate_query_wave(float &x0, float &x1, const RotDev &rk, int h, int lane) {
+  if (rk.kind == KVQ_ROT_DENSE) {
     const float *m = rk.matrix + static_cast<size_t>(h) * D * D;
     float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll 8
@@ -94,11 +118,106 @@ __device__ __forceinline__ void rotate_query_wave(float &x0, float &x1, const Ro
       a0 += zi * m[i * D + lane];
       a1 += zi * m[i * D + lane + 64];
     }
-    y0 = a0;
-    y1 = a1;
+    x0 = a0 * (kLog2eF * kInvSqrtD);
+    x1 = a1 * (kLog2eF * kInvSqrtD);
+    return;
   }
-  x0 = y0 * (kLog2eF * kInvSqrtD);
-  x1 = y1 * (kLog2eF * kInvSqrtD);
+  float s0 = 1.0f, s1 = 1.0f;
+  if (rk.kind == KVQ_ROT_SIGNED_HADAMARD) {
+    s0 = static_cast<float>(rk.signs[h * D + lane]);
+    s1 = static_cast<float>(rk.signs[h * D + lane + 64]);
+  }
+  rotate_query_signed(x0, x1, rk.kind, s0, s1, lane);
+}
+
+// ----------------------------------------------------------------- split merge
+// A split partial of one (query row, query head) is 132 floats: m (base-2 log
+// of the split's scale), l = sum_t 2^(x_t - m), z = sum_t 2^(x_t - m) z_t,
+// a flag word, and acc[c] = sum_t 2^(x_t - m) s_t code_t[c], over the split's
+// tokens t with x_t = logit_t in log2 units (l = NaN marks a bad input).
+
+// Rotated-domain output o'[c] = (sum_s 2^(m_s - m*) (acc_s[c] + z_s)) /
+// (sum_s 2^(m_s - m*) l_s) of the `splits` partials at p (stride 132 floats),
+// held by one wave as o0 = o'[lane], o1 = o'[lane + 64]; 0 when no token
+// counted, NaN when a split flagged a bad input.
+__device__ __forceinline__ void merge_splits_wave(const float *p, int splits, int lane, float &o0, float &o1) {
+  float mloc = -INFINITY;
+  for (int s2 = lane; s2 < splits; s2 += 64)
+    mloc = fmaxf(mloc, p[static_cast<size_t>(s2) * (D + 4)]);
+  const float mstar = wave_maxf(mloc);
+  float lloc = 0.0f, zloc = 0.0f, nanloc = 0.0f;
+  for (int s2 = lane; s2 < splits; s2 += 64) {
+    const float *q = p + static_cast<size_t>(s2) * (D + 4);
+    const float m = q[0], l = q[1], z = q[2];
+    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
+    if (l != l) nanloc = 1.0f;
+    if (w != 0.0f) {
+      lloc += w * l;
+      zloc += w * z;
+    }
+  }
+  const float l = wave_sum(lloc), z = wave_sum(zloc);
+  const bool any_nan = wave_maxf(nanloc) != 0.0f;
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 4
+  for (int s2 = 0; s2 < splits; ++s2) {
+    const float *q = p + static_cast<size_t>(s2) * (D + 4);
+    const float m = q[0];  // uniform
+    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
+    if (w != 0.0f) {
+      a0 += w * q[4 + lane];
+      a1 += w * q[4 + 64 + lane];
+    }
+  }
+  o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
+  o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
+  if (any_nan) o0 = o1 = __builtin_nanf("");
+}
+
+// out = o' R_V^T of KV head h (one wave, same register layout as above).
+__device__ __forceinline__ void unrotate_value_wave(float &o0, float &o1, const RotDev &rv, int h, int lane) {
+  if (rv.kind == KVQ_ROT_SIGNED_HADAMARD) {
+    // R[i][c] = s_i H[i][c] / sqrt(128), H symmetric: out = s * (o' H) / sqrt(128)
+    fwht128(o0, o1, lane);
+    o0 *= static_cast<float>(rv.signs[h * D + lane]) * kInvSqrtD;
+    o1 *= static_cast<float>(rv.signs[h * D + lane + 64]) * kInvSqrtD;
+  } else if (rv.kind == KVQ_ROT_DENSE) {
+    // out[i] = sum_c o'[c] R[i][c]
+    const float *m0 = rv.matrix + (static_cast<size_t>(h) * D + lane) * D;
+    const float *m1 = m0 + 64 * D;
+    float r0 = 0.0f, r1 = 0.0f;
+    for (int c = 0; c < D; c += 4) {
+      const float4 e0 = *reinterpret_cast<const float4 *>(m0 + c);
+      const float4 e1 = *reinterpret_cast<const float4 *>(m1 + c);
+      const float src = c < 64 ? o0 : o1;
+      const int cl = c & 63;
+      const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl));
+      const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 1));
+      const float v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 2));
+      const float v3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), cl + 3));
+      r0 += v0 * e0.x + v1 * e0.y + v2 * e0.z + v3 * e0.w;
+      r1 += v0 * e1.x + v1 * e1.y + v2 * e1.z + v3 * e1.w;
+    }
+    o0 = r0;
+    o1 = r1;
+  }
+}
+
+constexpr int kWoRows = 16;  // rows of o per W_O pass
+
+// Writes the output of (row, query head j) to out_o [rows][Hq][128] and, when
+// ot is not null, to the W_O operand copy laid out [row / 16][Hq * 128][16].
+__device__ __forceinline__ void store_output_wave(float *out_o, float *ot, size_t row, int j, int Hq, int lane,
+                                                  float r0, float r1) {
+  const size_t K = static_cast<size_t>(Hq) * D;
+  const size_t base = row * K + static_cast<size_t>(j) * D;
+  out_o[base + lane] = r0;
+  out_o[base + lane + 64] = r1;
+  if (ot) {
+    float *dst = ot + ((row / kWoRows) * K + static_cast<size_t>(j) * D) * kWoRows + row % kWoRows;
+    dst[static_cast<size_t>(lane) * kWoRows] = r0;
+    dst[static_cast<size_t>(lane + 64) * kWoRows] = r1;
+  }
 }
 
 // ----------------------------------------------------------------- launchers
@@ -111,10 +230,9 @@ struct DecodePlan {
   int max_seq_len, splits, split_tokens;                   // split_tokens % kChunk == 0
   int d_model, wo_ksplit, wo_kslice;
   size_t off_qrot, off_qsum, off_part, off_ypart;          // workspace layout (bytes)
-  size_t off_qdig, off_qexp;                               // key-side query digits (matrix-core kernel)
   size_t off_ot;                                           // o laid out for the W_O projection
-  int tiles_per_seq;                                       // 16-token tiles per sequence
-  size_t off_tiles, total;                                 // tile address table (matrix-core kernel)
+  size_t off_cnt;                                          // split arrival counters (matrix-core kernel)
+  size_t total;
 };
 DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, int max_seq_len, int d_model,
                             int num_splits);
@@ -126,19 +244,19 @@ hipError_t launch_query_rotation(const void *q, int dtype, const DecodePlan &pl,
 hipError_t launch_decode_split(const DecodePlan &pl, const uint8_t *pages, int64_t num_pages, int page_size,
                                const int32_t *page_table, int max_pages, const int32_t *seq_lens,
                                const float *qrot, const float *qsum, float *part, hipStream_t stream);
-// Same partials from the matrix-core kernel (rows_per_head <= 4).
+// Matrix-core decode attention (one launch): per (sequence, KV head, group
+// of 4 query rows) and split, the query rows are rotated (q and rk as in
+// launch_query_rotation; rk.kind == kRotPrescaled takes q as rotated fp32
+// rows), attended over the split's tokens, and the last split to finish
+// merges all splits, applies R_V^T and writes out_o (and ot when not null).
+// `counters` holds one 64-bit arrival counter per (sequence, KV head, row
+// group); `epoch` tags this launch's arrivals (counters of another epoch
+// count as zero; the last arrival leaves its counter at zero arrivals).
 bool decode_mfma_supported(const DecodePlan &pl, int page_size);
-// Prologue of the matrix-core kernel (one launch): rotated queries and their
-// sums, their fixed-point int8 digits (one 64-lane operand set per (sequence,
-// KV head)) and the absolute code / metadata addresses of every 16-token tile
-// (page indices validated here).
-hipError_t launch_decode_prologue(const DecodePlan &pl, const void *q, int dtype, RotDev rk, const uint8_t *pages,
-                                  int64_t num_pages, int page_size, const int32_t *page_table, int max_pages,
-                                  float *qrot, float *qsum, int32_t *qdig, int32_t *qexp, uint64_t *tiles,
-                                  hipStream_t stream);
-hipError_t launch_decode_split_mfma(const DecodePlan &pl, int page_size, const int32_t *seq_lens,
-                                    const int32_t *qdig, const int32_t *qexp, const float *qsum,
-                                    const uint64_t *tiles, float *part, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, RotDev rk, RotDev rv,
+                              const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
+                              int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
+                              float *out_o, float *ot, hipStream_t stream);
 // Split-K partial attention over raw (unquantized, unrotated) K and V that
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
@@ -147,7 +265,7 @@ hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const voi
 // copy `ot` when not null).
 hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, float *ot,
                           hipStream_t stream);
-// out_y = concat(out_o) W_O, from the copy written by launch_combine.
+// out_y = concat(out_o) W_O, from the copy `ot` written with out_o.
 hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *ypart,
                                 float *out_y, hipStream_t stream);
 
