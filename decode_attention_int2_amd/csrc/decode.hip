@@ -561,13 +561,14 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   const int max_chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   int splits = num_splits;
   if (splits <= 0) {
-    // ~2 workgroups of 4 waves per CU, all resident at once (a partial second
-    // round of workgroups would run the tail at low occupancy), and splits of
-    // at least 1024 tokens so the per-split prologue and merge stay small.
-    // A workgroup of the matrix-core kernel takes one group of 4 query rows.
+    // ~one workgroup (8 waves) of the matrix-core kernel per CU, all resident
+    // at once: two workgroups sharing a CU run at unequal speed (the older
+    // one's waves win the issue arbitration), so the younger one's tail runs
+    // at half occupancy; splits of at least 1024 tokens keep the per-split
+    // prologue and merge small.  A workgroup takes one group of 4 query rows.
     const int n_rg = (queries_per_seq * (Hq / H) + 3) / 4;
     const int units = num_seqs * H * n_rg > 0 ? num_seqs * H * n_rg : 1;
-    splits = (512 + units - 1) / units;
+    splits = (256 + units - 1) / units;
     const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens
     if (splits > max_by_len) splits = max_by_len;
   }
@@ -596,7 +597,8 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   pl.off_qsum = off;
   off = align(off + rows * Hq * sizeof(float));
   pl.off_part = off;
-  off = align(off + rows * Hq * static_cast<size_t>(pl.splits) * (D + 4) * sizeof(float));
+  // (the matrix-core kernel writes one partial per (split, wave))
+  off = align(off + rows * Hq * static_cast<size_t>(pl.splits) * kMfmaWaves * (D + 4) * sizeof(float));
   pl.off_ypart = off;
   off = align(off + (d_model > 0 && ks > 1 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
   pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection

@@ -34,11 +34,11 @@
 //   fast transform; a dense R_K is applied by an earlier launch) and forms
 //   their digits while its first key / value loads are in flight.
 // Addresses: the page of every 16-token tile is read from the page table with
-//   scalar loads one block ahead and turned into code / metadata base
-//   addresses on the scalar unit; every vector load is scalar base + per-lane
-//   constant offset.  The next 64-token block is fetched while the current
-//   one is computed; tiles past the split end are clamped into its last tile
-//   and masked.
+//   scalar loads one block ahead and turned into the (page, head) block base
+//   on the scalar unit (32-bit bounds check, one 32 x 32 -> 64-bit product);
+//   every vector load is scalar base + per-lane constant offset.  The next
+//   two 64-token blocks are in flight while the current one is computed;
+//   tiles past the split end are clamped into its last tile and masked.
 // Merge: each split writes an (m, l, z, acc[128]) partial with m = -kappa;
 //   the last split of a (sequence, KV head, row group) to arrive (a tagged
 //   arrival counter) merges the partials, applies R_V^T and writes the output.
@@ -67,21 +67,26 @@ __device__ __forceinline__ int slot(uint32_t x, int e) {
 }
 __device__ __forceinline__ float slot_inv(int e) { return e == 1 ? 0.25f : e == 2 ? 0.0625f : 1.0f; }
 
-__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
-__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ int dpp_ror4(int v) { return __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false); }
-__device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
+// (every source lane of these patterns exists, so bound_ctrl changes nothing;
+// it lets the compiler fold the move into the instruction that uses it)
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true); }
+__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true); }
+__device__ __forceinline__ int dpp_ror4(int v) { return __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true); }
+__device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true); }
 __device__ __forceinline__ float fdpp_xor1(float v) { return __int_as_float(dpp_xor1(__float_as_int(v))); }
 __device__ __forceinline__ float fdpp_xor2(float v) { return __int_as_float(dpp_xor2(__float_as_int(v))); }
 __device__ __forceinline__ float fdpp_ror4(float v) { return __int_as_float(dpp_ror4(__float_as_int(v))); }
 __device__ __forceinline__ float fdpp_ror8(float v) { return __int_as_float(dpp_ror8(__float_as_int(v))); }
 
 // max / sum over the 16 lanes of a DPP row (rotations reach every lane of the row)
+// (max(a, b) = med3(a, b, +inf) for the finite or -inf values reduced here:
+// one instruction, no NaN canonicalization)
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 __device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, fdpp_xor1(x));
-  x = fmaxf(x, fdpp_xor2(x));
-  x = fmaxf(x, fdpp_ror4(x));
-  x = fmaxf(x, fdpp_ror8(x));
+  x = max2(x, fdpp_xor1(x));
+  x = max2(x, fdpp_xor2(x));
+  x = max2(x, fdpp_ror4(x));
+  x = max2(x, fdpp_ror8(x));
   return x;
 }
 __device__ __forceinline__ float row16_sum(float x) {
@@ -114,8 +119,8 @@ struct MfmaArgs {
   int split_tokens, splits, max_seq_len;
   int P, p_shift;             // page size in tokens (a power of two) and its log2
   int max_pages;
-  int64_t num_pages;
-  uint64_t page_bytes;        // H * 72 * P
+  uint32_t np32;              // number of pages, at most 2^31 - 1 (page-table entries are int32)
+  uint32_t page_bytes;        // H * 72 * P (< 2^31)
   const uint8_t *pages;
   // page of entry i of sequence b: (ptab[b * tab_stride + (i & tab_mask)] & val_mask) + (i & id_mask) + b * base_mul;
   // with a page table: stride max_pages, masks ~0, ~0, 0, base_mul 0;
@@ -125,7 +130,8 @@ struct MfmaArgs {
   const int32_t *seq_lens;
   const void *q;              // query rows (dtype of the launch), or rotated fp32 rows
   RotDev rk, rv;
-  float *part;                // [rows][Hq][splits][132] split partials
+  float *part;                // [rows][Hq][parts][132] partials, one per (split, wave)
+  int parts;                  // splits * 4
   unsigned long long *counters;  // [num_seqs][H][n_rg] arrival counters
   uint32_t epoch;
   float *out_o, *ot;
@@ -136,42 +142,21 @@ struct MfmaArgs {
 // lane (col, grp): query row col/4, digit col%4; dim 16 (2 grp + m) + 4 bb + e
 // goes to dword [m][e], byte bb.  Slot e of the unpacked codes carries a
 // factor 1/slot_inv(e), divided out here.  Q = round(q' 2^S) with
-// |Q| < 2^26; S per query row from its largest |q'|.  Returns S of the
-// lane's digit row.
-__device__ __forceinline__ int query_digits(const float (*qs)[D], int lane, v4i bk[2]) {
+// |Q| < 2^26, S = qshift[r] per query row from its largest |q'|.  Returns
+// dword (m, e) of the lane's operand.
+__device__ __forceinline__ uint32_t query_digit_word(const float (*qs)[D], const int *qshift, int lane, int m,
+                                                    int e) {
   const int col = lane & 15, grp = lane >> 4, hr = col >> 2, dg = col & 3;
-  float qv[2][16];
-  float qabs = 0.0f;
+  const int sh = qshift[hr];
+  uint32_t word = 0;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const float x = qs[hr][16 * (2 * grp + m) + 4 * bb + e];
-        qv[m][4 * e + bb] = x * slot_inv(e);
-        qabs = fmaxf(qabs, fabsf(x));
-      }
-  // one shift S per query row: the row's 16 lanes x 4 lane groups hold all its dims
-  qabs = fmaxf(qabs, __shfl_xor(qabs, 16));
-  qabs = fmaxf(qabs, __shfl_xor(qabs, 32));
-  int e2 = 0;
-  (void)frexpf(qabs, &e2);  // qabs < 2^e2
-  const int qshift = 26 - e2;
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int Q = static_cast<int>(__builtin_rintf(ldexpf(qv[m][4 * e + bb], qshift)));
-        const int dig = (dg == 0) ? (Q >> 21) : ((Q >> (21 - 7 * dg)) & 127);
-        word |= (static_cast<uint32_t>(dig) & 0xffu) << (8 * bb);
-      }
-      bk[m][e] = static_cast<int>(word);
-    }
-  return qshift;
+  for (int bb = 0; bb < 4; ++bb) {
+    const float x = qs[hr][16 * (2 * grp + m) + 4 * bb + e] * slot_inv(e);
+    const int Q = static_cast<int>(__builtin_rintf(ldexpf(x, sh)));
+    const int dig = (dg == 0) ? (Q >> 21) : ((Q >> (21 - 7 * dg)) & 127);
+    word |= (static_cast<uint32_t>(dig) & 0xffu) << (8 * bb);
+  }
+  return word;
 }
 
 // Device-scope load of a split partial written by another workgroup.
@@ -180,15 +165,66 @@ __device__ __forceinline__ float load_partial(const float *p) {
 }
 
 // The merge of merge_splits_wave (same result, same order of operations)
-// with few memory round trips: the value sums of up to 8 splits are loaded
-// together with their scales.
-__device__ __forceinline__ void merge_partials(const float *p, int splits, int lane, float &o0, float &o1) {
+// with few memory round trips.  Up to 64 partials: lane u holds partial u's
+// (m, l, z) and the value sums come in batches of 16 partials, the first two
+// batches requested together with the statistics.  More partials: the
+// statistics in a lane loop, value sums in batches of 8 with their scales.
+__device__ __forceinline__ void merge_partials(const float *p, int parts, int lane, float &o0, float &o1) {
+  if (parts <= 64) {
+    constexpr int kB = 16;
+    float ma = -INFINITY, la = 0.0f, za = 0.0f;
+    if (lane < parts) {
+      const float *q = p + static_cast<size_t>(lane) * (D + 4);
+      ma = load_partial(q);
+      la = load_partial(q + 1);
+      za = load_partial(q + 2);
+    }
+    float xa0[kB], xa1[kB], xb0[kB], xb1[kB];
+    auto fetch = [&](float *v0, float *v1, int u0) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const float *q = p + static_cast<size_t>(min(u0 + u, parts - 1)) * (D + 4);
+        v0[u] = load_partial(q + 4 + lane);
+        v1[u] = load_partial(q + 4 + 64 + lane);
+      }
+    };
+    fetch(xa0, xa1, 0);
+    if (parts > kB) fetch(xb0, xb1, kB);
+    const float mstar = wave_maxf(ma);
+    const float wa = (ma == -INFINITY) ? 0.0f : exp2f(ma - mstar);
+    const bool any_nan = __any(la != la);
+    const float l = wave_sum(wa != 0.0f ? wa * la : 0.0f), z = wave_sum(wa != 0.0f ? wa * za : 0.0f);
+    float a0 = 0.0f, a1 = 0.0f;
+    auto accumulate = [&](const float *v0, const float *v1, int u0) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (u0 + u >= parts) break;
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa), u0 + u));
+        if (w != 0.0f) {
+          a0 += w * v0[u];
+          a1 += w * v1[u];
+        }
+      }
+    };
+    for (int u0 = 0; u0 < parts; u0 += 2 * kB) {
+      accumulate(xa0, xa1, u0);
+      if (u0 + 2 * kB < parts) fetch(xa0, xa1, u0 + 2 * kB);
+      if (u0 + kB < parts) {
+        accumulate(xb0, xb1, u0 + kB);
+        if (u0 + 3 * kB < parts) fetch(xb0, xb1, u0 + 3 * kB);
+      }
+    }
+    o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
+    o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
+    if (any_nan) o0 = o1 = __builtin_nanf("");
+    return;
+  }
   constexpr int kU = 8;
   float mv[kU], av0[kU], av1[kU];
   auto fetch = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const float *q = p + static_cast<size_t>(min(s0 + u, splits - 1)) * (D + 4);
+      const float *q = p + static_cast<size_t>(min(s0 + u, parts - 1)) * (D + 4);
       mv[u] = load_partial(q);
       av0[u] = load_partial(q + 4 + lane);
       av1[u] = load_partial(q + 4 + 64 + lane);
@@ -198,10 +234,10 @@ __device__ __forceinline__ void merge_partials(const float *p, int splits, int l
   float mloc = -INFINITY;
   bool nanloc = false;
   // split statistics: lane s2 holds split s2 (and s2 + 64, ...)
-  for (int s2 = lane; s2 < splits; s2 += 64) mloc = fmaxf(mloc, load_partial(p + static_cast<size_t>(s2) * (D + 4)));
+  for (int s2 = lane; s2 < parts; s2 += 64) mloc = fmaxf(mloc, load_partial(p + static_cast<size_t>(s2) * (D + 4)));
   const float mstar = wave_maxf(mloc);
   float lloc = 0.0f, zloc = 0.0f;
-  for (int s2 = lane; s2 < splits; s2 += 64) {
+  for (int s2 = lane; s2 < parts; s2 += 64) {
     const float *q = p + static_cast<size_t>(s2) * (D + 4);
     const float m = load_partial(q), l = load_partial(q + 1), z = load_partial(q + 2);
     const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
@@ -214,11 +250,11 @@ __device__ __forceinline__ void merge_partials(const float *p, int splits, int l
   const float l = wave_sum(lloc), z = wave_sum(zloc);
   const bool any_nan = __any(nanloc);
   float a0 = 0.0f, a1 = 0.0f;
-  for (int s0 = 0; s0 < splits; s0 += kU) {
+  for (int s0 = 0; s0 < parts; s0 += kU) {
     if (s0 > 0) fetch(s0);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      if (s0 + u >= splits) break;
+      if (s0 + u >= parts) break;
       const float w = (mv[u] == -INFINITY) ? 0.0f : exp2f(mv[u] - mstar);
       if (w != 0.0f) {
         a0 += w * av0[u];
@@ -241,11 +277,14 @@ __device__ __forceinline__ void store_partial(float *p, float v) {
 // arrivals; a word of another epoch (an earlier launch, or memory never
 // written by this kernel) or an impossible count reads as zero arrivals.
 // The last arrival writes zero arrivals back, so a replay with the same
-// epoch starts from zero as well.  Each failed exchange means another split
-// arrived in between, so the loop runs at most `splits` times.
+// epoch starts from zero as well.  The first exchange assumes that all other
+// splits have arrived (one round trip for the last split, which is the one
+// that goes on to merge); each failed exchange means the guess was wrong or
+// another split arrived in between, so the loop runs at most `splits` + 1
+// times.
 __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, uint32_t epoch, int splits) {
   const unsigned long long tag = static_cast<unsigned long long>(epoch) << 32;
-  unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long old = tag | static_cast<uint32_t>(splits - 1);
   for (;;) {
     uint32_t n = (old >> 32) == epoch ? static_cast<uint32_t>(old) : 0u;
     if (n >= static_cast<uint32_t>(splits)) n = 0;
@@ -257,7 +296,7 @@ __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, uint32_t ep
   }
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kMfmaWaves;  // waves per workgroup (one workgroup per CU)
 constexpr int kBlk = 64;  // tokens per wave iteration (4 tiles of 16)
 
 // Per-lane data of one 64-token block.
@@ -268,7 +307,8 @@ struct Blk {
   uint32_t vm[4];   // V metadata of token c of tile q
 };
 
-// Page of each tile of a block (wave-uniform) and the tile's first token in it.
+// Page of each tile of a block as read from the page table (wave-uniform)
+// and, for pages longer than one tile, the tile's first token in its page.
 struct Addr {
   int32_t pg[4], off[4];
 };
@@ -280,12 +320,13 @@ struct Ctx {
   int last_tile;        // last tile index of the split (loads clamp into it)
   int t_end;
   int c, g;
-  uint32_t vo_k, vo_v, vo_km, vo_vm;  // per-lane constant byte offsets
+  uint32_t vo_k, vo_v, vo_km, vo_vm;  // per-lane constant byte offsets from the (page, head) block
 };
 
-// Pages of the 4 tiles of the block at t0.  Every token read lies below the
-// sequence length, which is at most max_pages * P, so the page-table index
-// stays inside the row.
+// Page-table entries of the 4 tiles of the block at t0 (scalar loads; they
+// are used one block later).  Every token read lies below the sequence
+// length, which is at most max_pages * P, so the index stays inside the row.
+template <bool P16>
 __device__ __forceinline__ void load_addr(const Ctx &c, int t0, Addr &ad) {
   // the page table is read-only for the kernel's lifetime: constant address space, scalar loads
   const __attribute__((address_space(4))) int32_t *pt =
@@ -293,9 +334,9 @@ __device__ __forceinline__ void load_addr(const Ctx &c, int t0, Addr &ad) {
   const MfmaArgs &a = *c.a;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int tok = 16 * min(t0 / 16 + q, c.last_tile);
-    const int pi = tok >> a.p_shift;
-    ad.off[q] = tok & (a.P - 1);
+    const int tile = min((t0 >> 4) + q, c.last_tile);
+    const int pi = P16 ? tile : tile >> (a.p_shift - 4);
+    ad.off[q] = P16 ? 0 : (tile << 4) & (a.P - 1);
     ad.pg[q] = (pt[pi & a.tab_mask] & a.val_mask) + (pi & a.id_mask) + c.pg_base;
   }
 }
@@ -310,8 +351,12 @@ __device__ __forceinline__ uint32_t gload_u32(gbyte_ptr base, uint32_t off) {
   return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t *>(base + off);
 }
 
-// Issues the block's loads.  A page index outside the cache reads page 0
-// instead and sets `bad` (the rows' outputs become NaN).
+// Issues the block's loads.  A page index outside the cache (compared as
+// unsigned 32-bit, so negative entries fail too) reads page 0 instead and
+// sets `bad` (the rows' outputs become NaN).  The (page, head) block base is
+// pages + page * page_bytes (a 32 x 32 -> 64-bit product on the scalar
+// unit); the per-lane offsets carry the head and the section offsets.
+template <bool P16>
 __device__ __forceinline__ void load_block(const Ctx &c, const Addr &ad, Blk &o, bool &bad) {
   // (the empty asm keeps the 32-bit offsets in this block, so that the
   // loads are selected as scalar base + 32-bit VGPR offset)
@@ -320,17 +365,17 @@ __device__ __forceinline__ void load_block(const Ctx &c, const Addr &ad, Blk &o,
   const MfmaArgs &a = *c.a;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const bool ok = ad.pg[q] >= 0 && ad.pg[q] < a.num_pages;
+    const uint32_t pg = static_cast<uint32_t>(ad.pg[q]);
+    const bool ok = pg < a.np32;
     bad = bad || !ok;
     const uint64_t blk = reinterpret_cast<uint64_t>(a.pages) +
-                         static_cast<uint64_t>(ok ? ad.pg[q] : 0) * a.page_bytes;
-    const gbyte_ptr cb = reinterpret_cast<gbyte_ptr>(blk + 32u * static_cast<uint32_t>(ad.off[q]));
-    const gbyte_ptr mb = reinterpret_cast<gbyte_ptr>(blk + 64u * static_cast<uint32_t>(a.P) +
-                                                     4u * static_cast<uint32_t>(ad.off[q]));
-    o.kc[q] = gload_u64(cb, vo_k);
-    o.vx[q] = gload_u64(cb, vo_v);
-    o.km[q] = gload_u32(mb, vo_km);
-    o.vm[q] = gload_u32(mb, vo_vm);
+                         static_cast<uint64_t>(ok ? pg : 0u) * static_cast<uint64_t>(a.page_bytes);
+    const uint64_t cb = P16 ? blk : blk + 32u * static_cast<uint32_t>(ad.off[q]);
+    const uint64_t mb = P16 ? blk : blk + 4u * static_cast<uint32_t>(ad.off[q]);
+    o.kc[q] = gload_u64(reinterpret_cast<gbyte_ptr>(cb), vo_k);
+    o.vx[q] = gload_u64(reinterpret_cast<gbyte_ptr>(cb), vo_v);
+    o.km[q] = gload_u32(reinterpret_cast<gbyte_ptr>(mb), vo_km);
+    o.vm[q] = gload_u32(reinterpret_cast<gbyte_ptr>(mb), vo_vm);
   }
 }
 
@@ -347,6 +392,7 @@ struct State {
   float lsum, zsum;
   int kappa;
   bool have_ref;
+  bool flushed;         // (wave-uniform) the LDS accumulators hold flushed values
 };
 
 __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &blk, State &st, float *facc) {
@@ -363,7 +409,8 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     const float ks = half_bits_to_float(blk.km[q] & 0xffffu), kz = half_bits_to_float(blk.km[q] >> 16);
     sv[q] = half_bits_to_float(blk.vm[q] & 0xffffu);
     zv[q] = half_bits_to_float(blk.vm[q] >> 16);
-    const bool valid = st.row_ok && (t0 + 16 * q + c.c < c.t_end);
+    // (rows past the group's last hold q' = 0: finite logits, never stored)
+    const bool valid = 16 * q + c.c < c.t_end - t0;
     logit[q] = valid ? dot * (ks * st.unscale) + kz * st.qsum : -INFINITY;
     int es;
     (void)frexpf(sv[q], &es);  // s_v < 2^es
@@ -389,20 +436,23 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float *p = facc + (4 * i + r) * 64;
-        *p = (*p + static_cast<float>(byte_sum(st.accv[i][r], st.vx_lane))) * f2v;
+        *p = ((st.flushed ? *p : 0.0f) + static_cast<float>(byte_sum(st.accv[i][r], st.vx_lane))) * f2v;
       }
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.accv[i] = v4i{0, 0, 0, 0};
     st.lsum *= f2;
     st.zsum *= f2;
     st.kappa = newk;
+    st.flushed = true;
   }
   // ---- weights W = round(2^(logit + kappa) s_v) < 2^24, bytes offset to int8
   const float kf = static_cast<float>(st.kappa);
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float p = exp2f(logit[q] + kf);
+    // (hardware exp2: results below 2^-126 weigh nothing against the
+    // split's largest weight, >= 2^21, and masked tokens give exp2(-inf) = 0)
+    const float p = __builtin_amdgcn_exp2f(logit[q] + kf);
     st.lsum += p;
     st.zsum += p * zv[q];
     const uint32_t W = static_cast<uint32_t>(fmaf(p, sv[q], 0.5f));
@@ -429,13 +479,16 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     }
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
+template <int DT, bool P16>
+__global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float red[kWaves][4][4 + D];  // per wave, per row: m, l, z, flag, acc[128]
   __shared__ float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
   __shared__ float qs[4][D];               // q' of the group's rows
   __shared__ float qsum_s[4];
+  __shared__ int qshift_s[4];              // fixed-point shift S of each row's digits
+  __shared__ uint32_t digit_s[8][64];      // key-side A operand: dword [m][e] of each lane
   __shared__ uint32_t s_last;
+  __shared__ uint32_t s_next;               // next unclaimed 64-token block of the split
   const int s = blockIdx.x, b = blockIdx.z;
   const int h = blockIdx.y / a.n_rg, rg = blockIdx.y % a.n_rg;  // KV head, group of 4 query rows
   const int row0 = 4 * rg, nrows = min(4, a.R - row0);
@@ -459,8 +512,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   const uint32_t hoff = static_cast<uint32_t>(h) * 72u * static_cast<uint32_t>(a.P);
   c.vo_k = hoff + 32u * c.c + 8u * c.g;
   c.vo_v = hoff + 32u * a.P + 128u * c.g + 8u * c.c;
-  c.vo_km = hoff + 4u * c.c;
-  c.vo_vm = hoff + 4u * a.P + 4u * c.c;
+  c.vo_km = hoff + 64u * a.P + 4u * c.c;
+  c.vo_vm = hoff + 68u * a.P + 4u * c.c;
 
   // ---- loads of the query row of this wave (row0 + wave), then of the
   // first block, so that the query is prepared while the block is in flight
@@ -484,15 +537,26 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
     sb0 = sp[lane];
     sb1 = sp[lane + 64];
   }
-  constexpr int kStride = kWaves * kBlk;
-  int t0 = t_begin + wave * kBlk;
-  const int n_blk = t0 < c.t_end ? (c.t_end - t0 + kStride - 1) / kStride : 0;
-  Blk b0, b1;
-  Addr a0, a1;
-  // (unconditional: every address is clamped into the split, or tile 0)
-  load_addr(c, t0, a0);
-  load_block(c, a0, b0, bad);
-  load_addr(c, t0 + kStride, a1);
+  // blocks of the split: wave w starts with blocks w, w + 8, w + 16 and then
+  // claims the next unclaimed block from an LDS counter (waves of one CU
+  // progress at unequal speed; a static share would leave the slow waves'
+  // tail unhidden)
+  const int nb = c.t_end > t_begin ? (c.t_end - t_begin + kBlk - 1) / kBlk : 0;
+  if (threadIdx.x == 0) s_next = 3 * kWaves;  // (read after the barriers below)
+  // blocks jc[k] are in flight in buffer b[k]; ja[k] is a block whose
+  // page-table entries were fetched into ad[k]
+  int jc0 = wave, jc1 = wave + kWaves, jc2 = wave + 2 * kWaves, ja0 = 0, ja1 = 0, ja2 = 0;
+  Blk b0, b1, b2;
+  Addr a0, a1, a2;
+  // the first two blocks are in flight while the query rows are prepared,
+  // the third is issued after them (more loads ahead of the query rows'
+  // slow down their arrival at the start of the kernel); unconditional:
+  // every address is clamped into the split, or tile 0
+  load_addr<P16>(c, t_begin + kBlk * jc0, a0);
+  load_addr<P16>(c, t_begin + kBlk * jc1, a1);
+  load_addr<P16>(c, t_begin + kBlk * jc2, a2);
+  load_block<P16>(c, a0, b0, bad);
+  load_block<P16>(c, a1, b1, bad);
 
   // ---- query rows: q' = q R_K log2(e)/sqrt(128)
   {
@@ -502,20 +566,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
       y1 = DT == KVQ_F32 ? __uint_as_float(qb1) : __uint_as_float(qb1 << 16);
       rotate_query_signed(y0, y1, a.rk.kind, static_cast<float>(sb0), static_cast<float>(sb1), lane);
     }
-    const float sum = wave_sum(y0 + y1);
-    qs[wave][lane] = y0;
-    qs[wave][lane + 64] = y1;
-    if (lane == 0) qsum_s[wave] = sum;
+    if (wave < 4) {
+      const float sum = wave_sum(y0 + y1);
+      const float qabs = wave_maxf(fmaxf(fabsf(y0), fabsf(y1)));
+      int e2 = 0;
+      (void)frexpf(qabs, &e2);  // qabs < 2^e2
+      qs[wave][lane] = y0;
+      qs[wave][lane + 64] = y1;
+      if (lane == 0) {
+        qsum_s[wave] = sum;
+        qshift_s[wave] = 26 - e2;
+      }
+    }
   }
   __syncthreads();
-  // key-side A operand (row c = 4 r + d, k-slice g) and this lane's query row g
+  // key-side A operand (row c = 4 r + d, k-slice g), one dword per wave,
+  // and this lane's query row g
+  for (int d = wave; d < 8; d += kWaves) digit_s[d][lane] = query_digit_word(qs, qshift_s, lane, d >> 2, d & 3);
+  __syncthreads();
   State st;
   const int hr = c.g;  // query row (within the group) of the key-side lanes
-  {
-    const int qshift = query_digits(qs, lane, st.bk);
-    st.unscale = ldexpf(1.0f, -__shfl(qshift, 4 * hr));  // lane 4 hr forms the digits of row hr
-    st.qsum = qsum_s[hr];
-  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.bk[m][e] = static_cast<int>(digit_s[4 * m + e][lane]);
+  st.unscale = ldexpf(1.0f, -qshift_s[hr]);
+  st.qsum = qsum_s[hr];
+  load_block<P16>(c, a2, b2, bad);
   st.row_ok = hr < nrows;
   const int x = lane & 3;
   st.sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
@@ -529,32 +606,59 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
   st.lsum = st.zsum = 0.0f;
   st.kappa = 0;
   st.have_ref = false;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) facc[i * 64] = 0.0f;
+  st.flushed = false;
 
-  // ---- main loop: wave w takes blocks w, w+4, ...; block i+1 is in flight
-  // while block i is computed and the addresses of block i+2 are fetched
-  if (n_blk > 0) {
-    for (int i = 0; i < n_blk / 2; ++i) {
-      load_block(c, a1, b1, bad);
-      load_addr(c, t0 + 2 * kStride, a0);
-      compute_block(c, t0, b0, st, facc);
-      load_block(c, a0, b0, bad);
-      load_addr(c, t0 + 3 * kStride, a1);
-      compute_block(c, t0 + kStride, b1, st, facc);
-      t0 += 2 * kStride;
-    }
-    if (n_blk & 1) compute_block(c, t0, b0, st, facc);
+  // ---- main loop.  At the top of a step that computes block jc[k] (buffer
+  // b[k]): the wave's next two blocks are in flight in the other buffers,
+  // and ad[k] holds the page-table entries of the block after them (ja[k]).
+  // A step claims one more block before the computation, then issues the
+  // loads of ja[k] into the freed buffer and fetches the entries of the
+  // claimed block into ad[k+1] (whose block was issued two steps earlier).
+  // Claims increase, so a block past the split's end ends the loop; loads of
+  // such blocks re-read the split's last tile and are not used.
+  auto claim = [&]() -> uint32_t {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&s_next, 1u);
+    return v;
+  };
+  ja0 = __builtin_amdgcn_readfirstlane(claim());
+  load_addr<P16>(c, t_begin + kBlk * min(ja0, nb), a0);
+  auto step = [&](Blk &bk, int &jc, Addr &ak, int &ja, Addr &ak1, int &ja1n) {
+    const uint32_t v = claim();
+    compute_block(c, t_begin + kBlk * jc, bk, st, facc);
+    load_block<P16>(c, ak, bk, bad);
+    jc = ja;
+    ja1n = __builtin_amdgcn_readfirstlane(v);
+    load_addr<P16>(c, t_begin + kBlk * min(ja1n, nb), ak1);
+  };
+  for (;;) {
+    if (jc0 >= nb) break;
+    step(b0, jc0, a0, ja0, a1, ja1);
+    if (jc1 >= nb) break;
+    step(b1, jc1, a1, ja1, a2, ja2);
+    if (jc2 >= nb) break;
+    step(b2, jc2, a2, ja2, a0, ja0);
   }
 
-  // ---- per-wave result for each row
+  // ---- this wave's partial of each row: m = -kappa, l, z, flag, acc[128]
+  // (rows past the group's last are computed and never stored)
   const float lrow = row16_sum(st.lsum);
   const float zrow = row16_sum(st.zsum);
   const bool any_bad = __any(bad);
+  float *rw = &red[wave][0][0];  // [4][132], private to this wave
   // value accumulators: lane (4 r + x, g') holds column x (byte x, or the
   // ones for x = 3) of query row r for dims 8 (4 g' + i) + 4 hf + e
   const int vr = (lane >> 2) & 3;
   const float wbyte = x == 0 ? 1.0f : x == 1 ? 256.0f : x == 2 ? 65536.0f : 0.0f;
+  float vacc[32];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vacc[4 * k + i] = static_cast<float>(byte_sum(st.accv[k][i], x));
+  if (st.flushed) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) vacc[j] += facc[j * 64];
+  }
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -562,51 +666,43 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = 4 * hf + e;
-        float v = (facc[(4 * k + i) * 64] + static_cast<float>(byte_sum(st.accv[k][i], x))) * (wbyte * slot_inv(e));
+        float v = vacc[4 * k + i] * (wbyte * slot_inv(e));
         v += fdpp_xor1(v);
         v += fdpp_xor2(v);
-        if (x == 0 && vr < nrows) red[wave][vr][4 + 8 * (4 * c.g + i) + 4 * hf + e] = v;
+        if (x == 0) rw[vr * (D + 4) + 4 + 8 * (4 * c.g + i) + 4 * hf + e] = v;
       }
-  if (c.c == 0 && st.row_ok) {
-    red[wave][hr][0] = st.have_ref ? -static_cast<float>(st.kappa) : -INFINITY;
-    red[wave][hr][1] = lrow;
-    red[wave][hr][2] = zrow;
-    red[wave][hr][3] = any_bad ? 1.0f : 0.0f;
+  if (c.c == 0) {
+    const bool empty = !st.have_ref;  // no token of this wave counted for row hr
+    rw[hr * (D + 4) + 0] = empty ? -INFINITY : -static_cast<float>(st.kappa);
+    rw[hr * (D + 4) + 1] = any_bad ? __builtin_nanf("") : (empty ? 0.0f : lrow);
+    rw[hr * (D + 4) + 2] = empty ? 0.0f : zrow;
+    rw[hr * (D + 4) + 3] = 0.0f;
   }
-  __syncthreads();
-
-  // ---- merge the 4 waves (base-2 log-sum-exp) and write this split's partial
-  for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
-    const int r = idx / D, i = idx % D;
-    float mstar = -INFINITY;
-    bool nan = false;
+  // (an empty wave's accumulators are zero; the lanes of this wave read
+  // each other's LDS writes below)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // partial slot of this wave: split s, wave w -> s * 4 + w; stored with
+  // device-scope stores, consecutive lanes on consecutive floats
+  {
+    const int slot_w = s * kWaves + wave;
+    constexpr int kN = (4 * (D + 4) + 63) / 64;
+    float vals[kN];
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      mstar = fmaxf(mstar, red[w2][r][0]);
-      nan = nan || red[w2][r][3] != 0.0f;
-    }
-    float l = 0.0f, z = 0.0f, acc = 0.0f;
+    for (int k = 0; k < kN; ++k) vals[k] = rw[min(lane + 64 * k, 4 * (D + 4) - 1)];  // all reads, then the stores
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      if (red[w2][r][0] == -INFINITY) continue;
-      const float sc = exp2f(red[w2][r][0] - mstar);
-      l += sc * red[w2][r][1];
-      z += sc * red[w2][r][2];
-      acc += sc * red[w2][r][4 + i];
-    }
-    const int qq = (row0 + r) / a.G, g2 = (row0 + r) % a.G;
-    const size_t row = static_cast<size_t>(b) * a.Nq + qq;
-    float *dst = a.part + ((row * a.Hq + h * a.G + g2) * a.splits + s) * (D + 4);
-    store_partial(dst + 4 + i, mstar == -INFINITY ? 0.0f : acc);
-    if (i == 0) {
-      store_partial(dst, mstar);
-      store_partial(dst + 1, nan ? __builtin_nanf("") : (mstar == -INFINITY ? 0.0f : l));
-      store_partial(dst + 2, mstar == -INFINITY ? 0.0f : z);
-      store_partial(dst + 3, 0.0f);
+    for (int k = 0; k < kN; ++k) {
+      const int idx = lane + 64 * k;
+      if (idx < nrows * (D + 4)) {
+        const int r = idx / (D + 4), f = idx - r * (D + 4);
+        const int qq = (row0 + r) / a.G, g2 = (row0 + r) % a.G;
+        const size_t row = static_cast<size_t>(b) * a.Nq + qq;
+        store_partial(a.part + ((row * a.Hq + h * a.G + g2) * a.parts + slot_w) * (D + 4) + f, vals[k]);
+      }
     }
   }
 
-  // ---- the last split of this row group to arrive merges all splits.
+  // ---- the last split of this row group to arrive merges all partials.
   // The partials travel between workgroups (and XCDs) through device-scope
   // stores and loads only; every store of this workgroup is acknowledged
   // (all counters drained) before its arrival is counted, and the merging
@@ -621,7 +717,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(MfmaArgs a) {
     const int qq = (row0 + wave) / a.G, j = h * a.G + (row0 + wave) % a.G;
     const size_t row = static_cast<size_t>(b) * a.Nq + qq;
     float o0, o1;
-    merge_partials(a.part + (row * a.Hq + j) * a.splits * (D + 4), a.splits, lane, o0, o1);
+    merge_partials(a.part + (row * a.Hq + j) * a.parts * (D + 4), a.parts, lane, o0, o1);
     unrotate_value_wave(o0, o1, a.rv, h, lane);
     store_output_wave(a.out_o, a.ot, row, j, a.Hq, lane, o0, o1);
   }
@@ -654,6 +750,7 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.n_rg = (pl.rows_per_head + 3) / 4;
   a.split_tokens = pl.split_tokens;
   a.splits = pl.splits;
+  a.parts = pl.splits * kWaves;
   a.max_seq_len = pl.max_seq_len;
   a.P = page_size;
   a.p_shift = __builtin_ctz(static_cast<unsigned>(page_size));
@@ -669,8 +766,8 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
     a.id_mask = -1;
     a.base_mul = max_pages;
   }
-  a.num_pages = num_pages;
-  a.page_bytes = static_cast<uint64_t>(pl.H) * 72u * static_cast<uint64_t>(page_size);
+  a.np32 = static_cast<uint32_t>(num_pages < INT32_MAX ? num_pages : INT32_MAX);
+  a.page_bytes = static_cast<uint32_t>(pl.H) * 72u * static_cast<uint32_t>(page_size);
   a.pages = pages;
   a.seq_lens = seq_lens;
   a.q = q;
@@ -682,10 +779,18 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.out_o = out_o;
   a.ot = ot;
   const dim3 grid(pl.splits, pl.H * a.n_rg, pl.num_seqs);
-  if (dtype == KVQ_F32 || rk.kind == kRotPrescaled)
-    hipLaunchKernelGGL(decode_mfma_kernel<KVQ_F32>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_mfma_kernel<KVQ_BF16>, grid, dim3(256), 0, stream, a);
+  const bool f32 = dtype == KVQ_F32 || rk.kind == kRotPrescaled;
+  if (page_size == 16) {
+    if (f32)
+      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_F32, true>), grid, dim3(64 * kWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_BF16, true>), grid, dim3(64 * kWaves), 0, stream, a);
+  } else {
+    if (f32)
+      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_F32, false>), grid, dim3(64 * kWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_BF16, false>), grid, dim3(64 * kWaves), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ constexpr int kMaxRows = 64;   // query rows sharing one (sequence, KV head)
 constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
 constexpr int kMaxMfmaSplitTokens = 16384;  // tokens per split (page ids of a split fit in LDS)
 constexpr int kMaxSplits = 4096;            // split partials merged per (row, head)
+constexpr int kMfmaWaves = 8;               // waves per workgroup of the matrix-core decode kernel
 constexpr int64_t kMaxSeqLen = static_cast<int64_t>(kMaxSplits) * kMaxMfmaSplitTokens;
 
 // Rotation descriptor passed by value to kernels.
