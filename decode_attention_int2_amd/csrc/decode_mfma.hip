@@ -481,7 +481,7 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
 
 template <int DT, bool P16>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
-  __shared__ float red[kWaves][4][4 + D];  // per wave, per row: m, l, z, flag, acc[128]
+  __shared__ float red[kWaves][5][4 + D];  // per wave, per row: m, l, z, flag, acc[128]; row 4: unused stores
   __shared__ float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
   __shared__ float qs[4][D];               // q' of the group's rows
   __shared__ float qsum_s[4];
@@ -647,30 +647,41 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   const bool any_bad = __any(bad);
   float *rw = &red[wave][0][0];  // [4][132], private to this wave
   // value accumulators: lane (4 r + x, g') holds column x (byte x, or the
-  // ones for x = 3) of query row r for dims 8 (4 g' + i) + 4 hf + e
+  // ones for x = 3) of query row r for dims 8 (4 g' + i) + 4 hf + e.  The
+  // lane's column, offset-corrected in int32 (exact), times 256^x (0 for the
+  // ones) and the slot scale, summed over the quad (x = 0 keeps the sum).
   const int vr = (lane >> 2) & 3;
   const float wbyte = x == 0 ? 1.0f : x == 1 ? 256.0f : x == 2 ? 65536.0f : 0.0f;
-  float vacc[32];
+  const float wsc[4] = {wbyte, wbyte * 0.25f, wbyte * 0.0625f, wbyte};  // times slot_inv(e)
+  float t[32];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vacc[4 * k + i] = static_cast<float>(byte_sum(st.accv[k][i], x));
+    for (int i = 0; i < 4; ++i) {
+      const int d = st.accv[k][i];
+      const int ones = __builtin_amdgcn_mov_dpp(d, 0xFF, 0xF, 0xF, true);  // quad lane 3
+      t[4 * k + i] = static_cast<float>(d + 128 * ones);
+    }
   if (st.flushed) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) vacc[j] += facc[j * 64];
+    for (int j = 0; j < 32; ++j) t[j] += facc[j * 64];
   }
+  {
+#pragma clang fp contract(off)
+    // lanes x != 0 store their (unused) quad sums to row 4
+    const int lbase = x == 0 ? vr * (D + 4) + 4 + 32 * c.g : 4 * (D + 4) + lane;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = 4 * hf + e;
-        float v = vacc[4 * k + i] * (wbyte * slot_inv(e));
-        v += fdpp_xor1(v);
-        v += fdpp_xor2(v);
-        if (x == 0) rw[vr * (D + 4) + 4 + 8 * (4 * c.g + i) + 4 * hf + e] = v;
-      }
+        for (int i = 0; i < 4; ++i) {
+          float v = t[4 * (4 * hf + e) + i] * wsc[e];
+          v = v + fdpp_xor1(v);
+          v = v + fdpp_xor2(v);
+          rw[lbase + 8 * i + 4 * hf + e] = v;
+        }
+  }
   if (c.c == 0) {
     const bool empty = !st.have_ref;  // no token of this wave counted for row hr
     rw[hr * (D + 4) + 0] = empty ? -INFINITY : -static_cast<float>(st.kappa);
@@ -679,13 +690,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     rw[hr * (D + 4) + 3] = 0.0f;
   }
   // (an empty wave's accumulators are zero; the lanes of this wave read
-  // each other's LDS writes below)
+  // each other's LDS writes below: LDS operations of a wave complete in
+  // order, the fence keeps the compiler from reordering them)
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  // partial slot of this wave: split s, wave w -> s * 4 + w; stored with
+  // partial slot of this wave: split s, wave w -> s * kWaves + w; stored with
   // device-scope stores, consecutive lanes on consecutive floats
   {
     const int slot_w = s * kWaves + wave;
+    float *rb[4];  // partial base of each row of the group
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = min(row0 + r, a.R - 1);
+      const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
+      rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.parts + slot_w) * (D + 4);
+    }
     constexpr int kN = (4 * (D + 4) + 63) / 64;
     float vals[kN];
 #pragma unroll
@@ -693,12 +712,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int k = 0; k < kN; ++k) {
       const int idx = lane + 64 * k;
-      if (idx < nrows * (D + 4)) {
-        const int r = idx / (D + 4), f = idx - r * (D + 4);
-        const int qq = (row0 + r) / a.G, g2 = (row0 + r) % a.G;
-        const size_t row = static_cast<size_t>(b) * a.Nq + qq;
-        store_partial(a.part + ((row * a.Hq + h * a.G + g2) * a.parts + slot_w) * (D + 4) + f, vals[k]);
-      }
+      // rows covered by idx in [64k, 64k + 63]: (64k) / 132 and (64k + 63) / 132
+      constexpr int kRowStride = D + 4;
+      const int r_lo = (64 * k) / kRowStride, r_hi = (64 * k + 63) / kRowStride;
+      const int r = idx >= (r_lo + 1) * kRowStride ? r_hi : r_lo;
+      if (idx < nrows * kRowStride) store_partial(rb[r] + (idx - r * kRowStride), vals[k]);
     }
   }
 
