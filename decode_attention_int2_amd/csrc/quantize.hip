@@ -187,7 +187,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kQTiles = 64;       // 16-token tiles per workgroup
-constexpr int kQWaves = 4;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic rounds x to an integer (ties to even)
 constexpr uint32_t kMagicBits = 0x4B400000u;
 
@@ -199,20 +198,25 @@ __host__ __device__ constexpr uint32_t magic_pack_offset() {
   return acc;
 }
 
+// One side (keys or values) of a cache write.
+struct FastSide {
+  const uint16_t *x;    // [T][H][128] bf16 bits
+  const int8_t *signs;  // [H][128]
+  const float *matrix;  // [H][128][128]
+  float clip;
+  int side;             // 0 keys, 1 values
+};
+
 struct FastArgs {
-  const uint16_t *x;  // [T][H][128] bf16 bits
+  FastSide sd[2];       // the sides of the launch (sd[1] unused for one side)
   int64_t T;
   int H;
   const int64_t *slot_mapping;
-  const int8_t *signs;  // [H][128]
-  const float *matrix;  // [H][128][128]
-  const float *mean;    // [H][128] or null (keys only)
-  float clip;
+  const float *mean;    // [H][128] or null (keys only; the keys are sd[0])
   uint8_t *pages;
   int64_t num_pages;
   int P;
-  int side;     // 0 keys, 1 values
-  int p_shift;  // log2(P) if P is a power of two, else -1
+  int p_shift;          // log2(P) if P is a power of two, else -1
 };
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -227,18 +231,29 @@ __device__ __forceinline__ int qdpp_xor2(int v) { return __builtin_amdgcn_mov_dp
 // Output dim of A row r of accumulator tile nt.
 __device__ __forceinline__ int a_row_dim(int nt, int r) { return 32 * (r >> 2) + 4 * nt + (r & 3); }
 
-template <int KIND, bool kCenter, bool kWide>
-__global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
+constexpr int kQWavesF = 8;  // waves per workgroup of the cache-write kernel
+
+// kSides = 2: keys and values of each tile in one pass, so that every
+// (page, head) block of the cache is written whole within a few
+// instructions (writing its halves in two launches costs ~10% more time);
+// kStaged = number of staged rotations (1 when both sides use the same one).
+// (at most 128 VGPRs: two workgroups of 8 waves per CU)
+template <int KIND, bool kCenter, bool kWide, int kSides, int kStaged>
+__global__ __launch_bounds__(64 * kQWavesF, 4) void quantize_fast_kernel(FastArgs a) {
   constexpr int kParts = KIND == KVQ_ROT_DENSE ? 3 : (KIND == KVQ_ROT_SIGNED_HADAMARD ? 1 : 0);
-  extern __shared__ __attribute__((aligned(16))) uint4 ash[];  // [kParts][4 ks][8 nt][64 lanes]
+  extern __shared__ __attribute__((aligned(16))) uint4 ash[];  // [kStaged][kParts][4 ks][8 nt][64 lanes]
   __shared__ float mrot[D];
-  const int h = blockIdx.y;
+  // workgroup w takes head w % H of tile run w / H: the H heads of a run of
+  // tokens are read together
+  const int h = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.H));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tk = lane & 15, g = lane >> 4;
 
-  // ---- stage the rotation (A operand) and mu R
+  // ---- stage the rotations (A operands) and mu R
   if constexpr (kParts > 0) {
-    for (int e = threadIdx.x; e < 4 * 8 * 64; e += blockDim.x) {
+    for (int e2 = threadIdx.x; e2 < kStaged * 4 * 8 * 64; e2 += blockDim.x) {
+      const int st = e2 >> 11, e = e2 & 2047;
+      const FastSide &fs = a.sd[st];
       const int ks = e >> 9, nt = (e >> 6) & 7, ln = e & 63;
       const int d = a_row_dim(nt, ln & 15);
       const int k0 = 32 * ks + 8 * (ln >> 4);
@@ -250,10 +265,10 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
         for (int jj = 0; jj < 2; ++jj) {
           const int k = k0 + 2 * j2 + jj;
           if constexpr (KIND == KVQ_ROT_SIGNED_HADAMARD) {
-            const bool neg = (a.signs[h * D + k] < 0) != ((__popc(static_cast<unsigned>(k & d)) & 1) != 0);
+            const bool neg = (fs.signs[h * D + k] < 0) != ((__popc(static_cast<unsigned>(k & d)) & 1) != 0);
             (jj ? hi : lo)[0] = neg ? 0xBF80u : 0x3F80u;
           } else {
-            const float r = a.matrix[(static_cast<size_t>(h) * D + k) * D + d];
+            const float r = fs.matrix[(static_cast<size_t>(h) * D + k) * D + d];
             const uint32_t b0 = bf16_rne_bits(r);
             const float r1 = r - bf16_to_float(b0);
             const uint32_t b1 = bf16_rne_bits(r1);
@@ -268,10 +283,12 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
         for (int pp = 0; pp < kParts; ++pp) w[pp][j2] = lo[pp] | (hi[pp] << 16);
       }
 #pragma unroll
-      for (int pp = 0; pp < kParts; ++pp) ash[pp * 2048 + e] = uint4{w[pp][0], w[pp][1], w[pp][2], w[pp][3]};
+      for (int pp = 0; pp < kParts; ++pp)
+        ash[(st * kParts + pp) * 2048 + e] = uint4{w[pp][0], w[pp][1], w[pp][2], w[pp][3]};
     }
   }
   if constexpr (kCenter) {
+    const FastSide &fs = a.sd[0];
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
       const float *mu = a.mean + h * D;
       if constexpr (KIND == KVQ_ROT_IDENTITY) {
@@ -281,10 +298,10 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
         for (int k = 0; k < D; ++k) {
           double r;
           if constexpr (KIND == KVQ_ROT_SIGNED_HADAMARD)
-            r = static_cast<double>(a.signs[h * D + k]) * ((__popc(static_cast<unsigned>(k & d)) & 1) ? -1.0 : 1.0) *
+            r = static_cast<double>(fs.signs[h * D + k]) * ((__popc(static_cast<unsigned>(k & d)) & 1) ? -1.0 : 1.0) *
                 (1.0 / __builtin_sqrt(128.0));
           else
-            r = static_cast<double>(a.matrix[(static_cast<size_t>(h) * D + k) * D + d]);
+            r = static_cast<double>(fs.matrix[(static_cast<size_t>(h) * D + k) * D + d]);
           acc += static_cast<double>(mu[k]) * r;
         }
         // stored divided by the scale applied after the product (1/sqrt(128) for signed Hadamard)
@@ -295,98 +312,80 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
   __syncthreads();
 
   const int64_t n_tiles = (a.T + 15) / 16;
-  const int64_t tile_begin = static_cast<int64_t>(blockIdx.x) * kQTiles;
+  const int64_t tile_begin = static_cast<int64_t>(blockIdx.x / static_cast<unsigned>(a.H)) * kQTiles;
   const int64_t tile_end = min(tile_begin + kQTiles, n_tiles);
   const int64_t slots = a.num_pages * a.P;
   const size_t row_stride = static_cast<size_t>(a.H) * D;  // elements between tokens
   const float scale = KIND == KVQ_ROT_SIGNED_HADAMARD ? 0.08838834764831845f : 1.0f;  // 1/sqrt(128)
   const int qi = tk & 3;
 
-  // this lane's loads: 4 x 16 bytes of token tk (B operand k-slices, or 32 dims for identity)
-  // this lane's 4 x 16 B of token tk of `tile` and the token's destination
-  // slot (-1: not written), fetched together so the slot's latency is hidden
-  auto load_tile = [&](int64_t tile, uint4 (&xb)[4], int64_t &slot) {
-    const int64_t tt = tile * 16 + tk;
-    const int64_t t = min(tt, a.T - 1);
-    const uint16_t *row = a.x + static_cast<size_t>(t) * row_stride + static_cast<size_t>(h) * D;
+  // this lane's 4 x 16 B of token tk of `tile` (B operand k-slices, or 32
+  // dims for the identity) from x
+  auto load_tile = [&](const uint16_t *x, int64_t tile, uint4 (&xb)[4]) {
+    const int64_t t = min(tile * 16 + tk, a.T - 1);
+    const uint16_t *row = x + static_cast<size_t>(t) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int off = KIND == KVQ_ROT_IDENTITY ? 32 * g + 8 * ks : 32 * ks + 8 * g;
       xb[ks] = *reinterpret_cast<const uint4 *>(row + off);
     }
-    slot = tt < a.T ? (a.slot_mapping ? a.slot_mapping[t] : t) : -1;
+  };
+  // destination slot of token tk of `tile` (-1: not written)
+  auto load_slot = [&](int64_t tile) -> int64_t {
+    const int64_t tt = tile * 16 + tk;
+    const int64_t t = min(tt, a.T - 1);
+    return tt < a.T ? (a.slot_mapping ? a.slot_mapping[t] : t) : -1;
   };
 
-  // rotated values y[nt][i] = dim 32g + 4nt + i of token tk of the tile whose
-  // 16 B slices this lane holds (for the identity: its 32 dims directly)
-  auto rotate_pair = [&](const uint4 (&x0)[4], const uint4 (&x1)[4], float (&y0)[8][4], float (&y1)[8][4]) {
+  // rotated values y[nt][i] = dim 32g + 4nt + i of token tk (for the
+  // identity: its 32 dims directly), from the staged rotation `st`; the
+  // rotation slices are read from LDS right before their matrix-core steps
+  auto rotate = [&](const uint4 (&x0)[4], int st, bool center, float (&y0)[8][4]) {
     if constexpr (KIND == KVQ_ROT_IDENTITY) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint32_t w0[4] = {x0[ks].x, x0[ks].y, x0[ks].z, x0[ks].w};
-        const uint32_t w1[4] = {x1[ks].x, x1[ks].y, x1[ks].z, x1[ks].w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 8; ++j)
           y0[2 * ks + (j >> 2)][j & 3] = bf16_to_float((w0[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-          y1[2 * ks + (j >> 2)][j & 3] = bf16_to_float((w1[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-        }
       }
     } else {
-      // each A operand (rotation slice) read from LDS once feeds both tiles
-      v4f acc0[8], acc1[8];
+      const uint4 *as = ash + st * kParts * 2048;
+      v4f acc0[8];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc0[nt] = acc1[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      // the 8 A slices of a k-step are read from LDS together, one step ahead
-      // of their MFMAs (the scheduler barriers keep the reads from being
-      // sunk next to their uses, which would expose the LDS latency per MFMA)
-      uint4 acur[8], anext[8];
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acur[nt] = ash[nt * 64 + lane];
+      for (int nt = 0; nt < 8; ++nt) acc0[nt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      // (one k-step's slices at a time: the scheduler barrier keeps the LDS
+      // reads of later steps from being hoisted, which would cost registers)
 #pragma unroll
       for (int step = 0; step < kParts * 4; ++step) {
-        const int ks = step & 3;
-        if (step + 1 < kParts * 4) {
+        const v8bf b0 = __builtin_bit_cast(v8bf, x0[step & 3]);
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) anext[nt] = ash[((step + 1) * 8 + nt) * 64 + lane];
-        }
+        for (int nt = 0; nt < 8; ++nt)
+          acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, as[(step * 8 + nt) * 64 + lane]),
+                                                             b0, acc0[nt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        const v8bf b0 = __builtin_bit_cast(v8bf, x0[ks]);
-        const v8bf b1 = __builtin_bit_cast(v8bf, x1[ks]);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const v8bf aop = __builtin_bit_cast(v8bf, acur[nt]);
-          acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b0, acc0[nt], 0, 0, 0);
-          acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, b1, acc1[nt], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acur[nt] = anext[nt];
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y0[nt][i] = acc0[nt][i];  // rotated value / scale (the scale is applied in finish_tile)
-          y1[nt][i] = acc1[nt][i];
-        }
+        for (int i = 0; i < 4; ++i) y0[nt][i] = acc0[nt][i];  // rotated value / scale (applied in finish)
     }
     if constexpr (kCenter) {
-      // mrot holds mu R / scale for rotated kinds (mu for the identity)
+      if (center) {
+        // mrot holds mu R / scale for rotated kinds (mu for the identity)
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const float4 m = *reinterpret_cast<const float4 *>(&mrot[32 * g + 4 * nt]);
-        const float mm[4] = {m.x, m.y, m.z, m.w};
+        for (int nt = 0; nt < 8; ++nt) {
+          const float4 m = *reinterpret_cast<const float4 *>(&mrot[32 * g + 4 * nt]);
+          const float mm[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y0[nt][i] = y0[nt][i] - mm[i];
-          y1[nt][i] = y1[nt][i] - mm[i];
+          for (int i = 0; i < 4; ++i) y0[nt][i] = y0[nt][i] - mm[i];
         }
       }
     }
   };
 
-  // quantize, pack and write token tk of `tile` from its rotated values
-  auto finish_tile = [&](float (&y)[8][4], int64_t slot) {
+  // quantize, pack and write token tk of a tile from its rotated values
+  auto finish_tile = [&](float (&y)[8][4], int64_t slot, float clip, int side) {
     // ---- group statistics of token tk (its 4 lanes g hold 32 dims each)
     float mn = y[0][0], mx = y[0][0];
 #pragma unroll
@@ -411,8 +410,8 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
       mn = mn * scale;
       mx = mx * scale;
     }
-    float lo = a.clip * mn;
-    const float hi = a.clip * mx;
+    float lo = clip * mn;
+    const float hi = clip * mx;
     const float span = hi - lo;
     float s32 = span / 3.0f;
     asm volatile("" : "+v"(lo));
@@ -468,7 +467,7 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
     }
     uint8_t *base = a.pages + (static_cast<size_t>(page) * a.H + h) * static_cast<size_t>(72 * a.P);
 
-    if (a.side == 0) {
+    if (side == 0) {
       if (valid) *reinterpret_cast<uint2 *>(base + 32 * p + 8 * g) = uint2{cw[0], cw[1]};
     } else {
       // 4 consecutive tokens of a tile form one interleaved 128-byte V group
@@ -503,63 +502,71 @@ __global__ __launch_bounds__(256) void quantize_fast_kernel(FastArgs a) {
     }
     if (valid && g == 0) {
       const uint32_t meta = f16_bits(sh) | (f16_bits(zh) << 16);
-      *reinterpret_cast<uint32_t *>(base + (a.side ? 68 : 64) * a.P + 4 * p) = meta;
+      *reinterpret_cast<uint32_t *>(base + (side ? 68 : 64) * a.P + 4 * p) = meta;
     }
   };
 
-  // waves take tile pairs (2w, 2w+1), (2w+8, 2w+9), ...; the next pair is
-  // fetched while one is rotated and written (past the end loads re-read the
-  // last tile)
-  int64_t tile = tile_begin + 2 * wave;
+  // wave w takes tiles w, w+8, ...; the next tile (both sides) is fetched
+  // while one is rotated and written (past the end loads re-read the last tile)
+  // (two sides: the next tile's keys are fetched before this tile's keys are
+  // processed, its values before this tile's values, so at most three tiles
+  // of inputs are held at once)
+  int64_t tile = tile_begin + wave;
   if (tile >= tile_end) return;
-  uint4 xa[4], xb[4], na[4], nb[4];
-  int64_t sa, sb, sna, snb;
-  load_tile(tile, xa, sa);
-  load_tile(min(tile + 1, tile_end - 1), xb, sb);
-  for (; tile < tile_end; tile += 2 * kQWaves) {
-    const int64_t nxt = tile + 2 * kQWaves;
-    load_tile(min(nxt, tile_end - 1), na, sna);
-    load_tile(min(nxt + 1, tile_end - 1), nb, snb);
-    float ya[8][4], yb[8][4];
-    rotate_pair(xa, xb, ya, yb);
-    finish_tile(ya, sa);
-    if (tile + 1 < tile_end) finish_tile(yb, sb);
+  uint4 xa[kSides][4];
+  int64_t sa = load_slot(tile);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      xa[ks] = na[ks];
-      xb[ks] = nb[ks];
+  for (int sd = 0; sd < kSides; ++sd) load_tile(a.sd[sd].x, tile, xa[sd]);
+  for (; tile < tile_end; tile += kQWavesF) {
+    const int64_t nxt = min(tile + kQWavesF, tile_end - 1);
+    const int64_t sna = load_slot(nxt);
+#pragma unroll
+    for (int sd = 0; sd < kSides; ++sd) {
+      uint4 nx[4];
+      load_tile(a.sd[sd].x, nxt, nx);
+      float ya[8][4];
+      rotate(xa[sd], kStaged > 1 ? sd : 0, sd == 0 && a.sd[sd].side == 0, ya);
+      finish_tile(ya, sa, a.sd[sd].clip, a.sd[sd].side);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) xa[sd][ks] = nx[ks];
     }
     sa = sna;
-    sb = snb;
   }
 }
 
-template <int KIND, bool kCenter>
+template <int KIND, bool kCenter, int kSides, int kStaged>
 hipError_t launch_fast_kind(const FastArgs &a, bool wide, hipStream_t stream) {
   constexpr int kParts = KIND == KVQ_ROT_DENSE ? 3 : (KIND == KVQ_ROT_SIGNED_HADAMARD ? 1 : 0);
-  const size_t lds = static_cast<size_t>(kParts) * 2048 * sizeof(uint4);
+  const size_t lds = static_cast<size_t>(kStaged) * kParts * 2048 * sizeof(uint4);
   const int64_t n_tiles = (a.T + 15) / 16;
-  const dim3 grid(static_cast<unsigned>((n_tiles + kQTiles - 1) / kQTiles), static_cast<unsigned>(a.H));
-  auto kern = wide ? quantize_fast_kernel<KIND, kCenter, true> : quantize_fast_kernel<KIND, kCenter, false>;
+  const dim3 grid(static_cast<unsigned>((n_tiles + kQTiles - 1) / kQTiles * a.H));
+  auto kern = wide ? quantize_fast_kernel<KIND, kCenter, true, kSides, kStaged>
+                   : quantize_fast_kernel<KIND, kCenter, false, kSides, kStaged>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kQWavesF), lds, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fast_side(const FastArgs &a, int kind, bool wide, hipStream_t stream) {
+template <int kSides, int kStaged>
+hipError_t launch_fast_sides(const FastArgs &a, int kind, bool wide, hipStream_t stream) {
   const bool center = a.mean != nullptr;
+  if constexpr (kStaged == 2) {  // two dense rotations do not fit in LDS together
+    if (kind == KVQ_ROT_DENSE) return hipErrorInvalidValue;
+  }
   if (kind == KVQ_ROT_IDENTITY)
-    return center ? launch_fast_kind<KVQ_ROT_IDENTITY, true>(a, wide, stream)
-                  : launch_fast_kind<KVQ_ROT_IDENTITY, false>(a, wide, stream);
+    return center ? launch_fast_kind<KVQ_ROT_IDENTITY, true, kSides, kStaged>(a, wide, stream)
+                  : launch_fast_kind<KVQ_ROT_IDENTITY, false, kSides, kStaged>(a, wide, stream);
   if (kind == KVQ_ROT_SIGNED_HADAMARD)
-    return center ? launch_fast_kind<KVQ_ROT_SIGNED_HADAMARD, true>(a, wide, stream)
-                  : launch_fast_kind<KVQ_ROT_SIGNED_HADAMARD, false>(a, wide, stream);
-  return center ? launch_fast_kind<KVQ_ROT_DENSE, true>(a, wide, stream)
-                : launch_fast_kind<KVQ_ROT_DENSE, false>(a, wide, stream);
+    return center ? launch_fast_kind<KVQ_ROT_SIGNED_HADAMARD, true, kSides, kStaged>(a, wide, stream)
+                  : launch_fast_kind<KVQ_ROT_SIGNED_HADAMARD, false, kSides, kStaged>(a, wide, stream);
+  if constexpr (kStaged == 1)
+    return center ? launch_fast_kind<KVQ_ROT_DENSE, true, kSides, kStaged>(a, wide, stream)
+                  : launch_fast_kind<KVQ_ROT_DENSE, false, kSides, kStaged>(a, wide, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -575,13 +582,24 @@ hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_
     int p_shift = -1;
     for (int sh = 4; sh < 31; ++sh)
       if (page_size == (1 << sh)) p_shift = sh;
-    FastArgs fk{static_cast<const uint16_t *>(k), num_tokens, H, slot_mapping, rk.signs, rk.matrix, key_mean,
-                clip_k, pages, num_pages, page_size, 0, p_shift};
-    FastArgs fv{static_cast<const uint16_t *>(v), num_tokens, H, slot_mapping, rv.signs, rv.matrix, nullptr,
-                clip_v, pages, num_pages, page_size, 1, p_shift};
-    hipError_t e = launch_fast_side(fk, rk.kind, wide, stream);
+    const FastSide sk{static_cast<const uint16_t *>(k), rk.signs, rk.matrix, clip_k, 0};
+    const FastSide sv{static_cast<const uint16_t *>(v), rv.signs, rv.matrix, clip_v, 1};
+    // keys and values in one pass when both rotations fit in LDS together
+    // (signed Hadamard / identity, or one dense matrix shared by both sides);
+    // otherwise one launch per side
+    if (rk.kind == rv.kind) {
+      if (rk.kind != KVQ_ROT_DENSE)
+        return launch_fast_sides<2, 2>(FastArgs{{sk, sv}, num_tokens, H, slot_mapping, key_mean, pages, num_pages,
+                                                page_size, p_shift}, rk.kind, wide, stream);
+      if (rk.matrix == rv.matrix)
+        return launch_fast_sides<2, 1>(FastArgs{{sk, sv}, num_tokens, H, slot_mapping, key_mean, pages, num_pages,
+                                                page_size, p_shift}, rk.kind, wide, stream);
+    }
+    hipError_t e = launch_fast_sides<1, 1>(FastArgs{{sk, sk}, num_tokens, H, slot_mapping, key_mean, pages,
+                                                    num_pages, page_size, p_shift}, rk.kind, wide, stream);
     if (e != hipSuccess) return e;
-    return launch_fast_side(fv, rv.kind, wide, stream);
+    return launch_fast_sides<1, 1>(FastArgs{{sv, sv}, num_tokens, H, slot_mapping, nullptr, pages, num_pages,
+                                            page_size, p_shift}, rv.kind, wide, stream);
   }
   const int64_t items = num_tokens * H;
   int64_t blocks = (items + 3) / 4;
