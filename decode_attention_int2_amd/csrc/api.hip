@@ -1,10 +1,18 @@
 // api.hip -- the C ABI of libkvq: argument validation and launch order.
 // Every check that can run on the host runs before the first launch.
+#include <atomic>
+#include <chrono>
 #include <cmath>
 
 #include "kvq_internal.h"
 
 using namespace kvq;
+
+uint32_t kvq::next_launch_epoch() {
+  static std::atomic<uint32_t> next{
+      static_cast<uint32_t>(std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
+  return next.fetch_add(1);
+}
 
 namespace {
 
@@ -174,7 +182,9 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
     KVQ_TRY(launch_combine(pl, part, rv, out_o, ot, stream));
   }
   if (events && events->attn_stop) KVQ_TRY(hipEventRecord(events->attn_stop, stream));
-  if (w_o) KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, ypart, out_y, stream));
+  if (w_o)
+    KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, ypart, reinterpret_cast<uint64_t *>(ws + pl.off_wocnt), out_y,
+                                 stream));
   return KVQ_OK;
 }
 

@@ -389,127 +389,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *part, int n_i
   store_output_wave(out_o, ot, row, j, Hq, lane, o0, o1);
 }
 
-// ------------------------------------------------------------ W_O projection
-// y[row][n] = sum_k o[row][k] W_O[k][n].  A block takes 256 columns (4 per
-// lane) of one K slice for 16 rows; the 16 values o[.][k] of a k are one
-// scalar load (o laid out [K][16]) broadcast to every lane, so each W_O
-// element is loaded once per 16 rows and feeds 16 FMAs.  The block's 4 waves
-// split the slice and are summed in shared memory in a fixed order; slices
-// are summed by a second kernel in a fixed order.
-constexpr int kWoCols = 256;
-
-template <int DT>
-__device__ __forceinline__ float4 load_w4(const void *__restrict__ w, size_t idx, int n, int d_model) {
-  float e[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) e[c] = (n + c < d_model) ? load_elem<DT>(w, idx + c) : 0.0f;
-  return float4{e[0], e[1], e[2], e[3]};
-}
-
-constexpr int kWoWaves = 8;
-constexpr int kWoMaxSlice = 256;  // k per block (o slice staged in shared memory)
-
-template <int DT>
-__global__ __launch_bounds__(512) void wo_kernel(const float *__restrict__ ot, const void *__restrict__ w_o, int rows,
-                                                 int K, int d_model, int kslice, float *__restrict__ ypart) {
-  __shared__ float4 osh[kWoMaxSlice][kWoRows / 4];
-  __shared__ float4 red[4][kWoRows][64];  // [wave % 4][row][lane] column quads
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n = blockIdx.x * kWoCols + 4 * lane;
-  const int ks = blockIdx.y, rg = blockIdx.z;
-  const int k0 = ks * kslice, k1 = min(K, k0 + kslice);
-  // stage o[.][k0:k1] (16 rows per k, contiguous)
-  const float4 *src = reinterpret_cast<const float4 *>(ot + (static_cast<size_t>(rg) * K + k0) * kWoRows);
-  for (int idx = threadIdx.x; idx < (k1 - k0) * (kWoRows / 4); idx += blockDim.x)
-    osh[idx / (kWoRows / 4)][idx % (kWoRows / 4)] = src[idx];
-  __syncthreads();
-  const int kq = (kslice + kWoWaves - 1) / kWoWaves;
-  const int wk0 = min(k1, k0 + wave * kq), wk1 = min(k1, wk0 + kq);
-  float acc[kWoRows][4];
-#pragma unroll
-  for (int r = 0; r < kWoRows; ++r) acc[r][0] = acc[r][1] = acc[r][2] = acc[r][3] = 0.0f;
-  auto body = [&](int k, float4 w) {
-#pragma unroll
-    for (int r4 = 0; r4 < kWoRows / 4; ++r4) {
-      const float4 ov = osh[k - k0][r4];  // same address in every lane: broadcast
-      const float o4[4] = {ov.x, ov.y, ov.z, ov.w};
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        acc[4 * r4 + rr][0] += o4[rr] * w.x;
-        acc[4 * r4 + rr][1] += o4[rr] * w.y;
-        acc[4 * r4 + rr][2] += o4[rr] * w.z;
-        acc[4 * r4 + rr][3] += o4[rr] * w.w;
-      }
-    }
-  };
-  // block-uniform choice: whole 256-column block in range with 4-aligned rows -> vector loads only
-  if ((d_model & 3) == 0 && static_cast<int>(blockIdx.x + 1) * kWoCols <= d_model) {
-    // batches of 8 rows of W_O, the next batch in flight while one is used
-    using Raw = typename std::conditional<DT == KVQ_F32, float4, uint2>::type;
-    const Raw *wp = reinterpret_cast<const Raw *>(static_cast<const char *>(w_o) +
-                                                  (static_cast<size_t>(n) * (DT == KVQ_F32 ? 4 : 2)));
-    const size_t row_raw = static_cast<size_t>(d_model) / 4;  // Raw elements per W_O row
-    auto unpack = [](Raw r) -> float4 {
-      if constexpr (DT == KVQ_F32) {
-        return r;
-      } else {
-        return float4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
-                      __uint_as_float(r.y & 0xFFFF0000u)};
-      }
-    };
-    constexpr int kB = 8;
-    Raw cur[kB], nxt[kB];
-    if (wk0 < wk1) {
-#pragma unroll
-      for (int u = 0; u < kB; ++u) cur[u] = wp[static_cast<size_t>(min(wk0 + u, wk1 - 1)) * row_raw];
-      for (int k = wk0; k < wk1; k += kB) {
-#pragma unroll
-        for (int u = 0; u < kB; ++u) nxt[u] = wp[static_cast<size_t>(min(k + kB + u, wk1 - 1)) * row_raw];
-#pragma unroll
-        for (int u = 0; u < kB; ++u)
-          if (k + u < wk1) body(k + u, unpack(cur[u]));
-#pragma unroll
-        for (int u = 0; u < kB; ++u) cur[u] = nxt[u];
-      }
-    }
-  } else {
-    for (int k = wk0; k < wk1; ++k) body(k, load_w4<DT>(w_o, static_cast<size_t>(k) * d_model + n, n, d_model));
-  }
-  // fixed-order sum over the 8 waves: (w + (w+4)) for w < 4, then the four
-  if (wave >= 4) {
-#pragma unroll
-    for (int r = 0; r < kWoRows; ++r) red[wave - 4][r][lane] = float4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
-  }
-  __syncthreads();
-  if (wave < 4) {
-#pragma unroll
-    for (int r = 0; r < kWoRows; ++r) {
-      const float4 o = red[wave][r][lane];
-      red[wave][r][lane] = float4{acc[r][0] + o.x, acc[r][1] + o.y, acc[r][2] + o.z, acc[r][3] + o.w};
-    }
-  }
-  __syncthreads();
-  const int nrows = min(kWoRows, rows - rg * kWoRows);
-  for (int idx = threadIdx.x; idx < nrows * 64; idx += blockDim.x) {
-    const int r = idx >> 6, l = idx & 63;
-    const float4 a0 = red[0][r][l], a1 = red[1][r][l], a2 = red[2][r][l], a3 = red[3][r][l];
-    const float e[4] = {((a0.x + a1.x) + a2.x) + a3.x, ((a0.y + a1.y) + a2.y) + a3.y, ((a0.z + a1.z) + a2.z) + a3.z,
-                        ((a0.w + a1.w) + a2.w) + a3.w};
-    const int nn = blockIdx.x * kWoCols + 4 * l;
-    float *dst = ypart + (static_cast<size_t>(ks) * rows + rg * kWoRows + r) * d_model;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (nn + c < d_model) dst[nn + c] = e[c];
-  }
-}
-
-__global__ __launch_bounds__(256) void wo_reduce_kernel(const float *ypart, int ksplit, int total, float *y) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  float s = 0.0f;
-  for (int k = 0; k < ksplit; ++k) s += ypart[static_cast<size_t>(k) * total + idx];
-  y[idx] = s;
-}
 
 template <int RB>
 hipError_t launch_split_rb(const DecodePlan &pl, const SplitArgs &a, bool reference, int dtype,
@@ -583,12 +462,9 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   // W_O: K slices so that column blocks x slices x row groups fill the chip
   const int K = Hq * D;
   const size_t rows_w = static_cast<size_t>(num_seqs) * queries_per_seq;
-  const int col_blocks = d_model > 0 ? (d_model + kWoCols - 1) / kWoCols : 1;
+  const int col_blocks = d_model > 0 ? wo_col_blocks(d_model) : 1;
   const int row_groups = static_cast<int>((rows_w + kWoRows - 1) / kWoRows);
-  const int kslice = K < kWoMaxSlice ? K : kWoMaxSlice;
-  pl.wo_kslice = kslice;
-  pl.wo_ksplit = (K + kslice - 1) / kslice;
-  const int ks = pl.wo_ksplit;
+  const int ks = wo_kslices(K);
   const size_t rows = static_cast<size_t>(num_seqs) * queries_per_seq;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t off = 0;
@@ -603,6 +479,8 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   off = align(off + (d_model > 0 && ks > 1 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
   pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection
   off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * K * kWoRows * sizeof(float) : 0));
+  pl.off_wocnt = off;  // [row groups][column blocks] uint64 arrival counters of the W_O slices
+  off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * col_blocks * sizeof(uint64_t) : 0));
   const size_t n_rg_all = static_cast<size_t>(num_seqs) * H * ((queries_per_seq * (Hq / H) + 3) / 4);
   pl.off_cnt = off;  // [num_seqs][H][row groups] uint64
   off = align(off + n_rg_all * sizeof(uint64_t));
@@ -678,25 +556,5 @@ hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, fl
   return hipGetLastError();
 }
 
-hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *ypart,
-                                float *out_y, hipStream_t stream) {
-  const int rows = pl.num_seqs * pl.queries_per_seq;
-  if (rows == 0 || pl.d_model <= 0) return hipSuccess;
-  const int K = pl.Hq * D;
-  const int ks = pl.wo_ksplit;
-  float *dst = ks > 1 ? ypart : out_y;
-  dim3 grid((pl.d_model + kWoCols - 1) / kWoCols, ks, (rows + kWoRows - 1) / kWoRows);
-  if (dtype == KVQ_F32)
-    hipLaunchKernelGGL(wo_kernel<KVQ_F32>, grid, dim3(64 * kWoWaves), 0, stream, ot, w_o, rows, K, pl.d_model, pl.wo_kslice,
-                       dst);
-  else
-    hipLaunchKernelGGL(wo_kernel<KVQ_BF16>, grid, dim3(64 * kWoWaves), 0, stream, ot, w_o, rows, K, pl.d_model, pl.wo_kslice,
-                       dst);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ks == 1) return e;
-  const int total = rows * pl.d_model;
-  hipLaunchKernelGGL(wo_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, ypart, ks, total, out_y);
-  return hipGetLastError();
-}
 
 }  // namespace kvq

@@ -42,9 +42,6 @@
 // Merge: each split writes an (m, l, z, acc[128]) partial with m = -kappa;
 //   the last split of a (sequence, KV head, row group) to arrive (a tagged
 //   arrival counter) merges the partials, applies R_V^T and writes the output.
-#include <atomic>
-#include <chrono>
-
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -270,30 +267,6 @@ __device__ __forceinline__ void merge_partials(const float *p, int parts, int la
 // Device-scope store of a split partial (read by the merging workgroup).
 __device__ __forceinline__ void store_partial(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrival of one split at the counter of its (sequence, KV head, row group):
-// the high 32 bits hold the epoch of the launch, the low 32 bits the
-// arrivals; a word of another epoch (an earlier launch, or memory never
-// written by this kernel) or an impossible count reads as zero arrivals.
-// The last arrival writes zero arrivals back, so a replay with the same
-// epoch starts from zero as well.  The first exchange assumes that all other
-// splits have arrived (one round trip for the last split, which is the one
-// that goes on to merge); each failed exchange means the guess was wrong or
-// another split arrived in between, so the loop runs at most `splits` + 1
-// times.
-__device__ __forceinline__ bool arrive_last(unsigned long long *cnt, uint32_t epoch, int splits) {
-  const unsigned long long tag = static_cast<unsigned long long>(epoch) << 32;
-  unsigned long long old = tag | static_cast<uint32_t>(splits - 1);
-  for (;;) {
-    uint32_t n = (old >> 32) == epoch ? static_cast<uint32_t>(old) : 0u;
-    if (n >= static_cast<uint32_t>(splits)) n = 0;
-    ++n;
-    const unsigned long long want = n == static_cast<uint32_t>(splits) ? tag : (tag | n);
-    const unsigned long long seen = atomicCAS(cnt, old, want);
-    if (seen == old) return n == static_cast<uint32_t>(splits);
-    old = seen;
-  }
 }
 
 constexpr int kWaves = kMfmaWaves;  // waves per workgroup (one workgroup per CU)
@@ -754,11 +727,7 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
                               float *out_o, float *ot, hipStream_t stream) {
   if (pl.num_seqs == 0) return hipSuccess;
   if (rk.kind == KVQ_ROT_DENSE) return hipErrorInvalidValue;  // rotated by launch_query_rotation first
-  // arrival tags: a new value per launch, starting from a per-process value
-  // so that counters left in memory by other processes rarely carry it
-  static std::atomic<uint32_t> next_epoch{static_cast<uint32_t>(
-      std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
-  uint32_t epoch = next_epoch.fetch_add(1);
+  const uint32_t epoch = next_launch_epoch();
   MfmaArgs a{};
   a.R = pl.rows_per_head;
   a.G = pl.G;

@@ -221,6 +221,34 @@ __device__ __forceinline__ void store_output_wave(float *out_o, float *ot, size_
   }
 }
 
+// ----------------------------------------------------------------- arrivals
+// Arrival of one of `parts` workgroups at a shared counter: the high 32
+// bits hold the epoch of the launch, the low 32 bits the arrivals; a word of
+// another epoch (an earlier launch, or memory never written by this kernel)
+// or an impossible count reads as zero arrivals.  The last arrival writes
+// zero arrivals back, so a replay with the same epoch starts from zero as
+// well.  The first exchange assumes that all other parts have arrived (one
+// round trip for the last one, which goes on to combine their results); each
+// failed exchange means the guess was wrong or another part arrived in
+// between, so the loop runs at most `parts` + 1 times.  The caller makes its
+// results visible at device scope before arriving.
+__device__ __forceinline__ bool arrive_last(unsigned long long *cnt, uint32_t epoch, int parts) {
+  const unsigned long long tag = static_cast<unsigned long long>(epoch) << 32;
+  unsigned long long old = tag | static_cast<uint32_t>(parts - 1);
+  for (;;) {
+    uint32_t n = (old >> 32) == epoch ? static_cast<uint32_t>(old) : 0u;
+    if (n >= static_cast<uint32_t>(parts)) n = 0;
+    ++n;
+    const unsigned long long want = n == static_cast<uint32_t>(parts) ? tag : (tag | n);
+    const unsigned long long seen = atomicCAS(cnt, old, want);
+    if (seen == old) return n == static_cast<uint32_t>(parts);
+    old = seen;
+  }
+}
+// A new arrival tag per launch (host side), starting from a per-process value
+// so that counters left in memory by other processes rarely carry it.
+uint32_t next_launch_epoch();
+
 // ----------------------------------------------------------------- launchers
 hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
                            const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean, float clip_k,
@@ -229,9 +257,10 @@ hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_
 struct DecodePlan {
   int num_seqs, queries_per_seq, Hq, H, G, rows_per_head;  // rows_per_head = queries_per_seq * G
   int max_seq_len, splits, split_tokens;                   // split_tokens % kChunk == 0
-  int d_model, wo_ksplit, wo_kslice;
+  int d_model;
   size_t off_qrot, off_qsum, off_part, off_ypart;          // workspace layout (bytes)
   size_t off_ot;                                           // o laid out for the W_O projection
+  size_t off_wocnt;                                        // arrival counters of the W_O K slices
   size_t off_cnt;                                          // split arrival counters (matrix-core kernel)
   size_t total;
 };
@@ -267,8 +296,12 @@ hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const voi
 hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, float *ot,
                           hipStream_t stream);
 // out_y = concat(out_o) W_O, from the copy `ot` written with out_o.
+// out_y = concat(out_o) W_O on the matrix cores, from the copy `ot` written
+// with out_o; `counters` are the plan's W_O arrival counters.
 hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *ypart,
-                                float *out_y, hipStream_t stream);
+                                uint64_t *counters, float *out_y, hipStream_t stream);
+int wo_kslices(int K);          // K slices of the W_O projection
+int wo_col_blocks(int d_model); // column blocks of the W_O projection
 
 // Candidate search helpers.
 hipError_t launch_fill_i32(int32_t *p, int32_t value, int n, hipStream_t stream);
