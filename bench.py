@@ -51,6 +51,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-search measurement")
     ap.add_argument("--num-splits", type=int, default=0, help="split-K parts per sequence (0 = library default)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
@@ -198,6 +199,31 @@ def main():
 
     traffic = measured_traffic(a.traffic_json)
 
+    # calibration search (a separate workload of the same path): 65,536 tokens x 8
+    # KV heads, 9 dense candidates x 5 clips, 64 queries, per-head selection
+    cal = None
+    if not a.no_calibration:
+        del caches, ws
+        torch.cuda.empty_cache()
+        wc = synthetic.make("calib64k", dev)
+        C, n = len(wc.candidates), len(wc.clips)
+        T5, H5, Nq5, Hq5 = wc.tokens, wc.H, wc.q.shape[0], wc.Hq
+        out5 = torch.empty((H5, C, n), dtype=torch.float32, device=dev)
+        best5 = torch.empty((H5,), dtype=torch.int32, device=dev)
+        ws5 = torch.empty(kvq.kvq_candidate_workspace_bytes(T5, H5, Hq5, Nq5, C, n, wc.d_model), dtype=torch.uint8,
+                          device=dev)
+        rots5 = [kvq.Rotation(cd.kind, signs=cd.signs, matrix=cd.matrix) for cd in wc.candidates]
+        search = lambda i: kvq.kvq_candidate_nmse(wc.k, wc.v, wc.q, rots5, list(wc.clips), wc.w_o,
+                                                  kvq.KVQ_SELECT_PER_HEAD, out5, best5, workspace=ws5)
+        cal_ms = timed(search, 3)
+        # work of one search: attention of every variant (QK^T and PV) and the rotations
+        att_flop = C * n * Nq5 * Hq5 * T5 * 128 * 2 * 2
+        rot_flop = C * T5 * H5 * 2 * 128 * 128 * 2
+        cal = {"workload": "calib64k", "description": synthetic.DESCRIPTIONS["calib64k"], "ms": round(cal_ms, 3),
+               "variants": C * n, "attention_gflop": round(att_flop / 1e9, 1), "rotation_gflop": round(rot_flop / 1e9, 1),
+               "tflop_s": round((att_flop + rot_flop) / (cal_ms * 1e-3) / 1e12, 2),
+               "best": [int(x) for x in best5.cpu().tolist()]}
+
     base = None
     if not a.no_cpu_baseline:
         w_cpu = {"tokens": T, "k": w.k[:2 * T].float().cpu().numpy(), "v": w.v[:2 * T].float().cpu().numpy(),
@@ -232,6 +258,7 @@ def main():
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_mfma_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": base,
+        "calibration_search": cal,
     }
     print(json.dumps(out))
 
