@@ -1,5 +1,6 @@
 // api.hip -- the C ABI of libkvq: argument validation and launch order.
 // Every check that can run on the host runs before the first launch.
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cmath>
@@ -47,7 +48,8 @@ struct CandidateLayout {
   int64_t num_pages;
   DecodePlan plan;      // matrix-core decode of the quantized variants
   DecodePlan ref_plan;  // full-precision reference readout (VALU kernel): more splits
-  size_t off_cache, off_dec, off_refdec, off_seqlen, off_ohat, off_oref, off_nmse, total;
+  size_t cache_bytes;
+  size_t off_cache, off_dec, off_refdec, off_seqlen, off_ohat, off_oref, off_nmse, off_gram, off_den, total;
 };
 
 CandidateLayout candidate_layout(int64_t T, int H, int Hq, int Nq, int C, int n_clip) {
@@ -59,8 +61,9 @@ CandidateLayout candidate_layout(int64_t T, int H, int Hq, int Nq, int C, int n_
   L.ref_plan = make_decode_plan(1, Nq, Hq, H, static_cast<int>(T), 0, ref_splits);
   const int U = H;  // upper bound over both modes
   size_t off = 0;
-  L.off_cache = off;
-  off = align256(off + kvq_cache_bytes(L.num_pages, 16, H));
+  L.off_cache = off;  // one cache per clip ratio
+  L.cache_bytes = align256(kvq_cache_bytes(L.num_pages, 16, H));
+  off = align256(off + L.cache_bytes * n_clip);
   L.off_dec = off;
   off = align256(off + L.plan.total);
   L.off_refdec = off;
@@ -73,6 +76,11 @@ CandidateLayout candidate_layout(int64_t T, int H, int Hq, int Nq, int C, int n_
   off = align256(off + static_cast<size_t>(Nq) * Hq * D * sizeof(float));
   L.off_nmse = off;
   off = align256(off + static_cast<size_t>(U) * C * n_clip * Nq * sizeof(float));
+  L.off_gram = off;  // Gram blocks of W_O, sized for the larger of the two modes
+  off = align256(off + std::max(nmse_gram_floats(Hq, H, KVQ_SELECT_JOINT), nmse_gram_floats(Hq, H, KVQ_SELECT_PER_HEAD)) *
+                           sizeof(float));
+  L.off_den = off;   // reference output norms [U][Nq]
+  off = align256(off + static_cast<size_t>(U) * Nq * sizeof(double));
   L.total = off;
   return L;
 }
@@ -250,6 +258,9 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
     KVQ_TRY(launch_reference_split(rp, k, v, dtype, num_tokens, rq, rpart, stream));
     KVQ_TRY(launch_combine(rp, rpart, ident, o_ref, nullptr, stream));
   }
+  float *gram = reinterpret_cast<float *>(ws + L.off_gram);
+  double *den = reinterpret_cast<double *>(ws + L.off_den);
+  KVQ_TRY(launch_nmse_prepare(o_ref, w_o, dtype, Nq, Hq, H, d_model, mode, gram, den, stream));
   KVQ_TRY(launch_fill_i32(seq_len, static_cast<int32_t>(num_tokens), 1, stream));
   for (int r = 0; r < num_candidates; ++r) {
     const RotDev rot = to_dev(candidates[r]);
@@ -261,18 +272,20 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
       qk = qrot;
       rq = RotDev{kRotPrescaled, nullptr, nullptr};
     }
+    // the candidate's caches of every clip ratio in one pass (one rotation)
+    KVQ_TRY(launch_quantize_clips(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips, clips, num_clips,
+                                  pages, L.num_pages, 16, L.cache_bytes, stream));
     for (int i = 0; i < num_clips; ++i) {
-      KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips[i], clips[i], pages,
-                              L.num_pages, 16, stream));
+      uint8_t *pages_i = pages + static_cast<size_t>(i) * L.cache_bytes;
       if (mfma) {
-        KVQ_TRY(launch_decode_mfma(pl, qk, dtype, rq, rot, pages, L.num_pages, 16, nullptr,
+        KVQ_TRY(launch_decode_mfma(pl, qk, dtype, rq, rot, pages_i, L.num_pages, 16, nullptr,
                                    static_cast<int>(L.num_pages), seq_len, part, counters, o_hat, nullptr, stream));
       } else {
-        KVQ_TRY(launch_decode_split(pl, pages, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
+        KVQ_TRY(launch_decode_split(pl, pages_i, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,
                                     qrot, qsum, part, stream));
         KVQ_TRY(launch_combine(pl, part, rot, o_hat, nullptr, stream));
       }
-      KVQ_TRY(launch_nmse_terms(o_hat, o_ref, w_o, dtype, Nq, Hq, H, d_model, mode,
+      KVQ_TRY(launch_nmse_terms(o_hat, o_ref, gram, den, Nq, Hq, H, mode,
                                 nmse_q + (static_cast<size_t>(r) * num_clips + i) * Nq, stride_u, stream));
     }
   }

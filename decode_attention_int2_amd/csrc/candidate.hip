@@ -16,63 +16,91 @@ __global__ void fill_i32_kernel(int32_t *p, int32_t value, int n) {
   if (i < n) p[i] = value;
 }
 
-// One workgroup per (query q, unit u).  JOINT: unit = all query heads, the
-// per-head contributions are summed before squaring.  PER_HEAD: unit = the
-// query heads of KV head u, each contribution squared separately.
+// The post-W_O error of a unit through the Gram matrix of its W_O rows:
+// ||sum_j x_j W_j||^2 = x G x^T with G = W W^T over the unit's rows of W_O
+// (W_j = rows j*128 .. j*128+127).  PER_HEAD: each query head j of the unit
+// is squared separately, so only the diagonal blocks G_jj = W_j W_j^T are
+// needed (blocks of 128); JOINT: the unit is the whole layer output, one
+// block of K = Hq * 128.  G is computed once per search; the reference
+// output's square norms once per search; each variant then needs x G x^T of
+// its output error x = o_hat - o_ref only.
+
+// G[a][b] = sum_n W[a][n] W[b][n] for a, b in one block (fp32 products and
+// sums): one workgroup per 64 x 64 tile of a block, W staged 64 columns at a
+// time.  grid = (tiles per block, blocks).
 template <int DT>
-__global__ __launch_bounds__(256) void nmse_terms_kernel(const float *o_hat, const float *o_ref, const void *w_o,
-                                                         int Hq, int G, int d_model, int mode, float *nmse_q,
-                                                         size_t stride_u, int Nq) {
-  extern __shared__ float sh[];  // [2][nh][128]: delta o, reference o
-  __shared__ double red[2][4];
+__global__ __launch_bounds__(256) void gram_kernel(const void *w_o, int d_model, int bdim, float *g) {
+  __shared__ float wa[64][65], wb[64][65];
+  const int blk = blockIdx.y, tpr = bdim / 64;
+  const int ta = blockIdx.x / tpr, tb = blockIdx.x % tpr;
+  const int a0 = blk * bdim + 64 * ta, b0 = blk * bdim + 64 * tb;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // 4 x 4 entries: rows ty + 16 i, cols tx + 16 j
+  float acc[4][4] = {};
+  for (int n0 = 0; n0 < d_model; n0 += 64) {
+    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+      const int r = idx >> 6, cc = idx & 63;
+      const bool in = n0 + cc < d_model;
+      wa[r][cc] = in ? load_elem<DT>(w_o, static_cast<size_t>(a0 + r) * d_model + n0 + cc) : 0.0f;
+      wb[r][cc] = in ? load_elem<DT>(w_o, static_cast<size_t>(b0 + r) * d_model + n0 + cc) : 0.0f;
+    }
+    __syncthreads();
+    for (int cc = 0; cc < 64; ++cc) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = wa[ty + 16 * i][cc];
+        bv[i] = wb[tx + 16 * i][cc];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+    }
+    __syncthreads();
+  }
+  float *gb = g + static_cast<size_t>(blk) * bdim * bdim;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gb[static_cast<size_t>(64 * ta + ty + 16 * i) * bdim + 64 * tb + tx + 16 * j] = acc[i][j];
+}
+
+// One workgroup per (query q, unit u): e = sum over the unit's blocks of
+// x G x^T, x = x1 - x0 (x0 may be null).  kDen: store e as the unit's
+// reference norm den[u][q]; otherwise write the NMSE e / den[u][q].
+template <bool kDen>
+__global__ __launch_bounds__(256) void quadform_kernel(const float *x1, const float *x0, const float *g, int Hq,
+                                                       int blocks_per_unit, int bdim, double *den, float *nmse_q,
+                                                       size_t stride_u, int Nq) {
+  extern __shared__ float xs[];  // [bdim]
+  __shared__ double red[4];
   const int q = blockIdx.x, u = blockIdx.y;
-  const int j0 = (mode == KVQ_SELECT_JOINT) ? 0 : u * G;
-  const int nh = (mode == KVQ_SELECT_JOINT) ? Hq : G;
-  float *dob = sh, *orb = sh + nh * D;
-  for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
-    const size_t g = (static_cast<size_t>(q) * Hq + j0) * D + idx;
-    dob[idx] = o_hat[g] - o_ref[g];
-    orb[idx] = o_ref[g];
-  }
-  __syncthreads();
-  double num = 0.0, den = 0.0;
-  for (int n = threadIdx.x; n < d_model; n += 256) {
-    float dy_sum = 0.0f, y_sum = 0.0f;
-    for (int jj = 0; jj < nh; ++jj) {
-      float dy = 0.0f, y = 0.0f;
-      const size_t krow = static_cast<size_t>(j0 + jj) * D;
-      for (int k = 0; k < D; ++k) {
-        const float w = load_elem<DT>(w_o, (krow + k) * d_model + n);
-        dy += dob[jj * D + k] * w;
-        y += orb[jj * D + k] * w;
-      }
-      if (mode == KVQ_SELECT_JOINT) {
-        dy_sum += dy;
-        y_sum += y;
-      } else {
-        num += static_cast<double>(dy) * dy;
-        den += static_cast<double>(y) * y;
-      }
-    }
-    if (mode == KVQ_SELECT_JOINT) {
-      num += static_cast<double>(dy_sum) * dy_sum;
-      den += static_cast<double>(y_sum) * y_sum;
+  double e = 0.0;
+  for (int bi = 0; bi < blocks_per_unit; ++bi) {
+    const int blk = u * blocks_per_unit + bi;  // block index = first query head of the block / (bdim / 128)
+    const size_t xoff = static_cast<size_t>(q) * Hq * D + static_cast<size_t>(blk) * bdim;
+    __syncthreads();
+    for (int i = threadIdx.x; i < bdim; i += 256) xs[i] = x0 ? x1[xoff + i] - x0[xoff + i] : x1[xoff + i];
+    __syncthreads();
+    const float *gb = g + static_cast<size_t>(blk) * bdim * bdim;
+    // (G is symmetric bit for bit -- its two triangles are the same products
+    // summed in the same order -- so thread r reads column r: coalesced)
+    for (int r = threadIdx.x; r < bdim; r += 256) {
+      float t = 0.0f;
+      for (int cc = 0; cc < bdim; ++cc) t += gb[static_cast<size_t>(cc) * bdim + r] * xs[cc];
+      e += static_cast<double>(xs[r]) * t;
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    num += __shfl_xor(num, o);
-    den += __shfl_xor(den, o);
-  }
+  for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    red[0][wave] = num;
-    red[1][wave] = den;
-  }
+  if (lane == 0) red[wave] = e;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const double a = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const double b = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    nmse_q[static_cast<size_t>(u) * stride_u + q] = static_cast<float>(a / b);
+    const double tot = red[0] + red[1] + red[2] + red[3];
+    if constexpr (kDen)
+      den[static_cast<size_t>(u) * Nq + q] = tot;
+    else
+      nmse_q[static_cast<size_t>(u) * stride_u + q] = static_cast<float>(tot / den[static_cast<size_t>(u) * Nq + q]);
   }
 }
 
@@ -108,19 +136,50 @@ hipError_t launch_fill_i32(int32_t *p, int32_t value, int n, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const void *w_o, int dtype, int Nq, int Hq,
-                             int H, int d_model, int mode, float *nmse_q_out, size_t stride_u, hipStream_t stream) {
-  const int G = Hq / H;
-  const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
-  const int nh = (mode == KVQ_SELECT_JOINT) ? Hq : G;
-  const size_t smem = sizeof(float) * 2 * nh * D;
-  dim3 grid(Nq, U);
+// Block geometry of the NMSE unit: PER_HEAD blocks of 128 (one per query
+// head, G per unit), JOINT one block of Hq * 128.
+static void nmse_blocks(int Hq, int H, int mode, int &bdim, int &nblocks, int &per_unit) {
+  if (mode == KVQ_SELECT_JOINT) {
+    bdim = Hq * D;
+    nblocks = 1;
+    per_unit = 1;
+  } else {
+    bdim = D;
+    nblocks = Hq;
+    per_unit = Hq / H;
+  }
+}
+
+size_t nmse_gram_floats(int Hq, int H, int mode) {
+  int bdim, nb, pu;
+  nmse_blocks(Hq, H, mode, bdim, nb, pu);
+  return static_cast<size_t>(nb) * bdim * bdim;
+}
+
+hipError_t launch_nmse_prepare(const float *o_ref, const void *w_o, int dtype, int Nq, int Hq, int H, int d_model,
+                               int mode, float *gram, double *den, hipStream_t stream) {
+  int bdim, nb, pu;
+  nmse_blocks(Hq, H, mode, bdim, nb, pu);
+  const dim3 ggrid((bdim / 64) * (bdim / 64), nb);
   if (dtype == KVQ_F32)
-    hipLaunchKernelGGL(nmse_terms_kernel<KVQ_F32>, grid, dim3(256), smem, stream, o_hat, o_ref, w_o, Hq, G, d_model,
-                       mode, nmse_q_out, stride_u, Nq);
+    hipLaunchKernelGGL(gram_kernel<KVQ_F32>, ggrid, dim3(256), 0, stream, w_o, d_model, bdim, gram);
   else
-    hipLaunchKernelGGL(nmse_terms_kernel<KVQ_BF16>, grid, dim3(256), smem, stream, o_hat, o_ref, w_o, Hq, G,
-                       d_model, mode, nmse_q_out, stride_u, Nq);
+    hipLaunchKernelGGL(gram_kernel<KVQ_BF16>, ggrid, dim3(256), 0, stream, w_o, d_model, bdim, gram);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
+  hipLaunchKernelGGL(quadform_kernel<true>, dim3(Nq, U), dim3(256), sizeof(float) * bdim, stream, o_ref, nullptr,
+                     gram, Hq, pu, bdim, den, nullptr, size_t{0}, Nq);
+  return hipGetLastError();
+}
+
+hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const float *gram, const double *den, int Nq,
+                             int Hq, int H, int mode, float *nmse_q_out, size_t stride_u, hipStream_t stream) {
+  int bdim, nb, pu;
+  nmse_blocks(Hq, H, mode, bdim, nb, pu);
+  const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
+  hipLaunchKernelGGL(quadform_kernel<false>, dim3(Nq, U), dim3(256), sizeof(float) * bdim, stream, o_hat, o_ref,
+                     gram, Hq, pu, bdim, const_cast<double *>(den), nmse_q_out, stride_u, Nq);
   return hipGetLastError();
 }
 

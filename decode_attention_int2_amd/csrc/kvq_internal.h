@@ -253,6 +253,13 @@ uint32_t next_launch_epoch();
 hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
                            const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean, float clip_k,
                            float clip_v, uint8_t *pages, int64_t num_pages, int page_size, hipStream_t stream);
+// The same cache write for several clip ratios at once (keys: clips_k[c],
+// values: clips_v[c]), cache c at pages + c * clip_stride: one rotation and
+// one set of group statistics per tile for all of them.
+hipError_t launch_quantize_clips(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
+                                 const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean,
+                                 const float *clips_k, const float *clips_v, int nclip, uint8_t *pages,
+                                 int64_t num_pages, int page_size, size_t clip_stride, hipStream_t stream);
 
 struct DecodePlan {
   int num_seqs, queries_per_seq, Hq, H, G, rows_per_head;  // rows_per_head = queries_per_seq * G
@@ -305,8 +312,14 @@ int wo_col_blocks(int d_model); // column blocks of the W_O projection
 
 // Candidate search helpers.
 hipError_t launch_fill_i32(int32_t *p, int32_t value, int n, hipStream_t stream);
-hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const void *w_o, int dtype, int Nq, int Hq,
-                             int H, int d_model, int mode, float *nmse_q_out, size_t stride_u, hipStream_t stream);
+// Post-W_O NMSE through the Gram matrix of W_O (see candidate.hip):
+// prepare once per search (Gram blocks and the reference output's norms),
+// then one launch per variant.
+size_t nmse_gram_floats(int Hq, int H, int mode);
+hipError_t launch_nmse_prepare(const float *o_ref, const void *w_o, int dtype, int Nq, int Hq, int H, int d_model,
+                               int mode, float *gram, double *den, hipStream_t stream);
+hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const float *gram, const double *den, int Nq,
+                             int Hq, int H, int mode, float *nmse_q_out, size_t stride_u, hipStream_t stream);
 hipError_t launch_select(const float *nmse_q, int U, int C, int n_clip, int Nq, float *out_nmse, int32_t *out_best,
                          hipStream_t stream);
 

@@ -198,12 +198,14 @@ __host__ __device__ constexpr uint32_t magic_pack_offset() {
   return acc;
 }
 
+constexpr int kMaxClips = 8;  // clip ratios written by one launch (one cache each)
+
 // One side (keys or values) of a cache write.
 struct FastSide {
   const uint16_t *x;    // [T][H][128] bf16 bits
   const int8_t *signs;  // [H][128]
   const float *matrix;  // [H][128][128]
-  float clip;
+  float clip[kMaxClips];  // clip ratio of cache c (c < nclip)
   int side;             // 0 keys, 1 values
 };
 
@@ -217,6 +219,8 @@ struct FastArgs {
   int64_t num_pages;
   int P;
   int p_shift;          // log2(P) if P is a power of two, else -1
+  int nclip;            // caches written (one per clip ratio), at pages + c * clip_stride
+  size_t clip_stride;   // bytes between the caches of consecutive clip ratios
 };
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -238,7 +242,8 @@ constexpr int kQWavesF = 8;  // waves per workgroup of the cache-write kernel
 // instructions (writing its halves in two launches costs ~10% more time);
 // kStaged = number of staged rotations (1 when both sides use the same one).
 // (at most 128 VGPRs: two workgroups of 8 waves per CU)
-template <int KIND, bool kCenter, bool kWide, int kSides, int kStaged>
+// kClips: false = one clip ratio (clip[0], cache at pages), true = a.nclip.
+template <int KIND, bool kCenter, bool kWide, int kSides, int kStaged, bool kClips>
 __global__ __launch_bounds__(64 * kQWavesF, 4) void quantize_fast_kernel(FastArgs a) {
   constexpr int kParts = KIND == KVQ_ROT_DENSE ? 3 : (KIND == KVQ_ROT_SIGNED_HADAMARD ? 1 : 0);
   extern __shared__ __attribute__((aligned(16))) uint4 ash[];  // [kStaged][kParts][4 ks][8 nt][64 lanes]
@@ -385,7 +390,11 @@ __global__ __launch_bounds__(64 * kQWavesF, 4) void quantize_fast_kernel(FastArg
   };
 
   // quantize, pack and write token tk of a tile from its rotated values
-  auto finish_tile = [&](float (&y)[8][4], int64_t slot, float clip, int side) {
+  // quantize, pack and write token tk of a tile from its rotated values, for
+  // every clip ratio of the side (one cache each; statistics and
+  // destination computed once)
+  auto finish_tile = [&](float (&y)[8][4], int64_t slot, const FastSide &fs) {
+    const int side = fs.side;
     // ---- group statistics of token tk (its 4 lanes g hold 32 dims each)
     float mn = y[0][0], mx = y[0][0];
 #pragma unroll
@@ -410,41 +419,6 @@ __global__ __launch_bounds__(64 * kQWavesF, 4) void quantize_fast_kernel(FastArg
       mn = mn * scale;
       mx = mx * scale;
     }
-    float lo = clip * mn;
-    const float hi = clip * mx;
-    const float span = hi - lo;
-    float s32 = span / 3.0f;
-    asm volatile("" : "+v"(lo));
-    asm volatile("" : "+v"(s32));
-    const _Float16 sh = static_cast<_Float16>(s32);
-    const _Float16 zh = static_cast<_Float16>(lo);
-    const float s = static_cast<float>(sh);
-    const float z = static_cast<float>(zh);
-    const float inv = s != 0.0f ? 1.0f / s : 0.0f;  // s == 0: every code is 0
-    // rotated kinds: t = (u scale - z) inv computed as u (scale inv) - z inv
-    const float si = scale * inv, zi = z * inv;
-
-    // ---- codes, packed 16 per dword by shift-add of magic-biased values
-    uint32_t cw[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t acc = 0;
-#pragma unroll
-      for (int nt = 3; nt >= 0; --nt)
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          float tq;
-          if constexpr (KIND == KVQ_ROT_IDENTITY) {
-            const float t = (y[4 * half + nt][i] - z) * inv;
-            tq = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f) + kMagic;
-          } else {
-            const float t = __builtin_fmaf(y[4 * half + nt][i], si, -zi);
-            tq = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f) + kMagic;
-          }
-          acc = (acc << 2) + __float_as_uint(tq);
-        }
-      cw[half] = acc - magic_pack_offset();
-    }
 
     // ---- destination of token tk
     const bool valid = slot >= 0 && slot < slots;
@@ -465,44 +439,88 @@ __global__ __launch_bounds__(64 * kQWavesF, 4) void quantize_fast_kernel(FastArg
         p = static_cast<int>(us - pg * up);
       }
     }
-    uint8_t *base = a.pages + (static_cast<size_t>(page) * a.H + h) * static_cast<size_t>(72 * a.P);
-
-    if (side == 0) {
-      if (valid) *reinterpret_cast<uint2 *>(base + 32 * p + 8 * g) = uint2{cw[0], cw[1]};
-    } else {
-      // 4 consecutive tokens of a tile form one interleaved 128-byte V group
-      // when their slots are 4 consecutive, 4-aligned positions: transpose
-      // the quad's code bytes (lane qi takes bytes 8g+2qi, 8g+2qi+1 of all
-      // 4 tokens) and write 8 bytes per lane; otherwise write bytes singly.
+    uint8_t *base0 = a.pages + (static_cast<size_t>(page) * a.H + h) * static_cast<size_t>(72 * a.P);
+    // values: 4 consecutive tokens of a tile form one interleaved 128-byte V
+    // group when their slots are 4 consecutive, 4-aligned positions; then the
+    // quad's code bytes are transposed (lane qi takes bytes 8g+2qi, 8g+2qi+1
+    // of all 4 tokens) and each lane writes 8 bytes; otherwise bytes singly
+    int ok = 0;
+    if (side != 0) {
       const int slot_lo = static_cast<int>(slot);
       const int s0 = __builtin_amdgcn_mov_dpp(slot_lo, 0x00, 0xF, 0xF, false);  // quad lane 0
-      int ok = (valid && slot_lo == s0 + qi && (s0 & 3) == 0) ? 1 : 0;
+      ok = (valid && slot_lo == s0 + qi && (s0 & 3) == 0) ? 1 : 0;
       ok &= qdpp_xor1(ok);
       ok &= qdpp_xor2(ok);
-      const bool odd = (qi & 1) != 0, up2 = (qi & 2) != 0;
-      const uint32_t L = cw[0], Hh = cw[1];
-      const uint32_t r1 = static_cast<uint32_t>(qdpp_xor2(static_cast<int>(up2 ? L : Hh)));
-      const uint32_t X0 = up2 ? r1 : L, X1 = up2 ? Hh : r1;
-      const uint32_t sel_send = odd ? 0x05040100u : 0x07060302u;
-      const uint32_t sel_keep = odd ? 0x07060302u : 0x05040100u;
-      const uint32_t send = __builtin_amdgcn_perm(X1, X0, sel_send);
-      const uint32_t keep = __builtin_amdgcn_perm(X1, X0, sel_keep);
-      const uint32_t r2 = static_cast<uint32_t>(qdpp_xor1(static_cast<int>(send)));
-      const uint32_t E = odd ? r2 : keep, O = odd ? keep : r2;
-      const uint32_t W0 = __builtin_amdgcn_perm(O, E, 0x06020400u);
-      const uint32_t W1 = __builtin_amdgcn_perm(O, E, 0x07030501u);
-      uint8_t *vg = base + 32 * a.P + 128 * (p >> 2);
-      if (ok) {
-        *reinterpret_cast<uint2 *>(vg + 32 * g + 8 * qi) = uint2{W0, W1};
-      } else if (valid) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-          vg[4 * (8 * g + m) + (p & 3)] = static_cast<uint8_t>(cw[m >> 2] >> (8 * (m & 3)));
-      }
     }
-    if (valid && g == 0) {
-      const uint32_t meta = f16_bits(sh) | (f16_bits(zh) << 16);
-      *reinterpret_cast<uint32_t *>(base + (side ? 68 : 64) * a.P + 4 * p) = meta;
+
+    const int nclip = kClips ? a.nclip : 1;
+    for (int ci = 0; ci < nclip; ++ci) {
+      const float clip = fs.clip[ci];
+      uint8_t *base = base0 + static_cast<size_t>(ci) * a.clip_stride;
+      float lo = clip * mn;
+      const float hi = clip * mx;
+      const float span = hi - lo;
+      float s32 = span / 3.0f;
+      asm volatile("" : "+v"(lo));
+      asm volatile("" : "+v"(s32));
+      const _Float16 sh = static_cast<_Float16>(s32);
+      const _Float16 zh = static_cast<_Float16>(lo);
+      const float s = static_cast<float>(sh);
+      const float z = static_cast<float>(zh);
+      const float inv = s != 0.0f ? 1.0f / s : 0.0f;  // s == 0: every code is 0
+      // rotated kinds: t = (u scale - z) inv computed as u (scale inv) - z inv
+      const float si = scale * inv, zi = z * inv;
+
+      // ---- codes, packed 16 per dword by shift-add of magic-biased values
+      uint32_t cw[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int nt = 3; nt >= 0; --nt)
+#pragma unroll
+          for (int i = 3; i >= 0; --i) {
+            float tq;
+            if constexpr (KIND == KVQ_ROT_IDENTITY) {
+              const float t = (y[4 * half + nt][i] - z) * inv;
+              tq = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f) + kMagic;
+            } else {
+              const float t = __builtin_fmaf(y[4 * half + nt][i], si, -zi);
+              tq = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f) + kMagic;
+            }
+            acc = (acc << 2) + __float_as_uint(tq);
+          }
+        cw[half] = acc - magic_pack_offset();
+      }
+
+      if (side == 0) {
+        if (valid) *reinterpret_cast<uint2 *>(base + 32 * p + 8 * g) = uint2{cw[0], cw[1]};
+      } else {
+        const bool odd = (qi & 1) != 0, up2 = (qi & 2) != 0;
+        const uint32_t L = cw[0], Hh = cw[1];
+        const uint32_t r1 = static_cast<uint32_t>(qdpp_xor2(static_cast<int>(up2 ? L : Hh)));
+        const uint32_t X0 = up2 ? r1 : L, X1 = up2 ? Hh : r1;
+        const uint32_t sel_send = odd ? 0x05040100u : 0x07060302u;
+        const uint32_t sel_keep = odd ? 0x07060302u : 0x05040100u;
+        const uint32_t send = __builtin_amdgcn_perm(X1, X0, sel_send);
+        const uint32_t keep = __builtin_amdgcn_perm(X1, X0, sel_keep);
+        const uint32_t r2 = static_cast<uint32_t>(qdpp_xor1(static_cast<int>(send)));
+        const uint32_t E = odd ? r2 : keep, O = odd ? keep : r2;
+        const uint32_t W0 = __builtin_amdgcn_perm(O, E, 0x06020400u);
+        const uint32_t W1 = __builtin_amdgcn_perm(O, E, 0x07030501u);
+        uint8_t *vg = base + 32 * a.P + 128 * (p >> 2);
+        if (ok) {
+          *reinterpret_cast<uint2 *>(vg + 32 * g + 8 * qi) = uint2{W0, W1};
+        } else if (valid) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            vg[4 * (8 * g + m) + (p & 3)] = static_cast<uint8_t>(cw[m >> 2] >> (8 * (m & 3)));
+        }
+      }
+      if (valid && g == 0) {
+        const uint32_t meta = f16_bits(sh) | (f16_bits(zh) << 16);
+        *reinterpret_cast<uint32_t *>(base + (side ? 68 : 64) * a.P + 4 * p) = meta;
+      }
     }
   };
 
@@ -526,7 +544,7 @@ __global__ __launch_bounds__(64 * kQWavesF, 4) void quantize_fast_kernel(FastArg
       load_tile(a.sd[sd].x, nxt, nx);
       float ya[8][4];
       rotate(xa[sd], kStaged > 1 ? sd : 0, sd == 0 && a.sd[sd].side == 0, ya);
-      finish_tile(ya, sa, a.sd[sd].clip, a.sd[sd].side);
+      finish_tile(ya, sa, a.sd[sd]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) xa[sd][ks] = nx[ks];
     }
@@ -536,12 +554,14 @@ __global__ __launch_bounds__(64 * kQWavesF, 4) void quantize_fast_kernel(FastArg
 
 template <int KIND, bool kCenter, int kSides, int kStaged>
 hipError_t launch_fast_kind(const FastArgs &a, bool wide, hipStream_t stream) {
+  if (a.nclip > 1 && wide) return hipErrorInvalidValue;  // (several clips: workspace caches, never that large)
   constexpr int kParts = KIND == KVQ_ROT_DENSE ? 3 : (KIND == KVQ_ROT_SIGNED_HADAMARD ? 1 : 0);
   const size_t lds = static_cast<size_t>(kStaged) * kParts * 2048 * sizeof(uint4);
   const int64_t n_tiles = (a.T + 15) / 16;
   const dim3 grid(static_cast<unsigned>((n_tiles + kQTiles - 1) / kQTiles * a.H));
-  auto kern = wide ? quantize_fast_kernel<KIND, kCenter, true, kSides, kStaged>
-                   : quantize_fast_kernel<KIND, kCenter, false, kSides, kStaged>;
+  auto kern = a.nclip > 1 ? quantize_fast_kernel<KIND, kCenter, false, kSides, kStaged, true>
+              : wide      ? quantize_fast_kernel<KIND, kCenter, true, kSides, kStaged, false>
+                          : quantize_fast_kernel<KIND, kCenter, false, kSides, kStaged, false>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -571,41 +591,65 @@ hipError_t launch_fast_sides(const FastArgs &a, int kind, bool wide, hipStream_t
 
 }  // namespace
 
-hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
-                           const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean, float clip_k,
-                           float clip_v, uint8_t *pages, int64_t num_pages, int page_size, hipStream_t stream) {
-  if (num_tokens == 0) return hipSuccess;
-  QuantArgs a{k, v, num_tokens, H, slot_mapping, rk, rv, key_mean, clip_k, clip_v, pages, num_pages, page_size,
-              1.0 / __builtin_sqrt(128.0)};
-  if (dtype == KVQ_BF16) {
-    const bool wide = num_pages * static_cast<int64_t>(page_size) > (static_cast<int64_t>(1) << 31);
-    int p_shift = -1;
-    for (int sh = 4; sh < 31; ++sh)
-      if (page_size == (1 << sh)) p_shift = sh;
-    const FastSide sk{static_cast<const uint16_t *>(k), rk.signs, rk.matrix, clip_k, 0};
-    const FastSide sv{static_cast<const uint16_t *>(v), rv.signs, rv.matrix, clip_v, 1};
+hipError_t launch_quantize_clips(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
+                                 const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean,
+                                 const float *clips_k, const float *clips_v, int nclip, uint8_t *pages,
+                                 int64_t num_pages, int page_size, size_t clip_stride, hipStream_t stream) {
+  if (num_tokens == 0 || nclip <= 0) return hipSuccess;
+  if (dtype != KVQ_BF16) {
+    // fp32 inputs: the exact kernel, one launch per clip ratio
+    const int64_t items = num_tokens * H;
+    int64_t blocks = (items + 3) / 4;
+    if (blocks > 16384) blocks = 16384;
+    for (int c = 0; c < nclip; ++c) {
+      QuantArgs a{k, v, num_tokens, H, slot_mapping, rk, rv, key_mean, clips_k[c], clips_v[c],
+                  pages + static_cast<size_t>(c) * clip_stride, num_pages, page_size, 1.0 / __builtin_sqrt(128.0)};
+      hipLaunchKernelGGL(quantize_exact_kernel<KVQ_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const bool wide = num_pages * static_cast<int64_t>(page_size) > (static_cast<int64_t>(1) << 31);
+  int p_shift = -1;
+  for (int sh = 4; sh < 31; ++sh)
+    if (page_size == (1 << sh)) p_shift = sh;
+  for (int c0 = 0; c0 < nclip; c0 += kMaxClips) {
+    const int n = nclip - c0 < kMaxClips ? nclip - c0 : kMaxClips;
+    FastSide sk{static_cast<const uint16_t *>(k), rk.signs, rk.matrix, {}, 0};
+    FastSide sv{static_cast<const uint16_t *>(v), rv.signs, rv.matrix, {}, 1};
+    for (int c = 0; c < n; ++c) {
+      sk.clip[c] = clips_k[c0 + c];
+      sv.clip[c] = clips_v[c0 + c];
+    }
+    uint8_t *pg = pages + static_cast<size_t>(c0) * clip_stride;
+    hipError_t e;
     // keys and values in one pass when both rotations fit in LDS together
     // (signed Hadamard / identity, or one dense matrix shared by both sides);
     // otherwise one launch per side
-    if (rk.kind == rv.kind) {
-      if (rk.kind != KVQ_ROT_DENSE)
-        return launch_fast_sides<2, 2>(FastArgs{{sk, sv}, num_tokens, H, slot_mapping, key_mean, pages, num_pages,
-                                                page_size, p_shift}, rk.kind, wide, stream);
-      if (rk.matrix == rv.matrix)
-        return launch_fast_sides<2, 1>(FastArgs{{sk, sv}, num_tokens, H, slot_mapping, key_mean, pages, num_pages,
-                                                page_size, p_shift}, rk.kind, wide, stream);
+    if (rk.kind == rv.kind && rk.kind != KVQ_ROT_DENSE) {
+      e = launch_fast_sides<2, 2>(FastArgs{{sk, sv}, num_tokens, H, slot_mapping, key_mean, pg, num_pages, page_size,
+                                           p_shift, n, clip_stride}, rk.kind, wide, stream);
+    } else if (rk.kind == rv.kind && rk.matrix == rv.matrix) {
+      e = launch_fast_sides<2, 1>(FastArgs{{sk, sv}, num_tokens, H, slot_mapping, key_mean, pg, num_pages, page_size,
+                                           p_shift, n, clip_stride}, rk.kind, wide, stream);
+    } else {
+      e = launch_fast_sides<1, 1>(FastArgs{{sk, sk}, num_tokens, H, slot_mapping, key_mean, pg, num_pages, page_size,
+                                           p_shift, n, clip_stride}, rk.kind, wide, stream);
+      if (e == hipSuccess)
+        e = launch_fast_sides<1, 1>(FastArgs{{sv, sv}, num_tokens, H, slot_mapping, nullptr, pg, num_pages,
+                                             page_size, p_shift, n, clip_stride}, rv.kind, wide, stream);
     }
-    hipError_t e = launch_fast_sides<1, 1>(FastArgs{{sk, sk}, num_tokens, H, slot_mapping, key_mean, pages,
-                                                    num_pages, page_size, p_shift}, rk.kind, wide, stream);
     if (e != hipSuccess) return e;
-    return launch_fast_sides<1, 1>(FastArgs{{sv, sv}, num_tokens, H, slot_mapping, nullptr, pages, num_pages,
-                                            page_size, p_shift}, rv.kind, wide, stream);
   }
-  const int64_t items = num_tokens * H;
-  int64_t blocks = (items + 3) / 4;
-  if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(quantize_exact_kernel<KVQ_F32>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return hipSuccess;
+}
+
+hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
+                           const int64_t *slot_mapping, RotDev rk, RotDev rv, const float *key_mean, float clip_k,
+                           float clip_v, uint8_t *pages, int64_t num_pages, int page_size, hipStream_t stream) {
+  return launch_quantize_clips(k, v, dtype, num_tokens, H, slot_mapping, rk, rv, key_mean, &clip_k, &clip_v, 1, pages,
+                               num_pages, page_size, 0, stream);
 }
 
 }  // namespace kvq
