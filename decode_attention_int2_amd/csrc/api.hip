@@ -44,10 +44,13 @@ int check_cache(const kvq_cache *c) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// K, V, q and W_O are read with 16-byte vector loads (null passes: checked elsewhere)
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 struct CandidateLayout {
   int64_t num_pages;
   DecodePlan plan;      // matrix-core decode of the quantized variants
-  DecodePlan ref_plan;  // full-precision reference readout (VALU kernel): more splits
+  DecodePlan ref_plan;  // full-precision reference readout (fp32 matrix cores): more splits
   size_t cache_bytes;
   size_t off_cache, off_dec, off_refdec, off_seqlen, off_ohat, off_oref, off_nmse, off_gram, off_den, total;
 };
@@ -56,8 +59,9 @@ CandidateLayout candidate_layout(int64_t T, int H, int Hq, int Nq, int C, int n_
   CandidateLayout L{};
   L.num_pages = (T + 15) / 16;
   L.plan = make_decode_plan(1, Nq, Hq, H, static_cast<int>(T), 0, 0);
-  // the reference kernel runs one workgroup per (split, KV head) for all rows: ~4096 workgroups
-  const int ref_splits = (4096 + H - 1) / H;
+  // the reference kernel runs one wave per (split, KV head, 16 rows): ~4096 waves
+  const int ref_waves = H * ((Nq * (Hq / H) + 15) / 16);
+  const int ref_splits = (4096 + ref_waves - 1) / ref_waves;
   L.ref_plan = make_decode_plan(1, Nq, Hq, H, static_cast<int>(T), 0, ref_splits);
   const int U = H;  // upper bound over both modes
   size_t off = 0;
@@ -112,6 +116,7 @@ int kvq_quantize(const void *k, const void *v, int32_t dtype, int64_t num_tokens
   if (rc) return rc;
   if (!valid_clip(clip_k) || !valid_clip(clip_v)) return KVQ_ERR_INVALID_ARGUMENT;
   if (num_tokens > 0 && (!k || !v)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(v)) return KVQ_ERR_INVALID_ARGUMENT;
   if (num_tokens == 0) return KVQ_OK;
   KVQ_TRY(launch_quantize(k, v, dtype, num_tokens, cache->num_kv_heads, slot_mapping, to_dev(*rot_k),
                           to_dev(*rot_v), key_mean, clip_k, clip_v, cache->pages, cache->num_pages, cache->page_size,
@@ -155,6 +160,7 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
     return KVQ_ERR_INVALID_ARGUMENT;
   if (w_o && (d_model < 1 || !out_y)) return KVQ_ERR_INVALID_ARGUMENT;
   if (num_seqs > 0 && (!q || !seq_lens || !out_o)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(w_o)) return KVQ_ERR_INVALID_ARGUMENT;
   const DecodePlan pl = make_decode_plan(num_seqs, queries_per_seq, num_q_heads, H, max_seq_len,
                                          w_o ? d_model : 0, num_splits);
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return KVQ_ERR_WORKSPACE;
@@ -215,12 +221,14 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
   if (mode != KVQ_SELECT_JOINT && mode != KVQ_SELECT_PER_HEAD) return KVQ_ERR_UNSUPPORTED;
   if (!k || !v || !q || !candidates || !clips || !w_o || !out_nmse || !out_best) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(w_o)) return KVQ_ERR_INVALID_ARGUMENT;
   if (num_tokens < 1 || num_tokens > INT32_MAX || num_kv_heads < 1 || num_q_heads < 1 || num_queries < 1 ||
       num_candidates < 1 || num_clips < 1 || d_model < 1)
     return KVQ_ERR_INVALID_ARGUMENT;
   if (num_q_heads % num_kv_heads) return KVQ_ERR_INVALID_ARGUMENT;
   const int H = num_kv_heads, Hq = num_q_heads, G = Hq / H, Nq = num_queries;
   if (static_cast<int64_t>(Nq) * G > kMaxRows) return KVQ_ERR_UNSUPPORTED;
+  if (mode == KVQ_SELECT_JOINT && Hq > 64) return KVQ_ERR_UNSUPPORTED;  // joint Gram block of Hq * 128 rows
   for (int r = 0; r < num_candidates; ++r) {
     const int rc = check_rotation(&candidates[r]);
     if (rc) return rc;

@@ -65,43 +65,89 @@ __global__ __launch_bounds__(256) void gram_kernel(const void *w_o, int d_model,
     for (int j = 0; j < 4; ++j) gb[static_cast<size_t>(64 * ta + ty + 16 * i) * bdim + 64 * tb + tx + 16 * j] = acc[i][j];
 }
 
-// One workgroup per (query q, unit u): e = sum over the unit's blocks of
-// x G x^T, x = x1 - x0 (x0 may be null).  kDen: store e as the unit's
-// reference norm den[u][q]; otherwise write the NMSE e / den[u][q].
-template <bool kDen>
+// One workgroup per (unit u, QW queries): e_q = sum over the unit's blocks
+// of x_q G x_q^T, x = x1 - x0 (x0 may be null).  Thread t owns row
+// r = t % 128 (+ 128 i) of a block for the QW / 2 queries of half t / 128:
+// t_q(r) = sum_c G[c][r] x_q[c] (G is symmetric bit for bit -- its two
+// triangles are the same products summed in the same order -- so the reads
+// of column r are coalesced and each G value serves QW / 2 queries), then
+// e_q = sum_r x_q[r] t_q(r).  kDen: store e as the unit's reference norm
+// den[u][q]; otherwise write the NMSE e / den[u][q].  x is staged in LDS as
+// [QW][bdim] fp32 (at most 64 KiB: QW is picked from bdim).
+template <bool kDen, int QW>
 __global__ __launch_bounds__(256) void quadform_kernel(const float *x1, const float *x0, const float *g, int Hq,
                                                        int blocks_per_unit, int bdim, double *den, float *nmse_q,
                                                        size_t stride_u, int Nq) {
-  extern __shared__ float xs[];  // [bdim]
-  __shared__ double red[4];
-  const int q = blockIdx.x, u = blockIdx.y;
-  double e = 0.0;
+  constexpr int kHalf = QW / 2;
+  extern __shared__ float xs[];  // [QW][bdim]
+  __shared__ double red[4][kHalf];
+  const int u = blockIdx.y, q0 = blockIdx.x * QW;
+  const int nq = min(QW, Nq - q0);
+  const int r0 = threadIdx.x & 127, qh = threadIdx.x >> 7;
+  double e[kHalf] = {};
   for (int bi = 0; bi < blocks_per_unit; ++bi) {
-    const int blk = u * blocks_per_unit + bi;  // block index = first query head of the block / (bdim / 128)
-    const size_t xoff = static_cast<size_t>(q) * Hq * D + static_cast<size_t>(blk) * bdim;
+    const int blk = u * blocks_per_unit + bi;
     __syncthreads();
-    for (int i = threadIdx.x; i < bdim; i += 256) xs[i] = x0 ? x1[xoff + i] - x0[xoff + i] : x1[xoff + i];
+    for (int idx = threadIdx.x; idx < QW * bdim; idx += 256) {
+      const int qq = idx / bdim, i = idx - qq * bdim;
+      float v = 0.0f;
+      if (qq < nq) {
+        const size_t xo = static_cast<size_t>(q0 + qq) * Hq * D + static_cast<size_t>(blk) * bdim + i;
+        v = x0 ? x1[xo] - x0[xo] : x1[xo];
+      }
+      xs[idx] = v;
+    }
     __syncthreads();
     const float *gb = g + static_cast<size_t>(blk) * bdim * bdim;
-    // (G is symmetric bit for bit -- its two triangles are the same products
-    // summed in the same order -- so thread r reads column r: coalesced)
-    for (int r = threadIdx.x; r < bdim; r += 256) {
-      float t = 0.0f;
-      for (int cc = 0; cc < bdim; ++cc) t += gb[static_cast<size_t>(cc) * bdim + r] * xs[cc];
-      e += static_cast<double>(xs[r]) * t;
+    const float *xq = xs + kHalf * qh * bdim;
+    for (int r = r0; r < bdim; r += 128) {
+      float t[kHalf] = {};
+      for (int cc = 0; cc < bdim; ++cc) {
+        const float gv = gb[static_cast<size_t>(cc) * bdim + r];
+#pragma unroll
+        for (int j = 0; j < kHalf; ++j) t[j] += gv * xq[j * bdim + cc];
+      }
+#pragma unroll
+      for (int j = 0; j < kHalf; ++j) e[j] += static_cast<double>(xq[j * bdim + r]) * t[j];
     }
   }
-  for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
+  // sum over the 128 threads of each half (two waves each)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) red[wave] = e;
+#pragma unroll
+  for (int j = 0; j < kHalf; ++j) {
+    double v = e[j];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wave][j] = v;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const double tot = red[0] + red[1] + red[2] + red[3];
+  if (threadIdx.x < nq) {
+    const int h2 = threadIdx.x / kHalf, j = threadIdx.x % kHalf;
+    const double tot = red[2 * h2][j] + red[2 * h2 + 1][j];
+    const int q = q0 + threadIdx.x;
     if constexpr (kDen)
       den[static_cast<size_t>(u) * Nq + q] = tot;
     else
       nmse_q[static_cast<size_t>(u) * stride_u + q] = static_cast<float>(tot / den[static_cast<size_t>(u) * Nq + q]);
   }
+}
+
+template <bool kDen>
+hipError_t launch_quadform(const float *x1, const float *x0, const float *g, int Hq, int pu, int bdim, int U,
+                           double *den, float *nmse_q, size_t stride_u, int Nq, hipStream_t stream) {
+  constexpr size_t kLds = 64 * 1024;
+  const size_t row = sizeof(float) * bdim;
+  if (16 * row <= kLds)
+    hipLaunchKernelGGL((quadform_kernel<kDen, 16>), dim3((Nq + 15) / 16, U), dim3(256), 16 * row, stream, x1, x0, g,
+                       Hq, pu, bdim, den, nmse_q, stride_u, Nq);
+  else if (4 * row <= kLds)
+    hipLaunchKernelGGL((quadform_kernel<kDen, 4>), dim3((Nq + 3) / 4, U), dim3(256), 4 * row, stream, x1, x0, g, Hq,
+                       pu, bdim, den, nmse_q, stride_u, Nq);
+  else if (2 * row <= kLds)
+    hipLaunchKernelGGL((quadform_kernel<kDen, 2>), dim3((Nq + 1) / 2, U), dim3(256), 2 * row, stream, x1, x0, g, Hq,
+                       pu, bdim, den, nmse_q, stride_u, Nq);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // Mean over queries and first argmin in (candidate, clip) order, per unit.
@@ -168,9 +214,7 @@ hipError_t launch_nmse_prepare(const float *o_ref, const void *w_o, int dtype, i
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
-  hipLaunchKernelGGL(quadform_kernel<true>, dim3(Nq, U), dim3(256), sizeof(float) * bdim, stream, o_ref, nullptr,
-                     gram, Hq, pu, bdim, den, nullptr, size_t{0}, Nq);
-  return hipGetLastError();
+  return launch_quadform<true>(o_ref, nullptr, gram, Hq, pu, bdim, U, den, nullptr, size_t{0}, Nq, stream);
 }
 
 hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const float *gram, const double *den, int Nq,
@@ -178,9 +222,8 @@ hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const float
   int bdim, nb, pu;
   nmse_blocks(Hq, H, mode, bdim, nb, pu);
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
-  hipLaunchKernelGGL(quadform_kernel<false>, dim3(Nq, U), dim3(256), sizeof(float) * bdim, stream, o_hat, o_ref,
-                     gram, Hq, pu, bdim, const_cast<double *>(den), nmse_q_out, stride_u, Nq);
-  return hipGetLastError();
+  return launch_quadform<false>(o_hat, o_ref, gram, Hq, pu, bdim, U, const_cast<double *>(den), nmse_q_out, stride_u,
+                                Nq, stream);
 }
 
 hipError_t launch_select(const float *nmse_q, int U, int C, int n_clip, int Nq, float *out_nmse, int32_t *out_best,

@@ -57,9 +57,6 @@ struct SplitArgs {
   const int32_t *page_table;
   int max_pages;
   const int32_t *seq_lens;
-  // raw K/V (reference readout)
-  const void *k, *v;
-  int64_t num_tokens;
   const float *qrot, *qsum;
   float *part;
 };
@@ -303,74 +300,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   write_partial<RB>(sm, a, b, h, s, acc, bad);
 }
 
-// Partial attention over raw K, V [num_tokens][H][128] (every row attends all
-// tokens): the full-precision reference readout of the candidate search.
-template <int RB, int DT>
-__global__ __launch_bounds__(256) void reference_split_kernel(SplitArgs a) {
-  extern __shared__ float sm[];
-  using S = Smem<RB>;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  init_split<RB>(sm, a, b, h);
-  const int L = static_cast<int>(a.num_tokens);
-  const int t_begin = s * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, L);
-  float acc[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) acc[r] = 0.0f;
-  __syncthreads();
-  for (int tok0 = t_begin; tok0 < t_end; tok0 += kChunk) {
-    const int tt = tok0 + tid;
-    const bool valid = tt < t_end;
-    sm[S::kVs + tid] = valid ? 1.0f : 0.0f;
-    sm[S::kVz + tid] = 0.0f;
-    float dot[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) dot[r] = 0.0f;
-    if (valid) {
-      const size_t base = (static_cast<size_t>(tt) * a.H + h) * D;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        float kf[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) kf[e] = load_elem<DT>(a.k, base + 16 * w + e);
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          if (r < a.R) {
-            const float *qv = sm + S::kQ + r * D + 16 * w;
-            float d = dot[r];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) d += qv[e] * kf[e];
-            dot[r] = d;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-      if (r < a.R) sm[S::kW + r * kChunk + tid] = valid ? dot[r] : -INFINITY;
-    __syncthreads();
-    softmax_chunk<RB>(sm, a.R);
-    __syncthreads();
-    {
-      const int i = tid & 127, half = tid >> 7;
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-        if (r < a.R) acc[r] *= sm[S::kAlpha + r];
-      const int t_lo = half * (kChunk / 2);
-      const int t_hi = min(t_lo + kChunk / 2, t_end - tok0);
-      for (int t = t_lo; t < t_hi; ++t) {
-        const float vv = load_elem<DT>(a.v, (static_cast<size_t>(tok0 + t) * a.H + h) * D + i);
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-          if (r < a.R) acc[r] += sm[S::kW + r * kChunk + t] * vv;
-      }
-    }
-    __syncthreads();
-  }
-  write_partial<RB>(sm, a, b, h, s, acc, false);
-}
-
 // ------------------------------------------------------------ combine
 // Merge split partials (base-2 log-sum-exp), apply R_V^T, write out_o (and,
 // for the W_O projection, a copy of o laid out [row group][K][16 rows]).
@@ -391,38 +320,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *part, int n_i
 
 
 template <int RB>
-hipError_t launch_split_rb(const DecodePlan &pl, const SplitArgs &a, bool reference, int dtype,
-                           hipStream_t stream) {
+hipError_t launch_split_rb(const DecodePlan &pl, const SplitArgs &a, hipStream_t stream) {
   const size_t smem = Smem<RB>::bytes();
-  dim3 grid(pl.splits, pl.H, reference ? 1 : pl.num_seqs);
+  dim3 grid(pl.splits, pl.H, pl.num_seqs);
   if (smem > 65536) {
     // above the default dynamic shared-memory limit: opt in (gfx950 has 160 KB of LDS per workgroup)
-    hipError_t e = hipSuccess;
-    if (!reference)
-      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_split_kernel<RB>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-    else if (dtype == KVQ_F32)
-      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&reference_split_kernel<RB, KVQ_F32>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-    else
-      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&reference_split_kernel<RB, KVQ_BF16>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_split_kernel<RB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
   }
-  if (!reference) {
-    hipLaunchKernelGGL(decode_split_kernel<RB>, grid, dim3(256), smem, stream, a);
-  } else if (dtype == KVQ_F32) {
-    hipLaunchKernelGGL((reference_split_kernel<RB, KVQ_F32>), grid, dim3(256), smem, stream, a);
-  } else {
-    hipLaunchKernelGGL((reference_split_kernel<RB, KVQ_BF16>), grid, dim3(256), smem, stream, a);
-  }
+  hipLaunchKernelGGL(decode_split_kernel<RB>, grid, dim3(256), smem, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_split(const DecodePlan &pl, const SplitArgs &a, bool reference, int dtype, hipStream_t stream) {
-  if (pl.rows_per_head <= 4) return launch_split_rb<4>(pl, a, reference, dtype, stream);
-  if (pl.rows_per_head <= 16) return launch_split_rb<16>(pl, a, reference, dtype, stream);
-  return launch_split_rb<64>(pl, a, reference, dtype, stream);
+hipError_t launch_split(const DecodePlan &pl, const SplitArgs &a, hipStream_t stream) {
+  if (pl.rows_per_head <= 4) return launch_split_rb<4>(pl, a, stream);
+  if (pl.rows_per_head <= 16) return launch_split_rb<16>(pl, a, stream);
+  return launch_split_rb<64>(pl, a, stream);
 }
 
 }  // namespace
@@ -524,27 +438,7 @@ hipError_t launch_decode_split(const DecodePlan &pl, const uint8_t *pages, int64
   a.qrot = qrot;
   a.qsum = qsum;
   a.part = part;
-  return launch_split(pl, a, false, KVQ_F32, stream);
-}
-
-hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
-                                  int64_t num_tokens, const float *qrot, float *part, hipStream_t stream) {
-  SplitArgs a{};
-  a.R = pl.rows_per_head;
-  a.G = pl.G;
-  a.Hq = pl.Hq;
-  a.H = pl.H;
-  a.Nq = pl.queries_per_seq;
-  a.split_tokens = pl.split_tokens;
-  a.splits = pl.splits;
-  a.max_seq_len = pl.max_seq_len;
-  a.k = k;
-  a.v = v;
-  a.num_tokens = num_tokens;
-  a.qrot = qrot;
-  a.qsum = qrot;  // unused by the reference kernel's logits, read into shared memory only
-  a.part = part;
-  return launch_split(pl, a, true, dtype, stream);
+  return launch_split(pl, a, stream);
 }
 
 hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, float *ot,

@@ -22,6 +22,9 @@
  *     slot outside the cache is skipped by kvq_quantize; a page index outside
  *     the cache, or seq_len < 0 or > max_seq_len, makes kvq_decode_attn write
  *     NaN to every output of the affected sequence.
+ *   - K, V, q and W_O start at 16-byte aligned addresses (every hipMalloc
+ *     or torch allocation does); the kernels read them with 16-byte vector
+ *     loads, so an unaligned one returns KVQ_ERR_INVALID_ARGUMENT.
  *   - Head dimension and quantization group size are both 128 ([OptR],
  *     Appendix Table A; [Eval]: group size 128, per-token-group K/V).
  */
@@ -207,7 +210,8 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
  *   clips         host array [num_clips], each in (0, 1].
  *   w_o           [Hq*128][d_model], dtype.
  *   workspace     at least kvq_candidate_workspace_bytes(...) bytes.
- * Limits: num_queries * Hq / H <= 64, else UNSUPPORTED.
+ * Limits: num_queries * Hq / H <= 64, and Hq <= 64 in JOINT mode, else
+ * UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 size_t kvq_candidate_workspace_bytes(int64_t num_tokens, int32_t num_kv_heads, int32_t num_q_heads,
                                      int32_t num_queries, int32_t num_candidates, int32_t num_clips,
