@@ -76,6 +76,12 @@ def test_quantize_validation(lib):
     c8 = _cache(P=8)
     assert lib.kvq_quantize(fake, fake, 0, 4, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
                             ctypes.byref(c8), None) == 1
+    # K or V not 16-byte aligned -> INVALID
+    odd = ctypes.c_void_p(0x2008)
+    assert lib.kvq_quantize(odd, fake, 0, 4, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c), None) == 1
+    assert lib.kvq_quantize(fake, odd, 1, 4, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c), None) == 1
     # nothing to do: zero tokens succeeds without touching the device
     assert lib.kvq_quantize(None, None, 0, 0, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
                             ctypes.byref(c), None) == 0
@@ -96,6 +102,8 @@ def test_decode_validation(lib):
     assert call(pt=None, num_seqs=2) == 1       # contiguous table needs num_seqs * max_pages <= num_pages
     assert call(wo=fake, dm=16, y=None) == 1    # W_O without out_y
     assert call(ws=None) == 3 and call(wsb=8) == 3
+    assert call(q=ctypes.c_void_p(0x2004)) == 1                       # q not 16-byte aligned
+    assert call(wo=ctypes.c_void_p(0x2002), dm=16, y=fake) == 1       # W_O not 16-byte aligned
     assert call(num_seqs=0) == 0
 
 
@@ -115,3 +123,10 @@ def test_candidate_validation(lib):
     bad_clips = (ctypes.c_float * 2)(1.0, 0.0)
     assert call(cands=one, nc=1, clips=bad_clips) == 1
     assert lib.kvq_candidate_workspace_bytes(100, 2, 2, 4, 1, 2, 16) > 0
+    # checks that come before any launch, with otherwise valid arguments
+    good = (ctypes.c_float * 2)(1.0, 0.9)
+    call2 = lambda k=fake, v=fake, q=fake, wo=fake, H=2, Hq=2, nq=4, mode=0: lib.kvq_candidate_nmse(
+        k, v, q, 1, 100, H, Hq, nq, one, 1, good, 2, None, wo, 16, mode, fake, None, fake, fake, 1 << 30, None)
+    for bad in ("k", "v", "q", "wo"):
+        assert call2(**{bad: ctypes.c_void_p(0x2008)}) == 1          # not 16-byte aligned
+    assert call2(H=2, Hq=128, nq=1, mode=0) == 2                      # JOINT with more than 64 query heads
