@@ -74,8 +74,8 @@ CandidateLayout candidate_layout(int64_t T, int H, int Hq, int Nq, int C, int n_
   off = align256(off + L.ref_plan.total);
   L.off_seqlen = off;
   off = align256(off + sizeof(int32_t));
-  L.off_ohat = off;
-  off = align256(off + static_cast<size_t>(Nq) * Hq * D * sizeof(float));
+  L.off_ohat = off;  // decoded outputs of every variant [C * n_clip][Nq][Hq][128]
+  off = align256(off + static_cast<size_t>(C) * n_clip * Nq * Hq * D * sizeof(float));
   L.off_oref = off;
   off = align256(off + static_cast<size_t>(Nq) * Hq * D * sizeof(float));
   L.off_nmse = off;
@@ -228,6 +228,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   if (num_q_heads % num_kv_heads) return KVQ_ERR_INVALID_ARGUMENT;
   const int H = num_kv_heads, Hq = num_q_heads, G = Hq / H, Nq = num_queries;
   if (static_cast<int64_t>(Nq) * G > kMaxRows) return KVQ_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_candidates) * num_clips > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
   if (mode == KVQ_SELECT_JOINT && Hq > 64) return KVQ_ERR_UNSUPPORTED;  // joint Gram block of Hq * 128 rows
   for (int r = 0; r < num_candidates; ++r) {
     const int rc = check_rotation(&candidates[r]);
@@ -242,7 +243,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   uint8_t *pages = ws + L.off_cache;
   uint8_t *dec = ws + L.off_dec;
   int32_t *seq_len = reinterpret_cast<int32_t *>(ws + L.off_seqlen);
-  float *o_hat = reinterpret_cast<float *>(ws + L.off_ohat);
+  float *o_hat_all = reinterpret_cast<float *>(ws + L.off_ohat);
   float *o_ref = reinterpret_cast<float *>(ws + L.off_oref);
   float *nmse_q = out_nmse_per_query ? out_nmse_per_query : reinterpret_cast<float *>(ws + L.off_nmse);
   const DecodePlan &pl = L.plan;
@@ -285,6 +286,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
                                   pages, L.num_pages, 16, L.cache_bytes, stream));
     for (int i = 0; i < num_clips; ++i) {
       uint8_t *pages_i = pages + static_cast<size_t>(i) * L.cache_bytes;
+      float *o_hat = o_hat_all + (static_cast<size_t>(r) * num_clips + i) * Nq * Hq * D;
       if (mfma) {
         KVQ_TRY(launch_decode_mfma(pl, qk, dtype, rq, rot, pages_i, L.num_pages, 16, nullptr,
                                    static_cast<int>(L.num_pages), seq_len, part, counters, o_hat, nullptr, stream));
@@ -293,10 +295,11 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
                                     qrot, qsum, part, stream));
         KVQ_TRY(launch_combine(pl, part, rot, o_hat, nullptr, stream));
       }
-      KVQ_TRY(launch_nmse_terms(o_hat, o_ref, gram, den, Nq, Hq, H, mode,
-                                nmse_q + (static_cast<size_t>(r) * num_clips + i) * Nq, stride_u, stream));
     }
   }
+  // post-W_O NMSE of every variant in one launch
+  KVQ_TRY(launch_nmse_terms(o_hat_all, o_ref, gram, den, Nq, Hq, H, mode, num_candidates * num_clips, nmse_q, stride_u,
+                            stream));
   KVQ_TRY(launch_select(nmse_q, U, num_candidates, num_clips, Nq, out_nmse, out_best, stream));
   return KVQ_OK;
 }

@@ -75,15 +75,19 @@ __global__ __launch_bounds__(256) void gram_kernel(const void *w_o, int d_model,
 // den[u][q]; otherwise write the NMSE e / den[u][q].  x is staged in LDS as
 // [QW][bdim] fp32 (at most 64 KiB: QW is picked from bdim).
 template <bool kDen, int QW>
-__global__ __launch_bounds__(256) void quadform_kernel(const float *x1, const float *x0, const float *g, int Hq,
-                                                       int blocks_per_unit, int bdim, double *den, float *nmse_q,
-                                                       size_t stride_u, int Nq) {
+__global__ __launch_bounds__(256) void quadform_kernel(const float *x1_all, const float *x0, const float *g, int Hq,
+                                                       int blocks_per_unit, int bdim, double *den, float *nmse_q_all,
+                                                       size_t stride_u, int Nq, int nvar) {
   constexpr int kHalf = QW / 2;
   extern __shared__ float xs[];  // [QW][bdim]
   __shared__ double red[4][kHalf];
   const int u = blockIdx.y, q0 = blockIdx.x * QW;
   const int nq = min(QW, Nq - q0);
   const int r0 = threadIdx.x & 127, qh = threadIdx.x >> 7;
+  const size_t x_stride = static_cast<size_t>(Nq) * Hq * D;
+  for (int var = blockIdx.z; var < nvar; var += gridDim.z) {
+  const float *x1 = x1_all + var * x_stride;
+  float *nmse_q = kDen ? nullptr : nmse_q_all + static_cast<size_t>(var) * Nq;
   double e[kHalf] = {};
   for (int bi = 0; bi < blocks_per_unit; ++bi) {
     const int blk = u * blocks_per_unit + bi;
@@ -102,6 +106,7 @@ __global__ __launch_bounds__(256) void quadform_kernel(const float *x1, const fl
     const float *xq = xs + kHalf * qh * bdim;
     for (int r = r0; r < bdim; r += 128) {
       float t[kHalf] = {};
+#pragma unroll 8
       for (int cc = 0; cc < bdim; ++cc) {
         const float gv = gb[static_cast<size_t>(cc) * bdim + r];
 #pragma unroll
@@ -129,22 +134,25 @@ __global__ __launch_bounds__(256) void quadform_kernel(const float *x1, const fl
     else
       nmse_q[static_cast<size_t>(u) * stride_u + q] = static_cast<float>(tot / den[static_cast<size_t>(u) * Nq + q]);
   }
+  }
 }
 
+// x1 holds nvar variants [nvar][Nq][Hq][128]; variant v writes nmse_q + v * Nq.
 template <bool kDen>
 hipError_t launch_quadform(const float *x1, const float *x0, const float *g, int Hq, int pu, int bdim, int U,
-                           double *den, float *nmse_q, size_t stride_u, int Nq, hipStream_t stream) {
+                           double *den, float *nmse_q, size_t stride_u, int Nq, int nvar, hipStream_t stream) {
   constexpr size_t kLds = 64 * 1024;
   const size_t row = sizeof(float) * bdim;
+  const unsigned gz = static_cast<unsigned>(nvar < 65535 ? nvar : 65535);
   if (16 * row <= kLds)
-    hipLaunchKernelGGL((quadform_kernel<kDen, 16>), dim3((Nq + 15) / 16, U), dim3(256), 16 * row, stream, x1, x0, g,
-                       Hq, pu, bdim, den, nmse_q, stride_u, Nq);
+    hipLaunchKernelGGL((quadform_kernel<kDen, 16>), dim3((Nq + 15) / 16, U, gz), dim3(256), 16 * row, stream, x1, x0,
+                       g, Hq, pu, bdim, den, nmse_q, stride_u, Nq, nvar);
   else if (4 * row <= kLds)
-    hipLaunchKernelGGL((quadform_kernel<kDen, 4>), dim3((Nq + 3) / 4, U), dim3(256), 4 * row, stream, x1, x0, g, Hq,
-                       pu, bdim, den, nmse_q, stride_u, Nq);
+    hipLaunchKernelGGL((quadform_kernel<kDen, 4>), dim3((Nq + 3) / 4, U, gz), dim3(256), 4 * row, stream, x1, x0, g,
+                       Hq, pu, bdim, den, nmse_q, stride_u, Nq, nvar);
   else if (2 * row <= kLds)
-    hipLaunchKernelGGL((quadform_kernel<kDen, 2>), dim3((Nq + 1) / 2, U), dim3(256), 2 * row, stream, x1, x0, g, Hq,
-                       pu, bdim, den, nmse_q, stride_u, Nq);
+    hipLaunchKernelGGL((quadform_kernel<kDen, 2>), dim3((Nq + 1) / 2, U, gz), dim3(256), 2 * row, stream, x1, x0, g,
+                       Hq, pu, bdim, den, nmse_q, stride_u, Nq, nvar);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -214,16 +222,17 @@ hipError_t launch_nmse_prepare(const float *o_ref, const void *w_o, int dtype, i
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
-  return launch_quadform<true>(o_ref, nullptr, gram, Hq, pu, bdim, U, den, nullptr, size_t{0}, Nq, stream);
+  return launch_quadform<true>(o_ref, nullptr, gram, Hq, pu, bdim, U, den, nullptr, size_t{0}, Nq, 1, stream);
 }
 
 hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const float *gram, const double *den, int Nq,
-                             int Hq, int H, int mode, float *nmse_q_out, size_t stride_u, hipStream_t stream) {
+                             int Hq, int H, int mode, int nvar, float *nmse_q_out, size_t stride_u,
+                             hipStream_t stream) {
   int bdim, nb, pu;
   nmse_blocks(Hq, H, mode, bdim, nb, pu);
   const int U = (mode == KVQ_SELECT_JOINT) ? 1 : H;
   return launch_quadform<false>(o_hat, o_ref, gram, Hq, pu, bdim, U, const_cast<double *>(den), nmse_q_out, stride_u,
-                                Nq, stream);
+                                Nq, nvar, stream);
 }
 
 hipError_t launch_select(const float *nmse_q, int U, int C, int n_clip, int Nq, float *out_nmse, int32_t *out_best,

@@ -319,7 +319,8 @@ size_t nmse_gram_floats(int Hq, int H, int mode);
 hipError_t launch_nmse_prepare(const float *o_ref, const void *w_o, int dtype, int Nq, int Hq, int H, int d_model,
                                int mode, float *gram, double *den, hipStream_t stream);
 hipError_t launch_nmse_terms(const float *o_hat, const float *o_ref, const float *gram, const double *den, int Nq,
-                             int Hq, int H, int mode, float *nmse_q_out, size_t stride_u, hipStream_t stream);
+                             int Hq, int H, int mode, int nvar, float *nmse_q_out, size_t stride_u,
+                             hipStream_t stream);
 hipError_t launch_select(const float *nmse_q, int U, int C, int n_clip, int Nq, float *out_nmse, int32_t *out_best,
                          hipStream_t stream);
 
