@@ -52,6 +52,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-search measurement")
+    ap.add_argument("--calibration-only", action="store_true",
+                    help="only time the calibration search (calib64k) and print its figures")
     ap.add_argument("--num-splits", type=int, default=0, help="split-K parts per sequence (0 = library default)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
@@ -115,6 +117,32 @@ def cpu_baseline(w_cpu) -> dict:
             "quantize_mtok_s": S * T / (t1 - t0) / 1e6}
 
 
+def calibration_search(dev, timed):
+    """Time one kvq_candidate_nmse call on calib64k (65,536 tokens x 8 KV
+    heads, 9 dense candidates x 5 clips, 64 queries, per-head selection)."""
+    import torch
+    import synthetic
+    from decode_attention_int2_amd import kvq
+    wc = synthetic.make("calib64k", dev)
+    C, n = len(wc.candidates), len(wc.clips)
+    T5, H5, Nq5, Hq5 = wc.tokens, wc.H, wc.q.shape[0], wc.Hq
+    out5 = torch.empty((H5, C, n), dtype=torch.float32, device=dev)
+    best5 = torch.empty((H5,), dtype=torch.int32, device=dev)
+    ws5 = torch.empty(kvq.kvq_candidate_workspace_bytes(T5, H5, Hq5, Nq5, C, n, wc.d_model), dtype=torch.uint8,
+                      device=dev)
+    rots5 = [kvq.Rotation(cd.kind, signs=cd.signs, matrix=cd.matrix) for cd in wc.candidates]
+    search = lambda i: kvq.kvq_candidate_nmse(wc.k, wc.v, wc.q, rots5, list(wc.clips), wc.w_o,
+                                              kvq.KVQ_SELECT_PER_HEAD, out5, best5, workspace=ws5)
+    cal_ms = timed(search, 3)
+    # work of one search: attention of every variant (QK^T and PV) and the rotations
+    att_flop = C * n * Nq5 * Hq5 * T5 * 128 * 2 * 2
+    rot_flop = C * T5 * H5 * 2 * 128 * 128 * 2
+    return {"workload": "calib64k", "description": synthetic.DESCRIPTIONS["calib64k"], "ms": round(cal_ms, 3),
+            "variants": C * n, "attention_gflop": round(att_flop / 1e9, 1), "rotation_gflop": round(rot_flop / 1e9, 1),
+            "tflop_s": round((att_flop + rot_flop) / (cal_ms * 1e-3) / 1e12, 2),
+            "best": [int(x) for x in best5.cpu().tolist()]}
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -136,31 +164,7 @@ def main():
         print(json.dumps({"copy_bytes_read_per_launch": 1 << 30, "copy_bytes_written_per_launch": 1 << 30}))
         return
     kvq.load_library()
-    w = synthetic.make(WORKLOAD, dev)
-    B, T, H, Hq, dm, P = w.num_seqs, w.tokens, w.H, w.Hq, w.d_model, w.page_size
-    rot = kvq.Rotation(w.rot_k.kind, signs=w.rot_k.signs)
-    NC = 3
-    caches = [kvq.Cache(w.num_pages, P, H, device=dev) for _ in range(NC)]
-    max_pages = w.page_table.shape[1]
-    rows = B * w.queries_per_seq
-    out_o = torch.empty((rows, Hq, 128), dtype=torch.float32, device=dev)
-    out_y = torch.empty((rows, dm), dtype=torch.float32, device=dev)
-    ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, 1, Hq, H, T, dm, a.num_splits), dtype=torch.uint8,
-                     device=dev)
     stream = torch.cuda.current_stream()
-
-    def quantize(i):
-        kvq.kvq_quantize(w.k, w.v, caches[i % NC], rot, rot, clip_k=w.clip_k, clip_v=w.clip_v,
-                         slot_mapping=w.slot_mapping)
-
-    def decode(i, with_wo=True):
-        kvq.kvq_decode_attn(w.q, B, 1, caches[i % NC], w.page_table, max_pages, w.seq_lens, T, rot, rot, out_o,
-                            w_o=w.w_o if with_wo else None, out_y=out_y if with_wo else None, workspace=ws,
-                            num_splits=a.num_splits)
-
-    def step(i):
-        quantize(i)
-        decode(i + 1)
 
     def timed(fn, n):
         """Average GPU time (ms) of n back-to-back calls fn(i), one event pair
@@ -178,6 +182,34 @@ def main():
         torch.cuda.synchronize()
         timed.wall_s = time.perf_counter() - w0
         return e0.elapsed_time(e1) / n
+
+    if a.calibration_only:
+        print(json.dumps({"calibration_search": calibration_search(dev, timed)}))
+        return
+    w = synthetic.make(WORKLOAD, dev)
+    B, T, H, Hq, dm, P = w.num_seqs, w.tokens, w.H, w.Hq, w.d_model, w.page_size
+    rot = kvq.Rotation(w.rot_k.kind, signs=w.rot_k.signs)
+    NC = 3
+    caches = [kvq.Cache(w.num_pages, P, H, device=dev) for _ in range(NC)]
+    max_pages = w.page_table.shape[1]
+    rows = B * w.queries_per_seq
+    out_o = torch.empty((rows, Hq, 128), dtype=torch.float32, device=dev)
+    out_y = torch.empty((rows, dm), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, 1, Hq, H, T, dm, a.num_splits), dtype=torch.uint8,
+                     device=dev)
+
+    def quantize(i):
+        kvq.kvq_quantize(w.k, w.v, caches[i % NC], rot, rot, clip_k=w.clip_k, clip_v=w.clip_v,
+                         slot_mapping=w.slot_mapping)
+
+    def decode(i, with_wo=True):
+        kvq.kvq_decode_attn(w.q, B, 1, caches[i % NC], w.page_table, max_pages, w.seq_lens, T, rot, rot, out_o,
+                            w_o=w.w_o if with_wo else None, out_y=out_y if with_wo else None, workspace=ws,
+                            num_splits=a.num_splits)
+
+    def step(i):
+        quantize(i)
+        decode(i + 1)
 
     for i in range(NC):                     # every cache buffer holds a valid cache before warmup
         quantize(i)
@@ -199,30 +231,12 @@ def main():
 
     traffic = measured_traffic(a.traffic_json)
 
-    # calibration search (a separate workload of the same path): 65,536 tokens x 8
-    # KV heads, 9 dense candidates x 5 clips, 64 queries, per-head selection
+    # calibration search (a separate workload of the same path)
     cal = None
     if not a.no_calibration:
         del caches, ws
         torch.cuda.empty_cache()
-        wc = synthetic.make("calib64k", dev)
-        C, n = len(wc.candidates), len(wc.clips)
-        T5, H5, Nq5, Hq5 = wc.tokens, wc.H, wc.q.shape[0], wc.Hq
-        out5 = torch.empty((H5, C, n), dtype=torch.float32, device=dev)
-        best5 = torch.empty((H5,), dtype=torch.int32, device=dev)
-        ws5 = torch.empty(kvq.kvq_candidate_workspace_bytes(T5, H5, Hq5, Nq5, C, n, wc.d_model), dtype=torch.uint8,
-                          device=dev)
-        rots5 = [kvq.Rotation(cd.kind, signs=cd.signs, matrix=cd.matrix) for cd in wc.candidates]
-        search = lambda i: kvq.kvq_candidate_nmse(wc.k, wc.v, wc.q, rots5, list(wc.clips), wc.w_o,
-                                                  kvq.KVQ_SELECT_PER_HEAD, out5, best5, workspace=ws5)
-        cal_ms = timed(search, 3)
-        # work of one search: attention of every variant (QK^T and PV) and the rotations
-        att_flop = C * n * Nq5 * Hq5 * T5 * 128 * 2 * 2
-        rot_flop = C * T5 * H5 * 2 * 128 * 128 * 2
-        cal = {"workload": "calib64k", "description": synthetic.DESCRIPTIONS["calib64k"], "ms": round(cal_ms, 3),
-               "variants": C * n, "attention_gflop": round(att_flop / 1e9, 1), "rotation_gflop": round(rot_flop / 1e9, 1),
-               "tflop_s": round((att_flop + rot_flop) / (cal_ms * 1e-3) / 1e12, 2),
-               "best": [int(x) for x in best5.cpu().tolist()]}
+        cal = calibration_search(dev, timed)
 
     base = None
     if not a.no_cpu_baseline:
