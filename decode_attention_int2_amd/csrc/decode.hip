@@ -354,14 +354,19 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   const int max_chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
   int splits = num_splits;
   if (splits <= 0) {
-    // ~one workgroup (8 waves) of the matrix-core kernel per CU, all resident
-    // at once: two workgroups sharing a CU run at unequal speed (the older
-    // one's waves win the issue arbitration), so the younger one's tail runs
-    // at half occupancy; splits of at least 1024 tokens keep the per-split
-    // prologue and merge small.  A workgroup takes one group of 4 query rows.
+    // at most one workgroup (8 waves) of the matrix-core kernel per CU, all
+    // resident at once: two workgroups sharing a CU run at unequal speed (the
+    // older one's waves win the issue arbitration), so the younger one's tail
+    // runs at half occupancy, and workgroups past the 256th run as a second
+    // round.  Each split pays a fixed start-up round trip and adds 8 partials
+    // to the merge (one pass for up to 64): at most 8 splits unless a split
+    // would exceed 16K tokens; splits of at least 1024 tokens.  A workgroup
+    // takes one group of 4 query rows.
     const int n_rg = (queries_per_seq * (Hq / H) + 3) / 4;
     const int units = num_seqs * H * n_rg > 0 ? num_seqs * H * n_rg : 1;
-    splits = (256 + units - 1) / units;
+    splits = 256 / units;
+    const int by_len = (max_seq_len + 16383) / 16384;
+    if (splits > (by_len > 8 ? by_len : 8)) splits = by_len > 8 ? by_len : 8;
     const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens
     if (splits > max_by_len) splits = max_by_len;
   }

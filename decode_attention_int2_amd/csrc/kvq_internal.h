@@ -12,10 +12,10 @@ namespace kvq {
 constexpr int D = 128;         // head dimension == quantization group size
 constexpr int kMaxRows = 64;   // query rows sharing one (sequence, KV head)
 constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
-constexpr int kMaxMfmaSplitTokens = 16384;  // tokens per split (page ids of a split fit in LDS)
+constexpr int kMaxMfmaSplitTokens = 1 << 20;  // tokens per split (keeps split offsets far from int32 overflow)
 constexpr int kMaxSplits = 4096;            // split partials merged per (row, head)
 constexpr int kMfmaWaves = 8;               // waves per workgroup of the matrix-core decode kernel
-constexpr int64_t kMaxSeqLen = static_cast<int64_t>(kMaxSplits) * kMaxMfmaSplitTokens;
+constexpr int64_t kMaxSeqLen = static_cast<int64_t>(1) << 26;  // max_seq_len accepted by the decode entry point
 
 // Rotation descriptor passed by value to kernels.
 struct RotDev {
