@@ -358,15 +358,14 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
     // resident at once: two workgroups sharing a CU run at unequal speed (the
     // older one's waves win the issue arbitration), so the younger one's tail
     // runs at half occupancy, and workgroups past the 256th run as a second
-    // round.  Each split pays a fixed start-up round trip and adds 8 partials
-    // to the merge (one pass for up to 64): at most 8 splits unless a split
-    // would exceed 16K tokens; splits of at least 1024 tokens.  A workgroup
-    // takes one group of 4 query rows.
+    // round.  At most 64 splits (the last split merges up to 64 partials in
+    // one pass; past 8 splits each workgroup merges its waves' partials
+    // first); splits of at least 1024 tokens.  A workgroup takes one group of
+    // 4 query rows.
     const int n_rg = (queries_per_seq * (Hq / H) + 3) / 4;
     const int units = num_seqs * H * n_rg > 0 ? num_seqs * H * n_rg : 1;
     splits = 256 / units;
-    const int by_len = (max_seq_len + 16383) / 16384;
-    if (splits > (by_len > 8 ? by_len : 8)) splits = by_len > 8 ? by_len : 8;
+    if (splits > 64) splits = 64;
     const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens
     if (splits > max_by_len) splits = max_by_len;
   }
@@ -401,8 +400,8 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   pl.off_wocnt = off;  // [row groups][column blocks] uint64 arrival counters of the W_O slices
   off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * col_blocks * sizeof(uint64_t) : 0));
   const size_t n_rg_all = static_cast<size_t>(num_seqs) * H * ((queries_per_seq * (Hq / H) + 3) / 4);
-  pl.off_cnt = off;  // [num_seqs][H][row groups] uint64
-  off = align(off + n_rg_all * sizeof(uint64_t));
+  pl.off_cnt = off;  // [num_seqs][H][row groups][kArrivalWords] uint64
+  off = align(off + n_rg_all * kArrivalWords * sizeof(uint64_t));
   pl.total = off;
   return pl;
 }

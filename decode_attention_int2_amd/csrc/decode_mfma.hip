@@ -127,9 +127,10 @@ struct MfmaArgs {
   const int32_t *seq_lens;
   const void *q;              // query rows (dtype of the launch), or rotated fp32 rows
   RotDev rk, rv;
-  float *part;                // [rows][Hq][parts][132] partials, one per (split, wave)
-  int parts;                  // splits * 4
-  unsigned long long *counters;  // [num_seqs][H][n_rg] arrival counters
+  float *part;                // [rows][Hq][parts][132] partials, one per (split, wave) or per split
+  int parts;                  // splits * 8, or splits when the waves' partials are merged first (premerge)
+  int premerge;
+  unsigned long long *counters;  // [num_seqs][H][n_rg][kArrivalWords] arrival counters
   uint32_t epoch;
   float *out_o, *ot;
 };
@@ -474,6 +475,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   c.g = lane >> 4;
   float *facc = &facc_all[wave][lane];
 
+  // (the arrival counter's validation word, read now: its round trip is
+  // hidden behind the kernel's first loads)
+  unsigned long long *cnt = a.counters + unit * kArrivalWords;
+  bool cnt_valid = false;
+  if (threadIdx.x == 0)
+    cnt_valid = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == arrival_valid_value(cnt);
   int L = a.seq_lens[b];
   bool bad = L < 0 || L > a.max_seq_len;
   if (bad) L = 0;
@@ -667,29 +674,66 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // order, the fence keeps the compiler from reordering them)
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  // partial slot of this wave: split s, wave w -> s * kWaves + w; stored with
-  // device-scope stores, consecutive lanes on consecutive floats
-  {
-    const int slot_w = s * kWaves + wave;
-    float *rb[4];  // partial base of each row of the group
+  if (a.premerge) {
+    // many splits: the 8 waves' partials of each row are merged here first
+    // (one partial per split and row), so that the last split merges one
+    // per split
+    __syncthreads();
+    if (wave < nrows) {
+      const int r = wave;
+      float mw[kWaves], mstar = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rr = min(row0 + r, a.R - 1);
+      for (int w = 0; w < kWaves; ++w) {
+        mw[w] = red[w][r][0];
+        mstar = fmaxf(mstar, mw[w]);
+      }
+      float l = 0.0f, z = 0.0f, a0 = 0.0f, a1 = 0.0f;
+      bool nan = false;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float lw = red[w][r][1];
+        nan = nan || lw != lw;
+        const float al = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mstar);
+        if (al != 0.0f) {
+          l += al * lw;
+          z += al * red[w][r][2];
+          a0 += al * red[w][r][4 + lane];
+          a1 += al * red[w][r][4 + 64 + lane];
+        }
+      }
+      const int rr = row0 + r;
       const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
-      rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.parts + slot_w) * (D + 4);
+      float *dst = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.parts + s) * (D + 4);
+      store_partial(dst + 4 + lane, a0);
+      store_partial(dst + 4 + 64 + lane, a1);
+      if (lane < 4) store_partial(dst + lane, lane == 0 ? mstar : lane == 1 ? (nan ? __builtin_nanf("") : l)
+                                                              : lane == 2 ? z : 0.0f);
     }
-    constexpr int kN = (4 * (D + 4) + 63) / 64;
-    float vals[kN];
+  } else {
+    // partial slot of this wave: split s, wave w -> s * kWaves + w; stored with
+    // device-scope stores, consecutive lanes on consecutive floats
+    {
+      const int slot_w = s * kWaves + wave;
+      float *rb[4];  // partial base of each row of the group
 #pragma unroll
-    for (int k = 0; k < kN; ++k) vals[k] = rw[min(lane + 64 * k, 4 * (D + 4) - 1)];  // all reads, then the stores
+      for (int r = 0; r < 4; ++r) {
+        const int rr = min(row0 + r, a.R - 1);
+        const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
+        rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.parts + slot_w) * (D + 4);
+      }
+      constexpr int kN = (4 * (D + 4) + 63) / 64;
+      float vals[kN];
 #pragma unroll
-    for (int k = 0; k < kN; ++k) {
-      const int idx = lane + 64 * k;
-      // rows covered by idx in [64k, 64k + 63]: (64k) / 132 and (64k + 63) / 132
-      constexpr int kRowStride = D + 4;
-      const int r_lo = (64 * k) / kRowStride, r_hi = (64 * k + 63) / kRowStride;
-      const int r = idx >= (r_lo + 1) * kRowStride ? r_hi : r_lo;
-      if (idx < nrows * kRowStride) store_partial(rb[r] + (idx - r * kRowStride), vals[k]);
+      for (int k = 0; k < kN; ++k) vals[k] = rw[min(lane + 64 * k, 4 * (D + 4) - 1)];  // all reads, then the stores
+#pragma unroll
+      for (int k = 0; k < kN; ++k) {
+        const int idx = lane + 64 * k;
+        // rows covered by idx in [64k, 64k + 63]: (64k) / 132 and (64k + 63) / 132
+        constexpr int kRowStride = D + 4;
+        const int r_lo = (64 * k) / kRowStride, r_hi = (64 * k + 63) / kRowStride;
+        const int r = idx >= (r_lo + 1) * kRowStride ? r_hi : r_lo;
+        if (idx < nrows * kRowStride) store_partial(rb[r] + (idx - r * kRowStride), vals[k]);
+      }
     }
   }
 
@@ -701,7 +745,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // write-back or invalidation is needed for that.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) s_last = arrive_last(a.counters + unit, a.epoch, a.splits) ? 1u : 0u;
+  if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_valid, a.epoch, a.splits) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
   if (wave < nrows) {
@@ -737,7 +781,8 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.n_rg = (pl.rows_per_head + 3) / 4;
   a.split_tokens = pl.split_tokens;
   a.splits = pl.splits;
-  a.parts = pl.splits * kWaves;
+  a.premerge = pl.splits > kMaxSplitsNoPremerge ? 1 : 0;
+  a.parts = a.premerge ? pl.splits : pl.splits * kWaves;
   a.max_seq_len = pl.max_seq_len;
   a.P = page_size;
   a.p_shift = __builtin_ctz(static_cast<unsigned>(page_size));

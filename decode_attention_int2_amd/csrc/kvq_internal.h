@@ -15,6 +15,7 @@ constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
 constexpr int kMaxMfmaSplitTokens = 1 << 20;  // tokens per split (keeps split offsets far from int32 overflow)
 constexpr int kMaxSplits = 4096;            // split partials merged per (row, head)
 constexpr int kMfmaWaves = 8;               // waves per workgroup of the matrix-core decode kernel
+constexpr int kMaxSplitsNoPremerge = 8;     // more splits: the waves' partials are merged per split first
 constexpr int64_t kMaxSeqLen = static_cast<int64_t>(1) << 26;  // max_seq_len accepted by the decode entry point
 
 // Rotation descriptor passed by value to kernels.
@@ -245,6 +246,33 @@ __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, uint32_t ep
     old = seen;
   }
 }
+// Arrival counting without compare-and-swap retries (many workgroups may
+// arrive at once): c[0] counts arrivals with one fetch-add each and is reset
+// to 0 by the last arrival, so it starts every launch at 0 once c[1] holds
+// the validation value of this counter (read by the caller at kernel start:
+// `valid`).  A counter not yet validated (fresh workspace) counts with the
+// tagged compare-and-swap on c[2] for one launch, whose last arrival then
+// zeroes c[0] and validates it.  Every arrival of a launch reads the same c[1]:
+// only the launch's last arrival writes it.
+__device__ __forceinline__ unsigned long long arrival_valid_value(const unsigned long long *c) {
+  return static_cast<unsigned long long>(reinterpret_cast<uintptr_t>(c)) ^ 0x6b76715f61727276ull;
+}
+__device__ __forceinline__ bool arrive_counted(unsigned long long *c, bool valid, uint32_t epoch, int parts) {
+  if (valid) {
+    const unsigned long long old = atomicAdd(c, 1ull);
+    const bool last = old == static_cast<unsigned long long>(parts - 1);
+    if (last) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return last;
+  }
+  const bool last = arrive_last(c + 2, epoch, parts);
+  if (last) {
+    __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(c + 1, arrival_valid_value(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return last;
+}
+constexpr int kArrivalWords = 3;  // uint64 words per counted arrival point
+
 // A new arrival tag per launch (host side), starting from a per-process value
 // so that counters left in memory by other processes rarely carry it.
 uint32_t next_launch_epoch();

@@ -14,7 +14,7 @@ import torch
 import oracle
 import synthetic
 from kvq_testlib import (check_rotated_quantization, f32np, gpu_decode, gpu_quantize, gpu_rot,
-                         oracle_cache_and_decode, oracle_rot, rel_l2, tolerance)
+                         oracle_cache_and_decode, oracle_decode_on_cache, oracle_rot, rel_l2, tolerance)
 
 pytestmark = pytest.mark.gpu
 
@@ -153,6 +153,23 @@ def test_decode_split_count_invariance(dev):
     for ns in (0, 3, 12):
         o, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=ns)
         assert rel_l2(f32np(o), f32np(base)) < 5e-5
+
+
+def test_decode_premerged_splits_nan_and_parity(dev):
+    """More than 8 splits per sequence: the workgroup merges its waves'
+    partials first.  Parity with the oracle and NaN confined to the sequence
+    with an out-of-range page index (host-forced condition)."""
+    w = synthetic.make("paged16x32k", dev, tokens=3000, num_seqs=3, H=2, Hq=8, d_model=64)
+    cache = gpu_quantize(w, dev)
+    out_o, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=12)
+    (ref_o, _), _ = oracle_decode_on_cache(w, cache.pages.cpu().numpy(), range(3), with_wo=False)
+    assert rel_l2(f32np(out_o), ref_o) <= 1e-4
+    pt = w.page_table.clone()
+    pt[1, 100] = w.num_pages + 3                        # invalid page inside sequence 1
+    o2, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=12, page_table=pt)
+    o2 = f32np(o2)
+    assert np.all(np.isnan(o2[1]))
+    assert rel_l2(o2[[0, 2]], ref_o[[0, 2]]) <= 1e-4
 
 
 def test_decode_edge_cases(dev):
