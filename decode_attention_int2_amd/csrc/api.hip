@@ -27,8 +27,8 @@ int check_rotation(const kvq_rotation *r) {
       return KVQ_OK;
     case KVQ_ROT_SIGNED_HADAMARD:
       return r->signs ? KVQ_OK : KVQ_ERR_INVALID_ARGUMENT;
-    case KVQ_ROT_DENSE:
-      return r->matrix ? KVQ_OK : KVQ_ERR_INVALID_ARGUMENT;
+    case KVQ_ROT_DENSE:  // (read with 16-byte vector loads)
+      return r->matrix && (reinterpret_cast<uintptr_t>(r->matrix) & 15u) == 0 ? KVQ_OK : KVQ_ERR_INVALID_ARGUMENT;
     default:
       return KVQ_ERR_UNSUPPORTED;
   }
@@ -173,17 +173,9 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
   const RotDev rk = to_dev(*rot_k), rv = to_dev(*rot_v);
   if (decode_mfma_supported(pl, cache->page_size)) {
-    // one launch: query rotation, split attention, merge, R_V^T (a dense R_K
-    // is applied by its own launch first)
-    const void *qk = q;
-    RotDev rq = rk;
-    if (rk.kind == KVQ_ROT_DENSE) {
-      KVQ_TRY(launch_query_rotation(q, dtype, pl, rk, qrot, qsum, stream));
-      qk = qrot;
-      rq = RotDev{kRotPrescaled, nullptr, nullptr};
-    }
+    // one launch: query rotation, split attention, merge, R_V^T
     if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
-    KVQ_TRY(launch_decode_mfma(pl, qk, dtype, rq, rv, cache->pages, cache->num_pages, cache->page_size, page_table,
+    KVQ_TRY(launch_decode_mfma(pl, q, dtype, rk, rv, cache->pages, cache->num_pages, cache->page_size, page_table,
                                max_pages_per_seq, seq_lens, part, reinterpret_cast<uint64_t *>(ws + pl.off_cnt),
                                out_o, ot, stream));
     if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
@@ -273,14 +265,8 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
   KVQ_TRY(launch_fill_i32(seq_len, static_cast<int32_t>(num_tokens), 1, stream));
   for (int r = 0; r < num_candidates; ++r) {
     const RotDev rot = to_dev(candidates[r]);
-    // matrix-core path: queries rotated inside the decode launch, except a dense R_K (once per candidate)
-    const void *qk = q;
-    RotDev rq = rot;
-    if (!mfma || rot.kind == KVQ_ROT_DENSE) {
-      KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
-      qk = qrot;
-      rq = RotDev{kRotPrescaled, nullptr, nullptr};
-    }
+    // matrix-core path: queries rotated inside the decode launch
+    if (!mfma) KVQ_TRY(launch_query_rotation(q, dtype, pl, rot, qrot, qsum, stream));
     // the candidate's caches of every clip ratio in one pass (one rotation)
     KVQ_TRY(launch_quantize_clips(k, v, dtype, num_tokens, H, nullptr, rot, rot, key_mean, clips, clips, num_clips,
                                   pages, L.num_pages, 16, L.cache_bytes, stream));
@@ -288,7 +274,7 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
       uint8_t *pages_i = pages + static_cast<size_t>(i) * L.cache_bytes;
       float *o_hat = o_hat_all + (static_cast<size_t>(r) * num_clips + i) * Nq * Hq * D;
       if (mfma) {
-        KVQ_TRY(launch_decode_mfma(pl, qk, dtype, rq, rot, pages_i, L.num_pages, 16, nullptr,
+        KVQ_TRY(launch_decode_mfma(pl, q, dtype, rot, rot, pages_i, L.num_pages, 16, nullptr,
                                    static_cast<int>(L.num_pages), seq_len, part, counters, o_hat, nullptr, stream));
       } else {
         KVQ_TRY(launch_decode_split(pl, pages_i, L.num_pages, 16, nullptr, static_cast<int>(L.num_pages), seq_len,

@@ -453,7 +453,7 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     }
 }
 
-template <int DT, bool P16>
+template <int DT, bool P16, bool kDense>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float red[kWaves][5][4 + D];  // per wave, per row: m, l, z, flag, acc[128]; row 4: unused stores
   __shared__ float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
@@ -461,6 +461,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float qsum_s[4];
   __shared__ int qshift_s[4];              // fixed-point shift S of each row's digits
   __shared__ uint32_t digit_s[8][64];      // key-side A operand: dword [m][e] of each lane
+  __shared__ float qd_s[kDense ? 4 : 1][D];  // dense R_K: q R_K of the group's rows
   __shared__ uint32_t s_last;
   __shared__ uint32_t s_next;               // next unclaimed 64-token block of the split
   const int s = blockIdx.x, b = blockIdx.z;
@@ -517,6 +518,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     sb0 = sp[lane];
     sb1 = sp[lane + 64];
   }
+  // dense R_K: this thread's 8 x 16 bytes of the head's matrix (64 KB per
+  // workgroup, staged in LDS for the query rows' product)
+  // (eight named registers: an array here would be placed in LDS)
+  float4 rs0, rs1, rs2, rs3, rs4, rs5, rs6, rs7;
+  if constexpr (kDense) {
+    const float4 *rm = reinterpret_cast<const float4 *>(a.rk.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x;
+    constexpr int kT = 64 * kWaves;
+    rs0 = rm[0];
+    rs1 = rm[kT];
+    rs2 = rm[2 * kT];
+    rs3 = rm[3 * kT];
+    rs4 = rm[4 * kT];
+    rs5 = rm[5 * kT];
+    rs6 = rm[6 * kT];
+    rs7 = rm[7 * kT];
+  }
   // blocks of the split: wave w starts with blocks w, w + 8, w + 16 and then
   // claims the next unclaimed block from an LDS counter (waves of one CU
   // progress at unequal speed; a static share would leave the slow waves'
@@ -544,7 +561,42 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     if (wave < nrows) {
       y0 = DT == KVQ_F32 ? __uint_as_float(qb0) : __uint_as_float(qb0 << 16);
       y1 = DT == KVQ_F32 ? __uint_as_float(qb1) : __uint_as_float(qb1 << 16);
-      rotate_query_signed(y0, y1, a.rk.kind, static_cast<float>(sb0), static_cast<float>(sb1), lane);
+      if constexpr (!kDense)
+        rotate_query_signed(y0, y1, a.rk.kind, static_cast<float>(sb0), static_cast<float>(sb1), lane);
+    }
+    if constexpr (kDense) {
+      // q' = q R_K of the group's 4 rows (rows past the last are zero): the
+      // matrix goes to facc_all (unused until the first flush), the raw rows
+      // to qs; wave w forms columns 16 w .. 16 w + 15 of the 4 rows, each an
+      // fp32 sum in row order
+      float *rs = &facc_all[0][0];
+      {
+        float4 *rd = reinterpret_cast<float4 *>(rs) + threadIdx.x;
+        constexpr int kT = 64 * kWaves;
+        rd[0] = rs0;
+        rd[kT] = rs1;
+        rd[2 * kT] = rs2;
+        rd[3 * kT] = rs3;
+        rd[4 * kT] = rs4;
+        rd[5 * kT] = rs5;
+        rd[6 * kT] = rs6;
+        rd[7 * kT] = rs7;
+      }
+      if (wave < 4) {
+        qs[wave][lane] = y0;
+        qs[wave][lane + 64] = y1;
+      }
+      __syncthreads();
+      const int col = 16 * wave + (lane & 15), rr = lane >> 4;
+      float acc = 0.0f;
+#pragma unroll 8
+      for (int i = 0; i < D; ++i) acc += qs[rr][i] * rs[i * D + col];
+      qd_s[rr][col] = acc;
+      __syncthreads();
+      if (wave < 4) {
+        y0 = qd_s[wave][lane] * (kLog2eF * kInvSqrtD);
+        y1 = qd_s[wave][lane + 64] * (kLog2eF * kInvSqrtD);
+      }
     }
     if (wave < 4) {
       const float sum = wave_sum(y0 + y1);
@@ -770,7 +822,6 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
                               int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
                               float *out_o, float *ot, hipStream_t stream) {
   if (pl.num_seqs == 0) return hipSuccess;
-  if (rk.kind == KVQ_ROT_DENSE) return hipErrorInvalidValue;  // rotated by launch_query_rotation first
   const uint32_t epoch = next_launch_epoch();
   MfmaArgs a{};
   a.R = pl.rows_per_head;
@@ -812,17 +863,24 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.ot = ot;
   const dim3 grid(pl.splits, pl.H * a.n_rg, pl.num_seqs);
   const bool f32 = dtype == KVQ_F32 || rk.kind == kRotPrescaled;
+  const bool dense = rk.kind == KVQ_ROT_DENSE;
+  const dim3 block(64 * kWaves);
+#define KVQ_DECODE_LAUNCH(F32, P16, DENSE)                                                                     \
+  hipLaunchKernelGGL((decode_mfma_kernel<(F32) ? KVQ_F32 : KVQ_BF16, P16, DENSE>), grid, block, 0, stream, a)
   if (page_size == 16) {
-    if (f32)
-      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_F32, true>), grid, dim3(64 * kWaves), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_BF16, true>), grid, dim3(64 * kWaves), 0, stream, a);
+    if (dense) {
+      if (f32) KVQ_DECODE_LAUNCH(true, true, true); else KVQ_DECODE_LAUNCH(false, true, true);
+    } else {
+      if (f32) KVQ_DECODE_LAUNCH(true, true, false); else KVQ_DECODE_LAUNCH(false, true, false);
+    }
   } else {
-    if (f32)
-      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_F32, false>), grid, dim3(64 * kWaves), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<KVQ_BF16, false>), grid, dim3(64 * kWaves), 0, stream, a);
+    if (dense) {
+      if (f32) KVQ_DECODE_LAUNCH(true, false, true); else KVQ_DECODE_LAUNCH(false, false, true);
+    } else {
+      if (f32) KVQ_DECODE_LAUNCH(true, false, false); else KVQ_DECODE_LAUNCH(false, false, false);
+    }
   }
+#undef KVQ_DECODE_LAUNCH
   return hipGetLastError();
 }
 

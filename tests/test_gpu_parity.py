@@ -172,6 +172,28 @@ def test_decode_premerged_splits_nan_and_parity(dev):
     assert rel_l2(o2[[0, 2]], ref_o[[0, 2]]) <= 1e-4
 
 
+def test_decode_workspace_garbage_then_reuse(dev):
+    """The split arrival counters need no zeroed workspace: a workspace full
+    of random bytes (first call counts with the tagged compare-and-swap and
+    validates the counters), then the same workspace again (fetch-add
+    counting), then overwritten with random bytes again."""
+    from decode_attention_int2_amd import kvq
+    w = synthetic.make("paged16x32k", dev, tokens=3000, num_seqs=3, H=2, Hq=8, d_model=64)
+    cache = gpu_quantize(w, dev)
+    (ref_o, _), _ = oracle_decode_on_cache(w, cache.pages.cpu().numpy(), range(3), with_wo=False)
+    nbytes = kvq.kvq_decode_workspace_bytes(w.num_seqs, 1, w.Hq, w.H, w.tokens, 0, 12)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    for garbage in (True, False, False, True):
+        if garbage:
+            ws.copy_(torch.randint(0, 256, (nbytes,), generator=g, dtype=torch.uint8))
+        out_o = torch.full((w.num_seqs, w.Hq, 128), 12345.0, dtype=torch.float32, device=dev)
+        kvq.kvq_decode_attn(w.q, w.num_seqs, 1, cache, w.page_table, w.page_table.shape[1], w.seq_lens, w.tokens,
+                            gpu_rot(w.rot_k), gpu_rot(w.rot_v), out_o, workspace=ws, num_splits=12)
+        torch.cuda.synchronize()
+        assert rel_l2(f32np(out_o), ref_o) <= 1e-4
+
+
 def test_decode_edge_cases(dev):
     """Empty and one-token sequences; an out-of-range page index or seq_len
     gives NaN for that sequence only (host-forced condition)."""
