@@ -22,9 +22,10 @@
  *     slot outside the cache is skipped by kvq_quantize; a page index outside
  *     the cache, or seq_len < 0 or > max_seq_len, makes kvq_decode_attn write
  *     NaN to every output of the affected sequence.
- *   - K, V, q and W_O start at 16-byte aligned addresses (every hipMalloc
- *     or torch allocation does); the kernels read them with 16-byte vector
- *     loads, so an unaligned one returns KVQ_ERR_INVALID_ARGUMENT.
+ *   - K, V, q, W_O and dense rotation matrices start at 16-byte aligned
+ *     addresses (every hipMalloc or torch allocation does); the kernels read
+ *     them with 16-byte vector loads, so an unaligned one returns
+ *     KVQ_ERR_INVALID_ARGUMENT.
  *   - Head dimension and quantization group size are both 128 ([OptR],
  *     Appendix Table A; [Eval]: group size 128, per-token-group K/V).
  */

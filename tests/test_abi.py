@@ -82,6 +82,11 @@ def test_quantize_validation(lib):
                             ctypes.byref(c), None) == 1
     assert lib.kvq_quantize(fake, odd, 1, 4, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
                             ctypes.byref(c), None) == 1
+    # dense rotation matrix not 16-byte aligned -> INVALID
+    from decode_attention_int2_amd.kvq import _Rot
+    bad_dense = _Rot(2, None, 0x2004)
+    assert lib.kvq_quantize(fake, fake, 0, 4, None, ctypes.byref(bad_dense), ctypes.byref(ok_rot), None, f(1), f(1),
+                            ctypes.byref(c), None) == 1
     # nothing to do: zero tokens succeeds without touching the device
     assert lib.kvq_quantize(None, None, 0, 0, None, ctypes.byref(ok_rot), ctypes.byref(ok_rot), None, f(1), f(1),
                             ctypes.byref(c), None) == 0
