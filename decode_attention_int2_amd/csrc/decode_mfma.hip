@@ -800,14 +800,61 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_valid, a.epoch, a.splits) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
-  if (wave < nrows) {
-    const int qq = (row0 + wave) / a.G, j = h * a.G + (row0 + wave) % a.G;
-    const size_t row = static_cast<size_t>(b) * a.Nq + qq;
-    float o0, o1;
-    merge_partials(a.part + (row * a.Hq + j) * a.parts * (D + 4), a.parts, lane, o0, o1);
-    unrotate_value_wave(o0, o1, a.rv, h, lane);
-    store_output_wave(a.out_o, a.ot, row, j, a.Hq, lane, o0, o1);
+  // dense R_V: the head's matrix is staged in LDS by the whole workgroup
+  // (its loads go out together with the merge's)
+  const bool vdense = a.rv.kind == KVQ_ROT_DENSE;
+  float *rs = &facc_all[0][0];  // (free: the flushed accumulators are in the partials)
+  constexpr int kT = 64 * kWaves;
+  float4 v0, v1, v2, v3, v4, v5, v6, v7;
+  if (vdense) {
+    const float4 *rm = reinterpret_cast<const float4 *>(a.rv.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x;
+    v0 = rm[0];
+    v1 = rm[kT];
+    v2 = rm[2 * kT];
+    v3 = rm[3 * kT];
+    v4 = rm[4 * kT];
+    v5 = rm[5 * kT];
+    v6 = rm[6 * kT];
+    v7 = rm[7 * kT];
   }
+  const int qq = (row0 + min(wave, nrows - 1)) / a.G, j = h * a.G + (row0 + min(wave, nrows - 1)) % a.G;
+  const size_t row = static_cast<size_t>(b) * a.Nq + qq;
+  float o0 = 0.0f, o1 = 0.0f;
+  if (wave < nrows) merge_partials(a.part + (row * a.Hq + j) * a.parts * (D + 4), a.parts, lane, o0, o1);
+  if (vdense) {
+    float4 *rd = reinterpret_cast<float4 *>(rs) + threadIdx.x;
+    rd[0] = v0;
+    rd[kT] = v1;
+    rd[2 * kT] = v2;
+    rd[3 * kT] = v3;
+    rd[4 * kT] = v4;
+    rd[5 * kT] = v5;
+    rd[6 * kT] = v6;
+    rd[7 * kT] = v7;
+    // out[r][i] = sum_c o'[r][c] R_V[i][c]: the rows' o' to LDS (rows past
+    // the last are zero), wave w forms columns 16 w .. 16 w + 15 of the 4
+    // rows; column i starts its sum at c = i (mod 128), so the 16 columns of
+    // one instruction read 16 different banks
+    if (wave < 4) {
+      red[wave][0][lane] = o0;
+      red[wave][0][lane + 64] = o1;
+    }
+    __syncthreads();
+    const int col = 16 * wave + (lane & 15), rr = lane >> 4;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < D; ++k) {
+      const int cc = (k + col) & (D - 1);
+      acc += red[rr][0][cc] * rs[col * D + cc];
+    }
+    red[rr][1][col] = acc;
+    __syncthreads();
+    o0 = red[wave < 4 ? wave : 0][1][lane];
+    o1 = red[wave < 4 ? wave : 0][1][lane + 64];
+  } else if (wave < nrows) {
+    unrotate_value_wave(o0, o1, a.rv, h, lane);
+  }
+  if (wave < nrows) store_output_wave(a.out_o, a.ot, row, j, a.Hq, lane, o0, o1);
 }
 
 }  // namespace
