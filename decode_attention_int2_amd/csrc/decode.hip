@@ -397,8 +397,8 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   off = align(off + (d_model > 0 && ks > 1 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
   pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection
   off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * K * kWoRows * sizeof(float) : 0));
-  pl.off_wocnt = off;  // [row groups][column blocks] uint64 arrival counters of the W_O slices
-  off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * col_blocks * sizeof(uint64_t) : 0));
+  pl.off_wocnt = off;  // [row groups][column blocks][kArrivalWords] uint64 arrival counters of the W_O slices
+  off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * col_blocks * kArrivalWords * sizeof(uint64_t) : 0));
   const size_t n_rg_all = static_cast<size_t>(num_seqs) * H * ((queries_per_seq * (Hq / H) + 3) / 4);
   pl.off_cnt = off;  // [num_seqs][H][row groups][kArrivalWords] uint64
   off = align(off + n_rg_all * kArrivalWords * sizeof(uint64_t));

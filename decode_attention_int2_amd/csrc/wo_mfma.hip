@@ -76,7 +76,7 @@ struct WoArgs {
   const void *w;       // [K][d_model]
   int rows, K, d_model, kslices;
   float *ypart;        // [kslices][rows][d_model] slice sums (kslices > 1)
-  unsigned long long *counters;  // [row groups][column blocks]
+  unsigned long long *counters;  // [row groups][column blocks][kArrivalWords]
   uint32_t epoch;
   float *y;            // [rows][d_model]
 };
@@ -95,6 +95,12 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
   const int kw0 = ks * (kWaves * kWaveRows) + wave * kWaveRows;
   const int nk = min(max(a.K - kw0, 0), kWaveRows);  // rows of this wave
   const float *o = a.ot + static_cast<size_t>(rg) * a.K * 16;
+  // arrival counter of this (row group, column block) and its validation
+  // word (read now: the round trip overlaps the loads)
+  unsigned long long *cnt = a.counters + (static_cast<size_t>(rg) * gridDim.x + cb) * kArrivalWords;
+  bool cnt_valid = false;
+  if (a.kslices > 1 && threadIdx.x == 0)
+    cnt_valid = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == arrival_valid_value(cnt);
 
   // all loads of the wave first (rows past the wave's share read as zero)
   typename WRaw<DT>::type wv[kSteps];
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
-    s_last = arrive_last(a.counters + static_cast<size_t>(rg) * gridDim.x + cb, a.epoch, a.kslices) ? 1u : 0u;
+    s_last = arrive_counted(cnt, cnt_valid, a.epoch, a.kslices) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
 #pragma unroll
