@@ -52,6 +52,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-search measurement")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the decode figures of the batch-1 and long-context workloads")
     ap.add_argument("--calibration-only", action="store_true",
                     help="only time the calibration search (calib64k) and print its figures")
     ap.add_argument("--num-splits", type=int, default=0, help="split-K parts per sequence (0 = library default)")
@@ -86,6 +88,62 @@ def measured_traffic(path: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def host_cpu():
+    """(threads this process may use, logical CPUs of the host, CPU model)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return usable, os.cpu_count(), model
+
+
+def cpu_baseline_threaded(w_cpu, threads: int) -> dict:
+    """The same oracle calls on `threads` sequences at once (one sequence per
+    thread, its own cache; the oracle's C routines keep no shared state and
+    release the interpreter lock): cache writes, then decode steps."""
+    import numpy as np
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+
+    T = w_cpu["tokens"]
+    S = w_cpu["k"].shape[0] // T
+    H = w_cpu["k"].shape[1]
+    P = 16
+    pages = (T + P - 1) // P
+    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=w_cpu["signs"])
+    caches = [oracle.Cache(pages, P, H) for _ in range(S)]
+    slots = np.arange(T, dtype=np.int64)
+
+    def write(s):
+        oracle.quantize(w_cpu["k"][s * T:(s + 1) * T], w_cpu["v"][s * T:(s + 1) * T], caches[s], rot, rot,
+                        clip_k=0.96, clip_v=0.92, slot_mapping=slots)
+
+    def read(s):
+        oracle.decode(w_cpu["q"][s:s + 1], caches[s], [T], rot, rot, num_seqs=1, max_pages=pages)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(write, range(S)))
+        t1 = time.perf_counter()
+        list(ex.map(read, range(S)))
+        t2 = time.perf_counter()
+    usable, logical, model = host_cpu()
+    return {"value": S * T * H * BYTES_PER_TOKEN_HEAD / (t2 - t1) / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": f"{S} of 16 sequences x {H} KV heads x {T} tokens, one sequence per thread: "
+                                        f"oracle cache write {t1 - t0:.2f} s, oracle decode {t2 - t1:.2f} s",
+            "quantize_mtok_s": S * T / (t1 - t0) / 1e6, "host_logical_cpus": logical, "usable_cpus": usable,
+            "cpu_model": model}
+
+
 def cpu_baseline(w_cpu) -> dict:
     """The oracle as it stands, timed on this host on a bounded sample of the
     same workload (about 10-20 s single-threaded): two of the 16 sequences,
@@ -115,6 +173,36 @@ def cpu_baseline(w_cpu) -> dict:
             "sample": f"{S} of 16 sequences x {H} KV heads x {T} tokens: oracle cache write {t1 - t0:.2f} s, "
                       f"oracle decode ({q.shape[1]} query heads) {t2 - t1:.2f} s",
             "quantize_mtok_s": S * T / (t1 - t0) / 1e6}
+
+
+def decode_workload(name, dev, timed, median_of, min_bytes=0):
+    """Decode attention (no W_O) of another decode workload: average GPU time
+    of one call, median of 5 runs of 50 calls.  With min_bytes, the calls
+    rotate through enough cache copies that the caches together exceed it
+    (each call then reads its cache from HBM, not the 256 MB Infinity Cache)."""
+    import torch
+    import synthetic
+    from decode_attention_int2_amd import kvq
+    w = synthetic.make(name, dev)
+    B, T, H, Hq = w.num_seqs, w.tokens, w.H, w.Hq
+    rot = kvq.Rotation(w.rot_k.kind, signs=w.rot_k.signs, matrix=w.rot_k.matrix)
+    kv_bytes = B * T * H * BYTES_PER_TOKEN_HEAD
+    n = max(3, -(-min_bytes // kv_bytes))
+    caches = [kvq.Cache(w.num_pages, w.page_size, H, device=dev) for _ in range(n)]
+    for c in caches:
+        kvq.kvq_quantize(w.k, w.v, c, rot, rot, key_mean=w.key_mean, clip_k=w.clip_k, clip_v=w.clip_v,
+                         slot_mapping=w.slot_mapping)
+    del w.k, w.v
+    out_o = torch.empty((B * w.queries_per_seq, Hq, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, w.queries_per_seq, Hq, H, T, 0, 0), dtype=torch.uint8,
+                     device=dev)
+    dec = lambda i: kvq.kvq_decode_attn(w.q, B, w.queries_per_seq, caches[i % n], w.page_table,
+                                        w.page_table.shape[1], w.seq_lens, T, rot, rot, out_o, workspace=ws)
+    ms = median_of(lambda: timed(dec, 50))
+    return {"workload": name, "description": synthetic.DESCRIPTIONS[name], "cache_copies": n,
+            "source": "hbm" if n * kv_bytes > 2 * 256e6 else "mall-resident", "decode_attn_us": round(ms * 1e3, 2),
+            "gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
 
 def calibration_search(dev, timed):
@@ -183,6 +271,11 @@ def main():
         timed.wall_s = time.perf_counter() - w0
         return e0.elapsed_time(e1) / n
 
+    def median_of(fn, repeats=5):
+        """Median over repeats of fn() (each an average over a run of calls)."""
+        vals = sorted(fn() for _ in range(repeats))
+        return vals[len(vals) // 2]
+
     if a.calibration_only:
         print(json.dumps({"calibration_search": calibration_search(dev, timed)}))
         return
@@ -219,9 +312,10 @@ def main():
     torch.cuda.synchronize()
     step_ms = timed(lambda i: step(a.warmup + i), a.steps)
     wall = timed.wall_s
-    attn_ms = timed(lambda i: decode(i, with_wo=False), a.steps)
-    quant_ms = timed(quantize, a.steps)
-    decode_ms = timed(decode, a.steps)
+    # decode attention and the cache write: median of 5 runs of >= 50 (>= 20) calls
+    attn_ms = median_of(lambda: timed(lambda i: decode(i, with_wo=False), max(50, a.steps)))
+    quant_ms = median_of(lambda: timed(quantize, max(20, a.steps)))
+    decode_ms = median_of(lambda: timed(decode, max(50, a.steps)))
 
     kv_bytes = B * T * H * BYTES_PER_TOKEN_HEAD
     attn_gbs = kv_bytes / (attn_ms * 1e-3) / 1e9
@@ -231,18 +325,34 @@ def main():
 
     traffic = measured_traffic(a.traffic_json)
 
+    clip_k, clip_v, desc = w.clip_k, w.clip_v, synthetic.DESCRIPTIONS[WORKLOAD]
+    w_cpu = None
+    if not a.no_cpu_baseline:   # the oracle's sample: 2 of the 16 sequences, copied to the host
+        # threaded run: one sequence per usable CPU, at most 16 (this GPU's share of the host)
+        n_thr = max(1, min(16, host_cpu()[0], B))
+        n_cpu = max(2, n_thr)
+        w_cpu = {"tokens": T, "k": w.k[:n_cpu * T].float().cpu().numpy(), "v": w.v[:n_cpu * T].float().cpu().numpy(),
+                 "q": w.q[:n_cpu].float().cpu().numpy(), "signs": w.rot_k.signs.cpu().numpy(), "threads": n_thr}
+    del caches, ws, w
+    torch.cuda.empty_cache()
+    # the other decode workloads: batch 1 x 32K (from HBM, and as measured with
+    # 3 copies that stay in the Infinity Cache) and 4 x 131K tokens
+    others = None
+    if not a.no_other_workloads:
+        others = [decode_workload("gqa32k", dev, timed, median_of, min_bytes=600 << 20),
+                  decode_workload("gqa32k", dev, timed, median_of),
+                  decode_workload("long131k", dev, timed, median_of)]
+        torch.cuda.empty_cache()
     # calibration search (a separate workload of the same path)
     cal = None
     if not a.no_calibration:
-        del caches, ws
-        torch.cuda.empty_cache()
         cal = calibration_search(dev, timed)
 
     base = None
-    if not a.no_cpu_baseline:
-        w_cpu = {"tokens": T, "k": w.k[:2 * T].float().cpu().numpy(), "v": w.v[:2 * T].float().cpu().numpy(),
-                 "q": w.q[:2].float().cpu().numpy(), "signs": w.rot_k.signs.cpu().numpy()}
+    if w_cpu is not None:
         base = cpu_baseline(w_cpu)
+        base["threaded"] = cpu_baseline_threaded(w_cpu, w_cpu["threads"])
+        base["cpu_model"] = host_cpu()[2]
 
     out = {
         "metric": "INT2 decode-attn effective KV GB/s (% HBM peak) + quantize Mtok/s, 32K ctx",
@@ -257,10 +367,10 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "description": synthetic.DESCRIPTIONS[WORKLOAD], "batch": B,
+        "config": {"workload": WORKLOAD, "description": desc, "batch": B,
                    "context": T, "kv_heads": H, "q_heads": Hq, "head_dim": 128, "page_size": P, "d_model": dm,
                    "kv_input_dtype": "bf16", "cache": "int2 group-128 + fp16 scale/zero",
-                   "rotation": "signed_hadamard", "clip_k": w.clip_k, "clip_v": w.clip_v},
+                   "rotation": "signed_hadamard", "clip_k": clip_k, "clip_v": clip_v},
         "pct_hbm_peak": round(100.0 * attn_gbs / HBM_PEAK_GBS, 2),
         "decode_attn_us": round(attn_ms * 1e3, 2),
         "decode_call_us": round(decode_ms * 1e3, 2),
@@ -272,6 +382,7 @@ def main():
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_mfma_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": base,
+        "other_decode_workloads": others,
         "calibration_search": cal,
     }
     print(json.dumps(out))
