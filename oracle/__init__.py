@@ -73,6 +73,12 @@ def _load():
         lib.kvqo_attention_ref.argtypes = [P, i32, i32, P, P, i64, i32, P]
         lib.kvqo_candidate_nmse.argtypes = [P, P, P, i64, i32, i32, i32, P, i32, P, i32, P, P, i32, I,
                                             P, P, P]
+        lib.kvqo_f32_to_bf16.argtypes = [F]
+        lib.kvqo_f32_to_bf16.restype = ctypes.c_uint16
+        lib.kvqo_window_write.argtypes = [P, P, i64, i32, P, P, i32, P, P, P, P, i32, i32]
+        lib.kvqo_decode_windows_f64.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P, P]
+        lib.kvqo_bits_per_element.argtypes = [i64, i32, i32]
+        lib.kvqo_bits_per_element.restype = ctypes.c_double
         _lib = lib
     return _lib
 
@@ -204,6 +210,72 @@ def decode(q, cache: Cache, seq_lens, rot_k: Rotation, rot_v: Rotation, num_seqs
                            ctypes.byref(rk), ctypes.byref(rv), _ptr(wo), d_model, _ptr(out_o), _ptr(out_y)),
            "decode")
     return (out_o, out_y) if wo is not None else out_o
+
+
+class _Windows(ctypes.Structure):
+    _fields_ = [("sink_k", ctypes.c_void_p), ("sink_v", ctypes.c_void_p), ("recent_k", ctypes.c_void_p),
+                ("recent_v", ctypes.c_void_p), ("num_sink", ctypes.c_int32), ("num_recent", ctypes.c_int32),
+                ("key_mean", ctypes.c_void_p)]
+
+
+class Windows:
+    """BF16 sink and recent windows of num_seqs sequences (bf16 bits, uint16):
+    sink [num_seqs][num_sink][H][128], recent [num_seqs][num_recent][H][128]
+    (position p in slot p % num_recent); key_mean [H][128] centers the window
+    keys as the cache write centered the INT2 keys."""
+
+    def __init__(self, num_seqs: int, num_kv_heads: int, num_sink: int = 64, num_recent: int = 256,
+                 key_mean=None):
+        self.num_seqs, self.num_kv_heads = int(num_seqs), int(num_kv_heads)
+        self.num_sink, self.num_recent = int(num_sink), int(num_recent)
+        self.sink_k = np.zeros((num_seqs, num_sink, num_kv_heads, D), np.uint16)
+        self.sink_v = np.zeros_like(self.sink_k)
+        self.recent_k = np.zeros((num_seqs, num_recent, num_kv_heads, D), np.uint16)
+        self.recent_v = np.zeros_like(self.recent_k)
+        self.key_mean = _f32(key_mean)
+
+    def _c(self):
+        return _Windows(_ptr(self.sink_k).value, _ptr(self.sink_v).value, _ptr(self.recent_k).value,
+                        _ptr(self.recent_v).value, self.num_sink, self.num_recent,
+                        None if self.key_mean is None else _ptr(self.key_mean).value)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """fp32 -> bf16 bits (round to nearest even), elementwise."""
+    x = np.ascontiguousarray(x, np.float32)
+    f = _load().kvqo_f32_to_bf16
+    return np.array([f(float(e)) for e in x.ravel()], np.uint16).reshape(x.shape)
+
+
+def window_write(k, v, seq_idx, positions, windows: Windows):
+    k, v = _f32(k), _f32(v)
+    si = np.ascontiguousarray(seq_idx, np.int32)
+    ps = np.ascontiguousarray(positions, np.int32)
+    w = windows
+    _check(_load().kvqo_window_write(_ptr(k), _ptr(v), k.shape[0], k.shape[1], _ptr(si), _ptr(ps), w.num_seqs,
+                                     _ptr(w.sink_k), _ptr(w.sink_v), _ptr(w.recent_k), _ptr(w.recent_v),
+                                     w.num_sink, w.num_recent), "window_write")
+
+
+def decode_windows(q, cache: Cache, seq_lens, rot_k: Rotation, rot_v: Rotation, windows: Windows, num_seqs: int,
+                   queries_per_seq: int = 1, page_table=None, max_pages: int = 0) -> np.ndarray:
+    """fp64 out_o [rows][Hq][128] of the decode with BF16 sink and recent windows."""
+    q = _f32(q)
+    rows, Hq, _ = q.shape
+    pt = None if page_table is None else np.ascontiguousarray(page_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    c = cache._c()
+    rk, rv = rot_k._c(), rot_v._c()
+    wc = windows._c()
+    out = np.zeros((rows, Hq, D), np.float64)
+    _check(_load().kvqo_decode_windows_f64(_ptr(q), num_seqs, queries_per_seq, Hq, ctypes.byref(c), _ptr(pt),
+                                           max_pages, _ptr(sl), ctypes.byref(rk), ctypes.byref(rv),
+                                           ctypes.byref(wc), _ptr(out)), "decode_windows_f64")
+    return out
+
+
+def bits_per_element(seq_len: int, num_sink: int = 64, num_recent: int = 256) -> float:
+    return float(_load().kvqo_bits_per_element(seq_len, num_sink, num_recent))
 
 
 def attention_ref(q, k, v) -> np.ndarray:

@@ -638,3 +638,186 @@ int kvqo_candidate_nmse(const float *k, const float *v, const float *q, int64_t 
   free(mean);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* BF16 sink and recent windows (the header states the passages). */
+
+uint16_t kvqo_f32_to_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof(u));
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static double bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof(f));
+  return (double)f;
+}
+
+int kvqo_window_write(const float *k, const float *v, int64_t num_tokens, int32_t num_kv_heads,
+                      const int32_t *seq_idx, const int32_t *positions, int32_t num_seqs, uint16_t *sink_k,
+                      uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v, int32_t num_sink,
+                      int32_t num_recent) {
+  const int d = KVQO_D;
+  if (num_tokens < 0 || num_kv_heads < 1 || num_seqs < 0 || num_sink < 0 || num_recent < 0) return KVQO_ERR_ARG;
+  if (num_tokens > 0 && (!k || !v || !seq_idx || !positions)) return KVQO_ERR_ARG;
+  if ((num_sink > 0 && (!sink_k || !sink_v)) || (num_recent > 0 && (!recent_k || !recent_v))) return KVQO_ERR_ARG;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    const int32_t b = seq_idx[i], p = positions[i];
+    if (b < 0 || b >= num_seqs || p < 0) continue;
+    uint16_t *dk, *dv;
+    if (p < num_sink) {
+      dk = sink_k + ((size_t)b * num_sink + p) * num_kv_heads * d;
+      dv = sink_v + ((size_t)b * num_sink + p) * num_kv_heads * d;
+    } else if (num_recent > 0) {
+      dk = recent_k + ((size_t)b * num_recent + p % num_recent) * num_kv_heads * d;
+      dv = recent_v + ((size_t)b * num_recent + p % num_recent) * num_kv_heads * d;
+    } else {
+      continue;
+    }
+    for (size_t e = 0; e < (size_t)num_kv_heads * d; ++e) {
+      dk[e] = kvqo_f32_to_bf16(k[(size_t)i * num_kv_heads * d + e]);
+      dv[e] = kvqo_f32_to_bf16(v[(size_t)i * num_kv_heads * d + e]);
+    }
+  }
+  return KVQO_OK;
+}
+
+int kvqo_decode_windows_f64(const float *q, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                            const kvqo_cache *cache, const int32_t *page_table, int32_t max_pages,
+                            const int32_t *seq_lens, const kvqo_rotation *rot_k, const kvqo_rotation *rot_v,
+                            const kvqo_windows *win, double *out_o) {
+  const int d = KVQO_D;
+  if (!q || !cache || !cache->pages || !seq_lens || !rot_k || !rot_v || !win || !out_o) return KVQO_ERR_ARG;
+  if (num_seqs < 0 || queries_per_seq < 1 || num_q_heads < 1 || win->num_sink < 0 || win->num_recent < 0)
+    return KVQO_ERR_ARG;
+  if ((win->num_sink > 0 && (!win->sink_k || !win->sink_v)) ||
+      (win->num_recent > 0 && (!win->recent_k || !win->recent_v)))
+    return KVQO_ERR_ARG;
+  const int32_t H = cache->num_kv_heads, P = cache->page_size, S = win->num_sink, W = win->num_recent;
+  if (H < 1 || num_q_heads % H) return KVQO_ERR_ARG;
+  const int32_t G = num_q_heads / H;
+  double *rk = (double *)malloc(sizeof(double) * d * d);
+  double *rv = (double *)malloc(sizeof(double) * d * d);
+  double *qr = (double *)malloc(sizeof(double) * d);
+  double *o_int = (double *)malloc(sizeof(double) * d);
+  double *o_win = (double *)malloc(sizeof(double) * d);
+  uint8_t codes[KVQO_D];
+  uint16_t sb, zb;
+  int rc = (rk && rv && qr && o_int && o_win) ? KVQO_OK : KVQO_ERR_ARG;
+  for (int32_t b = 0; b < num_seqs && !rc; ++b) {
+    const int32_t L = seq_lens[b];
+    if (L < 0 || L > max_pages * P) {
+      rc = KVQO_ERR_ARG;
+      break;
+    }
+    const int32_t lo = L < S ? L : S;                /* sink: [0, lo)      */
+    const int32_t hi = L - W > lo ? L - W : lo;      /* INT2: [lo, hi)     */
+    const size_t n = (size_t)(L ? L : 1);            /* recent: [hi, L)    */
+    double *logit = (double *)malloc(sizeof(double) * n);
+    double *kt = (double *)malloc(sizeof(double) * n * d); /* INT2: rotated domain; window: k - mu */
+    double *vt = (double *)malloc(sizeof(double) * n * d); /* INT2: rotated domain; window: v      */
+    if (!logit || !kt || !vt) rc = KVQO_ERR_ARG;
+    for (int32_t h = 0; h < H && !rc; ++h) {
+      for (int32_t t = 0; t < L && !rc; ++t) {
+        double *kr = kt + (size_t)t * d, *vr = vt + (size_t)t * d;
+        if (t >= lo && t < hi) {
+          int64_t page = page_table ? page_table[(size_t)b * max_pages + t / P] : (int64_t)b * max_pages + t / P;
+          if (page < 0 || page >= cache->num_pages) {
+            rc = KVQO_ERR_ARG;
+            break;
+          }
+          const int64_t slot = page * P + t % P;
+          rc = kvqo_read_group(cache, slot, h, 0, codes, &sb, &zb);
+          for (int i = 0; i < d && !rc; ++i) kr[i] = (double)dequant(codes[i], sb, zb);
+          if (!rc) rc = kvqo_read_group(cache, slot, h, 1, codes, &sb, &zb);
+          for (int i = 0; i < d && !rc; ++i) vr[i] = (double)dequant(codes[i], sb, zb);
+        } else {
+          const uint16_t *ks, *vs;
+          if (t < lo) {
+            ks = win->sink_k + (((size_t)b * S + t) * H + h) * d;
+            vs = win->sink_v + (((size_t)b * S + t) * H + h) * d;
+          } else {
+            ks = win->recent_k + (((size_t)b * W + t % W) * H + h) * d;
+            vs = win->recent_v + (((size_t)b * W + t % W) * H + h) * d;
+          }
+          for (int i = 0; i < d; ++i) {
+            const double mu = win->key_mean ? (double)win->key_mean[(size_t)h * d + i] : 0.0;
+            kr[i] = bf16_to_f64(ks[i]) - mu;
+            vr[i] = bf16_to_f64(vs[i]);
+          }
+        }
+      }
+      if (rc) break;
+      rc = kvqo_rotation_matrix(rot_k->kind, rot_k->signs ? rot_k->signs + (size_t)h * d : NULL,
+                                rot_k->matrix ? rot_k->matrix + (size_t)h * d * d : NULL, rk);
+      if (!rc)
+        rc = kvqo_rotation_matrix(rot_v->kind, rot_v->signs ? rot_v->signs + (size_t)h * d : NULL,
+                                  rot_v->matrix ? rot_v->matrix + (size_t)h * d * d : NULL, rv);
+      if (rc) break;
+      for (int32_t qi = 0; qi < queries_per_seq; ++qi) {
+        const int64_t row = (int64_t)b * queries_per_seq + qi;
+        for (int32_t g = 0; g < G; ++g) {
+          const int32_t j = h * G + g;
+          const float *qv = q + ((size_t)row * num_q_heads + j) * d;
+          double *o = out_o + ((size_t)row * num_q_heads + j) * d;
+          for (int c = 0; c < d; ++c) { /* q' = q R_K for the INT2 keys */
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += (double)qv[i] * rk[i * d + c];
+            qr[c] = acc;
+          }
+          if (L == 0) {
+            for (int c = 0; c < d; ++c) o[c] = 0.0;
+            continue;
+          }
+          double mx = -INFINITY;
+          for (int32_t t = 0; t < L; ++t) {
+            const double *kr = kt + (size_t)t * d;
+            const int in_int2 = t >= lo && t < hi;
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += (in_int2 ? qr[i] : (double)qv[i]) * kr[i];
+            logit[t] = acc / sqrt((double)d);
+            if (logit[t] > mx) mx = logit[t];
+          }
+          double zsum = 0.0;
+          for (int c = 0; c < d; ++c) o_int[c] = o_win[c] = 0.0;
+          for (int32_t t = 0; t < L; ++t) {
+            const double p = exp(logit[t] - mx);
+            const double *vr = vt + (size_t)t * d;
+            double *acc = (t >= lo && t < hi) ? o_int : o_win;
+            zsum += p;
+            for (int c = 0; c < d; ++c) acc[c] += p * vr[c];
+          }
+          /* o = (o_int R_V^T + o_win) / zsum: the INT2 values are in the rotated domain */
+          for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += o_int[c] * rv[i * d + c];
+            o[i] = (acc + o_win[i]) / zsum;
+          }
+        }
+      }
+    }
+    free(logit);
+    free(kt);
+    free(vt);
+  }
+  free(rk);
+  free(rv);
+  free(qr);
+  free(o_int);
+  free(o_win);
+  return rc;
+}
+
+double kvqo_bits_per_element(int64_t L, int32_t num_sink, int32_t num_recent) {
+  if (L <= 0) return 0.0;
+  const int64_t sink = L < num_sink ? L : num_sink;
+  const int64_t rest = L - sink;
+  const int64_t recent = rest < num_recent ? rest : num_recent;
+  const int64_t int2 = rest - recent;
+  /* per head and side: an INT2 token stores 128 2-bit codes and two fp16 words, a window token 128 bf16 */
+  return ((double)int2 * (128.0 * 2.0 + 32.0) + (double)(sink + recent) * 128.0 * 16.0) / ((double)L * 128.0);
+}

@@ -125,4 +125,49 @@ int kvqo_candidate_nmse(const float *k, const float *v, const float *q, int64_t 
 #ifdef __cplusplus
 }
 #endif
+
+/* ------------------------------------------------------------------------ */
+/* BF16 sink and recent windows ("Output-Aware Rotation for INT2 KV-Cache
+ * Quantization", §5 setup: 64 sink and 256 recent tokens are kept in BF16,
+ * and the effective cost is 2.32 bits per element at a 64K-token context;
+ * §4: sink and recent tokens skip INT2 quantization, their keys keep the
+ * same centering and their values stay unchanged in BF16; Appendix, key
+ * reparameterization: the BF16 window keys keep the centering). */
+typedef struct {
+  const uint16_t *sink_k, *sink_v;     /* [num_seqs][num_sink][H][128] bf16 bits            */
+  const uint16_t *recent_k, *recent_v; /* [num_seqs][num_recent][H][128] bf16 bits: the
+                                          token at position p is in slot p % num_recent  */
+  int32_t num_sink, num_recent;
+  const float *key_mean;               /* [H][128] or NULL: the keys' centering mu        */
+} kvqo_windows;
+
+/* fp32 -> bf16 bits, round to nearest even (NaN stays NaN). */
+uint16_t kvqo_f32_to_bf16(float x);
+
+/* Window write of num_tokens tokens [num_tokens][H][128] (fp32; bf16 inputs
+ * widened): token i of sequence seq_idx[i] at position positions[i] goes to
+ * the sink when the position is below num_sink, else to recent slot
+ * position % num_recent (when num_recent > 0); out-of-range indices are
+ * skipped. */
+int kvqo_window_write(const float *k, const float *v, int64_t num_tokens, int32_t num_kv_heads,
+                      const int32_t *seq_idx, const int32_t *positions, int32_t num_seqs, uint16_t *sink_k,
+                      uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v, int32_t num_sink,
+                      int32_t num_recent);
+
+/* Decode with the windows, fp64: for a sequence of length L, positions below
+ * lo = min(num_sink, L) are sink tokens, positions in [hi, L) with
+ * hi = max(lo, L - num_recent) are recent tokens, and [lo, hi) are read from
+ * the INT2 cache (as kvqo_decode_f64).  One softmax over all L positions;
+ * a window token's logit is q . (k - mu) / sqrt(128) and its value is v
+ * itself; INT2 tokens as kvqo_decode_f64. */
+int kvqo_decode_windows_f64(const float *q, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                            const kvqo_cache *cache, const int32_t *page_table, int32_t max_pages,
+                            const int32_t *seq_lens, const kvqo_rotation *rot_k, const kvqo_rotation *rot_v,
+                            const kvqo_windows *win, double *out_o);
+
+/* Bits per cached element of a sequence of length L with the windows: each
+ * INT2 token stores 2 bits per element plus an fp16 scale and zero per group
+ * of 128 (2.25 bits per element), each window token 16 bits per element. */
+double kvqo_bits_per_element(int64_t L, int32_t num_sink, int32_t num_recent);
+
 #endif

@@ -408,3 +408,122 @@ def test_envelope_search_sanity_band(oracle):
     assert nm.shape == (1, 9, 5)
     assert sh_best * 3 < ident_best
     assert best[0] >= 5          # a signed-Hadamard candidate wins
+
+
+# ---------------------------------------------------------------- BF16 sink and recent windows
+def test_window_bits_per_element_closed_form(oracle):
+    """2.32 bits per element at a 64K context with 64 sink and 256 recent
+    BF16 tokens (the paper's section 5, Implementation Details): the oracle's
+    count is ((L - 320) * 2.25 + 320 * 16) / L."""
+    g = _gold()["bits_per_element"]
+    n, s, r = g["context_tokens"], g["sink_tokens"], g["recent_tokens"]
+    bpe = oracle.bits_per_element(n, s, r)
+    assert bpe == ((n - s - r) * 2.25 + (s + r) * 16.0) / n == 151856 / 65536
+    assert round(bpe, 2) == g["bpe_printed"]
+    assert oracle.bits_per_element(300, s, r) == 16.0      # every token in a window
+    assert oracle.bits_per_element(4096, 0, 0) == 2.25    # no windows: codes + fp16 scale and zero
+
+
+def test_window_bf16_rounding_ties_to_even(oracle):
+    bits = oracle.f32_to_bf16_bits(np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 65504.0], np.float32))
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x4780]
+    assert oracle.f32_to_bf16_bits(np.array([np.nan], np.float32))[0] & 0x7F80 == 0x7F80
+
+
+def _textbook_attention(q, k, v):
+    """softmax(q k^T / sqrt(128)) v in fp64 for one (query row, head): q [128], k, v [L][128]."""
+    x = (k.astype(np.float64) @ q.astype(np.float64)) / math.sqrt(D)
+    p = np.exp(x - x.max())
+    return (p / p.sum()) @ v.astype(np.float64)
+
+
+def _bf16_values(oracle, x):
+    b = oracle.f32_to_bf16_bits(x).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+def test_windows_only_decode_is_textbook_attention(oracle):
+    """A sequence no longer than 64 + 256 tokens is all windows: the decode is
+    plain softmax attention over the BF16 keys and values (their centering
+    shifts every logit by the same q . mu)."""
+    rng = np.random.default_rng(31)
+    H, Hq, L = 2, 4, 200
+    k = rng.standard_normal((L, H, D)).astype(np.float32)
+    v = rng.standard_normal((L, H, D)).astype(np.float32)
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    mu = rng.standard_normal((H, D)).astype(np.float32)
+    win = oracle.Windows(1, H, 64, 256, key_mean=mu)
+    oracle.window_write(k, v, np.zeros(L, np.int32), np.arange(L, dtype=np.int32), win)
+    cache = oracle.Cache(13, 16, H)          # never read: no position is an INT2 position
+    ident = oracle.Rotation(oracle.ROT_IDENTITY)
+    o = oracle.decode_windows(q, cache, [L], ident, ident, win, num_seqs=1, max_pages=13)
+    kb, vb = _bf16_values(oracle, k), _bf16_values(oracle, v)
+    for j in range(Hq):
+        ref = _textbook_attention(q[0, j], kb[:, j // 2], vb[:, j // 2])
+        assert np.allclose(o[0, j], ref, rtol=1e-12, atol=1e-13)
+
+
+def _grid_keys_values(rng, T, H, mu):
+    """Groups on a 2-bit grid c * s + z (codes 0 and 3 present, dyadic s and z),
+    keys shifted by mu (multiples of 1/4): exact in bf16, and the INT2 cache
+    write (identity rotation, clip 1, keys centered by mu) reproduces them."""
+    def grid():
+        g = np.zeros((T, H, D))
+        for t in range(T):
+            for h in range(H):
+                c = rng.integers(0, 4, D)
+                c[0], c[1] = 0, 3
+                g[t, h] = c * rng.choice([0.25, 0.5]) + rng.choice([-1.0, -0.5, 0.0])
+        return g
+    return (grid() + mu[None]).astype(np.float32), grid().astype(np.float32)
+
+
+def test_windows_mixed_decode_lossless_is_textbook_attention(oracle):
+    """Sink, INT2 middle and recent ring together, with keys centered by a
+    non-zero mean: on grid inputs the INT2 part is exact, so the decode equals
+    plain attention over the raw tokens.  The INT2 cache holds only the middle
+    positions and each window only its own, so reading a position from the
+    wrong store, or leaving the window keys uncentered, changes the result."""
+    rng = np.random.default_rng(32)
+    H, Hq, P = 2, 4, 16
+    lens = [457, 300]                        # INT2 middle [64, 201); all windows
+    mp = (max(lens) + P - 1) // P
+    mu = rng.integers(-4, 5, (H, D)).astype(np.float64) / 4
+    ident = oracle.Rotation(oracle.ROT_IDENTITY)
+    cache = oracle.Cache(2 * mp, P, H)
+    win = oracle.Windows(2, H, 64, 256, key_mean=mu)
+    page_table = rng.permutation(2 * mp).astype(np.int32).reshape(2, mp)
+    q = rng.standard_normal((2, Hq, D)).astype(np.float32)
+    ks, vs = [], []
+    for b, L in enumerate(lens):
+        k, v = _grid_keys_values(rng, L, H, mu)
+        ks.append(k)
+        vs.append(v)
+        lo, hi = min(64, L), max(min(64, L), L - 256)
+        mid = np.arange(lo, hi)
+        if mid.size:
+            slots = page_table[b, mid // P].astype(np.int64) * P + mid % P
+            oracle.quantize(k[mid], v[mid], cache, ident, ident, key_mean=mu, clip_k=1.0, clip_v=1.0,
+                            slot_mapping=slots)
+        oracle.window_write(k, v, np.full(L, b, np.int32), np.arange(L, dtype=np.int32), win)
+    o = oracle.decode_windows(q, cache, lens, ident, ident, win, num_seqs=2, page_table=page_table, max_pages=mp)
+    for b, L in enumerate(lens):
+        for j in range(Hq):
+            ref = _textbook_attention(q[b, j], ks[b][:, j // 2], vs[b][:, j // 2])
+            assert np.allclose(o[b, j], ref, rtol=1e-10, atol=1e-12), (b, j)
+
+
+def test_windows_of_size_zero_reduce_to_plain_decode(oracle):
+    rng = np.random.default_rng(33)
+    H, Hq, P, L = 2, 4, 16, 150
+    mp = (L + P - 1) // P
+    s = (rng.integers(0, 2, (H, D)) * 2 - 1).astype(np.int8)
+    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=s)
+    k = rng.standard_normal((L, H, D)).astype(np.float32)
+    v = rng.standard_normal((L, H, D)).astype(np.float32)
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    cache = oracle.Cache(mp, P, H)
+    oracle.quantize(k, v, cache, rot, rot, clip_k=0.96, clip_v=0.92)
+    ref = oracle.decode(q, cache, [L], rot, rot, num_seqs=1, max_pages=mp, f64=True)
+    got = oracle.decode_windows(q, cache, [L], rot, rot, oracle.Windows(1, H, 0, 0), num_seqs=1, max_pages=mp)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
