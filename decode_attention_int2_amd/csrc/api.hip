@@ -42,6 +42,21 @@ int check_cache(const kvq_cache *c) {
   return KVQ_OK;
 }
 
+// 0 = ok, else a kvq_status.
+int check_windows(const kvq_windows *w, int H) {
+  if (!w) return KVQ_ERR_INVALID_ARGUMENT;
+  if (w->num_seqs < 1 || w->num_kv_heads != H || H < 1 || w->num_sink < 0 || w->num_recent < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (w->num_sink % 16) return KVQ_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(w->num_sink) + w->num_recent > kMaxWindowTokens) return KVQ_ERR_UNSUPPORTED;
+  if (w->num_sink > 0 && (!w->sink_k || !w->sink_v)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (w->num_recent > 0 && (!w->recent_k || !w->recent_v)) return KVQ_ERR_INVALID_ARGUMENT;
+  for (const void *p : {static_cast<const void *>(w->sink_k), static_cast<const void *>(w->sink_v),
+                        static_cast<const void *>(w->recent_k), static_cast<const void *>(w->recent_v)})
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  return KVQ_OK;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // K, V, q and W_O are read with 16-byte vector loads (null passes: checked elsewhere)
@@ -134,12 +149,13 @@ size_t kvq_decode_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq, int
       .total;
 }
 
-int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
-                    const kvq_cache *cache, const int32_t *page_table, int32_t max_pages_per_seq,
-                    const int32_t *seq_lens, int32_t max_seq_len, const kvq_rotation *rot_k,
-                    const kvq_rotation *rot_v, const void *w_o, int32_t d_model, float *out_o, float *out_y,
-                    void *workspace, size_t workspace_bytes, int32_t num_splits, const kvq_decode_events *events,
-                    hipStream_t stream) {
+// kvq_decode_attn and kvq_decode_attn_windows (windows: NULL for none)
+static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                       const kvq_cache *cache, const int32_t *page_table, int32_t max_pages_per_seq,
+                       const int32_t *seq_lens, int32_t max_seq_len, const kvq_rotation *rot_k,
+                       const kvq_rotation *rot_v, const kvq_windows *windows, const float *key_mean, const void *w_o,
+                       int32_t d_model, float *out_o, float *out_y, void *workspace, size_t workspace_bytes,
+                       int32_t num_splits, const kvq_decode_events *events, hipStream_t stream) {
   if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
   int rc = check_cache(cache);
   if (rc) return rc;
@@ -161,6 +177,11 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   if (w_o && (d_model < 1 || !out_y)) return KVQ_ERR_INVALID_ARGUMENT;
   if (num_seqs > 0 && (!q || !seq_lens || !out_o)) return KVQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(w_o)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (windows) {
+    rc = check_windows(windows, H);
+    if (rc) return rc;
+    if (windows->num_seqs < num_seqs) return KVQ_ERR_INVALID_ARGUMENT;
+  }
   const DecodePlan pl = make_decode_plan(num_seqs, queries_per_seq, num_q_heads, H, max_seq_len,
                                          w_o ? d_model : 0, num_splits);
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return KVQ_ERR_WORKSPACE;
@@ -172,12 +193,23 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   float *ypart = reinterpret_cast<float *>(ws + pl.off_ypart);
   float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
   const RotDev rk = to_dev(*rot_k), rv = to_dev(*rot_v);
+  if (windows && !decode_mfma_supported(pl, cache->page_size)) return KVQ_ERR_UNSUPPORTED;
+  WindowDev wd{};
+  if (windows) {
+    wd.sink_k = static_cast<const uint16_t *>(windows->sink_k);
+    wd.sink_v = static_cast<const uint16_t *>(windows->sink_v);
+    wd.recent_k = static_cast<const uint16_t *>(windows->recent_k);
+    wd.recent_v = static_cast<const uint16_t *>(windows->recent_v);
+    wd.num_sink = windows->num_sink;
+    wd.num_recent = windows->num_recent;
+    wd.key_mean = key_mean;
+  }
   if (decode_mfma_supported(pl, cache->page_size)) {
     // one launch: query rotation, split attention, merge, R_V^T
     if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
     KVQ_TRY(launch_decode_mfma(pl, q, dtype, rk, rv, cache->pages, cache->num_pages, cache->page_size, page_table,
                                max_pages_per_seq, seq_lens, part, reinterpret_cast<uint64_t *>(ws + pl.off_cnt),
-                               out_o, ot, stream));
+                               out_o, ot, stream, windows ? &wd : nullptr));
     if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
   } else {
     KVQ_TRY(launch_query_rotation(q, dtype, pl, rk, qrot, qsum, stream));
@@ -192,6 +224,57 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
     KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, ypart, reinterpret_cast<uint64_t *>(ws + pl.off_wocnt), out_y,
                                  stream));
   return KVQ_OK;
+}
+
+int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                    const kvq_cache *cache, const int32_t *page_table, int32_t max_pages_per_seq,
+                    const int32_t *seq_lens, int32_t max_seq_len, const kvq_rotation *rot_k,
+                    const kvq_rotation *rot_v, const void *w_o, int32_t d_model, float *out_o, float *out_y,
+                    void *workspace, size_t workspace_bytes, int32_t num_splits, const kvq_decode_events *events,
+                    hipStream_t stream) {
+  return decode_attn(q, dtype, num_seqs, queries_per_seq, num_q_heads, cache, page_table, max_pages_per_seq, seq_lens,
+                     max_seq_len, rot_k, rot_v, nullptr, nullptr, w_o, d_model, out_o, out_y, workspace,
+                     workspace_bytes, num_splits, events, stream);
+}
+
+int kvq_decode_attn_windows(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,
+                            int32_t num_q_heads, const kvq_cache *cache, const int32_t *page_table,
+                            int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                            const kvq_rotation *rot_k, const kvq_rotation *rot_v, const kvq_windows *windows,
+                            const float *key_mean, const void *w_o, int32_t d_model, float *out_o, float *out_y,
+                            void *workspace, size_t workspace_bytes, int32_t num_splits, hipStream_t stream) {
+  if (!windows) return KVQ_ERR_INVALID_ARGUMENT;
+  return decode_attn(q, dtype, num_seqs, queries_per_seq, num_q_heads, cache, page_table, max_pages_per_seq, seq_lens,
+                     max_seq_len, rot_k, rot_v, windows, key_mean, w_o, d_model, out_o, out_y, workspace,
+                     workspace_bytes, num_splits, nullptr, stream);
+}
+
+int kvq_window_write(const void *k, const void *v, int32_t dtype, int64_t num_tokens, const int32_t *seq_idx,
+                     const int32_t *positions, const int32_t *seq_lens, const kvq_windows *windows,
+                     hipStream_t stream) {
+  if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
+  if (!windows) return KVQ_ERR_INVALID_ARGUMENT;
+  const int rc = check_windows(windows, windows->num_kv_heads);
+  if (rc) return rc;
+  if (num_tokens < 0 || num_tokens > INT32_MAX) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && (!k || !v || !seq_idx || !positions)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k) || !aligned16(v)) return KVQ_ERR_INVALID_ARGUMENT;
+  KVQ_TRY(launch_window_write(k, v, dtype, num_tokens, windows->num_kv_heads, seq_idx, positions, seq_lens,
+                              windows->num_seqs,
+                              static_cast<uint16_t *>(windows->sink_k), static_cast<uint16_t *>(windows->sink_v),
+                              static_cast<uint16_t *>(windows->recent_k), static_cast<uint16_t *>(windows->recent_v),
+                              windows->num_sink, windows->num_recent, stream));
+  return KVQ_OK;
+}
+
+double kvq_bits_per_element(int64_t seq_len, int32_t num_sink, int32_t num_recent) {
+  if (seq_len <= 0 || num_sink < 0 || num_recent < 0) return 0.0;
+  // window tokens: 128 bf16 per (head, side); INT2 tokens: 32 code bytes + fp16 scale and zero
+  const int64_t in_sink = seq_len < num_sink ? seq_len : num_sink;
+  const int64_t in_recent = seq_len - in_sink < num_recent ? seq_len - in_sink : num_recent;
+  const int64_t int2 = seq_len - in_sink - in_recent;
+  const double bits = static_cast<double>(int2) * (8.0 * (32 + 4)) + static_cast<double>(in_sink + in_recent) * 2048.0;
+  return bits / (static_cast<double>(seq_len) * 128.0);
 }
 
 size_t kvq_candidate_workspace_bytes(int64_t num_tokens, int32_t num_kv_heads, int32_t num_q_heads,

@@ -130,6 +130,12 @@ struct MfmaArgs {
   float *part;                // [rows][Hq][parts][132] partials, one per (split, wave) or per split
   int parts;                  // splits * 8, or splits when the waves' partials are merged first (premerge)
   int premerge;
+  // BF16 windows (decode with windows): sink [num_seqs][win_S][H][128] and
+  // recent [num_seqs][win_W][H][128] (position p in slot p % win_W), bf16;
+  // the window keys' centering win_mu [H][128] or null
+  const uint16_t *win_sk, *win_sv, *win_rk, *win_rv;
+  int win_S, win_W;
+  const float *win_mu;
   unsigned long long *counters;  // [num_seqs][H][n_rg][kArrivalWords] arrival counters
   uint32_t epoch;
   float *out_o, *ot;
@@ -167,7 +173,8 @@ __device__ __forceinline__ float load_partial(const float *p) {
 // (m, l, z) and the value sums come in batches of 16 partials, the first two
 // batches requested together with the statistics.  More partials: the
 // statistics in a lane loop, value sums in batches of 8 with their scales.
-__device__ __forceinline__ void merge_partials(const float *p, int parts, int lane, float &o0, float &o1) {
+__device__ __forceinline__ void merge_partials(const float *p, int parts, int lane, float &o0, float &o1,
+                                               float *m_out = nullptr, float *l_out = nullptr) {
   if (parts <= 64) {
     constexpr int kB = 16;
     float ma = -INFINITY, la = 0.0f, za = 0.0f;
@@ -215,6 +222,8 @@ __device__ __forceinline__ void merge_partials(const float *p, int parts, int la
     o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
     o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
     if (any_nan) o0 = o1 = __builtin_nanf("");
+    if (m_out) *m_out = mstar;
+    if (l_out) *l_out = l;
     return;
   }
   constexpr int kU = 8;
@@ -263,6 +272,8 @@ __device__ __forceinline__ void merge_partials(const float *p, int parts, int la
   o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
   o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
   if (any_nan) o0 = o1 = __builtin_nanf("");
+  if (m_out) *m_out = mstar;
+  if (l_out) *l_out = l;
 }
 
 // Device-scope store of a split partial (read by the merging workgroup).
@@ -453,11 +464,13 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     }
 }
 
-template <int DT, bool P16, bool kDense>
+constexpr int kWinChunks = kMaxWindowTokens / 64;  // chunks of 64 window tokens per sequence
+
+template <int DT, bool P16, bool kDense, bool kWin>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
-  __shared__ float red[kWaves][5][4 + D];  // per wave, per row: m, l, z, flag, acc[128]; row 4: unused stores
-  __shared__ float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
-  __shared__ float qs[4][D];               // q' of the group's rows
+  __shared__ __attribute__((aligned(16))) float red[kWaves][5][4 + D];  // per wave, per row: m, l, z, flag, acc[128]; row 4: unused stores
+  __shared__ __attribute__((aligned(16))) float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
+  __shared__ __attribute__((aligned(16))) float qs[4][D];               // q' of the group's rows
   __shared__ float qsum_s[4];
   __shared__ int qshift_s[4];              // fixed-point shift S of each row's digits
   __shared__ uint32_t digit_s[8][64];      // key-side A operand: dword [m][e] of each lane
@@ -485,8 +498,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   int L = a.seq_lens[b];
   bool bad = L < 0 || L > a.max_seq_len;
   if (bad) L = 0;
-  const int t_begin = s * a.split_tokens;
-  c.t_end = min(t_begin + a.split_tokens, L);
+  // INT2 positions [lo, hi): with windows the sink [0, lo) and the recent
+  // tokens [hi, L) are read from the BF16 windows in the merge
+  int lo = 0, hi = L;
+  if constexpr (kWin) {
+    lo = min(a.win_S, L);
+    hi = max(lo, L - a.win_W);
+  }
+  const int t_begin = max(s * a.split_tokens, lo);
+  c.t_end = min(s * a.split_tokens + a.split_tokens, hi);
   c.last_tile = c.t_end > t_begin ? (c.t_end - 1) / 16 : 0;  // (empty split: loads read tile 0, unused)
   c.ptab = a.ptab + static_cast<size_t>(b) * a.tab_stride;
   c.pg_base = b * a.base_mul;
@@ -800,6 +820,119 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_valid, a.epoch, a.splits) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
+  if constexpr (kWin) {
+    // ---- BF16 windows of this sequence and KV head, in fp32: the sink
+    // [0, lo) and the recent tokens [hi, L) against the group's raw query
+    // rows.  Result: per row the base-2 running max and sum (wave r holds
+    // row r) and the weighted values (thread (r, d) = (tid / 128, tid % 128)),
+    // left in LDS for the combination below.  All window loads are issued
+    // at once; each chunk of 64 tokens: logits from the keys in registers
+    // (a token's 16 lanes sum its 128 dims), values through LDS.
+    const int tid = threadIdx.x;
+    const int n_sink = lo, n_win = lo + (L - hi);
+    const size_t hstride = static_cast<size_t>(a.H) * D;  // elements between window tokens
+    const uint16_t *skb = a.win_sk + static_cast<size_t>(b) * a.win_S * hstride + static_cast<size_t>(h) * D;
+    const uint16_t *svb = a.win_sv + static_cast<size_t>(b) * a.win_S * hstride + static_cast<size_t>(h) * D;
+    const uint16_t *rkb = a.win_rk + static_cast<size_t>(b) * a.win_W * hstride + static_cast<size_t>(h) * D;
+    const uint16_t *rvb = a.win_rv + static_cast<size_t>(b) * a.win_W * hstride + static_cast<size_t>(h) * D;
+    uint4 wk[kWinChunks][2], wv[kWinChunks][2];
+#pragma unroll
+    for (int ch = 0; ch < kWinChunks; ++ch)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int idx = tid + 64 * kWaves * e, u = 64 * ch + (idx >> 4), part = idx & 15;
+        wk[ch][e] = wv[ch][e] = uint4{0u, 0u, 0u, 0u};
+        if (u < n_win) {
+          const bool sink = u < n_sink;
+          const size_t off = (sink ? static_cast<size_t>(u) : static_cast<size_t>((hi + u - n_sink) % a.win_W)) *
+                                 hstride + 8 * part;
+          wk[ch][e] = *reinterpret_cast<const uint4 *>((sink ? skb : rkb) + off);
+          wv[ch][e] = *reinterpret_cast<const uint4 *>((sink ? svb : rvb) + off);
+        }
+      }
+    // raw query rows scaled to base-2 logits (rows past the last: zero), and q . mu
+    float *qmu_s = &red[0][4][0];   // [8]: halves of q . mu per row
+    float *mlw_s = &red[0][4][16];  // [8]: window m (4), l (4) per row
+    float *xw = &red[1][0][0];      // [4][64]: logits, then weights, of a chunk
+    float *alw = &red[2][0][0];     // [4]: rescale factor of a chunk per row
+    float *vbuf = &facc_all[0][0];  // [64][128]: values of a chunk (fp32)
+    {
+      const int r = tid >> 7, i = tid & 127;
+      float x = 0.0f;
+      if (r < nrows) {
+        const int rr = row0 + r;
+        const size_t rj = (static_cast<size_t>(b) * a.Nq + rr / a.G) * a.Hq + h * a.G + rr % a.G;
+        x = DT == KVQ_F32 ? static_cast<const float *>(a.q)[rj * D + i]
+                          : __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(a.q)[rj * D + i]) << 16);
+        x *= kLog2eF * kInvSqrtD;
+      }
+      qs[r][i] = x;
+      const float qm = wave_sum(a.win_mu ? x * a.win_mu[static_cast<size_t>(h) * D + i] : 0.0f);
+      if (lane == 0) qmu_s[wave] = qm;
+    }
+    float m_run = -INFINITY, l_run = 0.0f, acc = 0.0f;
+    const int ar = tid >> 7, ad = tid & 127;
+    const int nch = (n_win + 63) / 64;
+#pragma unroll
+    for (int ch = 0; ch < kWinChunks; ++ch) {
+      if (ch >= nch) break;
+      __syncthreads();  // (qs, q . mu written; the previous chunk's LDS reads done)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int idx = tid + 64 * kWaves * e, tok = idx >> 4, part = idx & 15;
+        const uint4 w = wv[ch][e];
+        float4 *dst = reinterpret_cast<float4 *>(vbuf + tok * D + 8 * part);
+        dst[0] = float4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                        __uint_as_float(w.y & 0xFFFF0000u)};
+        dst[1] = float4{__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u), __uint_as_float(w.w << 16),
+                        __uint_as_float(w.w & 0xFFFF0000u)};
+        const uint4 kq = wk[ch][e];
+        const float kf[8] = {__uint_as_float(kq.x << 16), __uint_as_float(kq.x & 0xFFFF0000u),
+                             __uint_as_float(kq.y << 16), __uint_as_float(kq.y & 0xFFFF0000u),
+                             __uint_as_float(kq.z << 16), __uint_as_float(kq.z & 0xFFFF0000u),
+                             __uint_as_float(kq.w << 16), __uint_as_float(kq.w & 0xFFFF0000u)};
+        float dot[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float d = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) d += qs[r][8 * part + j] * kf[j];
+          d += __shfl_xor(d, 1);
+          d += __shfl_xor(d, 2);
+          d += __shfl_xor(d, 4);
+          d += __shfl_xor(d, 8);
+          dot[r] = d;
+        }
+        if (part == 0) {
+          const bool ok = 64 * ch + tok < n_win;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xw[r * 64 + tok] = ok ? dot[r] - (qmu_s[2 * r] + qmu_s[2 * r + 1]) : -INFINITY;
+        }
+      }
+      __syncthreads();
+      if (wave < 4) {  // online softmax of row `wave`, lane = token of the chunk
+        const float x = xw[wave * 64 + lane];
+        const float mn = fmaxf(m_run, wave_maxf(x));  // finite: the chunk holds a token
+        const float al = exp2f(m_run - mn);
+        const float pv = exp2f(x - mn);
+        l_run = l_run * al + wave_sum(pv);
+        m_run = mn;
+        xw[wave * 64 + lane] = pv;
+        if (lane == 0) alw[wave] = al;
+      }
+      __syncthreads();
+      acc *= alw[ar];
+#pragma unroll 8
+      for (int t = 0; t < 64; ++t) acc += xw[ar * 64 + t] * vbuf[t * D + ad];
+    }
+    __syncthreads();  // (all reads of qs, xw, vbuf done)
+    qs[ar][ad] = acc;
+    if (wave < 4 && lane == 0) {
+      mlw_s[wave] = m_run;
+      mlw_s[4 + wave] = l_run;
+    }
+    __syncthreads();
+  }
   // dense R_V: the head's matrix is staged in LDS by the whole workgroup
   // (its loads go out together with the merge's)
   const bool vdense = a.rv.kind == KVQ_ROT_DENSE;
@@ -819,8 +952,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   }
   const int qq = (row0 + min(wave, nrows - 1)) / a.G, j = h * a.G + (row0 + min(wave, nrows - 1)) % a.G;
   const size_t row = static_cast<size_t>(b) * a.Nq + qq;
-  float o0 = 0.0f, o1 = 0.0f;
-  if (wave < nrows) merge_partials(a.part + (row * a.Hq + j) * a.parts * (D + 4), a.parts, lane, o0, o1);
+  float o0 = 0.0f, o1 = 0.0f, mi = -INFINITY, li = 0.0f;
+  if (wave < nrows) merge_partials(a.part + (row * a.Hq + j) * a.parts * (D + 4), a.parts, lane, o0, o1, &mi, &li);
   if (vdense) {
     float4 *rd = reinterpret_cast<float4 *>(rs) + threadIdx.x;
     rd[0] = v0;
@@ -854,6 +987,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   } else if (wave < nrows) {
     unrotate_value_wave(o0, o1, a.rv, h, lane);
   }
+  if constexpr (kWin) {
+    // o = (2^(m_int2 - M) (o_int2 l_int2) + 2^(m_win - M) acc_win) / (2^(m_int2 - M) l_int2 + 2^(m_win - M) l_win),
+    // both parts in the unrotated domain (o_int2 normalized by its sum l_int2; NaN stays NaN)
+    if (wave < nrows) {
+      const float mw = red[0][4][16 + wave], lw = red[0][4][20 + wave];
+      const float M = fmaxf(mi, mw);
+      if (M == -INFINITY) {
+        o0 = o1 = o0 != o0 ? o0 : 0.0f;
+      } else {
+        const float w1 = (mi == -INFINITY ? 0.0f : exp2f(mi - M)) * li;
+        const float w2 = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+        const float den = w1 + w2 * lw;
+        o0 = (w1 * o0 + w2 * qs[wave][lane]) / den;
+        o1 = (w1 * o1 + w2 * qs[wave][lane + 64]) / den;
+      }
+    }
+  }
   if (wave < nrows) store_output_wave(a.out_o, a.ot, row, j, a.Hq, lane, o0, o1);
 }
 
@@ -867,7 +1017,7 @@ bool decode_mfma_supported(const DecodePlan &pl, int page_size) {
 hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, RotDev rk, RotDev rv,
                               const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
                               int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
-                              float *out_o, float *ot, hipStream_t stream) {
+                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win) {
   if (pl.num_seqs == 0) return hipSuccess;
   const uint32_t epoch = next_launch_epoch();
   MfmaArgs a{};
@@ -908,25 +1058,40 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.epoch = epoch;
   a.out_o = out_o;
   a.ot = ot;
+  if (win) {
+    a.win_sk = win->sink_k;
+    a.win_sv = win->sink_v;
+    a.win_rk = win->recent_k;
+    a.win_rv = win->recent_v;
+    a.win_S = win->num_sink;
+    a.win_W = win->num_recent;
+    a.win_mu = win->key_mean;
+  }
   const dim3 grid(pl.splits, pl.H * a.n_rg, pl.num_seqs);
   const bool f32 = dtype == KVQ_F32 || rk.kind == kRotPrescaled;
   const bool dense = rk.kind == KVQ_ROT_DENSE;
   const dim3 block(64 * kWaves);
-#define KVQ_DECODE_LAUNCH(F32, P16, DENSE)                                                                     \
-  hipLaunchKernelGGL((decode_mfma_kernel<(F32) ? KVQ_F32 : KVQ_BF16, P16, DENSE>), grid, block, 0, stream, a)
+#define KVQ_DECODE_LAUNCH(F32, P16, DENSE, WIN)                                                                \
+  hipLaunchKernelGGL((decode_mfma_kernel<(F32) ? KVQ_F32 : KVQ_BF16, P16, DENSE, WIN>), grid, block, 0, stream, a)
+#define KVQ_DECODE_LAUNCH_W(F32, P16, DENSE)              \
+  do {                                                    \
+    if (win) KVQ_DECODE_LAUNCH(F32, P16, DENSE, true);    \
+    else KVQ_DECODE_LAUNCH(F32, P16, DENSE, false);       \
+  } while (0)
   if (page_size == 16) {
     if (dense) {
-      if (f32) KVQ_DECODE_LAUNCH(true, true, true); else KVQ_DECODE_LAUNCH(false, true, true);
+      if (f32) KVQ_DECODE_LAUNCH_W(true, true, true); else KVQ_DECODE_LAUNCH_W(false, true, true);
     } else {
-      if (f32) KVQ_DECODE_LAUNCH(true, true, false); else KVQ_DECODE_LAUNCH(false, true, false);
+      if (f32) KVQ_DECODE_LAUNCH_W(true, true, false); else KVQ_DECODE_LAUNCH_W(false, true, false);
     }
   } else {
     if (dense) {
-      if (f32) KVQ_DECODE_LAUNCH(true, false, true); else KVQ_DECODE_LAUNCH(false, false, true);
+      if (f32) KVQ_DECODE_LAUNCH_W(true, false, true); else KVQ_DECODE_LAUNCH_W(false, false, true);
     } else {
-      if (f32) KVQ_DECODE_LAUNCH(true, false, false); else KVQ_DECODE_LAUNCH(false, false, false);
+      if (f32) KVQ_DECODE_LAUNCH_W(true, false, false); else KVQ_DECODE_LAUNCH_W(false, false, false);
     }
   }
+#undef KVQ_DECODE_LAUNCH_W
 #undef KVQ_DECODE_LAUNCH
   return hipGetLastError();
 }

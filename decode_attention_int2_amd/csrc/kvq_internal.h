@@ -318,10 +318,17 @@ hipError_t launch_decode_split(const DecodePlan &pl, const uint8_t *pages, int64
 // group); `epoch` tags this launch's arrivals (counters of another epoch
 // count as zero; the last arrival leaves its counter at zero arrivals).
 bool decode_mfma_supported(const DecodePlan &pl, int page_size);
+// BF16 sink and recent windows of a decode (device pointers, bf16 bits).
+struct WindowDev {
+  const uint16_t *sink_k, *sink_v, *recent_k, *recent_v;
+  int num_sink, num_recent;
+  const float *key_mean;
+};
+constexpr int kMaxWindowTokens = 384;  // num_sink + num_recent (the merge holds them in registers)
 hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, RotDev rk, RotDev rv,
                               const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
                               int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
-                              float *out_o, float *ot, hipStream_t stream);
+                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win = nullptr);
 // Split-K partial attention over raw (unquantized, unrotated) K and V that
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
@@ -339,6 +346,11 @@ int wo_kslices(int K);          // K slices of the W_O projection
 int wo_col_blocks(int d_model); // column blocks of the W_O projection
 
 // Candidate search helpers.
+hipError_t launch_window_write(const void *k, const void *v, int dtype, int64_t num_tokens, int H,
+                               const int32_t *seq_idx, const int32_t *positions, const int32_t *seq_lens,
+                               int num_seqs, uint16_t *sink_k,
+                               uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v, int num_sink,
+                               int num_recent, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t *p, int32_t value, int n, hipStream_t stream);
 // Post-W_O NMSE through the Gram matrix of W_O (see candidate.hip):
 // prepare once per search (Gram blocks and the reference output's norms),

@@ -22,6 +22,7 @@ KVQ_SELECT_JOINT, KVQ_SELECT_PER_HEAD = 0, 1
 HEAD_DIM = 128
 
 EXPORTED = ("kvq_cache_bytes", "kvq_quantize", "kvq_decode_workspace_bytes", "kvq_decode_attn",
+            "kvq_window_write", "kvq_decode_attn_windows", "kvq_bits_per_element",
             "kvq_candidate_workspace_bytes", "kvq_candidate_nmse", "kvq_status_string", "kvq_version")
 
 
@@ -69,6 +70,13 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_candidate_nmse.argtypes = [P, P, P, i32, i64, i32, i32, i32, P, i32, P, i32, P, P, i32, i32, P, P, P, P,
                                        sz, P]
     lib.kvq_candidate_nmse.restype = ctypes.c_int
+    lib.kvq_window_write.argtypes = [P, P, i32, i64, P, P, P, P, P]
+    lib.kvq_window_write.restype = ctypes.c_int
+    lib.kvq_decode_attn_windows.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, i32, P, P, P, P, P, i32, P, P, P, sz,
+                                            i32, P]
+    lib.kvq_decode_attn_windows.restype = ctypes.c_int
+    lib.kvq_bits_per_element.argtypes = [i64, i32, i32]
+    lib.kvq_bits_per_element.restype = ctypes.c_double
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
@@ -181,6 +189,65 @@ def kvq_decode_attn(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache:
                                max_seq_len, ctypes.byref(rk), ctypes.byref(rv), _dev_ptr(w_o, "w_o"), d_model,
                                _dev_ptr(out_o, "out_o"), _dev_ptr(out_y, "out_y"), _dev_ptr(workspace, "workspace"),
                                ws_bytes, num_splits, ev, _stream(stream)), "kvq_decode_attn")
+
+
+class _Windows(ctypes.Structure):
+    _fields_ = [("sink_k", ctypes.c_void_p), ("sink_v", ctypes.c_void_p), ("recent_k", ctypes.c_void_p),
+                ("recent_v", ctypes.c_void_p), ("num_seqs", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("num_sink", ctypes.c_int32), ("num_recent", ctypes.c_int32)]
+
+
+class Windows:
+    """kvq_windows: BF16 sink [num_seqs][num_sink][H][128] and recent [num_seqs][num_recent][H][128]
+    (position p in slot p % num_recent) buffers on the GPU."""
+
+    def __init__(self, num_seqs: int, num_kv_heads: int, num_sink: int = 64, num_recent: int = 256, device="cuda"):
+        self.num_seqs, self.num_kv_heads = int(num_seqs), int(num_kv_heads)
+        self.num_sink, self.num_recent = int(num_sink), int(num_recent)
+        shape_s = (self.num_seqs, self.num_sink, self.num_kv_heads, 128)
+        shape_r = (self.num_seqs, self.num_recent, self.num_kv_heads, 128)
+        self.sink_k = torch.zeros(shape_s, dtype=torch.bfloat16, device=device)
+        self.sink_v = torch.zeros(shape_s, dtype=torch.bfloat16, device=device)
+        self.recent_k = torch.zeros(shape_r, dtype=torch.bfloat16, device=device)
+        self.recent_v = torch.zeros(shape_r, dtype=torch.bfloat16, device=device)
+
+    def _c(self):
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+        return _Windows(ptr(self.sink_k), ptr(self.sink_v), ptr(self.recent_k), ptr(self.recent_v), self.num_seqs,
+                        self.num_kv_heads, self.num_sink, self.num_recent)
+
+
+def kvq_window_write(k: torch.Tensor, v: torch.Tensor, seq_idx: torch.Tensor, positions: torch.Tensor,
+                     windows: Windows, seq_lens: Optional[torch.Tensor] = None, stream=None) -> None:
+    w = windows._c()
+    _check(load_library().kvq_window_write(_dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k), k.shape[0],
+                                           _dev_ptr(seq_idx, "seq_idx"), _dev_ptr(positions, "positions"),
+                                           _dev_ptr(seq_lens, "seq_lens"), ctypes.byref(w), _stream(stream)),
+           "kvq_window_write")
+
+
+def kvq_decode_attn_windows(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache: Cache,
+                            page_table: Optional[torch.Tensor], max_pages_per_seq: int, seq_lens: torch.Tensor,
+                            max_seq_len: int, rot_k: Rotation, rot_v: Rotation, windows: Windows,
+                            out_o: torch.Tensor, key_mean: Optional[torch.Tensor] = None,
+                            w_o: Optional[torch.Tensor] = None, out_y: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None) -> None:
+    lib = load_library()
+    Hq = q.shape[1]
+    d_model = int(w_o.shape[1]) if w_o is not None else 0
+    c, rk, rv, w = cache._c(), rot_k._c(), rot_v._c(), windows._c()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.kvq_decode_attn_windows(_dev_ptr(q, "q"), _dtype_code(q), num_seqs, queries_per_seq, Hq,
+                                       ctypes.byref(c), _dev_ptr(page_table, "page_table"), max_pages_per_seq,
+                                       _dev_ptr(seq_lens, "seq_lens"), max_seq_len, ctypes.byref(rk),
+                                       ctypes.byref(rv), ctypes.byref(w), _dev_ptr(key_mean, "key_mean"),
+                                       _dev_ptr(w_o, "w_o"), d_model, _dev_ptr(out_o, "out_o"),
+                                       _dev_ptr(out_y, "out_y"), _dev_ptr(workspace, "workspace"), ws_bytes,
+                                       num_splits, _stream(stream)), "kvq_decode_attn_windows")
+
+
+def kvq_bits_per_element(seq_len: int, num_sink: int = 64, num_recent: int = 256) -> float:
+    return float(load_library().kvq_bits_per_element(seq_len, num_sink, num_recent))
 
 
 def kvq_candidate_workspace_bytes(num_tokens: int, num_kv_heads: int, num_q_heads: int, num_queries: int,

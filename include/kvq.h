@@ -189,6 +189,67 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
                     hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * BF16 sink and recent windows ([OptR] §5, implementation details: 64 sink
+ * and 256 recent tokens stay in BF16, 2.32 bits per element at a 64K-token
+ * context; §4: sink and recent tokens skip INT2 quantization, their keys
+ * keep the same centering, their values stay unchanged in BF16).
+ *
+ * For a sequence of length L: positions [0, lo), lo = min(num_sink, L), are
+ * sink tokens; positions [hi, L), hi = max(lo, L - num_recent), are recent
+ * tokens; positions [lo, hi) are read from the INT2 cache.  A window token's
+ * logit is q . (k - key_mean) / sqrt(128) (key_mean as at the cache write,
+ * or none) and its value is v itself; one softmax covers all L positions.
+ *
+ *   sink_k, sink_v      bf16 [num_seqs][num_sink][H][128]
+ *   recent_k, recent_v  bf16 [num_seqs][num_recent][H][128]: the token at
+ *                       position p sits in slot p % num_recent (a ring: a
+ *                       position leaves it when position p + num_recent is
+ *                       written, by which time it has left the window)
+ * Buffers are owned by the caller; pointers may be NULL for a size of zero.
+ * Limits: num_sink % 16 == 0 and num_sink + num_recent <= 384.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  void *sink_k, *sink_v;
+  void *recent_k, *recent_v;
+  int32_t num_seqs, num_kv_heads, num_sink, num_recent;
+} kvq_windows;
+
+/* Window write: token i (of num_tokens, k and v [num_tokens][H][128] in
+ * dtype) of sequence seq_idx[i] at position positions[i] goes to the sink
+ * when the position is below num_sink, else to its recent slot (skipped
+ * when num_recent == 0); fp32 inputs are rounded to bf16 (nearest even).
+ * seq_idx and positions are device int32 [num_tokens]; a token whose
+ * sequence is outside [0, num_seqs) or whose position is negative is
+ * skipped.  seq_lens (device int32 [num_seqs], or NULL) is each sequence's
+ * length once this write is done: a token at or past it is skipped, and a
+ * non-sink token goes to the ring only when its position is at least
+ * seq_lens[b] - num_recent, so one call can
+ * carry a whole prefill; with NULL every non-sink token goes to its slot, and
+ * two tokens of one call must not share a slot (which of them the slot keeps
+ * is then undefined).  INT2 codes are written by kvq_quantize as before
+ * (positions in the windows may be written there too; the decode does not
+ * read them). */
+int kvq_window_write(const void *k, const void *v, int32_t dtype, int64_t num_tokens, const int32_t *seq_idx,
+                     const int32_t *positions, const int32_t *seq_lens, const kvq_windows *windows,
+                     hipStream_t stream);
+
+/* kvq_decode_attn with the windows: the same arguments and workspace, plus
+ * the windows (H = the cache's KV heads) and the keys' centering key_mean
+ * (fp32 [H][128] or NULL, as given to kvq_quantize).  Returns UNSUPPORTED
+ * for page sizes that are not a power of two. */
+int kvq_decode_attn_windows(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,
+                            int32_t num_q_heads, const kvq_cache *cache, const int32_t *page_table,
+                            int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                            const kvq_rotation *rot_k, const kvq_rotation *rot_v, const kvq_windows *windows,
+                            const float *key_mean, const void *w_o, int32_t d_model, float *out_o, float *out_y,
+                            void *workspace, size_t workspace_bytes, int32_t num_splits, hipStream_t stream);
+
+/* Bits per cached element of one sequence of length L with the windows: INT2
+ * tokens 2.25 (2-bit codes and an fp16 scale and zero per 128), window tokens
+ * 16 (host function). */
+double kvq_bits_per_element(int64_t seq_len, int32_t num_sink, int32_t num_recent);
+
+/* ---------------------------------------------------------------------------
  * kvq_candidate_nmse -- batched post-W_O NMSE over a grid of candidate
  * rotations and clip ratios, and selection of the best one ([Eval], observed
  * envelope: identity + signed-Hadamard candidates x clip grid, chosen by

@@ -75,7 +75,7 @@ def _load():
                                             P, P, P]
         lib.kvqo_f32_to_bf16.argtypes = [F]
         lib.kvqo_f32_to_bf16.restype = ctypes.c_uint16
-        lib.kvqo_window_write.argtypes = [P, P, i64, i32, P, P, i32, P, P, P, P, i32, i32]
+        lib.kvqo_window_write.argtypes = [P, P, i64, i32, P, P, P, i32, P, P, P, P, i32, i32]
         lib.kvqo_decode_windows_f64.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P, P]
         lib.kvqo_bits_per_element.argtypes = [i64, i32, i32]
         lib.kvqo_bits_per_element.restype = ctypes.c_double
@@ -247,12 +247,14 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     return np.array([f(float(e)) for e in x.ravel()], np.uint16).reshape(x.shape)
 
 
-def window_write(k, v, seq_idx, positions, windows: Windows):
+def window_write(k, v, seq_idx, positions, windows: Windows, seq_lens=None):
     k, v = _f32(k), _f32(v)
     si = np.ascontiguousarray(seq_idx, np.int32)
     ps = np.ascontiguousarray(positions, np.int32)
+    sl = None if seq_lens is None else np.ascontiguousarray(seq_lens, np.int32)
     w = windows
-    _check(_load().kvqo_window_write(_ptr(k), _ptr(v), k.shape[0], k.shape[1], _ptr(si), _ptr(ps), w.num_seqs,
+    _check(_load().kvqo_window_write(_ptr(k), _ptr(v), k.shape[0], k.shape[1], _ptr(si), _ptr(ps), _ptr(sl),
+                                     w.num_seqs,
                                      _ptr(w.sink_k), _ptr(w.sink_v), _ptr(w.recent_k), _ptr(w.recent_v),
                                      w.num_sink, w.num_recent), "window_write")
 

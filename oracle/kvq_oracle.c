@@ -658,7 +658,8 @@ static double bf16_to_f64(uint16_t b) {
 }
 
 int kvqo_window_write(const float *k, const float *v, int64_t num_tokens, int32_t num_kv_heads,
-                      const int32_t *seq_idx, const int32_t *positions, int32_t num_seqs, uint16_t *sink_k,
+                      const int32_t *seq_idx, const int32_t *positions, const int32_t *seq_lens, int32_t num_seqs,
+                      uint16_t *sink_k,
                       uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v, int32_t num_sink,
                       int32_t num_recent) {
   const int d = KVQO_D;
@@ -667,12 +668,12 @@ int kvqo_window_write(const float *k, const float *v, int64_t num_tokens, int32_
   if ((num_sink > 0 && (!sink_k || !sink_v)) || (num_recent > 0 && (!recent_k || !recent_v))) return KVQO_ERR_ARG;
   for (int64_t i = 0; i < num_tokens; ++i) {
     const int32_t b = seq_idx[i], p = positions[i];
-    if (b < 0 || b >= num_seqs || p < 0) continue;
+    if (b < 0 || b >= num_seqs || p < 0 || (seq_lens && p >= seq_lens[b])) continue;
     uint16_t *dk, *dv;
     if (p < num_sink) {
       dk = sink_k + ((size_t)b * num_sink + p) * num_kv_heads * d;
       dv = sink_v + ((size_t)b * num_sink + p) * num_kv_heads * d;
-    } else if (num_recent > 0) {
+    } else if (num_recent > 0 && (!seq_lens || p >= seq_lens[b] - num_recent)) {
       dk = recent_k + ((size_t)b * num_recent + p % num_recent) * num_kv_heads * d;
       dv = recent_v + ((size_t)b * num_recent + p % num_recent) * num_kv_heads * d;
     } else {

@@ -147,10 +147,13 @@ uint16_t kvqo_f32_to_bf16(float x);
 /* Window write of num_tokens tokens [num_tokens][H][128] (fp32; bf16 inputs
  * widened): token i of sequence seq_idx[i] at position positions[i] goes to
  * the sink when the position is below num_sink, else to recent slot
- * position % num_recent (when num_recent > 0); out-of-range indices are
- * skipped. */
+ * position % num_recent (when num_recent > 0; with seq_lens, the lengths
+ * after the write, only when position >= seq_lens[b] - num_recent, and a
+ * position at or past seq_lens[b] is not written); tokens are written in
+ * index order; out-of-range indices are skipped. */
 int kvqo_window_write(const float *k, const float *v, int64_t num_tokens, int32_t num_kv_heads,
-                      const int32_t *seq_idx, const int32_t *positions, int32_t num_seqs, uint16_t *sink_k,
+                      const int32_t *seq_idx, const int32_t *positions, const int32_t *seq_lens, int32_t num_seqs,
+                      uint16_t *sink_k,
                       uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v, int32_t num_sink,
                       int32_t num_recent);
 

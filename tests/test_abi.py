@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared():
     hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char \*)\s*(kvq_\w+)\s*\(", hdr, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|double|const char \*)\s*(kvq_\w+)\s*\(", hdr, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -135,3 +135,41 @@ def test_candidate_validation(lib):
     for bad in ("k", "v", "q", "wo"):
         assert call2(**{bad: ctypes.c_void_p(0x2008)}) == 1          # not 16-byte aligned
     assert call2(H=2, Hq=128, nq=1, mode=0) == 2                      # JOINT with more than 64 query heads
+
+
+def test_window_validation(lib):
+    """Window entry points reject bad descriptors before any launch."""
+    from decode_attention_int2_amd.kvq import _Windows
+    fake = ctypes.c_void_p(0x2000)
+    good = _Windows(fake, fake, fake, fake, 2, 2, 64, 256)
+    seq = pos = fake
+    # window write: unknown dtype, null descriptor, sink not a multiple of 16, too many window tokens,
+    # unaligned buffers, negative token count
+    assert lib.kvq_window_write(fake, fake, 7, 4, seq, pos, None, ctypes.byref(good), None) == 2
+    assert lib.kvq_window_write(fake, fake, 1, 4, seq, pos, None, None, None) == 1
+    assert lib.kvq_window_write(fake, fake, 1, 4, seq, pos, None,
+                                ctypes.byref(_Windows(fake, fake, fake, fake, 2, 2, 8, 0)), None) == 2
+    assert lib.kvq_window_write(fake, fake, 1, 4, seq, pos, None,
+                                ctypes.byref(_Windows(fake, fake, fake, fake, 2, 2, 64, 336)), None) == 2
+    assert lib.kvq_window_write(fake, fake, 1, 4, seq, pos, None,
+                                ctypes.byref(_Windows(ctypes.c_void_p(0x2008), fake, fake, fake, 2, 2, 64, 256)),
+                                None) == 1
+    assert lib.kvq_window_write(fake, fake, 1, -1, seq, pos, None, ctypes.byref(good), None) == 1
+    assert lib.kvq_window_write(None, None, 1, 0, None, None, None, ctypes.byref(good), None) == 0   # nothing to do
+    # decode with windows: head count must match the cache, and the windows must cover num_seqs
+    c = _cache(pages=4, H=2)
+    r = _rot()
+    call = lambda w: lib.kvq_decode_attn_windows(fake, 1, 1, 1, 4, ctypes.byref(c), fake, 4, fake, 64, ctypes.byref(r),
+                                                 ctypes.byref(r), w, None, None, 0, fake, None, fake, 1 << 30, 0,
+                                                 None)
+    assert call(None) == 1
+    assert call(ctypes.byref(_Windows(fake, fake, fake, fake, 1, 3, 64, 256))) == 1
+    assert call(ctypes.byref(_Windows(fake, fake, fake, fake, 1, 2, 40, 0))) == 2            # sink % 16 != 0
+
+
+def test_bits_per_element_closed_form(lib):
+    """2.32 bits per element at 64K with 64 + 256 BF16 tokens (host function)."""
+    assert lib.kvq_bits_per_element(65536, 64, 256) == 151856 / 65536
+    assert round(lib.kvq_bits_per_element(65536, 64, 256), 2) == 2.32
+    assert lib.kvq_bits_per_element(320, 64, 256) == 16.0
+    assert lib.kvq_bits_per_element(4096, 0, 0) == 2.25
