@@ -325,6 +325,33 @@ def main():
 
     traffic = measured_traffic(a.traffic_json)
 
+    # the same decode with 64 sink and 256 recent BF16 tokens per sequence
+    # (INT2 for the rest): algorithmic bytes = INT2 bytes of the middle + bf16
+    # K and V of the windows
+    windows = None
+    if not a.no_other_workloads:
+        S_w, W_w = 64, 256
+        seq_idx = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T)
+        pos = torch.arange(T, dtype=torch.int32, device=dev).repeat(B)
+        gws = []
+        for i in range(NC):
+            gw = kvq.Windows(B, H, S_w, W_w, device=dev)
+            kvq.kvq_window_write(w.k, w.v, seq_idx, pos, gw, seq_lens=w.seq_lens)
+            gws.append(gw)
+        wr_ms = median_of(lambda: timed(lambda i: kvq.kvq_window_write(w.k, w.v, seq_idx, pos, gws[i % NC],
+                                                                        seq_lens=w.seq_lens), 5))
+        dec_w = lambda i: kvq.kvq_decode_attn_windows(w.q, B, 1, caches[i % NC], w.page_table, max_pages, w.seq_lens,
+                                                      T, rot, rot, gws[i % NC], out_o, workspace=ws,
+                                                      num_splits=a.num_splits)
+        win_ms = median_of(lambda: timed(dec_w, 50))
+        win_bytes = B * H * ((T - S_w - W_w) * BYTES_PER_TOKEN_HEAD + (S_w + W_w) * 2 * 128 * 2)
+        windows = {"num_sink": S_w, "num_recent": W_w, "decode_attn_us": round(win_ms * 1e3, 2),
+                   "algorithmic_bytes": win_bytes, "gbs": round(win_bytes / (win_ms * 1e-3) / 1e9, 1),
+                   "pct_hbm_peak": round(100.0 * win_bytes / (win_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                   "bits_per_element": round(kvq.kvq_bits_per_element(T, S_w, W_w), 4),
+                   "window_write_us_all_tokens": round(wr_ms * 1e3, 2)}
+        del gws
+
     clip_k, clip_v, desc = w.clip_k, w.clip_v, synthetic.DESCRIPTIONS[WORKLOAD]
     w_cpu = None
     if not a.no_cpu_baseline:   # the oracle's sample: 2 of the 16 sequences, copied to the host
@@ -382,6 +409,7 @@ def main():
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_mfma_kernel", "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": base,
+        "bf16_windows": windows,
         "other_decode_workloads": others,
         "calibration_search": cal,
     }
