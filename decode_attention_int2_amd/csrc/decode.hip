@@ -391,8 +391,8 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   pl.off_qsum = off;
   off = align(off + rows * Hq * sizeof(float));
   pl.off_part = off;
-  // (the matrix-core kernel writes one partial per (split, wave))
-  off = align(off + rows * Hq * static_cast<size_t>(pl.splits) * kMfmaWaves * (D + 4) * sizeof(float));
+  // (the matrix-core kernel writes one partial per (split, wave), and one per split for the BF16 windows)
+  off = align(off + rows * Hq * static_cast<size_t>(pl.splits) * (kMfmaWaves + 1) * (D + 4) * sizeof(float));
   pl.off_ypart = off;
   off = align(off + (d_model > 0 && ks > 1 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
   pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection

@@ -129,6 +129,7 @@ struct MfmaArgs {
   RotDev rk, rv;
   float *part;                // [rows][Hq][parts][132] partials, one per (split, wave) or per split
   int parts;                  // splits * 8, or splits when the waves' partials are merged first (premerge)
+  int pstride;                // partial slots per (row, head): parts, plus one window slot per split
   int premerge;
   // BF16 windows (decode with windows): sink [num_seqs][win_S][H][128] and
   // recent [num_seqs][win_W][H][128] (position p in slot p % win_W), bf16;
@@ -464,7 +465,32 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     }
 }
 
-constexpr int kWinChunks = kMaxWindowTokens / 64;  // chunks of 64 window tokens per sequence
+constexpr int kWinBatch = 3;  // window chunks of 64 tokens held in registers at once
+
+// Loads of the window tokens [u0, min(u1, u0 + 64 kWinBatch)) of sequence b,
+// KV head h (token u: sink position u when u < n_sink, else recent position
+// hi + u - n_sink in slot position % win_W): thread t takes 16 bytes (8
+// dims) of tokens 64 ch + t / 16 and 64 ch + 32 + t / 16; zero past u1.
+__device__ __forceinline__ void load_window_batch(const MfmaArgs &a, int b, int h, int u0, int u1, int n_sink, int hi,
+                                                  uint4 (&wk)[kWinBatch][2], uint4 (&wv)[kWinBatch][2]) {
+  const size_t hstride = static_cast<size_t>(a.H) * D;  // elements between window tokens
+  const size_t hoff = static_cast<size_t>(h) * D;
+#pragma unroll
+  for (int ch = 0; ch < kWinBatch; ++ch)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = threadIdx.x + 64 * kWaves * e, u = u0 + 64 * ch + (idx >> 4), part = idx & 15;
+      wk[ch][e] = wv[ch][e] = uint4{0u, 0u, 0u, 0u};
+      if (u < u1) {
+        const bool sink = u < n_sink;
+        const size_t tok = sink ? static_cast<size_t>(b) * a.win_S + u
+                                : static_cast<size_t>(b) * a.win_W + (hi + u - n_sink) % a.win_W;
+        const size_t off = tok * hstride + hoff + 8 * part;
+        wk[ch][e] = *reinterpret_cast<const uint4 *>((sink ? a.win_sk : a.win_rk) + off);
+        wv[ch][e] = *reinterpret_cast<const uint4 *>((sink ? a.win_sv : a.win_rv) + off);
+      }
+    }
+}
 
 template <int DT, bool P16, bool kDense, bool kWin>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
@@ -537,6 +563,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     const int8_t *sp = a.rk.kind == KVQ_ROT_SIGNED_HADAMARD ? a.rk.signs + h * D : static_cast<const int8_t *>(a.q);
     sb0 = sp[lane];
     sb1 = sp[lane + 64];
+  }
+  // BF16 windows: this split's slice [wu0, wu1) of the window tokens (sink
+  // positions [0, lo), then recent positions [hi, L)), in chunks of 64; the
+  // first kWinBatch chunks are loaded now, behind the query rows
+  const int n_sink = lo, n_win = lo + (L - hi);
+  int wu0 = 0, wu1 = 0;
+  uint4 wk[kWin ? kWinBatch : 1][2], wv[kWin ? kWinBatch : 1][2];
+  if constexpr (kWin) {
+    const int slice = 64 * ((((n_win + 63) / 64) + a.splits - 1) / a.splits);
+    wu0 = min(s * slice, n_win);
+    wu1 = min(wu0 + slice, n_win);
+    load_window_batch(a, b, h, wu0, wu1, n_sink, hi, wk, wv);
   }
   // dense R_K: this thread's 8 x 16 bytes of the head's matrix (64 KB per
   // workgroup, staged in LDS for the query rows' product)
@@ -645,6 +683,126 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   st.unscale = ldexpf(1.0f, -qshift_s[hr]);
   st.qsum = qsum_s[hr];
   load_block<P16>(c, a2, b2, bad);
+  if constexpr (kWin) {
+    // ---- this split's window tokens in fp32 while its first blocks load:
+    // logits of the group's raw query rows against q . (k - mu), a softmax
+    // per row (online across batches of 192 tokens), weighted raw values;
+    // stored as this split's window partial (m, l, 0, acc[128]), merged after
+    // the INT2 partials.  Per batch: the values go to LDS as bf16 and every
+    // lane's logits (a token's 16 lanes sum its 128 dims) to xw; one softmax
+    // pass per row; each thread then sums 4 dims of one row over a quarter of
+    // the tokens.  Raw query rows (scaled to base-2 logits) and q . mu into
+    // LDS (qs is free: the digits are built).
+    float *qmu_s = &red[0][4][0];   // [4]
+    float *xw = &red[1][0][0];      // [4][192]: logits, then weights (spans red[1], red[2])
+    float *alw = &red[3][0][0];     // [4]: rescale factor of a batch per row
+    uint16_t *vb16 = reinterpret_cast<uint16_t *>(&facc_all[0][0]);  // [192][128] bf16 values (free until the first flush)
+    constexpr int kWT = 64 * kWinBatch;
+    if (wave < 4) {
+      float r0 = 0.0f, r1 = 0.0f;
+      if (wave < nrows) {
+        r0 = (DT == KVQ_F32 ? __uint_as_float(qb0) : __uint_as_float(qb0 << 16)) * (kLog2eF * kInvSqrtD);
+        r1 = (DT == KVQ_F32 ? __uint_as_float(qb1) : __uint_as_float(qb1 << 16)) * (kLog2eF * kInvSqrtD);
+      }
+      qs[wave][lane] = r0;
+      qs[wave][lane + 64] = r1;
+      const float qm = a.win_mu ? wave_sum(r0 * a.win_mu[static_cast<size_t>(h) * D + lane] +
+                                           r1 * a.win_mu[static_cast<size_t>(h) * D + lane + 64])
+                                : 0.0f;
+      if (lane == 0) qmu_s[wave] = qm;
+    }
+    float m_run = -INFINITY, l_run = 0.0f;  // row `wave` (waves 0-3)
+    const int vr = threadIdx.x >> 7, g4 = threadIdx.x & 31, tp = (threadIdx.x >> 5) & 3;
+    float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // row vr, dims 4 g4 .. 4 g4 + 3, tokens tp (mod 4)
+    for (int u_b = wu0; u_b < wu1; u_b += kWT) {
+      if (u_b != wu0) load_window_batch(a, b, h, u_b, wu1, n_sink, hi, wk, wv);
+      const int nt = min(kWT, wu1 - u_b);
+      __syncthreads();  // (query rows written; the previous batch's LDS reads done)
+#pragma unroll
+      for (int ch = 0; ch < kWinBatch; ++ch) {
+        if (64 * ch >= nt) break;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int idx = threadIdx.x + 64 * kWaves * e, tok = 64 * ch + (idx >> 4), part = idx & 15;
+          *reinterpret_cast<uint4 *>(vb16 + tok * D + 8 * part) = wv[ch][e];
+          const uint4 kq = wk[ch][e];
+          const float kf[8] = {__uint_as_float(kq.x << 16), __uint_as_float(kq.x & 0xFFFF0000u),
+                               __uint_as_float(kq.y << 16), __uint_as_float(kq.y & 0xFFFF0000u),
+                               __uint_as_float(kq.z << 16), __uint_as_float(kq.z & 0xFFFF0000u),
+                               __uint_as_float(kq.w << 16), __uint_as_float(kq.w & 0xFFFF0000u)};
+          float dot[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float4 qa = *reinterpret_cast<const float4 *>(&qs[r][8 * part]);
+            const float4 qb = *reinterpret_cast<const float4 *>(&qs[r][8 * part + 4]);
+            float d = qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3];
+            d += qb.x * kf[4] + qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
+            d += __shfl_xor(d, 1);
+            d += __shfl_xor(d, 2);
+            d += __shfl_xor(d, 4);
+            d += __shfl_xor(d, 8);
+            dot[r] = d;
+          }
+          if (part == 0) {
+            const bool ok = tok < nt;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xw[r * kWT + tok] = ok ? dot[r] - qmu_s[r] : -INFINITY;
+          }
+        }
+      }
+      __syncthreads();
+      if (wave < 4) {  // softmax of row `wave` over the batch, lanes take tokens lane, lane + 64, lane + 128
+        float xv[kWinBatch], mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kWinBatch; ++i) {
+          xv[i] = lane + 64 * i < nt ? xw[wave * kWT + lane + 64 * i] : -INFINITY;
+          mx = fmaxf(mx, xv[i]);
+        }
+        const float mn = fmaxf(m_run, wave_maxf(mx));  // finite: the batch holds a token
+        const float al = exp2f(m_run - mn);
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWinBatch; ++i) {
+          const float pv = exp2f(xv[i] - mn);
+          ps += pv;
+          if (lane + 64 * i < nt) xw[wave * kWT + lane + 64 * i] = pv;
+        }
+        l_run = l_run * al + wave_sum(ps);
+        m_run = mn;
+        if (lane == 0) alw[wave] = al;
+      }
+      __syncthreads();
+      const float al = alw[vr];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc4[jj] *= al;
+      for (int t = tp; t < nt; t += 4) {
+        const float pv = xw[vr * kWT + t];
+        const uint2 v2 = *reinterpret_cast<const uint2 *>(vb16 + t * D + 4 * g4);
+        acc4[0] += pv * __uint_as_float(v2.x << 16);
+        acc4[1] += pv * __uint_as_float(v2.x & 0xFFFF0000u);
+        acc4[2] += pv * __uint_as_float(v2.y << 16);
+        acc4[3] += pv * __uint_as_float(v2.y & 0xFFFF0000u);
+      }
+    }
+    __syncthreads();  // (the values' LDS reads done)
+    // the 4 token parts of every (row, dim), summed through LDS, then the
+    // window partial of this split: slot parts + s (an empty slice stores m = -inf, l = 0)
+    float *wsum = &facc_all[0][0];  // [4 rows][4 parts][128]
+    *reinterpret_cast<float4 *>(wsum + (vr * 4 + tp) * D + 4 * g4) = float4{acc4[0], acc4[1], acc4[2], acc4[3]};
+    __syncthreads();
+    const int ad = threadIdx.x & 127;
+    const float wacc = (wsum[(vr * 4) * D + ad] + wsum[(vr * 4 + 1) * D + ad]) +
+                       (wsum[(vr * 4 + 2) * D + ad] + wsum[(vr * 4 + 3) * D + ad]);
+    auto win_slot = [&](int r) {
+      const int rr = row0 + r;
+      const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
+      return a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + a.parts + s) * (D + 4);
+    };
+    if (vr < nrows) store_partial(win_slot(vr) + 4 + ad, wacc);
+    // (row r's running max and sum are in wave r, which ran its softmax)
+    if (wave < nrows && lane < 4) store_partial(win_slot(wave) + lane, lane == 0 ? m_run : lane == 1 ? l_run : 0.0f);
+    __syncthreads();  // (wsum read before the main loop's flushes write facc_all)
+  }
   st.row_ok = hr < nrows;
   const int x = lane & 3;
   st.sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
@@ -775,7 +933,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       }
       const int rr = row0 + r;
       const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
-      float *dst = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.parts + s) * (D + 4);
+      float *dst = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + s) * (D + 4);
       store_partial(dst + 4 + lane, a0);
       store_partial(dst + 4 + 64 + lane, a1);
       if (lane < 4) store_partial(dst + lane, lane == 0 ? mstar : lane == 1 ? (nan ? __builtin_nanf("") : l)
@@ -791,7 +949,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int rr = min(row0 + r, a.R - 1);
         const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
-        rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.parts + slot_w) * (D + 4);
+        rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + slot_w) * (D + 4);
       }
       constexpr int kN = (4 * (D + 4) + 63) / 64;
       float vals[kN];
@@ -820,119 +978,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_valid, a.epoch, a.splits) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
-  if constexpr (kWin) {
-    // ---- BF16 windows of this sequence and KV head, in fp32: the sink
-    // [0, lo) and the recent tokens [hi, L) against the group's raw query
-    // rows.  Result: per row the base-2 running max and sum (wave r holds
-    // row r) and the weighted values (thread (r, d) = (tid / 128, tid % 128)),
-    // left in LDS for the combination below.  All window loads are issued
-    // at once; each chunk of 64 tokens: logits from the keys in registers
-    // (a token's 16 lanes sum its 128 dims), values through LDS.
-    const int tid = threadIdx.x;
-    const int n_sink = lo, n_win = lo + (L - hi);
-    const size_t hstride = static_cast<size_t>(a.H) * D;  // elements between window tokens
-    const uint16_t *skb = a.win_sk + static_cast<size_t>(b) * a.win_S * hstride + static_cast<size_t>(h) * D;
-    const uint16_t *svb = a.win_sv + static_cast<size_t>(b) * a.win_S * hstride + static_cast<size_t>(h) * D;
-    const uint16_t *rkb = a.win_rk + static_cast<size_t>(b) * a.win_W * hstride + static_cast<size_t>(h) * D;
-    const uint16_t *rvb = a.win_rv + static_cast<size_t>(b) * a.win_W * hstride + static_cast<size_t>(h) * D;
-    uint4 wk[kWinChunks][2], wv[kWinChunks][2];
-#pragma unroll
-    for (int ch = 0; ch < kWinChunks; ++ch)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int idx = tid + 64 * kWaves * e, u = 64 * ch + (idx >> 4), part = idx & 15;
-        wk[ch][e] = wv[ch][e] = uint4{0u, 0u, 0u, 0u};
-        if (u < n_win) {
-          const bool sink = u < n_sink;
-          const size_t off = (sink ? static_cast<size_t>(u) : static_cast<size_t>((hi + u - n_sink) % a.win_W)) *
-                                 hstride + 8 * part;
-          wk[ch][e] = *reinterpret_cast<const uint4 *>((sink ? skb : rkb) + off);
-          wv[ch][e] = *reinterpret_cast<const uint4 *>((sink ? svb : rvb) + off);
-        }
-      }
-    // raw query rows scaled to base-2 logits (rows past the last: zero), and q . mu
-    float *qmu_s = &red[0][4][0];   // [8]: halves of q . mu per row
-    float *mlw_s = &red[0][4][16];  // [8]: window m (4), l (4) per row
-    float *xw = &red[1][0][0];      // [4][64]: logits, then weights, of a chunk
-    float *alw = &red[2][0][0];     // [4]: rescale factor of a chunk per row
-    float *vbuf = &facc_all[0][0];  // [64][128]: values of a chunk (fp32)
-    {
-      const int r = tid >> 7, i = tid & 127;
-      float x = 0.0f;
-      if (r < nrows) {
-        const int rr = row0 + r;
-        const size_t rj = (static_cast<size_t>(b) * a.Nq + rr / a.G) * a.Hq + h * a.G + rr % a.G;
-        x = DT == KVQ_F32 ? static_cast<const float *>(a.q)[rj * D + i]
-                          : __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(a.q)[rj * D + i]) << 16);
-        x *= kLog2eF * kInvSqrtD;
-      }
-      qs[r][i] = x;
-      const float qm = wave_sum(a.win_mu ? x * a.win_mu[static_cast<size_t>(h) * D + i] : 0.0f);
-      if (lane == 0) qmu_s[wave] = qm;
-    }
-    float m_run = -INFINITY, l_run = 0.0f, acc = 0.0f;
-    const int ar = tid >> 7, ad = tid & 127;
-    const int nch = (n_win + 63) / 64;
-#pragma unroll
-    for (int ch = 0; ch < kWinChunks; ++ch) {
-      if (ch >= nch) break;
-      __syncthreads();  // (qs, q . mu written; the previous chunk's LDS reads done)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int idx = tid + 64 * kWaves * e, tok = idx >> 4, part = idx & 15;
-        const uint4 w = wv[ch][e];
-        float4 *dst = reinterpret_cast<float4 *>(vbuf + tok * D + 8 * part);
-        dst[0] = float4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
-                        __uint_as_float(w.y & 0xFFFF0000u)};
-        dst[1] = float4{__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u), __uint_as_float(w.w << 16),
-                        __uint_as_float(w.w & 0xFFFF0000u)};
-        const uint4 kq = wk[ch][e];
-        const float kf[8] = {__uint_as_float(kq.x << 16), __uint_as_float(kq.x & 0xFFFF0000u),
-                             __uint_as_float(kq.y << 16), __uint_as_float(kq.y & 0xFFFF0000u),
-                             __uint_as_float(kq.z << 16), __uint_as_float(kq.z & 0xFFFF0000u),
-                             __uint_as_float(kq.w << 16), __uint_as_float(kq.w & 0xFFFF0000u)};
-        float dot[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float d = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) d += qs[r][8 * part + j] * kf[j];
-          d += __shfl_xor(d, 1);
-          d += __shfl_xor(d, 2);
-          d += __shfl_xor(d, 4);
-          d += __shfl_xor(d, 8);
-          dot[r] = d;
-        }
-        if (part == 0) {
-          const bool ok = 64 * ch + tok < n_win;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) xw[r * 64 + tok] = ok ? dot[r] - (qmu_s[2 * r] + qmu_s[2 * r + 1]) : -INFINITY;
-        }
-      }
-      __syncthreads();
-      if (wave < 4) {  // online softmax of row `wave`, lane = token of the chunk
-        const float x = xw[wave * 64 + lane];
-        const float mn = fmaxf(m_run, wave_maxf(x));  // finite: the chunk holds a token
-        const float al = exp2f(m_run - mn);
-        const float pv = exp2f(x - mn);
-        l_run = l_run * al + wave_sum(pv);
-        m_run = mn;
-        xw[wave * 64 + lane] = pv;
-        if (lane == 0) alw[wave] = al;
-      }
-      __syncthreads();
-      acc *= alw[ar];
-#pragma unroll 8
-      for (int t = 0; t < 64; ++t) acc += xw[ar * 64 + t] * vbuf[t * D + ad];
-    }
-    __syncthreads();  // (all reads of qs, xw, vbuf done)
-    qs[ar][ad] = acc;
-    if (wave < 4 && lane == 0) {
-      mlw_s[wave] = m_run;
-      mlw_s[4 + wave] = l_run;
-    }
-    __syncthreads();
-  }
   // dense R_V: the head's matrix is staged in LDS by the whole workgroup
   // (its loads go out together with the merge's)
   const bool vdense = a.rv.kind == KVQ_ROT_DENSE;
@@ -953,7 +998,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   const int qq = (row0 + min(wave, nrows - 1)) / a.G, j = h * a.G + (row0 + min(wave, nrows - 1)) % a.G;
   const size_t row = static_cast<size_t>(b) * a.Nq + qq;
   float o0 = 0.0f, o1 = 0.0f, mi = -INFINITY, li = 0.0f;
-  if (wave < nrows) merge_partials(a.part + (row * a.Hq + j) * a.parts * (D + 4), a.parts, lane, o0, o1, &mi, &li);
+  float ow0 = 0.0f, ow1 = 0.0f, mw = -INFINITY, lw = 0.0f;  // the windows' partials (one per split)
+  if (wave < nrows) {
+    const float *base = a.part + (row * a.Hq + j) * a.pstride * (D + 4);
+    if constexpr (kWin) merge_partials(base + static_cast<size_t>(a.parts) * (D + 4), a.splits, lane, ow0, ow1, &mw, &lw);
+    merge_partials(base, a.parts, lane, o0, o1, &mi, &li);
+  }
   if (vdense) {
     float4 *rd = reinterpret_cast<float4 *>(rs) + threadIdx.x;
     rd[0] = v0;
@@ -988,19 +1038,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     unrotate_value_wave(o0, o1, a.rv, h, lane);
   }
   if constexpr (kWin) {
-    // o = (2^(m_int2 - M) (o_int2 l_int2) + 2^(m_win - M) acc_win) / (2^(m_int2 - M) l_int2 + 2^(m_win - M) l_win),
-    // both parts in the unrotated domain (o_int2 normalized by its sum l_int2; NaN stays NaN)
+    // o = (2^(m_int2 - M) l_int2 o_int2 + 2^(m_win - M) l_win o_win) / (2^(m_int2 - M) l_int2 + 2^(m_win - M) l_win),
+    // both parts normalized and in the unrotated domain (NaN stays NaN)
     if (wave < nrows) {
-      const float mw = red[0][4][16 + wave], lw = red[0][4][20 + wave];
       const float M = fmaxf(mi, mw);
       if (M == -INFINITY) {
         o0 = o1 = o0 != o0 ? o0 : 0.0f;
       } else {
         const float w1 = (mi == -INFINITY ? 0.0f : exp2f(mi - M)) * li;
-        const float w2 = mw == -INFINITY ? 0.0f : exp2f(mw - M);
-        const float den = w1 + w2 * lw;
-        o0 = (w1 * o0 + w2 * qs[wave][lane]) / den;
-        o1 = (w1 * o1 + w2 * qs[wave][lane + 64]) / den;
+        const float w2 = (mw == -INFINITY ? 0.0f : exp2f(mw - M)) * lw;
+        const float den = w1 + w2;
+        o0 = (w1 * o0 + w2 * ow0) / den;
+        o1 = (w1 * o1 + w2 * ow1) / den;
       }
     }
   }
@@ -1031,6 +1080,7 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.splits = pl.splits;
   a.premerge = pl.splits > kMaxSplitsNoPremerge ? 1 : 0;
   a.parts = a.premerge ? pl.splits : pl.splits * kWaves;
+  a.pstride = a.parts + (win ? pl.splits : 0);
   a.max_seq_len = pl.max_seq_len;
   a.P = page_size;
   a.p_shift = __builtin_ctz(static_cast<unsigned>(page_size));
