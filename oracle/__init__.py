@@ -79,6 +79,7 @@ def _load():
         lib.kvqo_decode_windows_f64.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P, P]
         lib.kvqo_bits_per_element.argtypes = [i64, i32, i32]
         lib.kvqo_bits_per_element.restype = ctypes.c_double
+        lib.kvqo_fold_value_rotation.argtypes = [P, i32, i32, i32, P, P]
         _lib = lib
     return _lib
 
@@ -278,6 +279,17 @@ def decode_windows(q, cache: Cache, seq_lens, rot_k: Rotation, rot_v: Rotation, 
 
 def bits_per_element(seq_len: int, num_sink: int = 64, num_recent: int = 256) -> float:
     return float(_load().kvqo_bits_per_element(seq_len, num_sink, num_recent))
+
+
+def fold_value_rotation(w, blocks_per_head: int, rot_v: Rotation) -> np.ndarray:
+    """out block b = R_V[b / blocks_per_head]^T w block b (blocks of 128 rows), fp32."""
+    w = _f32(w)
+    nb = w.shape[0] // D
+    out = np.zeros_like(w)
+    rv = rot_v._c()
+    _check(_load().kvqo_fold_value_rotation(_ptr(w), nb, blocks_per_head, w.shape[1], ctypes.byref(rv), _ptr(out)),
+           "fold_value_rotation")
+    return out
 
 
 def attention_ref(q, k, v) -> np.ndarray:

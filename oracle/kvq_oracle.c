@@ -822,3 +822,30 @@ double kvqo_bits_per_element(int64_t L, int32_t num_sink, int32_t num_recent) {
   /* per head and side: an INT2 token stores 128 2-bit codes and two fp16 words, a window token 128 bf16 */
   return ((double)int2 * (128.0 * 2.0 + 32.0) + (double)(sink + recent) * 128.0 * 16.0) / ((double)L * 128.0);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Value-rotation folding (the header states the passage). */
+int kvqo_fold_value_rotation(const float *w, int32_t num_blocks, int32_t blocks_per_head, int32_t cols,
+                             const kvqo_rotation *rot_v, float *out) {
+  const int d = KVQO_D;
+  if (!w || !out || !rot_v || num_blocks < 1 || blocks_per_head < 1 || cols < 1 || num_blocks % blocks_per_head)
+    return KVQO_ERR_ARG;
+  double *r = (double *)malloc(sizeof(double) * d * d);
+  if (!r) return KVQO_ERR_ARG;
+  int rc = KVQO_OK;
+  for (int32_t blk = 0; blk < num_blocks && !rc; ++blk) {
+    const int32_t h = blk / blocks_per_head;
+    rc = kvqo_rotation_matrix(rot_v->kind, rot_v->signs ? rot_v->signs + (size_t)h * d : NULL,
+                              rot_v->matrix ? rot_v->matrix + (size_t)h * d * d : NULL, r);
+    const float *wb = w + (size_t)blk * d * cols;
+    float *ob = out + (size_t)blk * d * cols;
+    for (int i = 0; i < d && !rc; ++i)
+      for (int32_t n = 0; n < cols; ++n) {
+        double acc = 0.0;  /* (R^T)[i][c] = R[c][i] */
+        for (int c = 0; c < d; ++c) acc += r[c * d + i] * (double)wb[(size_t)c * cols + n];
+        ob[(size_t)i * cols + n] = (float)acc;
+      }
+  }
+  free(r);
+  return rc;
+}

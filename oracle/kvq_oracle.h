@@ -173,4 +173,17 @@ int kvqo_decode_windows_f64(const float *q, int32_t num_seqs, int32_t queries_pe
  * of 128 (2.25 bits per element), each window token 16 bits per element. */
 double kvqo_bits_per_element(int64_t L, int32_t num_sink, int32_t num_recent);
 
+
+/* Value-rotation folding ("Output-Aware Rotation for INT2 KV-Cache
+ * Quantization", Appendix, equivalent inference implementation, Eq. (29)-(31):
+ * the value rotation and its inverse are folded into the projection weights).
+ * w holds num_blocks blocks of 128 rows, [num_blocks * 128][cols]; block b
+ * belongs to KV head b / blocks_per_head, and out block b = R_V[h]^T w block b
+ * (fp64 products in index order, rounded to fp32).  W_O [Hq*128][d_model]
+ * (rows of query head j): blocks_per_head = Hq / H, then y = o' W_O-folded
+ * for the rotated output o' = o R_V; W_V in [H*128][d_in] row layout (the
+ * pages' W_{V,h}): blocks_per_head = 1, then x W_V-folded^T = (x W_V^T) R_V. */
+int kvqo_fold_value_rotation(const float *w, int32_t num_blocks, int32_t blocks_per_head, int32_t cols,
+                             const kvqo_rotation *rot_v, float *out);
+
 #endif

@@ -527,3 +527,64 @@ def test_windows_of_size_zero_reduce_to_plain_decode(oracle):
     ref = oracle.decode(q, cache, [L], rot, rot, num_seqs=1, max_pages=mp, f64=True)
     got = oracle.decode_windows(q, cache, [L], rot, rot, oracle.Windows(1, H, 0, 0), num_seqs=1, max_pages=mp)
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- value-rotation folding
+def test_fold_identity_rotation_is_a_copy(oracle):
+    rng = np.random.default_rng(51)
+    w = rng.standard_normal((4 * D, 40)).astype(np.float32)
+    out = oracle.fold_value_rotation(w, 2, oracle.Rotation(oracle.ROT_IDENTITY))
+    assert np.array_equal(out, w)
+
+
+def test_fold_preserves_column_norms_per_block(oracle):
+    """R_V is orthogonal: every column of every block keeps its norm."""
+    rng = np.random.default_rng(52)
+    H = 2
+    s = (rng.integers(0, 2, (H, D)) * 2 - 1).astype(np.int8)
+    w = rng.standard_normal((4 * D, 24)).astype(np.float32)
+    out = oracle.fold_value_rotation(w, 2, oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=s))
+    for b in range(4):
+        a = np.linalg.norm(w[b * D:(b + 1) * D].astype(np.float64), axis=0)
+        c = np.linalg.norm(out[b * D:(b + 1) * D].astype(np.float64), axis=0)
+        assert np.allclose(a, c, rtol=1e-6)
+
+
+@pytest.mark.parametrize("kind", ["sh", "dense"])
+def test_fold_wo_equals_explicit_inverse_rotation(oracle, kind):
+    """Eq. (31): decoding with the explicit R_V^T and W_O equals decoding in
+    the rotated value domain (identity R_V at decode) with the folded W_O."""
+    rng = np.random.default_rng(53)
+    T, H, Hq, P, dm = 45, 2, 4, 16, 20
+    if kind == "sh":
+        rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=(rng.integers(0, 2, (H, D)) * 2 - 1).astype(np.int8))
+    else:
+        import scipy.linalg
+        m = np.stack([scipy.linalg.expm((lambda a: a - a.T)(rng.normal(0, 0.1, (D, D)))) for _ in range(H)])
+        rot = oracle.Rotation(oracle.ROT_DENSE, matrix=m.astype(np.float32))
+    ident = oracle.Rotation(oracle.ROT_IDENTITY)
+    k = rng.standard_normal((T, H, D)).astype(np.float32)
+    v = rng.standard_normal((T, H, D)).astype(np.float32)
+    w = (rng.standard_normal((Hq * D, dm)) / 20).astype(np.float32)
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    cache = oracle.Cache((T + P - 1) // P, P, H)
+    oracle.quantize(k, v, cache, rot, rot)
+    _, y = oracle.decode(q, cache, [T], rot, rot, num_seqs=1, max_pages=cache.num_pages, w_o=w, d_model=dm)
+    wf = oracle.fold_value_rotation(w, Hq // H, rot)
+    _, y2 = oracle.decode(q, cache, [T], rot, ident, num_seqs=1, max_pages=cache.num_pages, w_o=wf, d_model=dm)
+    assert np.allclose(y, y2, rtol=1e-5, atol=1e-6 * np.abs(y).max())
+
+
+def test_fold_wv_equals_rotating_the_values(oracle):
+    """Eq. (30): x W_V-folded^T = (x W_V^T) R_V, with W_V in [H*128][d_in]."""
+    rng = np.random.default_rng(54)
+    H, din = 2, 48
+    s = (rng.integers(0, 2, (H, D)) * 2 - 1).astype(np.int8)
+    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=s)
+    wv = rng.standard_normal((H * D, din)).astype(np.float32)
+    x = rng.standard_normal((5, din)).astype(np.float32)
+    v = (x.astype(np.float64) @ wv.astype(np.float64).T).reshape(5, H, D).astype(np.float32)
+    vr = oracle.rotate(v, rot)
+    wf = oracle.fold_value_rotation(wv, 1, rot)
+    vf = (x.astype(np.float64) @ wf.astype(np.float64).T).reshape(5, H, D)
+    assert np.allclose(vf, vr, rtol=1e-5, atol=1e-5)
