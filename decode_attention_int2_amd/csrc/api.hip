@@ -267,6 +267,21 @@ int kvq_window_write(const void *k, const void *v, int32_t dtype, int64_t num_to
   return KVQ_OK;
 }
 
+int kvq_fold_value_rotation(const void *w, int32_t dtype, int32_t num_blocks, int32_t blocks_per_head, int32_t cols,
+                            const kvq_rotation *rot_v, void *out, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
+  const int rc = check_rotation(rot_v);
+  if (rc) return rc;
+  if (!w || !out || num_blocks < 1 || blocks_per_head < 1 || cols < 1 || num_blocks % blocks_per_head ||
+      num_blocks > 65535)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t bytes = static_cast<size_t>(num_blocks) * D * cols * (dtype == KVQ_F32 ? 4 : 2);
+  const uintptr_t wa = reinterpret_cast<uintptr_t>(w), oa = reinterpret_cast<uintptr_t>(out);
+  if (wa < oa + bytes && oa < wa + bytes) return KVQ_ERR_INVALID_ARGUMENT;  // overlapping buffers
+  KVQ_TRY(launch_fold_value_rotation(w, dtype, num_blocks, blocks_per_head, cols, to_dev(*rot_v), out, stream));
+  return KVQ_OK;
+}
+
 double kvq_bits_per_element(int64_t seq_len, int32_t num_sink, int32_t num_recent) {
   if (seq_len <= 0 || num_sink < 0 || num_recent < 0) return 0.0;
   // window tokens: 128 bf16 per (head, side); INT2 tokens: 32 code bytes + fp16 scale and zero

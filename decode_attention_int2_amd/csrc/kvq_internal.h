@@ -351,6 +351,8 @@ hipError_t launch_window_write(const void *k, const void *v, int dtype, int64_t 
                                int num_seqs, uint16_t *sink_k,
                                uint16_t *sink_v, uint16_t *recent_k, uint16_t *recent_v, int num_sink,
                                int num_recent, hipStream_t stream);
+hipError_t launch_fold_value_rotation(const void *w, int dtype, int num_blocks, int blocks_per_head, int cols,
+                                      RotDev rv, void *out, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t *p, int32_t value, int n, hipStream_t stream);
 // Post-W_O NMSE through the Gram matrix of W_O (see candidate.hip):
 // prepare once per search (Gram blocks and the reference output's norms),

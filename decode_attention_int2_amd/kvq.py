@@ -22,7 +22,7 @@ KVQ_SELECT_JOINT, KVQ_SELECT_PER_HEAD = 0, 1
 HEAD_DIM = 128
 
 EXPORTED = ("kvq_cache_bytes", "kvq_quantize", "kvq_decode_workspace_bytes", "kvq_decode_attn",
-            "kvq_window_write", "kvq_decode_attn_windows", "kvq_bits_per_element",
+            "kvq_window_write", "kvq_decode_attn_windows", "kvq_bits_per_element", "kvq_fold_value_rotation",
             "kvq_candidate_workspace_bytes", "kvq_candidate_nmse", "kvq_status_string", "kvq_version")
 
 
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_decode_attn_windows.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, i32, P, P, P, P, P, i32, P, P, P, sz,
                                             i32, P]
     lib.kvq_decode_attn_windows.restype = ctypes.c_int
+    lib.kvq_fold_value_rotation.argtypes = [P, i32, i32, i32, i32, P, P, P]
+    lib.kvq_fold_value_rotation.restype = ctypes.c_int
     lib.kvq_bits_per_element.argtypes = [i64, i32, i32]
     lib.kvq_bits_per_element.restype = ctypes.c_double
     lib.kvq_status_string.argtypes = [ctypes.c_int]
@@ -244,6 +246,15 @@ def kvq_decode_attn_windows(q: torch.Tensor, num_seqs: int, queries_per_seq: int
                                        _dev_ptr(w_o, "w_o"), d_model, _dev_ptr(out_o, "out_o"),
                                        _dev_ptr(out_y, "out_y"), _dev_ptr(workspace, "workspace"), ws_bytes,
                                        num_splits, _stream(stream)), "kvq_decode_attn_windows")
+
+
+def kvq_fold_value_rotation(w: torch.Tensor, blocks_per_head: int, rot_v: Rotation, out: torch.Tensor,
+                            stream=None) -> None:
+    """out block b = R_V[b / blocks_per_head]^T w block b (blocks of 128 rows); out has w's shape and dtype."""
+    r = rot_v._c()
+    _check(load_library().kvq_fold_value_rotation(_dev_ptr(w, "w"), _dtype_code(w), w.shape[0] // 128, blocks_per_head,
+                                                  w.shape[1], ctypes.byref(r), _dev_ptr(out, "out"), _stream(stream)),
+           "kvq_fold_value_rotation")
 
 
 def kvq_bits_per_element(seq_len: int, num_sink: int = 64, num_recent: int = 256) -> float:

@@ -250,6 +250,23 @@ int kvq_decode_attn_windows(const void *q, int32_t dtype, int32_t num_seqs, int3
 double kvq_bits_per_element(int64_t seq_len, int32_t num_sink, int32_t num_recent);
 
 /* ---------------------------------------------------------------------------
+ * kvq_fold_value_rotation -- value-rotation folding ([OptR] Appendix,
+ * equivalent inference implementation, Eq. (29)-(31)): out block b =
+ * R_V[h]^T w block b, for w = num_blocks blocks of 128 rows, [num_blocks *
+ * 128][cols] in dtype, block b belonging to KV head h = b / blocks_per_head.
+ *   W_O [Hq*128][d_model], blocks_per_head = Hq / H: kvq_decode_attn with an
+ *       identity rot_v and the folded W_O gives the same out_y as rot_v with
+ *       W_O (out_o is then o R_V, the rotated output).
+ *   W_V in [H*128][d_in] rows (v = x W_V^T), blocks_per_head = 1: the
+ *       folded W_V projects values that are already rotated (cache write
+ *       with an identity rot_v).
+ * fp32 sums, the result rounded to dtype (nearest even); out must not
+ * overlap w.  One-time weight preparation (not a per-step kernel).
+ * ------------------------------------------------------------------------- */
+int kvq_fold_value_rotation(const void *w, int32_t dtype, int32_t num_blocks, int32_t blocks_per_head, int32_t cols,
+                            const kvq_rotation *rot_v, void *out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * kvq_candidate_nmse -- batched post-W_O NMSE over a grid of candidate
  * rotations and clip ratios, and selection of the best one ([Eval], observed
  * envelope: identity + signed-Hadamard candidates x clip grid, chosen by
