@@ -80,6 +80,7 @@ def _load():
         lib.kvqo_bits_per_element.argtypes = [i64, i32, i32]
         lib.kvqo_bits_per_element.restype = ctypes.c_double
         lib.kvqo_fold_value_rotation.argtypes = [P, i32, i32, i32, P, P]
+        lib.kvqo_decode_causal_f64.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -279,6 +280,22 @@ def decode_windows(q, cache: Cache, seq_lens, rot_k: Rotation, rot_v: Rotation, 
 
 def bits_per_element(seq_len: int, num_sink: int = 64, num_recent: int = 256) -> float:
     return float(_load().kvqo_bits_per_element(seq_len, num_sink, num_recent))
+
+
+def decode_causal(q, cache: Cache, seq_lens, rot_k: Rotation, rot_v: Rotation, num_seqs: int,
+                  queries_per_seq: int = 1, page_table=None, max_pages: int = 0) -> np.ndarray:
+    """fp64 out_o [rows][Hq][128]: row qi of a sequence attends its first L - (queries_per_seq - 1 - qi) tokens."""
+    q = _f32(q)
+    rows, Hq, _ = q.shape
+    pt = None if page_table is None else np.ascontiguousarray(page_table, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    c = cache._c()
+    rk, rv = rot_k._c(), rot_v._c()
+    out = np.zeros((rows, Hq, D), np.float64)
+    _check(_load().kvqo_decode_causal_f64(_ptr(q), num_seqs, queries_per_seq, Hq, ctypes.byref(c), _ptr(pt),
+                                          max_pages, _ptr(sl), ctypes.byref(rk), ctypes.byref(rv), _ptr(out)),
+           "decode_causal_f64")
+    return out
 
 
 def fold_value_rotation(w, blocks_per_head: int, rot_v: Rotation) -> np.ndarray:

@@ -849,3 +849,25 @@ int kvqo_fold_value_rotation(const float *w, int32_t num_blocks, int32_t blocks_
   free(r);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Causal queries (the header states the passage). */
+int kvqo_decode_causal_f64(const float *q, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                           const kvqo_cache *cache, const int32_t *page_table, int32_t max_pages,
+                           const int32_t *seq_lens, const kvqo_rotation *rot_k, const kvqo_rotation *rot_v,
+                           double *out_o) {
+  if (!q || !seq_lens || !out_o || num_seqs < 0 || queries_per_seq < 1 || num_q_heads < 1) return KVQO_ERR_ARG;
+  const size_t row_elems = (size_t)num_q_heads * KVQO_D;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    for (int32_t qi = 0; qi < queries_per_seq; ++qi) {
+      int32_t len = seq_lens[b] - (queries_per_seq - 1 - qi);
+      if (len < 0) len = 0;
+      const size_t row = (size_t)b * queries_per_seq + qi;
+      const int rc = kvqo_decode_f64(q + row * row_elems, 1, 1, num_q_heads, cache,
+                                     page_table ? page_table + (size_t)b * max_pages : NULL, max_pages, &len, rot_k,
+                                     rot_v, out_o + row * row_elems);
+      if (rc) return rc;
+    }
+  }
+  return KVQO_OK;
+}

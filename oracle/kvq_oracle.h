@@ -186,4 +186,16 @@ double kvqo_bits_per_element(int64_t L, int32_t num_sink, int32_t num_recent);
 int kvqo_fold_value_rotation(const float *w, int32_t num_blocks, int32_t blocks_per_head, int32_t cols,
                              const kvqo_rotation *rot_v, float *out);
 
+
+/* Causal queries (the final query positions of a sequence, "Output-Aware
+ * Rotation for INT2 KV-Cache Quantization", Appendix: the objective over the
+ * final 64 query positions; causal attention distributions): row qi of
+ * sequence b is position L - queries_per_seq + qi and attends the first
+ * L - (queries_per_seq - 1 - qi) tokens; each row is kvqo_decode_f64 over
+ * that prefix (no token: o = 0). */
+int kvqo_decode_causal_f64(const float *q, int32_t num_seqs, int32_t queries_per_seq, int32_t num_q_heads,
+                           const kvqo_cache *cache, const int32_t *page_table, int32_t max_pages,
+                           const int32_t *seq_lens, const kvqo_rotation *rot_k, const kvqo_rotation *rot_v,
+                           double *out_o);
+
 #endif

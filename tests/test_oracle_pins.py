@@ -588,3 +588,36 @@ def test_fold_wv_equals_rotating_the_values(oracle):
     wf = oracle.fold_value_rotation(wv, 1, rot)
     vf = (x.astype(np.float64) @ wf.astype(np.float64).T).reshape(5, H, D)
     assert np.allclose(vf, vr, rtol=1e-5, atol=1e-5)
+
+
+# ---------------------------------------------------------------- causal queries
+def test_causal_decode_reduces_to_plain_decode(oracle):
+    """The last of a sequence's causal rows, and a single causal row, attend
+    the whole sequence: they equal the plain decode.  A row whose prefix is
+    one token returns that token's value (v_hat R_V^T)."""
+    rng = np.random.default_rng(61)
+    H, Hq, P, L, nq = 2, 4, 16, 70, 5
+    s = (rng.integers(0, 2, (H, D)) * 2 - 1).astype(np.int8)
+    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=s)
+    k = rng.standard_normal((L, H, D)).astype(np.float32)
+    v = rng.standard_normal((L, H, D)).astype(np.float32)
+    q = rng.standard_normal((nq, Hq, D)).astype(np.float32)
+    mp = (L + P - 1) // P
+    cache = oracle.Cache(mp, P, H)
+    oracle.quantize(k, v, cache, rot, rot)
+    causal = oracle.decode_causal(q, cache, [L], rot, rot, num_seqs=1, queries_per_seq=nq, max_pages=mp)
+    plain = oracle.decode(q, cache, [L], rot, rot, num_seqs=1, queries_per_seq=nq, max_pages=mp, f64=True)
+    assert np.array_equal(causal[nq - 1], plain[nq - 1])
+    for qi in range(nq - 1):                 # shorter prefixes differ from the full-cache rows
+        assert not np.allclose(causal[qi], plain[qi])
+    one = oracle.decode_causal(q[:1], cache, [L], rot, rot, num_seqs=1, queries_per_seq=1, max_pages=mp)
+    assert np.array_equal(one[0], plain[0])
+    # a 3-row chunk over a 3-token sequence: row 0 attends token 0 only
+    tiny = oracle.decode_causal(q[:3], cache, [3], rot, rot, num_seqs=1, queries_per_seq=3, max_pages=mp)
+    codes, sb, zb = oracle.read_group(cache, 0, 0, 1)
+    vhat = np.array([oracle.f16_bits_to_f32(zb) + c * oracle.f16_bits_to_f32(sb) for c in codes], np.float64)
+    r = oracle.rotation_matrix(oracle.ROT_SIGNED_HADAMARD, signs=s[0])
+    assert np.allclose(tiny[0, 0], vhat @ r.T, rtol=1e-12, atol=1e-12)
+    # a chunk longer than the sequence: its first rows have no token
+    none = oracle.decode_causal(q, cache, [2], rot, rot, num_seqs=1, queries_per_seq=nq, max_pages=mp)
+    assert np.all(none[:3] == 0.0)
