@@ -155,7 +155,8 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
                        const int32_t *seq_lens, int32_t max_seq_len, const kvq_rotation *rot_k,
                        const kvq_rotation *rot_v, const kvq_windows *windows, const float *key_mean, const void *w_o,
                        int32_t d_model, float *out_o, float *out_y, void *workspace, size_t workspace_bytes,
-                       int32_t num_splits, const kvq_decode_events *events, hipStream_t stream) {
+                       int32_t num_splits, const kvq_decode_events *events, hipStream_t stream,
+                       bool causal = false) {
   if (!valid_dtype(dtype)) return KVQ_ERR_UNSUPPORTED;
   int rc = check_cache(cache);
   if (rc) return rc;
@@ -193,7 +194,8 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
   float *ypart = reinterpret_cast<float *>(ws + pl.off_ypart);
   float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
   const RotDev rk = to_dev(*rot_k), rv = to_dev(*rot_v);
-  if (windows && !decode_mfma_supported(pl, cache->page_size)) return KVQ_ERR_UNSUPPORTED;
+  if ((windows || causal) && !decode_mfma_supported(pl, cache->page_size)) return KVQ_ERR_UNSUPPORTED;
+  if (windows && causal) return KVQ_ERR_UNSUPPORTED;
   WindowDev wd{};
   if (windows) {
     wd.sink_k = static_cast<const uint16_t *>(windows->sink_k);
@@ -209,7 +211,7 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
     if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
     KVQ_TRY(launch_decode_mfma(pl, q, dtype, rk, rv, cache->pages, cache->num_pages, cache->page_size, page_table,
                                max_pages_per_seq, seq_lens, part, reinterpret_cast<uint64_t *>(ws + pl.off_cnt),
-                               out_o, ot, stream, windows ? &wd : nullptr));
+                               out_o, ot, stream, windows ? &wd : nullptr, causal));
     if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
   } else {
     KVQ_TRY(launch_query_rotation(q, dtype, pl, rk, qrot, qsum, stream));
@@ -247,6 +249,17 @@ int kvq_decode_attn_windows(const void *q, int32_t dtype, int32_t num_seqs, int3
   return decode_attn(q, dtype, num_seqs, queries_per_seq, num_q_heads, cache, page_table, max_pages_per_seq, seq_lens,
                      max_seq_len, rot_k, rot_v, windows, key_mean, w_o, d_model, out_o, out_y, workspace,
                      workspace_bytes, num_splits, nullptr, stream);
+}
+
+int kvq_decode_attn_causal(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,
+                           int32_t num_q_heads, const kvq_cache *cache, const int32_t *page_table,
+                           int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                           const kvq_rotation *rot_k, const kvq_rotation *rot_v, const void *w_o, int32_t d_model,
+                           float *out_o, float *out_y, void *workspace, size_t workspace_bytes, int32_t num_splits,
+                           hipStream_t stream) {
+  return decode_attn(q, dtype, num_seqs, queries_per_seq, num_q_heads, cache, page_table, max_pages_per_seq, seq_lens,
+                     max_seq_len, rot_k, rot_v, nullptr, nullptr, w_o, d_model, out_o, out_y, workspace,
+                     workspace_bytes, num_splits, nullptr, stream, true);
 }
 
 int kvq_window_write(const void *k, const void *v, int32_t dtype, int64_t num_tokens, const int32_t *seq_idx,

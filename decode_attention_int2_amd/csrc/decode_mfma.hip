@@ -130,6 +130,7 @@ struct MfmaArgs {
   float *part;                // [rows][Hq][parts][132] partials, one per (split, wave) or per split
   int parts;                  // splits * 8, or splits when the waves' partials are merged first (premerge)
   int pstride;                // partial slots per (row, head): parts, plus one window slot per split
+  int causal;                 // row qi of a sequence attends its first L - (Nq - 1 - qi) tokens
   int premerge;
   // BF16 windows (decode with windows): sink [num_seqs][win_S][H][128] and
   // recent [num_seqs][win_W][H][128] (position p in slot p % win_W), bf16;
@@ -379,6 +380,7 @@ struct State {
   int kappa;
   bool have_ref;
   bool flushed;         // (wave-uniform) the LDS accumulators hold flushed values
+  int tlim;             // tokens below tlim count for this lane's query row (split end, or the row's causal length)
 };
 
 __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &blk, State &st, float *facc) {
@@ -396,7 +398,7 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     sv[q] = half_bits_to_float(blk.vm[q] & 0xffffu);
     zv[q] = half_bits_to_float(blk.vm[q] >> 16);
     // (rows past the group's last hold q' = 0: finite logits, never stored)
-    const bool valid = 16 * q + c.c < c.t_end - t0;
+    const bool valid = 16 * q + c.c < st.tlim - t0;
     logit[q] = valid ? dot * (ks * st.unscale) + kz * st.qsum : -INFINITY;
     int es;
     (void)frexpf(sv[q], &es);  // s_v < 2^es
@@ -804,6 +806,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     __syncthreads();  // (wsum read before the main loop's flushes write facc_all)
   }
   st.row_ok = hr < nrows;
+  st.tlim = c.t_end;
+  if (a.causal) st.tlim = min(c.t_end, L - (a.Nq - 1 - (row0 + hr) / a.G));
   const int x = lane & 3;
   st.sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
   st.sel2 = (x & 2) ? 0x03020706u : 0x05040100u;
@@ -1066,7 +1070,7 @@ bool decode_mfma_supported(const DecodePlan &pl, int page_size) {
 hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, RotDev rk, RotDev rv,
                               const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
                               int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
-                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win) {
+                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win, bool causal) {
   if (pl.num_seqs == 0) return hipSuccess;
   const uint32_t epoch = next_launch_epoch();
   MfmaArgs a{};
@@ -1081,6 +1085,7 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.premerge = pl.splits > kMaxSplitsNoPremerge ? 1 : 0;
   a.parts = a.premerge ? pl.splits : pl.splits * kWaves;
   a.pstride = a.parts + (win ? pl.splits : 0);
+  a.causal = causal ? 1 : 0;
   a.max_seq_len = pl.max_seq_len;
   a.P = page_size;
   a.p_shift = __builtin_ctz(static_cast<unsigned>(page_size));

@@ -328,7 +328,8 @@ constexpr int kMaxWindowTokens = 384;  // num_sink + num_recent (the merge holds
 hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, RotDev rk, RotDev rv,
                               const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
                               int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
-                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win = nullptr);
+                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win = nullptr,
+                              bool causal = false);
 // Split-K partial attention over raw (unquantized, unrotated) K and V that
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,

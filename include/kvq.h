@@ -188,6 +188,20 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
                     void *workspace, size_t workspace_bytes, int32_t num_splits, const kvq_decode_events *events,
                     hipStream_t stream);
 
+/* kvq_decode_attn with causal queries (a chunk of the last query positions,
+ * as in the pages' objective over the final 64 query positions of a
+ * sequence, [OptR] Appendix, calibration data and output-space error): the
+ * queries_per_seq rows of sequence b are its last positions, so row qi
+ * attends tokens t < seq_lens[b] - (queries_per_seq - 1 - qi) only (a row
+ * left with no token gives out_o = 0).  Same arguments, workspace and limits
+ * as kvq_decode_attn; UNSUPPORTED for page sizes that are not a power of two. */
+int kvq_decode_attn_causal(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,
+                           int32_t num_q_heads, const kvq_cache *cache, const int32_t *page_table,
+                           int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                           const kvq_rotation *rot_k, const kvq_rotation *rot_v, const void *w_o, int32_t d_model,
+                           float *out_o, float *out_y, void *workspace, size_t workspace_bytes, int32_t num_splits,
+                           hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * BF16 sink and recent windows ([OptR] §5, implementation details: 64 sink
  * and 256 recent tokens stay in BF16, 2.32 bits per element at a 64K-token
