@@ -328,6 +328,11 @@ __device__ __forceinline__ void load_addr(const Ctx &c, int t0, Addr &ad) {
   }
 }
 
+__device__ __forceinline__ void repoint_all(Addr &ad) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ad.pg[q] = 0;
+}
+
 // global-memory pointers (address space 1): scalar base + 32-bit lane offset
 typedef const __attribute__((address_space(1))) uint8_t *gbyte_ptr;
 __device__ __forceinline__ uint2 gload_u64(gbyte_ptr base, uint32_t off) {
@@ -364,6 +369,15 @@ __device__ __forceinline__ void load_block(const Ctx &c, const Addr &ad, Blk &o,
     o.km[q] = gload_u32(reinterpret_cast<gbyte_ptr>(mb), vo_km);
     o.vm[q] = gload_u32(reinterpret_cast<gbyte_ptr>(mb), vo_vm);
   }
+}
+
+// The split's last block may hold slots at or past the sequence's end, whose
+// bytes may be anything: their tokens are masked, and the value metadata is
+// zeroed so that no inf or NaN scale or zero-point reaches the sums (0 * inf).
+__device__ __forceinline__ void mask_tail_meta(const Ctx &c, int t0, Blk &blk) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (t0 + 16 * q + c.c >= c.t_end) blk.vm[q] = 0u;
 }
 
 struct State {
@@ -517,12 +531,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   c.g = lane >> 4;
   float *facc = &facc_all[wave][lane];
 
-  // (the arrival counter's validation word, read now: its round trip is
-  // hidden behind the kernel's first loads)
+  // the arrival counter and its validation word (read by wave 0 once the
+  // prologue's loads are out -- loads complete in issue order, so the
+  // coherent read's round trip delays none of them -- and compared at the
+  // arrival)
   unsigned long long *cnt = a.counters + unit * kArrivalWords;
-  bool cnt_valid = false;
-  if (threadIdx.x == 0)
-    cnt_valid = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == arrival_valid_value(cnt);
+  unsigned long long cnt_word = 0;
   int L = a.seq_lens[b];
   bool bad = L < 0 || L > a.max_seq_len;
   if (bad) L = 0;
@@ -612,6 +626,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   load_addr<P16>(c, t_begin + kBlk * jc0, a0);
   load_addr<P16>(c, t_begin + kBlk * jc1, a1);
   load_addr<P16>(c, t_begin + kBlk * jc2, a2);
+  if (nb == 0) {
+    // an empty split (a sequence with no token here, perhaps none at all)
+    // reads page 0, unused: its table entry 0 need not be valid
+    repoint_all(a0);
+    repoint_all(a1);
+    repoint_all(a2);
+  }
   load_block<P16>(c, a0, b0, bad);
   load_block<P16>(c, a1, b1, bad);
 
@@ -685,6 +706,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   st.unscale = ldexpf(1.0f, -qshift_s[hr]);
   st.qsum = qsum_s[hr];
   load_block<P16>(c, a2, b2, bad);
+  if (wave == 0) cnt_word = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (kWin) {
     // ---- this split's window tokens in fp32 while its first blocks load:
     // logits of the group's raw query rows against q . (k - mu), a softmax
@@ -839,6 +861,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   load_addr<P16>(c, t_begin + kBlk * min(ja0, nb), a0);
   auto step = [&](Blk &bk, int &jc, Addr &ak, int &ja, Addr &ak1, int &ja1n) {
     const uint32_t v = claim();
+    if (jc == nb - 1) mask_tail_meta(c, t_begin + kBlk * jc, bk);  // (wave-uniform: one block per split)
     compute_block(c, t_begin + kBlk * jc, bk, st, facc);
     load_block<P16>(c, ak, bk, bad);
     jc = ja;
@@ -979,7 +1002,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // write-back or invalidation is needed for that.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_valid, a.epoch, a.splits) ? 1u : 0u;
+  if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_word == arrival_valid_value(cnt), a.epoch, a.splits) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
   // dense R_V: the head's matrix is staged in LDS by the whole workgroup

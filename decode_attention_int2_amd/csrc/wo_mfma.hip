@@ -95,12 +95,8 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
   const int kw0 = ks * (kWaves * kWaveRows) + wave * kWaveRows;
   const int nk = min(max(a.K - kw0, 0), kWaveRows);  // rows of this wave
   const float *o = a.ot + static_cast<size_t>(rg) * a.K * 16;
-  // arrival counter of this (row group, column block) and its validation
-  // word (read now: the round trip overlaps the loads)
+  // arrival counter of this (row group, column block)
   unsigned long long *cnt = a.counters + (static_cast<size_t>(rg) * gridDim.x + cb) * kArrivalWords;
-  bool cnt_valid = false;
-  if (a.kslices > 1 && threadIdx.x == 0)
-    cnt_valid = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == arrival_valid_value(cnt);
 
   // all loads of the wave first (rows past the wave's share read as zero)
   typename WRaw<DT>::type wv[kSteps];
@@ -126,6 +122,11 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
       }
     }
   }
+  // the counter's validation word, read by wave 0 behind its loads (which
+  // complete in issue order: the coherent read delays none of them) and
+  // compared at the arrival
+  unsigned long long cnt_word = 0;
+  if (a.kslices > 1 && wave == 0) cnt_word = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   v4f acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
-    s_last = arrive_counted(cnt, cnt_valid, a.epoch, a.kslices) ? 1u : 0u;
+    s_last = arrive_counted(cnt, cnt_word == arrival_valid_value(cnt), a.epoch, a.kslices) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
 #pragma unroll

@@ -215,6 +215,43 @@ def test_decode_edge_cases(dev):
     assert np.all(o[0] == 0.0) and rel_l2(o[1], ref_o[1]) <= 2e-2
 
 
+@pytest.mark.parametrize("page_size,splits", [(16, 0), (16, 3), (64, 0)])
+def test_decode_ignores_slots_and_table_entries_past_the_length(dev, page_size, splits):
+    """Positions at or past a sequence's length are never used: their cache
+    slots hold 0xFF bytes (codes 3, fp16 NaN metadata) and their page-table
+    entries point outside the cache, and the outputs still match the oracle
+    reading the valid positions; an empty sequence with a wholly invalid
+    table row gives zeros."""
+    from decode_attention_int2_amd import kvq
+    T = 900
+    w = synthetic.make("paged16x32k", dev, tokens=T, num_seqs=4, H=2, Hq=8, d_model=64, page_size=page_size)
+    cache = gpu_quantize(w, dev)
+    lens = [T, 37, 0, 517]
+    w.seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    P = page_size
+    pages = cache.pages.cpu().numpy()
+    pt = w.page_table.cpu().numpy().copy()
+    for b, L in enumerate(lens):
+        for p in range(L, T):
+            pg, o = pt[b, p // P], p % P
+            for lo, width in ((32 * o, 32), (32 * P + 32 * o, 32), (64 * P + 4 * o, 4), (68 * P + 4 * o, 4)):
+                pages[pg, :, lo:lo + width] = 0xFF
+        first_unused = (L + P - 1) // P
+        pt[b, first_unused:] = w.num_pages + 1000 + np.arange(pt.shape[1] - first_unused)
+    cache.pages.copy_(torch.from_numpy(pages))
+    ptd = torch.from_numpy(pt).to(dev)
+    out_o, out_y = gpu_decode(w, cache, dev, page_table=ptd, num_splits=splits)
+    w.page_table = ptd
+    (ref_o, ref_y), _ = oracle_decode_on_cache(w, pages, range(4))
+    o, y = f32np(out_o), f32np(out_y)
+    assert np.all(o[2] == 0.0) and np.all(y[2] == 0.0)
+    live = [0, 1, 3]
+    eo, ey = rel_l2(o[live], ref_o[live]), rel_l2(y[live], ref_y[live])
+    per = max(rel_l2(o[r, j], ref_o[r, j]) for r in live for j in range(w.Hq))
+    print(f"P={P} splits={splits}: rel-L2 out_o {eo:.2e} (worst head {per:.2e}), out_y {ey:.2e}")
+    assert eo <= 1e-4 and per <= 1e-4 and ey <= 1e-4
+
+
 def test_api_rejects_bad_arguments(dev):
     from decode_attention_int2_amd import kvq
     w = synthetic.make("paged16x32k", dev, tokens=64, num_seqs=1, H=2, Hq=4, d_model=32)
