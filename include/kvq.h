@@ -149,6 +149,10 @@ int kvq_quantize(const void *k, const void *v, int32_t dtype, int64_t num_tokens
  *   o'     = sum_t p_t v_hat_t;   out_o[r][j] = o' R_V[h]^T
  *   out_y[r] = sum_j out_o[r][j] W_O[j*128 : j*128+128, :]
  * Token t of sequence b sits in page page_table[b][t / P] at position t % P.
+ * Only tokens t < seq_lens[b] are used: the cache slots at or past a
+ * sequence's length and the table entries of pages holding none of its
+ * tokens may hold anything (a table entry outside [0, num_pages) for a page
+ * that does hold tokens makes that sequence's outputs NaN).
  *
  *   q            [num_seqs * queries_per_seq][Hq][128], dtype.
  *   page_table   int32 [num_seqs][max_pages_per_seq], or NULL for page
