@@ -21,6 +21,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Xclang", "-tar
          "-packed-fp32-ops", "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
          # matrix-core results and accumulators in ordinary VGPRs (no AGPR copies)
          "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
+         # every atomic here is issued by one lane (block claims, arrivals):
+         # no wave-wide rewrite, whose immediate wait on the returned value
+         # would also wait for the scalar loads in flight
+         "-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None",
+         # loops whose branches are all wave-uniform keep their exits: a
+         # restructured exit path back to the loop head makes the wait
+         # insertion assume the newest loads feed the first step (the decode
+         # loop would then drain its loads in flight once per iteration)
+         "-Xarch_device", "-mllvm=-structurizecfg-skip-uniform-regions=true",
          "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -419,14 +419,11 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     umax = fmaxf(umax, logit[q] + static_cast<float>(es));
   }
   umax = row16_max(umax);
-  int need = st.kappa;
-  if (umax != -INFINITY) {
-    need = (kWeightBits - 1) - static_cast<int>(ceilf(umax));
-    if (!st.have_ref) {
-      st.kappa = need - kHeadroom;
-      st.have_ref = true;
-    }
-  }
+  // (selects, no branch; a row whose tokens are all masked keeps its scale)
+  const bool fin = umax != -INFINITY;
+  const int need = fin ? (kWeightBits - 1) - static_cast<int>(ceilf(fin ? umax : 0.0f)) : st.kappa;
+  st.kappa = fin && !st.have_ref ? need - kHeadroom : st.kappa;
+  st.have_ref = st.have_ref || fin;
   // wave-uniform decision: flush when any row outgrew its headroom
   if (__any(st.have_ref && need < st.kappa)) {
     const int newk = (st.have_ref && need < st.kappa) ? need - kHeadroom : st.kappa;
@@ -852,11 +849,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // claimed block into ad[k+1] (whose block was issued two steps earlier).
   // Claims increase, so a block past the split's end ends the loop; loads of
   // such blocks re-read the split's last tile and are not used.
-  auto claim = [&]() -> uint32_t {
-    uint32_t v = 0;
-    if (lane == 0) v = atomicAdd(&s_next, 1u);
-    return v;
-  };
+  // (every lane takes part, lane 0 adding 1 and the others 0: no divergent
+  // branch in the loop, whose exits then stay direct -- a restructured exit
+  // that could reach the loop head from mid-body would make the first step
+  // wait for all three blocks in flight)
+  auto claim = [&]() -> uint32_t { return atomicAdd(&s_next, lane == 0 ? 1u : 0u); };
   ja0 = __builtin_amdgcn_readfirstlane(claim());
   load_addr<P16>(c, t_begin + kBlk * min(ja0, nb), a0);
   auto step = [&](Blk &bk, int &jc, Addr &ak, int &ja, Addr &ak1, int &ja1n) {
