@@ -191,7 +191,6 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
   float *qrot = reinterpret_cast<float *>(ws + pl.off_qrot);
   float *qsum = reinterpret_cast<float *>(ws + pl.off_qsum);
   float *part = reinterpret_cast<float *>(ws + pl.off_part);
-  float *ypart = reinterpret_cast<float *>(ws + pl.off_ypart);
   float *ot = w_o ? reinterpret_cast<float *>(ws + pl.off_ot) : nullptr;
   const RotDev rk = to_dev(*rot_k), rv = to_dev(*rot_v);
   if ((windows || causal) && !decode_mfma_supported(pl, cache->page_size)) return KVQ_ERR_UNSUPPORTED;
@@ -211,7 +210,8 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
     if (events && events->split_start) KVQ_TRY(hipEventRecord(events->split_start, stream));
     KVQ_TRY(launch_decode_mfma(pl, q, dtype, rk, rv, cache->pages, cache->num_pages, cache->page_size, page_table,
                                max_pages_per_seq, seq_lens, part, reinterpret_cast<uint64_t *>(ws + pl.off_cnt),
-                               out_o, ot, stream, windows ? &wd : nullptr, causal));
+                               out_o, ot, stream, windows ? &wd : nullptr, causal, w_o ? out_y : nullptr,
+                               pl.d_model));
     if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
   } else {
     KVQ_TRY(launch_query_rotation(q, dtype, pl, rk, qrot, qsum, stream));
@@ -219,12 +219,11 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
     KVQ_TRY(launch_decode_split(pl, cache->pages, cache->num_pages, cache->page_size, page_table, max_pages_per_seq,
                                 seq_lens, qrot, qsum, part, stream));
     if (events && events->split_stop) KVQ_TRY(hipEventRecord(events->split_stop, stream));
-    KVQ_TRY(launch_combine(pl, part, rv, out_o, ot, stream));
+    KVQ_TRY(launch_combine(pl, part, rv, out_o, ot, stream, w_o ? out_y : nullptr));
   }
   if (events && events->attn_stop) KVQ_TRY(hipEventRecord(events->attn_stop, stream));
   if (w_o)
-    KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, ypart, reinterpret_cast<uint64_t *>(ws + pl.off_wocnt), out_y,
-                                 stream));
+    KVQ_TRY(launch_wo_projection(pl, ot, w_o, dtype, out_y, stream));
   return KVQ_OK;
 }
 

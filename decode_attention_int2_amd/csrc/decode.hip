@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 constexpr int kMaxCombineSplits = kMaxSplits;
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *part, int n_items, int splits, int Hq, int G,
-                                                      RotDev rv, float *out_o, float *ot) {
+                                                      RotDev rv, float *out_o, float *ot, float *y_zero, int d_model) {
   const int lane = threadIdx.x & 63;
   const int rj = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rj >= n_items) return;
@@ -316,6 +316,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *part, int n_i
   merge_splits_wave(part + static_cast<size_t>(rj) * splits * (D + 4), splits, lane, o0, o1);
   unrotate_value_wave(o0, o1, rv, j / G, lane);
   store_output_wave(out_o, ot, row, j, Hq, lane, o0, o1);
+  if (y_zero && j == 0)  // the row's W_O output starts at zero (the projection adds into it)
+    for (int i = lane; i < d_model; i += 64) y_zero[static_cast<size_t>(row) * d_model + i] = 0.0f;
 }
 
 
@@ -380,9 +382,7 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   // W_O: K slices so that column blocks x slices x row groups fill the chip
   const int K = Hq * D;
   const size_t rows_w = static_cast<size_t>(num_seqs) * queries_per_seq;
-  const int col_blocks = d_model > 0 ? wo_col_blocks(d_model) : 1;
   const int row_groups = static_cast<int>((rows_w + kWoRows - 1) / kWoRows);
-  const int ks = wo_kslices(K);
   const size_t rows = static_cast<size_t>(num_seqs) * queries_per_seq;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t off = 0;
@@ -393,12 +393,8 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
   pl.off_part = off;
   // (the matrix-core kernel writes one partial per (split, wave), and one per split for the BF16 windows)
   off = align(off + rows * Hq * static_cast<size_t>(pl.splits) * (kMfmaWaves + 1) * (D + 4) * sizeof(float));
-  pl.off_ypart = off;
-  off = align(off + (d_model > 0 && ks > 1 ? static_cast<size_t>(ks) * rows * d_model * sizeof(float) : 0));
   pl.off_ot = off;  // [row groups][K][16] copy of o for the W_O projection
   off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * K * kWoRows * sizeof(float) : 0));
-  pl.off_wocnt = off;  // [row groups][column blocks][kArrivalWords] uint64 arrival counters of the W_O slices
-  off = align(off + (d_model > 0 ? static_cast<size_t>(row_groups) * col_blocks * kArrivalWords * sizeof(uint64_t) : 0));
   const size_t n_rg_all = static_cast<size_t>(num_seqs) * H * ((queries_per_seq * (Hq / H) + 3) / 4);
   pl.off_cnt = off;  // [num_seqs][H][row groups][kArrivalWords] uint64
   off = align(off + n_rg_all * kArrivalWords * sizeof(uint64_t));
@@ -446,11 +442,11 @@ hipError_t launch_decode_split(const DecodePlan &pl, const uint8_t *pages, int64
 }
 
 hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, float *ot,
-                          hipStream_t stream) {
+                          hipStream_t stream, float *y_zero) {
   const int n = pl.num_seqs * pl.queries_per_seq * pl.Hq;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3((n + 3) / 4), dim3(256), 0, stream, part, n, pl.splits, pl.Hq, pl.G, rv,
-                     out_o, ot);
+                     out_o, ot, y_zero, pl.d_model);
   return hipGetLastError();
 }
 

@@ -141,6 +141,8 @@ struct MfmaArgs {
   unsigned long long *counters;  // [num_seqs][H][n_rg][kArrivalWords] arrival counters
   uint32_t epoch;
   float *out_o, *ot;
+  float *y_zero;              // [num_seqs * Nq][d_model] to clear (the W_O launch adds into it), or null
+  int d_model;
 };
 
 // Fixed-point int8 digits of the 4 query rows of a row group (qs: their q',
@@ -1078,6 +1080,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     }
   }
   if (wave < nrows) store_output_wave(a.out_o, a.ot, row, j, a.Hq, lane, o0, o1);
+  if (a.y_zero && h == 0) {
+    // the query positions of this group start their W_O rows at zero (the
+    // projection that follows on the stream adds its K slices into them)
+    for (int r = 0; r < nrows; ++r) {
+      const int qr = (row0 + r) / a.G;
+      if (r > 0 && qr == (row0 + r - 1) / a.G) continue;
+      float *yr = a.y_zero + (static_cast<size_t>(b) * a.Nq + qr) * a.d_model;
+      for (int i = threadIdx.x; i < a.d_model; i += 64 * kWaves) yr[i] = 0.0f;
+    }
+  }
 }
 
 }  // namespace
@@ -1090,7 +1102,8 @@ bool decode_mfma_supported(const DecodePlan &pl, int page_size) {
 hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, RotDev rk, RotDev rv,
                               const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
                               int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
-                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win, bool causal) {
+                              float *out_o, float *ot, hipStream_t stream, const WindowDev *win, bool causal,
+                              float *y_zero, int d_model) {
   if (pl.num_seqs == 0) return hipSuccess;
   const uint32_t epoch = next_launch_epoch();
   MfmaArgs a{};
@@ -1133,6 +1146,8 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.epoch = epoch;
   a.out_o = out_o;
   a.ot = ot;
+  a.y_zero = y_zero;
+  a.d_model = d_model;
   if (win) {
     a.win_sk = win->sink_k;
     a.win_sv = win->sink_v;

@@ -293,9 +293,8 @@ struct DecodePlan {
   int num_seqs, queries_per_seq, Hq, H, G, rows_per_head;  // rows_per_head = queries_per_seq * G
   int max_seq_len, splits, split_tokens;                   // split_tokens % kChunk == 0
   int d_model;
-  size_t off_qrot, off_qsum, off_part, off_ypart;          // workspace layout (bytes)
+  size_t off_qrot, off_qsum, off_part;                     // workspace layout (bytes)
   size_t off_ot;                                           // o laid out for the W_O projection
-  size_t off_wocnt;                                        // arrival counters of the W_O K slices
   size_t off_cnt;                                          // split arrival counters (matrix-core kernel)
   size_t total;
 };
@@ -329,20 +328,21 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
                               const uint8_t *pages, int64_t num_pages, int page_size, const int32_t *page_table,
                               int max_pages, const int32_t *seq_lens, float *part, uint64_t *counters,
                               float *out_o, float *ot, hipStream_t stream, const WindowDev *win = nullptr,
-                              bool causal = false);
+                              bool causal = false, float *y_zero = nullptr, int d_model = 0);
 // Split-K partial attention over raw (unquantized, unrotated) K and V that
 // every query row attends in full (reference readout of the candidate search).
 hipError_t launch_reference_split(const DecodePlan &pl, const void *k, const void *v, int dtype,
                                   int64_t num_tokens, const float *qrot, float *part, hipStream_t stream);
 // Merge splits, inverse value rotation, write out_o (and the W_O operand
-// copy `ot` when not null).
+// copy `ot` when not null).  y_zero (rows x pl.d_model, or null) is cleared
+// for the W_O projection, which adds into it.
 hipError_t launch_combine(const DecodePlan &pl, const float *part, RotDev rv, float *out_o, float *ot,
-                          hipStream_t stream);
-// out_y = concat(out_o) W_O, from the copy `ot` written with out_o.
+                          hipStream_t stream, float *y_zero = nullptr);
 // out_y = concat(out_o) W_O on the matrix cores, from the copy `ot` written
-// with out_o; `counters` are the plan's W_O arrival counters.
-hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *ypart,
-                                uint64_t *counters, float *out_y, hipStream_t stream);
+// with out_o.  With several K slices the slices add into out_y, which the
+// launch that wrote `ot` has cleared (y_zero).
+hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *out_y,
+                                hipStream_t stream);
 int wo_kslices(int K);          // K slices of the W_O projection
 int wo_col_blocks(int d_model); // column blocks of the W_O projection
 

@@ -14,9 +14,9 @@
 // One workgroup of 8 waves per (64 columns, K slice of 1,024 rows, row
 // group); each wave takes 128 rows of the slice and issues all of its loads
 // before the first product.  The 8 waves are summed in LDS in a fixed order;
-// with several K slices each workgroup stores its slice sum and the last of
-// them to arrive (tagged arrival counter) adds the slices in slice order, so
-// the result does not depend on timing.
+// with several K slices each workgroup adds its slice sum into y with fp32
+// atomics (y cleared by the launch that wrote the o copy), so the order of
+// the slice additions, and the last bits of y, vary from run to run.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -75,16 +75,12 @@ struct WoArgs {
   const float *ot;     // [row groups][K][16]
   const void *w;       // [K][d_model]
   int rows, K, d_model, kslices;
-  float *ypart;        // [kslices][rows][d_model] slice sums (kslices > 1)
-  unsigned long long *counters;  // [row groups][column blocks][kArrivalWords]
-  uint32_t epoch;
   float *y;            // [rows][d_model]
 };
 
 template <int DT>
 __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
   __shared__ float red[kWaves][16][kCols + 4];  // per wave: 16 rows x 64 columns (padded)
-  __shared__ uint32_t s_last;
   const int cb = blockIdx.x, ks = blockIdx.y, rg = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = lane & 15, kg = lane >> 4;
@@ -95,8 +91,6 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
   const int kw0 = ks * (kWaves * kWaveRows) + wave * kWaveRows;
   const int nk = min(max(a.K - kw0, 0), kWaveRows);  // rows of this wave
   const float *o = a.ot + static_cast<size_t>(rg) * a.K * 16;
-  // arrival counter of this (row group, column block)
-  unsigned long long *cnt = a.counters + (static_cast<size_t>(rg) * gridDim.x + cb) * kArrivalWords;
 
   // all loads of the wave first (rows past the wave's share read as zero)
   typename WRaw<DT>::type wv[kSteps];
@@ -122,11 +116,6 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
       }
     }
   }
-  // the counter's validation word, read by wave 0 behind its loads (which
-  // complete in issue order: the coherent read delays none of them) and
-  // compared at the arrival
-  unsigned long long cnt_word = 0;
-  if (a.kslices > 1 && wave == 0) cnt_word = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   v4f acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -159,31 +148,13 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
     }
     return;
   }
-  // slice sums: device-scope stores, acknowledged before the arrival
+  // several K slices: each adds its sums into y (cleared by the launch that
+  // wrote ot), fp32 atomics at the device's memory, no reply awaited
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int idx = threadIdx.x + 512 * u, r = idx >> 6, col = idx & 63;
     if (r < nrows && n0 + col < a.d_model)
-      __hip_atomic_store(a.ypart + (static_cast<size_t>(ks) * a.rows + rg * 16 + r) * a.d_model + n0 + col, sums[u],
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = arrive_counted(cnt, cnt_word == arrival_valid_value(cnt), a.epoch, a.kslices) ? 1u : 0u;
-  __syncthreads();
-  if (s_last == 0) return;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int idx = threadIdx.x + 512 * u, r = idx >> 6, col = idx & 63;
-    if (r < nrows && n0 + col < a.d_model) {
-      const size_t off = static_cast<size_t>(rg * 16 + r) * a.d_model + n0 + col;
-      float v = __hip_atomic_load(a.ypart + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int s2 = 1; s2 < a.kslices; ++s2)
-        v += __hip_atomic_load(a.ypart + static_cast<size_t>(s2) * a.rows * a.d_model + off, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      a.y[off] = v;
-    }
+      unsafeAtomicAdd(a.y + static_cast<size_t>(rg * 16 + r) * a.d_model + n0 + col, sums[u]);
   }
 }
 
@@ -192,8 +163,8 @@ __global__ __launch_bounds__(64 * kWaves) void wo_mfma_kernel(WoArgs a) {
 int wo_kslices(int K) { return (K + kWaves * kWaveRows - 1) / (kWaves * kWaveRows); }
 int wo_col_blocks(int d_model) { return (d_model + kCols - 1) / kCols; }
 
-hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *ypart,
-                                uint64_t *counters, float *out_y, hipStream_t stream) {
+hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const void *w_o, int dtype, float *out_y,
+                                hipStream_t stream) {
   const int rows = pl.num_seqs * pl.queries_per_seq;
   if (rows == 0 || pl.d_model <= 0) return hipSuccess;
   WoArgs a{};
@@ -203,9 +174,6 @@ hipError_t launch_wo_projection(const DecodePlan &pl, const float *ot, const voi
   a.K = pl.Hq * D;
   a.d_model = pl.d_model;
   a.kslices = wo_kslices(a.K);
-  a.ypart = ypart;
-  a.counters = reinterpret_cast<unsigned long long *>(counters);
-  a.epoch = next_launch_epoch();
   a.y = out_y;
   const dim3 grid(wo_col_blocks(pl.d_model), a.kslices, (rows + 15) / 16);
   if (dtype == KVQ_F32)
