@@ -11,9 +11,11 @@
 // bytes for bf16) and tile j's output column c is n0 + 4c + j.  bf16
 // weights are widened exactly; products and sums are fp32.
 //
-// One workgroup of 8 waves per (64 columns, K slice of 1,024 rows, row
-// group); each wave takes 128 rows of the slice and issues all of its loads
-// before the first product.  The 8 waves are summed in LDS in a fixed order;
+// One workgroup of 8 waves per (64 columns, K slice of 512 rows, row
+// group); each wave takes 64 rows of the slice and issues all of its loads
+// before the first product.  (Slices of 512 rows give two workgroups per CU
+// at d_model = 4096, whose load round trips overlap: 2.7 us less per call
+// than slices of 1,024 rows at 16 rows x [4096, 4096].)  The 8 waves are summed in LDS in a fixed order;
 // with several K slices each workgroup adds its slice sum into y with fp32
 // atomics (y cleared by the launch that wrote the o copy), so the order of
 // the slice additions, and the last bits of y, vary from run to run.
@@ -26,7 +28,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kCols = 64;                 // columns per workgroup
 constexpr int kWaves = 8;
-constexpr int kWaveRows = 128;            // K rows per wave
+constexpr int kWaveRows = 64;             // K rows per wave
 constexpr int kSteps = kWaveRows / 4;     // matrix-core steps per wave
 
 template <int DT>
