@@ -252,6 +252,21 @@ def test_decode_ignores_slots_and_table_entries_past_the_length(dev, page_size, 
     assert eo <= 1e-4 and per <= 1e-4 and ey <= 1e-4
 
 
+def test_decode_vector_path_pages_of_48_tokens(dev):
+    """A page size that is not a power of two takes the VALU split kernel and
+    the separate merge launch, which also clears out_y before the W_O
+    projection adds its K slices (d_model 200: two slices, ragged column
+    block); out_y starts at 12345 so a row left uncleared fails."""
+    w = synthetic.make("paged16x32k", dev, tokens=900, num_seqs=3, H=2, Hq=8, d_model=200, page_size=48)
+    w.seq_lens = torch.tensor([900, 433, 47], dtype=torch.int32, device=dev)
+    cache = gpu_quantize(w, dev)
+    out_o, out_y = gpu_decode(w, cache, dev)
+    (ref_o, ref_y), _ = oracle_decode_on_cache(w, cache.pages.cpu().numpy(), range(3))
+    eo, ey = rel_l2(f32np(out_o), ref_o), rel_l2(f32np(out_y), ref_y)
+    print(f"P=48: rel-L2 out_o {eo:.2e}, out_y {ey:.2e}")
+    assert eo <= 1e-4 and ey <= 1e-4
+
+
 def test_api_rejects_bad_arguments(dev):
     from decode_attention_int2_amd import kvq
     w = synthetic.make("paged16x32k", dev, tokens=64, num_seqs=1, H=2, Hq=4, d_model=32)
