@@ -379,6 +379,148 @@ def test_candidate_nmse_zero_when_lossless_and_scale_invariant(oracle):
     assert np.allclose(a, c, rtol=1e-12)
 
 
+# ---------------------------------------------------------------- candidate search: closed forms
+def _dequant_group(oracle, x, clip):
+    """x_hat of one 128-group through the oracle's quantizer (pinned above by
+    brute force), widened to fp64."""
+    codes, sb, zb = oracle.quantize_group(x, clip)
+    s, z = np.float32(oracle.f16_bits_to_f32(sb)), np.float32(oracle.f16_bits_to_f32(zb))
+    return (codes.astype(np.float32) * s + z).astype(np.float64)
+
+
+def _constant_value_case(rng, T, H, G, dm, zero_block=None):
+    """Every token of KV head h carries the same value vector u_h, so the
+    softmax weights sum the same vector: o = u_h for any keys and queries, in
+    the full-precision readout, and o_hat = u_hat_h (one quantized group) in
+    the quantized one [OptR, §3 Eq. (1)-(2)]."""
+    Hq = H * G
+    u = rng.standard_normal((H, D)).astype(np.float32)
+    u[:, :4] *= 8.0                                  # outliers: the INT2 error is large
+    k = (rng.standard_normal((T, H, D)) * 2).astype(np.float32)
+    v = np.broadcast_to(u[None], (T, H, D)).copy()
+    q = rng.standard_normal((3, Hq, D)).astype(np.float32)
+    w = rng.standard_normal((Hq * D, dm)).astype(np.float32)
+    for j in range(Hq):                               # head blocks of very different scale
+        w[j * D:(j + 1) * D] *= np.float32(3.0 ** j)
+    if zero_block is not None:
+        w[zero_block * D:(zero_block + 1) * D] = 0.0
+    return k, v, q, w, u
+
+
+def test_candidate_nmse_constant_values_closed_form(oracle):
+    """NMSE = ||(u_hat - u) W||^2 / ||u W||^2 with the denominator on the
+    full-precision output ([Eval]: NMSE against the unquantized output; [OptR]
+    §3.2 Eq. (10)); per KV head the squared errors and the squared norms of
+    its query heads are pooled before the ratio; joint mode sums the heads'
+    contributions y = sum_j o_j W_j before the norms (Eq. (3))."""
+    rng = np.random.default_rng(21)
+    T, H, G, dm = 40, 2, 2, 24
+    k, v, q, w, u = _constant_value_case(rng, T, H, G, dm)
+    ident = oracle.Rotation(oracle.ROT_IDENTITY)
+    clips = [1.0, 0.7]
+    w64 = w.astype(np.float64)
+    blk = [w64[j * D:(j + 1) * D] for j in range(H * G)]
+    for mode in (oracle.SELECT_PER_HEAD, oracle.SELECT_JOINT):
+        nm, nq, _ = oracle.candidate_nmse(k, v, q, [ident], clips, w, mode)
+        for ci, c in enumerate(clips):
+            uh = np.stack([_dequant_group(oracle, u[h], c) for h in range(H)])
+            du = uh - u.astype(np.float64)
+            if mode == oracle.SELECT_PER_HEAD:
+                for h in range(H):
+                    js = range(h * G, (h + 1) * G)
+                    num = sum(float(np.sum((du[h] @ blk[j]) ** 2)) for j in js)
+                    den = sum(float(np.sum((u[h].astype(np.float64) @ blk[j]) ** 2)) for j in js)
+                    expect = num / den
+                    assert abs(nm[h, 0, ci] - expect) <= 1e-9 * expect
+                    assert np.allclose(nq[h, 0, ci], expect, rtol=1e-9)
+                    # the pins discriminate: the prediction's norm and the mean of per-head ratios differ
+                    den_hat = sum(float(np.sum((uh[h] @ blk[j]) ** 2)) for j in js)
+                    ratios = [float(np.sum((du[h] @ blk[j]) ** 2) / np.sum((u[h].astype(np.float64) @ blk[j]) ** 2))
+                              for j in js]
+                    assert abs(num / den_hat - expect) > 1e-4 * expect
+                    assert abs(np.mean(ratios) - expect) > 1e-3 * expect
+            else:
+                dy = sum(du[j // G] @ blk[j] for j in range(H * G))
+                y = sum(u[j // G].astype(np.float64) @ blk[j] for j in range(H * G))
+                expect = float(np.sum(dy ** 2) / np.sum(y ** 2))
+                assert abs(nm[0, 0, ci] - expect) <= 1e-9 * expect
+                sep = sum(float(np.sum((du[j // G] @ blk[j]) ** 2)) for j in range(H * G)) / \
+                    sum(float(np.sum((u[j // G].astype(np.float64) @ blk[j]) ** 2)) for j in range(H * G))
+                assert abs(sep - expect) > 1e-4 * expect   # joint is not the pooled per-head sum
+
+
+def test_candidate_nmse_zero_wo_block_is_pooled_not_averaged(oracle):
+    """A query head whose W_O block is zero contributes nothing to the
+    post-W_O output: the per-head objective of its KV head is the other query
+    head's ratio alone (a mean of per-query-head ratios would divide 0 by 0)."""
+    rng = np.random.default_rng(22)
+    T, H, G, dm = 24, 1, 2, 16
+    k, v, q, w, u = _constant_value_case(rng, T, H, G, dm, zero_block=1)
+    ident = oracle.Rotation(oracle.ROT_IDENTITY)
+    nm, _, _ = oracle.candidate_nmse(k, v, q, [ident], [0.8], w, oracle.SELECT_PER_HEAD)
+    du = _dequant_group(oracle, u[0], 0.8) - u[0].astype(np.float64)
+    w0 = w[:D].astype(np.float64)
+    expect = float(np.sum((du @ w0) ** 2) / np.sum((u[0].astype(np.float64) @ w0) ** 2))
+    assert np.isfinite(nm[0, 0, 0]) and abs(nm[0, 0, 0] - expect) <= 1e-9 * expect
+
+
+def test_candidate_selection_takes_the_first_minimum(oracle):
+    """Exact ties (a candidate listed twice, a clip listed twice) select the
+    first of the tied entries in (candidate, clip) order, as numpy's argmin
+    over the row-major grid does."""
+    rng = np.random.default_rng(23)
+    T, H, G, dm = 48, 2, 1, 16
+    k = (rng.standard_normal((T, H, D)) * 1.5).astype(np.float32)
+    v = rng.standard_normal((T, H, D)).astype(np.float32)
+    v[:, :, :3] *= 6.0
+    q = rng.standard_normal((2, H * G, D)).astype(np.float32)
+    w = rng.standard_normal((H * G * D, dm)).astype(np.float32)
+    s = np.where(rng.random((H, D)) < 0.5, -1, 1).astype(np.int8)
+    sh = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=s)
+    clips = [0.85, 0.85, 1.0]
+    for mode in (oracle.SELECT_JOINT, oracle.SELECT_PER_HEAD):
+        nm, _, best = oracle.candidate_nmse(k, v, q, [sh, sh], clips, w, mode)
+        assert np.array_equal(nm[:, 0], nm[:, 1]) and np.array_equal(nm[:, :, 0], nm[:, :, 1])
+        for u in range(nm.shape[0]):
+            flat = nm[u].reshape(-1)
+            assert best[u] == int(np.argmin(flat))
+            assert best[u] < len(clips) and best[u] != 1   # candidate 0, and clip 0 over its duplicate
+
+
+def test_paged_decode_equals_contiguous_decode(oracle):
+    """Token t of sequence b is read from page page_table[b][t / P] at
+    position t % P (the cache layout of the C header): a permuted page table
+    with the tokens written through the matching slots decodes exactly as the
+    contiguous layout does, ragged last pages included."""
+    rng = np.random.default_rng(24)
+    B, H, Hq, P = 3, 2, 4, 16
+    lens = [70, 33, 16]
+    mp = 5
+    s = np.where(rng.random((H, D)) < 0.5, -1, 1).astype(np.int8)
+    rot = oracle.Rotation(oracle.ROT_SIGNED_HADAMARD, signs=s)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    contig = oracle.Cache(B * mp, P, H)
+    perm_pages = 2 * B * mp
+    paged = oracle.Cache(perm_pages, P, H)
+    table = rng.permutation(perm_pages)[:B * mp].reshape(B, mp).astype(np.int32)
+    for b, L in enumerate(lens):
+        k = (rng.standard_normal((L, H, D)) * 2).astype(np.float32)
+        v = rng.standard_normal((L, H, D)).astype(np.float32)
+        t = np.arange(L)
+        oracle.quantize(k, v, contig, rot, rot, clip_k=0.9, clip_v=0.95, slot_mapping=b * mp * P + t)
+        oracle.quantize(k, v, paged, rot, rot, clip_k=0.9, clip_v=0.95,
+                        slot_mapping=table[b, t // P].astype(np.int64) * P + t % P)
+    table[1, 3:] = -7          # entries of pages past a sequence's end are never read
+    a = oracle.decode(q, contig, lens, rot, rot, num_seqs=B, max_pages=mp, f64=True)
+    b2 = oracle.decode(q, paged, lens, rot, rot, num_seqs=B, page_table=table, max_pages=mp, f64=True)
+    assert np.array_equal(a, b2)
+    # and a wrong page in range changes the result
+    bad = table.copy()
+    bad[0, [0, 1]] = bad[0, [1, 0]]
+    c = oracle.decode(q, paged, lens, rot, rot, num_seqs=B, page_table=bad, max_pages=mp, f64=True)
+    assert not np.array_equal(a[0], c[0]) and np.array_equal(a[1:], c[1:])
+
+
 def test_population_sd_matches_page_figures(oracle):
     g = _gold()["threshold_quality"]
     nq = g["queries"]
