@@ -189,9 +189,21 @@ def decode_workload(name, dev, timed, median_of, min_bytes=0):
     kv_bytes = B * T * H * BYTES_PER_TOKEN_HEAD
     n = max(3, -(-min_bytes // kv_bytes))
     caches = [kvq.Cache(w.num_pages, w.page_size, H, device=dev) for _ in range(n)]
-    for c in caches:
-        kvq.kvq_quantize(w.k, w.v, c, rot, rot, key_mean=w.key_mean, clip_k=w.clip_k, clip_v=w.clip_v,
-                         slot_mapping=w.slot_mapping)
+    write = lambda i: kvq.kvq_quantize(w.k, w.v, caches[i % n], rot, rot, key_mean=w.key_mean, clip_k=w.clip_k,
+                                       clip_v=w.clip_v, slot_mapping=w.slot_mapping)
+    for i in range(n):
+        write(i)
+    # the cache write of the whole batch (dense rotation for the learned-rotation workloads)
+    wr_ms = median_of(lambda: timed(write, 10), 3)
+    n_tok = B * T
+    in_bytes = n_tok * H * 2 * 128 * w.k.element_size()
+    wr_bytes = in_bytes + kv_bytes
+    write_rec = {"rotation": {0: "identity", 1: "signed_hadamard", 2: "dense"}[w.rot_k.kind],
+                 "key_centering": w.key_mean is not None, "cache_write_us": round(wr_ms * 1e3, 2),
+                 "cache_write_mtok_s": round(n_tok / (wr_ms * 1e-3) / 1e6, 1),
+                 "cache_write_gbs": round(wr_bytes / (wr_ms * 1e-3) / 1e9, 1),
+                 "cache_write_pct_hbm_peak": round(100.0 * wr_bytes / (wr_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                 "cache_write_input_source": "hbm" if in_bytes > 2 * 256e6 else "mall-resident"}
     del w.k, w.v
     out_o = torch.empty((B * w.queries_per_seq, Hq, 128), dtype=torch.float32, device=dev)
     ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, w.queries_per_seq, Hq, H, T, 0, 0), dtype=torch.uint8,
@@ -202,7 +214,115 @@ def decode_workload(name, dev, timed, median_of, min_bytes=0):
     return {"workload": name, "description": synthetic.DESCRIPTIONS[name], "cache_copies": n,
             "source": "hbm" if n * kv_bytes > 2 * 256e6 else "mall-resident", "decode_attn_us": round(ms * 1e3, 2),
             "gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100.0 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+            "pct_hbm_peak": round(100.0 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2), **write_rec}
+
+
+def envelope_protocol(dev, timed, median_of):
+    """The evaluation page's protocol on its own workload (4,096 tokens x 4 KV
+    heads x 128, fp32, W_O [512, 128]): the joint search of identity + 8
+    signed-Hadamard candidates x 5 clips on 1 calibration query, the cache
+    write at the selected variant, then the decode of each of the 10 fresh
+    queries (one query per call, W_O included) and their post-W_O NMSE
+    statistics.  The page's own figures (host reference math next to an
+    NVIDIA L4) are quoted beside them for context."""
+    import torch
+    import synthetic
+    from decode_attention_int2_amd import kvq
+    w = synthetic.make("envelope", dev)
+    T, H, Hq, dm = w.tokens, w.H, w.Hq, w.d_model
+    clips, C = list(w.clips), len(w.candidates)
+    rots = [kvq.Rotation(c.kind, signs=c.signs, matrix=c.matrix) for c in w.candidates]
+    q_cal, q_eval = w.q[:1].contiguous(), w.q[1:].contiguous()
+    out = torch.empty((1, C, len(clips)), dtype=torch.float32, device=dev)
+    best = torch.empty((1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(kvq.kvq_candidate_workspace_bytes(T, H, Hq, 1, C, len(clips), dm), dtype=torch.uint8, device=dev)
+    search = lambda i: kvq.kvq_candidate_nmse(w.k, w.v, q_cal, rots, clips, w.w_o, kvq.KVQ_SELECT_JOINT, out, best,
+                                              workspace=ws)
+    search_ms = median_of(lambda: timed(search, 5), 3)
+    b = int(best.item())
+    r, ci = divmod(b, len(clips))
+    cache = kvq.Cache(w.num_pages, w.page_size, H, device=dev)
+    write = lambda i: kvq.kvq_quantize(w.k, w.v, cache, rots[r], rots[r], clip_k=clips[ci], clip_v=clips[ci],
+                                       slot_mapping=w.slot_mapping)
+    write_ms = median_of(lambda: timed(write, 20), 3)
+    out_o = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
+    out_y = torch.empty((1, dm), dtype=torch.float32, device=dev)
+    dws = torch.empty(kvq.kvq_decode_workspace_bytes(1, 1, Hq, H, T, dm, 0), dtype=torch.uint8, device=dev)
+    one = lambda i: kvq.kvq_decode_attn(q_eval[i % 10:i % 10 + 1], 1, 1, cache, w.page_table, w.page_table.shape[1],
+                                        w.seq_lens, T, rots[r], rots[r], out_o, w_o=w.w_o, out_y=out_y, workspace=dws)
+    dec_ms = median_of(lambda: timed(one, 50))
+    # per-query NMSE of the 10 fresh queries at the selected variant (C = 1, one clip)
+    e_out = torch.empty((1, 1, 1), dtype=torch.float32, device=dev)
+    e_q = torch.empty((1, 1, 1, 10), dtype=torch.float32, device=dev)
+    e_best = torch.empty((1,), dtype=torch.int32, device=dev)
+    e_ws = torch.empty(kvq.kvq_candidate_workspace_bytes(T, H, Hq, 10, 1, 1, dm), dtype=torch.uint8, device=dev)
+    kvq.kvq_candidate_nmse(w.k, w.v, q_eval, [rots[r]], [clips[ci]], w.w_o, kvq.KVQ_SELECT_JOINT, e_out, e_best,
+                           out_nmse_per_query=e_q, workspace=e_ws)
+    torch.cuda.synchronize()
+    x = e_q.double().cpu().flatten()
+    mean = float(x.mean())
+    sd = float(((x - mean) ** 2).mean().sqrt())
+    ok = (x <= 10.0).double()
+    qm = float(ok.mean())
+    qsd = float(((ok - qm) ** 2).mean().sqrt())
+    ident = out[0, 0].min().item()
+    return {"workload": "envelope", "description": synthetic.DESCRIPTIONS["envelope"],
+            "search_ms": round(search_ms, 4), "selected": {"candidate": r, "clip": clips[ci]},
+            "search_nmse_selected": round(float(out[0].flatten()[b]), 6), "search_nmse_identity_best": round(ident, 6),
+            "cache_write_us_selected": round(write_ms * 1e3, 2),
+            "calibration_plus_quantize_ms": round(search_ms + write_ms, 4),
+            "decode_us_per_query": round(dec_ms * 1e3, 2),
+            "fresh_queries": {"nmse_mean": round(mean, 6), "nmse_sd_population": round(sd, 6),
+                              "threshold_quality_mean": round(qm, 2), "threshold_quality_sd": round(qsd, 2)},
+            "packed_kv_code_bytes": T * H * 2 * 32, "metadata_bytes": T * H * 2 * 4,
+            "page_figures_for_context": {"calibration_plus_quantize_ms": 319.27, "decode_ms_per_query": 19.19,
+                                         "hardware": "host reference math beside one NVIDIA L4"}}
+
+
+def cpu_baseline_search(threads: int) -> dict:
+    """The oracle's candidate search as it stands, timed on this host: the
+    envelope's whole joint search (9 x 5 variants, 1 query, 4,096 tokens x 4
+    heads), and a bounded sample of the calibration search (one KV head x one
+    candidate x 5 clips x 64 queries x 65,536 tokens; the full search is 8
+    heads x 9 candidates of such work) single-threaded and with one head per
+    thread."""
+    import numpy as np
+    import oracle
+    import synthetic
+    from concurrent.futures import ThreadPoolExecutor
+    w = synthetic.make("envelope", "cpu")
+    f = lambda t: t.float().numpy()
+    cands = [oracle.Rotation(c.kind, None if c.signs is None else c.signs.numpy(),
+                             None if c.matrix is None else c.matrix.numpy()) for c in w.candidates]
+    t0 = time.perf_counter()
+    oracle.candidate_nmse(f(w.k), f(w.v), f(w.q[:1]), cands, list(w.clips), f(w.w_o), oracle.SELECT_JOINT)
+    env_s = time.perf_counter() - t0
+    wc = synthetic.make("calib64k", "cpu")
+    k, v, q, wo = f(wc.k), f(wc.v), f(wc.q), f(wc.w_o)
+    heads = min(threads, wc.H)
+
+    def one(h):
+        c = [oracle.Rotation(wc.candidates[0].kind, matrix=wc.candidates[0].matrix.numpy()[h:h + 1])]
+        oracle.candidate_nmse(np.ascontiguousarray(k[:, h:h + 1]), np.ascontiguousarray(v[:, h:h + 1]),
+                              np.ascontiguousarray(q[:, h:h + 1]), c, list(wc.clips), wo[h * 128:(h + 1) * 128],
+                              oracle.SELECT_JOINT)
+    t0 = time.perf_counter()
+    one(0)
+    one_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=heads) as ex:
+        list(ex.map(one, range(heads)))
+    thr_s = time.perf_counter() - t0
+    full_units = wc.H * len(wc.candidates)
+    return {"envelope_search": {"value_s": round(env_s, 3), "cores": 1, "kind": "oracle",
+                                "sample": "whole joint search: 9 candidates x 5 clips, 1 query, 4,096 x 4 heads"},
+            "calibration_search": {"value_s_estimated_full": round(one_s * full_units, 1), "cores": 1, "kind": "oracle",
+                                   "sample": f"1 KV head x 1 candidate x 5 clips (x {full_units} for the full "
+                                             f"search): {one_s:.2f} s"},
+            "calibration_search_threaded": {"value_s_estimated_full": round(thr_s * full_units / heads, 1),
+                                            "cores": heads, "kind": "oracle",
+                                            "sample": f"{heads} KV heads x 1 candidate x 5 clips, one head per "
+                                                      f"thread: {thr_s:.2f} s"}}
 
 
 def calibration_search(dev, timed):
@@ -370,16 +490,20 @@ def main():
                   decode_workload("gqa32k", dev, timed, median_of),
                   decode_workload("long131k", dev, timed, median_of)]
         torch.cuda.empty_cache()
-    # calibration search (a separate workload of the same path)
-    cal = None
+    # calibration search (a separate workload of the same path) and the
+    # evaluation page's own protocol
+    cal = env = None
     if not a.no_calibration:
         cal = calibration_search(dev, timed)
+        env = envelope_protocol(dev, timed, median_of)
 
     base = None
     if w_cpu is not None:
         base = cpu_baseline(w_cpu)
         base["threaded"] = cpu_baseline_threaded(w_cpu, w_cpu["threads"])
         base["cpu_model"] = host_cpu()[2]
+        if not a.no_calibration:
+            base["search"] = cpu_baseline_search(w_cpu["threads"])
 
     out = {
         "metric": "INT2 decode-attn effective KV GB/s (% HBM peak) + quantize Mtok/s, 32K ctx",
@@ -392,7 +516,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16",
+        "arithmetic": "INT2 codes on the int8 matrix cores (exact int32 sums) + fp32 softmax and merge",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "description": desc, "batch": B,
                    "context": T, "kv_heads": H, "q_heads": Hq, "head_dim": 128, "page_size": P, "d_model": dm,
@@ -412,6 +537,7 @@ def main():
         "bf16_windows": windows,
         "other_decode_workloads": others,
         "calibration_search": cal,
+        "envelope_protocol": env,
     }
     print(json.dumps(out))
 

@@ -15,6 +15,22 @@ uint32_t kvq::next_launch_epoch() {
   return next.fetch_add(1);
 }
 
+int kvq::device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;  // (no device visible: the sizes of an MI355X)
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 namespace {
 
 bool valid_dtype(int32_t dt) { return dt == KVQ_F32 || dt == KVQ_BF16; }

@@ -359,14 +359,14 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
     // at most one workgroup (8 waves) of the matrix-core kernel per CU, all
     // resident at once: two workgroups sharing a CU run at unequal speed (the
     // older one's waves win the issue arbitration), so the younger one's tail
-    // runs at half occupancy, and workgroups past the 256th run as a second
+    // runs at half occupancy, and workgroups past one per CU run as a second
     // round.  At most 64 splits (the last split merges up to 64 partials in
     // one pass; past 8 splits each workgroup merges its waves' partials
     // first); splits of at least 1024 tokens.  A workgroup takes one group of
     // 4 query rows.
     const int n_rg = (queries_per_seq * (Hq / H) + 3) / 4;
     const int units = num_seqs * H * n_rg > 0 ? num_seqs * H * n_rg : 1;
-    splits = 256 / units;
+    splits = device_cu_count() / units;
     if (splits > 64) splits = 64;
     const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens
     if (splits > max_by_len) splits = max_by_len;

@@ -21,15 +21,17 @@
 //   receives the 4 digit sums of query row g against token c of the tile and
 //   forms the logit alone: no cross-lane reduction.
 // Values:
-//   w_t = 2^(logit_t + kappa) s_t rounded to an integer < 2^24 is split into
-//   its 3 bytes; each byte b is fed as the int8 b - 128, and a fourth column
-//   of ones accumulates sum_t c_t to undo the offset.  kappa is a per-row
-//   power-of-two scale chosen from a running bound of logit + log2(s) with
-//   2^2 of headroom; if the bound outgrows it the int32 accumulators are
-//   flushed to fp32 in LDS (rare) and the scale moves.  l = sum 2^(logit +
-//   kappa) and z = sum 2^(logit + kappa) z_t stay in fp32 per lane.  The bytes
-//   reach the MFMA's B layout (column 4 r + byte, k = 16 tokens per lane
-//   group) by a byte transpose inside each lane quad and one lane permutation.
+//   w_t = 2^(logit_t + kappa) s_t rounded to an integer < 2^27 is split into
+//   four 7-bit digits (non-negative int8 lanes: no offset to undo); column
+//   x of a row accumulates sum_t digit_x(w_t) c_t exactly in int32 and the
+//   row's value sum is sum_x 128^x column_x.  kappa is a per-row power-of-two
+//   scale chosen from a running bound of logit + log2(s) with 2^2 of
+//   headroom, so the split's largest weight carries at least 2^23 units; if
+//   the bound outgrows it the int32 accumulators are flushed to fp32 in LDS
+//   (rare) and the scale moves.  l = sum 2^(logit + kappa) and z = sum
+//   2^(logit + kappa) z_t stay in fp32 per lane.  The digits reach the
+//   MFMA's B layout (column 4 r + digit, k = 16 tokens per lane group) by a
+//   byte transpose inside each lane quad and one lane permutation.
 // Query: each workgroup rotates its own query rows (signed Hadamard by the
 //   fast transform; a dense R_K is applied by an earlier launch) and forms
 //   their digits while its first key / value loads are in flight.
@@ -51,8 +53,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kM0 = 0x03030303u, kM1 = 0x0C0C0C0Cu, kM2 = 0x30303030u;
 constexpr int kHeadroom = 2;       // log2 headroom of the value scale
-constexpr int kWeightBits = 24;    // value weights are integers < 2^24 (3 bytes)
-constexpr uint32_t kByteOffset = 0x01808080u;  // bytes 0-2: b -> b - 128 as int8; byte 3: the ones column
+constexpr int kWeightBits = 28;    // value weights are integers < 2^27: four 7-bit digits
+
+// The 7-bit digits of w < 2^28, digit x in byte x (each byte < 128, so the
+// int8 MFMA operand needs no offset correction).
+__device__ __forceinline__ uint32_t weight_digits(uint32_t w) {
+  return (w & 0x7Fu) | ((w << 1) & 0x7F00u) | ((w << 2) & 0x7F0000u) | ((w << 3) & 0x7F000000u);
+}
 
 // The 4 code slots of every byte of x as int8 lanes; slot 1 and 2 are scaled by 4 and 16.
 __device__ __forceinline__ v4i slots(uint32_t x) {
@@ -100,15 +107,6 @@ __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t a, uint32_t sel
   a = __builtin_amdgcn_perm(static_cast<uint32_t>(dpp_xor1(static_cast<int>(a))), a, sel1);
   a = __builtin_amdgcn_perm(static_cast<uint32_t>(dpp_xor2(static_cast<int>(a))), a, sel2);
   return a;
-}
-
-// Sum over tokens of (byte x of W) * code for value-accumulator lane x of a
-// quad (x < 3): the MFMA summed (byte - 128) * code, the quad's lane 3 holds
-// sum code; the correction is applied in int32 (|.| < 2^31 over a split) so
-// that no large offset is cancelled in fp32.  Lane x = 3 yields 0.
-__device__ __forceinline__ int byte_sum(int d, int x) {
-  const int ones = __builtin_amdgcn_mov_dpp(d, 0xFF, 0xF, 0xF, false);  // quad lane 3
-  return x < 3 ? d + 128 * ones : 0;
 }
 
 struct MfmaArgs {
@@ -390,7 +388,6 @@ struct State {
   uint32_t sel1, sel2;  // byte-transpose selectors
   int src_lane4;        // 4 * lane whose bytes this lane takes for the value operand
   int krow_lane4;       // 4 * a lane of the query row of this lane's value accumulators
-  int vx_lane;          // this lane's column within its quad (byte index, 3 = ones)
   v4i accv[8];      // value accumulators (int32, MFMA), 16 dims each
   float lsum, zsum;
   int kappa;
@@ -437,7 +434,7 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float *p = facc + (4 * i + r) * 64;
-        *p = ((st.flushed ? *p : 0.0f) + static_cast<float>(byte_sum(st.accv[i][r], st.vx_lane))) * f2v;
+        *p = ((st.flushed ? *p : 0.0f) + static_cast<float>(st.accv[i][r])) * f2v;
       }
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.accv[i] = v4i{0, 0, 0, 0};
@@ -446,20 +443,20 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     st.kappa = newk;
     st.flushed = true;
   }
-  // ---- weights W = round(2^(logit + kappa) s_v) < 2^24, bytes offset to int8
+  // ---- weights W = round(2^(logit + kappa) s_v) < 2^27 as four 7-bit digits
   const float kf = static_cast<float>(st.kappa);
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     // (hardware exp2: results below 2^-126 weigh nothing against the
-    // split's largest weight, >= 2^21, and masked tokens give exp2(-inf) = 0)
+    // split's largest weight, >= 2^23, and masked tokens give exp2(-inf) = 0)
     const float p = __builtin_amdgcn_exp2f(logit[q] + kf);
     st.lsum += p;
     st.zsum += p * zv[q];
     const uint32_t W = static_cast<uint32_t>(fmaf(p, sv[q], 0.5f));
-    w[q] = W ^ kByteOffset;
+    w[q] = weight_digits(W);
   }
-  // quad lane x takes byte x (digit x, or the ones for x = 3) of its quad's 4 tokens;
+  // quad lane x takes digit x (byte x) of its quad's 4 tokens;
   // then the lanes move to the B layout: column 4 r + x, k-slice = token group
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -835,7 +832,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // value operand lane 16 g' + 4 r + x takes from lane 16 r + 4 g' + x
   st.src_lane4 = 4 * (16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + x);
   st.krow_lane4 = 4 * (16 * ((lane >> 2) & 3));
-  st.vx_lane = x;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.accv[i] = v4i{0, 0, 0, 0};
   st.lsum = st.zsum = 0.0f;
@@ -882,22 +878,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   const float zrow = row16_sum(st.zsum);
   const bool any_bad = __any(bad);
   float *rw = &red[wave][0][0];  // [4][132], private to this wave
-  // value accumulators: lane (4 r + x, g') holds column x (byte x, or the
-  // ones for x = 3) of query row r for dims 8 (4 g' + i) + 4 hf + e.  The
-  // lane's column, offset-corrected in int32 (exact), times 256^x (0 for the
-  // ones) and the slot scale, summed over the quad (x = 0 keeps the sum).
+  // value accumulators: lane (4 r + x, g') holds column x (digit x) of
+  // query row r for dims 8 (4 g' + i) + 4 hf + e (an exact int32 sum).  The
+  // lane's column times 128^x and the slot scale, summed over the quad (x = 0
+  // keeps the sum).
   const int vr = (lane >> 2) & 3;
-  const float wbyte = x == 0 ? 1.0f : x == 1 ? 256.0f : x == 2 ? 65536.0f : 0.0f;
-  const float wsc[4] = {wbyte, wbyte * 0.25f, wbyte * 0.0625f, wbyte};  // times slot_inv(e)
+  const float wdig = x == 0 ? 1.0f : x == 1 ? 128.0f : x == 2 ? 16384.0f : 2097152.0f;
+  const float wsc[4] = {wdig, wdig * 0.25f, wdig * 0.0625f, wdig};  // times slot_inv(e)
   float t[32];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = st.accv[k][i];
-      const int ones = __builtin_amdgcn_mov_dpp(d, 0xFF, 0xF, 0xF, true);  // quad lane 3
-      t[4 * k + i] = static_cast<float>(d + 128 * ones);
-    }
+    for (int i = 0; i < 4; ++i) t[4 * k + i] = static_cast<float>(st.accv[k][i]);
   if (st.flushed) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) t[j] += facc[j * 64];
@@ -1001,7 +993,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // write-back or invalidation is needed for that.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_word == arrival_valid_value(cnt), a.epoch, a.splits) ? 1u : 0u;
+  if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_word == arrival_valid_value(cnt, a.splits), a.epoch, a.splits) ? 1u : 0u;
   __syncthreads();
   if (s_last == 0) return;
   // dense R_V: the head's matrix is staged in LDS by the whole workgroup

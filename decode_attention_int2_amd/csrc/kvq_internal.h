@@ -12,7 +12,10 @@ namespace kvq {
 constexpr int D = 128;         // head dimension == quantization group size
 constexpr int kMaxRows = 64;   // query rows sharing one (sequence, KV head)
 constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
-constexpr int kMaxMfmaSplitTokens = 1 << 20;  // tokens per split (keeps split offsets far from int32 overflow)
+// tokens per split: a value-accumulator column of the matrix-core decode
+// gains at most 127 (digit) x 48 (code in the 16x slot) per token, so one
+// wave taking a whole split keeps its int32 sums below 2^18 * 6096 < 2^31
+constexpr int kMaxMfmaSplitTokens = 1 << 18;
 constexpr int kMaxSplits = 4096;            // split partials merged per (row, head)
 constexpr int kMfmaWaves = 8;               // waves per workgroup of the matrix-core decode kernel
 constexpr int kMaxSplitsNoPremerge = 8;     // more splits: the waves' partials are merged per split first
@@ -254,20 +257,29 @@ __device__ __forceinline__ bool arrive_last(unsigned long long *cnt, uint32_t ep
 // tagged compare-and-swap on c[2] for one launch, whose last arrival then
 // zeroes c[0] and validates it.  Every arrival of a launch reads the same c[1]:
 // only the launch's last arrival writes it.
-__device__ __forceinline__ unsigned long long arrival_valid_value(const unsigned long long *c) {
-  return static_cast<unsigned long long>(reinterpret_cast<uintptr_t>(c)) ^ 0x6b76715f61727276ull;
+// The validation value depends on the counter's address and its number of
+// parts, so a word validated by a launch of another shape does not count.
+__device__ __forceinline__ unsigned long long arrival_valid_value(const unsigned long long *c, int parts) {
+  return (static_cast<unsigned long long>(reinterpret_cast<uintptr_t>(c)) ^ 0x6b76715f61727276ull) +
+         (static_cast<unsigned long long>(parts) << 48);
 }
 __device__ __forceinline__ bool arrive_counted(unsigned long long *c, bool valid, uint32_t epoch, int parts) {
   if (valid) {
     const unsigned long long old = atomicAdd(c, 1ull);
-    const bool last = old == static_cast<unsigned long long>(parts - 1);
-    if (last) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return last;
+    if (old < static_cast<unsigned long long>(parts)) {
+      const bool last = old == static_cast<unsigned long long>(parts - 1);
+      if (last) __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return last;
+    }
+    // c[0] holds a value no launch of this counter leaves behind (the word
+    // was part of another workspace layout since): every arrival of this
+    // launch sees such a value (the count only grows) and counts with the
+    // tagged compare-and-swap instead, whose last arrival resets c[0]
   }
   const bool last = arrive_last(c + 2, epoch, parts);
   if (last) {
     __hip_atomic_store(c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(c + 1, arrival_valid_value(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(c + 1, arrival_valid_value(c, parts), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return last;
 }
@@ -276,6 +288,8 @@ constexpr int kArrivalWords = 3;  // uint64 words per counted arrival point
 // A new arrival tag per launch (host side), starting from a per-process value
 // so that counters left in memory by other processes rarely carry it.
 uint32_t next_launch_epoch();
+// Compute units of the current device (read once per device and kept).
+int device_cu_count();
 
 // ----------------------------------------------------------------- launchers
 hipError_t launch_quantize(const void *k, const void *v, int dtype, int64_t num_tokens, int H,

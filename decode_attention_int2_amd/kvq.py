@@ -113,6 +113,56 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
+# ---- argument contract of include/kvq.h, checked before any pointer is taken:
+# a wrong element type or a short buffer would otherwise be read or written
+# past its end by a kernel.
+def _need(t, name: str, dtype=None, shape=None, min_numel: Optional[int] = None, optional: bool = False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in allowed)}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
+
+
+_FLOAT_IO = (torch.float32, torch.bfloat16)
+
+
+def _need_kv(k, v, H: Optional[int] = None):
+    _need(k, "k", _FLOAT_IO)
+    _need(v, "v", _FLOAT_IO)
+    if k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError(f"k must be [tokens][H][{HEAD_DIM}], not {tuple(k.shape)}")
+    if H is not None and k.shape[1] != H:
+        raise ValueError(f"k has {k.shape[1]} KV heads, the cache {H}")
+    _need(v, "v", k.dtype, tuple(k.shape))
+
+
+def _need_rot(rot: "Rotation", H: int, name: str):
+    if not isinstance(rot, Rotation):
+        raise TypeError(f"{name} must be a Rotation")
+    if rot.kind == KVQ_ROT_SIGNED_HADAMARD:
+        _need(rot.signs, f"{name}.signs", torch.int8, (H, HEAD_DIM))
+    elif rot.kind == KVQ_ROT_DENSE:
+        _need(rot.matrix, f"{name}.matrix", torch.float32, (H, HEAD_DIM, HEAD_DIM))
+
+
+def _need_cache(cache: "Cache"):
+    _need(cache.pages, "cache.pages", torch.uint8, min_numel=cache.num_pages * cache.num_kv_heads * 72 * cache.page_size)
+
+
+def _need_key_mean(key_mean, H: int):
+    _need(key_mean, "key_mean", torch.float32, (H, HEAD_DIM), optional=True)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -157,6 +207,13 @@ def _check(rc: int, what: str):
 def kvq_quantize(k: torch.Tensor, v: torch.Tensor, cache: Cache, rot_k: Rotation, rot_v: Rotation,
                  key_mean: Optional[torch.Tensor] = None, clip_k: float = 1.0, clip_v: float = 1.0,
                  slot_mapping: Optional[torch.Tensor] = None, stream=None) -> None:
+    H = cache.num_kv_heads
+    _need_kv(k, v, H)
+    _need(slot_mapping, "slot_mapping", torch.int64, (k.shape[0],), optional=True)
+    _need_rot(rot_k, H, "rot_k")
+    _need_rot(rot_v, H, "rot_v")
+    _need_key_mean(key_mean, H)
+    _need_cache(cache)
     lib = load_library()
     c, rk, rv = cache._c(), rot_k._c(), rot_v._c()
     _check(lib.kvq_quantize(_dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k), k.shape[0],
@@ -171,6 +228,30 @@ def kvq_decode_workspace_bytes(num_seqs: int, queries_per_seq: int, num_q_heads:
                                                          max_seq_len, d_model, num_splits))
 
 
+def _need_decode(q, num_seqs: int, queries_per_seq: int, cache: "Cache", page_table, max_pages_per_seq: int,
+                 seq_lens, rot_k, rot_v, out_o, w_o, out_y):
+    H = cache.num_kv_heads
+    _need(q, "q", _FLOAT_IO)
+    rows = int(num_seqs) * int(queries_per_seq)
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [num_seqs * queries_per_seq = {rows}][Hq][{HEAD_DIM}], not {tuple(q.shape)}")
+    Hq = q.shape[1]
+    if Hq % H:
+        raise ValueError(f"num_q_heads {Hq} is not a multiple of num_kv_heads {H}")
+    _need_cache(cache)
+    _need(page_table, "page_table", torch.int32, min_numel=int(num_seqs) * int(max_pages_per_seq), optional=True)
+    _need(seq_lens, "seq_lens", torch.int32, min_numel=int(num_seqs))
+    _need_rot(rot_k, H, "rot_k")
+    _need_rot(rot_v, H, "rot_v")
+    _need(out_o, "out_o", torch.float32, (rows, Hq, HEAD_DIM))
+    if w_o is not None:
+        _need(w_o, "w_o", q.dtype)
+        if w_o.dim() != 2 or w_o.shape[0] != Hq * HEAD_DIM:
+            raise ValueError(f"w_o must be [{Hq * HEAD_DIM}][d_model], not {tuple(w_o.shape)}")
+        _need(out_y, "out_y", torch.float32, (rows, w_o.shape[1]))
+    _need(out_y, "out_y", torch.float32, optional=True)
+
+
 def kvq_decode_attn(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache: Cache,
                     page_table: Optional[torch.Tensor], max_pages_per_seq: int, seq_lens: torch.Tensor,
                     max_seq_len: int, rot_k: Rotation, rot_v: Rotation, out_o: torch.Tensor,
@@ -179,6 +260,8 @@ def kvq_decode_attn(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache:
                     split_events: Optional[tuple] = None) -> None:
     """split_events: optional (start, stop) or (start, stop, attn_stop) torch.cuda.Event tuple: start/stop
     are recorded around the split-K kernel, attn_stop after the merge (before W_O)."""
+    _need_decode(q, num_seqs, queries_per_seq, cache, page_table, max_pages_per_seq, seq_lens, rot_k, rot_v, out_o,
+                 w_o, out_y)
     lib = load_library()
     Hq = q.shape[1]
     d_model = int(w_o.shape[1]) if w_o is not None else 0
@@ -202,6 +285,8 @@ def kvq_decode_attn_causal(q: torch.Tensor, num_seqs: int, queries_per_seq: int,
                            workspace: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None) -> None:
     """Rows of a sequence are its last queries_per_seq positions: row qi attends the first
     seq_len - (queries_per_seq - 1 - qi) tokens."""
+    _need_decode(q, num_seqs, queries_per_seq, cache, page_table, max_pages_per_seq, seq_lens, rot_k, rot_v, out_o,
+                 w_o, out_y)
     lib = load_library()
     Hq = q.shape[1]
     d_model = int(w_o.shape[1]) if w_o is not None else 0
@@ -241,8 +326,24 @@ class Windows:
                         self.num_kv_heads, self.num_sink, self.num_recent)
 
 
+def _need_windows(windows: Windows, H: int):
+    if not isinstance(windows, Windows):
+        raise TypeError("windows must be a Windows")
+    if windows.num_kv_heads != H:
+        raise ValueError(f"windows hold {windows.num_kv_heads} KV heads, the cache {H}")
+    for name, n in (("sink", windows.num_sink), ("recent", windows.num_recent)):
+        shape = (windows.num_seqs, n, H, HEAD_DIM)
+        _need(getattr(windows, name + "_k"), f"windows.{name}_k", torch.bfloat16, shape)
+        _need(getattr(windows, name + "_v"), f"windows.{name}_v", torch.bfloat16, shape)
+
+
 def kvq_window_write(k: torch.Tensor, v: torch.Tensor, seq_idx: torch.Tensor, positions: torch.Tensor,
                      windows: Windows, seq_lens: Optional[torch.Tensor] = None, stream=None) -> None:
+    _need_kv(k, v, windows.num_kv_heads)
+    _need_windows(windows, windows.num_kv_heads)
+    _need(seq_idx, "seq_idx", torch.int32, (k.shape[0],))
+    _need(positions, "positions", torch.int32, (k.shape[0],))
+    _need(seq_lens, "seq_lens", torch.int32, min_numel=windows.num_seqs, optional=True)
     w = windows._c()
     _check(load_library().kvq_window_write(_dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(k), k.shape[0],
                                            _dev_ptr(seq_idx, "seq_idx"), _dev_ptr(positions, "positions"),
@@ -256,6 +357,10 @@ def kvq_decode_attn_windows(q: torch.Tensor, num_seqs: int, queries_per_seq: int
                             out_o: torch.Tensor, key_mean: Optional[torch.Tensor] = None,
                             w_o: Optional[torch.Tensor] = None, out_y: Optional[torch.Tensor] = None,
                             workspace: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None) -> None:
+    _need_decode(q, num_seqs, queries_per_seq, cache, page_table, max_pages_per_seq, seq_lens, rot_k, rot_v, out_o,
+                 w_o, out_y)
+    _need_windows(windows, cache.num_kv_heads)
+    _need_key_mean(key_mean, cache.num_kv_heads)
     lib = load_library()
     Hq = q.shape[1]
     d_model = int(w_o.shape[1]) if w_o is not None else 0
@@ -273,6 +378,14 @@ def kvq_decode_attn_windows(q: torch.Tensor, num_seqs: int, queries_per_seq: int
 def kvq_fold_value_rotation(w: torch.Tensor, blocks_per_head: int, rot_v: Rotation, out: torch.Tensor,
                             stream=None) -> None:
     """out block b = R_V[b / blocks_per_head]^T w block b (blocks of 128 rows); out has w's shape and dtype."""
+    _need(w, "w", _FLOAT_IO)
+    if w.dim() != 2 or w.shape[0] % HEAD_DIM:
+        raise ValueError(f"w must be [blocks * {HEAD_DIM}][cols], not {tuple(w.shape)}")
+    nb = w.shape[0] // HEAD_DIM
+    if blocks_per_head < 1 or nb % blocks_per_head:
+        raise ValueError(f"{nb} blocks are not a multiple of blocks_per_head {blocks_per_head}")
+    _need(out, "out", w.dtype, tuple(w.shape))
+    _need_rot(rot_v, nb // blocks_per_head, "rot_v")
     r = rot_v._c()
     _check(load_library().kvq_fold_value_rotation(_dev_ptr(w, "w"), _dtype_code(w), w.shape[0] // 128, blocks_per_head,
                                                   w.shape[1], ctypes.byref(r), _dev_ptr(out, "out"), _stream(stream)),
@@ -294,9 +407,24 @@ def kvq_candidate_nmse(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, candid
                        out_best: torch.Tensor, out_nmse_per_query: Optional[torch.Tensor] = None,
                        key_mean: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                        stream=None) -> None:
-    lib = load_library()
+    _need_kv(k, v)
     T, H = k.shape[0], k.shape[1]
+    _need(q, "q", k.dtype)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or q.shape[1] % H:
+        raise ValueError(f"q must be [queries][Hq][{HEAD_DIM}] with Hq a multiple of {H}, not {tuple(q.shape)}")
     Nq, Hq = q.shape[0], q.shape[1]
+    _need(w_o, "w_o", k.dtype)
+    if w_o.dim() != 2 or w_o.shape[0] != Hq * HEAD_DIM:
+        raise ValueError(f"w_o must be [{Hq * HEAD_DIM}][d_model], not {tuple(w_o.shape)}")
+    for i, c in enumerate(candidates):
+        _need_rot(c, H, f"candidates[{i}]")
+    _need_key_mean(key_mean, H)
+    U = 1 if mode == KVQ_SELECT_JOINT else H
+    grid = U * len(candidates) * len(clips)
+    _need(out_nmse, "out_nmse", torch.float32, min_numel=grid)
+    _need(out_best, "out_best", torch.int32, min_numel=U)
+    _need(out_nmse_per_query, "out_nmse_per_query", torch.float32, min_numel=grid * Nq, optional=True)
+    lib = load_library()
     rots = (_Rot * len(candidates))(*[c._c() for c in candidates])
     cl = (ctypes.c_float * len(clips))(*[float(x) for x in clips])
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

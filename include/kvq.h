@@ -10,7 +10,11 @@
  *   - Pointers are device pointers unless an argument says "host".  All
  *     arrays are dense, row-major, with the shapes given below.
  *   - The caller owns every buffer.  The library allocates and frees no
- *     memory and keeps no mutable global state between calls.
+ *     memory.  Its only process-wide state is a counter that tags each
+ *     decode launch and the compute-unit count of each device (read once:
+ *     it sizes the split plan, so workspace sizes are those of the device
+ *     current when they are queried);
+ *     both are safe to use from several threads.
  *   - Work is enqueued on `stream` and is asynchronous; results are ready
  *     after the caller synchronizes that stream.
  *   - All arguments that can be checked on the host are checked before the
@@ -169,6 +173,11 @@ int kvq_quantize(const void *k, const void *v, int32_t dtype, int64_t num_tokens
  *   events       host pointer to a kvq_decode_events, or NULL.
  * Limits: Hq % H == 0 (else INVALID_ARGUMENT); queries_per_seq * Hq / H <= 64
  * and max_seq_len <= 2^26, else UNSUPPORTED.
+ * Kernels: page sizes that are powers of two (16, 32, 64, ...) run the
+ * matrix-core decode (one launch: query rotation, split attention, merge,
+ * inverse value rotation).  Other multiples of 16 run a vector-unit split
+ * kernel and a separate merge launch, about 4x slower at the same size; the
+ * causal and windowed variants below do not take such page sizes.
  * ------------------------------------------------------------------------- */
 /* Optional timing hook of kvq_decode_attn: when non-NULL, split_start and
  * split_stop are recorded on `stream` immediately before and after the
