@@ -4,6 +4,7 @@
 #include <atomic>
 #include <chrono>
 #include <cmath>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -252,6 +253,53 @@ int kvq_decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t quer
   return decode_attn(q, dtype, num_seqs, queries_per_seq, num_q_heads, cache, page_table, max_pages_per_seq, seq_lens,
                      max_seq_len, rot_k, rot_v, nullptr, nullptr, w_o, d_model, out_o, out_y, workspace,
                      workspace_bytes, num_splits, events, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation decode
+// Scratch of kvq_decode_attn_noalloc: a file-scope device array, one copy per
+// GPU for the life of the process.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device, with that device current, and kept.
+namespace {
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxScratchDevices];
+
+// 0 = ok (the current device's scratch address in *out), else a kvq_status.
+int current_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return KVQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kvq_decode_attn_noalloc(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,
+                            int32_t num_q_heads, const kvq_cache *cache, const int32_t *page_table,
+                            int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                            const kvq_rotation *rot_k, const kvq_rotation *rot_v, const void *w_o, int32_t d_model,
+                            float *out_o, float *out_y, int32_t num_splits, hipStream_t stream) {
+  void *ws = nullptr;
+  const int rc = current_scratch(&ws);
+  if (rc) return rc;
+  // (the shared decode path validates every argument first and returns
+  // KVQ_ERR_WORKSPACE, launching nothing, when the plan needs more scratch)
+  return decode_attn(q, dtype, num_seqs, queries_per_seq, num_q_heads, cache, page_table, max_pages_per_seq, seq_lens,
+                     max_seq_len, rot_k, rot_v, nullptr, nullptr, w_o, d_model, out_o, out_y, ws,
+                     KVQ_NOALLOC_SCRATCH_BYTES, num_splits, nullptr, stream);
 }
 
 int kvq_decode_attn_windows(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,

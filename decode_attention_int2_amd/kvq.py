@@ -22,7 +22,7 @@ KVQ_SELECT_JOINT, KVQ_SELECT_PER_HEAD = 0, 1
 HEAD_DIM = 128
 
 EXPORTED = ("kvq_cache_bytes", "kvq_quantize", "kvq_decode_workspace_bytes", "kvq_decode_attn",
-            "kvq_decode_attn_causal", "kvq_window_write", "kvq_decode_attn_windows", "kvq_bits_per_element", "kvq_fold_value_rotation",
+            "kvq_decode_attn_causal", "kvq_decode_attn_noalloc", "kvq_window_write", "kvq_decode_attn_windows", "kvq_bits_per_element", "kvq_fold_value_rotation",
             "kvq_candidate_workspace_bytes", "kvq_candidate_nmse", "kvq_status_string", "kvq_version")
 
 
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_candidate_nmse.argtypes = [P, P, P, i32, i64, i32, i32, i32, P, i32, P, i32, P, P, i32, i32, P, P, P, P,
                                        sz, P]
     lib.kvq_candidate_nmse.restype = ctypes.c_int
+    lib.kvq_decode_attn_noalloc.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, i32, P, P, P, i32, P, P, i32, P]
+    lib.kvq_decode_attn_noalloc.restype = ctypes.c_int
     lib.kvq_decode_attn_causal.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, i32, P, P, P, i32, P, P, P, sz, i32, P]
     lib.kvq_decode_attn_causal.restype = ctypes.c_int
     lib.kvq_window_write.argtypes = [P, P, i32, i64, P, P, P, P, P]
@@ -276,6 +278,30 @@ def kvq_decode_attn(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache:
                                max_seq_len, ctypes.byref(rk), ctypes.byref(rv), _dev_ptr(w_o, "w_o"), d_model,
                                _dev_ptr(out_o, "out_o"), _dev_ptr(out_y, "out_y"), _dev_ptr(workspace, "workspace"),
                                ws_bytes, num_splits, ev, _stream(stream)), "kvq_decode_attn")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def kvq_decode_attn_noalloc(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache: Cache,
+                            page_table: Optional[torch.Tensor], max_pages_per_seq: int, seq_lens: torch.Tensor,
+                            max_seq_len: int, rot_k: Rotation, rot_v: Rotation, out_o: torch.Tensor,
+                            w_o: Optional[torch.Tensor] = None, out_y: Optional[torch.Tensor] = None,
+                            num_splits: int = 0, stream=None) -> None:
+    """kvq_decode_attn without a workspace: the library's per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES) holds the partials; nothing is allocated."""
+    _need_decode(q, num_seqs, queries_per_seq, cache, page_table, max_pages_per_seq, seq_lens, rot_k, rot_v, out_o,
+                 w_o, out_y)
+    lib = load_library()
+    Hq = q.shape[1]
+    d_model = int(w_o.shape[1]) if w_o is not None else 0
+    c, rk, rv = cache._c(), rot_k._c(), rot_v._c()
+    _check(lib.kvq_decode_attn_noalloc(_dev_ptr(q, "q"), _dtype_code(q), num_seqs, queries_per_seq, Hq,
+                                       ctypes.byref(c), _dev_ptr(page_table, "page_table"), max_pages_per_seq,
+                                       _dev_ptr(seq_lens, "seq_lens"), max_seq_len, ctypes.byref(rk),
+                                       ctypes.byref(rv), _dev_ptr(w_o, "w_o"), d_model, _dev_ptr(out_o, "out_o"),
+                                       _dev_ptr(out_y, "out_y"), num_splits, _stream(stream)),
+           "kvq_decode_attn_noalloc")
 
 
 def kvq_decode_attn_causal(q: torch.Tensor, num_seqs: int, queries_per_seq: int, cache: Cache,

@@ -11,10 +11,11 @@
  *     arrays are dense, row-major, with the shapes given below.
  *   - The caller owns every buffer.  The library allocates and frees no
  *     memory.  Its only process-wide state is a counter that tags each
- *     decode launch and the compute-unit count of each device (read once:
- *     it sizes the split plan, so workspace sizes are those of the device
- *     current when they are queried);
- *     both are safe to use from several threads.
+ *     decode launch, the compute-unit count of each device (read once: it
+ *     sizes the split plan, so workspace sizes are those of the device
+ *     current when they are queried) and the device address of the
+ *     no-allocation scratch array; all three are safe to use from several
+ *     threads.
  *   - Work is enqueued on `stream` and is asynchronous; results are ready
  *     after the caller synchronizes that stream.
  *   - All arguments that can be checked on the host are checked before the
@@ -214,6 +215,28 @@ int kvq_decode_attn_causal(const void *q, int32_t dtype, int32_t num_seqs, int32
                            const kvq_rotation *rot_k, const kvq_rotation *rot_v, const void *w_o, int32_t d_model,
                            float *out_o, float *out_y, void *workspace, size_t workspace_bytes, int32_t num_splits,
                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * kvq_decode_attn_noalloc -- kvq_decode_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, results and limits as
+ * kvq_decode_attn, without the workspace: the split partials, the W_O operand
+ * copy and the arrival counters live in a device array of the library of
+ * KVQ_NOALLOC_SCRATCH_BYTES, one per GPU, held from the first call on that
+ * GPU until the process ends.  The call allocates and frees nothing.
+ * Returns KVQ_ERR_WORKSPACE, launching nothing, when the shapes need more
+ * than that (kvq_decode_workspace_bytes(...) > KVQ_NOALLOC_SCRATCH_BYTES).
+ * Every call on one GPU uses the same array (nothing in it needs clearing
+ * between calls): two calls that may run at the same time on one GPU (on
+ * different streams, or from different threads) race and must not overlap.
+ * ------------------------------------------------------------------------- */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int kvq_decode_attn_noalloc(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,
+                            int32_t num_q_heads, const kvq_cache *cache, const int32_t *page_table,
+                            int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                            const kvq_rotation *rot_k, const kvq_rotation *rot_v, const void *w_o, int32_t d_model,
+                            float *out_o, float *out_y, int32_t num_splits, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * BF16 sink and recent windows ([OptR] §5, implementation details: 64 sink
