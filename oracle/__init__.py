@@ -81,6 +81,7 @@ def _load():
         lib.kvqo_bits_per_element.restype = ctypes.c_double
         lib.kvqo_fold_value_rotation.argtypes = [P, i32, i32, i32, P, P]
         lib.kvqo_decode_causal_f64.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P]
+        lib.kvqo_quantize_dequant_groups.argtypes = [P, i64, F, P, P]
         _lib = lib
     return _lib
 
@@ -159,6 +160,18 @@ def quantize_group(x, clip: float):
     _check(_load().kvqo_quantize_group(_ptr(x), x.size, ctypes.c_float(clip), _ptr(codes), _ptr(sb), _ptr(zb)),
            "quantize_group")
     return codes, int(sb[0]), int(zb[0])
+
+
+def quantize_dequant_groups(x, clip: float):
+    """Groups of 128 (x [n][128] fp32): (dequantized Q2 values fp32, in-range
+    flags bool) -- the C oracle's quantizer, with the pass-through flags of the
+    straight-through estimator."""
+    x = np.ascontiguousarray(x, np.float32).reshape(-1, D)
+    xh = np.zeros_like(x)
+    m = np.zeros(x.shape, np.uint8)
+    _check(_load().kvqo_quantize_dequant_groups(_ptr(x), x.shape[0], ctypes.c_float(clip), _ptr(xh), _ptr(m)),
+           "quantize_dequant_groups")
+    return xh, m.astype(bool)
 
 
 def rotate(x, rot: Rotation, mean=None) -> np.ndarray:

@@ -176,6 +176,36 @@ static float dequant(uint8_t code, uint16_t sb, uint16_t zb) {
   return prod + z;
 }
 
+/* Q2 then dequantization of n consecutive groups of 128 (x [n][128]), with
+ * the straight-through estimator's pass-through flags of the OptR
+ * calibration [OptR, §4.5 Eq. (18)]: x_hat = code * s + z of the group's Q2
+ * (the values the cache would hold), in_range = 1 where lo <= x <= hi, the
+ * group's clipping range.  READING: Eq. (18)'s |Z| <= tau_c, with tau_c
+ * "determined by the clip ratio", is the range [c*min, c*max] that Q2 clips
+ * to (R2): the gradient passes where the value is not clipped. */
+int kvqo_quantize_dequant_groups(const float *x, int64_t n, float clip, float *x_hat, uint8_t *in_range) {
+  if (!x || !x_hat || !in_range || n < 0) return KVQO_ERR_ARG;
+  const int d = KVQO_D;
+  uint8_t codes[KVQO_D];
+  for (int64_t g = 0; g < n; ++g) {
+    const float *xg = x + (size_t)g * d;
+    uint16_t sb, zb;
+    int rc = kvqo_quantize_group(xg, d, clip, codes, &sb, &zb);
+    if (rc) return rc;
+    float mn = xg[0], mx = xg[0];
+    for (int i = 1; i < d; ++i) {
+      if (xg[i] < mn) mn = xg[i];
+      if (xg[i] > mx) mx = xg[i];
+    }
+    float lo = clip * mn, hi = clip * mx;
+    for (int i = 0; i < d; ++i) {
+      x_hat[(size_t)g * d + i] = dequant(codes[i], sb, zb);
+      in_range[(size_t)g * d + i] = (uint8_t)(xg[i] >= lo && xg[i] <= hi);
+    }
+  }
+  return KVQO_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Packed paged cache [OptR, §1 and §6: rotation keeps the cache shape and the
  * paged layout; the cache-write step quantizes, packs and writes].  Layout

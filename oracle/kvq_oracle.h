@@ -60,6 +60,11 @@ int kvqo_rotation_matrix(int kind, const int8_t *signs, const float *matrix, dou
 int kvqo_quantize_group(const float *x, int n, float clip, uint8_t *codes, uint16_t *scale_bits,
                         uint16_t *zero_bits);
 
+/* n groups of 128: x_hat = dequantized Q2 values, in_range = 1 where the
+ * value lies inside the group's clipping range [c*min, c*max] (the
+ * straight-through estimator of the OptR calibration passes gradients there). */
+int kvqo_quantize_dequant_groups(const float *x, int64_t n, float clip, float *x_hat, uint8_t *in_range);
+
 /* Paged packed cache, byte layout fixed by the C-ABI header of the library
  * (see the per-field comments in kvq_oracle.c, which restate it). */
 typedef struct {

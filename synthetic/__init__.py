@@ -244,3 +244,47 @@ def ragged_seq_lens(num_seqs: int, max_tokens: int, seed: int, page_size: int = 
     if num_seqs >= 3:
         lens[2] = max_tokens
     return lens.to(torch.int32)
+
+
+@dataclasses.dataclass
+class TraceSet:
+    """Calibration traces of one layer: k, v [num_seqs][max_len][H][128] (zero
+    past each length), q [num_seqs][nq][Hq][128] (the queries of each
+    sequence's final nq positions), lens (host list)."""
+    k: torch.Tensor
+    v: torch.Tensor
+    q: torch.Tensor
+    lens: list
+
+
+def optr_traces(seed: int, num_seqs: int, min_len: int, max_len: int, H: int, Hq: int, nq: int = 64,
+                dtype: str = "bf16") -> TraceSet:
+    """Synthetic calibration traces with the decode workloads' distribution
+    (K, V ~ N(0,1) per channel, 4 outlier channels per head x10, key offsets
+    ~ N(0, 2); queries ~ N(0, 1)) and seeded lengths in [min_len, max_len]
+    (the paper keeps calibration sequences of at least 328 tokens)."""
+    g = _gen(seed, 11, "cpu")
+    lens = torch.randint(min_len, max_len + 1, (num_seqs,), generator=g).tolist()
+    L = max(lens)
+    k = torch.randn((num_seqs, L, H, D), generator=g) * _outlier_mask(H, g, "cpu")
+    v = torch.randn((num_seqs, L, H, D), generator=g) * _outlier_mask(H, g, "cpu")
+    k += torch.randn((H, D), generator=g) * math.sqrt(2.0)
+    q = torch.randn((num_seqs, nq, Hq, D), generator=g)
+    for b, n in enumerate(lens):
+        k[b, n:] = 0.0
+        v[b, n:] = 0.0
+    return TraceSet(k=_to_dtype(k, dtype), v=_to_dtype(v, dtype), q=_to_dtype(q, dtype), lens=lens)
+
+
+def optr_problem(seed: int, H: int, Hq: int, d_model: int, calib=(6, 328, 700), heldout=(5, 328, 700), nq: int = 64,
+                 dtype: str = "bf16") -> dict:
+    """A calibration problem: calibration and held-out traces (disjoint draws),
+    W_O [Hq*128][d_model] ~ N(0, 1/(Hq*128)), and base rotations R0_K, R0_V
+    (fp32 [H][128][128], learned-rotation draws: the method accepts any
+    orthogonal initialization)."""
+    g = _gen(seed, 12, "cpu")
+    fan_in = Hq * D
+    return {"calib": optr_traces(seed * 2 + 1, *calib, H, Hq, nq, dtype),
+            "heldout": optr_traces(seed * 2 + 2, *heldout, H, Hq, nq, dtype),
+            "w_o": _to_dtype(torch.randn((fan_in, d_model), generator=g) / math.sqrt(fan_in), dtype),
+            "r0_k": learned_rotation(H, g), "r0_v": learned_rotation(H, g), "nq": nq, "H": H, "Hq": Hq}
