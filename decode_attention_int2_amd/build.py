@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "wo_mfma.hip", "candidate.hip", "reference_mfma.hip", "windows.hip", "fold.hip"]
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "wo_mfma.hip", "candidate.hip", "reference_mfma.hip", "windows.hip", "fold.hip", "optr.hip"]
 # -packed-fp32-ops: no v_pk_*_f32 instructions; denormals kept; IEEE fp32 division.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",

@@ -23,7 +23,8 @@ HEAD_DIM = 128
 
 EXPORTED = ("kvq_cache_bytes", "kvq_quantize", "kvq_decode_workspace_bytes", "kvq_decode_attn",
             "kvq_decode_attn_causal", "kvq_decode_attn_noalloc", "kvq_window_write", "kvq_decode_attn_windows", "kvq_bits_per_element", "kvq_fold_value_rotation",
-            "kvq_candidate_workspace_bytes", "kvq_candidate_nmse", "kvq_status_string", "kvq_version")
+            "kvq_candidate_workspace_bytes", "kvq_candidate_nmse", "kvq_optr_workspace_bytes", "kvq_optr_calibrate",
+            "kvq_optr_loss_grad", "kvq_status_string", "kvq_version")
 
 
 class KvqError(RuntimeError):
@@ -83,6 +84,12 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_fold_value_rotation.restype = ctypes.c_int
     lib.kvq_bits_per_element.argtypes = [i64, i32, i32]
     lib.kvq_bits_per_element.restype = ctypes.c_double
+    lib.kvq_optr_workspace_bytes.argtypes = [P, P, i32, i32, i32, i32]
+    lib.kvq_optr_workspace_bytes.restype = sz
+    lib.kvq_optr_calibrate.argtypes = [i32, P, P, i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.kvq_optr_calibrate.restype = ctypes.c_int
+    lib.kvq_optr_loss_grad.argtypes = [i32, i32, P, i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, sz, P]
+    lib.kvq_optr_loss_grad.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
@@ -460,6 +467,112 @@ def kvq_candidate_nmse(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, candid
                                   _dev_ptr(out_nmse_per_query, "out_nmse_per_query"), _dev_ptr(out_best, "out_best"),
                                   _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
            "kvq_candidate_nmse")
+
+
+class _TraceSet(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("max_len", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("q", ctypes.c_void_p)]
+
+
+class _OptrConfig(ctypes.Structure):
+    _fields_ = [("lambda_k", ctypes.c_double), ("clip_k", ctypes.c_float), ("clip_v", ctypes.c_float),
+                ("num_sink", ctypes.c_int32), ("num_recent", ctypes.c_int32), ("steps", ctypes.c_int32),
+                ("lr", ctypes.c_double), ("eval_every", ctypes.c_int32)]
+
+
+OPTR_DEFAULTS = dict(lambda_k=1.0, clip_k=0.96, clip_v=0.92, num_sink=64, num_recent=256, steps=80, lr=0.02,
+                     eval_every=20)
+
+
+class _Traces:
+    """A kvq_trace_set built from an object with k, v [S][L][H][128], q [S][nq][Hq][128]
+    (GPU tensors of one dtype) and lens (host list); keeps the host length array alive."""
+
+    def __init__(self, t, H: int, Hq: int):
+        _need(t.k, "traces.k", _FLOAT_IO)
+        if t.k.dim() != 4 or t.k.shape[2] != H or t.k.shape[3] != HEAD_DIM:
+            raise ValueError(f"traces.k must be [seqs][max_len][{H}][{HEAD_DIM}], not {tuple(t.k.shape)}")
+        _need(t.v, "traces.v", t.k.dtype, tuple(t.k.shape))
+        S, Lm = t.k.shape[0], t.k.shape[1]
+        _need(t.q, "traces.q", t.k.dtype)
+        if t.q.dim() != 4 or t.q.shape[0] != S or t.q.shape[2] != Hq or t.q.shape[3] != HEAD_DIM:
+            raise ValueError(f"traces.q must be [{S}][queries][{Hq}][{HEAD_DIM}], not {tuple(t.q.shape)}")
+        self.nq = int(t.q.shape[1])
+        lens = [int(x) for x in t.lens]
+        if len(lens) != S or any(not (self.nq <= n <= Lm) for n in lens):
+            raise ValueError(f"lens must hold {S} lengths in [{self.nq}, {Lm}]")
+        self.dtype = t.k.dtype
+        self._lens = (ctypes.c_int32 * S)(*lens)
+        self.c = _TraceSet(S, Lm, ctypes.cast(self._lens, ctypes.c_void_p), _dev_ptr(t.k, "traces.k"),
+                           _dev_ptr(t.v, "traces.v"), _dev_ptr(t.q, "traces.q"))
+
+
+def _optr_config(cfg: Optional[dict]) -> _OptrConfig:
+    c = dict(OPTR_DEFAULTS, **(cfg or {}))
+    return _OptrConfig(c["lambda_k"], c["clip_k"], c["clip_v"], c["num_sink"], c["num_recent"], c["steps"], c["lr"],
+                       c["eval_every"])
+
+
+def kvq_optr_workspace_bytes(calib, heldout, num_kv_heads: int, num_q_heads: int, d_model: int) -> int:
+    a = _Traces(calib, num_kv_heads, num_q_heads)
+    b = _Traces(heldout, num_kv_heads, num_q_heads) if heldout is not None else None
+    return int(load_library().kvq_optr_workspace_bytes(ctypes.byref(a.c), ctypes.byref(b.c) if b else None,
+                                                       num_kv_heads, num_q_heads, a.nq, d_model))
+
+
+def kvq_optr_calibrate(calib, heldout, num_kv_heads: int, num_q_heads: int, w_o: torch.Tensor, r0_k: torch.Tensor,
+                       r0_v: torch.Tensor, out_r_k: torch.Tensor, out_r_v: torch.Tensor, cfg: Optional[dict] = None,
+                       key_mean: Optional[torch.Tensor] = None, out_key_mean: Optional[torch.Tensor] = None,
+                       out_log: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """OptR calibration (Algorithm 1) of one layer; cfg overrides OPTR_DEFAULTS (the paper's Table A)."""
+    H, Hq = int(num_kv_heads), int(num_q_heads)
+    a = _Traces(calib, H, Hq)
+    b = _Traces(heldout, H, Hq)
+    if b.nq != a.nq or b.dtype != a.dtype:
+        raise ValueError("held-out traces must have the calibration traces' query count and dtype")
+    _need(w_o, "w_o", a.dtype)
+    if w_o.dim() != 2 or w_o.shape[0] != Hq * HEAD_DIM:
+        raise ValueError(f"w_o must be [{Hq * HEAD_DIM}][d_model], not {tuple(w_o.shape)}")
+    for name, t in (("r0_k", r0_k), ("r0_v", r0_v), ("out_r_k", out_r_k), ("out_r_v", out_r_v)):
+        _need(t, name, torch.float32, (H, HEAD_DIM, HEAD_DIM))
+    _need_key_mean(key_mean, H)
+    _need(out_key_mean, "out_key_mean", torch.float32, (H, HEAD_DIM), optional=True)
+    c = _optr_config(cfg)
+    n_ck = max(1, c.steps // c.eval_every)
+    _need(out_log, "out_log", torch.float64, (H, 2, c.steps + n_ck + 1), optional=True)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().kvq_optr_calibrate(
+        _dtype_code(w_o), ctypes.byref(a.c), ctypes.byref(b.c), H, Hq, a.nq, _dev_ptr(w_o, "w_o"), int(w_o.shape[1]),
+        _dev_ptr(r0_k, "r0_k"), _dev_ptr(r0_v, "r0_v"), _dev_ptr(key_mean, "key_mean"), ctypes.byref(c),
+        _dev_ptr(out_r_k, "out_r_k"), _dev_ptr(out_r_v, "out_r_v"), _dev_ptr(out_key_mean, "out_key_mean"),
+        _dev_ptr(out_log, "out_log"), _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
+        "kvq_optr_calibrate")
+
+
+def kvq_optr_loss_grad(phase: int, traces, num_kv_heads: int, num_q_heads: int, w_o: torch.Tensor, r0: torch.Tensor,
+                       a: torch.Tensor, key_mean: torch.Tensor, out_loss: torch.Tensor, out_grad: torch.Tensor,
+                       r_k_hat: Optional[torch.Tensor] = None, cfg: Optional[dict] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """L_K (phase 0) or L_V (phase 1) and dL/dA at generator a (fp64 [H][128][128]), per KV head."""
+    H, Hq = int(num_kv_heads), int(num_q_heads)
+    t = _Traces(traces, H, Hq)
+    _need(w_o, "w_o", t.dtype)
+    if w_o.dim() != 2 or w_o.shape[0] != Hq * HEAD_DIM:
+        raise ValueError(f"w_o must be [{Hq * HEAD_DIM}][d_model], not {tuple(w_o.shape)}")
+    _need(r0, "r0", torch.float32, (H, HEAD_DIM, HEAD_DIM))
+    _need(a, "a", torch.float64, (H, HEAD_DIM, HEAD_DIM))
+    _need(r_k_hat, "r_k_hat", torch.float32, (H, HEAD_DIM, HEAD_DIM), optional=phase == 0)
+    _need(key_mean, "key_mean", torch.float32, (H, HEAD_DIM))
+    _need(out_loss, "out_loss", torch.float64, (H,))
+    _need(out_grad, "out_grad", torch.float64, (H, HEAD_DIM, HEAD_DIM))
+    c = _optr_config(cfg)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().kvq_optr_loss_grad(
+        _dtype_code(w_o), phase, ctypes.byref(t.c), H, Hq, t.nq, _dev_ptr(w_o, "w_o"), int(w_o.shape[1]),
+        _dev_ptr(r0, "r0"), _dev_ptr(a, "a"), _dev_ptr(r_k_hat, "r_k_hat"), _dev_ptr(key_mean, "key_mean"),
+        ctypes.byref(c), _dev_ptr(out_loss, "out_loss"), _dev_ptr(out_grad, "out_grad"),
+        _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)), "kvq_optr_loss_grad")
 
 
 def kvq_version() -> int:

@@ -353,6 +353,85 @@ int kvq_candidate_nmse(const void *k, const void *v, const void *q, int32_t dtyp
                        float *out_nmse, float *out_nmse_per_query, int32_t *out_best, void *workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * OptR offline calibration ([OptR] Appendix "OptR Algorithm", Algorithm 1;
+ * §4.1 key reparameterization; §4.2 Eq. (11): R = R0 exp(A - A^T); §4.3
+ * Eq. (12)-(14): key loss KL(p || p^K) + lambda_K ||e_K||^2 / d_model; §4.4
+ * Eq. (15)-(16): value loss under the selected key attention; §4.5 Eq. (17)-
+ * (18): the INT2 path with a straight-through estimator; Appendix,
+ * calibration details and Table A: Adam, 80 steps, learning rate 0.02,
+ * held-out selection every 20 steps, the final 64 query positions, clip
+ * ratios 0.96 / 0.92, 64 sink and 256 recent BF16 tokens, lambda_K = 1).
+ *
+ * Traces of one layer: per sequence b of length L_b, keys and values of
+ * every position and the queries of its final num_queries positions (query t
+ * of them sits at position L_b - num_queries + t and attends positions
+ * s <= that one).  For each KV head h (query heads h G .. h G + G - 1, G =
+ * Hq / H): the key mean (the mean of every cached key of the calibration
+ * set, unless key_mean is given); then A_K from 0 by Adam on L_K over the
+ * calibration set, the held-out L_K checked after every eval_every steps and
+ * the first minimum kept; then A_V likewise on L_V, whose attention is that
+ * of the selected key rotation.  Positions [0, min(num_sink, L)) and
+ * [max(that, L - num_recent), L) stay unquantized (keys centered); the rest
+ * go through rotation, clipping, INT2 rounding (the fp32 sequence of
+ * kvq_quantize) and dequantization, with the gradient passed where a value
+ * lies inside its group's clipping range [c min, c max] and blocked
+ * elsewhere.  Post-W_O errors use query head j's rows j*128 .. j*128+127 of
+ * W_O [Hq*128][d_model]; losses are means over every (query, query head)
+ * pair of the set.  Arithmetic is fp64 except the INT2 quantizer (fp32).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t num_seqs;          /* 1 .. 64 */
+  int32_t max_len;           /* row count of k and v per sequence */
+  const int32_t *seq_lens;   /* host [num_seqs], each in [num_queries, max_len] */
+  const void *k, *v;         /* [num_seqs][max_len][H][128], dtype (rows past a length unused) */
+  const void *q;             /* [num_seqs][num_queries][Hq][128], dtype */
+} kvq_trace_set;
+
+typedef struct {
+  double lambda_k;           /* weight of the post-W_O key error (1.0) */
+  float clip_k, clip_v;      /* clip ratios in (0, 1] (0.96, 0.92), fp32 as in kvq_quantize */
+  int32_t num_sink, num_recent;  /* BF16 window sizes (64, 256), >= 0 */
+  int32_t steps;             /* Adam steps per phase (80) */
+  double lr;                 /* Adam learning rate (0.02); betas 0.9, 0.999, eps 1e-8 */
+  int32_t eval_every;        /* held-out checkpoint period (20); with fewer steps, the last step */
+} kvq_optr_config;
+
+size_t kvq_optr_workspace_bytes(const kvq_trace_set *calib, const kvq_trace_set *heldout, int32_t num_kv_heads,
+                                int32_t num_q_heads, int32_t num_queries, int32_t d_model);
+
+/* calib, heldout, cfg: host structs (arrays device, seq_lens host).
+ *   w_o          [Hq*128][d_model], dtype.
+ *   r0_k, r0_v   fp32 [H][128][128] base rotations (any orthogonal).
+ *   key_mean     fp32 [H][128], or NULL to estimate it from calib.
+ *   out_r_k/v    fp32 [H][128][128]: R0 exp(A - A^T) of the selected A.
+ *   out_key_mean fp32 [H][128] or NULL: the centering used.
+ *   out_log      fp64 [H][2][steps + C + 1] or NULL (C = steps / eval_every,
+ *                at least 1): per phase (keys, values) the training loss of
+ *                every step (at the generator before its update), the
+ *                held-out loss at each checkpoint, and the selected step.
+ * Errors: INVALID_ARGUMENT (shapes, lengths, config), UNSUPPORTED (dtype,
+ * more than 64 sequences), WORKSPACE, HIP. */
+int kvq_optr_calibrate(int32_t dtype, const kvq_trace_set *calib, const kvq_trace_set *heldout, int32_t num_kv_heads,
+                       int32_t num_q_heads, int32_t num_queries, const void *w_o, int32_t d_model, const float *r0_k,
+                       const float *r0_v, const float *key_mean, const kvq_optr_config *cfg, float *out_r_k,
+                       float *out_r_v, float *out_key_mean, double *out_log, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* One objective and its gradient at a given generator, per KV head (the
+ * building block of kvq_optr_calibrate, for checking it or driving another
+ * optimizer): phase 0 = L_K at R0 exp(A - A^T) (r0 = the key base rotation),
+ * phase 1 = L_V at R0 exp(A - A^T) (r0 = the value base rotation) under the
+ * attention of the key rotation r_k_hat (fp32 [H][128][128]).
+ *   a          fp64 [H][128][128] device;  key_mean fp32 [H][128] (required).
+ *   out_loss   fp64 [H];  out_grad fp64 [H][128][128] = dL/dA.
+ * Workspace: kvq_optr_workspace_bytes(set, NULL, ...). */
+int kvq_optr_loss_grad(int32_t dtype, int32_t phase, const kvq_trace_set *set, int32_t num_kv_heads,
+                       int32_t num_q_heads, int32_t num_queries, const void *w_o, int32_t d_model, const float *r0,
+                       const double *a, const float *r_k_hat, const float *key_mean, const kvq_optr_config *cfg,
+                       double *out_loss, double *out_grad, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* Human-readable name of a kvq_status value (static string). */
 const char *kvq_status_string(int status);
 /* KVQ_VERSION of the built library. */

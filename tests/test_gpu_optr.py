@@ -1,0 +1,135 @@
+"""OptR calibration on the GPU (kvq_optr_loss_grad, kvq_optr_calibrate)
+against the fp64 oracle (oracle/optr.py) on seeded synthetic traces
+("Output-Aware Rotation for INT2 KV-Cache Quantization": Algorithm 1; §4.2-
+§4.5, Eq. (11)-(18)).
+
+Both sides compute in fp64 and take the INT2 decisions in the same fp32
+sequence on the same fp32-rounded rotated values, so they differ only by
+fp64 summation order (~1e-16 relative per operation).  Bars: losses within
+1e-9 relative, gradients within 1e-8 (rel-L2) at one point; over a whole
+calibration, the per-step training losses and held-out values within 1e-7
+relative, the same selected checkpoints and the rotations within 1e-6.
+(An fp64 rotated value within ~1e-16 of an fp32 rounding boundary could
+still round differently on the two sides; at these sizes that has
+probability ~1e-4 per run.)"""
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_attention_int2_amd import kvq
+    kvq.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def optr(oracle):
+    from oracle import optr as o
+    return o
+
+
+def _gpu(ts, dev):
+    return types.SimpleNamespace(k=ts.k.to(dev), v=ts.v.to(dev), q=ts.q.to(dev), lens=list(ts.lens))
+
+
+def _host(optr, ts):
+    f = lambda t: t.float().numpy()
+    return optr.TraceSet(f(ts.k), f(ts.v), f(ts.q), list(ts.lens))
+
+
+@pytest.mark.parametrize("phase", [0, 1])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_optr_loss_and_gradient_match_oracle(dev, optr, phase, dtype):
+    from decode_attention_int2_amd import kvq
+    pb = synthetic.optr_problem(3, H=2, Hq=4, d_model=96, calib=(2, 200, 260), heldout=(1, 200, 260), nq=16,
+                                dtype=dtype)
+    H, Hq, nq = pb["H"], pb["Hq"], pb["nq"]
+    G = Hq // H
+    cfg = dict(lambda_k=0.7, clip_k=0.9, clip_v=0.85, num_sink=16, num_recent=48)
+    ocfg = optr.Config(**cfg)
+    cal = _host(optr, pb["calib"])
+    mu = optr.key_mean(cal)
+    g = torch.Generator().manual_seed(21 + phase)
+    A = torch.randn((H, D, D), generator=g, dtype=torch.float64) * 0.02
+    r0 = pb["r0_k"] if phase == 0 else pb["r0_v"]
+    # the key rotation whose attention the value objective uses (a rotation, fp32)
+    rk = torch.stack([optr.rotation(torch.randn((D, D), generator=g, dtype=torch.float64) * 0.01,
+                                    pb["r0_k"][h].double()) for h in range(H)]).float()
+    gcal = _gpu(pb["calib"], dev)
+    ws = torch.empty(kvq.kvq_optr_workspace_bytes(gcal, None, H, Hq, pb["w_o"].shape[1]), dtype=torch.uint8,
+                     device=dev)
+    out_loss = torch.empty(H, dtype=torch.float64, device=dev)
+    out_grad = torch.empty((H, D, D), dtype=torch.float64, device=dev)
+    kvq.kvq_optr_loss_grad(phase, gcal, H, Hq, pb["w_o"].to(dev), r0.to(dev), A.to(dev), torch.from_numpy(mu).to(dev),
+                           out_loss, out_grad, r_k_hat=rk.to(dev) if phase else None, cfg=cfg, workspace=ws)
+    torch.cuda.synchronize()
+    wo = torch.from_numpy(pb["w_o"].double().numpy())
+    for h in range(H):
+        a = A[h].clone().requires_grad_(True)
+        if phase == 0:
+            L = optr.key_loss(a, r0[h].double(), cal, h, G, nq, mu, wo, ocfg)
+        else:
+            p_hat = optr.key_attention(cal, h, G, nq, mu, rk[h].double(), ocfg)
+            L = optr.value_loss(a, r0[h].double(), cal, h, G, nq, p_hat, wo, ocfg)
+        L.backward()
+        lg, lo = float(out_loss[h]), float(L.detach())
+        gg, go = out_grad[h].cpu(), a.grad
+        el = abs(lg - lo) / abs(lo)
+        eg = float((gg - go).norm() / go.norm())
+        print(f"{dtype} phase {phase} head {h}: loss GPU {lg:.12g} oracle {lo:.12g} (rel {el:.1e}), "
+              f"grad rel-L2 {eg:.1e}", flush=True)
+        assert el <= 1e-9 and eg <= 1e-8
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_optr_calibration_matches_oracle(dev, optr, dtype):
+    """Algorithm 1 end to end (8 Adam steps per phase, checkpoints every 4):
+    key mean, per-step training losses, held-out values, selected steps and
+    the returned rotations."""
+    import time
+    from decode_attention_int2_amd import kvq
+    pb = synthetic.optr_problem(5, H=2, Hq=4, d_model=96, calib=(2, 200, 260), heldout=(2, 200, 260), nq=16,
+                                dtype=dtype)
+    H, Hq, nq = pb["H"], pb["Hq"], pb["nq"]
+    cfg = dict(steps=8, eval_every=4, num_sink=16, num_recent=48)
+    gcal, ghel = _gpu(pb["calib"], dev), _gpu(pb["heldout"], dev)
+    ws = torch.empty(kvq.kvq_optr_workspace_bytes(gcal, ghel, H, Hq, pb["w_o"].shape[1]), dtype=torch.uint8,
+                     device=dev)
+    rk = torch.empty((H, D, D), dtype=torch.float32, device=dev)
+    rv = torch.empty_like(rk)
+    mu = torch.empty((H, D), dtype=torch.float32, device=dev)
+    log = torch.full((H, 2, 8 + 2 + 1), float("nan"), dtype=torch.float64, device=dev)
+    t0 = time.perf_counter()
+    kvq.kvq_optr_calibrate(gcal, ghel, H, Hq, pb["w_o"].to(dev), pb["r0_k"].to(dev), pb["r0_v"].to(dev), rk, rv,
+                           cfg=cfg, out_key_mean=mu, out_log=log, workspace=ws)
+    torch.cuda.synchronize()
+    gpu_s = time.perf_counter() - t0
+    ocfg = optr.Config(**dict(optr.Config().__dict__, **cfg))
+    res = optr.calibrate(_host(optr, pb["calib"]), _host(optr, pb["heldout"]), Hq, nq, pb["w_o"].float().numpy(),
+                         pb["r0_k"].numpy(), pb["r0_v"].numpy(), ocfg)
+    assert np.array_equal(mu.cpu().numpy(), res["key_mean"])
+    lg = log.cpu().numpy()
+    for h in range(H):
+        for ph, name in ((0, "key"), (1, "value")):
+            ol = res["log"][h][name]
+            tr = np.abs(lg[h, ph, :8] - ol["train"]) / np.abs(ol["train"])
+            he = np.abs(lg[h, ph, 8:10] - ol["heldout"]) / np.abs(ol["heldout"])
+            print(f"{dtype} head {h} {name}: train losses {np.round(ol['train'], 5).tolist()}, held-out "
+                  f"{np.round(ol['heldout'], 6).tolist()}, selected {ol['selected_step']} (GPU {lg[h, ph, 10]:.0f}); "
+                  f"max rel diff train {tr.max():.1e}, held-out {he.max():.1e}", flush=True)
+            assert tr.max() <= 1e-7 and he.max() <= 1e-7
+            assert int(lg[h, ph, 10]) == ol["selected_step"]
+    er = max(float(np.abs(rk.cpu().numpy() - res["r_k"]).max()), float(np.abs(rv.cpu().numpy() - res["r_v"]).max()))
+    print(f"{dtype}: rotations max |diff| {er:.1e}; GPU calibration {gpu_s * 1e3:.1f} ms", flush=True)
+    assert er <= 1e-6
