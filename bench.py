@@ -325,6 +325,58 @@ def cpu_baseline_search(threads: int) -> dict:
                                                       f"thread: {thr_s:.2f} s"}}
 
 
+def optr_calibration(dev, cpu_sample: bool) -> dict:
+    """The OptR offline calibration (Algorithm 1) of one synthetic layer at the
+    paper's settings: 8 KV heads, 32 query heads, d_model 4096, 6 calibration
+    and 5 held-out bf16 sequences of 328-700 tokens, the final 64 query
+    positions, 80 Adam steps per phase, held-out checks every 20 steps; one
+    timed call after an untimed one.  With cpu_sample, the oracle's time for a
+    bounded sample (one KV head, 4 steps per phase, one checkpoint each),
+    scaled by 8 heads x 20 to the full calibration."""
+    import types
+    import torch
+    import synthetic
+    from decode_attention_int2_amd import kvq
+    H, Hq, dm = 8, 32, 4096
+    pb = synthetic.optr_problem(11, H=H, Hq=Hq, d_model=dm)
+    g = lambda ts: types.SimpleNamespace(k=ts.k.to(dev), v=ts.v.to(dev), q=ts.q.to(dev), lens=list(ts.lens))
+    cal, hel = g(pb["calib"]), g(pb["heldout"])
+    ws = torch.empty(kvq.kvq_optr_workspace_bytes(cal, hel, H, Hq, dm), dtype=torch.uint8, device=dev)
+    rk = torch.empty((H, 128, 128), dtype=torch.float32, device=dev)
+    rv = torch.empty_like(rk)
+    args = (cal, hel, H, Hq, pb["w_o"].to(dev), pb["r0_k"].to(dev), pb["r0_v"].to(dev), rk, rv)
+    kvq.kvq_optr_calibrate(*args, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    kvq.kvq_optr_calibrate(*args, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    out = {"workload": "one layer, 8/32 heads, d_model 4096, 6 + 5 sequences of 328-700 tokens, 64 queries, "
+                       "80 + 80 Adam steps", "ms": round(ms, 2), "arithmetic": "fp64 (INT2 quantizer in fp32)",
+           "workspace_mb": round(ws.numel() / 2 ** 20, 1),
+           "page_figures_for_context": {"calibration_min_per_model": [6.25, 7.05, 11.03],
+                                        "models": ["Qwen3-4B", "Qwen3-8B", "Phi4-14B"], "hardware": "one A100"}}
+    del ws
+    if cpu_sample:
+        import numpy as np
+        from oracle import optr
+        G = Hq // H
+        f = lambda t: t.float().numpy()
+        sub = lambda ts: optr.TraceSet(np.ascontiguousarray(f(ts.k)[:, :, :1]), np.ascontiguousarray(f(ts.v)[:, :, :1]),
+                                       np.ascontiguousarray(f(ts.q)[:, :, :G]), list(ts.lens))
+        t0 = time.perf_counter()
+        optr.calibrate(sub(pb["calib"]), sub(pb["heldout"]), G, pb["nq"], f(pb["w_o"])[:G * 128],
+                       pb["r0_k"].numpy()[:1], pb["r0_v"].numpy()[:1], optr.Config(steps=4, eval_every=4))
+        s = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value_s_estimated_full": round(s * H * 20, 1), "cores": torch.get_num_threads(),
+                               "kind": "oracle",
+                               "sample": f"1 KV head x 4 steps per phase ({s:.2f} s), x 8 heads x 20 for the full "
+                                         f"calibration (fp64 torch ops, {torch.get_num_threads()} threads)"}
+    return out
+
+
 def calibration_search(dev, timed):
     """Time one kvq_candidate_nmse call on calib64k (65,536 tokens x 8 KV
     heads, 9 dense candidates x 5 clips, 64 queries, per-head selection)."""
@@ -492,10 +544,11 @@ def main():
         torch.cuda.empty_cache()
     # calibration search (a separate workload of the same path) and the
     # evaluation page's own protocol
-    cal = env = None
+    cal = env = optr_cal = None
     if not a.no_calibration:
         cal = calibration_search(dev, timed)
         env = envelope_protocol(dev, timed, median_of)
+        optr_cal = optr_calibration(dev, not a.no_cpu_baseline)
 
     base = None
     if w_cpu is not None:
@@ -538,6 +591,7 @@ def main():
         "other_decode_workloads": others,
         "calibration_search": cal,
         "envelope_protocol": env,
+        "optr_calibration": optr_cal,
     }
     print(json.dumps(out))
 
