@@ -111,7 +111,6 @@ __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t a, uint32_t sel
 
 struct MfmaArgs {
   int R, G, Hq, H, Nq, n_rg;  // n_rg: groups of 4 query rows per KV head
-  int num_work;               // splits * H * n_rg * num_seqs workgroups of work
   int split_tokens, splits, max_seq_len;
   int P, p_shift;             // page size in tokens (a power of two) and its log2
   int max_pages;
@@ -516,16 +515,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float qd_s[kDense ? 4 : 1][D];  // dense R_K: q R_K of the group's rows
   __shared__ uint32_t s_last;
   __shared__ uint32_t s_next;               // next unclaimed 64-token block of the split
-  // Work index of this workgroup: the dispatcher hands workgroup i to XCD
-  // i % 8, so the work is laid out XCD-major (XCD x takes work items
-  // [x per, (x + 1) per)) with the row groups of one (sequence, KV head,
-  // split) adjacent: they read the same cache bytes and share that XCD's L2.
-  // Work items past the end (padding to a multiple of 8) exit at once.
-  const int per = (a.num_work + 7) / 8;
-  const int wk = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
-  if (wk >= a.num_work) return;
-  const int rg = wk % a.n_rg, s = (wk / a.n_rg) % a.splits;
-  const int h = (wk / (a.n_rg * a.splits)) % a.H, b = wk / (a.n_rg * a.splits * a.H);
+  const int s = blockIdx.x, b = blockIdx.z;
+  const int h = blockIdx.y / a.n_rg, rg = blockIdx.y % a.n_rg;  // KV head, group of 4 query rows
   const int row0 = 4 * rg, nrows = min(4, a.R - row0);
   const size_t unit = (static_cast<size_t>(b) * a.H + h) * a.n_rg + rg;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1158,10 +1149,7 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
     a.win_W = win->num_recent;
     a.win_mu = win->key_mean;
   }
-  const int64_t work = static_cast<int64_t>(pl.splits) * pl.H * a.n_rg * pl.num_seqs;
-  if (work > INT32_MAX - 8) return hipErrorInvalidValue;
-  a.num_work = static_cast<int>(work);
-  const dim3 grid(static_cast<unsigned>(8 * ((work + 7) / 8)));
+  const dim3 grid(pl.splits, pl.H * a.n_rg, pl.num_seqs);
   const bool f32 = dtype == KVQ_F32 || rk.kind == kRotPrescaled;
   const bool dense = rk.kind == KVQ_ROT_DENSE;
   const dim3 block(64 * kWaves);
