@@ -13,7 +13,9 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvq.so")
+# (KVQ_LIB points the loader at another build of the library, e.g. the
+# sanitizer build of the test suite)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID_ARGUMENT, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = 0, 1, 2, 3, 4
 KVQ_F32, KVQ_BF16 = 0, 1

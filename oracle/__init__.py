@@ -22,7 +22,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
+# (KVQ_ORACLE_LIB points the loader at another build of the same source, e.g.
+# the sanitizer build of the test suite)
+_LIB_PATH = os.environ.get("KVQ_ORACLE_LIB") or os.path.join(_HERE, "libkvq_oracle.so")
 
 ROT_IDENTITY, ROT_SIGNED_HADAMARD, ROT_DENSE = 0, 1, 2
 SELECT_JOINT, SELECT_PER_HEAD = 0, 1
