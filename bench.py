@@ -45,6 +45,11 @@ BYTES_PER_TOKEN_HEAD = 72      # 2 x 32 B codes + 2 x 4 B fp16 scale/zero
 WORKLOAD = "paged16x32k"
 
 
+def progress(msg: str) -> None:
+    """One line per finished phase on stderr (a long profiled run stays visibly alive)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -484,10 +489,12 @@ def main():
     torch.cuda.synchronize()
     step_ms = timed(lambda i: step(a.warmup + i), a.steps)
     wall = timed.wall_s
+    progress(f"steps: {step_ms:.3f} ms per step")
     # decode attention and the cache write: median of 5 runs of >= 50 (>= 20) calls
     attn_ms = median_of(lambda: timed(lambda i: decode(i, with_wo=False), max(50, a.steps)))
     quant_ms = median_of(lambda: timed(quantize, max(20, a.steps)))
     decode_ms = median_of(lambda: timed(decode, max(50, a.steps)))
+    progress(f"decode attention {attn_ms * 1e3:.2f} us, cache write {quant_ms * 1e3:.2f} us, call {decode_ms * 1e3:.2f} us")
 
     kv_bytes = B * T * H * BYTES_PER_TOKEN_HEAD
     attn_gbs = kv_bytes / (attn_ms * 1e-3) / 1e9
@@ -523,6 +530,7 @@ def main():
                    "bits_per_element": round(kvq.kvq_bits_per_element(T, S_w, W_w), 4),
                    "window_write_us_all_tokens": round(wr_ms * 1e3, 2)}
         del gws
+        progress(f"windows decode {win_ms * 1e3:.2f} us")
 
     clip_k, clip_v, desc = w.clip_k, w.clip_v, synthetic.DESCRIPTIONS[WORKLOAD]
     w_cpu = None
@@ -538,21 +546,26 @@ def main():
     # 3 copies that stay in the Infinity Cache) and 4 x 131K tokens
     others = None
     if not a.no_other_workloads:
-        others = [decode_workload("gqa32k", dev, timed, median_of, min_bytes=600 << 20),
-                  decode_workload("gqa32k", dev, timed, median_of),
-                  decode_workload("long131k", dev, timed, median_of)]
+        others = []
+        for name, mb in (("gqa32k", 600 << 20), ("gqa32k", 0), ("long131k", 0)):
+            others.append(decode_workload(name, dev, timed, median_of, min_bytes=mb))
+            progress(f"{name}: decode {others[-1]['decode_attn_us']} us, cache write {others[-1]['cache_write_us']} us")
         torch.cuda.empty_cache()
     # calibration search (a separate workload of the same path) and the
     # evaluation page's own protocol
     cal = env = optr_cal = None
     if not a.no_calibration:
         cal = calibration_search(dev, timed)
+        progress(f"calibration search {cal['ms']} ms")
         env = envelope_protocol(dev, timed, median_of)
+        progress(f"envelope protocol: search {env['search_ms']} ms")
         optr_cal = optr_calibration(dev, not a.no_cpu_baseline)
+        progress(f"OptR calibration {optr_cal['ms']} ms")
 
     base = None
     if w_cpu is not None:
         base = cpu_baseline(w_cpu)
+        progress("cpu baseline")
         base["threaded"] = cpu_baseline_threaded(w_cpu, w_cpu["threads"])
         base["cpu_model"] = host_cpu()[2]
         if not a.no_calibration:
