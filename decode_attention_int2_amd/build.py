@@ -42,12 +42,16 @@ def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, lib: str = LIB, build_dir: str = BUILD, host_flags=()) -> str:
+PHASES_LIB = os.path.join(PKG, "libkvq_phases.so")
+
+
+def build(verbose: bool = False, lib: str = LIB, build_dir: str = BUILD, host_flags=(), defines=()) -> str:
     """Compile every source and link lib.  host_flags are passed to the host
     compilation only (each behind -Xarch_host), e.g. the sanitizers of the
-    host-side validation test."""
+    host-side validation test; defines (-D...) to both compilations, e.g.
+    KVQ_PHASE_TIMESTAMPS for the diagnostic phase-timestamp library."""
     os.makedirs(build_dir, exist_ok=True)
-    extra = [f for fl in host_flags for f in ("-Xarch_host", fl)]
+    extra = [f for fl in host_flags for f in ("-Xarch_host", fl)] + [f"-D{d}" for d in defines]
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
     tmp = lib + ".tmp"
@@ -62,5 +66,10 @@ def build(verbose: bool = False, lib: str = LIB, build_dir: str = BUILD, host_fl
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--phase-timestamps" in sys.argv[1:]:
+        # the diagnostic library of phase_profile.py (timestamps at the decode
+        # kernel's phase boundaries); libkvq.so is not touched
+        build(verbose=True, lib=PHASES_LIB, build_dir=BUILD + "_phases", defines=("KVQ_PHASE_TIMESTAMPS",))
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -46,6 +46,21 @@
 //   arrival counter) merges the partials, applies R_V^T and writes the output.
 #include "kvq_internal.h"
 
+#ifdef KVQ_PHASE_TIMESTAMPS
+// Diagnostic build (libkvq_phases.so) only: every wave of a launch records
+// the wall clock at its phase boundaries -- entry, main loop start, main loop
+// end, arrival counted, and in the merging workgroup: partials merged, value
+// rotation applied, outputs stored -- with the hardware ids of its compute
+// unit.  Waves past kPhaseWaves record nothing.
+constexpr int kPhaseWaves = 8192;
+constexpr int kPhaseFields = 12;  // hw id, xcc id, blocks, t entry, t loop, t loop end, t arrived, t merged,
+                                  // t rotated, t stored, 2 unused
+__device__ unsigned long long kvq_phase_ts[kPhaseWaves * kPhaseFields];
+#define KVQ_PHASE(i) (phase_t[i] = wall_clock64())
+#else
+#define KVQ_PHASE(i) ((void)0)
+#endif
+
 namespace kvq {
 namespace {
 
@@ -525,6 +540,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float qd_s[kDense ? 4 : 1][D];  // dense R_K: q R_K of the group's rows
   __shared__ uint32_t s_last;
   __shared__ uint32_t s_next;               // next unclaimed 64-token block of the split
+#ifdef KVQ_PHASE_TIMESTAMPS
+  unsigned long long phase_t[7] = {0, 0, 0, 0, 0, 0, 0};
+#endif
+  KVQ_PHASE(0);
   const int s = blockIdx.x, b = blockIdx.z;
   const int h = blockIdx.y / a.n_rg, rg = blockIdx.y % a.n_rg;  // KV head, group of 4 query rows
   const int row0 = 4 * rg, nrows = min(4, a.R - row0);
@@ -873,6 +892,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     ja1n = __builtin_amdgcn_readfirstlane(v);
     load_addr<P16>(c, t_begin + kBlk * min(ja1n, nb), ak1);
   };
+  KVQ_PHASE(1);
   for (;;) {
     if (jc0 >= nb) break;
     step(b0, jc0, a0, ja0, a1, ja1);
@@ -882,6 +902,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     step(b2, jc2, a2, ja2, a0, ja0);
   }
 
+  KVQ_PHASE(2);
   // ---- this wave's partial of each row: m = -kappa, l, z, flag, acc[128]
   // (rows past the group's last are computed and never stored)
   const float lrow = row16_sum(st.lsum);
@@ -1005,7 +1026,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __syncthreads();
   if (threadIdx.x == 0) s_last = arrive_counted(cnt, cnt_word == arrival_valid_value(cnt, a.splits), a.epoch, a.splits) ? 1u : 0u;
   __syncthreads();
+  KVQ_PHASE(3);
+#ifdef KVQ_PHASE_TIMESTAMPS
+  // (vector stores by lanes 0-11, one field each)
+  auto phase_store = [&]() {
+    const unsigned wid = ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * kWaves + wave;
+    if (wid < kPhaseWaves && lane < kPhaseFields) {
+      const unsigned long long hw = static_cast<unsigned>(__builtin_amdgcn_s_getreg((31 << 11) | 4));  // HW_ID
+      const unsigned long long xcc = static_cast<unsigned>(__builtin_amdgcn_s_getreg((3 << 11) | 20));  // XCC_ID
+      const unsigned long long f[kPhaseFields] = {hw, xcc, static_cast<unsigned long long>(nb), phase_t[0],
+                                                  phase_t[1], phase_t[2], phase_t[3], phase_t[4], phase_t[5],
+                                                  phase_t[6], 0, 0};
+      unsigned long long v = f[0];
+#pragma unroll
+      for (int i = 1; i < kPhaseFields; ++i) v = lane == i ? f[i] : v;
+      kvq_phase_ts[wid * kPhaseFields + lane] = v;
+    }
+  };
+  if (s_last == 0) {
+    phase_store();
+    return;
+  }
+#else
   if (s_last == 0) return;
+#endif
   // dense R_V: the head's matrix is staged in LDS by the whole workgroup
   // (its loads go out together with the merge's)
   const bool vdense = a.rv.kind == KVQ_ROT_DENSE;
@@ -1032,6 +1076,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     if constexpr (kWin) merge_partials(base + static_cast<size_t>(a.parts) * (D + 4), a.splits, lane, ow0, ow1, &mw, &lw);
     merge_partials(base, a.parts, lane, o0, o1, &mi, &li);
   }
+#ifdef KVQ_PHASE_TIMESTAMPS
+  __builtin_amdgcn_s_waitcnt(0);
+  KVQ_PHASE(4);
+#endif
   if (vdense) {
     float4 *rd = reinterpret_cast<float4 *>(rs) + threadIdx.x;
     rd[0] = v0;
@@ -1081,6 +1129,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       }
     }
   }
+  KVQ_PHASE(5);
   if (wave < nrows) store_output_wave(a.out_o, a.ot, row, j, a.Hq, lane, o0, o1);
   if (a.y_zero && h == 0) {
     // the query positions of this group start their W_O rows at zero (the
@@ -1092,6 +1141,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       for (int i = threadIdx.x; i < a.d_model; i += 64 * kWaves) yr[i] = 0.0f;
     }
   }
+#ifdef KVQ_PHASE_TIMESTAMPS
+  __builtin_amdgcn_s_waitcnt(0);
+  KVQ_PHASE(6);
+  phase_store();
+#endif
 }
 
 }  // namespace
@@ -1193,3 +1247,25 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
 }
 
 }  // namespace kvq
+
+#ifdef KVQ_PHASE_TIMESTAMPS
+// Diagnostic entry points of the phase-timestamp build (not part of
+// libkvq.so): copy the per-wave records of the last launches to host memory
+// (`bytes` at most kPhaseWaves x kPhaseFields x 8) and clear them; the wall
+// clock's rate in kHz.
+extern "C" int kvq_phase_timestamps(void *host, size_t bytes) {
+  const size_t n = bytes < sizeof(kvq_phase_ts) ? bytes : sizeof(kvq_phase_ts);
+  if (hipDeviceSynchronize() != hipSuccess) return 5;
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(kvq_phase_ts), n, 0, hipMemcpyDeviceToHost) != hipSuccess) return 5;
+  static unsigned long long zeros[kPhaseWaves * kPhaseFields];
+  return hipMemcpyToSymbol(HIP_SYMBOL(kvq_phase_ts), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice) == hipSuccess
+             ? 0
+             : 5;
+}
+extern "C" int kvq_phase_clock_khz() {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return -1;
+  return khz;
+}
+#endif
