@@ -537,7 +537,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ float qsum_s[4];
   __shared__ int qshift_s[4];              // fixed-point shift S of each row's digits
   __shared__ uint32_t digit_s[8][64];      // key-side A operand: dword [m][e] of each lane
-  __shared__ float qd_s[kDense ? 4 : 1][D];  // dense R_K: q R_K of the group's rows
   __shared__ uint32_t s_last;
   __shared__ uint32_t s_next;               // next unclaimed 64-token block of the split
 #ifdef KVQ_PHASE_TIMESTAMPS
@@ -617,21 +616,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     wu1 = min(wu0 + slice, n_win);
     load_window_batch(a, b, h, wu0, wu1, n_sink, hi, wk, wv);
   }
-  // dense R_K: this thread's 8 x 16 bytes of the head's matrix (64 KB per
-  // workgroup, staged in LDS for the query rows' product)
+  // dense R_K: thread (quarter kq = t / 128, column j = t % 128) holds
+  // R_K[32 kq + i][j], i < 32, for the query rows' product below (each load
+  // instruction reads 64 consecutive floats of one matrix row)
   // (eight named registers: an array here would be placed in LDS)
   float4 rs0, rs1, rs2, rs3, rs4, rs5, rs6, rs7;
   if constexpr (kDense) {
-    const float4 *rm = reinterpret_cast<const float4 *>(a.rk.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x;
-    constexpr int kT = 64 * kWaves;
-    rs0 = rm[0];
-    rs1 = rm[kT];
-    rs2 = rm[2 * kT];
-    rs3 = rm[3 * kT];
-    rs4 = rm[4 * kT];
-    rs5 = rm[5 * kT];
-    rs6 = rm[6 * kT];
-    rs7 = rm[7 * kT];
+    const float *rm = a.rk.matrix + static_cast<size_t>(h) * D * D + (threadIdx.x >> 7) * 32 * D + (threadIdx.x & 127);
+    auto col4 = [&](int i0) { return float4{rm[i0 * D], rm[(i0 + 1) * D], rm[(i0 + 2) * D], rm[(i0 + 3) * D]}; };
+    rs0 = col4(0);
+    rs1 = col4(4);
+    rs2 = col4(8);
+    rs3 = col4(12);
+    rs4 = col4(16);
+    rs5 = col4(20);
+    rs6 = col4(24);
+    rs7 = col4(28);
   }
   // blocks of the split: wave w starts with blocks w, w + 8, w + 16 and then
   // claims the next unclaimed block from an LDS counter (waves of one CU
@@ -672,36 +672,43 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     }
     if constexpr (kDense) {
       // q' = q R_K of the group's 4 rows (rows past the last are zero): the
-      // matrix goes to facc_all (unused until the first flush), the raw rows
-      // to qs; wave w forms columns 16 w .. 16 w + 15 of the 4 rows, each an
-      // fp32 sum in row order
-      float *rs = &facc_all[0][0];
-      {
-        float4 *rd = reinterpret_cast<float4 *>(rs) + threadIdx.x;
-        constexpr int kT = 64 * kWaves;
-        rd[0] = rs0;
-        rd[kT] = rs1;
-        rd[2 * kT] = rs2;
-        rd[3 * kT] = rs3;
-        rd[4 * kT] = rs4;
-        rd[5 * kT] = rs5;
-        rd[6 * kT] = rs6;
-        rd[7 * kT] = rs7;
-      }
+      // raw rows go to qs; thread (kq, j) sums its quarter of column j for
+      // the 4 rows (fp32, in row order; the rows' values are read by all
+      // lanes of a wave at once), the quarters meet in facc_all (unused until
+      // the first flush) and are added in quarter order
       if (wave < 4) {
         qs[wave][lane] = y0;
         qs[wave][lane + 64] = y1;
       }
       __syncthreads();
-      const int col = 16 * wave + (lane & 15), rr = lane >> 4;
-      float acc = 0.0f;
-#pragma unroll 8
-      for (int i = 0; i < D; ++i) acc += qs[rr][i] * rs[i * D + col];
-      qd_s[rr][col] = acc;
+      const int kq = threadIdx.x >> 7, jc = threadIdx.x & 127;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(&qs[r][32 * kq]);
+        const float4 rq[8] = {rs0, rs1, rs2, rs3, rs4, rs5, rs6, rs7};
+        float acc = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float4 x = x4[m];
+          acc += x.x * rq[m].x;
+          acc += x.y * rq[m].y;
+          acc += x.z * rq[m].z;
+          acc += x.w * rq[m].w;
+        }
+        pr[r] = acc;
+      }
+      float *qpart = &facc_all[0][0];  // [quarter][row][column]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qpart[(kq * 4 + r) * D + jc] = pr[r];
       __syncthreads();
       if (wave < 4) {
-        y0 = qd_s[wave][lane] * (kLog2eF * kInvSqrtD);
-        y1 = qd_s[wave][lane + 64] * (kLog2eF * kInvSqrtD);
+        auto col = [&](int j) {
+          return ((qpart[(0 * 4 + wave) * D + j] + qpart[(1 * 4 + wave) * D + j]) + qpart[(2 * 4 + wave) * D + j]) +
+                 qpart[(3 * 4 + wave) * D + j];
+        };
+        y0 = col(lane) * (kLog2eF * kInvSqrtD);
+        y1 = col(lane + 64) * (kLog2eF * kInvSqrtD);
       }
     }
     if (wave < 4) {
@@ -1053,19 +1060,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // dense R_V: the head's matrix is staged in LDS by the whole workgroup
   // (its loads go out together with the merge's)
   const bool vdense = a.rv.kind == KVQ_ROT_DENSE;
-  float *rs = &facc_all[0][0];  // (free: the flushed accumulators are in the partials)
-  constexpr int kT = 64 * kWaves;
+  // (thread t holds R_V[t / 4][32 (t % 4) .. 32 (t % 4) + 31], 128 consecutive bytes)
   float4 v0, v1, v2, v3, v4, v5, v6, v7;
   if (vdense) {
-    const float4 *rm = reinterpret_cast<const float4 *>(a.rv.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x;
+    const float4 *rm =
+        reinterpret_cast<const float4 *>(a.rv.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x * 8;
     v0 = rm[0];
-    v1 = rm[kT];
-    v2 = rm[2 * kT];
-    v3 = rm[3 * kT];
-    v4 = rm[4 * kT];
-    v5 = rm[5 * kT];
-    v6 = rm[6 * kT];
-    v7 = rm[7 * kT];
+    v1 = rm[1];
+    v2 = rm[2];
+    v3 = rm[3];
+    v4 = rm[4];
+    v5 = rm[5];
+    v6 = rm[6];
+    v7 = rm[7];
   }
   const int qq = (row0 + min(wave, nrows - 1)) / a.G, j = h * a.G + (row0 + min(wave, nrows - 1)) % a.G;
   const size_t row = static_cast<size_t>(b) * a.Nq + qq;
@@ -1081,32 +1088,33 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   KVQ_PHASE(4);
 #endif
   if (vdense) {
-    float4 *rd = reinterpret_cast<float4 *>(rs) + threadIdx.x;
-    rd[0] = v0;
-    rd[kT] = v1;
-    rd[2 * kT] = v2;
-    rd[3 * kT] = v3;
-    rd[4 * kT] = v4;
-    rd[5 * kT] = v5;
-    rd[6 * kT] = v6;
-    rd[7 * kT] = v7;
     // out[r][i] = sum_c o'[r][c] R_V[i][c]: the rows' o' to LDS (rows past
-    // the last are zero), wave w forms columns 16 w .. 16 w + 15 of the 4
-    // rows; column i starts its sum at c = i (mod 128), so the 16 columns of
-    // one instruction read 16 different banks
+    // the last are zero); thread t sums its 32 columns of row i = t / 4 for
+    // the 4 rows (fp32, in column order; 4 addresses per instruction), and
+    // the 4 threads of row i add their sums (lanes t ^ 1, then t ^ 2)
     if (wave < 4) {
       red[wave][0][lane] = o0;
       red[wave][0][lane + 64] = o1;
     }
     __syncthreads();
-    const int col = 16 * wave + (lane & 15), rr = lane >> 4;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) {
-      const int cc = (k + col) & (D - 1);
-      acc += red[rr][0][cc] * rs[col * D + cc];
+    const int ri = threadIdx.x >> 2, c0 = 32 * (threadIdx.x & 3);
+    const float4 rv4[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 *x4 = reinterpret_cast<const float4 *>(&red[r][0][c0]);
+      float acc = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float4 x = x4[m];
+        acc += x.x * rv4[m].x;
+        acc += x.y * rv4[m].y;
+        acc += x.z * rv4[m].z;
+        acc += x.w * rv4[m].w;
+      }
+      acc += fdpp_xor1(acc);
+      acc += fdpp_xor2(acc);
+      if ((threadIdx.x & 3) == 0) red[r][1][ri] = acc;
     }
-    red[rr][1][col] = acc;
     __syncthreads();
     o0 = red[wave < 4 ? wave : 0][1][lane];
     o1 = red[wave < 4 ? wave : 0][1][lane + 64];
