@@ -9,7 +9,8 @@ then, on a GPU:
 
 The workload's cache is written into three rotating buffers (as bench.py
 does, so that each decode reads its cache from HBM); after untimed launches,
-each recorded launch is one kvq_decode_attn call (no W_O).  Per launch, with
+each recorded launch is the last of a run of back-to-back kvq_decode_attn
+calls (no W_O), as in a decode loop.  Per launch, with
 times relative to the first wave's entry:
   * entry: when the last workgroup started;
   * loop start: when each wave began its main loop (query rows ready, first
@@ -97,6 +98,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="paged16x32k")
     ap.add_argument("--launches", type=int, default=5)
+    ap.add_argument("--run", type=int, default=20, help="back-to-back launches per record (the last is recorded)")
     ap.add_argument("--raw", default=None, help="also write every wave's record of every launch here (JSON lines)")
     a = ap.parse_args()
     import torch
@@ -130,7 +132,11 @@ def main():
     khz = lib.kvq_phase_clock_khz()
     per = []
     for i in range(a.launches):
-        dec(30 + i)
+        # a run of back-to-back launches; the records are the last one's (each
+        # wave overwrites its own), taken in steady state: a launch right
+        # after an idle GPU starts its XCDs up to ~4 us apart
+        for j in range(a.run):
+            dec(30 + i * a.run + j)
         if lib.kvq_phase_timestamps(ctypes.addressof(buf), ctypes.sizeof(buf)) != 0:
             raise SystemExit("kvq_phase_timestamps failed")
         rec = []
