@@ -961,9 +961,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
   if (a.premerge) {
-    // many splits: the 8 waves' partials of each row are merged here first
-    // (one partial per split and row), so that the last split merges one
-    // per split
+    // more than one split: the 8 waves' partials of each row are merged
+    // here first (one partial per split and row), so that the last split
+    // merges one per split
     __syncthreads();
     if (wave < nrows) {
       const int r = wave;

@@ -18,7 +18,10 @@ constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
 constexpr int kMaxMfmaSplitTokens = 1 << 18;
 constexpr int kMaxSplits = 4096;            // split partials merged per (row, head)
 constexpr int kMfmaWaves = 8;               // waves per workgroup of the matrix-core decode kernel
-constexpr int kMaxSplitsNoPremerge = 8;     // more splits: the waves' partials are merged per split first
+constexpr int kMaxSplitsNoPremerge = 1;     // more splits: the waves' partials are merged per split first (the last
+                                             // split then loads one partial per split: 16 x 32K 59.3 -> 57.6 us,
+                                             // 4 x 131K 78.1 -> 75.3 us against merging the 8 waves' partials of
+                                             // up to 8 splits at the end)
 constexpr int64_t kMaxSeqLen = static_cast<int64_t>(1) << 26;  // max_seq_len accepted by the decode entry point
 
 // Rotation descriptor passed by value to kernels.
