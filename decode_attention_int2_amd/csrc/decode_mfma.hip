@@ -54,7 +54,7 @@
 // unit.  Waves past kPhaseWaves record nothing.
 constexpr int kPhaseWaves = 8192;
 constexpr int kPhaseFields = 12;  // hw id, xcc id, blocks, t entry, t loop, t loop end, t arrived, t merged,
-                                  // t rotated, t stored, 2 unused
+                                  // t rotated, t stored, t query digits ready, t first block's data
 __device__ unsigned long long kvq_phase_ts[kPhaseWaves * kPhaseFields];
 #define KVQ_PHASE(i) (phase_t[i] = wall_clock64())
 #else
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ uint32_t s_last;
   __shared__ uint32_t s_next;               // next unclaimed 64-token block of the split
 #ifdef KVQ_PHASE_TIMESTAMPS
-  unsigned long long phase_t[7] = {0, 0, 0, 0, 0, 0, 0};
+  unsigned long long phase_t[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
 #endif
   KVQ_PHASE(0);
   const int s = blockIdx.x, b = blockIdx.z;
@@ -729,6 +729,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // and this lane's query row g
   for (int d = wave; d < 8; d += kWaves) digit_s[d][lane] = query_digit_word(qs, qshift_s, lane, d >> 2, d & 3);
   __syncthreads();
+  KVQ_PHASE(7);  // query digits ready
   State st;
   const int hr = c.g;  // query row (within the group) of the key-side lanes
 #pragma unroll
@@ -900,6 +901,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     load_addr<P16>(c, t_begin + kBlk * min(ja1n, nb), ak1);
   };
   KVQ_PHASE(1);
+#ifdef KVQ_PHASE_TIMESTAMPS
+  {
+    // (diagnostic: waits for the first block's key codes)
+    uint32_t first = b0.kc[0].x;
+    asm volatile("" : "+v"(first));
+    phase_t[8] = wall_clock64() + (first & 0u);
+  }
+#endif
   for (;;) {
     if (jc0 >= nb) break;
     step(b0, jc0, a0, ja0, a1, ja1);
@@ -1043,7 +1052,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       const unsigned long long xcc = static_cast<unsigned>(__builtin_amdgcn_s_getreg((3 << 11) | 20));  // XCC_ID
       const unsigned long long f[kPhaseFields] = {hw, xcc, static_cast<unsigned long long>(nb), phase_t[0],
                                                   phase_t[1], phase_t[2], phase_t[3], phase_t[4], phase_t[5],
-                                                  phase_t[6], 0, 0};
+                                                  phase_t[6], phase_t[7], phase_t[8]};
       unsigned long long v = f[0];
 #pragma unroll
       for (int i = 1; i < kPhaseFields; ++i) v = lane == i ? f[i] : v;

@@ -13,6 +13,8 @@ each recorded launch is the last of a run of back-to-back kvq_decode_attn
 calls (no W_O), as in a decode loop.  Per launch, with
 times relative to the first wave's entry:
   * entry: when the last workgroup started;
+  * query ready: when each wave's workgroup had its query digits;
+  * first block: when each wave's first block of cache data had arrived;
   * loop start: when each wave began its main loop (query rows ready, first
     blocks in flight);
   * loop end: when each workgroup's last wave left its main loop (the
@@ -40,8 +42,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PHASE_WAVES, PHASE_FIELDS, WAVES = 8192, 12, 8
-# record fields: hw id, xcc id, blocks, t entry, t loop, t loop end, t arrived, t merged, t rotated, t stored
-HW, XCC, NB, T0, T1, T2, T3, T4, T5, T6 = range(10)
+# record fields: hw id, xcc id, blocks, t entry, t loop, t loop end, t arrived, t merged, t rotated, t stored,
+# t query digits ready, t first block's data
+HW, XCC, NB, T0, T1, T2, T3, T4, T5, T6, TQ, TB = range(12)
 
 
 def _pct(xs, p):
@@ -74,6 +77,8 @@ def launch_stats(rec, khz):
     return {
         "workgroups": len(wgs),
         "entry_last_us": max(entry),
+        "query_ready_median_us": statistics.median(us(r[TQ] - t0) for r in rec),
+        "first_block_median_us": statistics.median(us(r[TB] - t0) for r in rec),
         "loop_start_median_us": statistics.median(loop0),
         "loop_start_max_us": max(loop0),
         "loop_wave_median_us": statistics.median(loop_wave),
