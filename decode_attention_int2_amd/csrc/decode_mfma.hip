@@ -22,9 +22,10 @@
 //   forms the logit alone: no cross-lane reduction.
 // Values:
 //   w_t = 2^(logit_t + kappa) s_t rounded to an integer < 2^27 is split into
-//   four 7-bit digits (non-negative int8 lanes: no offset to undo); column
-//   x of a row accumulates sum_t digit_x(w_t) c_t exactly in int32 and the
-//   row's value sum is sum_x 128^x column_x.  kappa is a per-row power-of-two
+//   four balanced base-256 digits in [-128, 127] (int8 lanes; two integer
+//   operations per weight); column x of a row accumulates
+//   sum_t digit_x(w_t) c_t exactly in int32 and the row's value sum is
+//   sum_x 256^x column_x.  kappa is a per-row power-of-two
 //   scale chosen from a running bound of logit + log2(s) with 2^2 of
 //   headroom, so the split's largest weight carries at least 2^23 units; if
 //   the bound outgrows it the int32 accumulators are flushed to fp32 in LDS
@@ -68,13 +69,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kM0 = 0x03030303u, kM1 = 0x0C0C0C0Cu, kM2 = 0x30303030u;
 constexpr int kHeadroom = 2;       // log2 headroom of the value scale
-constexpr int kWeightBits = 28;    // value weights are integers < 2^27: four 7-bit digits
+constexpr int kWeightBits = 28;    // value weights are integers < 2^27: four base-256 digits
 
-// The 7-bit digits of w < 2^28, digit x in byte x (each byte < 128, so the
-// int8 MFMA operand needs no offset correction).
-__device__ __forceinline__ uint32_t weight_digits(uint32_t w) {
-  return (w & 0x7Fu) | ((w << 1) & 0x7F00u) | ((w << 2) & 0x7F0000u) | ((w << 3) & 0x7F000000u);
-}
+// The balanced base-256 digits of w < 2^31 - 2^24 as int8 lanes, digit x in
+// byte x: with b_x the bytes of w + 0x80808080 (no carry out of the word),
+// w = sum_x (b_x - 128) 256^x, and b_x - 128 as an int8 is b_x with its top
+// bit flipped.
+__device__ __forceinline__ uint32_t weight_digits(uint32_t w) { return (w + 0x80808080u) ^ 0x80808080u; }
 
 // The 4 code slots of every byte of x as int8 lanes; slot 1 and 2 are scaled by 4 and 16.
 __device__ __forceinline__ v4i slots(uint32_t x) {
@@ -98,14 +99,13 @@ __device__ __forceinline__ float fdpp_ror4(float v) { return __int_as_float(dpp_
 __device__ __forceinline__ float fdpp_ror8(float v) { return __int_as_float(dpp_ror8(__float_as_int(v))); }
 
 // max / sum over the 16 lanes of a DPP row (rotations reach every lane of the row)
-// (max(a, b) = med3(a, b, +inf) for the finite or -inf values reduced here:
-// one instruction, no NaN canonicalization)
-__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
-__device__ __forceinline__ float row16_max(float x) {
-  x = max2(x, fdpp_xor1(x));
-  x = max2(x, fdpp_xor2(x));
-  x = max2(x, fdpp_ror4(x));
-  x = max2(x, fdpp_ror8(x));
+// (integer maximum: the moves fold into v_max_i32's DPP form; a float
+// maximum would canonicalize each moved value first)
+__device__ __forceinline__ int row16_max(int x) {
+  x = max(x, dpp_xor1(x));
+  x = max(x, dpp_xor2(x));
+  x = max(x, dpp_ror4(x));
+  x = max(x, dpp_ror8(x));
   return x;
 }
 __device__ __forceinline__ float row16_sum(float x) {
@@ -429,9 +429,13 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
   for (int q = 0; q < 4; ++q) {
     v4i dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.bk[0], slots(blk.kc[q].x), v4i{0, 0, 0, 0}, 0, 0, 0);
     dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.bk[1], slots(blk.kc[q].y), dk, 0, 0, 0);
-    const int low = (dk[2] << 7) + dk[3];  // |.| < 2^26: no int32 overflow
-    const float dot = fmaf(static_cast<float>(dk[0]), 2097152.0f,
-                           fmaf(static_cast<float>(dk[1]), 16384.0f, static_cast<float>(low)));
+    // digit sums over 128 dims (32 per slot, digits below 2^7, the top one
+    // below 2^5 in magnitude, against codes of at most 3, 12, 48, 3 per
+    // slot): |dk0| < 2^17 and 0 <= dk1..3 < 2^19, so dk0 128 + dk1 is exact
+    // in fp32 (< 2^24) and dk2 128 + dk3 (< 2^26) is rounded once
+    const int high = dk[0] * 128 + dk[1];
+    const int low = dk[2] * 128 + dk[3];
+    const float dot = fmaf(static_cast<float>(high), 16384.0f, static_cast<float>(low));
     const float ks = half_bits_to_float(blk.km[q] & 0xffffu), kz = half_bits_to_float(blk.km[q] >> 16);
     sv[q] = half_bits_to_float(blk.vm[q] & 0xffffu);
     zv[q] = half_bits_to_float(blk.vm[q] >> 16);
@@ -442,10 +446,14 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     (void)frexpf(sv[q], &es);  // s_v < 2^es
     umax = fmaxf(umax, logit[q] + static_cast<float>(es));
   }
-  umax = row16_max(umax);
+  // the row's largest ceil(logit + es) (ceil is monotonic, so this is the
+  // ceiling of the row's largest bound); a lane with every token masked
+  // contributes kNoBound
+  constexpr int kNoBound = -(1 << 30);
+  const int ubound = row16_max(umax == -INFINITY ? kNoBound : static_cast<int>(ceilf(umax)));
   // (selects, no branch; a row whose tokens are all masked keeps its scale)
-  const bool fin = umax != -INFINITY;
-  const int need = fin ? (kWeightBits - 1) - static_cast<int>(ceilf(fin ? umax : 0.0f)) : st.kappa;
+  const bool fin = ubound != kNoBound;
+  const int need = fin ? (kWeightBits - 1) - ubound : st.kappa;
   st.kappa = fin && !st.have_ref ? need - kHeadroom : st.kappa;
   st.have_ref = st.have_ref || fin;
   // wave-uniform decision: flush when any row outgrew its headroom
@@ -468,7 +476,7 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     st.kappa = newk;
     st.flushed = true;
   }
-  // ---- weights W = round(2^(logit + kappa) s_v) < 2^27 as four 7-bit digits
+  // ---- weights W = round(2^(logit + kappa) s_v) < 2^27 as four base-256 digits
   const float kf = static_cast<float>(st.kappa);
   uint32_t w[4];
 #pragma unroll
@@ -927,10 +935,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   float *rw = &red[wave][0][0];  // [4][132], private to this wave
   // value accumulators: lane (4 r + x, g') holds column x (digit x) of
   // query row r for dims 8 (4 g' + i) + 4 hf + e (an exact int32 sum).  The
-  // lane's column times 128^x and the slot scale, summed over the quad (x = 0
+  // lane's column times 256^x and the slot scale, summed over the quad (x = 0
   // keeps the sum).
   const int vr = (lane >> 2) & 3;
-  const float wdig = x == 0 ? 1.0f : x == 1 ? 128.0f : x == 2 ? 16384.0f : 2097152.0f;
+  const float wdig = x == 0 ? 1.0f : x == 1 ? 256.0f : x == 2 ? 65536.0f : 16777216.0f;
   const float wsc[4] = {wdig, wdig * 0.25f, wdig * 0.0625f, wdig};  // times slot_inv(e)
   float t[32];
 #pragma unroll
