@@ -546,7 +546,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   __shared__ int qshift_s[4];              // fixed-point shift S of each row's digits
   __shared__ uint32_t digit_s[8][64];      // key-side A operand: dword [m][e] of each lane
   __shared__ uint32_t s_last;
-  __shared__ uint32_t s_next;               // next unclaimed 64-token block of the split
+  // word 0: the next unclaimed 64-token block of the split; words 1-63: the
+  // other lanes' targets of a claim (each adds 0 to a word of its own)
+  __shared__ uint32_t s_claim[64];
 #ifdef KVQ_PHASE_TIMESTAMPS
   unsigned long long phase_t[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
 #endif
@@ -646,7 +648,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // progress at unequal speed; a static share would leave the slow waves'
   // tail unhidden)
   const int nb = c.t_end > t_begin ? (c.t_end - t_begin + kBlk - 1) / kBlk : 0;
-  if (threadIdx.x == 0) s_next = 3 * kWaves;  // (read after the barriers below)
+  if (threadIdx.x == 0) s_claim[0] = 3 * kWaves;  // (read after the barriers below)
   // blocks jc[k] are in flight in buffer b[k]; ja[k] is a block whose
   // page-table entries were fetched into ad[k]
   int jc0 = wave, jc1 = wave + kWaves, jc2 = wave + 2 * kWaves, ja0 = 0, ja1 = 0, ja2 = 0;
@@ -892,11 +894,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // claimed block into ad[k+1] (whose block was issued two steps earlier).
   // Claims increase, so a block past the split's end ends the loop; loads of
   // such blocks re-read the split's last tile and are not used.
-  // (every lane takes part, lane 0 adding 1 and the others 0: no divergent
-  // branch in the loop, whose exits then stay direct -- a restructured exit
-  // that could reach the loop head from mid-body would make the first step
-  // wait for all three blocks in flight)
-  auto claim = [&]() -> uint32_t { return atomicAdd(&s_next, lane == 0 ? 1u : 0u); };
+  // (every lane takes part, lane 0 adding 1 to the counter and the others 0
+  // to words of their own: no divergent branch in the loop, whose exits then
+  // stay direct -- a restructured exit that could reach the loop head from
+  // mid-body would make the first step wait for all three blocks in flight
+  // -- and no bank conflict: 64 lanes on the counter's one word serialize)
+  auto claim = [&]() -> uint32_t { return atomicAdd(&s_claim[lane], lane == 0 ? 1u : 0u); };
   ja0 = __builtin_amdgcn_readfirstlane(claim());
   load_addr<P16>(c, t_begin + kBlk * min(ja0, nb), a0);
   auto step = [&](Blk &bk, int &jc, Addr &ak, int &ja, Addr &ak1, int &ja1n) {
