@@ -162,7 +162,7 @@ size_t kvq_decode_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq, int
       num_q_heads % num_kv_heads)
     return 0;
   return make_decode_plan(num_seqs, queries_per_seq, num_q_heads, num_kv_heads, max_seq_len, d_model > 0 ? d_model : 0,
-                          num_splits)
+                          num_splits, 0)
       .total;
 }
 
@@ -201,7 +201,7 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
     if (windows->num_seqs < num_seqs) return KVQ_ERR_INVALID_ARGUMENT;
   }
   const DecodePlan pl = make_decode_plan(num_seqs, queries_per_seq, num_q_heads, H, max_seq_len,
-                                         w_o ? d_model : 0, num_splits);
+                                         w_o ? d_model : 0, num_splits, cache->page_size, windows != nullptr);
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return KVQ_ERR_WORKSPACE;
   if (num_seqs == 0) return KVQ_OK;
   uint8_t *ws = static_cast<uint8_t *>(workspace);

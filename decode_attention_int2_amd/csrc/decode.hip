@@ -344,7 +344,7 @@ hipError_t launch_split(const DecodePlan &pl, const SplitArgs &a, hipStream_t st
 }  // namespace
 
 DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, int max_seq_len, int d_model,
-                            int num_splits) {
+                            int num_splits, int page_size, bool windows) {
   DecodePlan pl{};
   pl.num_seqs = num_seqs;
   pl.queries_per_seq = queries_per_seq;
@@ -362,10 +362,12 @@ DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, in
     // runs at half occupancy, and workgroups past one per CU run as a second
     // round.  At most 64 splits (the last split merges up to 64 partials in
     // one pass; past 8 splits each workgroup merges its waves' partials
-    // first); splits of at least 1024 tokens.  A workgroup takes one group of
-    // 4 query rows.
+    // first); splits of at least 1024 tokens.  A workgroup takes one or two
+    // groups of 4 query rows.
     const int n_rg = (queries_per_seq * (Hq / H) + 3) / 4;
-    const int units = num_seqs * H * n_rg > 0 ? num_seqs * H * n_rg : 1;
+    const int per_wg = mfma_row_groups_per_workgroup(n_rg, page_size, windows);
+    const int n_wy = (n_rg + per_wg - 1) / per_wg;
+    const int units = num_seqs * H * n_wy > 0 ? num_seqs * H * n_wy : 1;
     splits = device_cu_count() / units;
     if (splits > 64) splits = 64;
     const int max_by_len = max_chunks / 4 > 0 ? max_chunks / 4 : 1;  // >= 4 chunks of 256 tokens

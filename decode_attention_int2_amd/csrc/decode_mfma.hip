@@ -1,9 +1,10 @@
 // decode_mfma.hip -- decode attention over the packed INT2 cache on the
 // gfx950 matrix cores (v_mfma_i32_16x16x64_i8) in one launch: query
 // rotation, split-K attention, split merge and inverse value rotation.  A
-// workgroup takes one group of 4 query rows of one (sequence, KV head) --
-// up to 64 rows per KV head: GQA group x queries per sequence -- and one
-// split of the sequence's tokens.
+// workgroup takes one or two groups of 4 query rows of one (sequence, KV
+// head) -- up to 64 rows per KV head: GQA group x queries per sequence --
+// and one split of the sequence's tokens; with two groups each block's codes
+// are unpacked once and serve both.
 //
 // [OptR] = "Output-Aware Rotation for INT2 KV-Cache Quantization":
 //   Appendix Eq. (21)-(22), (26): logit = (q R_K) . k_R / sqrt(128) against the
@@ -126,6 +127,7 @@ __device__ __forceinline__ uint32_t quad_byte_transpose(uint32_t a, uint32_t sel
 
 struct MfmaArgs {
   int R, G, Hq, H, Nq, n_rg;  // n_rg: groups of 4 query rows per KV head
+  int n_wy;                   // workgroups per KV head along grid y: n_rg / RG rounded up
   int split_tokens, splits, max_seq_len;
   int P, p_shift;             // page size in tokens (a power of two) and its log2
   int max_pages;
@@ -405,11 +407,11 @@ __device__ __forceinline__ void mask_tail_meta(const Ctx &c, int t0, Blk &blk) {
     if (t0 + 16 * q + c.c >= c.t_end) blk.vm[q] = 0u;
 }
 
+// Per-lane state of one group of 4 query rows.
 struct State {
   v4i bk[2];        // key-side A operand (query digits), dims half m
   float qsum;       // sum of q' of this lane's query row (zero-point term)
   float unscale;    // 2^-S of this lane's query row
-  bool row_ok;
   uint32_t sel1, sel2;  // byte-transpose selectors
   int src_lane4;        // 4 * lane whose bytes this lane takes for the value operand
   int krow_lane4;       // 4 * a lane of the query row of this lane's value accumulators
@@ -421,84 +423,106 @@ struct State {
   int tlim;             // tokens below tlim count for this lane's query row (split end, or the row's causal length)
 };
 
-__device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &blk, State &st, float *facc) {
+constexpr int kFaccFloats = 32 * 64;  // flushed value accumulators of one row group per wave: [slot][lane]
+
+// One 64-token block for RG groups of 4 query rows.  What depends on the
+// block alone -- the key and value code slots, the metadata, the bound of
+// log2 s_v -- is formed once and serves every row group (each extra row
+// group costs its MFMAs and its per-row work only).  facc: this lane's word
+// of the wave's flushed accumulators, row group r at facc + r kFaccFloats.
+template <int RG>
+__device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &blk, State (&st)[RG], float *facc) {
   // ---- keys: lane (c, g) gets the 4 digit sums of query row g and token (q, c)
-  float logit[4], sv[4], zv[4];
-  float umax = -INFINITY;
+  float logit[RG][4], sv[4], zv[4];
+  float umax[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) umax[r] = -INFINITY;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    v4i dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.bk[0], slots(blk.kc[q].x), v4i{0, 0, 0, 0}, 0, 0, 0);
-    dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.bk[1], slots(blk.kc[q].y), dk, 0, 0, 0);
-    // digit sums over 128 dims (32 per slot, digits below 2^7, the top one
-    // below 2^5 in magnitude, against codes of at most 3, 12, 48, 3 per
-    // slot): |dk0| < 2^17 and 0 <= dk1..3 < 2^19, so dk0 128 + dk1 is exact
-    // in fp32 (< 2^24) and dk2 128 + dk3 (< 2^26) is rounded once
-    const int high = dk[0] * 128 + dk[1];
-    const int low = dk[2] * 128 + dk[3];
-    const float dot = fmaf(static_cast<float>(high), 16384.0f, static_cast<float>(low));
+    const v4i kx = slots(blk.kc[q].x), ky = slots(blk.kc[q].y);
     const float ks = half_bits_to_float(blk.km[q] & 0xffffu), kz = half_bits_to_float(blk.km[q] >> 16);
     sv[q] = half_bits_to_float(blk.vm[q] & 0xffffu);
     zv[q] = half_bits_to_float(blk.vm[q] >> 16);
-    // (rows past the group's last hold q' = 0: finite logits, never stored)
-    const bool valid = 16 * q + c.c < st.tlim - t0;
-    logit[q] = valid ? dot * (ks * st.unscale) + kz * st.qsum : -INFINITY;
     int es;
     (void)frexpf(sv[q], &es);  // s_v < 2^es
-    umax = fmaxf(umax, logit[q] + static_cast<float>(es));
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      v4i dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st[r].bk[0], kx, v4i{0, 0, 0, 0}, 0, 0, 0);
+      dk = __builtin_amdgcn_mfma_i32_16x16x64_i8(st[r].bk[1], ky, dk, 0, 0, 0);
+      // digit sums over 128 dims (32 per slot, digits below 2^7, the top one
+      // below 2^5 in magnitude, against codes of at most 3, 12, 48, 3 per
+      // slot): |dk0| < 2^17 and 0 <= dk1..3 < 2^19, so dk0 128 + dk1 is exact
+      // in fp32 (< 2^24) and dk2 128 + dk3 (< 2^26) is rounded once
+      const int high = dk[0] * 128 + dk[1];
+      const int low = dk[2] * 128 + dk[3];
+      const float dot = fmaf(static_cast<float>(high), 16384.0f, static_cast<float>(low));
+      // (rows past the group's last hold q' = 0: finite logits, never stored;
+      // the value is formed first, so that the mask is a select, not a branch)
+      const bool valid = 16 * q + c.c < st[r].tlim - t0;
+      const float lv = dot * (ks * st[r].unscale) + kz * st[r].qsum;
+      logit[r][q] = valid ? lv : -INFINITY;
+      umax[r] = fmaxf(umax[r], logit[r][q] + static_cast<float>(es));
+    }
   }
-  // the row's largest ceil(logit + es) (ceil is monotonic, so this is the
-  // ceiling of the row's largest bound); a lane with every token masked
-  // contributes kNoBound
-  constexpr int kNoBound = -(1 << 30);
-  const int ubound = row16_max(umax == -INFINITY ? kNoBound : static_cast<int>(ceilf(umax)));
-  // (selects, no branch; a row whose tokens are all masked keeps its scale)
-  const bool fin = ubound != kNoBound;
-  const int need = fin ? (kWeightBits - 1) - ubound : st.kappa;
-  st.kappa = fin && !st.have_ref ? need - kHeadroom : st.kappa;
-  st.have_ref = st.have_ref || fin;
-  // wave-uniform decision: flush when any row outgrew its headroom
-  if (__any(st.have_ref && need < st.kappa)) {
-    const int newk = (st.have_ref && need < st.kappa) ? need - kHeadroom : st.kappa;
-    const float f2 = ldexpf(1.0f, newk - st.kappa);  // factor of query row g
-    // the value accumulators of this lane belong to query row (c >> 2)
-    const float f2v = __int_as_float(__builtin_amdgcn_ds_bpermute(st.krow_lane4, __float_as_int(f2)));
+  v4i bv[RG];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+  for (int r = 0; r < RG; ++r) {
+    State &sr = st[r];
+    // the row's largest ceil(logit + es) (ceil is monotonic, so this is the
+    // ceiling of the row's largest bound); a lane with every token masked
+    // contributes kNoBound
+    constexpr int kNoBound = -(1 << 30);
+    const int ubound = row16_max(umax[r] == -INFINITY ? kNoBound : static_cast<int>(ceilf(umax[r])));
+    // (selects, no branch; a row whose tokens are all masked keeps its scale)
+    const bool fin = ubound != kNoBound;
+    const int need = fin ? (kWeightBits - 1) - ubound : sr.kappa;
+    sr.kappa = fin && !sr.have_ref ? need - kHeadroom : sr.kappa;
+    sr.have_ref = sr.have_ref || fin;
+    // wave-uniform decision: flush when any row outgrew its headroom
+    if (__any(sr.have_ref && need < sr.kappa)) {
+      const int newk = (sr.have_ref && need < sr.kappa) ? need - kHeadroom : sr.kappa;
+      const float f2 = ldexpf(1.0f, newk - sr.kappa);  // factor of query row g
+      // the value accumulators of this lane belong to query row (c >> 2)
+      const float f2v = __int_as_float(__builtin_amdgcn_ds_bpermute(sr.krow_lane4, __float_as_int(f2)));
+      float *fr = facc + r * kFaccFloats;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float *p = facc + (4 * i + r) * 64;
-        *p = ((st.flushed ? *p : 0.0f) + static_cast<float>(st.accv[i][r])) * f2v;
-      }
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.accv[i] = v4i{0, 0, 0, 0};
-    st.lsum *= f2;
-    st.zsum *= f2;
-    st.kappa = newk;
-    st.flushed = true;
+        for (int k = 0; k < 4; ++k) {
+          float *pk = fr + (4 * i + k) * 64;
+          *pk = ((sr.flushed ? *pk : 0.0f) + static_cast<float>(sr.accv[i][k])) * f2v;
+        }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sr.accv[i] = v4i{0, 0, 0, 0};
+      sr.lsum *= f2;
+      sr.zsum *= f2;
+      sr.kappa = newk;
+      sr.flushed = true;
+    }
+    // ---- weights W = round(2^(logit + kappa) s_v) < 2^27 as four base-256 digits
+    const float kf = static_cast<float>(sr.kappa);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // (hardware exp2: results below 2^-126 weigh nothing against the
+      // split's largest weight, >= 2^23, and masked tokens give exp2(-inf) = 0)
+      const float pq = __builtin_amdgcn_exp2f(logit[r][q] + kf);
+      sr.lsum += pq;
+      sr.zsum += pq * zv[q];
+      const uint32_t W = static_cast<uint32_t>(fmaf(pq, sv[q], 0.5f));
+      w[q] = weight_digits(W);
+    }
+    // quad lane x takes digit x (byte x) of its quad's 4 tokens;
+    // then the lanes move to the B layout: column 4 r + x, k-slice = token group
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q] = quad_byte_transpose(w[q], sr.sel1, sr.sel2);
+      w[q] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sr.src_lane4, static_cast<int>(w[q])));
+    }
+    bv[r] = v4i{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
   }
-  // ---- weights W = round(2^(logit + kappa) s_v) < 2^27 as four base-256 digits
-  const float kf = static_cast<float>(st.kappa);
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // (hardware exp2: results below 2^-126 weigh nothing against the
-    // split's largest weight, >= 2^23, and masked tokens give exp2(-inf) = 0)
-    const float p = __builtin_amdgcn_exp2f(logit[q] + kf);
-    st.lsum += p;
-    st.zsum += p * zv[q];
-    const uint32_t W = static_cast<uint32_t>(fmaf(p, sv[q], 0.5f));
-    w[q] = weight_digits(W);
-  }
-  // quad lane x takes digit x (byte x) of its quad's 4 tokens;
-  // then the lanes move to the B layout: column 4 r + x, k-slice = token group
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    w[q] = quad_byte_transpose(w[q], st.sel1, st.sel2);
-    w[q] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(st.src_lane4, static_cast<int>(w[q])));
-  }
-  const v4i bv{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
 
-  // ---- values: 8 MFMAs (16 dims each), k = the 64 tokens of the block
+  // ---- values: 8 MFMAs (16 dims each) per row group, k = the 64 tokens of the block
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -506,7 +530,9 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
       const uint32_t x0 = hf ? blk.vx[0].y : blk.vx[0].x, x1 = hf ? blk.vx[1].y : blk.vx[1].x;
       const uint32_t x2 = hf ? blk.vx[2].y : blk.vx[2].x, x3 = hf ? blk.vx[3].y : blk.vx[3].x;
       const v4i av{slot(x0, e), slot(x1, e), slot(x2, e), slot(x3, e)};
-      st.accv[4 * hf + e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, st.accv[4 * hf + e], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+        st[r].accv[4 * hf + e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv[r], st[r].accv[4 * hf + e], 0, 0, 0);
     }
 }
 
@@ -537,14 +563,27 @@ __device__ __forceinline__ void load_window_batch(const MfmaArgs &a, int b, int 
     }
 }
 
-template <int DT, bool P16, bool kDense, bool kWin, bool NT>
+// RG: groups of 4 query rows per workgroup (1, or 2 without BF16 windows):
+// every wave computes each of its blocks for the RG groups.
+template <int DT, bool P16, bool kDense, bool kWin, bool NT, int RG>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[kWaves][5][4 + D];  // per wave, per row: m, l, z, flag, acc[128]; row 4: unused stores
-  __shared__ __attribute__((aligned(16))) float facc_all[kWaves][32 * 64];  // flushed value accumulators, [slot][lane]
-  __shared__ __attribute__((aligned(16))) float qs[4][D];               // q' of the group's rows
-  __shared__ float qsum_s[4];
-  __shared__ int qshift_s[4];              // fixed-point shift S of each row's digits
-  __shared__ uint32_t digit_s[8][64];      // key-side A operand: dword [m][e] of each lane
+  static_assert(RG == 1 || (RG == 2 && !kWin), "two row groups per workgroup only without windows");
+  constexpr int kRows = 4 * RG;  // query rows of the workgroup
+  // per wave, per row: m, l, z, flag, acc[128]; row kRows: unused stores.
+  // With one row group these rows have their own array (the window code
+  // uses them while facc_all holds its values); with two, each wave's rows
+  // lie in its own flushed accumulators, free once the main loop is done
+  // (LDS: the accumulators of two row groups are 128 KB)
+  __shared__ __attribute__((aligned(16))) float red_own[RG == 1 ? kWaves : 1][RG == 1 ? 5 : 1][4 + D];
+  __shared__ __attribute__((aligned(16))) float facc_all[kWaves][RG * kFaccFloats];  // flushed value accumulators, [row group][slot][lane]
+  __shared__ __attribute__((aligned(16))) float qs[kRows][D];            // q' of the workgroup's rows
+  __shared__ float qsum_s[kRows];
+  __shared__ int qshift_s[kRows];          // fixed-point shift S of each row's digits
+  __shared__ uint32_t digit_s[RG][8][64];  // key-side A operand: dword [m][e] of each lane, per row group
+  auto red = [&](int w, int r) -> float * {
+    if constexpr (RG == 1) return &red_own[w][r][0];
+    else return &facc_all[w][r * (D + 4)];
+  };
   __shared__ uint32_t s_last;
   // word 0: the next unclaimed 64-token block of the split; words 1-63: the
   // other lanes' targets of a claim (each adds 0 to a word of its own)
@@ -554,8 +593,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
 #endif
   KVQ_PHASE(0);
   const int s = blockIdx.x, b = blockIdx.z;
-  const int h = blockIdx.y / a.n_rg, rg = blockIdx.y % a.n_rg;  // KV head, group of 4 query rows
-  const int row0 = 4 * rg, nrows = min(4, a.R - row0);
+  // KV head, first group of 4 query rows (of RG)
+  const int h = blockIdx.y / a.n_wy, rg = (blockIdx.y % a.n_wy) * RG;
+  const int row0 = 4 * rg, nrows = min(kRows, a.R - row0);
   const size_t unit = (static_cast<size_t>(b) * a.H + h) * a.n_rg + rg;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -681,20 +721,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
         rotate_query_signed(y0, y1, a.rk.kind, static_cast<float>(sb0), static_cast<float>(sb1), lane);
     }
     if constexpr (kDense) {
-      // q' = q R_K of the group's 4 rows (rows past the last are zero): the
-      // raw rows go to qs; thread (kq, j) sums its quarter of column j for
-      // the 4 rows (fp32, in row order; the rows' values are read by all
+      // q' = q R_K of the workgroup's rows (rows past the last are zero):
+      // the raw rows go to qs; thread (kq, j) sums its quarter of column j
+      // for the rows (fp32, in row order; the rows' values are read by all
       // lanes of a wave at once), the quarters meet in facc_all (unused until
       // the first flush) and are added in quarter order
-      if (wave < 4) {
+      if (wave < kRows) {
         qs[wave][lane] = y0;
         qs[wave][lane + 64] = y1;
       }
       __syncthreads();
       const int kq = threadIdx.x >> 7, jc = threadIdx.x & 127;
-      float pr[4];
+      float pr[kRows];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kRows; ++r) {
         const float4 *x4 = reinterpret_cast<const float4 *>(&qs[r][32 * kq]);
         const float4 rq[8] = {rs0, rs1, rs2, rs3, rs4, rs5, rs6, rs7};
         float acc = 0.0f;
@@ -708,20 +748,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
         }
         pr[r] = acc;
       }
-      float *qpart = &facc_all[0][0];  // [quarter][row][column]
+      float *qpart = &facc_all[0][0];  // [quarter][row][column]: 4 kRows D floats, within facc_all[0]
+      static_assert(4 * kRows * D <= RG * kFaccFloats, "quarter sums fit in wave 0's accumulators");
 #pragma unroll
-      for (int r = 0; r < 4; ++r) qpart[(kq * 4 + r) * D + jc] = pr[r];
+      for (int r = 0; r < kRows; ++r) qpart[(kq * kRows + r) * D + jc] = pr[r];
       __syncthreads();
-      if (wave < 4) {
+      if (wave < kRows) {
         auto col = [&](int j) {
-          return ((qpart[(0 * 4 + wave) * D + j] + qpart[(1 * 4 + wave) * D + j]) + qpart[(2 * 4 + wave) * D + j]) +
-                 qpart[(3 * 4 + wave) * D + j];
+          return ((qpart[(0 * kRows + wave) * D + j] + qpart[(1 * kRows + wave) * D + j]) +
+                  qpart[(2 * kRows + wave) * D + j]) +
+                 qpart[(3 * kRows + wave) * D + j];
         };
         y0 = col(lane) * (kLog2eF * kInvSqrtD);
         y1 = col(lane + 64) * (kLog2eF * kInvSqrtD);
       }
     }
-    if (wave < 4) {
+    if (wave < kRows) {
       const float sum = wave_sum(y0 + y1);
       const float qabs = wave_maxf(fmaxf(fabsf(y0), fabsf(y1)));
       int e2 = 0;
@@ -735,19 +777,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     }
   }
   __syncthreads();
-  // key-side A operand (row c = 4 r + d, k-slice g), one dword per wave,
-  // and this lane's query row g
-  for (int d = wave; d < 8; d += kWaves) digit_s[d][lane] = query_digit_word(qs, qshift_s, lane, d >> 2, d & 3);
+  // key-side A operand of each row group (row c = 4 r + d, k-slice g), one
+  // dword per wave and row group, and this lane's query row g
+  for (int d = wave; d < 8 * RG; d += kWaves)
+    digit_s[d >> 3][d & 7][lane] = query_digit_word(&qs[4 * (d >> 3)], &qshift_s[4 * (d >> 3)], lane, (d & 7) >> 2, d & 3);
   __syncthreads();
   KVQ_PHASE(7);  // query digits ready
-  State st;
-  const int hr = c.g;  // query row (within the group) of the key-side lanes
+  State st[RG];
+  const int hr = c.g;  // query row (within each group) of the key-side lanes
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int r = 0; r < RG; ++r) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st.bk[m][e] = static_cast<int>(digit_s[4 * m + e][lane]);
-  st.unscale = ldexpf(1.0f, -qshift_s[hr]);
-  st.qsum = qsum_s[hr];
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[r].bk[m][e] = static_cast<int>(digit_s[r][4 * m + e][lane]);
+    st[r].unscale = ldexpf(1.0f, -qshift_s[4 * r + hr]);
+    st[r].qsum = qsum_s[4 * r + hr];
+  }
   load_block<P16, NT>(c, a2, b2, bad);
   if (wave == 0) cnt_word = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (kWin) {
@@ -760,9 +806,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     // pass per row; each thread then sums 4 dims of one row over a quarter of
     // the tokens.  Raw query rows (scaled to base-2 logits) and q . mu into
     // LDS (qs is free: the digits are built).
-    float *qmu_s = &red[0][4][0];   // [4]
-    float *xw = &red[1][0][0];      // [4][192]: logits, then weights (spans red[1], red[2])
-    float *alw = &red[3][0][0];     // [4]: rescale factor of a batch per row
+    float *qmu_s = red(0, 4);       // [4]
+    float *xw = red(1, 0);          // [4][192]: logits, then weights (spans red[1], red[2])
+    float *alw = red(3, 0);         // [4]: rescale factor of a batch per row
     uint16_t *vb16 = reinterpret_cast<uint16_t *>(&facc_all[0][0]);  // [192][128] bf16 values (free until the first flush)
     constexpr int kWT = 64 * kWinBatch;
     if (wave < 4) {
@@ -870,21 +916,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     if (wave < nrows && lane < 4) store_partial(win_slot(wave) + lane, lane == 0 ? m_run : lane == 1 ? l_run : 0.0f);
     __syncthreads();  // (wsum read before the main loop's flushes write facc_all)
   }
-  st.row_ok = hr < nrows;
-  st.tlim = c.t_end;
-  if (a.causal) st.tlim = min(c.t_end, L - (a.Nq - 1 - (row0 + hr) / a.G));
   const int x = lane & 3;
-  st.sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
-  st.sel2 = (x & 2) ? 0x03020706u : 0x05040100u;
-  // value operand lane 16 g' + 4 r + x takes from lane 16 r + 4 g' + x
-  st.src_lane4 = 4 * (16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + x);
-  st.krow_lane4 = 4 * (16 * ((lane >> 2) & 3));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.accv[i] = v4i{0, 0, 0, 0};
-  st.lsum = st.zsum = 0.0f;
-  st.kappa = 0;
-  st.have_ref = false;
-  st.flushed = false;
+  for (int r = 0; r < RG; ++r) {
+    st[r].tlim = c.t_end;
+    if (a.causal) st[r].tlim = min(c.t_end, L - (a.Nq - 1 - (row0 + 4 * r + hr) / a.G));
+    st[r].sel1 = (x & 1) ? 0x03070105u : 0x06020400u;
+    st[r].sel2 = (x & 2) ? 0x03020706u : 0x05040100u;
+    // value operand lane 16 g' + 4 r + x takes from lane 16 r + 4 g' + x
+    st[r].src_lane4 = 4 * (16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + x);
+    st[r].krow_lane4 = 4 * (16 * ((lane >> 2) & 3));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st[r].accv[i] = v4i{0, 0, 0, 0};
+    st[r].lsum = st[r].zsum = 0.0f;
+    st[r].kappa = 0;
+    st[r].have_ref = false;
+    st[r].flushed = false;
+  }
 
   // ---- main loop.  At the top of a step that computes block jc[k] (buffer
   // b[k]): the wave's next two blocks are in flight in the other buffers,
@@ -905,7 +953,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   auto step = [&](Blk &bk, int &jc, Addr &ak, int &ja, Addr &ak1, int &ja1n) {
     const uint32_t v = claim();
     if (jc == nb - 1) mask_tail_meta(c, t_begin + kBlk * jc, bk);  // (wave-uniform: one block per split)
-    compute_block(c, t_begin + kBlk * jc, bk, st, facc);
+    compute_block<RG>(c, t_begin + kBlk * jc, bk, st, facc);
     load_block<P16, NT>(c, ak, bk, bad);
     jc = ja;
     ja1n = __builtin_amdgcn_readfirstlane(v);
@@ -931,11 +979,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
 
   KVQ_PHASE(2);
   // ---- this wave's partial of each row: m = -kappa, l, z, flag, acc[128]
-  // (rows past the group's last are computed and never stored)
-  const float lrow = row16_sum(st.lsum);
-  const float zrow = row16_sum(st.zsum);
+  // (rows past the workgroup's last are computed and never stored)
   const bool any_bad = __any(bad);
-  float *rw = &red[wave][0][0];  // [4][132], private to this wave
+  float *rw = red(wave, 0);  // [kRows + 1][132], private to this wave
   // value accumulators: lane (4 r + x, g') holds column x (digit x) of
   // query row r for dims 8 (4 g' + i) + 4 hf + e (an exact int32 sum).  The
   // lane's column times 256^x and the slot scale, summed over the quad (x = 0
@@ -943,37 +989,47 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   const int vr = (lane >> 2) & 3;
   const float wdig = x == 0 ? 1.0f : x == 1 ? 256.0f : x == 2 ? 65536.0f : 16777216.0f;
   const float wsc[4] = {wdig, wdig * 0.25f, wdig * 0.0625f, wdig};  // times slot_inv(e)
-  float t[32];
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
+  for (int g = 0; g < RG; ++g) {
+    // (with two row groups, rw lies in this wave's flushed accumulators of
+    // group 0: group g's are read before its rows are written, and rows
+    // 0..kRows end before group 1's accumulators begin)
+    static_assert(RG == 1 || (kRows + 1) * (D + 4) <= kFaccFloats, "partial rows within group 0's accumulators");
+    const float lrow = row16_sum(st[g].lsum);
+    const float zrow = row16_sum(st[g].zsum);
+    float t[32];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t[4 * k + i] = static_cast<float>(st.accv[k][i]);
-  if (st.flushed) {
+    for (int k = 0; k < 8; ++k)
 #pragma unroll
-    for (int j = 0; j < 32; ++j) t[j] += facc[j * 64];
-  }
-  {
+      for (int i = 0; i < 4; ++i) t[4 * k + i] = static_cast<float>(st[g].accv[k][i]);
+    if (st[g].flushed) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) t[j] += facc[g * kFaccFloats + j * 64];
+    }
+    {
 #pragma clang fp contract(off)
-    // lanes x != 0 store their (unused) quad sums to row 4
-    const int lbase = x == 0 ? vr * (D + 4) + 4 + 32 * c.g : 4 * (D + 4) + lane;
+      // lanes x != 0 store their (unused) quad sums to row kRows
+      const int lbase = x == 0 ? (4 * g + vr) * (D + 4) + 4 + 32 * c.g : kRows * (D + 4) + lane;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = t[4 * (4 * hf + e) + i] * wsc[e];
-          v = v + fdpp_xor1(v);
-          v = v + fdpp_xor2(v);
-          rw[lbase + 8 * i + 4 * hf + e] = v;
-        }
-  }
-  if (c.c == 0) {
-    const bool empty = !st.have_ref;  // no token of this wave counted for row hr
-    rw[hr * (D + 4) + 0] = empty ? -INFINITY : -static_cast<float>(st.kappa);
-    rw[hr * (D + 4) + 1] = any_bad ? __builtin_nanf("") : (empty ? 0.0f : lrow);
-    rw[hr * (D + 4) + 2] = empty ? 0.0f : zrow;
-    rw[hr * (D + 4) + 3] = 0.0f;
+          for (int i = 0; i < 4; ++i) {
+            float v = t[4 * (4 * hf + e) + i] * wsc[e];
+            v = v + fdpp_xor1(v);
+            v = v + fdpp_xor2(v);
+            rw[lbase + 8 * i + 4 * hf + e] = v;
+          }
+    }
+    if (c.c == 0) {
+      const bool empty = !st[g].have_ref;  // no token of this wave counted for row hr of group g
+      float *rr = rw + (4 * g + hr) * (D + 4);
+      rr[0] = empty ? -INFINITY : -static_cast<float>(st[g].kappa);
+      rr[1] = any_bad ? __builtin_nanf("") : (empty ? 0.0f : lrow);
+      rr[2] = empty ? 0.0f : zrow;
+      rr[3] = 0.0f;
+    }
   }
   // (an empty wave's accumulators are zero; the lanes of this wave read
   // each other's LDS writes below: LDS operations of a wave complete in
@@ -990,21 +1046,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       float mw[kWaves], mstar = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        mw[w] = red[w][r][0];
+        mw[w] = red(w, r)[0];
         mstar = fmaxf(mstar, mw[w]);
       }
       float l = 0.0f, z = 0.0f, a0 = 0.0f, a1 = 0.0f;
       bool nan = false;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float lw = red[w][r][1];
+        const float *rwr = red(w, r);
+        const float lw = rwr[1];
         nan = nan || lw != lw;
         const float al = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mstar);
         if (al != 0.0f) {
           l += al * lw;
-          z += al * red[w][r][2];
-          a0 += al * red[w][r][4 + lane];
-          a1 += al * red[w][r][4 + 64 + lane];
+          z += al * rwr[2];
+          a0 += al * rwr[4 + lane];
+          a1 += al * rwr[4 + 64 + lane];
         }
       }
       const int rr = row0 + r;
@@ -1020,17 +1077,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     // device-scope stores, consecutive lanes on consecutive floats
     {
       const int slot_w = s * kWaves + wave;
-      float *rb[4];  // partial base of each row of the group
+      float *rb[kRows];  // partial base of each row of the workgroup
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kRows; ++r) {
         const int rr = min(row0 + r, a.R - 1);
         const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
         rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + slot_w) * (D + 4);
       }
-      constexpr int kN = (4 * (D + 4) + 63) / 64;
+      constexpr int kN = (kRows * (D + 4) + 63) / 64;
       float vals[kN];
 #pragma unroll
-      for (int k = 0; k < kN; ++k) vals[k] = rw[min(lane + 64 * k, 4 * (D + 4) - 1)];  // all reads, then the stores
+      for (int k = 0; k < kN; ++k) vals[k] = rw[min(lane + 64 * k, kRows * (D + 4) - 1)];  // all reads, then the stores
 #pragma unroll
       for (int k = 0; k < kN; ++k) {
         const int idx = lane + 64 * k;
@@ -1110,18 +1167,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   if (vdense) {
     // out[r][i] = sum_c o'[r][c] R_V[i][c]: the rows' o' to LDS (rows past
     // the last are zero); thread t sums its 32 columns of row i = t / 4 for
-    // the 4 rows (fp32, in column order; 4 addresses per instruction), and
+    // each row (fp32, in column order; 4 addresses per instruction), and
     // the 4 threads of row i add their sums (lanes t ^ 1, then t ^ 2)
-    if (wave < 4) {
-      red[wave][0][lane] = o0;
-      red[wave][0][lane + 64] = o1;
+    if (wave < kRows) {
+      red(wave, 0)[lane] = o0;
+      red(wave, 0)[lane + 64] = o1;
     }
     __syncthreads();
     const int ri = threadIdx.x >> 2, c0 = 32 * (threadIdx.x & 3);
     const float4 rv4[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4 *x4 = reinterpret_cast<const float4 *>(&red[r][0][c0]);
+    for (int r = 0; r < kRows; ++r) {
+      const float4 *x4 = reinterpret_cast<const float4 *>(red(r, 0) + c0);
       float acc = 0.0f;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -1133,11 +1190,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       }
       acc += fdpp_xor1(acc);
       acc += fdpp_xor2(acc);
-      if ((threadIdx.x & 3) == 0) red[r][1][ri] = acc;
+      if ((threadIdx.x & 3) == 0) red(r, 1)[ri] = acc;
     }
     __syncthreads();
-    o0 = red[wave < 4 ? wave : 0][1][lane];
-    o1 = red[wave < 4 ? wave : 0][1][lane + 64];
+    o0 = red(wave < kRows ? wave : 0, 1)[lane];
+    o1 = red(wave < kRows ? wave : 0, 1)[lane + 64];
   } else if (wave < nrows) {
     unrotate_value_wave(o0, o1, a.rv, h, lane);
   }
@@ -1197,6 +1254,10 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
   a.H = pl.H;
   a.Nq = pl.queries_per_seq;
   a.n_rg = (pl.rows_per_head + 3) / 4;
+  // two row groups per workgroup when there are two or more (the blocks'
+  // codes are unpacked once for both), one with BF16 windows
+  const int rg_per_wg = mfma_row_groups_per_workgroup(a.n_rg, page_size, win != nullptr);
+  a.n_wy = (a.n_rg + rg_per_wg - 1) / rg_per_wg;
   a.split_tokens = pl.split_tokens;
   a.splits = pl.splits;
   a.premerge = pl.splits > kMaxSplitsNoPremerge ? 1 : 0;
@@ -1241,35 +1302,45 @@ hipError_t launch_decode_mfma(const DecodePlan &pl, const void *q, int dtype, Ro
     a.win_W = win->num_recent;
     a.win_mu = win->key_mean;
   }
-  const dim3 grid(pl.splits, pl.H * a.n_rg, pl.num_seqs);
+  const dim3 grid(pl.splits, pl.H * a.n_wy, pl.num_seqs);
   const bool f32 = dtype == KVQ_F32 || rk.kind == kRotPrescaled;
   const bool dense = rk.kind == KVQ_ROT_DENSE;
   const dim3 block(64 * kWaves);
-  // (one row group per KV head: the cache bytes are read once, streamed)
-  const bool nt = a.n_rg == 1;
-#define KVQ_DECODE_LAUNCH(F32, P16, DENSE, WIN, NT)                                                              \
-  hipLaunchKernelGGL((decode_mfma_kernel<(F32) ? KVQ_F32 : KVQ_BF16, P16, DENSE, WIN, NT>), grid, block, 0, stream, \
-                     a)
-#define KVQ_DECODE_LAUNCH_W(F32, P16, DENSE)                   \
-  do {                                                         \
-    if (win) KVQ_DECODE_LAUNCH(F32, P16, DENSE, true, true);   \
-    else if (nt) KVQ_DECODE_LAUNCH(F32, P16, DENSE, false, true); \
-    else KVQ_DECODE_LAUNCH(F32, P16, DENSE, false, false);     \
+  // (one workgroup per KV head along y: the cache bytes are read once, streamed)
+  const bool nt = a.n_wy == 1;
+#define KVQ_DECODE_LAUNCH(F32, P16, DENSE, WIN, NT, RG)                                                          \
+  hipLaunchKernelGGL((decode_mfma_kernel<(F32) ? KVQ_F32 : KVQ_BF16, P16, DENSE, WIN, NT, RG>), grid, block, 0, \
+                     stream, a)
+  // 16-token pages: one row group (n_rg == 1: streamed) or two per workgroup
+#define KVQ_DECODE_LAUNCH_16(F32, DENSE)                                        \
+  do {                                                                          \
+    if (win) KVQ_DECODE_LAUNCH(F32, true, DENSE, true, true, 1);                \
+    else if (rg_per_wg == 1) KVQ_DECODE_LAUNCH(F32, true, DENSE, false, true, 1); \
+    else if (nt) KVQ_DECODE_LAUNCH(F32, true, DENSE, false, true, 2);           \
+    else KVQ_DECODE_LAUNCH(F32, true, DENSE, false, false, 2);                  \
+  } while (0)
+  // longer pages: one row group per workgroup
+#define KVQ_DECODE_LAUNCH_P(F32, DENSE)                             \
+  do {                                                              \
+    if (win) KVQ_DECODE_LAUNCH(F32, false, DENSE, true, true, 1);   \
+    else if (nt) KVQ_DECODE_LAUNCH(F32, false, DENSE, false, true, 1); \
+    else KVQ_DECODE_LAUNCH(F32, false, DENSE, false, false, 1);     \
   } while (0)
   if (page_size == 16) {
     if (dense) {
-      if (f32) KVQ_DECODE_LAUNCH_W(true, true, true); else KVQ_DECODE_LAUNCH_W(false, true, true);
+      if (f32) KVQ_DECODE_LAUNCH_16(true, true); else KVQ_DECODE_LAUNCH_16(false, true);
     } else {
-      if (f32) KVQ_DECODE_LAUNCH_W(true, true, false); else KVQ_DECODE_LAUNCH_W(false, true, false);
+      if (f32) KVQ_DECODE_LAUNCH_16(true, false); else KVQ_DECODE_LAUNCH_16(false, false);
     }
   } else {
     if (dense) {
-      if (f32) KVQ_DECODE_LAUNCH_W(true, false, true); else KVQ_DECODE_LAUNCH_W(false, false, true);
+      if (f32) KVQ_DECODE_LAUNCH_P(true, true); else KVQ_DECODE_LAUNCH_P(false, true);
     } else {
-      if (f32) KVQ_DECODE_LAUNCH_W(true, false, false); else KVQ_DECODE_LAUNCH_W(false, false, false);
+      if (f32) KVQ_DECODE_LAUNCH_P(true, false); else KVQ_DECODE_LAUNCH_P(false, false);
     }
   }
-#undef KVQ_DECODE_LAUNCH_W
+#undef KVQ_DECODE_LAUNCH_P
+#undef KVQ_DECODE_LAUNCH_16
 #undef KVQ_DECODE_LAUNCH
   return hipGetLastError();
 }

@@ -13,8 +13,9 @@ constexpr int D = 128;         // head dimension == quantization group size
 constexpr int kMaxRows = 64;   // query rows sharing one (sequence, KV head)
 constexpr int kChunk = 256;    // tokens per inner iteration of a decode split
 // tokens per split: a value-accumulator column of the matrix-core decode
-// gains at most 127 (digit) x 48 (code in the 16x slot) per token, so one
-// wave taking a whole split keeps its int32 sums below 2^18 * 6096 < 2^31
+// gains at most 128 (digit magnitude) x 48 (code in the 16x slot) per token,
+// so one wave taking a whole split keeps its int32 sums below
+// 2^18 * 6144 < 2^31
 constexpr int kMaxMfmaSplitTokens = 1 << 18;
 constexpr int kMaxSplits = 4096;            // split partials merged per (row, head)
 constexpr int kMfmaWaves = 8;               // waves per workgroup of the matrix-core decode kernel
@@ -23,6 +24,17 @@ constexpr int kMaxSplitsNoPremerge = 1;     // more splits: the waves' partials 
                                              // 4 x 131K 78.1 -> 75.3 us against merging the 8 waves' partials of
                                              // up to 8 splits at the end)
 constexpr int64_t kMaxSeqLen = static_cast<int64_t>(1) << 26;  // max_seq_len accepted by the decode entry point
+
+// Groups of 4 query rows that one workgroup of the matrix-core decode takes
+// (of n_rg per (sequence, KV head)): two when there are two or more, the
+// pages hold 16 tokens and there are no BF16 windows, so that each block's
+// codes are unpacked once for both groups and read by half as many
+// workgroups (with longer pages the kernel's per-tile page offsets leave
+// too few registers for two groups).  page_size 0: not known yet (a
+// workspace size), which takes the choice with more splits.
+inline int mfma_row_groups_per_workgroup(int n_rg, int page_size, bool windows) {
+  return (!windows && n_rg >= 2 && page_size <= 16) ? 2 : 1;
+}
 
 // Rotation descriptor passed by value to kernels.
 struct RotDev {
@@ -315,8 +327,11 @@ struct DecodePlan {
   size_t off_cnt;                                          // split arrival counters (matrix-core kernel)
   size_t total;
 };
+// page_size, windows: of the decode the plan is for (they decide the row
+// groups per workgroup of the matrix-core kernel, and so the default split
+// count); page_size 0 sizes a workspace for any page size.
 DecodePlan make_decode_plan(int num_seqs, int queries_per_seq, int Hq, int H, int max_seq_len, int d_model,
-                            int num_splits);
+                            int num_splits, int page_size = 16, bool windows = false);
 
 // Rotated, pre-scaled queries and their sums (prologue of the decode step).
 hipError_t launch_query_rotation(const void *q, int dtype, const DecodePlan &pl, RotDev rk, float *qrot,

@@ -139,6 +139,41 @@ def test_decode_parity(dev, case):
     assert max(per) <= tol
 
 
+@pytest.mark.parametrize("case", ["gqa8_pair", "odd_groups", "partial_rows", "pair_one_split", "pages64"])
+def test_decode_two_row_groups_per_workgroup(dev, case):
+    """Decodes with two or more groups of 4 query rows per (sequence, KV
+    head).  With 16-token pages one workgroup takes two groups (each block's
+    codes unpacked once for both): a full pair (GQA group of 8, one query),
+    an odd number of groups (the last workgroup's second group is empty), a
+    pair whose second group holds 2 rows, one split (8 rows stored per wave,
+    no premerge), and 64-token pages (one group per workgroup).  The oracle
+    decodes the GPU's own cache bytes; every (row, head) within 1e-4."""
+    splits, seq_lens = 0, None
+    if case == "gqa8_pair":
+        w = synthetic.make("paged16x32k", dev, tokens=1500, num_seqs=3, H=2, Hq=16, d_model=64)
+        seq_lens = synthetic.ragged_seq_lens(3, 1500, seed=21).to(dev)
+    elif case == "odd_groups":
+        w = synthetic.make("gqa32k", dev, tokens=1300, H=2, Hq=8, d_model=64, queries=3)
+    elif case == "partial_rows":
+        w = synthetic.make("long131k", dev, tokens=900, num_seqs=2, H=2, Hq=6, d_model=96, queries=2)
+        seq_lens = synthetic.ragged_seq_lens(2, 900, seed=22).to(dev)
+    elif case == "pair_one_split":
+        w = synthetic.make("paged16x32k", dev, tokens=1200, num_seqs=2, H=2, Hq=16, d_model=64)
+        splits = 1
+    else:
+        w = synthetic.make("paged16x32k", dev, tokens=1500, num_seqs=2, H=2, Hq=16, d_model=64, page_size=64)
+    if seq_lens is not None:
+        w.seq_lens = seq_lens
+    print(f"{case}: rows per KV head {w.queries_per_seq * w.Hq // w.H}, page size {w.page_size}", flush=True)
+    cache = gpu_quantize(w, dev)
+    out_o, _ = gpu_decode(w, cache, dev, with_wo=False, num_splits=splits)
+    (ref_o, _), rows = oracle_decode_on_cache(w, cache.pages.cpu().numpy(), range(w.num_seqs), with_wo=False)
+    o = f32np(out_o)[rows]
+    per = [rel_l2(o[r, j], ref_o[r, j]) for r in range(ref_o.shape[0]) for j in range(ref_o.shape[1])]
+    print(f"{case}: max rel-L2 per (row, head) {max(per):.2e}", flush=True)
+    assert max(per) <= 1e-4
+
+
 def test_decode_split_count_invariance(dev):
     """The split-K log-sum-exp merge equals a single pass (one split).
 
