@@ -77,6 +77,25 @@ __device__ __forceinline__ float rot_entry(const RotDev &r, int h, int i, int j,
 }
 
 // One wave holds a 128-vector as x0 = x[lane], x1 = x[lane + 64].
+// The value of lane (this lane ^ d) of a wave, d a power of two below 64,
+// without the LDS: DPP moves within rows of 16 lanes (d = 4: a half-row
+// mirror, lane i <- 7 - i, then lanes ^3 within quads, i.e. i <- i ^ 4) and
+// VALU row swaps across rows (d = 16, 32: the swap returns this lane's own
+// value and its partner's; the one that is not its own bits is the partner's,
+// and when both are, they are the same value).  (Every source lane of these
+// DPP patterns exists, so bound_ctrl changes nothing.)
+__device__ __forceinline__ int lane_xor(int x, int d) {
+  if (d == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);
+  if (d == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);
+  if (d == 4) return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true), 0x1B, 0xF, 0xF, true);
+  if (d == 8) return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);
+  const unsigned u = static_cast<unsigned>(x);
+  const auto r = d == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return static_cast<int>(r[0] == u ? r[1] : r[0]);
+}
+__device__ __forceinline__ float lane_xor(float x, int d) { return __int_as_float(lane_xor(__float_as_int(x), d)); }
+
 // In-place fast Walsh-Hadamard transform: x <- x H, H[i][j] = (-1)^popcount(i & j)
 // (Sylvester order, unnormalized): one butterfly stage per index bit.
 __device__ __forceinline__ void fwht128(float &x0, float &x1, int lane) {
@@ -85,19 +104,22 @@ __device__ __forceinline__ void fwht128(float &x0, float &x1, int lane) {
   x1 = b;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
-    const float p0 = __shfl_xor(x0, d), p1 = __shfl_xor(x1, d);
+    const float p0 = lane_xor(x0, d), p1 = lane_xor(x1, d);
     const bool upper = (lane & d) != 0;
     x0 = upper ? p0 - x0 : x0 + p0;
     x1 = upper ? p1 - x1 : x1 + p1;
   }
 }
 
+// butterfly reductions: every lane ends with the same value
 __device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += lane_xor(x, o);
   return x;
 }
 __device__ __forceinline__ float wave_maxf(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, lane_xor(x, o));
   return x;
 }
 
