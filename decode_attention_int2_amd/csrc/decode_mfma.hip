@@ -55,8 +55,9 @@
 // rotation applied, outputs stored -- with the hardware ids of its compute
 // unit.  Waves past kPhaseWaves record nothing.
 constexpr int kPhaseWaves = 8192;
-constexpr int kPhaseFields = 12;  // hw id, xcc id, blocks, t entry, t loop, t loop end, t arrived, t merged,
-                                  // t rotated, t stored, t query digits ready, t first block's data
+constexpr int kPhaseFields = 14;  // hw id, xcc id, blocks, t entry, t loop, t loop end, t arrived, t merged,
+                                  // t rotated, t stored, t query digits ready, t first block's data,
+                                  // t first blocks' loads issued, t query row loaded
 __device__ unsigned long long kvq_phase_ts[kPhaseWaves * kPhaseFields];
 #define KVQ_PHASE(i) (phase_t[i] = wall_clock64())
 #else
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // other lanes' targets of a claim (each adds 0 to a word of its own)
   __shared__ uint32_t s_claim[64];
 #ifdef KVQ_PHASE_TIMESTAMPS
-  unsigned long long phase_t[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  unsigned long long phase_t[11] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #endif
   KVQ_PHASE(0);
   const int s = blockIdx.x, b = blockIdx.z;
@@ -710,6 +711,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   }
   load_block<P16, NT>(c, a0, b0, bad);
   load_block<P16, NT>(c, a1, b1, bad);
+#ifdef KVQ_PHASE_TIMESTAMPS
+  phase_t[9] = wall_clock64();  // (diagnostic: the first blocks' loads issued)
+  {
+    // (diagnostic: waits for this wave's query row)
+    uint32_t qv = qb0;
+    asm volatile("" : "+v"(qv));
+    phase_t[10] = wall_clock64() + (qv & 0u);
+  }
+#endif
 
   // ---- query rows: q' = q R_K log2(e)/sqrt(128)
   {
@@ -1120,7 +1130,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       const unsigned long long xcc = static_cast<unsigned>(__builtin_amdgcn_s_getreg((3 << 11) | 20));  // XCC_ID
       const unsigned long long f[kPhaseFields] = {hw, xcc, static_cast<unsigned long long>(nb), phase_t[0],
                                                   phase_t[1], phase_t[2], phase_t[3], phase_t[4], phase_t[5],
-                                                  phase_t[6], phase_t[7], phase_t[8]};
+                                                  phase_t[6], phase_t[7], phase_t[8], phase_t[9], phase_t[10]};
       unsigned long long v = f[0];
 #pragma unroll
       for (int i = 1; i < kPhaseFields; ++i) v = lane == i ? f[i] : v;

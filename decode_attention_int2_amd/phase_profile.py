@@ -13,6 +13,9 @@ each recorded launch is the last of a run of back-to-back kvq_decode_attn
 calls (no W_O), as in a decode loop.  Per launch, with
 times relative to the first wave's entry:
   * entry: when the last workgroup started;
+  * blocks issued: when each wave had issued its first two blocks' loads
+    (their page-table entries read);
+  * query row loaded: when each wave's query row had arrived;
   * query ready: when each wave's workgroup had its query digits;
   * first block: when each wave's first block of cache data had arrived;
   * loop start: when each wave began its main loop (query rows ready, first
@@ -41,10 +44,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PHASE_WAVES, PHASE_FIELDS, WAVES = 8192, 12, 8
+PHASE_WAVES, PHASE_FIELDS, WAVES = 8192, 14, 8
 # record fields: hw id, xcc id, blocks, t entry, t loop, t loop end, t arrived, t merged, t rotated, t stored,
-# t query digits ready, t first block's data
-HW, XCC, NB, T0, T1, T2, T3, T4, T5, T6, TQ, TB = range(12)
+# t query digits ready, t first block's data, t first blocks' loads issued, t query row loaded
+HW, XCC, NB, T0, T1, T2, T3, T4, T5, T6, TQ, TB, TI, TQL = range(14)
 
 
 def _pct(xs, p):
@@ -77,6 +80,8 @@ def launch_stats(rec, khz):
     return {
         "workgroups": len(wgs),
         "entry_last_us": max(entry),
+        "blocks_issued_median_us": statistics.median(us(r[TI] - t0) for r in rec),
+        "query_row_loaded_median_us": statistics.median(us(r[TQL] - t0) for r in rec),
         "query_ready_median_us": statistics.median(us(r[TQ] - t0) for r in rec),
         "first_block_median_us": statistics.median(us(r[TB] - t0) for r in rec),
         "loop_start_median_us": statistics.median(loop0),
