@@ -68,15 +68,21 @@ def _args():
     return ap.parse_args()
 
 
-SPLIT_KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_int2_amd", "csrc", "decode_mfma.hip")
+# the decode kernel's device code: its own file and the shared device helpers it includes
+SPLIT_KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_int2_amd", "csrc", f)
+                        for f in ("decode_mfma.hip", "kvq_internal.h")]
 
 
 def kernel_source_digest() -> str:
-    """sha256 of the split kernel's source: counter figures taken from another
-    version of the kernel are not reported."""
+    """sha256 of the split kernel's sources (concatenated in the order above):
+    counter figures taken from another version of the kernel are not
+    reported."""
     import hashlib
-    with open(SPLIT_KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in SPLIT_KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(path: str):
