@@ -189,36 +189,49 @@ __device__ __forceinline__ float load_partial(const float *p) {
 }
 
 // The merge of merge_splits_wave (same result, same order of operations)
-// with few memory round trips.  Up to 64 partials: lane u holds partial u's
-// (m, l, z) and the value sums come in batches of 16 partials, the first two
-// batches requested together with the statistics.  More partials: the
-// statistics in a lane loop, value sums in batches of 8 with their scales.
-__device__ __forceinline__ void merge_partials(const float *p, int parts, int lane, float &o0, float &o1,
-                                               float *m_out = nullptr, float *l_out = nullptr) {
-  if (parts <= 64) {
-    constexpr int kB = 16;
-    float ma = -INFINITY, la = 0.0f, za = 0.0f;
-    if (lane < parts) {
-      const float *q = p + static_cast<size_t>(lane) * (D + 4);
-      ma = load_partial(q);
-      la = load_partial(q + 1);
-      za = load_partial(q + 2);
-    }
-    float xa0[kB], xa1[kB], xb0[kB], xb1[kB];
-    auto fetch = [&](float *v0, float *v1, int u0) {
+// with few memory round trips, in two stages so that a caller can issue
+// other loads between them (a wave's loads complete in issue order, so
+// loads issued after merge_load do not delay the partials).  Up to 64
+// partials: lane u holds partial u's (m, l, z) and the value sums come in
+// batches of 16 partials, the first two batches requested by merge_load
+// together with the statistics.  More partials: merge_load requests
+// nothing; the statistics in a lane loop, value sums in batches of 8 with
+// their scales.
+constexpr int kMergeBatch = 16;
+struct MergeIn {
+  float ma, la, za;                              // partial `lane`'s statistics
+  float xa0[kMergeBatch], xa1[kMergeBatch];      // value sums of batches 0, 2, ...
+  float xb0[kMergeBatch], xb1[kMergeBatch];      // value sums of batches 1, 3, ...
+};
+__device__ __forceinline__ void merge_fetch(const float *p, int parts, int lane, float *v0, float *v1, int u0) {
 #pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const float *q = p + static_cast<size_t>(min(u0 + u, parts - 1)) * (D + 4);
-        v0[u] = load_partial(q + 4 + lane);
-        v1[u] = load_partial(q + 4 + 64 + lane);
-      }
-    };
-    fetch(xa0, xa1, 0);
-    if (parts > kB) fetch(xb0, xb1, kB);
-    const float mstar = wave_maxf(ma);
-    const float wa = (ma == -INFINITY) ? 0.0f : exp2f(ma - mstar);
-    const bool any_nan = __any(la != la);
-    const float l = wave_sum(wa != 0.0f ? wa * la : 0.0f), z = wave_sum(wa != 0.0f ? wa * za : 0.0f);
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const float *q = p + static_cast<size_t>(min(u0 + u, parts - 1)) * (D + 4);
+    v0[u] = load_partial(q + 4 + lane);
+    v1[u] = load_partial(q + 4 + 64 + lane);
+  }
+}
+__device__ __forceinline__ void merge_load(const float *p, int parts, int lane, MergeIn &in) {
+  if (parts > 64) return;
+  in.ma = -INFINITY;
+  in.la = in.za = 0.0f;
+  if (lane < parts) {
+    const float *q = p + static_cast<size_t>(lane) * (D + 4);
+    in.ma = load_partial(q);
+    in.la = load_partial(q + 1);
+    in.za = load_partial(q + 2);
+  }
+  merge_fetch(p, parts, lane, in.xa0, in.xa1, 0);
+  if (parts > kMergeBatch) merge_fetch(p, parts, lane, in.xb0, in.xb1, kMergeBatch);
+}
+__device__ __forceinline__ void merge_reduce(const float *p, int parts, int lane, MergeIn &in, float &o0, float &o1,
+                                             float *m_out = nullptr, float *l_out = nullptr) {
+  if (parts <= 64) {
+    constexpr int kB = kMergeBatch;
+    const float mstar = wave_maxf(in.ma);
+    const float wa = (in.ma == -INFINITY) ? 0.0f : exp2f(in.ma - mstar);
+    const bool any_nan = __any(in.la != in.la);
+    const float l = wave_sum(wa != 0.0f ? wa * in.la : 0.0f), z = wave_sum(wa != 0.0f ? wa * in.za : 0.0f);
     float a0 = 0.0f, a1 = 0.0f;
     auto accumulate = [&](const float *v0, const float *v1, int u0) {
 #pragma unroll
@@ -232,11 +245,11 @@ __device__ __forceinline__ void merge_partials(const float *p, int parts, int la
       }
     };
     for (int u0 = 0; u0 < parts; u0 += 2 * kB) {
-      accumulate(xa0, xa1, u0);
-      if (u0 + 2 * kB < parts) fetch(xa0, xa1, u0 + 2 * kB);
+      accumulate(in.xa0, in.xa1, u0);
+      if (u0 + 2 * kB < parts) merge_fetch(p, parts, lane, in.xa0, in.xa1, u0 + 2 * kB);
       if (u0 + kB < parts) {
-        accumulate(xb0, xb1, u0 + kB);
-        if (u0 + 3 * kB < parts) fetch(xb0, xb1, u0 + 3 * kB);
+        accumulate(in.xb0, in.xb1, u0 + kB);
+        if (u0 + 3 * kB < parts) merge_fetch(p, parts, lane, in.xb0, in.xb1, u0 + 3 * kB);
       }
     }
     o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
@@ -294,6 +307,12 @@ __device__ __forceinline__ void merge_partials(const float *p, int parts, int la
   if (any_nan) o0 = o1 = __builtin_nanf("");
   if (m_out) *m_out = mstar;
   if (l_out) *l_out = l;
+}
+__device__ __forceinline__ void merge_partials(const float *p, int parts, int lane, float &o0, float &o1,
+                                               float *m_out = nullptr, float *l_out = nullptr) {
+  MergeIn in;
+  merge_load(p, parts, lane, in);
+  merge_reduce(p, parts, lane, in, o0, o1, m_out, l_out);
 }
 
 // Device-scope store of a split partial (read by the merging workgroup).
@@ -1144,8 +1163,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
 #else
   if (s_last == 0) return;
 #endif
-  // dense R_V: the head's matrix is staged in LDS by the whole workgroup
-  // (its loads go out together with the merge's)
+  const int qq = (row0 + min(wave, nrows - 1)) / a.G, j = h * a.G + (row0 + min(wave, nrows - 1)) % a.G;
+  const size_t row = static_cast<size_t>(b) * a.Nq + qq;
+  const float *base = a.part + (row * a.Hq + j) * a.pstride * (D + 4);
+  // the merging waves request their partials first, then (dense R_V) the
+  // matrix: a wave's loads complete in issue order, so the merge does not
+  // wait for the matrix's 64 KB
+  MergeIn in;
+  if (wave < nrows) merge_load(base, a.parts, lane, in);
+  __builtin_amdgcn_sched_barrier(0);
   const bool vdense = a.rv.kind == KVQ_ROT_DENSE;
   // (thread t holds R_V[t / 4][32 (t % 4) .. 32 (t % 4) + 31], 128 consecutive bytes)
   float4 v0, v1, v2, v3, v4, v5, v6, v7;
@@ -1161,14 +1187,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     v6 = rm[6];
     v7 = rm[7];
   }
-  const int qq = (row0 + min(wave, nrows - 1)) / a.G, j = h * a.G + (row0 + min(wave, nrows - 1)) % a.G;
-  const size_t row = static_cast<size_t>(b) * a.Nq + qq;
   float o0 = 0.0f, o1 = 0.0f, mi = -INFINITY, li = 0.0f;
   float ow0 = 0.0f, ow1 = 0.0f, mw = -INFINITY, lw = 0.0f;  // the windows' partials (one per split)
   if (wave < nrows) {
-    const float *base = a.part + (row * a.Hq + j) * a.pstride * (D + 4);
     if constexpr (kWin) merge_partials(base + static_cast<size_t>(a.parts) * (D + 4), a.splits, lane, ow0, ow1, &mw, &lw);
-    merge_partials(base, a.parts, lane, o0, o1, &mi, &li);
+    merge_reduce(base, a.parts, lane, in, o0, o1, &mi, &li);
   }
 #ifdef KVQ_PHASE_TIMESTAMPS
   __builtin_amdgcn_s_waitcnt(0);
