@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void quadform_kernel(const float *x1_all, cons
 #pragma unroll
   for (int j = 0; j < kHalf; ++j) {
     double v = e[j];
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    for (int o = 32; o > 0; o >>= 1) v += lane_xor(v, o);
     if (lane == 0) red[wave][j] = v;
   }
   __syncthreads();

@@ -879,10 +879,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
             const float4 qb = *reinterpret_cast<const float4 *>(&qs[r][8 * part + 4]);
             float d = qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3];
             d += qb.x * kf[4] + qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
-            d += __shfl_xor(d, 1);
-            d += __shfl_xor(d, 2);
-            d += __shfl_xor(d, 4);
-            d += __shfl_xor(d, 8);
+            d += lane_xor(d, 1);
+            d += lane_xor(d, 2);
+            d += lane_xor(d, 4);
+            d += lane_xor(d, 8);
             dot[r] = d;
           }
           if (part == 0) {

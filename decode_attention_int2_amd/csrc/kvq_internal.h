@@ -95,6 +95,13 @@ __device__ __forceinline__ int lane_xor(int x, int d) {
   return static_cast<int>(r[0] == u ? r[1] : r[0]);
 }
 __device__ __forceinline__ float lane_xor(float x, int d) { return __int_as_float(lane_xor(__float_as_int(x), d)); }
+// (each half of the double separately: the row swaps' value test picks the
+// partner's half or, when the two halves agree, either)
+__device__ __forceinline__ double lane_xor(double x, int d) {
+  const long long b = __double_as_longlong(x);
+  const int lo = lane_xor(static_cast<int>(b), d), hi = lane_xor(static_cast<int>(b >> 32), d);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
 
 // In-place fast Walsh-Hadamard transform: x <- x H, H[i][j] = (-1)^popcount(i & j)
 // (Sylvester order, unnormalized): one butterfly stage per index bit.

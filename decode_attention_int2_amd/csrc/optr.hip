@@ -375,11 +375,11 @@ __global__ __launch_bounds__(256) void narrow_kernel(const double *x, size_t n, 
 
 // ---------------------------------------------------------------- quantizer with straight-through flags
 __device__ __forceinline__ float wmin(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, lane_xor(x, o));
   return x;
 }
 __device__ __forceinline__ float wmax(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, lane_xor(x, o));
   return x;
 }
 
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void err_rows_kernel(const double *x, double *
   const double *a = x + row * D;
   double *c = xg + row * D;
   double s = a[lane] * c[lane] + a[lane + 64] * c[lane + 64];
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  for (int o = 32; o > 0; o >>= 1) s += lane_xor(s, o);
   if (lane == 0) e2[row] = s * inv_dm;
   c[lane] *= coef;
   c[lane + 64] *= coef;

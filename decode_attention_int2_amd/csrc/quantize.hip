@@ -30,11 +30,11 @@ struct QuantArgs {
 };
 
 __device__ __forceinline__ float wave_min(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, lane_xor(x, o));
   return x;
 }
 __device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, lane_xor(x, o));
   return x;
 }
 

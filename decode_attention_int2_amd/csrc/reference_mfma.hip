@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256) void reference_mfma_kernel(RefArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (t0 + 4 * kg + i < t_end) ? sv[i] : -INFINITY;
     float tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = fmaxf(tm, lane_xor(tm, 16));
+    tm = fmaxf(tm, lane_xor(tm, 32));
     const float mn = fmaxf(m, tm);  // finite: token t0 is in range
     const float alpha = exp2f(m - mn);
     float p[4], ps = 0.0f;
@@ -169,8 +169,8 @@ __global__ __launch_bounds__(256) void reference_mfma_kernel(RefArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(elem8<DT>(vc[st], dt), p[st], o[dt], 0, 0, 0);
   }
   // the row's sum over its 4 lanes (same running max in all of them)
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l += lane_xor(l, 16);
+  l += lane_xor(l, 32);
   if (!row_ok) return;
   float *dst = a.part + ((static_cast<size_t>(qi) * a.Hq + j) * a.splits + s) * (D + 4);
 #pragma unroll
