@@ -105,13 +105,14 @@ __device__ __forceinline__ double lane_xor(double x, int d) {
 
 // In-place fast Walsh-Hadamard transform: x <- x H, H[i][j] = (-1)^popcount(i & j)
 // (Sylvester order, unnormalized): one butterfly stage per index bit.
-__device__ __forceinline__ void fwht128(float &x0, float &x1, int lane) {
-  const float a = x0 + x1, b = x0 - x1;  // bit 6: pairs (lane, lane + 64)
+template <typename T>
+__device__ __forceinline__ void fwht128(T &x0, T &x1, int lane) {
+  const T a = x0 + x1, b = x0 - x1;  // bit 6: pairs (lane, lane + 64)
   x0 = a;
   x1 = b;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
-    const float p0 = lane_xor(x0, d), p1 = lane_xor(x1, d);
+    const T p0 = lane_xor(x0, d), p1 = lane_xor(x1, d);
     const bool upper = (lane & d) != 0;
     x0 = upper ? p0 - x0 : x0 + p0;
     x1 = upper ? p1 - x1 : x1 + p1;

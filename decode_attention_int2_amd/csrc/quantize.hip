@@ -83,6 +83,18 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(QuantArgs a) {
         if (rot.kind == KVQ_ROT_IDENTITY) {
           r0 = mean ? x0 - mean[h * D + lane] : x0;
           r1 = mean ? x1 - mean[h * D + lane + 64] : x1;
+        } else if (rot.kind == KVQ_ROT_SIGNED_HADAMARD) {
+          // z' = (s z) H / sqrt(128) in fp64 by the fast transform (the same
+          // sums as the index-order product, in butterfly order: they differ
+          // in fp64 rounding only), then one rounding to fp32
+          const int8_t *sg = rot.signs + h * D;
+          double y0 = (static_cast<double>(x0) - (mean ? static_cast<double>(mean[h * D + lane]) : 0.0)) *
+                      static_cast<double>(sg[lane]);
+          double y1 = (static_cast<double>(x1) - (mean ? static_cast<double>(mean[h * D + lane + 64]) : 0.0)) *
+                      static_cast<double>(sg[lane + 64]);
+          fwht128(y0, y1, lane);
+          r0 = static_cast<float>(y0 * a.inv_sqrt_d);
+          r1 = static_cast<float>(y1 * a.inv_sqrt_d);
         } else {
           zsh[wave][lane] = static_cast<double>(x0) - (mean ? static_cast<double>(mean[h * D + lane]) : 0.0);
           zsh[wave][lane + 64] =
@@ -90,27 +102,15 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(QuantArgs a) {
         }
       }
       __syncthreads();
-      if (active && rot.kind != KVQ_ROT_IDENTITY) {
+      if (active && rot.kind == KVQ_ROT_DENSE) {
         // z' = z R in fp64, summed in index order: products and sums rounded
         // separately, then one rounding to fp32.
         double acc0 = 0.0, acc1 = 0.0;
-        if (rot.kind == KVQ_ROT_DENSE) {
-          const float *m = rot.matrix + static_cast<size_t>(h) * D * D;
-          for (int i = 0; i < D; ++i) {
-            const double zi = zsh[wave][i];
-            acc0 = acc0 + zi * static_cast<double>(m[i * D + lane]);
-            acc1 = acc1 + zi * static_cast<double>(m[i * D + lane + 64]);
-          }
-        } else {
-          const int8_t *s = rot.signs + h * D;
-          for (int i = 0; i < D; ++i) {
-            const double zi = zsh[wave][i];
-            const double si = static_cast<double>(s[i]);
-            const double e0 = si * static_cast<double>(hadamard_sign(i, lane)) * a.inv_sqrt_d;
-            const double e1 = si * static_cast<double>(hadamard_sign(i, lane + 64)) * a.inv_sqrt_d;
-            acc0 = acc0 + zi * e0;
-            acc1 = acc1 + zi * e1;
-          }
+        const float *m = rot.matrix + static_cast<size_t>(h) * D * D;
+        for (int i = 0; i < D; ++i) {
+          const double zi = zsh[wave][i];
+          acc0 = acc0 + zi * static_cast<double>(m[i * D + lane]);
+          acc1 = acc1 + zi * static_cast<double>(m[i * D + lane + 64]);
         }
         r0 = static_cast<float>(acc0);
         r1 = static_cast<float>(acc1);
