@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *part, int n_i
   if (rj >= n_items) return;
   const int row = rj / Hq, j = rj % Hq;
   float o0, o1;
-  merge_splits_wave(part + static_cast<size_t>(rj) * splits * (D + 4), splits, lane, o0, o1);
+  merge_partials(part + static_cast<size_t>(rj) * splits * (D + 4), splits, lane, o0, o1);
   unrotate_value_wave(o0, o1, rv, j / G, lane);
   store_output_wave(out_o, ot, row, j, Hq, lane, o0, o1);
   if (y_zero && j == 0)  // the row's W_O output starts at zero (the projection adds into it)

@@ -186,42 +186,153 @@ __device__ __forceinline__ void rotate_query_wave(float &x0, float &x1, const Ro
 // a flag word, and acc[c] = sum_t 2^(x_t - m) s_t code_t[c], over the split's
 // tokens t with x_t = logit_t in log2 units (l = NaN marks a bad input).
 
-// Rotated-domain output o'[c] = (sum_s 2^(m_s - m*) (acc_s[c] + z_s)) /
-// (sum_s 2^(m_s - m*) l_s) of the `splits` partials at p (stride 132 floats),
-// held by one wave as o0 = o'[lane], o1 = o'[lane + 64]; 0 when no token
-// counted, NaN when a split flagged a bad input.
-__device__ __forceinline__ void merge_splits_wave(const float *p, int splits, int lane, float &o0, float &o1) {
+// Device-scope load of a split partial written by another workgroup (of
+// this launch or an earlier one).
+__device__ __forceinline__ float load_partial(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same for two consecutive floats (8-byte aligned): one 8-byte load.
+__device__ __forceinline__ float2 load_partial2(const float *p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32))};
+}
+
+// Merge of the `parts` partials at p (stride 132 floats) into the
+// rotated-domain output o'[c] = (sum_s 2^(m_s - m*) (acc_s[c] + z_s)) /
+// (sum_s 2^(m_s - m*) l_s), m* = max_s m_s, held by one wave as
+// o0 = o'[lane], o1 = o'[lane + 64]: 0 when no token counted, NaN when a
+// partial flagged a bad input; the value sums are added in partial order.
+// Few memory round trips, in two stages so that a caller can issue
+// other loads between them (a wave's loads complete in issue order, so
+// loads issued after merge_load do not delay the partials).  Up to 64
+// partials: lane u holds partial u's (m, l, z); the value sums come in
+// batches of 16 partials, lane l reading dims 2l and 2l + 1 of each (one
+// 8-byte load per partial), the first two batches requested by merge_load
+// together with the statistics: 34 loads, within the 63 a wave can have in
+// flight, so 32 partials arrive in one round trip.  The sums are moved to
+// the (l, l + 64) lane layout at the end.  More partials: merge_load
+// requests nothing; the statistics in a lane loop, value sums in batches of
+// 8 with their scales.
+constexpr int kMergeBatch = 16;
+struct MergeIn {
+  float ma, la, za;           // partial `lane`'s statistics
+  float2 xa[kMergeBatch];     // value sums of batches 0, 2, ... (dims 2 lane, 2 lane + 1)
+  float2 xb[kMergeBatch];     // value sums of batches 1, 3, ...
+};
+__device__ __forceinline__ void merge_fetch(const float *p, int parts, int lane, float2 *v, int u0) {
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    v[u] = load_partial2(p + static_cast<size_t>(min(u0 + u, parts - 1)) * (D + 4) + 4 + 2 * lane);
+}
+__device__ __forceinline__ void merge_load(const float *p, int parts, int lane, MergeIn &in) {
+  if (parts > 64) return;
+  in.ma = -INFINITY;
+  in.la = in.za = 0.0f;
+  if (lane < parts) {
+    const float *q = p + static_cast<size_t>(lane) * (D + 4);
+    const float2 ml = load_partial2(q);
+    in.ma = ml.x;
+    in.la = ml.y;
+    in.za = load_partial(q + 2);
+  }
+  merge_fetch(p, parts, lane, in.xa, 0);
+  if (parts > kMergeBatch) merge_fetch(p, parts, lane, in.xb, kMergeBatch);
+}
+__device__ __forceinline__ void merge_reduce(const float *p, int parts, int lane, MergeIn &in, float &o0, float &o1,
+                                             float *m_out = nullptr, float *l_out = nullptr) {
+  if (parts <= 64) {
+    constexpr int kB = kMergeBatch;
+    const float mstar = wave_maxf(in.ma);
+    const float wa = (in.ma == -INFINITY) ? 0.0f : exp2f(in.ma - mstar);
+    const bool any_nan = __any(in.la != in.la);
+    const float l = wave_sum(wa != 0.0f ? wa * in.la : 0.0f), z = wave_sum(wa != 0.0f ? wa * in.za : 0.0f);
+    float e0 = 0.0f, e1 = 0.0f;  // dims 2 lane, 2 lane + 1
+    auto accumulate = [&](const float2 *v, int u0) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (u0 + u >= parts) break;
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa), u0 + u));
+        if (w != 0.0f) {
+          e0 += w * v[u].x;
+          e1 += w * v[u].y;
+        }
+      }
+    };
+    for (int u0 = 0; u0 < parts; u0 += 2 * kB) {
+      accumulate(in.xa, u0);
+      if (u0 + 2 * kB < parts) merge_fetch(p, parts, lane, in.xa, u0 + 2 * kB);
+      if (u0 + kB < parts) {
+        accumulate(in.xb, u0 + kB);
+        if (u0 + 3 * kB < parts) merge_fetch(p, parts, lane, in.xb, u0 + 3 * kB);
+      }
+    }
+    // dim d sits in lane d / 2 (component d % 2): lane l takes dims l and l + 64
+    const int src0 = lane >> 1, src1 = 32 + (lane >> 1);
+    const float p00 = __shfl(e0, src0), p01 = __shfl(e1, src0);
+    const float p10 = __shfl(e0, src1), p11 = __shfl(e1, src1);
+    const float a0 = (lane & 1) ? p01 : p00, a1 = (lane & 1) ? p11 : p10;
+    o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
+    o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
+    if (any_nan) o0 = o1 = __builtin_nanf("");
+    if (m_out) *m_out = mstar;
+    if (l_out) *l_out = l;
+    return;
+  }
+  constexpr int kU = 8;
+  float mv[kU], av0[kU], av1[kU];
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float *q = p + static_cast<size_t>(min(s0 + u, parts - 1)) * (D + 4);
+      mv[u] = load_partial(q);
+      av0[u] = load_partial(q + 4 + lane);
+      av1[u] = load_partial(q + 4 + 64 + lane);
+    }
+  };
+  fetch(0);
   float mloc = -INFINITY;
-  for (int s2 = lane; s2 < splits; s2 += 64)
-    mloc = fmaxf(mloc, p[static_cast<size_t>(s2) * (D + 4)]);
+  bool nanloc = false;
+  // split statistics: lane s2 holds split s2 (and s2 + 64, ...)
+  for (int s2 = lane; s2 < parts; s2 += 64) mloc = fmaxf(mloc, load_partial(p + static_cast<size_t>(s2) * (D + 4)));
   const float mstar = wave_maxf(mloc);
-  float lloc = 0.0f, zloc = 0.0f, nanloc = 0.0f;
-  for (int s2 = lane; s2 < splits; s2 += 64) {
+  float lloc = 0.0f, zloc = 0.0f;
+  for (int s2 = lane; s2 < parts; s2 += 64) {
     const float *q = p + static_cast<size_t>(s2) * (D + 4);
-    const float m = q[0], l = q[1], z = q[2];
+    const float m = load_partial(q), l = load_partial(q + 1), z = load_partial(q + 2);
     const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
-    if (l != l) nanloc = 1.0f;
+    if (l != l) nanloc = true;
     if (w != 0.0f) {
       lloc += w * l;
       zloc += w * z;
     }
   }
   const float l = wave_sum(lloc), z = wave_sum(zloc);
-  const bool any_nan = wave_maxf(nanloc) != 0.0f;
+  const bool any_nan = __any(nanloc);
   float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll 4
-  for (int s2 = 0; s2 < splits; ++s2) {
-    const float *q = p + static_cast<size_t>(s2) * (D + 4);
-    const float m = q[0];  // uniform
-    const float w = (m == -INFINITY) ? 0.0f : exp2f(m - mstar);
-    if (w != 0.0f) {
-      a0 += w * q[4 + lane];
-      a1 += w * q[4 + 64 + lane];
+  for (int s0 = 0; s0 < parts; s0 += kU) {
+    if (s0 > 0) fetch(s0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s0 + u >= parts) break;
+      const float w = (mv[u] == -INFINITY) ? 0.0f : exp2f(mv[u] - mstar);
+      if (w != 0.0f) {
+        a0 += w * av0[u];
+        a1 += w * av1[u];
+      }
     }
   }
   o0 = (l > 0.0f) ? (a0 + z) / l : 0.0f;
   o1 = (l > 0.0f) ? (a1 + z) / l : 0.0f;
   if (any_nan) o0 = o1 = __builtin_nanf("");
+  if (m_out) *m_out = mstar;
+  if (l_out) *l_out = l;
+}
+__device__ __forceinline__ void merge_partials(const float *p, int parts, int lane, float &o0, float &o1,
+                                               float *m_out = nullptr, float *l_out = nullptr) {
+  MergeIn in;
+  merge_load(p, parts, lane, in);
+  merge_reduce(p, parts, lane, in, o0, o1, m_out, l_out);
 }
 
 // out = o' R_V^T of KV head h (one wave, same register layout as above).

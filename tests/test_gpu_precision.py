@@ -40,14 +40,15 @@ def test_fp32_long_sequence_default_plan(dev):
     assert e <= 1e-4 and ey <= 1e-4
 
 
-@pytest.mark.parametrize("gap_log2", [20.0, 22.0, 24.0])
-def test_fp32_dominant_token_and_long_tail_in_one_split(dev, gap_log2):
+@pytest.mark.parametrize("gap_log2,queries", [(20.0, 1), (22.0, 1), (24.0, 1), (20.0, 8), (24.0, 8)])
+def test_fp32_dominant_token_and_long_tail_in_one_split(dev, gap_log2, queries):
     """One split of 131,072 tokens: one dominant token whose logit lies about
     gap_log2 binary orders above the others, and a tail whose values share a
     direction opposite to the dominant value, so that the tail's ~3-10% of the
-    softmax mass visibly moves the output."""
+    softmax mass visibly moves the output.  4 query rows per KV head (one
+    group per workgroup) and 32 (four pairs of groups)."""
     T, H, Hq = 131072, 1, 4
-    w = synthetic.make("envelope", dev, tokens=T, H=H, Hq=Hq, queries=1, d_model=64)
+    w = synthetic.make("envelope", dev, tokens=T, H=H, Hq=Hq, queries=queries, d_model=64)
     g = torch.Generator().manual_seed(9100 + int(gap_log2))
     s = 0.5
     z = torch.randn(128, generator=g, dtype=torch.float64)
@@ -62,7 +63,7 @@ def test_fp32_dominant_token_and_long_tail_in_one_split(dev, gap_log2):
     k[pos, 0] = (beta * z / z.norm()).to(torch.float32)
     v[pos, 0] = -u
     w.k, w.v = k.contiguous().to(dev), v.contiguous().to(dev)
-    w.q = q.expand(1, Hq, 128).contiguous().to(dev)
+    w.q = q.expand(queries, Hq, 128).contiguous().to(dev)
     w.rot_k = w.rot_v = synthetic.RotationSpec(synthetic.ROT_IDENTITY)
     w.clip_k = w.clip_v = 1.0
     cache = gpu_quantize(w, dev)
@@ -79,5 +80,5 @@ def test_fp32_dominant_token_and_long_tail_in_one_split(dev, gap_log2):
     print(f"gap {gap_log2}: log2 gaps {gap.min():.1f}..{gap.max():.1f}, tail mass {tail_mass:.3f}", flush=True)
     assert abs(np.median(gap) - gap_log2) < 2 and tail_mass > 5e-3
     e = _per_row_head(f32np(out_o), ref_o)
-    print(f"gap {gap_log2}: max rel-L2 per (row, head) {e:.2e}", flush=True)
+    print(f"gap {gap_log2}, {queries * Hq // H} rows: max rel-L2 per (row, head) {e:.2e}", flush=True)
     assert e <= 1e-4
