@@ -5,7 +5,7 @@ libkvq.so, plus a wall-clock read at each phase boundary of every wave).
 Build the library on the build host first:
     python -m decode_attention_int2_amd.build --phase-timestamps
 then, on a GPU:
-    python -m decode_attention_int2_amd.phase_profile [--workload paged16x32k] [--launches 5]
+    python -m decode_attention_int2_amd.phase_profile [--workload paged16x32k] [--launches 5] [--windows 64,256]
 
 The workload's cache is written into three rotating buffers (as bench.py
 does, so that each decode reads its cache from HBM); after untimed launches,
@@ -110,6 +110,7 @@ def main():
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--run", type=int, default=20, help="back-to-back launches per record (the last is recorded)")
     ap.add_argument("--raw", default=None, help="also write every wave's record of every launch here (JSON lines)")
+    ap.add_argument("--windows", default=None, help="SINK,RECENT: decode with BF16 sink and recent windows of these sizes")
     a = ap.parse_args()
     import torch
     import synthetic
@@ -134,6 +135,19 @@ def main():
                      device=dev)
     dec = lambda i: kvq.kvq_decode_attn(w.q, B, w.queries_per_seq, caches[i % n], w.page_table,
                                         w.page_table.shape[1], w.seq_lens, T, rot, rot, out_o, workspace=ws)
+    if a.windows:
+        # the windows' bf16 copies of the same K, V (one set per cache buffer)
+        S_w, W_w = (int(x) for x in a.windows.split(","))
+        seq_idx = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T)
+        pos = torch.arange(T, dtype=torch.int32, device=dev).repeat(B)
+        gws = []
+        for i in range(n):
+            gw = kvq.Windows(B, H, S_w, W_w, device=dev)
+            kvq.kvq_window_write(w.k, w.v, seq_idx, pos, gw, seq_lens=w.seq_lens)
+            gws.append(gw)
+        dec = lambda i: kvq.kvq_decode_attn_windows(w.q, B, w.queries_per_seq, caches[i % n], w.page_table,
+                                                    w.page_table.shape[1], w.seq_lens, T, rot, rot, gws[i % n],
+                                                    out_o, workspace=ws)
     for i in range(30):
         dec(i)
     buf = (ctypes.c_ulonglong * (PHASE_WAVES * PHASE_FIELDS))()
@@ -160,7 +174,8 @@ def main():
                 f.write(json.dumps({"launch": i, "khz": khz, "waves": rec}) + "\n")
         print(f"launch {i}: {json.dumps(per[-1])}", file=sys.stderr, flush=True)
     keys = [k for k in per[0] if not k.endswith("_by_xcd_us")]
-    out = {"workload": a.workload, "launches": a.launches, "clock_khz": khz, "kv_bytes": B * T * H * 72}
+    out = {"workload": a.workload + (f" windows {a.windows}" if a.windows else ""), "launches": a.launches,
+           "clock_khz": khz, "kv_bytes": B * T * H * 72}
     for k in keys:
         vals = [p[k] for p in per if p[k] is not None]
         out[k] = round(statistics.median(vals), 2) if vals else None
