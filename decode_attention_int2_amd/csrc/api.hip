@@ -199,6 +199,7 @@ static int decode_attn(const void *q, int32_t dtype, int32_t num_seqs, int32_t q
     rc = check_windows(windows, H);
     if (rc) return rc;
     if (windows->num_seqs < num_seqs) return KVQ_ERR_INVALID_ARGUMENT;
+    if (!aligned16(key_mean)) return KVQ_ERR_INVALID_ARGUMENT;  // (read with 16-byte loads)
   }
   const DecodePlan pl = make_decode_plan(num_seqs, queries_per_seq, num_q_heads, H, max_seq_len,
                                          w_o ? d_model : 0, num_splits, cache->page_size, windows != nullptr);

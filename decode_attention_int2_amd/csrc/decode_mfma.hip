@@ -68,6 +68,8 @@ namespace kvq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf_w __attribute__((ext_vector_type(8)));
+typedef float v4bf_f __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kM0 = 0x03030303u, kM1 = 0x0C0C0C0Cu, kM2 = 0x30303030u;
 constexpr int kHeadroom = 2;       // log2 headroom of the value scale
@@ -424,33 +426,6 @@ __device__ __forceinline__ void compute_block(const Ctx &c, int t0, const Blk &b
     }
 }
 
-constexpr int kWinBatch = 3;  // window chunks of 64 tokens held in registers at once
-
-// Loads of the window tokens [u0, min(u1, u0 + 64 kWinBatch)) of sequence b,
-// KV head h (token u: sink position u when u < n_sink, else recent position
-// hi + u - n_sink in slot position % win_W): thread t takes 16 bytes (8
-// dims) of tokens 64 ch + t / 16 and 64 ch + 32 + t / 16; zero past u1.
-__device__ __forceinline__ void load_window_batch(const MfmaArgs &a, int b, int h, int u0, int u1, int n_sink, int hi,
-                                                  uint4 (&wk)[kWinBatch][2], uint4 (&wv)[kWinBatch][2]) {
-  const size_t hstride = static_cast<size_t>(a.H) * D;  // elements between window tokens
-  const size_t hoff = static_cast<size_t>(h) * D;
-#pragma unroll
-  for (int ch = 0; ch < kWinBatch; ++ch)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int idx = threadIdx.x + 64 * kWaves * e, u = u0 + 64 * ch + (idx >> 4), part = idx & 15;
-      wk[ch][e] = wv[ch][e] = uint4{0u, 0u, 0u, 0u};
-      if (u < u1) {
-        const bool sink = u < n_sink;
-        const size_t tok = sink ? static_cast<size_t>(b) * a.win_S + u
-                                : static_cast<size_t>(b) * a.win_W + (hi + u - n_sink) % a.win_W;
-        const size_t off = tok * hstride + hoff + 8 * part;
-        wk[ch][e] = *reinterpret_cast<const uint4 *>((sink ? a.win_sk : a.win_rk) + off);
-        wv[ch][e] = *reinterpret_cast<const uint4 *>((sink ? a.win_sv : a.win_rv) + off);
-      }
-    }
-}
-
 // RG: groups of 4 query rows per workgroup (1, or 2 without BF16 windows):
 // every wave computes each of its blocks for the RG groups.
 template <int DT, bool P16, bool kDense, bool kWin, bool NT, int RG>
@@ -543,16 +518,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     sb1 = sp[lane + 64];
   }
   // BF16 windows: this split's slice [wu0, wu1) of the window tokens (sink
-  // positions [0, lo), then recent positions [hi, L)), in chunks of 64; the
-  // first kWinBatch chunks are loaded now, behind the query rows
+  // positions [0, lo), then recent positions [hi, L)), in tiles of 16,
+  // computed after the main loop
   const int n_sink = lo, n_win = lo + (L - hi);
   int wu0 = 0, wu1 = 0;
-  uint4 wk[kWin ? kWinBatch : 1][2], wv[kWin ? kWinBatch : 1][2];
   if constexpr (kWin) {
-    const int slice = 64 * ((((n_win + 63) / 64) + a.splits - 1) / a.splits);
+    const int slice = 16 * ((((n_win + 15) / 16) + a.splits - 1) / a.splits);
     wu0 = min(s * slice, n_win);
     wu1 = min(wu0 + slice, n_win);
-    load_window_batch(a, b, h, wu0, wu1, n_sink, hi, wk, wv);
   }
   // dense R_K: thread (quarter kq = t / 128, column j = t % 128) holds
   // R_K[32 kq + i][j], i < 32, for the query rows' product below (each load
@@ -693,126 +666,30 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   }
   load_block<P16, NT>(c, a2, b2, bad);
   if (wave == 0) cnt_word = __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if constexpr (kWin) {
-    // ---- this split's window tokens in fp32 while its first blocks load:
-    // logits of the group's raw query rows against q . (k - mu), a softmax
-    // per row (online across batches of 192 tokens), weighted raw values;
-    // stored as this split's window partial (m, l, 0, acc[128]), merged after
-    // the INT2 partials.  Per batch: the values go to LDS as bf16 and every
-    // lane's logits (a token's 16 lanes sum its 128 dims) to xw; one softmax
-    // pass per row; each thread then sums 4 dims of one row over a quarter of
-    // the tokens.  Raw query rows (scaled to base-2 logits) and q . mu into
-    // LDS (qs is free: the digits are built).
-    float *qmu_s = red(0, 4);       // [4]
-    float *xw = red(1, 0);          // [4][192]: logits, then weights (spans red[1], red[2])
-    float *alw = red(3, 0);         // [4]: rescale factor of a batch per row
-    uint16_t *vb16 = reinterpret_cast<uint16_t *>(&facc_all[0][0]);  // [192][128] bf16 values (free until the first flush)
-    constexpr int kWT = 64 * kWinBatch;
-    if (wave < 4) {
-      float r0 = 0.0f, r1 = 0.0f;
-      if (wave < nrows) {
-        r0 = (DT == KVQ_F32 ? __uint_as_float(qb0) : __uint_as_float(qb0 << 16)) * (kLog2eF * kInvSqrtD);
-        r1 = (DT == KVQ_F32 ? __uint_as_float(qb1) : __uint_as_float(qb1 << 16)) * (kLog2eF * kInvSqrtD);
-      }
-      qs[wave][lane] = r0;
-      qs[wave][lane + 64] = r1;
-      const float qm = a.win_mu ? wave_sum(r0 * a.win_mu[static_cast<size_t>(h) * D + lane] +
-                                           r1 * a.win_mu[static_cast<size_t>(h) * D + lane + 64])
-                                : 0.0f;
-      if (lane == 0) qmu_s[wave] = qm;
-    }
-    float m_run = -INFINITY, l_run = 0.0f;  // row `wave` (waves 0-3)
-    const int vr = threadIdx.x >> 7, g4 = threadIdx.x & 31, tp = (threadIdx.x >> 5) & 3;
-    float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // row vr, dims 4 g4 .. 4 g4 + 3, tokens tp (mod 4)
-    for (int u_b = wu0; u_b < wu1; u_b += kWT) {
-      if (u_b != wu0) load_window_batch(a, b, h, u_b, wu1, n_sink, hi, wk, wv);
-      const int nt = min(kWT, wu1 - u_b);
-      __syncthreads();  // (query rows written; the previous batch's LDS reads done)
+  // BF16 windows: the window rows' loads (win_load: lane (token n, g) takes
+  // dims 32 ks + 8 g .. + 7 of token n of a tile; tokens past the slice read
+  // its last token and are masked), issued when the wave's main loop ends
+  const int wn = lane & 15, wg = lane >> 4, wr = wn >> 2, wpart = wn & 3;
+  const int w_tiles = kWin ? (wu1 - wu0 + 15) / 16 : 0;
+  uint4 wkr[kWin ? 2 : 1][4], wvr[kWin ? 2 : 1][4];
+  auto win_load = [&](int t0, uint4 (&kr)[kWin ? 2 : 1][4], uint4 (&vr)[kWin ? 2 : 1][4]) {
+    const size_t hstride = static_cast<size_t>(a.H) * D;  // elements between window tokens
 #pragma unroll
-      for (int ch = 0; ch < kWinBatch; ++ch) {
-        if (64 * ch >= nt) break;
+    for (int tl = 0; tl < 2; ++tl) {
+      const int u = min(wu0 + 16 * (t0 + kWaves * tl) + wn, wu1 - 1);
+      const bool sink = u < n_sink;
+      const size_t tok = sink ? static_cast<size_t>(b) * a.win_S + u
+                              : static_cast<size_t>(b) * a.win_W + (hi + u - n_sink) % a.win_W;
+      const size_t off = tok * hstride + static_cast<size_t>(h) * D + 8 * wg;
+      const uint16_t *kp = (sink ? a.win_sk : a.win_rk) + off;
+      const uint16_t *vp = (sink ? a.win_sv : a.win_rv) + off;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int idx = threadIdx.x + 64 * kWaves * e, tok = 64 * ch + (idx >> 4), part = idx & 15;
-          *reinterpret_cast<uint4 *>(vb16 + tok * D + 8 * part) = wv[ch][e];
-          const uint4 kq = wk[ch][e];
-          const float kf[8] = {__uint_as_float(kq.x << 16), __uint_as_float(kq.x & 0xFFFF0000u),
-                               __uint_as_float(kq.y << 16), __uint_as_float(kq.y & 0xFFFF0000u),
-                               __uint_as_float(kq.z << 16), __uint_as_float(kq.z & 0xFFFF0000u),
-                               __uint_as_float(kq.w << 16), __uint_as_float(kq.w & 0xFFFF0000u)};
-          float dot[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float4 qa = *reinterpret_cast<const float4 *>(&qs[r][8 * part]);
-            const float4 qb = *reinterpret_cast<const float4 *>(&qs[r][8 * part + 4]);
-            float d = qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3];
-            d += qb.x * kf[4] + qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
-            d += lane_xor(d, 1);
-            d += lane_xor(d, 2);
-            d += lane_xor(d, 4);
-            d += lane_xor(d, 8);
-            dot[r] = d;
-          }
-          if (part == 0) {
-            const bool ok = tok < nt;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xw[r * kWT + tok] = ok ? dot[r] - qmu_s[r] : -INFINITY;
-          }
-        }
-      }
-      __syncthreads();
-      if (wave < 4) {  // softmax of row `wave` over the batch, lanes take tokens lane, lane + 64, lane + 128
-        float xv[kWinBatch], mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < kWinBatch; ++i) {
-          xv[i] = lane + 64 * i < nt ? xw[wave * kWT + lane + 64 * i] : -INFINITY;
-          mx = fmaxf(mx, xv[i]);
-        }
-        const float mn = fmaxf(m_run, wave_maxf(mx));  // finite: the batch holds a token
-        const float al = exp2f(m_run - mn);
-        float ps = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kWinBatch; ++i) {
-          const float pv = exp2f(xv[i] - mn);
-          ps += pv;
-          if (lane + 64 * i < nt) xw[wave * kWT + lane + 64 * i] = pv;
-        }
-        l_run = l_run * al + wave_sum(ps);
-        m_run = mn;
-        if (lane == 0) alw[wave] = al;
-      }
-      __syncthreads();
-      const float al = alw[vr];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc4[jj] *= al;
-      for (int t = tp; t < nt; t += 4) {
-        const float pv = xw[vr * kWT + t];
-        const uint2 v2 = *reinterpret_cast<const uint2 *>(vb16 + t * D + 4 * g4);
-        acc4[0] += pv * __uint_as_float(v2.x << 16);
-        acc4[1] += pv * __uint_as_float(v2.x & 0xFFFF0000u);
-        acc4[2] += pv * __uint_as_float(v2.y << 16);
-        acc4[3] += pv * __uint_as_float(v2.y & 0xFFFF0000u);
+      for (int ks = 0; ks < 4; ++ks) {
+        kr[tl][ks] = *reinterpret_cast<const uint4 *>(kp + 32 * ks);
+        vr[tl][ks] = *reinterpret_cast<const uint4 *>(vp + 32 * ks);
       }
     }
-    __syncthreads();  // (the values' LDS reads done)
-    // the 4 token parts of every (row, dim), summed through LDS, then the
-    // window partial of this split: slot parts + s (an empty slice stores m = -inf, l = 0)
-    float *wsum = &facc_all[0][0];  // [4 rows][4 parts][128]
-    *reinterpret_cast<float4 *>(wsum + (vr * 4 + tp) * D + 4 * g4) = float4{acc4[0], acc4[1], acc4[2], acc4[3]};
-    __syncthreads();
-    const int ad = threadIdx.x & 127;
-    const float wacc = (wsum[(vr * 4) * D + ad] + wsum[(vr * 4 + 1) * D + ad]) +
-                       (wsum[(vr * 4 + 2) * D + ad] + wsum[(vr * 4 + 3) * D + ad]);
-    auto win_slot = [&](int r) {
-      const int rr = row0 + r;
-      const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
-      return a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + a.parts + s) * (D + 4);
-    };
-    if (vr < nrows) store_partial(win_slot(vr) + 4 + ad, wacc);
-    // (row r's running max and sum are in wave r, which ran its softmax)
-    if (wave < nrows && lane < 4) store_partial(win_slot(wave) + lane, lane == 0 ? m_run : lane == 1 ? l_run : 0.0f);
-    __syncthreads();  // (wsum read before the main loop's flushes write facc_all)
-  }
+  };
   const int x = lane & 3;
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
@@ -875,6 +752,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   }
 
   KVQ_PHASE(2);
+  uint4 wqv[kWin ? (DT == KVQ_F32 ? 8 : 4) : 1];
+  float4 wmu[kWin ? 8 : 1];
+  if constexpr (kWin) {
+    // the raw query values and mu of the window key products' B operands
+    // (lane (n, g), n = 4 r + part: row r, dims 32 ks + 8 g .. + 7), then
+    // the wave's first window tiles (loads complete in issue order: the
+    // operands are built while the tiles are on their way)
+    const int r = row0 + min(wr, nrows - 1);
+    const size_t rj = (static_cast<size_t>(b) * a.Nq + r / a.G) * a.Hq + h * a.G + r % a.G;
+    const float *mu = a.win_mu ? a.win_mu + static_cast<size_t>(h) * D : nullptr;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d0 = 32 * ks + 8 * wg;
+      if constexpr (DT == KVQ_F32) {
+        const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.q) + rj * D + d0);
+        wqv[2 * ks] = qp[0];
+        wqv[2 * ks + 1] = qp[1];
+      } else {
+        wqv[ks] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + rj * D + d0);
+      }
+      const float4 *mp = reinterpret_cast<const float4 *>(mu ? mu + d0 : static_cast<const float *>(a.q));
+      wmu[2 * ks] = mp[0];
+      wmu[2 * ks + 1] = mp[1];
+    }
+    if (wave < w_tiles) win_load(wave, wkr, wvr);
+  }
   // ---- this wave's partial of each row: m = -kappa, l, z, flag, acc[128]
   // (rows past the workgroup's last are computed and never stored)
   const bool any_bad = __any(bad);
@@ -933,6 +836,174 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // order, the fence keeps the compiler from reordering them)
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  if constexpr (kWin) {
+    // ---- this split's window tokens [wu0, wu1) (fp32 products on the bf16
+    // matrix cores), once its INT2 blocks are done: the window bytes are
+    // read after the INT2 stream, not in the burst of the first blocks.  Each
+    // wave takes 16-token tiles w, w + 8, ... in pairs (the first pair's
+    // rows requested when its main loop ended):
+    //   S^T = K Q^T (v_mfma_f32_16x16x32_bf16): A = the tile's key rows (bf16,
+    //   exact), B = the raw query rows as 3 bf16 parts (built before the
+    //   loop): lane (4 r + part, g) receives the part's products for tokens
+    //   4g..4g+3, summed over the parts by two quad lane exchanges;
+    //   out = P V: A = the weights p = 2^(x - m) as 3 bf16 parts (row 4 r +
+    //   part; the k order of the 32 tokens is (tile 0, 4g + i), (tile 1,
+    //   4g + i), which is where the key product left them), B = the values in
+    //   that k order, transposed through the wave's 8 KB of facc_all (free
+    //   once its partial rows are formed).
+    // The 8 waves' (m, l, acc) meet in LDS; the split's window partial is
+    // (m, l, 0, acc[128]), merged after the INT2 partials.
+    // the B operands of the window key products: the raw query rows, scaled
+    // to base-2 logits, as 3 bf16 parts (column n = 4 r + part, part 3 zero;
+    // k-slice ks of lane (n, g) holds dims 32 ks + 8 g .. + 7), and q . mu of
+    // the lane's row
+    v8bf_w qop[4];
+    float qmu_r = 0.0f;
+    {
+    const bool row_live = wr < nrows;
+    float qm = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float qv[8];
+      if constexpr (DT == KVQ_F32) {
+        const uint4 u0 = wqv[2 * ks], u1 = wqv[2 * ks + 1];
+        const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = __uint_as_float(w8[i]);
+      } else {
+        const uint4 u0 = wqv[ks];
+        const uint32_t w4[4] = {u0.x, u0.y, u0.z, u0.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = __uint_as_float((w4[i >> 1] >> (16 * (i & 1))) << 16);
+      }
+      const float4 m0 = wmu[2 * ks], m1 = wmu[2 * ks + 1];
+      const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = row_live ? qv[i] * (kLog2eF * kInvSqrtD) : 0.0f;
+        if (a.win_mu) qm += v * mv[i];
+        const __bf16 hb = static_cast<__bf16>(v);
+        const float r1 = v - static_cast<float>(hb);
+        const __bf16 md = static_cast<__bf16>(r1);
+        const __bf16 lo2 = static_cast<__bf16>(r1 - static_cast<float>(md));
+        qop[ks][i] = wpart == 0 ? hb : wpart == 1 ? md : wpart == 2 ? lo2 : static_cast<__bf16>(0.0f);
+      }
+    }
+    // q . mu of row wr: the lane holds 32 of its dims, the 4 lanes g the rest
+    qm += lane_xor(qm, 16);
+    qm += lane_xor(qm, 32);
+    qmu_r = qm;
+    }
+    uint16_t *vt = reinterpret_cast<uint16_t *>(&facc_all[wave][0]);  // [128 dims][32 k positions] bf16
+    float m_run = -INFINITY, l_part = 0.0f;  // row wr
+    v4bf_f acc_o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc_o[dt] = v4bf_f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t0 = wave; t0 < w_tiles; t0 += 2 * kWaves) {
+      if (t0 != wave) win_load(t0, wkr, wvr);
+      const int tt[2] = {t0, t0 + kWaves};
+      // logits of row wr, tokens 4 wg + i of each tile
+      float x[2][4];
+      float cm = -INFINITY;
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+        v4bf_f sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_w, wkr[tl][ks]), qop[ks], sacc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sacc[i];
+          v += lane_xor(v, 1);
+          v += lane_xor(v, 2);
+          const bool ok = tt[tl] < w_tiles && wu0 + 16 * tt[tl] + 4 * wg + i < wu1;
+          x[tl][i] = ok ? v - qmu_r : -INFINITY;
+          cm = fmaxf(cm, x[tl][i]);
+        }
+      }
+      cm = fmaxf(cm, lane_xor(cm, 16));
+      cm = fmaxf(cm, lane_xor(cm, 32));
+      const float mn = fmaxf(m_run, cm);  // finite: tile t0 holds a token
+      const float al = m_run == -INFINITY ? 0.0f : exp2f(m_run - mn);
+      m_run = mn;
+      l_part *= al;
+      // the output rows' rescale: lane (dim, g) holds rows g (parts 0..3)
+      const float al_g = __shfl(al, 4 * wg);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc_o[dt] *= al_g;
+      // weights as the A operand of P V: row 4 wr + wpart, k = 8 wg + 4 tile + i
+      v8bf_w pa;
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = x[tl][i] == -INFINITY ? 0.0f : exp2f(x[tl][i] - mn);
+          if (wpart == 0) l_part += pv;
+          const __bf16 hb = static_cast<__bf16>(pv);
+          const float r1 = pv - static_cast<float>(hb);
+          const __bf16 md = static_cast<__bf16>(r1);
+          const __bf16 lo2 = static_cast<__bf16>(r1 - static_cast<float>(md));
+          pa[4 * tl + i] = wpart == 0 ? hb : wpart == 1 ? md : wpart == 2 ? lo2 : static_cast<__bf16>(0.0f);
+        }
+      // values transposed through LDS: vt[dim][8 (n / 4) + 4 tile + n % 4] from lane (token n, g)
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+        const int pos = 8 * (wn >> 2) + 4 * tl + (wn & 3);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint32_t w4[4] = {wvr[tl][ks].x, wvr[tl][ks].y, wvr[tl][ks].z, wvr[tl][ks].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t hv = (w4[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+            vt[(32 * ks + 8 * wg + i) * 32 + pos] = tt[tl] < w_tiles ? static_cast<uint16_t>(hv) : 0;
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint4 vb = *reinterpret_cast<const uint4 *>(vt + (16 * dt + wn) * 32 + 8 * wg);
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(v8bf_w, vb), acc_o[dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    // the wave's row sums: l over the row's 16 lanes of part 0; out[row wg]
+    // [16 dt + wn] = the parts' sum of acc_o[dt]
+    l_part += lane_xor(l_part, 16);
+    l_part += lane_xor(l_part, 32);
+    float *wps = &facc_all[wave][0];  // [4 rows][4 + 128]: m, l, -, -, acc (after this wave's vt reads)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) wps[wg * (D + 4) + 4 + 16 * dt + wn] = acc_o[dt][0] + acc_o[dt][1] + acc_o[dt][2];
+    if (wg == 0 && wpart == 0) {
+      wps[wr * (D + 4)] = m_run;
+      wps[wr * (D + 4) + 1] = l_part;
+    }
+    __syncthreads();
+    // the 8 waves' partials of each (row, dim), then the window partial of
+    // this split: slot parts + s (an empty slice stores m = -inf, l = 0)
+    const int vrow = threadIdx.x >> 7, ad = threadIdx.x & 127;
+    float ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, facc_all[w][vrow * (D + 4)]);
+    float o = 0.0f, lw = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = facc_all[w][vrow * (D + 4)];
+      const float sc = mw == -INFINITY ? 0.0f : exp2f(mw - ms);
+      o += sc * facc_all[w][vrow * (D + 4) + 4 + ad];
+      lw += sc * facc_all[w][vrow * (D + 4) + 1];
+    }
+    if (vrow < nrows) {
+      const int rr = row0 + vrow;
+      const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
+      float *slot = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + a.parts + s) * (D + 4);
+      store_partial(slot + 4 + ad, o);
+      if (ad < 4) store_partial(slot + ad, ad == 0 ? ms : ad == 1 ? lw : 0.0f);
+    }
+    __syncthreads();  // (the partials read before LDS is used again)
+  }
   if (a.premerge) {
     // more than one split: the 8 waves' partials of each row are merged
     // here first (one partial per split and row), so that the last split

@@ -285,8 +285,9 @@ int kvq_window_write(const void *k, const void *v, int32_t dtype, int64_t num_to
 
 /* kvq_decode_attn with the windows: the same arguments and workspace, plus
  * the windows (H = the cache's KV heads) and the keys' centering key_mean
- * (fp32 [H][128] or NULL, as given to kvq_quantize).  Returns UNSUPPORTED
- * for page sizes that are not a power of two. */
+ * (fp32 [H][128] or NULL, as given to kvq_quantize; 16-byte aligned, else
+ * INVALID_ARGUMENT).  Returns UNSUPPORTED for page sizes that are not a power
+ * of two. */
 int kvq_decode_attn_windows(const void *q, int32_t dtype, int32_t num_seqs, int32_t queries_per_seq,
                             int32_t num_q_heads, const kvq_cache *cache, const int32_t *page_table,
                             int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
