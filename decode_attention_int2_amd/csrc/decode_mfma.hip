@@ -35,8 +35,8 @@
 //   MFMA's B layout (column 4 r + digit, k = 16 tokens per lane group) by a
 //   byte transpose inside each lane quad and one lane permutation.
 // Query: each workgroup rotates its own query rows (signed Hadamard by the
-//   fast transform; a dense R_K is applied by an earlier launch) and forms
-//   their digits while its first key / value loads are in flight.
+//   fast transform, a dense R_K as a product with the matrix in registers)
+//   and forms their digits while its first key / value loads are in flight.
 // Addresses: the page of every 16-token tile is read from the page table with
 //   scalar loads one block ahead and turned into the (page, head) block base
 //   on the scalar unit (32-bit bounds check, one 32 x 32 -> 64-bit product);
@@ -46,6 +46,9 @@
 // Merge: each split writes an (m, l, z, acc[128]) partial with m = -kappa;
 //   the last split of a (sequence, KV head, row group) to arrive (a tagged
 //   arrival counter) merges the partials, applies R_V^T and writes the output.
+// BF16 windows (kWin): after its main loop each split attends its slice of
+//   the sink and recent window tokens on the bf16 matrix cores and stores a
+//   window partial of its own, merged beside the INT2 partials.
 #include "kvq_internal.h"
 
 #ifdef KVQ_PHASE_TIMESTAMPS
