@@ -677,6 +677,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   uint4 wkr[kWin ? 2 : 1][4], wvr[kWin ? 2 : 1][4];
   auto win_load = [&](int t0, uint4 (&kr)[kWin ? 2 : 1][4], uint4 (&vr)[kWin ? 2 : 1][4]) {
     const size_t hstride = static_cast<size_t>(a.H) * D;  // elements between window tokens
+    // the four window pointers as uniform values: a per-lane choice between
+    // two argument fields would otherwise become a per-lane load of the
+    // chosen field, and its wait would hold back every load in flight
+    using gu16 = const __attribute__((address_space(1))) uint16_t;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    using gu4 = const __attribute__((address_space(1))) u32x4;
+    auto uniform = [](const uint16_t *ptr) {
+      // (readfirstlane returns an int: each half is widened as unsigned)
+      const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+      const uint64_t w0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+      const uint64_t w1 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+      return (gu16 *)((w1 << 32) | w0);  // (global memory: loads stay off the LDS counter)
+    };
+    gu16 *sk = uniform(a.win_sk), *rk = uniform(a.win_rk), *sv = uniform(a.win_sv), *rv = uniform(a.win_rv);
 #pragma unroll
     for (int tl = 0; tl < 2; ++tl) {
       const int u = min(wu0 + 16 * (t0 + kWaves * tl) + wn, wu1 - 1);
@@ -684,12 +698,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       const size_t tok = sink ? static_cast<size_t>(b) * a.win_S + u
                               : static_cast<size_t>(b) * a.win_W + (hi + u - n_sink) % a.win_W;
       const size_t off = tok * hstride + static_cast<size_t>(h) * D + 8 * wg;
-      const uint16_t *kp = (sink ? a.win_sk : a.win_rk) + off;
-      const uint16_t *vp = (sink ? a.win_sv : a.win_rv) + off;
+      gu16 *kp = (sink ? sk : rk) + off;
+      gu16 *vp = (sink ? sv : rv) + off;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        kr[tl][ks] = *reinterpret_cast<const uint4 *>(kp + 32 * ks);
-        vr[tl][ks] = *reinterpret_cast<const uint4 *>(vp + 32 * ks);
+        const u32x4 kx = *reinterpret_cast<gu4 *>(kp + 32 * ks), vx = *reinterpret_cast<gu4 *>(vp + 32 * ks);
+        kr[tl][ks] = uint4{kx.x, kx.y, kx.z, kx.w};
+        vr[tl][ks] = uint4{vx.x, vx.y, vx.z, vx.w};
       }
     }
   };
@@ -745,6 +760,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     phase_t[8] = wall_clock64() + (first & 0u);
   }
 #endif
+  // With BF16 windows the loop also ends once a round's last claim is past
+  // the split's end; the blocks still in flight in b0, b1, b2 (claimed in
+  // that order: a valid prefix) are then computed after the wave's first
+  // window tiles are requested, so the tiles arrive while they are computed.
+  bool drain = false;  // (wave-uniform)
   for (;;) {
     if (jc0 >= nb) break;
     step(b0, jc0, a0, ja0, a1, ja1);
@@ -752,6 +772,33 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     step(b1, jc1, a1, ja1, a2, ja2);
     if (jc2 >= nb) break;
     step(b2, jc2, a2, ja2, a0, ja0);
+    if constexpr (kWin) {
+      if (ja0 >= nb) {
+        drain = true;
+        break;
+      }
+    }
+  }
+  if constexpr (kWin) {
+    if (drain) {
+      auto last = [&](int jc, Blk &bk) {
+        if (jc == nb - 1) mask_tail_meta(c, t_begin + kBlk * jc, bk);
+        compute_block<RG>(c, t_begin + kBlk * jc, bk, st, facc);
+      };
+      auto last3 = [&]() {
+        if (jc0 < nb) last(jc0, b0);
+        if (jc1 < nb) last(jc1, b1);
+        if (jc2 < nb) last(jc2, b2);
+      };
+      if (w_tiles > 0) {
+        // (every wave loads: past the slice's tiles the clamped tokens repeat
+        // its last; no branch around the loads, so the blocks' waits stay exact)
+        win_load(wave, wkr, wvr);
+        last3();
+      } else {
+        last3();
+      }
+    }
   }
 
   KVQ_PHASE(2);
@@ -779,7 +826,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       wmu[2 * ks] = mp[0];
       wmu[2 * ks + 1] = mp[1];
     }
-    if (wave < w_tiles) win_load(wave, wkr, wvr);
+    if (!drain && wave < w_tiles) win_load(wave, wkr, wvr);
   }
   // ---- this wave's partial of each row: m = -kappa, l, z, flag, acc[128]
   // (rows past the workgroup's last are computed and never stored)
