@@ -107,13 +107,20 @@ CASES = {
     "long_dense_multiquery": ("long131k", dict(tokens=1100, num_seqs=2, H=2, Hq=4, d_model=96, queries=3),
                               [1100, 333], 64, 256, False),
     "envelope_f32_small_windows": ("envelope", dict(tokens=700, queries=2), None, 16, 40, True),
+    # 22 splits of ~1,600 INT2 tokens: every wave of the long sequence completes
+    # rounds of claims and computes its last blocks after requesting its window
+    # tiles; splits 20 and 21 get no window tile (20 tiles of 16), and the
+    # short sequence's waves leave their loops before a full round
+    "paged_sh_22_splits": ("paged16x32k", dict(tokens=36000, num_seqs=2, H=2, Hq=8, d_model=64),
+                           [36000, 20000], 64, 256, False, 22),
 }
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_decode_with_windows_matches_oracle(dev, case):
     from decode_attention_int2_amd import kvq
-    name, over, lens, S, W, with_wo = CASES[case]
+    name, over, lens, S, W, with_wo, *splits = CASES[case]
+    splits = splits[0] if splits else 0
     w = synthetic.make(name, dev, **over)
     if name == "envelope":
         w.rot_k = w.rot_v = w.candidates[3]
@@ -126,10 +133,10 @@ def test_decode_with_windows_matches_oracle(dev, case):
     out_o = torch.full((rows, w.Hq, 128), 12345.0, dtype=torch.float32, device=dev)
     out_y = torch.full((rows, w.d_model), 12345.0, dtype=torch.float32, device=dev) if with_wo else None
     ws = torch.empty(max(1, kvq.kvq_decode_workspace_bytes(B, qps, w.Hq, w.H, w.tokens, w.d_model if with_wo else 0,
-                                                           0)), dtype=torch.uint8, device=dev)
+                                                           splits)), dtype=torch.uint8, device=dev)
     kvq.kvq_decode_attn_windows(w.q, B, qps, cache, w.page_table, w.page_table.shape[1], w.seq_lens, w.tokens,
                                 gpu_rot(w.rot_k), gpu_rot(w.rot_v), gw, out_o, key_mean=w.key_mean,
-                                w_o=w.w_o if with_wo else None, out_y=out_y, workspace=ws)
+                                w_o=w.w_o if with_wo else None, out_y=out_y, workspace=ws, num_splits=splits)
     torch.cuda.synchronize()
     oc = oracle.Cache(w.num_pages, w.page_size, w.H)
     oc.pages[...] = cache.pages.cpu().numpy()
