@@ -1067,20 +1067,28 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
         mw[w] = red(w, r)[0];
         mstar = fmaxf(mstar, mw[w]);
       }
+      // every wave's (l, z, acc) read at once, then summed in wave order (a
+      // wave without tokens adds nothing): one LDS round trip, not one per wave
+      float lw[kWaves], zw[kWaves], x0[kWaves], x1[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float *rwr = red(w, r);
+        lw[w] = rwr[1];
+        zw[w] = rwr[2];
+        x0[w] = rwr[4 + lane];
+        x1[w] = rwr[4 + 64 + lane];
+      }
       float l = 0.0f, z = 0.0f, a0 = 0.0f, a1 = 0.0f;
       bool nan = false;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float *rwr = red(w, r);
-        const float lw = rwr[1];
-        nan = nan || lw != lw;
+        nan = nan || lw[w] != lw[w];
         const float al = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mstar);
-        if (al != 0.0f) {
-          l += al * lw;
-          z += al * rwr[2];
-          a0 += al * rwr[4 + lane];
-          a1 += al * rwr[4 + 64 + lane];
-        }
+        const bool on = al != 0.0f;
+        l += on ? al * lw[w] : 0.0f;
+        z += on ? al * zw[w] : 0.0f;
+        a0 += on ? al * x0[w] : 0.0f;
+        a1 += on ? al * x1[w] : 0.0f;
       }
       const int rr = row0 + r;
       const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
