@@ -596,9 +596,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     if constexpr (kDense) {
       // q' = q R_K of the workgroup's rows (rows past the last are zero):
       // the raw rows go to qs; thread (kq, j) sums its quarter of column j
-      // for the rows (fp32, in row order; the rows' values are read by all
-      // lanes of a wave at once), the quarters meet in facc_all (unused until
-      // the first flush) and are added in quarter order
+      // for the rows (fp32, four interleaved partial sums over i mod 4, added
+      // pairwise; the rows' values are read by all lanes of a wave at once,
+      // a row's eight reads issued together), the quarters meet in facc_all
+      // (unused until the first flush) and are added in quarter order
       if (wave < kRows) {
         qs[wave][lane] = y0;
         qs[wave][lane + 64] = y1;
@@ -610,16 +611,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
       for (int r = 0; r < kRows; ++r) {
         const float4 *x4 = reinterpret_cast<const float4 *>(&qs[r][32 * kq]);
         const float4 rq[8] = {rs0, rs1, rs2, rs3, rs4, rs5, rs6, rs7};
-        float acc = 0.0f;
+        float4 x[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) x[m] = x4[m];
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const float4 x = x4[m];
-          acc += x.x * rq[m].x;
-          acc += x.y * rq[m].y;
-          acc += x.z * rq[m].z;
-          acc += x.w * rq[m].w;
+          a0 += x[m].x * rq[m].x;
+          a1 += x[m].y * rq[m].y;
+          a2 += x[m].z * rq[m].z;
+          a3 += x[m].w * rq[m].w;
         }
-        pr[r] = acc;
+        pr[r] = (a0 + a1) + (a2 + a3);
       }
       float *qpart = &facc_all[0][0];  // [quarter][row][column]: 4 kRows D floats, within facc_all[0]
       static_assert(4 * kRows * D <= RG * kFaccFloats, "quarter sums fit in wave 0's accumulators");
@@ -1197,8 +1200,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   if (vdense) {
     // out[r][i] = sum_c o'[r][c] R_V[i][c]: the rows' o' to LDS (rows past
     // the last are zero); thread t sums its 32 columns of row i = t / 4 for
-    // each row (fp32, in column order; 4 addresses per instruction), and
-    // the 4 threads of row i add their sums (lanes t ^ 1, then t ^ 2)
+    // each row (fp32, four interleaved partial sums over c mod 4, added
+    // pairwise; a row's eight reads issued together, 4 addresses per
+    // instruction), and the 4 threads of row i add their sums (lanes t ^ 1,
+    // then t ^ 2)
     if (wave < kRows) {
       red(wave, 0)[lane] = o0;
       red(wave, 0)[lane + 64] = o1;
@@ -1209,15 +1214,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const float4 *x4 = reinterpret_cast<const float4 *>(red(r, 0) + c0);
-      float acc = 0.0f;
+      float4 x[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) x[m] = x4[m];
+      float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const float4 x = x4[m];
-        acc += x.x * rv4[m].x;
-        acc += x.y * rv4[m].y;
-        acc += x.z * rv4[m].z;
-        acc += x.w * rv4[m].w;
+        a0 += x[m].x * rv4[m].x;
+        a1 += x[m].y * rv4[m].y;
+        a2 += x[m].z * rv4[m].z;
+        a3 += x[m].w * rv4[m].w;
       }
+      float acc = (a0 + a1) + (a2 + a3);
       acc += fdpp_xor1(acc);
       acc += fdpp_xor2(acc);
       if ((threadIdx.x & 3) == 0) red(r, 1)[ri] = acc;
