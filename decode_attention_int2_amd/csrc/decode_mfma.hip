@@ -562,18 +562,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // the third is issued after them (more loads ahead of the query rows'
   // slow down their arrival at the start of the kernel); unconditional:
   // every address is clamped into the split, or tile 0
+  // (the third block's table entries are read after the first two blocks'
+  // loads are out: scalar loads are awaited all at once, so reading them
+  // with the first entries would hold those loads back by a round trip)
   load_addr<P16>(c, t_begin + kBlk * jc0, a0);
   load_addr<P16>(c, t_begin + kBlk * jc1, a1);
-  load_addr<P16>(c, t_begin + kBlk * jc2, a2);
   if (nb == 0) {
     // an empty split (a sequence with no token here, perhaps none at all)
     // reads page 0, unused: its table entry 0 need not be valid
     repoint_all(a0);
     repoint_all(a1);
-    repoint_all(a2);
   }
   load_block<P16, NT>(c, a0, b0, bad);
   load_block<P16, NT>(c, a1, b1, bad);
+  load_addr<P16>(c, t_begin + kBlk * jc2, a2);
+  if (nb == 0) repoint_all(a2);
 #ifdef KVQ_PHASE_TIMESTAMPS
   phase_t[9] = wall_clock64();  // (diagnostic: the first blocks' loads issued)
   {
