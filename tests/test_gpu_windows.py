@@ -113,6 +113,10 @@ CASES = {
     # short sequence's waves leave their loops before a full round
     "paged_sh_22_splits": ("paged16x32k", dict(tokens=36000, num_seqs=2, H=2, Hq=8, d_model=64),
                            [36000, 20000], 64, 256, False, 22),
+    # 64-token pages, 6 splits of ~2,000 tokens (the last blocks computed after
+    # the window tiles' request, on the 64-token page addressing), W_O
+    "pages64_6_splits": ("paged16x32k", dict(tokens=12800, num_seqs=2, H=2, Hq=8, d_model=64, page_size=64),
+                         [12800, 7000], 64, 256, True, 6),
 }
 
 
