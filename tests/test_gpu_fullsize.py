@@ -162,3 +162,42 @@ def test_fullsize_calibration_search_all_heads(dev):
           flush=True)
     assert rel.max() <= 1e-3
     check_selection(best, rbest, ref)
+
+
+def test_fullsize_windows_decode_sampled(dev):
+    """The BF16-window decode at the paged workload's full size (16 x 32,768
+    tokens x 8 KV heads, 64 sink + 256 recent tokens, the default split plan
+    bench.py times): sequences 0 and 15 against the oracle, whose windows are
+    written by the oracle from those sequences' own tokens and whose cache is
+    the GPU's bytes; bar 1e-4 per (row, head)."""
+    from decode_attention_int2_amd import kvq
+    w = synthetic.make("paged16x32k", dev)
+    cache = gpu_quantize(w, dev)
+    B, T, H, qps = w.num_seqs, w.tokens, w.H, w.queries_per_seq
+    S_w, W_w = 64, 256
+    seq_idx = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T)
+    pos = torch.arange(T, dtype=torch.int32, device=dev).repeat(B)
+    gw = kvq.Windows(B, H, S_w, W_w, device=dev)
+    kvq.kvq_window_write(w.k, w.v, seq_idx, pos, gw, seq_lens=w.seq_lens)
+    out_o = torch.full((B * qps, w.Hq, 128), 12345.0, dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_decode_workspace_bytes(B, qps, w.Hq, H, T, 0, 0), dtype=torch.uint8, device=dev)
+    kvq.kvq_decode_attn_windows(w.q, B, qps, cache, w.page_table, w.page_table.shape[1], w.seq_lens, T,
+                                gpu_rot(w.rot_k), gpu_rot(w.rot_v), gw, out_o, key_mean=w.key_mean, workspace=ws)
+    torch.cuda.synchronize()
+    seqs = [0, 15]
+    oc = oracle.Cache(w.num_pages, w.page_size, H)
+    oc.pages[...] = cache.pages.cpu().numpy()
+    lens = w.seq_lens.cpu().numpy()[seqs]
+    ow = oracle.Windows(len(seqs), H, S_w, W_w, key_mean=None if w.key_mean is None else f32np(w.key_mean))
+    for i, s in enumerate(seqs):
+        oracle.window_write(f32np(w.k[s * T:(s + 1) * T]), f32np(w.v[s * T:(s + 1) * T]), np.full(T, i, np.int32),
+                            np.arange(T, dtype=np.int32), ow, seq_lens=lens)
+    rows = np.concatenate([np.arange(s * qps, (s + 1) * qps) for s in seqs])
+    pt = w.page_table.cpu().numpy()[seqs]
+    ref = oracle.decode_windows(f32np(w.q)[rows], oc, lens, oracle_rot(w.rot_k), oracle_rot(w.rot_v), ow,
+                                num_seqs=len(seqs), queries_per_seq=qps, page_table=pt, max_pages=pt.shape[1])
+    o = f32np(out_o)[rows]
+    per = max(rel_l2(o[r, j], ref[r, j]) for r in range(o.shape[0]) for j in range(o.shape[1]))
+    print(f"full-size windows decode: sequences {seqs}: worst (row, head) rel-L2 {per:.2e}", flush=True)
+    assert per <= 1e-4
+    assert np.all(np.isfinite(f32np(out_o)))
