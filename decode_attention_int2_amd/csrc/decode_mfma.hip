@@ -892,7 +892,86 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // order, the fence keeps the compiler from reordering them)
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  // the INT2 partials of this split: merged over its waves (premerge) or
+  // one per wave, stored for the merging workgroup (with BF16 windows before
+  // the window work, so that the query and mu loads of the window operands
+  // and the stores' acknowledgement overlap it)
+  auto int2_partials = [&]() {
+    if (a.premerge) {
+      // more than one split: the 8 waves' partials of each row are merged
+      // here first (one partial per split and row), so that the last split
+      // merges one per split
+      __syncthreads();
+      if (wave < nrows) {
+        const int r = wave;
+        float mw[kWaves], mstar = -INFINITY;
+  #pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          mw[w] = red(w, r)[0];
+          mstar = fmaxf(mstar, mw[w]);
+        }
+        // every wave's (l, z, acc) read at once, then summed in wave order (a
+        // wave without tokens adds nothing): one LDS round trip, not one per wave
+        float lw[kWaves], zw[kWaves], x0[kWaves], x1[kWaves];
+  #pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float *rwr = red(w, r);
+          lw[w] = rwr[1];
+          zw[w] = rwr[2];
+          x0[w] = rwr[4 + lane];
+          x1[w] = rwr[4 + 64 + lane];
+        }
+        float l = 0.0f, z = 0.0f, a0 = 0.0f, a1 = 0.0f;
+        bool nan = false;
+  #pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          nan = nan || lw[w] != lw[w];
+          const float al = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mstar);
+          const bool on = al != 0.0f;
+          l += on ? al * lw[w] : 0.0f;
+          z += on ? al * zw[w] : 0.0f;
+          a0 += on ? al * x0[w] : 0.0f;
+          a1 += on ? al * x1[w] : 0.0f;
+        }
+        const int rr = row0 + r;
+        const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
+        float *dst = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + s) * (D + 4);
+        store_partial(dst + 4 + lane, a0);
+        store_partial(dst + 4 + 64 + lane, a1);
+        if (lane < 4) store_partial(dst + lane, lane == 0 ? mstar : lane == 1 ? (nan ? __builtin_nanf("") : l)
+                                                                : lane == 2 ? z : 0.0f);
+      }
+    } else {
+      // partial slot of this wave: split s, wave w -> s * kWaves + w; stored with
+      // device-scope stores, consecutive lanes on consecutive floats
+      {
+        const int slot_w = s * kWaves + wave;
+        float *rb[kRows];  // partial base of each row of the workgroup
+  #pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+          const int rr = min(row0 + r, a.R - 1);
+          const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
+          rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + slot_w) * (D + 4);
+        }
+        constexpr int kN = (kRows * (D + 4) + 63) / 64;
+        float vals[kN];
+  #pragma unroll
+        for (int k = 0; k < kN; ++k) vals[k] = rw[min(lane + 64 * k, kRows * (D + 4) - 1)];  // all reads, then the stores
+  #pragma unroll
+        for (int k = 0; k < kN; ++k) {
+          const int idx = lane + 64 * k;
+          // rows covered by idx in [64k, 64k + 63]: (64k) / 132 and (64k + 63) / 132
+          constexpr int kRowStride = D + 4;
+          const int r_lo = (64 * k) / kRowStride, r_hi = (64 * k + 63) / kRowStride;
+          const int r = idx >= (r_lo + 1) * kRowStride ? r_hi : r_lo;
+          if (idx < nrows * kRowStride) store_partial(rb[r] + (idx - r * kRowStride), vals[k]);
+        }
+      }
+    }
+
+  };
   if constexpr (kWin) {
+    int2_partials();
     // ---- this split's window tokens [wu0, wu1) (fp32 products on the bf16
     // matrix cores), once its INT2 blocks are done: the window bytes are
     // read after the INT2 stream, not in the burst of the first blocks.  Each
@@ -1060,77 +1139,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
     }
     __syncthreads();  // (the partials read before LDS is used again)
   }
-  if (a.premerge) {
-    // more than one split: the 8 waves' partials of each row are merged
-    // here first (one partial per split and row), so that the last split
-    // merges one per split
-    __syncthreads();
-    if (wave < nrows) {
-      const int r = wave;
-      float mw[kWaves], mstar = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        mw[w] = red(w, r)[0];
-        mstar = fmaxf(mstar, mw[w]);
-      }
-      // every wave's (l, z, acc) read at once, then summed in wave order (a
-      // wave without tokens adds nothing): one LDS round trip, not one per wave
-      float lw[kWaves], zw[kWaves], x0[kWaves], x1[kWaves];
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float *rwr = red(w, r);
-        lw[w] = rwr[1];
-        zw[w] = rwr[2];
-        x0[w] = rwr[4 + lane];
-        x1[w] = rwr[4 + 64 + lane];
-      }
-      float l = 0.0f, z = 0.0f, a0 = 0.0f, a1 = 0.0f;
-      bool nan = false;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        nan = nan || lw[w] != lw[w];
-        const float al = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mstar);
-        const bool on = al != 0.0f;
-        l += on ? al * lw[w] : 0.0f;
-        z += on ? al * zw[w] : 0.0f;
-        a0 += on ? al * x0[w] : 0.0f;
-        a1 += on ? al * x1[w] : 0.0f;
-      }
-      const int rr = row0 + r;
-      const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
-      float *dst = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + s) * (D + 4);
-      store_partial(dst + 4 + lane, a0);
-      store_partial(dst + 4 + 64 + lane, a1);
-      if (lane < 4) store_partial(dst + lane, lane == 0 ? mstar : lane == 1 ? (nan ? __builtin_nanf("") : l)
-                                                              : lane == 2 ? z : 0.0f);
-    }
-  } else {
-    // partial slot of this wave: split s, wave w -> s * kWaves + w; stored with
-    // device-scope stores, consecutive lanes on consecutive floats
-    {
-      const int slot_w = s * kWaves + wave;
-      float *rb[kRows];  // partial base of each row of the workgroup
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        const int rr = min(row0 + r, a.R - 1);
-        const size_t row = static_cast<size_t>(b) * a.Nq + rr / a.G;
-        rb[r] = a.part + ((row * a.Hq + h * a.G + rr % a.G) * a.pstride + slot_w) * (D + 4);
-      }
-      constexpr int kN = (kRows * (D + 4) + 63) / 64;
-      float vals[kN];
-#pragma unroll
-      for (int k = 0; k < kN; ++k) vals[k] = rw[min(lane + 64 * k, kRows * (D + 4) - 1)];  // all reads, then the stores
-#pragma unroll
-      for (int k = 0; k < kN; ++k) {
-        const int idx = lane + 64 * k;
-        // rows covered by idx in [64k, 64k + 63]: (64k) / 132 and (64k + 63) / 132
-        constexpr int kRowStride = D + 4;
-        const int r_lo = (64 * k) / kRowStride, r_hi = (64 * k + 63) / kRowStride;
-        const int r = idx >= (r_lo + 1) * kRowStride ? r_hi : r_lo;
-        if (idx < nrows * kRowStride) store_partial(rb[r] + (idx - r * kRowStride), vals[k]);
-      }
-    }
-  }
+  if constexpr (!kWin) int2_partials();
 
   // ---- the last split of this row group to arrive merges all partials.
   // The partials travel between workgroups (and XCDs) through device-scope
