@@ -49,6 +49,8 @@
 // BF16 windows (kWin): after its main loop each split attends its slice of
 //   the sink and recent window tokens on the bf16 matrix cores and stores a
 //   window partial of its own, merged beside the INT2 partials.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 #ifdef KVQ_PHASE_TIMESTAMPS
@@ -1181,29 +1183,63 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(MfmaArgs a) {
   // the merging waves request their partials first, then (dense R_V) the
   // matrix: a wave's loads complete in issue order, so the merge does not
   // wait for the matrix's 64 KB
-  MergeIn in;
-  if (wave < nrows) merge_load(base, a.parts, lane, in);
-  __builtin_amdgcn_sched_barrier(0);
+  // (without a dense R_V, two copies of the merge: batches of 8 partials
+  // when every count is at most 8, so that few copies of the last partial
+  // are requested, and of 16, each with its own exact waits; with one, the
+  // second copy alone: measured slower with both)
   const bool vdense = a.rv.kind == KVQ_ROT_DENSE;
   // (thread t holds R_V[t / 4][32 (t % 4) .. 32 (t % 4) + 31], 128 consecutive bytes)
   float4 v0, v1, v2, v3, v4, v5, v6, v7;
-  if (vdense) {
-    const float4 *rm =
-        reinterpret_cast<const float4 *>(a.rv.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x * 8;
-    v0 = rm[0];
-    v1 = rm[1];
-    v2 = rm[2];
-    v3 = rm[3];
-    v4 = rm[4];
-    v5 = rm[5];
-    v6 = rm[6];
-    v7 = rm[7];
-  }
   float o0 = 0.0f, o1 = 0.0f, mi = -INFINITY, li = 0.0f;
   float ow0 = 0.0f, ow1 = 0.0f, mw = -INFINITY, lw = 0.0f;  // the windows' partials (one per split)
-  if (wave < nrows) {
-    if constexpr (kWin) merge_partials(base + static_cast<size_t>(a.parts) * (D + 4), a.splits, lane, ow0, ow1, &mw, &lw);
-    merge_reduce(base, a.parts, lane, in, o0, o1, &mi, &li);
+  auto merge_all = [&](auto batch) {
+    constexpr int N = decltype(batch)::value;
+    MergeIn in;
+    if (wave < nrows) merge_load<N>(base, a.parts, lane, in);
+    __builtin_amdgcn_sched_barrier(0);
+    if (vdense) {
+      const float4 *rm =
+          reinterpret_cast<const float4 *>(a.rv.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x * 8;
+      v0 = rm[0];
+      v1 = rm[1];
+      v2 = rm[2];
+      v3 = rm[3];
+      v4 = rm[4];
+      v5 = rm[5];
+      v6 = rm[6];
+      v7 = rm[7];
+    }
+    if (wave < nrows) {
+      if constexpr (kWin)
+        merge_partials<N>(base + static_cast<size_t>(a.parts) * (D + 4), a.splits, lane, ow0, ow1, &mw, &lw);
+      merge_reduce<N>(base, a.parts, lane, in, o0, o1, &mi, &li);
+    }
+  };
+  if constexpr (kDense) {
+    MergeIn in;
+    if (wave < nrows) merge_load(base, a.parts, lane, in);
+    __builtin_amdgcn_sched_barrier(0);
+    if (vdense) {
+      const float4 *rm =
+          reinterpret_cast<const float4 *>(a.rv.matrix + static_cast<size_t>(h) * D * D) + threadIdx.x * 8;
+      v0 = rm[0];
+      v1 = rm[1];
+      v2 = rm[2];
+      v3 = rm[3];
+      v4 = rm[4];
+      v5 = rm[5];
+      v6 = rm[6];
+      v7 = rm[7];
+    }
+    if (wave < nrows) {
+      if constexpr (kWin)
+        merge_partials(base + static_cast<size_t>(a.parts) * (D + 4), a.splits, lane, ow0, ow1, &mw, &lw);
+      merge_reduce(base, a.parts, lane, in, o0, o1, &mi, &li);
+    }
+  } else if (a.parts <= 8 && (!kWin || a.splits <= 8)) {
+    merge_all(std::integral_constant<int, 8>{});
+  } else {
+    merge_all(std::integral_constant<int, kMergeBatch>{});
   }
 #ifdef KVQ_PHASE_TIMESTAMPS
   __builtin_amdgcn_s_waitcnt(0);

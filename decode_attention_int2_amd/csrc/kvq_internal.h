@@ -220,13 +220,17 @@ struct MergeIn {
   float2 xa[kMergeBatch];     // value sums of batches 0, 2, ... (dims 2 lane, 2 lane + 1)
   float2 xb[kMergeBatch];     // value sums of batches 1, 3, ...
 };
+// N partials per batch (N <= kMergeBatch; a caller that knows parts <= N
+// requests fewer copies of the last one)
+template <int N = kMergeBatch>
 __device__ __forceinline__ void merge_fetch(const float *p, int parts, int lane, float2 *v, int u0) {
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u)
+  for (int u = 0; u < N; ++u)
     v[u] = load_partial2(p + static_cast<size_t>(min(u0 + u, parts - 1)) * (D + 4) + 4 + 2 * lane);
 }
+template <int N = kMergeBatch>
 __device__ __forceinline__ void merge_load(const float *p, int parts, int lane, MergeIn &in) {
-  if (parts > 64) return;
+  if (parts > 4 * N) return;
   in.ma = -INFINITY;
   in.la = in.za = 0.0f;
   if (lane < parts) {
@@ -236,13 +240,14 @@ __device__ __forceinline__ void merge_load(const float *p, int parts, int lane, 
     in.la = ml.y;
     in.za = load_partial(q + 2);
   }
-  merge_fetch(p, parts, lane, in.xa, 0);
-  if (parts > kMergeBatch) merge_fetch(p, parts, lane, in.xb, kMergeBatch);
+  merge_fetch<N>(p, parts, lane, in.xa, 0);
+  if (parts > N) merge_fetch<N>(p, parts, lane, in.xb, N);
 }
+template <int N = kMergeBatch>
 __device__ __forceinline__ void merge_reduce(const float *p, int parts, int lane, MergeIn &in, float &o0, float &o1,
                                              float *m_out = nullptr, float *l_out = nullptr) {
-  if (parts <= 64) {
-    constexpr int kB = kMergeBatch;
+  if (parts <= 4 * N) {
+    constexpr int kB = N;
     const float mstar = wave_maxf(in.ma);
     const float wa = (in.ma == -INFINITY) ? 0.0f : exp2f(in.ma - mstar);
     const bool any_nan = __any(in.la != in.la);
@@ -261,10 +266,10 @@ __device__ __forceinline__ void merge_reduce(const float *p, int parts, int lane
     };
     for (int u0 = 0; u0 < parts; u0 += 2 * kB) {
       accumulate(in.xa, u0);
-      if (u0 + 2 * kB < parts) merge_fetch(p, parts, lane, in.xa, u0 + 2 * kB);
+      if (u0 + 2 * kB < parts) merge_fetch<N>(p, parts, lane, in.xa, u0 + 2 * kB);
       if (u0 + kB < parts) {
         accumulate(in.xb, u0 + kB);
-        if (u0 + 3 * kB < parts) merge_fetch(p, parts, lane, in.xb, u0 + 3 * kB);
+        if (u0 + 3 * kB < parts) merge_fetch<N>(p, parts, lane, in.xb, u0 + 3 * kB);
       }
     }
     // dim d sits in lane d / 2 (component d % 2): lane l takes dims l and l + 64
@@ -328,11 +333,12 @@ __device__ __forceinline__ void merge_reduce(const float *p, int parts, int lane
   if (m_out) *m_out = mstar;
   if (l_out) *l_out = l;
 }
+template <int N = kMergeBatch>
 __device__ __forceinline__ void merge_partials(const float *p, int parts, int lane, float &o0, float &o1,
                                                float *m_out = nullptr, float *l_out = nullptr) {
   MergeIn in;
-  merge_load(p, parts, lane, in);
-  merge_reduce(p, parts, lane, in, o0, o1, m_out, l_out);
+  merge_load<N>(p, parts, lane, in);
+  merge_reduce<N>(p, parts, lane, in, o0, o1, m_out, l_out);
 }
 
 // out = o' R_V^T of KV head h (one wave, same register layout as above).
